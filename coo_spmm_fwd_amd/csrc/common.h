@@ -1,0 +1,129 @@
+// common.h -- internal declarations of the coospmm HIP library (gfx950).
+//
+// The library implements the truly sparse COO layer of "Beyond Masked
+// Sparsity: SNACK Enables Truly Sparse Neural Networks on GPU" (Abstract):
+// only the stored connections of W are kept and touched.  This header is
+// private to the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/coospmm.h"
+
+namespace csp {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ---------------------------------------------------------------------------
+// Layer state.  All arrays live in device memory owned by the layer.
+//   canonical order  : entries sorted by (row, col)
+//   transposed view  : canonical indices sorted by (col, row)
+// ---------------------------------------------------------------------------
+struct Workspace {
+    // Sort and restructure scratch, sized at create from nnz and the shape.
+    void *key_a = nullptr, *key_b = nullptr;  // nkey_cap keys (8 bytes each)
+    int32_t *idx_a = nullptr, *idx_b = nullptr;  // nkey_cap
+    uint32_t *u_a = nullptr, *u_b = nullptr;     // nkey_cap (flags / scans)
+    uint32_t *hist = nullptr;                    // radix histograms + scan partials
+    int32_t *rows_k = nullptr, *cols_k = nullptr;  // nnz: kept entries during restructure
+    void *vals_k = nullptr;                        // nnz values
+    int32_t *rp_k = nullptr;                       // out + 1: kept row offsets
+    uint64_t *acc_a = nullptr, *acc_b = nullptr;   // nnz: accepted regrow positions
+    uint32_t *sel = nullptr;                       // small select state / flags (256 words)
+    int64_t nkey_cap = 0;
+    size_t hist_words = 0;
+};
+
+struct ActBuffer {
+    // Batch-major copies of dense operands ([n][ld] per batch chunk), grown on demand.
+    void *a = nullptr, *b = nullptr;
+    size_t bytes = 0;
+};
+
+}  // namespace csp
+
+struct csp_layer {
+    int64_t out = 0, in = 0, nnz = 0;
+    int dtype = CSP_F32;
+    int esz = 4;  // bytes per value
+    int device = 0;
+    int32_t *rows = nullptr, *cols = nullptr;
+    void *vals = nullptr;
+    int32_t *row_ptr = nullptr;
+    int32_t *perm_c = nullptr, *rows_by_col = nullptr, *col_ptr = nullptr;
+    csp::Workspace ws;
+    csp::ActBuffer act;
+};
+
+namespace csp {
+
+// Error reporting (layer.hip).
+csp_status set_error(csp_status st, const char *fmt, ...);
+csp_status hip_error(hipError_t e, const char *what);
+
+#define CSP_HIP(call)                                         \
+    do {                                                      \
+        hipError_t e_ = (call);                               \
+        if (e_ != hipSuccess) return ::csp::hip_error(e_, #call); \
+    } while (0)
+
+#define CSP_LAUNCHED(what)                                    \
+    do {                                                      \
+        hipError_t e_ = hipGetLastError();                    \
+        if (e_ != hipSuccess) return ::csp::hip_error(e_, what); \
+    } while (0)
+
+__host__ __device__ inline int bits_for(uint64_t max_value) {  // bits needed to represent max_value
+    int b = 0;
+    while (b < 64 && (max_value >> b) != 0) ++b;
+    return b;
+}
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// sort.hip : integer building blocks (all enqueue on `s`, no host sync)
+// ---------------------------------------------------------------------------
+// Words of scratch that radix_sort_pairs / exclusive_scan need for n items.
+size_t sort_hist_words(int64_t n);
+// Stable LSD radix sort of (key, value) pairs on bits [0, end_bit).  Keys are
+// uint32 (key_bytes 4) or uint64 (key_bytes 8).  Result in keys_out/vals_out;
+// keys_tmp/vals_tmp are ping-pong scratch.  keys_in may equal keys_tmp.
+csp_status radix_sort_pairs(int key_bytes, const void *keys_in, const int32_t *vals_in, void *keys_out,
+                            int32_t *vals_out, void *keys_tmp, int32_t *vals_tmp, int64_t n, int end_bit,
+                            uint32_t *hist, hipStream_t s);
+// Exclusive prefix sum of n uint32 (in place allowed); optional *total on device.
+csp_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *partials, uint32_t *total,
+                              hipStream_t s);
+// ptr[i] = first index j with sorted[j] >= i, for i in [0, nseg]  (sorted int32, length n)
+csp_status segment_offsets(const int32_t *sorted, int64_t n, int32_t *ptr, int64_t nseg, hipStream_t s);
+csp_status fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// build.hip : canonical order and the transposed view
+// ---------------------------------------------------------------------------
+// Sorts input triples into the layer arrays; sets bit 1 of flags[0] on a bad
+// index and bit 2 on a duplicate.
+csp_status build_canonical(csp_layer *L, const int32_t *rows, const int32_t *cols, const void *vals,
+                           uint32_t *flags, hipStream_t s);
+// Rebuilds row_ptr, perm_c, rows_by_col, col_ptr from the canonical arrays.
+csp_status build_index(csp_layer *L, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// spmm.hip : the three products
+// ---------------------------------------------------------------------------
+csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, hipStream_t s);
+csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, hipStream_t s);
+csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// restructure.hip
+// ---------------------------------------------------------------------------
+csp_status run_restructure(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,
+                           hipStream_t s);
+int64_t regrow_batch_cap(const csp_layer *L);
+
+}  // namespace csp

@@ -1,0 +1,286 @@
+// layer.hip -- the C ABI of the truly sparse COO layer (include/coospmm.h):
+// argument checks on the host, layer memory, and the calls into the kernels.
+// Method: "Beyond Masked Sparsity: SNACK Enables Truly Sparse Neural Networks
+// on GPU", Abstract (COO storage of non-zero connections only; forward and
+// backward on the sparse storage; restructuring for dynamic sparse training).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "common.h"
+
+namespace csp {
+
+static thread_local char g_last_error[512] = "";
+
+csp_status set_error(csp_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+csp_status hip_error(hipError_t e, const char *what)
+{
+    if (e == hipErrorOutOfMemory) return set_error(CSP_ERR_NO_MEMORY, "%s: %s", what, hipGetErrorString(e));
+    return set_error(CSP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+namespace {
+
+constexpr int64_t kIndexLimit = 0x7FFFFFFF;  // int32 indices and offsets
+
+// Runs the body with the layer's device current, restoring the caller's.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard()
+    {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+csp_status dalloc(void **p, size_t bytes, const char *what)
+{
+    *p = nullptr;
+    if (bytes == 0) bytes = 256;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        (void)hipGetLastError();
+        return set_error(CSP_ERR_NO_MEMORY, "cannot allocate %zu bytes for %s", bytes, what);
+    }
+    return CSP_OK;
+}
+
+void free_layer(csp_layer *L)
+{
+    if (!L) return;
+    void *ptrs[] = {L->rows, L->cols, L->vals, L->row_ptr, L->perm_c, L->rows_by_col, L->col_ptr,
+                    L->ws.key_a, L->ws.key_b, L->ws.idx_a, L->ws.idx_b, L->ws.u_a, L->ws.u_b, L->ws.hist,
+                    L->ws.rows_k, L->ws.cols_k, L->ws.vals_k, L->ws.rp_k, L->ws.acc_a, L->ws.acc_b, L->ws.sel,
+                    L->act.a, L->act.b};
+    for (void *p : ptrs)
+        if (p) (void)hipFree(p);
+    delete L;
+}
+
+csp_status alloc_layer(csp_layer *L)
+{
+    const int64_t nnz = L->nnz, out = L->out, in = L->in;
+    const size_t n = (size_t)(nnz > 0 ? nnz : 1);
+    Workspace &W = L->ws;
+    W.nkey_cap = nnz > 65536 ? nnz : 65536;
+    W.hist_words = sort_hist_words(W.nkey_cap);
+    const size_t cap = (size_t)W.nkey_cap;
+    struct Req { void **p; size_t bytes; const char *what; } reqs[] = {
+        {(void **)&L->rows, 4 * n, "rows"},
+        {(void **)&L->cols, 4 * n, "cols"},
+        {(void **)&L->vals, (size_t)L->esz * n, "values"},
+        {(void **)&L->row_ptr, 4 * (size_t)(out + 1), "row offsets"},
+        {(void **)&L->perm_c, 4 * n, "column permutation"},
+        {(void **)&L->rows_by_col, 4 * n, "rows by column"},
+        {(void **)&L->col_ptr, 4 * (size_t)(in + 1), "column offsets"},
+        {&W.key_a, 8 * cap, "sort keys"},
+        {&W.key_b, 8 * cap, "sort keys"},
+        {(void **)&W.idx_a, 4 * cap, "sort values"},
+        {(void **)&W.idx_b, 4 * cap, "sort values"},
+        {(void **)&W.u_a, 4 * cap, "scan scratch"},
+        {(void **)&W.u_b, 4 * cap, "scan scratch"},
+        {(void **)&W.hist, 4 * W.hist_words, "histograms"},
+        {(void **)&W.rows_k, 4 * n, "kept rows"},
+        {(void **)&W.cols_k, 4 * n, "kept cols"},
+        {&W.vals_k, (size_t)L->esz * n, "kept values"},
+        {(void **)&W.rp_k, 4 * (size_t)(out + 1), "kept offsets"},
+        {(void **)&W.acc_a, 8 * n, "regrow positions"},
+        {(void **)&W.acc_b, 8 * n, "regrow positions"},
+        {(void **)&W.sel, 4 * 1024, "select state"},
+    };
+    for (auto &r : reqs) {
+        csp_status st = dalloc(r.p, r.bytes, r.what);
+        if (st != CSP_OK) return st;
+    }
+    return CSP_OK;
+}
+
+uint32_t regrow_word(const csp_layer *L, float v)
+{
+    uint32_t u;
+    std::memcpy(&u, &v, 4);
+    if (L->dtype == CSP_F32) return u;
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;                  // nearest even
+}
+
+}  // namespace
+}  // namespace csp
+
+using namespace csp;
+
+extern "C" {
+
+csp_status sparse_layer_create(int64_t out_features, int64_t in_features, int64_t nnz, const int32_t *rows,
+                               const int32_t *cols, const void *vals, csp_dtype dtype, void *stream,
+                               sparse_layer_t *out_layer)
+{
+    if (!out_layer) return set_error(CSP_ERR_INVALID_ARG, "out_layer is NULL");
+    *out_layer = nullptr;
+    if (out_features <= 0 || in_features <= 0 || out_features > kIndexLimit || in_features > kIndexLimit)
+        return set_error(CSP_ERR_INVALID_ARG, "shape %lld x %lld outside [1, 2^31)", (long long)out_features,
+                         (long long)in_features);
+    if (nnz < 0 || nnz > kIndexLimit || nnz > out_features * in_features)
+        return set_error(CSP_ERR_INVALID_ARG, "nnz %lld outside [0, min(out*in, 2^31))", (long long)nnz);
+    if (nnz > 0 && (!rows || !cols || !vals)) return set_error(CSP_ERR_INVALID_ARG, "NULL triple array");
+    if (dtype != CSP_F32 && dtype != CSP_BF16) return set_error(CSP_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+
+    csp_layer *L = new (std::nothrow) csp_layer;
+    if (!L) return set_error(CSP_ERR_NO_MEMORY, "host allocation failed");
+    L->out = out_features;
+    L->in = in_features;
+    L->nnz = nnz;
+    L->dtype = dtype;
+    L->esz = dtype == CSP_BF16 ? 2 : 4;
+    if (hipGetDevice(&L->device) != hipSuccess) {
+        delete L;
+        return set_error(CSP_ERR_HIP, "hipGetDevice failed");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    csp_status st = alloc_layer(L);
+    if (st == CSP_OK) st = fill_u32(L->ws.sel, 0u, 1024, s);
+    if (st == CSP_OK) st = build_canonical(L, rows, cols, vals, L->ws.sel, s);
+    if (st == CSP_OK) st = build_index(L, s);
+    uint32_t flags = 0;
+    if (st == CSP_OK) {
+        hipError_t e = hipMemcpyAsync(&flags, L->ws.sel, sizeof flags, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) st = hip_error(e, "reading the validation flags");
+    }
+    if (st == CSP_OK && (flags & 2u)) st = set_error(CSP_ERR_INDEX_RANGE, "a row or column index is out of range");
+    if (st == CSP_OK && (flags & 4u)) st = set_error(CSP_ERR_DUPLICATE, "a (row, col) pair appears more than once");
+    if (st != CSP_OK) {
+        (void)hipStreamSynchronize(s);
+        free_layer(L);
+        return st;
+    }
+    *out_layer = L;
+    return CSP_OK;
+}
+
+void sparse_layer_destroy(sparse_layer_t layer)
+{
+    if (!layer) return;
+    DeviceGuard g(layer->device);
+    (void)hipDeviceSynchronize();
+    free_layer(layer);
+}
+
+csp_status spmm_fwd(sparse_layer_t L, const void *X, int64_t B, void *Y, void *stream)
+{
+    if (!L || !X || !Y) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_fwd");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    return launch_fwd(L, X, B, Y, (hipStream_t)stream);
+}
+
+csp_status spmm_bwd_input(sparse_layer_t L, const void *dY, int64_t B, void *dX, void *stream)
+{
+    if (!L || !dY || !dX) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_input");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    if (L->dtype != CSP_F32) return set_error(CSP_ERR_DTYPE, "spmm_bwd_input supports fp32 layers only");
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    return launch_bwd_input(L, dY, B, dX, (hipStream_t)stream);
+}
+
+csp_status spmm_bwd_values(sparse_layer_t L, const void *dY, const void *X, int64_t B, float *dW, void *stream)
+{
+    if (!L || !dY || !X || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_values");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    if (L->dtype != CSP_F32) return set_error(CSP_ERR_DTYPE, "spmm_bwd_values supports fp32 layers only");
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    return launch_bwd_values(L, dY, X, B, dW, (hipStream_t)stream);
+}
+
+csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_t step, float regrow_value,
+                       void *stream)
+{
+    if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
+    if (n_prune < 0 || n_prune > L->nnz)
+        return set_error(CSP_ERR_INVALID_ARG, "n_prune %lld outside [0, nnz = %lld]", (long long)n_prune,
+                         (long long)L->nnz);
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    hipStream_t s = (hipStream_t)stream;
+    csp_status st = run_restructure(L, n_prune, seed, step, regrow_word(L, regrow_value), s);
+    if (st == CSP_OK && n_prune > 0) {
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) st = hip_error(e, "restructure");
+    }
+    return st;
+}
+
+int64_t sparse_layer_nnz(sparse_layer_t L) { return L ? L->nnz : -1; }
+
+csp_status sparse_layer_shape(sparse_layer_t L, int64_t *out_features, int64_t *in_features, int32_t *dtype)
+{
+    if (!L || !out_features || !in_features || !dtype) return set_error(CSP_ERR_INVALID_ARG, "NULL argument");
+    *out_features = L->out;
+    *in_features = L->in;
+    *dtype = L->dtype;
+    return CSP_OK;
+}
+
+csp_status sparse_layer_export(sparse_layer_t L, int32_t *rows, int32_t *cols, void *vals, void *stream)
+{
+    if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
+    DeviceGuard g(L->device);
+    hipStream_t s = (hipStream_t)stream;
+    const size_t n = (size_t)L->nnz;
+    if (n == 0) return CSP_OK;
+    if (rows) CSP_HIP(hipMemcpyAsync(rows, L->rows, 4 * n, hipMemcpyDeviceToDevice, s));
+    if (cols) CSP_HIP(hipMemcpyAsync(cols, L->cols, 4 * n, hipMemcpyDeviceToDevice, s));
+    if (vals) CSP_HIP(hipMemcpyAsync(vals, L->vals, (size_t)L->esz * n, hipMemcpyDeviceToDevice, s));
+    return CSP_OK;
+}
+
+csp_status sparse_layer_export_index(sparse_layer_t L, int32_t *row_ptr, int32_t *perm_c, int32_t *rows_by_col,
+                                     int32_t *col_ptr, void *stream)
+{
+    if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
+    DeviceGuard g(L->device);
+    hipStream_t s = (hipStream_t)stream;
+    const size_t n = (size_t)L->nnz;
+    if (row_ptr) CSP_HIP(hipMemcpyAsync(row_ptr, L->row_ptr, 4 * (size_t)(L->out + 1), hipMemcpyDeviceToDevice, s));
+    if (col_ptr) CSP_HIP(hipMemcpyAsync(col_ptr, L->col_ptr, 4 * (size_t)(L->in + 1), hipMemcpyDeviceToDevice, s));
+    if (n == 0) return CSP_OK;
+    if (perm_c) CSP_HIP(hipMemcpyAsync(perm_c, L->perm_c, 4 * n, hipMemcpyDeviceToDevice, s));
+    if (rows_by_col) CSP_HIP(hipMemcpyAsync(rows_by_col, L->rows_by_col, 4 * n, hipMemcpyDeviceToDevice, s));
+    return CSP_OK;
+}
+
+csp_status sparse_layer_set_values(sparse_layer_t L, const void *vals, void *stream)
+{
+    if (!L || (!vals && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to sparse_layer_set_values");
+    if (L->nnz == 0) return CSP_OK;
+    DeviceGuard g(L->device);
+    CSP_HIP(hipMemcpyAsync(L->vals, vals, (size_t)L->esz * (size_t)L->nnz, hipMemcpyDeviceToDevice,
+                           (hipStream_t)stream));
+    return CSP_OK;
+}
+
+void *sparse_layer_values(sparse_layer_t L) { return L ? L->vals : nullptr; }
+
+const char *sparse_layer_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+/*
+ * coospmm.h -- C ABI of the truly sparse COO layer for AMD MI355X (gfx950).
+ *
+ * Method: "Beyond Masked Sparsity: SNACK Enables Truly Sparse Neural Networks
+ * on GPU" (arXiv:2610.04093), Abstract.  The page describes a layer that keeps
+ * only the non-zero connections of a weight matrix, in COO form, computes the
+ * forward product and the backward gradients on that sparse storage alone (no
+ * dense weight tensor and no mask), and offers an API to restructure the
+ * connections during dynamic sparse training.  It prints no formulas; this
+ * header states the definitions the library implements.
+ *
+ * Notation.  W has out_features rows and in_features columns and is stored as
+ * nnz triples (row_k, col_k, v_k).  Dense operands are row-major, contiguous:
+ *   X, dX : [B, in_features]      Y, dY : [B, out_features]
+ *
+ * Conventions shared by every call:
+ *   - Device pointers unless stated otherwise; all arrays must be 4-byte
+ *     aligned (values of a bf16 layer: 2-byte aligned).
+ *   - "stream" is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls enqueue their kernels on it and return without waiting, except
+ *     where a call says it synchronizes.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - Errors are returned as a negative csp_status; nothing aborts.  The text
+ *     of the last error of the calling thread is sparse_layer_last_error().
+ *   - A layer must not be used by two streams at the same time.
+ *   - Index limits: out_features, in_features, nnz < 2^31; B >= 1.
+ */
+#ifndef COOSPMM_H
+#define COOSPMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct csp_layer *sparse_layer_t;
+
+typedef enum {
+    CSP_OK = 0,
+    CSP_ERR_INVALID_ARG = -1, /* bad pointer, size or count (checked on the host, before any launch) */
+    CSP_ERR_INDEX_RANGE = -2, /* a row or column index outside the layer (found on the device) */
+    CSP_ERR_DUPLICATE = -3,   /* a (row, col) pair given twice (found on the device) */
+    CSP_ERR_NO_MEMORY = -4,   /* a device allocation failed */
+    CSP_ERR_HIP = -5,         /* a HIP runtime call failed */
+    CSP_ERR_DTYPE = -6        /* the call does not support the layer's value type */
+} csp_status;
+
+typedef enum {
+    CSP_F32 = 0, /* fp32 values and activations, fp32 accumulation */
+    CSP_BF16 = 1 /* bf16 values and activations, fp32 accumulation, bf16 output */
+} csp_dtype;
+
+/*
+ * sparse_layer_create -- build a layer from COO triples (the page's COO
+ * weight storage, Abstract).
+ *   rows[nnz], cols[nnz] : int32 device arrays, any order, 0 <= row < out,
+ *                          0 <= col < in, no repeated (row, col) pair.
+ *   vals[nnz]            : device array of dtype.
+ * The layer copies the triples into memory it owns and puts them in canonical
+ * order: sorted by (row, col).  It also builds row offsets, and the transposed
+ * view (canonical indices sorted by (col, row)) used by the input gradient.
+ * nnz = 0 is valid.  Synchronizes on "stream" once, to read the validation
+ * result; returns CSP_ERR_INDEX_RANGE or CSP_ERR_DUPLICATE without creating a
+ * layer when the triples are invalid.  On success *out_layer owns device
+ * memory until sparse_layer_destroy.
+ */
+csp_status sparse_layer_create(int64_t out_features, int64_t in_features, int64_t nnz, const int32_t *rows,
+                               const int32_t *cols, const void *vals, csp_dtype dtype, void *stream,
+                               sparse_layer_t *out_layer);
+
+/* Frees the layer's device memory (waits for the device first).  NULL is a no-op. */
+void sparse_layer_destroy(sparse_layer_t layer);
+
+/*
+ * spmm_fwd -- forward product of the sparse layer (Abstract: the layer
+ * computes only its stored connections):
+ *     Y[b, r] = sum over stored k with row_k = r of v_k * X[b, col_k]
+ * i.e. Y = X W^T.  X [B, in] and Y [B, out] have the layer's dtype.  A row
+ * with no stored entry gives exactly 0.  fp32 accumulation in any order.
+ */
+csp_status spmm_fwd(sparse_layer_t layer, const void *X, int64_t B, void *Y, void *stream);
+
+/*
+ * spmm_bwd_input -- gradient with respect to the layer input (Abstract:
+ * gradients are backpropagated on the sparse storage):
+ *     dX[b, c] = sum over stored k with col_k = c of v_k * dY[b, row_k]
+ * i.e. dX = dY W.  dY [B, out], dX [B, in], fp32 layers only (CSP_ERR_DTYPE
+ * for bf16).
+ */
+csp_status spmm_bwd_input(sparse_layer_t layer, const void *dY, int64_t B, void *dX, void *stream);
+
+/*
+ * spmm_bwd_values -- gradient with respect to the stored values only, a
+ * sampled dense-dense product:
+ *     dW[k] = sum_b dY[b, row_k] * X[b, col_k]   for every stored k
+ * dW [nnz] is fp32 and in canonical (row, col) order (the order of
+ * sparse_layer_export and sparse_layer_values).  fp32 layers only.
+ */
+csp_status spmm_bwd_values(sparse_layer_t layer, const void *dY, const void *X, int64_t B, float *dW,
+                           void *stream);
+
+/*
+ * restructure -- one prune-and-regrow step of dynamic sparse training
+ * (Abstract: an API for restructuring connections).  The rule:
+ *  1. prune the n_prune stored entries with the smallest |v|, ordered by the
+ *     bit pattern of |v| (so +0 = -0 and NaN sorts above +inf), ties broken
+ *     by canonical index;
+ *  2. regrow n_prune entries, value regrow_value, at positions that are empty
+ *     after the prune (a just-pruned position may come back).  Candidates come
+ *     from a counter-based stream: candidate i is word (i mod 4) of the
+ *     Philox4x64-10 block with counter (i div 4, step, 0, 0) and key
+ *     (seed, 0), mapped to position floor(u * out * in / 2^64) = row * in +
+ *     col; walking i = 0, 1, 2, ..., a candidate is taken when its position
+ *     is empty and not taken before, until n_prune are taken;
+ *  3. restore canonical order and rebuild offsets and the transposed view.
+ * nnz is unchanged, and the result is a pure function of (layer contents,
+ * n_prune, seed, step, regrow_value).  0 <= n_prune <= nnz, else
+ * CSP_ERR_INVALID_ARG.  Synchronizes on "stream" (it reads back how many
+ * candidates were accepted; usually once).  regrow_value is rounded to the
+ * layer's dtype.
+ */
+csp_status restructure(sparse_layer_t layer, int64_t n_prune, uint64_t seed, uint64_t step, float regrow_value,
+                       void *stream);
+
+/* Number of stored entries; -1 for NULL. */
+int64_t sparse_layer_nnz(sparse_layer_t layer);
+/* Shape and dtype; returns CSP_ERR_INVALID_ARG for NULL arguments. */
+csp_status sparse_layer_shape(sparse_layer_t layer, int64_t *out_features, int64_t *in_features, int32_t *dtype);
+
+/*
+ * sparse_layer_export -- copy the canonical triples into caller device arrays
+ * rows[nnz], cols[nnz] (int32) and vals[nnz] (layer dtype).  Any pointer may
+ * be NULL to skip that array.
+ */
+csp_status sparse_layer_export(sparse_layer_t layer, int32_t *rows, int32_t *cols, void *vals, void *stream);
+
+/*
+ * sparse_layer_export_index -- copy the derived index arrays into caller
+ * device arrays: row_ptr[out+1] (first canonical index of each row),
+ * perm_c[nnz] (canonical indices in (col, row) order), rows_by_col[nnz]
+ * (row of each perm_c entry) and col_ptr[in+1] (first perm_c position of each
+ * column).  Any pointer may be NULL.
+ */
+csp_status sparse_layer_export_index(sparse_layer_t layer, int32_t *row_ptr, int32_t *perm_c,
+                                     int32_t *rows_by_col, int32_t *col_ptr, void *stream);
+
+/*
+ * sparse_layer_values -- device pointer to the layer's canonical values
+ * (nnz elements of the layer dtype), for in-place optimizer updates between
+ * calls.  Valid until the layer is destroyed; restructure rewrites it in
+ * place.  NULL for a NULL layer.
+ */
+void *sparse_layer_values(sparse_layer_t layer);
+
+/*
+ * sparse_layer_set_values -- overwrite the canonical values with vals[nnz]
+ * (device array of the layer dtype, canonical order), e.g. after an
+ * optimizer step kept outside the library.  Structure is unchanged.
+ */
+csp_status sparse_layer_set_values(sparse_layer_t layer, const void *vals, void *stream);
+
+/* Text of the calling thread's last error ("" if none). */
+const char *sparse_layer_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* COOSPMM_H */

@@ -1,0 +1,145 @@
+"""GPU parity of restructure (prune + regrow + re-sort): bit-exact against the oracle, step by step."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from coo_spmm_fwd_amd import binding as csp
+from coo_spmm_fwd_amd import workloads as W
+from tests.gpu_util import FP32_REL, assert_within, bits, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def export(h):
+    return tuple(host(t) for t in csp.sparse_layer_export(h))
+
+
+def check_state(orc, h, out, in_, rows, cols, vals):
+    """GPU layer holds exactly (rows, cols, vals) and its index arrays match the oracle's."""
+    r, c, v = export(h)
+    assert np.array_equal(r, rows) and np.array_equal(c, cols)
+    assert np.array_equal(bits(v), bits(vals))
+    ref = orc.canonicalize(out, in_, rows, cols, vals)
+    assert ref["status"] == 0 and np.array_equal(ref["rows"], rows)     # still canonical, no duplicates
+    row_ptr, perm_c, rbc, col_ptr = (host(t) for t in csp.sparse_layer_export_index(h))
+    assert np.array_equal(row_ptr, ref["row_ptr"]) and np.array_equal(col_ptr, ref["col_ptr"])
+    assert np.array_equal(perm_c, ref["perm_c"]) and np.array_equal(rbc, ref["rows_by_col"])
+
+
+def run_steps(orc, L: W.CooWeights, n_prune, seed, steps, regrow=0.0):
+    """Create the layer and run `steps` restructures, checking every step against the oracle."""
+    h = csp.sparse_layer_create(L.out, L.in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals)
+        rows, cols, vals = c["rows"], c["cols"], c["vals"]
+        for step in range(steps):
+            r0 = orc.restructure(L.out, L.in_, rows, cols, vals, n_prune, seed, step, regrow)
+            csp.restructure(h, n_prune, seed, step, regrow)
+            rows, cols, vals = r0[0], r0[1], r0[2]
+            check_state(orc, h, L.out, L.in_, rows, cols, vals)
+        return h, rows, cols, vals
+    except Exception:
+        csp.sparse_layer_destroy(h)
+        raise
+
+
+@pytest.mark.parametrize("out,in_,nnz,n_prune,seed", [
+    (6, 7, 12, 3, 1), (6, 7, 42, 5, 2), (6, 7, 40, 40, 3), (20, 30, 200, 20, 5), (1, 50, 10, 4, 6),
+    (50, 1, 10, 4, 7), (1000, 700, 35000, 3500, 11), (333, 777, 50000, 1, 12), (30, 30, 900, 5, 13)])
+def test_restructure_matches_oracle(orc, out, in_, nnz, n_prune, seed):
+    L = W.random_layer(out, in_, nnz, seed=seed)
+    if nnz >= 6:   # plant magnitude ties and signed zeros
+        L.vals[1] = -L.vals[0]
+        L.vals[2] = 0.0
+        L.vals[3] = -0.0
+    h, *_ = run_steps(orc, L, n_prune, seed, steps=3, regrow=0.5)
+    csp.sparse_layer_destroy(h)
+
+
+def test_restructure_zero_prune_is_identity(orc):
+    L = W.random_layer(100, 90, 900, seed=3)
+    h, rows, cols, vals = run_steps(orc, L, 0, 1, steps=1)
+    csp.sparse_layer_destroy(h)
+
+
+def test_restructure_multi_batch_path(orc, monkeypatch):
+    """Tiny candidate batches force several regrow rounds; the result must not change."""
+    monkeypatch.setenv("COOSPMM_REGROW_BATCH", "37")
+    L = W.random_layer(200, 150, 15000, seed=17)
+    h, *_ = run_steps(orc, L, 1500, 4, steps=2)
+    csp.sparse_layer_destroy(h)
+
+
+def test_restructure_bf16(orc):
+    L = W.random_layer(300, 200, 6000, seed=19, dtype="bf16")
+    h = csp.sparse_layer_create(300, 200, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(300, 200, L.rows, L.cols, L.vals)
+        regrow_bits = W.f32_to_bf16_bits(np.array([0.125], np.float32))[0]
+        rr, cr, vr, _ = orc.restructure(300, 200, c["rows"], c["cols"], c["vals"], 600, 9, 2, regrow_bits)
+        csp.restructure(h, 600, 9, 2, 0.125)
+        check_state(orc, h, 300, 200, rr, cr, vr)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_restructure_rejects_bad_count():
+    L = W.random_layer(10, 10, 20, seed=1)
+    h = csp.sparse_layer_create(10, 10, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        for bad in (-1, 21):
+            with pytest.raises(csp.CspError) as e:
+                csp.restructure(h, bad, 1, 1)
+            assert e.value.status == -1
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_products_after_restructure(orc):
+    """After restructure the products use the new structure (offsets and transposed view rebuilt)."""
+    L = W.random_layer(700, 500, 20000, seed=23)
+    h, rows, cols, vals = run_steps(orc, L, 2000, 8, steps=2)
+    try:
+        X = W.random_dense((16, 500), 1)
+        dY = W.random_dense((16, 700), 2)
+        Y = host(csp.spmm_fwd(h, dev(X)))
+        ref, S = orc.spmm_fwd(700, 500, rows, cols, vals, X)
+        assert_within(Y, ref, S, FP32_REL, "fwd after restructure")
+        dX = host(csp.spmm_bwd_input(h, dev(dY)))
+        ref, S = orc.spmm_bwd_input(700, 500, rows, cols, vals, dY)
+        assert_within(dX, ref, S, FP32_REL, "dX after restructure")
+        dW = host(csp.spmm_bwd_values(h, dev(dY), dev(X)))
+        ref, S = orc.spmm_bwd_values(700, 500, rows, cols, dY, X)
+        assert_within(dW, ref, S, FP32_REL, "dW after restructure")
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_dst_loop_full_size(orc):
+    """8192x8192 at 95% sparsity, B=64: 10 steps of value gradient, SGD (harness), restructure of 10%."""
+    w, layers, acts = W.build("dst8192_b64_s95")
+    L = layers[0]
+    n_prune = int(np.floor(w.prune_frac * L.nnz))
+    h = csp.sparse_layer_create(L.out, L.in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals)
+        X, dY = dev(acts[64]["X"]), dev(acts[64]["dY"])
+        for step in range(w.steps):
+            dW = csp.spmm_bwd_values(h, dY, X)
+            _, _, v = csp.sparse_layer_export(h)
+            csp.sparse_layer_set_values(h, (v - 1e-3 * dW).contiguous())
+            rows, cols, vals = export(h)
+            r0 = orc.restructure(L.out, L.in_, rows, cols, vals, n_prune, w.seed, step, 0.0)
+            csp.restructure(h, n_prune, w.seed, step, 0.0)
+            r, c_, v_ = export(h)
+            assert np.array_equal(r, r0[0]) and np.array_equal(c_, r0[1])
+            assert np.array_equal(bits(v_), bits(r0[2])), f"step {step}"
+        check_state(orc, h, L.out, L.in_, r0[0], r0[1], r0[2])
+    finally:
+        csp.sparse_layer_destroy(h)
