@@ -1,0 +1,278 @@
+"""Throughput of the truly sparse COO layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--warm]
+
+One step is one training pass of the layer over one batch: spmm_fwd, then
+spmm_bwd (input gradient and value gradient in one launch sequence).  The
+default workload is the single sparse linear layer 4096 x 4096 at 95%
+unstructured sparsity (838,861 stored fp32 entries), batch 16.
+
+Inputs are resident in HBM before timing starts.  Unless --warm is given,
+steps cycle through enough replicas of the layer and its dense operands
+(together more than twice the 256 MiB last-level cache) that each step reads
+its data from HBM rather than from cache.
+
+Printed: one JSON line.  `value` is the effective bandwidth of the step:
+algorithmic bytes of forward + input gradient + value gradient (byte models
+below) over the measured step time.  `roofline` covers the dominant kernel,
+timed with HIP events that the library records immediately around it, in a
+second pass with the same work.  `cpu_baseline` times the CPU oracle (plain C
+loops, fp64 accumulation, one core) on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "coo_spmm_fwd_amd", "csrc", "spmm.hip")
+
+
+# ------------------------------------------------------------------ byte models
+def bytes_fwd(nnz, out, in_, B, sv=4, sx=4):
+    """Forward: column index + value per entry, row offsets, X read once, Y written once."""
+    return nnz * (sv + 4) + 4 * (out + 1) + sx * B * (in_ + out)
+
+
+def bytes_dx(nnz, out, in_, B):
+    """Input gradient: gathered value + permutation + row index per entry, column offsets, dY, dX."""
+    return nnz * (4 + 4 + 4) + 4 * (in_ + 1) + 4 * B * (in_ + out)
+
+
+def bytes_dw(nnz, out, in_, B):
+    """Value gradient: column index read + dW written per entry, row offsets, X and dY."""
+    return nnz * (4 + 4) + 4 * (out + 1) + 4 * B * (in_ + out)
+
+
+def bytes_bwd_fused(nnz, out, in_, B):
+    """Both gradients in one column-order pass: row index, permutation, gathered value,
+    dW write per entry; column offsets; X and dY read once; dX written once."""
+    return nnz * 16 + 4 * (in_ + 1) + 4 * B * (2 * in_ + out)
+
+
+def source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel: str, launch_args: dict):
+    """HBM bytes per launch from committed counter runs, if taken on the current kernel source."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = rec.get(kernel)
+    if not e or e.get("source_sha") != source_sha() or e.get("args") != launch_args:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(w, L, acts, B, budget_s=12.0):
+    """The oracle as written (fp64 loops, one core) on the same step: forward, dX, dW."""
+    import numpy as np
+    import oracle
+    orc = oracle.default()
+    X, dY = acts[B]["X"], acts[B]["dY"]
+    canon = orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals)
+    reps, t_all = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, X)
+        orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dY)
+        orc.spmm_bwd_values(L.out, L.in_, canon["rows"], canon["cols"], dY, X)
+        t_all += time.perf_counter() - t0
+        reps += 1
+        if t_all >= budget_s or reps >= 100:
+            break
+    step_s = t_all / reps
+    nbytes = bytes_fwd(L.nnz, L.out, L.in_, B) + bytes_dx(L.nnz, L.out, L.in_, B) + bytes_dw(L.nnz, L.out, L.in_, B)
+    return {"value": round(nbytes / step_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full step(s) (forward, input gradient, value gradient) of the same layer and batch, "
+                      f"{step_s * 1e3:.1f} ms per step"}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="linear4096_b16_s95")
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--warm", action="store_true", help="reuse one replica (cache-resident data)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--eager", action="store_true", help="launch each call from Python instead of graph replay")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each MI355X runs its own layer; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from coo_spmm_fwd_amd import binding as csp
+    from coo_spmm_fwd_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    w, layers, acts = W.build(args.workload)
+    if w.dtype != "f32" or len(layers) != 1:
+        print(f"workload {args.workload} is not a single fp32 training layer", file=sys.stderr)
+        sys.exit(2)
+    L = layers[0]
+    B = args.batch or w.batches[0]
+    if B not in acts:
+        acts[B] = dict(X=W.random_dense((B, L.in_), 11), dY=W.random_dense((B, L.out), 12))
+    nnz, out, in_ = L.nnz, L.out, L.in_
+
+    b_fwd, b_dx, b_dw = bytes_fwd(nnz, out, in_, B), bytes_dx(nnz, out, in_, B), bytes_dw(nnz, out, in_, B)
+    b_bwd = bytes_bwd_fused(nnz, out, in_, B)
+    step_bytes = b_fwd + b_dx + b_dw
+    # bytes one step touches in one replica: structure of both orders, values, dW, dense operands
+    touched = nnz * (4 * 5 + 4) + 4 * B * (3 * in_ + 2 * out)
+    R = 1 if args.warm else max(2, -(-2 * MALL_BYTES // touched) + 1)
+
+    t = lambda a: torch.from_numpy(a).to(dev)
+    rows, cols, vals = t(L.rows), t(L.cols), t(L.vals)
+    handles = [csp.sparse_layer_create(out, in_, rows, cols, vals) for _ in range(R)]
+    Xs = [t(acts[B]["X"]) for _ in range(R)]
+    dYs = [t(acts[B]["dY"]) for _ in range(R)]
+    Ys = [torch.empty((B, out), device=dev) for _ in range(R)]
+    dXs = [torch.empty((B, in_), device=dev) for _ in range(R)]
+    dWs = [torch.empty((nnz,), device=dev) for _ in range(R)]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        j = i % R
+        csp.spmm_fwd(handles[j], Xs[j], Ys[j], stream=stream)
+        csp.spmm_bwd(handles[j], dYs[j], Xs[j], dXs[j], dWs[j], stream=stream)
+
+    for i in range(max(args.warmup, R)):  # eager warm-up; also sizes every layer's operand workspace
+        step(i)
+    torch.cuda.synchronize()
+
+    # One HIP graph per replica holds one step (two library calls, five kernels),
+    # so the timed loop is K graph launches and host-side Python costs stay out.
+    graphs = []
+    if not args.eager:
+        for j in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s_cap = torch.cuda.current_stream()
+                csp.spmm_fwd(handles[j], Xs[j], Ys[j], stream=s_cap)
+                csp.spmm_bwd(handles[j], dYs[j], Xs[j], dXs[j], dWs[j], stream=s_cap)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        if graphs:
+            graphs[i % R].replay()
+        else:
+            step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # second pass, same work: events around each op and around the main kernels
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for evs in ev:  # instantiate the events
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(K):
+        j = i % R
+        a = ev[i]
+        a[0].record(stream)
+        csp.sparse_layer_time_next(handles[j], a[1], a[2])
+        csp.spmm_fwd(handles[j], Xs[j], Ys[j], stream=stream)
+        a[3].record(stream)
+        csp.sparse_layer_time_next(handles[j], a[4], a[5])
+        csp.spmm_bwd(handles[j], dYs[j], Xs[j], dXs[j], dWs[j], stream=stream)
+    torch.cuda.synchronize()
+    fwd_op = sum(a[0].elapsed_time(a[3]) for a in ev) / K
+    fwd_k = sum(a[1].elapsed_time(a[2]) for a in ev) / K
+    bwd_k = sum(a[4].elapsed_time(a[5]) for a in ev) / K
+    ld = 1
+    while ld < min(B, 64):
+        ld *= 2
+    kernels = {
+        "forward": {"name": f"k_segment_spmm<{ld}, F32, false, false>", "us": fwd_k * 1e3, "bytes": b_fwd},
+        "backward": {"name": f"k_bwd_cols<{ld}, false>", "us": bwd_k * 1e3, "bytes": b_bwd},
+    }
+    dom_key = max(kernels, key=lambda k: kernels[k]["us"])
+    dom = kernels[dom_key]
+    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+    traffic = traffic_for(dom["name"], {"workload": args.workload, "batch": B})
+
+    # restructure on the same layer (10% of entries), timed separately
+    n_prune = nnz // 10
+    torch.cuda.synchronize()
+    r0 = time.perf_counter()
+    csp.restructure(handles[0], n_prune, seed=w.seed, step=1)
+    restructure_ms = (time.perf_counter() - r0) * 1e3
+
+    del graphs
+    torch.cuda.synchronize()
+    for h in handles:
+        csp.sparse_layer_destroy(h)
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    flops = 3 * 2 * nnz * B
+    rec = {
+        "metric": "SpMM fwd+bwd effective GB/s and GFLOP/s (2*nnz*B); % of HBM roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "out": out, "in": in_, "nnz": nnz, "batch": B,
+                   "sparsity": round(1 - nnz / (out * in_), 4), "step": "spmm_fwd + spmm_bwd (dX and dW)",
+                   "replicas": R, "cache": "warm" if args.warm else "cold",
+                   "launch": "eager" if args.eager else "hip_graph_per_step"},
+        "gflops": round(flops / (ms_per_step * 1e-3) / 1e9, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": dom["name"], "avg_launch_us": round(dom["us"], 3),
+                     "bytes_per_launch": dom["bytes"]},
+        "ops_us": {"forward_call": round(fwd_op * 1e3, 3), "forward_kernel": round(fwd_k * 1e3, 3),
+                   "backward_kernel": round(bwd_k * 1e3, 3)},
+        "restructure_ms": round(restructure_ms, 3),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu:
+        rec["cpu_baseline"] = cpu_baseline(w, L, acts, B)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

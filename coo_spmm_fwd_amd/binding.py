@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(HERE, "libcoospmm.so")
 CSP_F32, CSP_BF16 = 0, 1
 STATUS = {0: "CSP_OK", -1: "CSP_ERR_INVALID_ARG", -2: "CSP_ERR_INDEX_RANGE", -3: "CSP_ERR_DUPLICATE",
           -4: "CSP_ERR_NO_MEMORY", -5: "CSP_ERR_HIP", -6: "CSP_ERR_DTYPE"}
-EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_bwd_input", "spmm_bwd_values",
+EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_bwd_input", "spmm_bwd_values", "spmm_bwd",
             "restructure", "sparse_layer_nnz", "sparse_layer_shape", "sparse_layer_export",
-            "sparse_layer_export_index", "sparse_layer_values", "sparse_layer_set_values",
+            "sparse_layer_export_index", "sparse_layer_values", "sparse_layer_set_values", "sparse_layer_time_next",
             "sparse_layer_last_error"]
 
 
@@ -52,6 +52,8 @@ def load(path: str = LIB_PATH):
     L.spmm_bwd_input.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]
     L.spmm_bwd_values.restype = c_int
     L.spmm_bwd_values.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]
+    L.spmm_bwd.restype = c_int
+    L.spmm_bwd.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]
     L.restructure.restype = c_int
     L.restructure.argtypes = [c_void_p, c_int64, c_uint64, c_uint64, c_float, c_void_p]
     L.sparse_layer_nnz.restype = c_int64
@@ -66,6 +68,8 @@ def load(path: str = LIB_PATH):
     L.sparse_layer_values.argtypes = [c_void_p]
     L.sparse_layer_set_values.restype = c_int
     L.sparse_layer_set_values.argtypes = [c_void_p, c_void_p, c_void_p]
+    L.sparse_layer_time_next.restype = c_int
+    L.sparse_layer_time_next.argtypes = [c_void_p, c_void_p, c_void_p]
     L.sparse_layer_last_error.restype = c_char_p
     L.sparse_layer_last_error.argtypes = []
     _lib = L
@@ -189,6 +193,23 @@ def spmm_bwd_values(layer: int, dY, X, dW=None, stream=None):
     return dW
 
 
+def spmm_bwd(layer: int, dY, X, dX=None, dW=None, stream=None):
+    """Both gradients in one pass: dX = dY W and dW[k] = sum_b dY[b, row_k] X[b, col_k]."""
+    out, in_, dt = sparse_layer_shape(layer)
+    nnz = sparse_layer_nnz(layer)
+    B = int(X.shape[0])
+    gp = _dev(dY, "dY", _torch_dtype(dt), (B, out))
+    xp = _dev(X, "X", _torch_dtype(dt), (B, in_))
+    if dX is None:
+        dX = _torch().empty((B, in_), dtype=X.dtype, device=X.device)
+    if dW is None:
+        dW = _torch().empty((nnz,), dtype=_torch().float32, device=X.device)
+    dxp = _dev(dX, "dX", _torch_dtype(dt), (B, in_))
+    wp = _dev(dW, "dW", _torch().float32, (nnz,))
+    _check(load().spmm_bwd(c_void_p(layer), gp, xp, B, dxp, wp, _stream(stream)))
+    return dX, dW
+
+
 def restructure(layer: int, n_prune: int, seed: int, step: int, regrow_value: float = 0.0, stream=None):
     """Prune n_prune smallest-|v| entries and regrow as many at empty positions (synchronizes)."""
     _check(load().restructure(c_void_p(layer), int(n_prune), int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
@@ -236,3 +257,9 @@ def sparse_layer_set_values(layer: int, vals, stream=None):
     nnz = sparse_layer_nnz(layer)
     vp = _dev(vals, "vals", _torch_dtype(dt), (nnz,))
     _check(load().sparse_layer_set_values(c_void_p(layer), vp, _stream(stream)))
+
+
+def sparse_layer_time_next(layer: int, ev_before, ev_after):
+    """Bracket the main kernel of the next product call with two torch.cuda.Event objects."""
+    _check(load().sparse_layer_time_next(c_void_p(layer), c_void_p(ev_before.cuda_event),
+                                         c_void_p(ev_after.cuda_event)))

@@ -55,6 +55,50 @@ __global__ void k_rows_by_col(const int32_t *__restrict__ rows, const int32_t *_
     if (j < nnz) rows_by_col[j] = rows[perm[j]];
 }
 
+// Tasks per segment: one for a segment of at most kTaskChunk entries (also
+// for an empty one, which still owns its zero output), else one per chunk.
+__global__ void k_seg_pieces(const int32_t *__restrict__ ptr, int64_t nseg, uint32_t *__restrict__ pieces)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nseg) return;
+    int64_t len = (int64_t)ptr[i + 1] - ptr[i];
+    pieces[i] = len <= kTaskChunk ? 1u : (uint32_t)((len + kTaskChunk - 1) / kTaskChunk);
+}
+
+__global__ void k_emit_tasks(const int32_t *__restrict__ ptr, const int32_t *__restrict__ first, int64_t nseg,
+                             int4 *__restrict__ desc, int64_t cap, int4 *__restrict__ split,
+                             uint32_t *__restrict__ nsplit)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nseg) return;
+    const int32_t f = first[i], p = first[i + 1] - f, b = ptr[i], e = ptr[i + 1];
+    for (int32_t j = 0; j < p && (int64_t)f + j < cap; ++j) {
+        const int32_t kb = b + j * kTaskChunk;
+        const int32_t ke = kb + kTaskChunk < e ? kb + kTaskChunk : e;
+        desc[f + j] = make_int4((int32_t)i, kb, ke, p > 1 ? f + j : -1);
+    }
+    if (p > 1) split[atomicAdd(nsplit, 1u)] = make_int4((int32_t)i, f, p, 0);
+}
+
+// seg_first[0..nseg) = exclusive scan of the per-segment task counts,
+// seg_first[nseg] = the total; then one descriptor per task and one record
+// per split segment (their order is irrelevant: each record is self-contained).
+csp_status build_tasks(TaskList &T, const int32_t *ptr, int64_t nseg, uint32_t *partials, uint32_t *nsplit,
+                       hipStream_t s)
+{
+    const unsigned grid = (unsigned)ceil_div(nseg, 256);
+    uint32_t *first = (uint32_t *)T.seg_first;
+    k_seg_pieces<<<grid, 256, 0, s>>>(ptr, nseg, first);
+    CSP_LAUNCHED("k_seg_pieces");
+    csp_status st = exclusive_scan_u32(first, first, nseg, partials, first + nseg, s);
+    if (st != CSP_OK) return st;
+    st = fill_u32(nsplit, 0u, 1, s);
+    if (st != CSP_OK) return st;
+    k_emit_tasks<<<grid, 256, 0, s>>>(ptr, T.seg_first, nseg, T.desc, T.cap, T.split, nsplit);
+    CSP_LAUNCHED("k_emit_tasks");
+    return CSP_OK;
+}
+
 }  // namespace
 
 csp_status build_index(csp_layer *L, hipStream_t s)
@@ -72,7 +116,29 @@ csp_status build_index(csp_layer *L, hipStream_t s)
         k_rows_by_col<<<grid, 256, 0, s>>>(L->rows, L->perm_c, nnz, L->rows_by_col);
         CSP_LAUNCHED("k_rows_by_col");
     }
-    return segment_offsets((const int32_t *)L->ws.key_a, nnz, L->col_ptr, L->in, s);
+    st = segment_offsets((const int32_t *)L->ws.key_a, nnz, L->col_ptr, L->in, s);
+    if (st != CSP_OK) return st;
+
+    // Task lists for the row-order and column-order passes (scan partials in
+    // the now free radix histogram area); the task and split counts are read back.
+    uint32_t *nsplit = L->ws.sel + 512;  // two words outside the select state
+    st = build_tasks(L->row_tasks, L->row_ptr, L->out, L->ws.hist, nsplit, s);
+    if (st != CSP_OK) return st;
+    st = build_tasks(L->col_tasks, L->col_ptr, L->in, L->ws.hist, nsplit + 1, s);
+    if (st != CSP_OK) return st;
+    int32_t counts[4] = {0, 0, 0, 0};
+    CSP_HIP(hipMemcpyAsync(&counts[0], L->row_tasks.seg_first + L->out, 4, hipMemcpyDeviceToHost, s));
+    CSP_HIP(hipMemcpyAsync(&counts[1], L->col_tasks.seg_first + L->in, 4, hipMemcpyDeviceToHost, s));
+    CSP_HIP(hipMemcpyAsync(&counts[2], nsplit, 8, hipMemcpyDeviceToHost, s));
+    CSP_HIP(hipStreamSynchronize(s));
+    L->row_tasks.count = counts[0];
+    L->col_tasks.count = counts[1];
+    L->row_tasks.nsplit = counts[2];
+    L->col_tasks.nsplit = counts[3];
+    if (L->row_tasks.count > L->row_tasks.cap || L->col_tasks.count > L->col_tasks.cap)
+        return set_error(CSP_ERR_HIP, "task list overflow (%lld/%lld, %lld/%lld)", (long long)L->row_tasks.count,
+                         (long long)L->row_tasks.cap, (long long)L->col_tasks.count, (long long)L->col_tasks.cap);
+    return CSP_OK;
 }
 
 template <typename K>

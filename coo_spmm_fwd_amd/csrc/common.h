@@ -38,9 +38,28 @@ struct Workspace {
 };
 
 struct ActBuffer {
-    // Batch-major copies of dense operands ([n][ld] per batch chunk), grown on demand.
+    // Batch-minor copies of dense operands ([chunk][n][ld]) and split-segment
+    // partial sums, grown on demand with the batch size.
     void *a = nullptr, *b = nullptr;
     size_t bytes = 0;
+    float *partial = nullptr;
+    size_t partial_bytes = 0;
+};
+
+// Segments (rows for the row-order passes, columns for the transposed ones)
+// are cut into tasks of at most kTaskChunk entries; one wavefront runs one
+// task.  A segment cut into several tasks ("split") gets its output from a
+// separate fixup launch that adds the tasks' partial sums in task order, so
+// results do not depend on scheduling and no cross-wave fence is needed.
+constexpr int kTaskChunk = 512;
+
+struct TaskList {
+    int4 *desc = nullptr;   // [cap] {segment, first entry, end entry, partial slot or -1}
+    int4 *split = nullptr;  // [nseg] {segment, first task, task count, 0} of split segments
+    int32_t *seg_first = nullptr;  // [nseg + 1] first task of each segment
+    int64_t count = 0;      // tasks in use
+    int64_t nsplit = 0;     // split segments in use
+    int64_t cap = 0;
 };
 
 }  // namespace csp
@@ -54,11 +73,22 @@ struct csp_layer {
     void *vals = nullptr;
     int32_t *row_ptr = nullptr;
     int32_t *perm_c = nullptr, *rows_by_col = nullptr, *col_ptr = nullptr;
+    csp::TaskList row_tasks, col_tasks;
     csp::Workspace ws;
     csp::ActBuffer act;
+    hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request
 };
 
 namespace csp {
+
+// Records the layer's pending timing events around one main-kernel launch
+// (before = true: just before it, then false: just after it, clearing the request).
+inline void timing_mark(csp_layer *L, bool before, hipStream_t s)
+{
+    hipEvent_t &e = before ? L->time_before : L->time_after;
+    if (e) (void)hipEventRecord(e, s);
+    if (!before) L->time_before = L->time_after = nullptr;
+}
 
 // Error reporting (layer.hip).
 csp_status set_error(csp_status st, const char *fmt, ...);
@@ -109,8 +139,10 @@ csp_status fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s);
 // index and bit 2 on a duplicate.
 csp_status build_canonical(csp_layer *L, const int32_t *rows, const int32_t *cols, const void *vals,
                            uint32_t *flags, hipStream_t s);
-// Rebuilds row_ptr, perm_c, rows_by_col, col_ptr from the canonical arrays.
+// Rebuilds row_ptr, perm_c, rows_by_col, col_ptr and both task lists from the
+// canonical arrays.  Synchronizes on s (reads back the task counts).
 csp_status build_index(csp_layer *L, hipStream_t s);
+inline int64_t task_cap(int64_t nseg, int64_t nnz) { return nseg + (nnz + kTaskChunk - 1) / kTaskChunk; }
 
 // ---------------------------------------------------------------------------
 // spmm.hip : the three products
@@ -118,6 +150,7 @@ csp_status build_index(csp_layer *L, hipStream_t s);
 csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, hipStream_t s);
 csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, hipStream_t s);
 csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s);
+csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // restructure.hip

@@ -68,7 +68,9 @@ void free_layer(csp_layer *L)
     void *ptrs[] = {L->rows, L->cols, L->vals, L->row_ptr, L->perm_c, L->rows_by_col, L->col_ptr,
                     L->ws.key_a, L->ws.key_b, L->ws.idx_a, L->ws.idx_b, L->ws.u_a, L->ws.u_b, L->ws.hist,
                     L->ws.rows_k, L->ws.cols_k, L->ws.vals_k, L->ws.rp_k, L->ws.acc_a, L->ws.acc_b, L->ws.sel,
-                    L->act.a, L->act.b};
+                    L->act.a, L->act.b, L->act.partial,
+                    L->row_tasks.desc, L->row_tasks.split, L->row_tasks.seg_first,
+                    L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete L;
@@ -81,7 +83,11 @@ csp_status alloc_layer(csp_layer *L)
     Workspace &W = L->ws;
     W.nkey_cap = nnz > 65536 ? nnz : 65536;
     W.hist_words = sort_hist_words(W.nkey_cap);
+    const int64_t nseg_max = out > in ? out : in;
+    if (W.hist_words < (size_t)(ceil_div(nseg_max, 4096) + 64)) W.hist_words = (size_t)(ceil_div(nseg_max, 4096) + 64);
     const size_t cap = (size_t)W.nkey_cap;
+    L->row_tasks.cap = task_cap(out, nnz);
+    L->col_tasks.cap = task_cap(in, nnz);
     struct Req { void **p; size_t bytes; const char *what; } reqs[] = {
         {(void **)&L->rows, 4 * n, "rows"},
         {(void **)&L->cols, 4 * n, "cols"},
@@ -104,6 +110,12 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&W.acc_a, 8 * n, "regrow positions"},
         {(void **)&W.acc_b, 8 * n, "regrow positions"},
         {(void **)&W.sel, 4 * 1024, "select state"},
+        {(void **)&L->row_tasks.desc, 16 * (size_t)L->row_tasks.cap, "row tasks"},
+        {(void **)&L->row_tasks.split, 16 * (size_t)out, "split rows"},
+        {(void **)&L->row_tasks.seg_first, 4 * (size_t)(out + 1), "row task offsets"},
+        {(void **)&L->col_tasks.desc, 16 * (size_t)L->col_tasks.cap, "column tasks"},
+        {(void **)&L->col_tasks.split, 16 * (size_t)in, "split columns"},
+        {(void **)&L->col_tasks.seg_first, 4 * (size_t)(in + 1), "column task offsets"},
     };
     for (auto &r : reqs) {
         csp_status st = dalloc(r.p, r.bytes, r.what);
@@ -212,6 +224,16 @@ csp_status spmm_bwd_values(sparse_layer_t L, const void *dY, const void *X, int6
     return launch_bwd_values(L, dY, X, B, dW, (hipStream_t)stream);
 }
 
+csp_status spmm_bwd(sparse_layer_t L, const void *dY, const void *X, int64_t B, void *dX, float *dW, void *stream)
+{
+    if (!L || !dY || !X || !dX || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    if (L->dtype != CSP_F32) return set_error(CSP_ERR_DTYPE, "spmm_bwd supports fp32 layers only");
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    return launch_bwd(L, dY, X, B, dX, dW, (hipStream_t)stream);
+}
+
 csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_t step, float regrow_value,
                        void *stream)
 {
@@ -280,6 +302,14 @@ csp_status sparse_layer_set_values(sparse_layer_t L, const void *vals, void *str
 }
 
 void *sparse_layer_values(sparse_layer_t L) { return L ? L->vals : nullptr; }
+
+csp_status sparse_layer_time_next(sparse_layer_t L, void *ev_before, void *ev_after)
+{
+    if (!L || !ev_before || !ev_after) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to sparse_layer_time_next");
+    L->time_before = (hipEvent_t)ev_before;
+    L->time_after = (hipEvent_t)ev_after;
+    return CSP_OK;
+}
 
 const char *sparse_layer_last_error(void) { return g_last_error; }
 

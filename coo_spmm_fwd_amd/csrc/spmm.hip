@@ -6,16 +6,23 @@
 //   input grad   dX[b,c] = sum_{k in col c} v_k dY[b,row_k]
 //   value grad   dW_k    = sum_b dY[b,row_k] X[b,col_k]
 //
-// Memory layout.  Dense operands arrive row-major ([B, n]).  For B > 1 each
-// kernel first copies its gathered operand to a batch-minor layout [n][ld]
-// (ld = batch padded to a power of two, at most 64; larger batches are cut
-// into chunks of 64), so that the B values one stored entry needs are one
-// contiguous 4*ld-byte run: a single coalesced load instead of B scattered
-// ones.  Inside a wavefront, lane = (slot s, batch b) with S = 64/ld slots:
-// each slot walks every S-th entry of a segment, and slots are summed with
-// cross-lane shuffles at the end of the segment.  No MFMA: an unstructured
-// gather is not a dense contraction; the kernels are bound by HBM for the
-// COO stream and by L2/L1 for the operand gathers.
+// Layout.  Dense operands arrive row-major ([B, n]).  For B > 1 each call
+// first copies the operand it gathers to a batch-minor layout [chunk][n][ld]
+// (ld = batch rounded up to a power of two, at most 64; a batch above 64 is cut
+// into chunks of 64), so the B values one stored entry needs form one
+// contiguous 4*ld-byte run: one coalesced load instead of B scattered ones.
+//
+// Work split.  One wavefront runs one task: up to kTaskChunk consecutive
+// entries of one segment (a row for the forward pass and the value gradient,
+// a column for the input gradient).  Lane = (slot s, batch b) with S = 64/ld
+// slots.  A pass first loads 256 of the task's index/value words with
+// coalesced loads (4 per lane), then hands them to the slots with cross-lane
+// reads (v_readlane when S = 1, ds_bpermute otherwise), so all of the pass's
+// operand gathers can be in flight together.  Slots are summed at the end of
+// the task with cross-lane adds; per-entry sums over the batch (value
+// gradient) use DPP row operations.  No MFMA: an unstructured gather is not a
+// dense contraction; the bound is HBM for the COO stream and L1/L2 for the
+// operand gathers.
 #include "common.h"
 
 namespace csp {
@@ -25,13 +32,11 @@ namespace {
 struct F32 {
     using T = float;
     __device__ static float load(const float *p, int64_t i) { return p[i]; }
-    __device__ static float to_f(float v) { return v; }
     __device__ static float from_f(float v) { return v; }
 };
 struct BF16 {
     using T = uint16_t;
     __device__ static float load(const uint16_t *p, int64_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
-    __device__ static float to_f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
     __device__ static uint16_t from_f(float f)  // round to nearest even
     {
         uint32_t u = __float_as_uint(f);
@@ -48,266 +53,624 @@ inline int pow2_ld(int64_t B)
     return ld;
 }
 
+__device__ inline int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int CTRL>
+__device__ inline float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// v from lane (lane xor OFF): DPP for 1 and 2, ds_swizzle (bit-mask mode,
+// within 32 lanes) for 4, 8, 16, ds_bpermute for 32.
+template <int OFF>
+__device__ inline float xor_lane(float v)
+{
+    if constexpr (OFF == 1) return dpp<0xB1>(v);
+    else if constexpr (OFF == 2) return dpp<0x4E>(v);
+    else if constexpr (OFF < 32) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (OFF << 10)));
+    else return __shfl_xor(v, 32, 64);
+}
+
+// Sum over each aligned group of LD lanes; every lane of the group gets it.
+// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes inside a quad, row_half_mirror
+// and row_mirror pair the two halves of 8- and 16-lane groups (all lanes of a
+// half already agree), ds_swizzle xor-16 and a bpermute xor-32 finish.
+template <int LD>
+__device__ inline float group_sum(float v)
+{
+    if constexpr (LD >= 2) v += dpp<0xB1>(v);
+    if constexpr (LD >= 4) v += dpp<0x4E>(v);
+    if constexpr (LD >= 8) v += dpp<0x141>(v);
+    if constexpr (LD >= 16) v += dpp<0x140>(v);
+    if constexpr (LD >= 32) v += xor_lane<16>(v);
+    if constexpr (LD >= 64) v += xor_lane<32>(v);
+    return v;
+}
+
+// Sum over the S slots (lanes b, b+LD, b+2LD, ...): xor exchanges keep lane mod LD.
+template <int LD>
+__device__ inline float slot_sum(float v)
+{
+    if constexpr (LD <= 1) v += xor_lane<1>(v);
+    if constexpr (LD <= 2) v += xor_lane<2>(v);
+    if constexpr (LD <= 4) v += xor_lane<4>(v);
+    if constexpr (LD <= 8) v += xor_lane<8>(v);
+    if constexpr (LD <= 16) v += xor_lane<16>(v);
+    if constexpr (LD <= 32) v += xor_lane<32>(v);
+    return v;
+}
+
 // ------------------------------------------------------- batch-minor copy
-// X [B, n] row-major -> XT[ch][n][ld], zero-padded in the batch dimension.
-template <typename T>
-__global__ __launch_bounds__(256) void k_batch_minor(const T *__restrict__ X, int64_t B, int64_t n, int ld,
-                                                     T *__restrict__ XT)
+// One or two operands [B, n] -> [chunk][n][ld]; reads coalesced, writes
+// scattered (the small writes merge in L2).  The pad slots of the last chunk
+// (batch index >= B) are written as zeros, so consumers never mask them.
+template <typename T, typename I>
+__global__ __launch_bounds__(256) void k_batch_minor(const T *__restrict__ X1, I n1, T *__restrict__ O1,
+                                                     const T *__restrict__ X2, I n2, T *__restrict__ O2, I B,
+                                                     int ld_log2, I pad)
 {
-    __shared__ T tile[64][65];
-    const int t = threadIdx.x;
-    const int64_t c0 = (int64_t)blockIdx.x * 64;
-    const int64_t ch = blockIdx.y;
-    const int tot = ld * 64;
-    for (int e = t; e < tot; e += 256) {
-        int bl = e >> 6, c = e & 63;
-        int64_t b = ch * ld + bl;
-        tile[bl][c] = (b < B && c0 + c < n) ? X[b * n + c0 + c] : T(0);
-    }
-    __syncthreads();
-    for (int e = t; e < tot; e += 256) {
-        int c = e / ld, bl = e % ld;
-        if (c0 + c < n) XT[((ch * n) + c0 + c) * ld + bl] = tile[bl][c];
-    }
-}
-
-// ------------------------------------------------------------- forward
-// One wavefront per output row; 4 rows per 256-thread block.
-template <int LD, typename D>
-__global__ __launch_bounds__(256) void k_fwd_rows(int64_t out, int64_t in, const int32_t *__restrict__ row_ptr,
-                                                  const int32_t *__restrict__ cols,
-                                                  const typename D::T *__restrict__ vals,
-                                                  const typename D::T *__restrict__ XT, int64_t B,
-                                                  typename D::T *__restrict__ Y)
-{
-    constexpr int S = kWave / LD;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= out) return;
-    const int lane = threadIdx.x & 63, s = lane / LD, b = lane % LD;
-    const int64_t ch = blockIdx.y;
-    const typename D::T *xt = XT + ch * in * LD;
-    const int k0 = row_ptr[r], k1 = row_ptr[r + 1];
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int k = k0 + s;
-    for (; k + 3 * S < k1; k += 4 * S) {
-        int c0 = cols[k], c1 = cols[k + S], c2 = cols[k + 2 * S], c3 = cols[k + 3 * S];
-        float v0 = D::load(vals, k), v1 = D::load(vals, k + S), v2 = D::load(vals, k + 2 * S),
-              v3 = D::load(vals, k + 3 * S);
-        a0 += v0 * D::load(xt, (int64_t)c0 * LD + b);
-        a1 += v1 * D::load(xt, (int64_t)c1 * LD + b);
-        a2 += v2 * D::load(xt, (int64_t)c2 * LD + b);
-        a3 += v3 * D::load(xt, (int64_t)c3 * LD + b);
-    }
-    for (; k < k1; k += S) a0 += D::load(vals, k) * D::load(xt, (int64_t)cols[k] * LD + b);
-    float acc = (a0 + a1) + (a2 + a3);
-#pragma unroll
-    for (int off = LD; off < kWave; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    const int64_t bg = ch * LD + b;
-    if (s == 0 && bg < B) Y[bg * out + r] = D::from_f(acc);
-}
-
-// ---------------------------------------------------------- input gradient
-// One wavefront per input column, over the transposed view.
-template <int LD>
-__global__ __launch_bounds__(256) void k_bwd_input_cols(int64_t out, int64_t in, const int32_t *__restrict__ col_ptr,
-                                                        const int32_t *__restrict__ rows_by_col,
-                                                        const int32_t *__restrict__ perm_c,
-                                                        const float *__restrict__ vals,
-                                                        const float *__restrict__ dYT, int64_t B,
-                                                        float *__restrict__ dX)
-{
-    constexpr int S = kWave / LD;
-    const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (c >= in) return;
-    const int lane = threadIdx.x & 63, s = lane / LD, b = lane % LD;
-    const int64_t ch = blockIdx.y;
-    const float *dyt = dYT + ch * out * LD;
-    const int j0 = col_ptr[c], j1 = col_ptr[c + 1];
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-    int j = j0 + s;
-    for (; j + 3 * S < j1; j += 4 * S) {
-        int r0 = rows_by_col[j], r1 = rows_by_col[j + S], r2 = rows_by_col[j + 2 * S], r3 = rows_by_col[j + 3 * S];
-        float v0 = vals[perm_c[j]], v1 = vals[perm_c[j + S]], v2 = vals[perm_c[j + 2 * S]],
-              v3 = vals[perm_c[j + 3 * S]];
-        a0 += v0 * dyt[(int64_t)r0 * LD + b];
-        a1 += v1 * dyt[(int64_t)r1 * LD + b];
-        a2 += v2 * dyt[(int64_t)r2 * LD + b];
-        a3 += v3 * dyt[(int64_t)r3 * LD + b];
-    }
-    for (; j < j1; j += S) a0 += vals[perm_c[j]] * dyt[(int64_t)rows_by_col[j] * LD + b];
-    float acc = (a0 + a1) + (a2 + a3);
-#pragma unroll
-    for (int off = LD; off < kWave; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    const int64_t bg = ch * LD + b;
-    if (s == 0 && bg < B) dX[bg * in + c] = acc;
-}
-
-// ---------------------------------------------------------- value gradient
-// One thread per stored entry: dot product over the batch of two
-// batch-minor rows (dY row of row_k, X row of col_k).
-template <int LD>
-__global__ __launch_bounds__(256) void k_bwd_values(int64_t nnz, int64_t out, int64_t in, int nch,
-                                                    const int32_t *__restrict__ rows,
-                                                    const int32_t *__restrict__ cols, const float *__restrict__ dYT,
-                                                    const float *__restrict__ XT, float *__restrict__ dW)
-{
-    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (k >= nnz) return;
-    const int64_t r = rows[k], c = cols[k];
-    float acc0 = 0.f, acc1 = 0.f;
-    for (int ch = 0; ch < nch; ++ch) {
-        const float *dy = dYT + ((int64_t)ch * out + r) * LD;
-        const float *x = XT + ((int64_t)ch * in + c) * LD;
-        if constexpr (LD >= 4) {
-#pragma unroll
-            for (int b = 0; b < LD; b += 4) {
-                float4 p = *(const float4 *)(dy + b);
-                float4 q = *(const float4 *)(x + b);
-                acc0 += p.x * q.x + p.z * q.z;
-                acc1 += p.y * q.y + p.w * q.w;
-            }
+    const I ld = I(1) << ld_log2;
+    const I tot1 = B * n1, tot = tot1 + B * n2;
+    const I last = (B + pad) / ld - 1;  // chunk holding the pad slots
+    const I all = tot + pad * (n1 + n2);
+    for (I i = (I)blockIdx.x * blockDim.x + threadIdx.x; i < all; i += (I)gridDim.x * blockDim.x) {
+        if (i < tot) {
+            const bool first = i < tot1;
+            const I j = first ? i : i - tot1;
+            const I n = first ? n1 : n2;
+            const I b = j / n, c = j - b * n;
+            const I ch = b >> ld_log2, bl = b & (ld - 1);
+            const I dst = (((ch * n) + c) << ld_log2) + bl;
+            if (first) O1[dst] = X1[j];
+            else O2[dst] = X2[j];
         } else {
-#pragma unroll
-            for (int b = 0; b < LD; ++b) acc0 += dy[b] * x[b];
+            I j = i - tot;
+            const bool first = j < pad * n1;
+            if (!first) j -= pad * n1;
+            const I c = j / pad, k = j - c * pad;
+            const I n = first ? n1 : n2;
+            const I dst = (((last * n) + c) << ld_log2) + (ld - pad + k);
+            if (first) O1[dst] = T(0);
+            else O2[dst] = T(0);
         }
     }
-    dW[k] = acc0 + acc1;
+}
+
+// Lane map.  Each lane owns VW consecutive batch values of an entry (one
+// 16-byte load when VW = 4), LPE = LD/VW lanes cover one entry, and the
+// wave steps through S = 64/LPE entries at a time.  A pass loads 256 of the
+// task's index/value words with coalesced loads (4 per lane) and then walks
+// them in 64-entry blocks of IT = 64/S steps.  Gathers inside one straight
+// run of blocks are all in flight together; an exit test (skip the rest once
+// past the end) splits runs, so tests sit only where a run would otherwise
+// grow past about 16 gathers.  Entries past the end read index word 0 (always valid) and
+// their contribution is zeroed.
+template <int LD>
+struct Map {
+    static constexpr int VW = LD >= 4 ? 4 : LD;
+    static constexpr int LPE = LD / VW;
+    static constexpr int S = kWave / LPE;
+    static constexpr int IT = kWave / S;
+    // Exit test before 64-entry block u: every block when a block holds 16 or
+    // more gathers (S <= 4), only at the half pass when it holds 4 or 8, never
+    // when it holds 2 or fewer.
+    static constexpr bool exit_before(int u) { return S <= 4 ? u > 0 : (S < 32 ? u == 2 : false); }
+};
+
+// Element offset of row c of a batch-minor operand: 32-bit unless the
+// operand chunk holds 2^30 elements or more.
+template <bool kWide>
+__device__ inline auto row_off(int32_t c, int ld)
+{
+    if constexpr (kWide) return (int64_t)c * ld;
+    else return (uint32_t)c * (uint32_t)ld;
+}
+constexpr int kPerLane = 4;
+constexpr int kPass = kWave * kPerLane;
+
+template <int VW>
+__device__ inline void load_vec(const float *__restrict__ p, float (&x)[VW])
+{
+    if constexpr (VW == 4) {
+        const float4 f = *reinterpret_cast<const float4 *>(p);
+        x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+    } else if constexpr (VW == 2) {
+        const float2 f = *reinterpret_cast<const float2 *>(p);
+        x[0] = f.x; x[1] = f.y;
+    } else {
+        x[0] = p[0];
+    }
+}
+template <int VW>
+__device__ inline void load_vec(const uint16_t *__restrict__ p, float (&x)[VW])
+{
+    if constexpr (VW == 4) {
+        const uint2 f = *reinterpret_cast<const uint2 *>(p);
+        x[0] = __uint_as_float(f.x << 16); x[1] = __uint_as_float(f.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(f.y << 16); x[3] = __uint_as_float(f.y & 0xFFFF0000u);
+    } else if constexpr (VW == 2) {
+        const uint32_t f = *reinterpret_cast<const uint32_t *>(p);
+        x[0] = __uint_as_float(f << 16); x[1] = __uint_as_float(f & 0xFFFF0000u);
+    } else {
+        x[0] = __uint_as_float((uint32_t)p[0] << 16);
+    }
+}
+
+// Index word of entry l of a 64-entry block (no exchange needed when S = 64).
+template <int S>
+__device__ inline int32_t entry_i(int32_t v, int l)
+{
+    if constexpr (S == kWave) return v;
+    else return __builtin_amdgcn_ds_bpermute(l << 2, v);
+}
+template <int S>
+__device__ inline float entry_f(float v, int l)
+{
+    return __int_as_float(entry_i<S>(__float_as_int(v), l));
+}
+
+struct Task {
+    int32_t seg, kb, n, slot;
+};
+__device__ inline Task load_task(const int4 *__restrict__ desc, int64_t t)
+{
+    const int4 d = desc[t];
+    return Task{uniform(d.x), uniform(d.y), uniform(d.z) - uniform(d.y), uniform(d.w)};
+}
+
+// ------------------------------------------------- segment sums (fwd, dX)
+// out[b, seg] = sum over the segment's entries e of val(e) * opT[idx[e]][b]
+// where val(e) = vals[e] (forward, row order) or vals[perm[e]] (input
+// gradient, column order).  A split segment's task stores its partial sums
+// instead (slot >= 0); the fixup launch finishes the segment.
+template <int LD, class D, bool kPerm, bool kWide>
+__global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
+                                                      const int32_t *__restrict__ idx,
+                                                      const int32_t *__restrict__ perm,
+                                                      const typename D::T *__restrict__ vals,
+                                                      const typename D::T *__restrict__ opT, int64_t n_op,
+                                                      int64_t n_seg, int64_t B, int nch,
+                                                      float *__restrict__ partial, typename D::T *__restrict__ out)
+{
+    using M = Map<LD>;
+    constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntasks) return;
+    const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
+    const Task T = load_task(desc, t);
+
+    for (int ch = 0; ch < nch; ++ch) {
+        const typename D::T *op = opT + (int64_t)ch * n_op * LD + q * VW;
+        float acc[VW];
+#pragma unroll
+        for (int w = 0; w < VW; ++w) acc[w] = 0.f;
+        for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
+            const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
+            int32_t ci[kPerLane];
+            float vv[kPerLane];
+#pragma unroll
+            for (int u = 0; u < kPerLane; ++u) {
+                const int e = u * kWave + lane;
+                const bool ok = e < m;
+                const int32_t ec = T.kb + p0 + (ok ? e : m - 1);
+                const int32_t c = idx[ec];
+                float v;
+                if constexpr (kPerm) v = D::load(vals, perm[ec]);
+                else v = D::load(vals, ec);
+                ci[u] = ok ? c : 0;
+                vv[u] = ok ? v : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kPerLane; ++u) {
+                if (M::exit_before(u) && u * kWave >= m) break;
+                float x[IT][VW], v[IT];
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const int l = i * S + s;
+                    const int32_t c = entry_i<S>(ci[u], l);
+                    v[i] = entry_f<S>(vv[u], l);
+                    load_vec<VW>(op + row_off<kWide>(c, LD), x[i]);
+                }
+                if ((u + 1) * kWave <= m) {
+#pragma unroll
+                    for (int i = 0; i < IT; ++i)
+#pragma unroll
+                        for (int w = 0; w < VW; ++w) acc[w] += v[i] * x[i][w];
+                } else {  // block holding the end of the task
+#pragma unroll
+                    for (int i = 0; i < IT; ++i) {
+                        const bool ok = u * kWave + i * S + s < m;
+#pragma unroll
+                        for (int w = 0; w < VW; ++w) acc[w] += v[i] * (ok ? x[i][w] : 0.f);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < VW; ++w) acc[w] = slot_sum<LPE>(acc[w]);
+        if (s == 0) {
+#pragma unroll
+            for (int w = 0; w < VW; ++w) {
+                const int64_t b = (int64_t)ch * LD + q * VW + w;
+                if (b >= B) continue;
+                if (T.slot < 0) out[b * n_seg + T.seg] = D::from_f(acc[w]);
+                else partial[((int64_t)T.slot * nch + ch) * LD + q * VW + w] = acc[w];
+            }
+        }
+    }
+}
+
+// Finish split segments: out[b, seg] = sum over the segment's tasks, in task
+// order, of their partial sums.  One thread per (split segment, batch index).
+template <class D>
+__global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ split, int64_t nsplit,
+                                                     const float *__restrict__ partial, int64_t B, int ld, int nch,
+                                                     int64_t n_seg, typename D::T *__restrict__ out)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nsplit * B) return;
+    const int64_t q = i / B, bg = i - q * B;
+    const int4 r = split[q];
+    const int64_t ch = bg / ld, bl = bg - ch * ld;
+    const float *src = partial + ((int64_t)r.y * nch + ch) * ld + bl;
+    const int64_t stride = (int64_t)nch * ld;
+    float tot = 0.f;
+    int32_t p = 0;
+    for (; p + 8 <= r.z; p += 8) {  // eight independent loads in flight, added in task order
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = src[(p + j) * stride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tot += v[j];
+    }
+    for (; p < r.z; ++p) tot += src[p * stride];
+    out[bg * n_seg + r.x] = D::from_f(tot);
+}
+
+// ----------------------------------------------- value gradient, row order
+// dW[e] = sum_b dYT[row][b] * XT[col_e][b] over one row task.  Each entry's
+// batch sum (VW values per lane, then LPE lanes) is staged in LDS -- every
+// lane of the entry's group writes the same value to the same word, so no
+// lane test is needed -- and each 64-entry block leaves as one coalesced row.
+template <int LD, bool kWide>
+__global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ desc, int64_t ntasks,
+                                                     const int32_t *__restrict__ cols, const float *__restrict__ XT,
+                                                     const float *__restrict__ dYT, int64_t in, int64_t out,
+                                                     int64_t B, int nch, float *__restrict__ dW)
+{
+    using M = Map<LD>;
+    constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
+    __shared__ float stage[4][kWave];
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntasks) return;
+    const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
+    float *lds = stage[threadIdx.x >> 6];
+    const Task T = load_task(desc, t);
+    for (int ch = 0; ch < nch; ++ch) {
+        float dy[VW];
+        load_vec<VW>(dYT + ((int64_t)ch * out + T.seg) * LD + q * VW, dy);
+        const float *xt = XT + (int64_t)ch * in * LD + q * VW;
+        for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
+            const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
+            int32_t ci[kPerLane];
+#pragma unroll
+            for (int u = 0; u < kPerLane; ++u) {
+                const int e = u * kWave + lane;
+                const int32_t c = cols[T.kb + p0 + (e < m ? e : m - 1)];
+                ci[u] = e < m ? c : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < kPerLane; ++u) {
+                if (u * kWave >= m) break;
+                float x[IT][VW];
+#pragma unroll
+                for (int i = 0; i < IT; ++i) load_vec<VW>(xt + row_off<kWide>(entry_i<S>(ci[u], i * S + s), LD), x[i]);
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    float p = 0.f;
+#pragma unroll
+                    for (int w = 0; w < VW; ++w) p += dy[w] * x[i][w];
+                    lds[i * S + s] = group_sum<LPE>(p);
+                }
+                const float r = lds[lane];
+                const int32_t e = p0 + u * kWave + lane;
+                if (e < T.n) {
+                    if (ch == 0) dW[T.kb + e] = r;
+                    else dW[T.kb + e] += r;
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------ both gradients, column order
+// For one column task: dX[b, c] = sum_j v_j dYT[r_j][b] and, for each entry,
+// dW[perm_j] = sum_b XT[c][b] dYT[r_j][b]; every gathered dY run feeds both.
+template <int LD, bool kWide>
+__global__ __launch_bounds__(256) void k_bwd_cols(const int4 *__restrict__ desc, int64_t ntasks,
+                                                  const int32_t *__restrict__ rows_by_col,
+                                                  const int32_t *__restrict__ perm_c, const float *__restrict__ vals,
+                                                  const float *__restrict__ XT, const float *__restrict__ dYT,
+                                                  int64_t in, int64_t out, int64_t B, int nch,
+                                                  float *__restrict__ partial, float *__restrict__ dX,
+                                                  float *__restrict__ dW)
+{
+    using M = Map<LD>;
+    constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
+    __shared__ float stage[4][kWave];
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntasks) return;
+    const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
+    float *lds = stage[threadIdx.x >> 6];
+    const Task T = load_task(desc, t);
+    for (int ch = 0; ch < nch; ++ch) {
+        float xc[VW];
+        load_vec<VW>(XT + ((int64_t)ch * in + T.seg) * LD + q * VW, xc);
+        const float *dyt = dYT + (int64_t)ch * out * LD + q * VW;
+        float acc[VW];
+#pragma unroll
+        for (int w = 0; w < VW; ++w) acc[w] = 0.f;
+        for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
+            const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
+            int32_t ri[kPerLane], pk[kPerLane];
+            float vv[kPerLane];
+#pragma unroll
+            for (int u = 0; u < kPerLane; ++u) {
+                const int e = u * kWave + lane;
+                const bool ok = e < m;
+                const int32_t ec = T.kb + p0 + (ok ? e : m - 1);
+                const int32_t r = rows_by_col[ec];
+                pk[u] = perm_c[ec];
+                const float v = vals[pk[u]];
+                ri[u] = ok ? r : 0;
+                vv[u] = ok ? v : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kPerLane; ++u) {
+                if (u * kWave >= m) break;
+                float y[IT][VW], v[IT];
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    const int l = i * S + s;
+                    const int32_t r = entry_i<S>(ri[u], l);
+                    v[i] = entry_f<S>(vv[u], l);
+                    load_vec<VW>(dyt + row_off<kWide>(r, LD), y[i]);
+                }
+                if ((u + 1) * kWave > m) {  // block holding the end of the task
+#pragma unroll
+                    for (int i = 0; i < IT; ++i) {
+                        const bool ok = u * kWave + i * S + s < m;
+#pragma unroll
+                        for (int w = 0; w < VW; ++w) y[i][w] = ok ? y[i][w] : 0.f;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < IT; ++i) {
+                    float p = 0.f;
+#pragma unroll
+                    for (int w = 0; w < VW; ++w) {
+                        acc[w] += v[i] * y[i][w];
+                        p += xc[w] * y[i][w];
+                    }
+                    lds[i * S + s] = group_sum<LPE>(p);
+                }
+                const float r = lds[lane];
+                if (u * kWave + lane < m) {
+                    if (ch == 0) dW[pk[u]] = r;
+                    else dW[pk[u]] += r;
+                }
+            }
+        }
+#pragma unroll
+        for (int w = 0; w < VW; ++w) acc[w] = slot_sum<LPE>(acc[w]);
+        if (s == 0) {
+#pragma unroll
+            for (int w = 0; w < VW; ++w) {
+                const int64_t b = (int64_t)ch * LD + q * VW + w;
+                if (b >= B) continue;
+                if (T.slot < 0) dX[b * in + T.seg] = acc[w];
+                else partial[((int64_t)T.slot * nch + ch) * LD + q * VW + w] = acc[w];
+            }
+        }
+    }
 }
 
 // ------------------------------------------------------------ host side
-csp_status ensure_act(csp_layer *L, size_t bytes)
-{
-    if (L->act.bytes >= bytes) return CSP_OK;
-    if (L->act.a) CSP_HIP(hipFree(L->act.a));
-    if (L->act.b) CSP_HIP(hipFree(L->act.b));
-    L->act.a = L->act.b = nullptr;
-    L->act.bytes = 0;
-    if (hipMalloc(&L->act.a, bytes) != hipSuccess || hipMalloc(&L->act.b, bytes) != hipSuccess) {
-        (void)hipGetLastError();
-        if (L->act.a) (void)hipFree(L->act.a);
-        L->act.a = nullptr;
-        return set_error(CSP_ERR_NO_MEMORY, "cannot allocate %zu bytes of operand workspace", bytes);
-    }
-    L->act.bytes = bytes;
-    return CSP_OK;
-}
-
-// Copy a [B, n] operand to batch-minor layout; returns the pointer to use.
-csp_status batch_minor(csp_layer *L, const void *X, int64_t B, int64_t n, void *dst, const void **xt,
-                       hipStream_t s)
-{
-    if (B == 1) {  // [1, n] is already batch-minor
-        *xt = X;
-        return CSP_OK;
-    }
-    const int ld = pow2_ld(B);
-    const int64_t nch = ceil_div(B, ld);
-    dim3 grid((unsigned)ceil_div(n, 64), (unsigned)nch);
-    if (L->esz == 4)
-        k_batch_minor<float><<<grid, 256, 0, s>>>((const float *)X, B, n, ld, (float *)dst);
-    else
-        k_batch_minor<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)X, B, n, ld, (uint16_t *)dst);
-    CSP_LAUNCHED("k_batch_minor");
-    *xt = dst;
-    return CSP_OK;
-}
-
 size_t batch_minor_bytes(const csp_layer *L, int64_t B, int64_t n)
 {
     const int ld = pow2_ld(B);
     return (size_t)ceil_div(B, ld) * (size_t)n * (size_t)ld * (size_t)L->esz;
 }
 
-template <typename D>
+csp_status ensure_act(csp_layer *L, int64_t B)
+{
+    const int ld = pow2_ld(B);
+    const int64_t nch = ceil_div(B, ld);
+    const size_t bytes = batch_minor_bytes(L, B, L->in > L->out ? L->in : L->out);
+    const int64_t tcap = L->row_tasks.cap > L->col_tasks.cap ? L->row_tasks.cap : L->col_tasks.cap;
+    const size_t pbytes = (size_t)tcap * (size_t)nch * (size_t)ld * sizeof(float);
+    if (L->act.bytes < bytes) {
+        if (L->act.a) CSP_HIP(hipFree(L->act.a));
+        if (L->act.b) CSP_HIP(hipFree(L->act.b));
+        L->act.a = L->act.b = nullptr;
+        L->act.bytes = 0;
+        if (hipMalloc(&L->act.a, bytes) != hipSuccess || hipMalloc(&L->act.b, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return set_error(CSP_ERR_NO_MEMORY, "cannot allocate %zu bytes of operand workspace", bytes);
+        }
+        L->act.bytes = bytes;
+    }
+    if (L->act.partial_bytes < pbytes) {
+        if (L->act.partial) CSP_HIP(hipFree(L->act.partial));
+        L->act.partial = nullptr;
+        L->act.partial_bytes = 0;
+        if (hipMalloc(&L->act.partial, pbytes) != hipSuccess) {
+            (void)hipGetLastError();
+            return set_error(CSP_ERR_NO_MEMORY, "cannot allocate %zu bytes of partial sums", pbytes);
+        }
+        L->act.partial_bytes = pbytes;
+    }
+    return CSP_OK;
+}
+
+// Batch-minor copies of up to two operands (B == 1 needs none: [1, n] already is).
+csp_status batch_minor(csp_layer *L, int64_t B, const void *X1, int64_t n1, void *O1, const void *X2, int64_t n2,
+                       void *O2, hipStream_t s)
+{
+    if (B == 1) return CSP_OK;
+    const int ld = pow2_ld(B);
+    int ld_log2 = 0;
+    while ((1 << ld_log2) < ld) ++ld_log2;
+    if (!X2) n2 = 0;
+    const int64_t tot = B * (n1 + n2) + (ceil_div(B, ld) * ld - B) * (n1 + n2);
+    int64_t blocks = ceil_div(tot, 256);
+    if (blocks > 8192) blocks = 8192;
+    const int64_t pad = ceil_div(B, ld) * ld - B;
+    const bool small = tot + pad * (n1 + n2) < (int64_t(1) << 31);
+#define CSP_BM(T, I)                                                                                           \
+    k_batch_minor<T, I><<<(unsigned)blocks, 256, 0, s>>>((const T *)X1, (I)n1, (T *)O1, (const T *)X2, (I)n2, \
+                                                         (T *)O2, (I)B, ld_log2, (I)pad)
+    if (L->esz == 4) {
+        if (small) CSP_BM(float, int32_t); else CSP_BM(float, int64_t);
+    } else {
+        if (small) CSP_BM(uint16_t, int32_t); else CSP_BM(uint16_t, int64_t);
+    }
+#undef CSP_BM
+    CSP_LAUNCHED("k_batch_minor");
+    return CSP_OK;
+}
+
+#define CSP_LD_SWITCH_W(ld, MACRO, W) \
+    switch (ld) {                     \
+    case 1: MACRO(1, W); break;       \
+    case 2: MACRO(2, W); break;       \
+    case 4: MACRO(4, W); break;       \
+    case 8: MACRO(8, W); break;       \
+    case 16: MACRO(16, W); break;     \
+    case 32: MACRO(32, W); break;     \
+    default: MACRO(64, W); break;     \
+    }
+#define CSP_LD_SWITCH(ld, wide, MACRO)           \
+    do {                                         \
+        if (wide) CSP_LD_SWITCH_W(ld, MACRO, true) \
+        else CSP_LD_SWITCH_W(ld, MACRO, false)     \
+    } while (0)
+
+// Operands whose chunk holds 2^30 or more elements need 64-bit offsets.
+inline bool wide_operand(int64_t n, int ld) { return n * (int64_t)ld >= (int64_t(1) << 30); }
+
+template <class D>
+csp_status split_fixup(csp_layer *L, const TaskList &TL, int64_t B, int64_t n_seg, void *out, hipStream_t s)
+{
+    if (TL.nsplit == 0) return CSP_OK;
+    const int ld = pow2_ld(B);
+    const int nch = (int)ceil_div(B, ld);
+    k_split_fixup<D><<<(unsigned)ceil_div(TL.nsplit * B, 256), 256, 0, s>>>(TL.split, TL.nsplit, L->act.partial, B, ld,
+                                                                          nch, n_seg, (typename D::T *)out);
+    CSP_LAUNCHED("k_split_fixup");
+    return CSP_OK;
+}
+
+template <class D>
 csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    dim3 grid((unsigned)ceil_div(L->out, 4), (unsigned)ceil_div(B, ld));
-    const T *v = (const T *)L->vals;
-    const T *x = (const T *)XT;
-    T *y = (T *)Y;
-    switch (ld) {
-    case 1: k_fwd_rows<1, D><<<grid, 256, 0, s>>>(L->out, L->in, L->row_ptr, L->cols, v, x, B, y); break;
-    case 2: k_fwd_rows<2, D><<<grid, 256, 0, s>>>(L->out, L->in, L->row_ptr, L->cols, v, x, B, y); break;
-    case 4: k_fwd_rows<4, D><<<grid, 256, 0, s>>>(L->out, L->in, L->row_ptr, L->cols, v, x, B, y); break;
-    case 8: k_fwd_rows<8, D><<<grid, 256, 0, s>>>(L->out, L->in, L->row_ptr, L->cols, v, x, B, y); break;
-    case 16: k_fwd_rows<16, D><<<grid, 256, 0, s>>>(L->out, L->in, L->row_ptr, L->cols, v, x, B, y); break;
-    case 32: k_fwd_rows<32, D><<<grid, 256, 0, s>>>(L->out, L->in, L->row_ptr, L->cols, v, x, B, y); break;
-    default: k_fwd_rows<64, D><<<grid, 256, 0, s>>>(L->out, L->in, L->row_ptr, L->cols, v, x, B, y); break;
-    }
-    CSP_LAUNCHED("k_fwd_rows");
-    return CSP_OK;
+    const int nch = (int)ceil_div(B, ld);
+    const TaskList &TL = L->row_tasks;
+    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    timing_mark(L, true, s);
+#define CSP_FWD(LDV, W)                                                                                     \
+    k_segment_spmm<LDV, D, false, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, nullptr,                 \
+                                                       (const T *)L->vals, (const T *)XT, L->in, L->out, B, \
+                                                       nch, L->act.partial, (T *)Y)
+    CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_FWD);
+#undef CSP_FWD
+    CSP_LAUNCHED("k_segment_spmm (forward)");
+    timing_mark(L, false, s);
+    return split_fixup<D>(L, TL, B, L->out, Y, s);
 }
 
 }  // namespace
 
 csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, hipStream_t s)
 {
-    csp_status st = ensure_act(L, batch_minor_bytes(L, B, L->in));
+    csp_status st = ensure_act(L, B);
     if (st != CSP_OK) return st;
-    const void *xt = nullptr;
-    st = batch_minor(L, X, B, L->in, L->act.a, &xt, s);
+    st = batch_minor(L, B, X, L->in, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
+    const void *xt = B == 1 ? X : L->act.a;
     return L->dtype == CSP_BF16 ? fwd_dispatch<BF16>(L, xt, B, Y, s) : fwd_dispatch<F32>(L, xt, B, Y, s);
 }
 
 csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, hipStream_t s)
 {
-    csp_status st = ensure_act(L, batch_minor_bytes(L, B, L->out));
+    csp_status st = ensure_act(L, B);
     if (st != CSP_OK) return st;
-    const void *dyt = nullptr;
-    st = batch_minor(L, dY, B, L->out, L->act.a, &dyt, s);
+    st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
+    const float *dyt = (const float *)(B == 1 ? dY : L->act.a);
     const int ld = pow2_ld(B);
-    dim3 grid((unsigned)ceil_div(L->in, 4), (unsigned)ceil_div(B, ld));
-    const float *v = (const float *)L->vals, *g = (const float *)dyt;
-    float *o = (float *)dX;
-#define CSP_BWD_IN(LDV)                                                                                      \
-    k_bwd_input_cols<LDV><<<grid, 256, 0, s>>>(L->out, L->in, L->col_ptr, L->rows_by_col, L->perm_c, v, g, B, o)
-    switch (ld) {
-    case 1: CSP_BWD_IN(1); break;
-    case 2: CSP_BWD_IN(2); break;
-    case 4: CSP_BWD_IN(4); break;
-    case 8: CSP_BWD_IN(8); break;
-    case 16: CSP_BWD_IN(16); break;
-    case 32: CSP_BWD_IN(32); break;
-    default: CSP_BWD_IN(64); break;
-    }
-#undef CSP_BWD_IN
-    CSP_LAUNCHED("k_bwd_input_cols");
-    return CSP_OK;
+    const int nch = (int)ceil_div(B, ld);
+    const TaskList &TL = L->col_tasks;
+    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    timing_mark(L, true, s);
+#define CSP_DX(LDV, W)                                                                                          \
+    k_segment_spmm<LDV, F32, true, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, L->perm_c,           \
+                                                        (const float *)L->vals, dyt, L->out, L->in, B, nch,     \
+                                                        L->act.partial, (float *)dX)
+    CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_DX);
+#undef CSP_DX
+    CSP_LAUNCHED("k_segment_spmm (input gradient)");
+    timing_mark(L, false, s);
+    return split_fixup<F32>(L, TL, B, L->in, dX, s);
 }
 
 csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s)
 {
     if (L->nnz == 0) return CSP_OK;
-    size_t need = batch_minor_bytes(L, B, L->in > L->out ? L->in : L->out);
-    csp_status st = ensure_act(L, need);
+    csp_status st = ensure_act(L, B);
     if (st != CSP_OK) return st;
-    const void *xt = nullptr, *dyt = nullptr;
-    st = batch_minor(L, X, B, L->in, L->act.a, &xt, s);
+    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
     if (st != CSP_OK) return st;
-    st = batch_minor(L, dY, B, L->out, L->act.b, &dyt, s);
-    if (st != CSP_OK) return st;
+    const float *xt = (const float *)(B == 1 ? X : L->act.a);
+    const float *dyt = (const float *)(B == 1 ? dY : L->act.b);
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
-    const unsigned grid = (unsigned)ceil_div(L->nnz, 256);
-    const float *g = (const float *)dyt, *x = (const float *)xt;
-#define CSP_BWD_V(LDV) \
-    k_bwd_values<LDV><<<grid, 256, 0, s>>>(L->nnz, L->out, L->in, nch, L->rows, L->cols, g, x, dW)
-    switch (ld) {
-    case 1: CSP_BWD_V(1); break;
-    case 2: CSP_BWD_V(2); break;
-    case 4: CSP_BWD_V(4); break;
-    case 8: CSP_BWD_V(8); break;
-    case 16: CSP_BWD_V(16); break;
-    case 32: CSP_BWD_V(32); break;
-    default: CSP_BWD_V(64); break;
-    }
-#undef CSP_BWD_V
-    CSP_LAUNCHED("k_bwd_values");
+    const TaskList &TL = L->row_tasks;
+    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    timing_mark(L, true, s);
+#define CSP_DW(LDV, W) \
+    k_values_rows<LDV, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, xt, dyt, L->in, L->out, B, nch, dW)
+    CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_DW);
+#undef CSP_DW
+    CSP_LAUNCHED("k_values_rows");
+    timing_mark(L, false, s);
     return CSP_OK;
+}
+
+csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, hipStream_t s)
+{
+    csp_status st = ensure_act(L, B);
+    if (st != CSP_OK) return st;
+    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
+    if (st != CSP_OK) return st;
+    const float *xt = (const float *)(B == 1 ? X : L->act.a);
+    const float *dyt = (const float *)(B == 1 ? dY : L->act.b);
+    const int ld = pow2_ld(B);
+    const int nch = (int)ceil_div(B, ld);
+    const TaskList &TL = L->col_tasks;
+    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    timing_mark(L, true, s);
+#define CSP_BWD(LDV, W)                                                                                       \
+    k_bwd_cols<LDV, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, L->perm_c, (const float *)L->vals, \
+                                         xt, dyt, L->in, L->out, B, nch, L->act.partial, (float *)dX, dW)
+    CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_BWD);
+#undef CSP_BWD
+    CSP_LAUNCHED("k_bwd_cols");
+    timing_mark(L, false, s);
+    return split_fixup<F32>(L, TL, B, L->in, dX, s);
 }
 
 }  // namespace csp

@@ -101,6 +101,15 @@ csp_status spmm_bwd_values(sparse_layer_t layer, const void *dY, const void *X, 
                            void *stream);
 
 /*
+ * spmm_bwd -- both gradients of one backward step in a single pass over the
+ * transposed view: dX as in spmm_bwd_input and dW as in spmm_bwd_values, with
+ * each gathered dY row used for both.  Same layouts and results (within the
+ * fp32 tolerance of each) as the two separate calls; fp32 layers only.
+ */
+csp_status spmm_bwd(sparse_layer_t layer, const void *dY, const void *X, int64_t B, void *dX, float *dW,
+                    void *stream);
+
+/*
  * restructure -- one prune-and-regrow step of dynamic sparse training
  * (Abstract: an API for restructuring connections).  The rule:
  *  1. prune the n_prune stored entries with the smallest |v|, ordered by the
@@ -159,6 +168,16 @@ void *sparse_layer_values(sparse_layer_t layer);
  * optimizer step kept outside the library.  Structure is unchanged.
  */
 csp_status sparse_layer_set_values(sparse_layer_t layer, const void *vals, void *stream);
+
+/*
+ * sparse_layer_time_next -- profiling aid: the next product call on this
+ * layer (spmm_fwd, spmm_bwd_input, spmm_bwd_values or spmm_bwd) records
+ * ev_before on its stream immediately before launching its main kernel and
+ * ev_after immediately after, then forgets the request.  The events are
+ * caller-owned hipEvent_t handles passed as void*.  Operand copies and other
+ * helper kernels of the call fall outside the bracket.
+ */
+csp_status sparse_layer_time_next(sparse_layer_t layer, void *ev_before, void *ev_after);
 
 /* Text of the calling thread's last error ("" if none). */
 const char *sparse_layer_last_error(void);

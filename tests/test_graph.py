@@ -1,0 +1,49 @@
+"""The product calls can be captured in a HIP graph: every replay equals the eager result bit for bit.
+
+Replays are interleaved with the program's own eager work and synchronizations.
+"""
+import pytest
+import torch
+
+from coo_spmm_fwd_amd import binding as csp
+from coo_spmm_fwd_amd import workloads as W
+from tests.gpu_util import dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("B", [1, 16, 64])
+def test_graph_replay_matches_eager(B):
+    L = W.random_layer(2000, 1500, 120000, seed=31 + B)
+    h = csp.sparse_layer_create(L.out, L.in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        X = dev(W.random_dense((B, L.in_), 1))
+        dY = dev(W.random_dense((B, L.out), 2))
+        Y_ref = csp.spmm_fwd(h, X)
+        dX_ref, dW_ref = csp.spmm_bwd(h, dY, X)
+        torch.cuda.synchronize()
+        Y = torch.full_like(Y_ref, float("nan"))
+        dX = torch.full_like(dX_ref, float("nan"))
+        dW = torch.full_like(dW_ref, float("nan"))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = torch.cuda.current_stream()
+            csp.spmm_fwd(h, X, Y, stream=s)
+            csp.spmm_bwd(h, dY, X, dX, dW, stream=s)
+        for rep in range(4):
+            Y.fill_(float("nan"))
+            dX.fill_(float("nan"))
+            dW.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Y, Y_ref), rep
+            assert torch.equal(dX, dX_ref), rep
+            assert torch.equal(dW, dW_ref), rep
+            # eager work between replays, on other buffers
+            csp.spmm_fwd(h, dev(W.random_dense((B, L.in_), 10 + rep)))
+            torch.cuda.synchronize()
+        del g
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h)

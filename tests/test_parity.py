@@ -45,7 +45,7 @@ def check_canonical(layer: Layer):
     assert np.array_equal(col_ptr, c["col_ptr"])
 
 
-def check_ops(orc, layer: Layer, B: int, seed: int, rel=FP32_REL, ops=("fwd", "dX", "dW"), integer=False):
+def check_ops(orc, layer: Layer, B: int, seed: int, rel=FP32_REL, ops=("fwd", "dX", "dW", "bwd"), integer=False):
     L = layer.L
     X = W.random_dense((B, L.in_), seed, dtype=L.dtype, integer=integer)
     dY = W.random_dense((B, L.out), seed + 1, dtype=L.dtype, integer=integer)
@@ -68,6 +68,15 @@ def check_ops(orc, layer: Layer, B: int, seed: int, rel=FP32_REL, ops=("fwd", "d
         if integer:
             assert np.array_equal(dW.astype(np.float64), ref)
         assert_within(dW, ref, S, rel, f"dW B={B}")
+    if "bwd" in ops:
+        dX, dW = (host(t) for t in csp.spmm_bwd(layer.h, dev(dY), dev(X)))
+        ref, S = orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dY)
+        assert_within(dX, ref, S, rel, f"fused dX B={B}")
+        c = layer.canon
+        ref, S = orc.spmm_bwd_values(L.out, L.in_, c["rows"], c["cols"], dY, X)
+        if integer:
+            assert np.array_equal(dW.astype(np.float64), ref)
+        assert_within(dW, ref, S, rel, f"fused dW B={B}")
 
 
 # ------------------------------------------------------------------ small and ragged
@@ -141,6 +150,9 @@ def test_bf16_forward(orc):
         with pytest.raises(csp.CspError) as e:
             csp.spmm_bwd_values(layer.h, dev(W.random_dense((4, 900), 2, dtype="bf16")), X)
         assert e.value.status == -6
+        with pytest.raises(csp.CspError) as e:
+            csp.spmm_bwd(layer.h, dev(W.random_dense((4, 900), 2, dtype="bf16")), X)
+        assert e.value.status == -6
     finally:
         layer.close()
 
@@ -213,8 +225,11 @@ def test_full_size_linear(orc, name):
             ref, S = orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dY)
             assert_within(dX, ref, S, FP32_REL, f"{name} dX")
             dW = host(csp.spmm_bwd_values(layer.h, dev(dY), dev(X)))
-            ref, S = orc.spmm_bwd_values(L.out, L.in_, layer.canon["rows"], layer.canon["cols"], dY, X)
-            assert_within(dW, ref, S, FP32_REL, f"{name} dW")
+            refw, Sw = orc.spmm_bwd_values(L.out, L.in_, layer.canon["rows"], layer.canon["cols"], dY, X)
+            assert_within(dW, refw, Sw, FP32_REL, f"{name} dW")
+            dX2, dW2 = (host(t) for t in csp.spmm_bwd(layer.h, dev(dY), dev(X)))
+            assert_within(dX2, ref, S, FP32_REL, f"{name} fused dX")
+            assert_within(dW2, refw, Sw, FP32_REL, f"{name} fused dW")
     finally:
         layer.close()
 
