@@ -77,6 +77,75 @@ def traffic_for(kernel: str, launch_args: dict):
     return e.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------ HBM counters
+COPY_KERNEL_KEY = "copyBuffer"   # the runtime's device-to-device copy kernel (torch copy_ of a tensor)
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter, match):
+    """Average counter value (KiB) per dispatch of kernels whose name satisfies match()."""
+    per = {}
+    for r in rows:
+        name = r.get("Kernel_Name", "").replace("csp::(anonymous namespace)::", "")
+        if r.get("Counter_Name") != counter or not match(name):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        return None, 0
+    return sum(per.values()) / len(per), len(per)
+
+
+def ingest_counters(fetch_dir, write_dir, workload, batch, copy_mib=256):
+    """Scale each counter by what it reads for a plain copy of known size, then store bytes per launch."""
+    from coo_spmm_fwd_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    B = batch or w.batches[0]
+    ld = 1
+    while ld < min(B, 64):
+        ld *= 2
+    fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    copy_bytes = copy_mib << 20
+    # the calibration copy is the only copy dispatch of that size (grid of copy_bytes / 2048 work-items)
+    big = [r for r in fetch + write if COPY_KERNEL_KEY in r.get("Kernel_Name", "")]
+    gmax = max((int(r["Grid_Size"]) for r in big), default=0)
+    is_copy = lambda n: COPY_KERNEL_KEY in n
+    fetch_c = [r for r in fetch if is_copy(r.get("Kernel_Name", "")) and int(r["Grid_Size"]) == gmax]
+    write_c = [r for r in write if is_copy(r.get("Kernel_Name", "")) and int(r["Grid_Size"]) == gmax]
+    cf, _ = _per_dispatch(fetch_c, "FETCH_SIZE", lambda n: True)
+    cw, _ = _per_dispatch(write_c, "WRITE_SIZE", lambda n: True)
+    f_scale = copy_bytes / (cf * 1024) if cf else None
+    w_scale = copy_bytes / (cw * 1024) if cw else None
+    rec = {}
+    for name in (f"k_bwd_cols<{ld}, false>", f"k_segment_spmm<{ld}, F32, false, false>"):
+        m = lambda n, name=name: name in n
+        kf, nf = _per_dispatch(fetch, "FETCH_SIZE", m)
+        kw, nw = _per_dispatch(write, "WRITE_SIZE", m)
+        if kf is None or kw is None or f_scale is None or w_scale is None:
+            continue
+        fb, wb = kf * 1024 * f_scale, kw * 1024 * w_scale
+        rec[name] = {"source_sha": source_sha(), "args": {"workload": workload, "batch": B},
+                     "fetch_kib_raw": kf, "write_kib_raw": kw, "dispatches": [nf, nw],
+                     "copy_scale": {"fetch": f_scale, "write": w_scale, "copy_bytes": copy_bytes},
+                     "hbm_bytes_per_launch": round(fb + wb)}
+    os.makedirs(os.path.dirname(PROFILE_TRAFFIC), exist_ok=True)
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec, indent=1))
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(w, L, acts, B, budget_s=12.0):
     """The oracle as written (fp64 loops, one core) on the same step: forward, dX, dW."""
@@ -113,7 +182,14 @@ def main():
     ap.add_argument("--warm", action="store_true", help="reuse one replica (cache-resident data)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--eager", action="store_true", help="launch each call from Python instead of graph replay")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_counters.json")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters, workload=args.workload, batch=args.batch)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(each MI355X runs its own layer; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
@@ -233,6 +309,15 @@ def main():
     r0 = time.perf_counter()
     csp.restructure(handles[0], n_prune, seed=w.seed, step=1)
     restructure_ms = (time.perf_counter() - r0) * 1e3
+
+    if args.calibrate_copy:
+        n = (args.calibrate_copy << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     del graphs
     torch.cuda.synchronize()
