@@ -53,10 +53,11 @@ def bytes_dw(nnz, out, in_, B):
     return nnz * (4 + 4) + 4 * (out + 1) + 4 * B * (in_ + out)
 
 
-def bytes_bwd_fused(nnz, out, in_, B):
-    """Both gradients in one column-order pass: row index, permutation, gathered value,
-    dW write per entry; column offsets; X and dY read once; dX written once."""
-    return nnz * 16 + 4 * (in_ + 1) + 4 * B * (2 * in_ + out)
+def bytes_gradients(nnz, out, in_, B):
+    """Both gradients in one launch: input gradient over the transposed view (row index and
+    column-ordered value per entry) and value gradient over rows (column index read, dW written
+    per entry); both offset arrays; X and dY read once; dX written once."""
+    return nnz * 16 + 4 * (in_ + 1) + 4 * (out + 1) + 4 * B * (2 * in_ + out)
 
 
 def source_sha() -> str:
@@ -129,7 +130,7 @@ def ingest_counters(fetch_dir, write_dir, workload, batch, copy_mib=256):
     f_scale = copy_bytes / (cf * 1024) if cf else None
     w_scale = copy_bytes / (cw * 1024) if cw else None
     rec = {}
-    for name in (f"k_bwd_cols<{ld}, false>", f"k_segment_spmm<{ld}, F32, false, false>"):
+    for name in (f"k_gradients<{ld}, false>", f"k_segment_spmm<{ld}, F32, false>"):
         m = lambda n, name=name: name in n
         kf, nf = _per_dispatch(fetch, "FETCH_SIZE", m)
         kw, nw = _per_dispatch(write, "WRITE_SIZE", m)
@@ -216,7 +217,7 @@ def main():
     nnz, out, in_ = L.nnz, L.out, L.in_
 
     b_fwd, b_dx, b_dw = bytes_fwd(nnz, out, in_, B), bytes_dx(nnz, out, in_, B), bytes_dw(nnz, out, in_, B)
-    b_bwd = bytes_bwd_fused(nnz, out, in_, B)
+    b_bwd = bytes_gradients(nnz, out, in_, B)
     step_bytes = b_fwd + b_dx + b_dw
     # bytes one step touches in one replica: structure of both orders, values, dW, dense operands
     touched = nnz * (4 * 5 + 4) + 4 * B * (3 * in_ + 2 * out)
@@ -295,8 +296,8 @@ def main():
     while ld < min(B, 64):
         ld *= 2
     kernels = {
-        "forward": {"name": f"k_segment_spmm<{ld}, F32, false, false>", "us": fwd_k * 1e3, "bytes": b_fwd},
-        "backward": {"name": f"k_bwd_cols<{ld}, false>", "us": bwd_k * 1e3, "bytes": b_bwd},
+        "forward": {"name": f"k_segment_spmm<{ld}, F32, false>", "us": fwd_k * 1e3, "bytes": b_fwd},
+        "backward": {"name": f"k_gradients<{ld}, false>", "us": bwd_k * 1e3, "bytes": b_bwd},
     }
     dom_key = max(kernels, key=lambda k: kernels[k]["us"])
     dom = kernels[dom_key]

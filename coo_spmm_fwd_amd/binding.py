@@ -252,11 +252,33 @@ def sparse_layer_values(layer: int) -> int:
 
 
 def sparse_layer_set_values(layer: int, vals, stream=None):
-    """Overwrite the canonical values with the device tensor vals[nnz] (layer dtype)."""
+    """Overwrite the canonical values with the device tensor vals[nnz] (layer dtype) and refresh
+    the column-ordered copy; vals=None only refreshes the copy after in-place updates."""
     _, _, dt = sparse_layer_shape(layer)
     nnz = sparse_layer_nnz(layer)
-    vp = _dev(vals, "vals", _torch_dtype(dt), (nnz,))
+    vp = None if vals is None else _dev(vals, "vals", _torch_dtype(dt), (nnz,))
     _check(load().sparse_layer_set_values(c_void_p(layer), vp, _stream(stream)))
+
+
+class _DeviceArray:
+    """Minimal __cuda_array_interface__ holder for a library-owned device array."""
+
+    def __init__(self, ptr: int, n: int, typestr: str):
+        self.__cuda_array_interface__ = {"shape": (n,), "typestr": typestr, "data": (ptr, False),
+                                         "strides": None, "version": 2}
+
+
+def sparse_layer_values_tensor(layer: int):
+    """Zero-copy torch view of the layer's canonical values (valid until the layer is destroyed).
+    After writing into it, call sparse_layer_set_values(layer, None)."""
+    torch = _torch()
+    _, _, dt = sparse_layer_shape(layer)
+    nnz = sparse_layer_nnz(layer)
+    ptr = sparse_layer_values(layer)
+    if nnz == 0:
+        return torch.empty(0, dtype=_torch_dtype(dt), device="cuda")
+    t = torch.as_tensor(_DeviceArray(ptr, nnz, "<u2" if dt == CSP_BF16 else "<f4"), device="cuda")
+    return t.view(torch.bfloat16) if dt == CSP_BF16 else t
 
 
 def sparse_layer_time_next(layer: int, ev_before, ev_after):

@@ -55,6 +55,14 @@ __global__ void k_rows_by_col(const int32_t *__restrict__ rows, const int32_t *_
     if (j < nnz) rows_by_col[j] = rows[perm[j]];
 }
 
+template <typename V>
+__global__ void k_gather_vals(const V *__restrict__ vals, const int32_t *__restrict__ perm, int64_t n,
+                              V *__restrict__ out)
+{
+    int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j < n) out[j] = vals[perm[j]];
+}
+
 // Tasks per segment: one for a segment of at most kTaskChunk entries (also
 // for an empty one, which still owns its zero output), else one per chunk.
 __global__ void k_seg_pieces(const int32_t *__restrict__ ptr, int64_t nseg, uint32_t *__restrict__ pieces)
@@ -101,6 +109,20 @@ csp_status build_tasks(TaskList &T, const int32_t *ptr, int64_t nseg, uint32_t *
 
 }  // namespace
 
+csp_status refresh_column_values(csp_layer *L, hipStream_t s)
+{
+    if (L->nnz == 0) return CSP_OK;
+    const unsigned grid = (unsigned)ceil_div(L->nnz, 256);
+    if (L->esz == 4)
+        k_gather_vals<uint32_t><<<grid, 256, 0, s>>>((const uint32_t *)L->vals, L->perm_c, L->nnz,
+                                                     (uint32_t *)L->vals_c);
+    else
+        k_gather_vals<uint16_t><<<grid, 256, 0, s>>>((const uint16_t *)L->vals, L->perm_c, L->nnz,
+                                                     (uint16_t *)L->vals_c);
+    CSP_LAUNCHED("k_gather_vals");
+    return CSP_OK;
+}
+
 csp_status build_index(csp_layer *L, hipStream_t s)
 {
     const int64_t nnz = L->nnz;
@@ -115,6 +137,8 @@ csp_status build_index(csp_layer *L, hipStream_t s)
         if (st != CSP_OK) return st;
         k_rows_by_col<<<grid, 256, 0, s>>>(L->rows, L->perm_c, nnz, L->rows_by_col);
         CSP_LAUNCHED("k_rows_by_col");
+        st = refresh_column_values(L, s);
+        if (st != CSP_OK) return st;
     }
     st = segment_offsets((const int32_t *)L->ws.key_a, nnz, L->col_ptr, L->in, s);
     if (st != CSP_OK) return st;

@@ -73,6 +73,7 @@ struct csp_layer {
     void *vals = nullptr;
     int32_t *row_ptr = nullptr;
     int32_t *perm_c = nullptr, *rows_by_col = nullptr, *col_ptr = nullptr;
+    void *vals_c = nullptr;  // values in transposed (col, row) order: vals_c[j] = vals[perm_c[j]]
     csp::TaskList row_tasks, col_tasks;
     csp::Workspace ws;
     csp::ActBuffer act;
@@ -139,9 +140,11 @@ csp_status fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s);
 // index and bit 2 on a duplicate.
 csp_status build_canonical(csp_layer *L, const int32_t *rows, const int32_t *cols, const void *vals,
                            uint32_t *flags, hipStream_t s);
-// Rebuilds row_ptr, perm_c, rows_by_col, col_ptr and both task lists from the
-// canonical arrays.  Synchronizes on s (reads back the task counts).
+// Rebuilds row_ptr, perm_c, rows_by_col, col_ptr, vals_c and both task lists
+// from the canonical arrays.  Synchronizes on s (reads back the task counts).
 csp_status build_index(csp_layer *L, hipStream_t s);
+// vals_c[j] = vals[perm_c[j]] after the canonical values changed.
+csp_status refresh_column_values(csp_layer *L, hipStream_t s);
 inline int64_t task_cap(int64_t nseg, int64_t nnz) { return nseg + (nnz + kTaskChunk - 1) / kTaskChunk; }
 
 // ---------------------------------------------------------------------------

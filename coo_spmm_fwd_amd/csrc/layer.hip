@@ -65,7 +65,7 @@ csp_status dalloc(void **p, size_t bytes, const char *what)
 void free_layer(csp_layer *L)
 {
     if (!L) return;
-    void *ptrs[] = {L->rows, L->cols, L->vals, L->row_ptr, L->perm_c, L->rows_by_col, L->col_ptr,
+    void *ptrs[] = {L->rows, L->cols, L->vals, L->row_ptr, L->perm_c, L->rows_by_col, L->col_ptr, L->vals_c,
                     L->ws.key_a, L->ws.key_b, L->ws.idx_a, L->ws.idx_b, L->ws.u_a, L->ws.u_b, L->ws.hist,
                     L->ws.rows_k, L->ws.cols_k, L->ws.vals_k, L->ws.rp_k, L->ws.acc_a, L->ws.acc_b, L->ws.sel,
                     L->act.a, L->act.b, L->act.partial,
@@ -96,6 +96,7 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&L->perm_c, 4 * n, "column permutation"},
         {(void **)&L->rows_by_col, 4 * n, "rows by column"},
         {(void **)&L->col_ptr, 4 * (size_t)(in + 1), "column offsets"},
+        {&L->vals_c, (size_t)L->esz * n, "column-ordered values"},
         {&W.key_a, 8 * cap, "sort keys"},
         {&W.key_b, 8 * cap, "sort keys"},
         {(void **)&W.idx_a, 4 * cap, "sort values"},
@@ -293,12 +294,13 @@ csp_status sparse_layer_export_index(sparse_layer_t L, int32_t *row_ptr, int32_t
 
 csp_status sparse_layer_set_values(sparse_layer_t L, const void *vals, void *stream)
 {
-    if (!L || (!vals && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to sparse_layer_set_values");
+    if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
     if (L->nnz == 0) return CSP_OK;
     DeviceGuard g(L->device);
-    CSP_HIP(hipMemcpyAsync(L->vals, vals, (size_t)L->esz * (size_t)L->nnz, hipMemcpyDeviceToDevice,
-                           (hipStream_t)stream));
-    return CSP_OK;
+    hipStream_t s = (hipStream_t)stream;
+    if (vals)
+        CSP_HIP(hipMemcpyAsync(L->vals, vals, (size_t)L->esz * (size_t)L->nnz, hipMemcpyDeviceToDevice, s));
+    return refresh_column_values(L, s);
 }
 
 void *sparse_layer_values(sparse_layer_t L) { return L ? L->vals : nullptr; }

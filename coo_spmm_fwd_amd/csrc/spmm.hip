@@ -156,6 +156,8 @@ struct Map {
     // more gathers (S <= 4), only at the half pass when it holds 4 or 8, never
     // when it holds 2 or fewer.
     static constexpr bool exit_before(int u) { return S <= 4 ? u > 0 : (S < 32 ? u == 2 : false); }
+    // Gathers held in registers at once within a block (B = 64 has 16 steps per block).
+    static constexpr int G = IT < 8 ? IT : 8;
 };
 
 // Element offset of row c of a batch-minor operand: 32-bit unless the
@@ -210,6 +212,14 @@ __device__ inline float entry_f(float v, int l)
     return __int_as_float(entry_i<S>(__float_as_int(v), l));
 }
 
+// Keeps the gathers of the next 64-entry block from being hoisted above an
+// exit test (which would put every block's gathers in registers at once).
+__device__ inline void block_fence()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
 struct Task {
     int32_t seg, kb, n, slot;
 };
@@ -220,23 +230,19 @@ __device__ inline Task load_task(const int4 *__restrict__ desc, int64_t t)
 }
 
 // ------------------------------------------------- segment sums (fwd, dX)
-// out[b, seg] = sum over the segment's entries e of val(e) * opT[idx[e]][b]
-// where val(e) = vals[e] (forward, row order) or vals[perm[e]] (input
-// gradient, column order).  A split segment's task stores its partial sums
-// instead (slot >= 0); the fixup launch finishes the segment.
-template <int LD, class D, bool kPerm, bool kWide>
-__global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
-                                                      const int32_t *__restrict__ idx,
-                                                      const int32_t *__restrict__ perm,
-                                                      const typename D::T *__restrict__ vals,
-                                                      const typename D::T *__restrict__ opT, int64_t n_op,
-                                                      int64_t n_seg, int64_t B, int nch,
-                                                      float *__restrict__ partial, typename D::T *__restrict__ out)
+// For one task of a segment: out[b, seg] = sum over its entries e of
+// vals[e] * opT[idx[e]][b].  Forward: row tasks over (cols, vals, X).
+// Input gradient: column tasks over (rows_by_col, column-ordered value
+// copy, dY).  A split segment's task stores its partial sums instead
+// (slot >= 0); the fixup launch finishes the segment.
+template <int LD, class D, bool kWide>
+__device__ __attribute__((always_inline)) inline void segment_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ idx,
+                                    const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
+                                    int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
+                                    typename D::T *__restrict__ out)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= ntasks) return;
     const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
     const Task T = load_task(desc, t);
 
@@ -255,34 +261,39 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
                 const bool ok = e < m;
                 const int32_t ec = T.kb + p0 + (ok ? e : m - 1);
                 const int32_t c = idx[ec];
-                float v;
-                if constexpr (kPerm) v = D::load(vals, perm[ec]);
-                else v = D::load(vals, ec);
+                const float v = D::load(vals, ec);
                 ci[u] = ok ? c : 0;
                 vv[u] = ok ? v : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < kPerLane; ++u) {
-                if (M::exit_before(u) && u * kWave >= m) break;
-                float x[IT][VW], v[IT];
-#pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    const int l = i * S + s;
-                    const int32_t c = entry_i<S>(ci[u], l);
-                    v[i] = entry_f<S>(vv[u], l);
-                    load_vec<VW>(op + row_off<kWide>(c, LD), x[i]);
+                if (M::exit_before(u)) {
+                    block_fence();
+                    if (u * kWave >= m) break;
                 }
-                if ((u + 1) * kWave <= m) {
 #pragma unroll
-                    for (int i = 0; i < IT; ++i)
+                for (int i0 = 0; i0 < IT; i0 += M::G) {
+                    if (i0 > 0) block_fence();
+                    float x[M::G][VW], v[M::G];
 #pragma unroll
-                        for (int w = 0; w < VW; ++w) acc[w] += v[i] * x[i][w];
-                } else {  // block holding the end of the task
+                    for (int j = 0; j < M::G; ++j) {
+                        const int l = (i0 + j) * S + s;
+                        const int32_t c = entry_i<S>(ci[u], l);
+                        v[j] = entry_f<S>(vv[u], l);
+                        load_vec<VW>(op + row_off<kWide>(c, LD), x[j]);
+                    }
+                    if ((u + 1) * kWave <= m) {
 #pragma unroll
-                    for (int i = 0; i < IT; ++i) {
-                        const bool ok = u * kWave + i * S + s < m;
+                        for (int j = 0; j < M::G; ++j)
 #pragma unroll
-                        for (int w = 0; w < VW; ++w) acc[w] += v[i] * (ok ? x[i][w] : 0.f);
+                            for (int w = 0; w < VW; ++w) acc[w] += v[j] * x[j][w];
+                    } else {  // block holding the end of the task
+#pragma unroll
+                        for (int j = 0; j < M::G; ++j) {
+                            const bool ok = u * kWave + (i0 + j) * S + s < m;
+#pragma unroll
+                            for (int w = 0; w < VW; ++w) acc[w] += v[j] * (ok ? x[j][w] : 0.f);
+                        }
                     }
                 }
             }
@@ -299,6 +310,19 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
             }
         }
     }
+}
+
+template <int LD, class D, bool kWide>
+__global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
+                                                      const int32_t *__restrict__ idx,
+                                                      const typename D::T *__restrict__ vals,
+                                                      const typename D::T *__restrict__ opT, int64_t n_op,
+                                                      int64_t n_seg, int64_t B, int nch,
+                                                      float *__restrict__ partial, typename D::T *__restrict__ out)
+{
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= ntasks) return;
+    segment_task<LD, D, kWide>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out);
 }
 
 // Finish split segments: out[b, seg] = sum over the segment's tasks, in task
@@ -332,18 +356,16 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
 // dW[e] = sum_b dYT[row][b] * XT[col_e][b] over one row task.  Each entry's
 // batch sum (VW values per lane, then LPE lanes) is staged in LDS -- every
 // lane of the entry's group writes the same value to the same word, so no
-// lane test is needed -- and each 64-entry block leaves as one coalesced row.
+// lane test is needed -- and each 64-entry block leaves as one coalesced row
+// in canonical order.
 template <int LD, bool kWide>
-__global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ desc, int64_t ntasks,
-                                                     const int32_t *__restrict__ cols, const float *__restrict__ XT,
-                                                     const float *__restrict__ dYT, int64_t in, int64_t out,
-                                                     int64_t B, int nch, float *__restrict__ dW)
+__device__ __attribute__((always_inline)) inline void values_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ cols,
+                                   const float *__restrict__ XT, const float *__restrict__ dYT, int64_t in,
+                                   int64_t out, int nch, float *__restrict__ dW)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
     __shared__ float stage[4][kWave];
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= ntasks) return;
     const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
     float *lds = stage[threadIdx.x >> 6];
     const Task T = load_task(desc, t);
@@ -362,16 +384,22 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
             }
 #pragma unroll
             for (int u = 0; u < kPerLane; ++u) {
+                if (M::exit_before(u)) block_fence();
                 if (u * kWave >= m) break;
-                float x[IT][VW];
 #pragma unroll
-                for (int i = 0; i < IT; ++i) load_vec<VW>(xt + row_off<kWide>(entry_i<S>(ci[u], i * S + s), LD), x[i]);
+                for (int i0 = 0; i0 < IT; i0 += M::G) {
+                    if (i0 > 0) block_fence();
+                    float x[M::G][VW];
 #pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    float p = 0.f;
+                    for (int j = 0; j < M::G; ++j)
+                        load_vec<VW>(xt + row_off<kWide>(entry_i<S>(ci[u], (i0 + j) * S + s), LD), x[j]);
 #pragma unroll
-                    for (int w = 0; w < VW; ++w) p += dy[w] * x[i][w];
-                    lds[i * S + s] = group_sum<LPE>(p);
+                    for (int j = 0; j < M::G; ++j) {
+                        float p = 0.f;
+#pragma unroll
+                        for (int w = 0; w < VW; ++w) p += dy[w] * x[j][w];
+                        lds[(i0 + j) * S + s] = group_sum<LPE>(p);
+                    }
                 }
                 const float r = lds[lane];
                 const int32_t e = p0 + u * kWave + lane;
@@ -384,95 +412,50 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
     }
 }
 
-// ------------------------------------------ both gradients, column order
-// For one column task: dX[b, c] = sum_j v_j dYT[r_j][b] and, for each entry,
-// dW[perm_j] = sum_b XT[c][b] dYT[r_j][b]; every gathered dY run feeds both.
 template <int LD, bool kWide>
-__global__ __launch_bounds__(256) void k_bwd_cols(const int4 *__restrict__ desc, int64_t ntasks,
-                                                  const int32_t *__restrict__ rows_by_col,
-                                                  const int32_t *__restrict__ perm_c, const float *__restrict__ vals,
-                                                  const float *__restrict__ XT, const float *__restrict__ dYT,
-                                                  int64_t in, int64_t out, int64_t B, int nch,
-                                                  float *__restrict__ partial, float *__restrict__ dX,
-                                                  float *__restrict__ dW)
+__global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ desc, int64_t ntasks,
+                                                     const int32_t *__restrict__ cols, const float *__restrict__ XT,
+                                                     const float *__restrict__ dYT, int64_t in, int64_t out,
+                                                     int nch, float *__restrict__ dW)
 {
-    using M = Map<LD>;
-    constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
-    __shared__ float stage[4][kWave];
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
-    float *lds = stage[threadIdx.x >> 6];
-    const Task T = load_task(desc, t);
-    for (int ch = 0; ch < nch; ++ch) {
-        float xc[VW];
-        load_vec<VW>(XT + ((int64_t)ch * in + T.seg) * LD + q * VW, xc);
-        const float *dyt = dYT + (int64_t)ch * out * LD + q * VW;
-        float acc[VW];
-#pragma unroll
-        for (int w = 0; w < VW; ++w) acc[w] = 0.f;
-        for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
-            const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
-            int32_t ri[kPerLane], pk[kPerLane];
-            float vv[kPerLane];
-#pragma unroll
-            for (int u = 0; u < kPerLane; ++u) {
-                const int e = u * kWave + lane;
-                const bool ok = e < m;
-                const int32_t ec = T.kb + p0 + (ok ? e : m - 1);
-                const int32_t r = rows_by_col[ec];
-                pk[u] = perm_c[ec];
-                const float v = vals[pk[u]];
-                ri[u] = ok ? r : 0;
-                vv[u] = ok ? v : 0.f;
-            }
-#pragma unroll
-            for (int u = 0; u < kPerLane; ++u) {
-                if (u * kWave >= m) break;
-                float y[IT][VW], v[IT];
-#pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    const int l = i * S + s;
-                    const int32_t r = entry_i<S>(ri[u], l);
-                    v[i] = entry_f<S>(vv[u], l);
-                    load_vec<VW>(dyt + row_off<kWide>(r, LD), y[i]);
-                }
-                if ((u + 1) * kWave > m) {  // block holding the end of the task
-#pragma unroll
-                    for (int i = 0; i < IT; ++i) {
-                        const bool ok = u * kWave + i * S + s < m;
-#pragma unroll
-                        for (int w = 0; w < VW; ++w) y[i][w] = ok ? y[i][w] : 0.f;
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < IT; ++i) {
-                    float p = 0.f;
-#pragma unroll
-                    for (int w = 0; w < VW; ++w) {
-                        acc[w] += v[i] * y[i][w];
-                        p += xc[w] * y[i][w];
-                    }
-                    lds[i * S + s] = group_sum<LPE>(p);
-                }
-                const float r = lds[lane];
-                if (u * kWave + lane < m) {
-                    if (ch == 0) dW[pk[u]] = r;
-                    else dW[pk[u]] += r;
-                }
-            }
-        }
-#pragma unroll
-        for (int w = 0; w < VW; ++w) acc[w] = slot_sum<LPE>(acc[w]);
-        if (s == 0) {
-#pragma unroll
-            for (int w = 0; w < VW; ++w) {
-                const int64_t b = (int64_t)ch * LD + q * VW + w;
-                if (b >= B) continue;
-                if (T.slot < 0) dX[b * in + T.seg] = acc[w];
-                else partial[((int64_t)T.slot * nch + ch) * LD + q * VW + w] = acc[w];
-            }
-        }
+    values_task<LD, kWide>(desc, t, cols, XT, dYT, in, out, nch, dW);
+}
+
+// --------------------------------------------------- both gradients
+// The two gradients are independent; one launch runs both so that their
+// latency chains overlap: even/odd blocks alternate between input-gradient
+// column tasks and value-gradient row tasks, the longer list's surplus
+// blocks come last.
+template <int LD, bool kWide>
+__global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_desc, int64_t ncol_tasks,
+                                                   const int4 *__restrict__ row_desc, int64_t nrow_tasks,
+                                                   const int32_t *__restrict__ rows_by_col,
+                                                   const float *__restrict__ vals_c, const int32_t *__restrict__ cols,
+                                                   const float *__restrict__ XT, const float *__restrict__ dYT,
+                                                   int64_t in, int64_t out, int64_t B, int nch,
+                                                   float *__restrict__ partial, float *__restrict__ dX,
+                                                   float *__restrict__ dW)
+{
+    const int64_t ncb = (ncol_tasks + 3) / 4, nrb = (nrow_tasks + 3) / 4;
+    const int64_t m = ncb < nrb ? ncb : nrb;
+    const int64_t bid = blockIdx.x;
+    bool col;
+    int64_t blk;
+    if (bid < 2 * m) {
+        col = (bid & 1) == 0;
+        blk = bid >> 1;
+    } else {
+        col = ncb > nrb;
+        blk = m + (bid - 2 * m);
+    }
+    const int64_t t = blk * 4 + (threadIdx.x >> 6);
+    if (col) {
+        if (t < ncol_tasks)
+            segment_task<LD, F32, kWide>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, nch, partial, dX);
+    } else if (t < nrow_tasks) {
+        values_task<LD, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW);
     }
 }
 
@@ -551,8 +534,8 @@ csp_status batch_minor(csp_layer *L, int64_t B, const void *X1, int64_t n1, void
     case 32: MACRO(32, W); break;     \
     default: MACRO(64, W); break;     \
     }
-#define CSP_LD_SWITCH(ld, wide, MACRO)           \
-    do {                                         \
+#define CSP_LD_SWITCH(ld, wide, MACRO)             \
+    do {                                           \
         if (wide) CSP_LD_SWITCH_W(ld, MACRO, true) \
         else CSP_LD_SWITCH_W(ld, MACRO, false)     \
     } while (0)
@@ -581,10 +564,9 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, hipStr
     const TaskList &TL = L->row_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
-#define CSP_FWD(LDV, W)                                                                                     \
-    k_segment_spmm<LDV, D, false, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, nullptr,                 \
-                                                       (const T *)L->vals, (const T *)XT, L->in, L->out, B, \
-                                                       nch, L->act.partial, (T *)Y)
+#define CSP_FWD(LDV, W)                                                                                          \
+    k_segment_spmm<LDV, D, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, \
+                                                   L->in, L->out, B, nch, L->act.partial, (T *)Y)
     CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_FWD);
 #undef CSP_FWD
     CSP_LAUNCHED("k_segment_spmm (forward)");
@@ -616,10 +598,9 @@ csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, h
     const TaskList &TL = L->col_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
-#define CSP_DX(LDV, W)                                                                                          \
-    k_segment_spmm<LDV, F32, true, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, L->perm_c,           \
-                                                        (const float *)L->vals, dyt, L->out, L->in, B, nch,     \
-                                                        L->act.partial, (float *)dX)
+#define CSP_DX(LDV, W)                                                                                           \
+    k_segment_spmm<LDV, F32, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, (const float *)L->vals_c, \
+                                                     dyt, L->out, L->in, B, nch, L->act.partial, (float *)dX)
     CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_DX);
 #undef CSP_DX
     CSP_LAUNCHED("k_segment_spmm (input gradient)");
@@ -642,8 +623,8 @@ csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
 #define CSP_DW(LDV, W) \
-    k_values_rows<LDV, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, xt, dyt, L->in, L->out, B, nch, dW)
-    CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_DW);
+    k_values_rows<LDV, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, xt, dyt, L->in, L->out, nch, dW)
+    CSP_LD_SWITCH(ld, wide_operand(L->in > L->out ? L->in : L->out, ld), CSP_DW);
 #undef CSP_DW
     CSP_LAUNCHED("k_values_rows");
     timing_mark(L, false, s);
@@ -660,17 +641,44 @@ csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, vo
     const float *dyt = (const float *)(B == 1 ? dY : L->act.b);
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
-    const TaskList &TL = L->col_tasks;
-    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    const TaskList &CT = L->col_tasks, &RT = L->row_tasks;
+    const int64_t nrow = L->nnz > 0 ? RT.count : 0;  // no value-gradient work for an empty layer
+    const bool wide = wide_operand(L->in > L->out ? L->in : L->out, ld);
+    // One launch for both gradients overlaps their latency chains, but the two
+    // interleaved passes gather from both batch-minor tables at once; when the
+    // tables together exceed about half an XCD's 4 MiB L2 they evict each
+    // other, so the passes run as two launches instead.
+    const int64_t table_bytes = (int64_t)sizeof(float) * ld * (L->in + L->out);
+    if (table_bytes > (int64_t(2) << 20)) {
+        const unsigned gx = (unsigned)ceil_div(CT.count, 4), gw = (unsigned)ceil_div(nrow, 4);
+        timing_mark(L, true, s);
+#define CSP_DX2(LDV, W)                                                                                        \
+    k_segment_spmm<LDV, F32, W><<<gx, 256, 0, s>>>(CT.desc, CT.count, L->rows_by_col, (const float *)L->vals_c, \
+                                                   dyt, L->out, L->in, B, nch, L->act.partial, (float *)dX)
+        CSP_LD_SWITCH(ld, wide, CSP_DX2);
+#undef CSP_DX2
+        CSP_LAUNCHED("k_segment_spmm (input gradient)");
+        if (gw > 0) {
+#define CSP_DW2(LDV, W) \
+    k_values_rows<LDV, W><<<gw, 256, 0, s>>>(RT.desc, nrow, L->cols, xt, dyt, L->in, L->out, nch, dW)
+            CSP_LD_SWITCH(ld, wide, CSP_DW2);
+#undef CSP_DW2
+            CSP_LAUNCHED("k_values_rows");
+        }
+        timing_mark(L, false, s);
+        return split_fixup<F32>(L, CT, B, L->in, dX, s);
+    }
+    const unsigned grid = (unsigned)(ceil_div(CT.count, 4) + ceil_div(nrow, 4));
     timing_mark(L, true, s);
-#define CSP_BWD(LDV, W)                                                                                       \
-    k_bwd_cols<LDV, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, L->perm_c, (const float *)L->vals, \
-                                         xt, dyt, L->in, L->out, B, nch, L->act.partial, (float *)dX, dW)
-    CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_BWD);
-#undef CSP_BWD
-    CSP_LAUNCHED("k_bwd_cols");
+#define CSP_BOTH(LDV, W)                                                                                            \
+    k_gradients<LDV, W><<<grid, 256, 0, s>>>(CT.desc, CT.count, RT.desc, nrow, L->rows_by_col,                    \
+                                             (const float *)L->vals_c, L->cols, xt, dyt, L->in, L->out, B, nch,   \
+                                             L->act.partial, (float *)dX, dW)
+    CSP_LD_SWITCH(ld, wide, CSP_BOTH);
+#undef CSP_BOTH
+    CSP_LAUNCHED("k_gradients");
     timing_mark(L, false, s);
-    return split_fixup<F32>(L, TL, B, L->in, dX, s);
+    return split_fixup<F32>(L, CT, B, L->in, dX, s);
 }
 
 }  // namespace csp

@@ -158,14 +158,19 @@ csp_status sparse_layer_export_index(sparse_layer_t layer, int32_t *row_ptr, int
  * sparse_layer_values -- device pointer to the layer's canonical values
  * (nnz elements of the layer dtype), for in-place optimizer updates between
  * calls.  Valid until the layer is destroyed; restructure rewrites it in
- * place.  NULL for a NULL layer.
+ * place.  NULL for a NULL layer.  The input-gradient pass reads a
+ * column-ordered copy of the values: after writing through this pointer,
+ * call sparse_layer_set_values(layer, NULL, stream) before the next
+ * spmm_bwd_input or spmm_bwd.
  */
 void *sparse_layer_values(sparse_layer_t layer);
 
 /*
  * sparse_layer_set_values -- overwrite the canonical values with vals[nnz]
  * (device array of the layer dtype, canonical order), e.g. after an
- * optimizer step kept outside the library.  Structure is unchanged.
+ * optimizer step kept outside the library, and refresh the column-ordered
+ * copy.  vals = NULL only refreshes the copy (values already changed in
+ * place).  Structure is unchanged.  Asynchronous on stream.
  */
 csp_status sparse_layer_set_values(sparse_layer_t layer, const void *vals, void *stream);
 

@@ -121,6 +121,30 @@ def test_products_after_restructure(orc):
         csp.sparse_layer_destroy(h)
 
 
+def test_in_place_value_update_then_refresh(orc):
+    """Values changed through the zero-copy view are seen by every pass once the copy is refreshed."""
+    L = W.random_layer(500, 400, 20000, seed=29)
+    h = csp.sparse_layer_create(500, 400, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(500, 400, L.rows, L.cols, L.vals)
+        v = csp.sparse_layer_values_tensor(h)
+        v.mul_(-2.0)
+        v[:7] = 0.5
+        csp.sparse_layer_set_values(h, None)
+        newv = host(v.clone())
+        rows, cols = c["rows"], c["cols"]
+        X = W.random_dense((8, 400), 3)
+        dY = W.random_dense((8, 500), 4)
+        Y = host(csp.spmm_fwd(h, dev(X)))
+        ref, S = orc.spmm_fwd(500, 400, rows, cols, newv, X)
+        assert_within(Y, ref, S, FP32_REL, "fwd after in-place update")
+        for dX in (host(csp.spmm_bwd_input(h, dev(dY))), host(csp.spmm_bwd(h, dev(dY), dev(X))[0])):
+            ref, S = orc.spmm_bwd_input(500, 400, rows, cols, newv, dY)
+            assert_within(dX, ref, S, FP32_REL, "dX after in-place update")
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
 def test_dst_loop_full_size(orc):
     """8192x8192 at 95% sparsity, B=64: 10 steps of value gradient, SGD (harness), restructure of 10%."""
     w, layers, acts = W.build("dst8192_b64_s95")
