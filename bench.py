@@ -148,28 +148,75 @@ def ingest_counters(fetch_dir, write_dir, workload, batch, copy_mib=256):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(w, L, acts, B, budget_s=12.0):
-    """The oracle as written (fp64 loops, one core) on the same step: forward, dX, dW."""
+def cpu_baseline(kind, layers, acts, B, n_prune=0, seed=0, budget_s=12.0):
+    """The oracle as written (fp64 loops, one core) on the same step, repeated until ~budget_s."""
     import numpy as np
     import oracle
     orc = oracle.default()
     X, dY = acts[B]["X"], acts[B]["dY"]
-    canon = orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals)
+    canon = [orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals) for L in layers]
+
+    def one_step():
+        if kind == "inference":
+            L = layers[0]
+            orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, X)
+            return
+        if kind == "mlp":
+            L1, L2 = layers
+            H, _ = orc.spmm_fwd(L1.out, L1.in_, L1.rows, L1.cols, L1.vals, X)
+            A = orc.gelu(H).astype(np.float32)
+            orc.spmm_fwd(L2.out, L2.in_, L2.rows, L2.cols, L2.vals, A)
+            dA, _ = orc.spmm_bwd_input(L2.out, L2.in_, L2.rows, L2.cols, L2.vals, dY)
+            orc.spmm_bwd_values(L2.out, L2.in_, canon[1]["rows"], canon[1]["cols"], dY, A)
+            dH = (dA * orc.gelu_grad(H)).astype(np.float32)
+            orc.spmm_bwd_input(L1.out, L1.in_, L1.rows, L1.cols, L1.vals, dH)
+            orc.spmm_bwd_values(L1.out, L1.in_, canon[0]["rows"], canon[0]["cols"], dH, X)
+            return
+        L = layers[0]
+        orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, X)
+        orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dY)
+        orc.spmm_bwd_values(L.out, L.in_, canon[0]["rows"], canon[0]["cols"], dY, X)
+        if kind == "dst":
+            c = canon[0]
+            orc.restructure(L.out, L.in_, c["rows"], c["cols"], c["vals"], n_prune, seed, 1)
+
     reps, t_all = 0, 0.0
     while True:
         t0 = time.perf_counter()
-        orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, X)
-        orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dY)
-        orc.spmm_bwd_values(L.out, L.in_, canon["rows"], canon["cols"], dY, X)
+        one_step()
         t_all += time.perf_counter() - t0
         reps += 1
         if t_all >= budget_s or reps >= 100:
             break
     step_s = t_all / reps
-    nbytes = bytes_fwd(L.nnz, L.out, L.in_, B) + bytes_dx(L.nnz, L.out, L.in_, B) + bytes_dw(L.nnz, L.out, L.in_, B)
+    nbytes = step_bytes(kind, layers, B, n_prune)
     return {"value": round(nbytes / step_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full step(s) (forward, input gradient, value gradient) of the same layer and batch, "
-                      f"{step_s * 1e3:.1f} ms per step"}
+            "sample": f"{reps} full step(s) of the same workload and batch on one core, {step_s * 1e3:.1f} ms per step"}
+
+
+# ------------------------------------------------------------------ steps
+def workload_kind(w) -> str:
+    if w.dtype == "bf16":
+        return "inference"
+    if len(w.layers) == 2:
+        return "mlp"
+    if w.prune_frac > 0:
+        return "dst"
+    return "linear"
+
+
+def step_bytes(kind, layers, B, n_prune=0):
+    """Algorithmic bytes of one step: forward + input gradient + value gradient of every layer
+    (forward only for inference), plus 36 B per entry for a restructure."""
+    tot = 0
+    for L in layers:
+        sv = 2 if L.dtype == "bf16" else 4
+        tot += bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)
+        if kind != "inference":
+            tot += bytes_dx(L.nnz, L.out, L.in_, B) + bytes_dw(L.nnz, L.out, L.in_, B)
+    if kind == "dst":
+        tot += 36 * layers[0].nnz
+    return tot
 
 
 # ------------------------------------------------------------------ main
@@ -207,54 +254,118 @@ def main():
     torch.cuda.set_device(dev)
 
     w, layers, acts = W.build(args.workload)
-    if w.dtype != "f32" or len(layers) != 1:
-        print(f"workload {args.workload} is not a single fp32 training layer", file=sys.stderr)
-        sys.exit(2)
-    L = layers[0]
-    B = args.batch or w.batches[0]
+    kind = workload_kind(w)
+    B = args.batch or (max(w.batches) if kind == "mlp" else w.batches[0])
     if B not in acts:
-        acts[B] = dict(X=W.random_dense((B, L.in_), 11), dY=W.random_dense((B, L.out), 12))
-    nnz, out, in_ = L.nnz, L.out, L.in_
-
-    b_fwd, b_dx, b_dw = bytes_fwd(nnz, out, in_, B), bytes_dx(nnz, out, in_, B), bytes_dw(nnz, out, in_, B)
-    b_bwd = bytes_gradients(nnz, out, in_, B)
-    step_bytes = b_fwd + b_dx + b_dw
-    # bytes one step touches in one replica: structure of both orders, values, dW, dense operands
-    touched = nnz * (4 * 5 + 4) + 4 * B * (3 * in_ + 2 * out)
+        acts[B] = dict(X=W.random_dense((B, layers[0].in_), 11, dtype=w.dtype),
+                       dY=W.random_dense((B, layers[-1].out), 12, dtype=w.dtype))
+    n_prune = int(w.prune_frac * layers[0].nnz) if kind == "dst" else 0
+    sbytes = step_bytes(kind, layers, B, n_prune)
+    # bytes one step touches in one replica: both index orders, both value orders, dW, dense operands
+    touched = sum(L.nnz * 28 + 4 * B * (3 * L.in_ + 2 * L.out) for L in layers)
     R = 1 if args.warm else max(2, -(-2 * MALL_BYTES // touched) + 1)
 
-    t = lambda a: torch.from_numpy(a).to(dev)
-    rows, cols, vals = t(L.rows), t(L.cols), t(L.vals)
-    handles = [csp.sparse_layer_create(out, in_, rows, cols, vals) for _ in range(R)]
-    Xs = [t(acts[B]["X"]) for _ in range(R)]
-    dYs = [t(acts[B]["dY"]) for _ in range(R)]
-    Ys = [torch.empty((B, out), device=dev) for _ in range(R)]
-    dXs = [torch.empty((B, in_), device=dev) for _ in range(R)]
-    dWs = [torch.empty((nnz,), device=dev) for _ in range(R)]
+    def t(a):
+        if a.dtype.name == "uint16":
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    uploaded = [(t(L.rows), t(L.cols), t(L.vals)) for L in layers]
+    reps = []
+    for j in range(R):
+        st = {"h": [csp.sparse_layer_create(L.out, L.in_, *u) for L, u in zip(layers, uploaded)],
+              "X": t(acts[B]["X"]), "dY": t(acts[B]["dY"])}
+        if kind == "mlp":
+            L1, L2 = layers
+            st.update(H=torch.empty((B, L1.out), device=dev), A=torch.empty((B, L1.out), device=dev),
+                      Y=torch.empty((B, L2.out), device=dev), dA=torch.empty((B, L1.out), device=dev),
+                      dH=torch.empty((B, L1.out), device=dev), dX=torch.empty((B, L1.in_), device=dev),
+                      dW1=torch.empty((L1.nnz,), device=dev), dW2=torch.empty((L2.nnz,), device=dev))
+        else:
+            L = layers[0]
+            st.update(Y=torch.empty((B, L.out), device=dev, dtype=st["X"].dtype))
+            if kind != "inference":
+                st.update(dX=torch.empty((B, L.in_), device=dev), dW=torch.empty((L.nnz,), device=dev))
+        reps.append(st)
+
+    ld = 1
+    while ld < min(B, 64):
+        ld *= 2
+    fwd_name = f"k_segment_spmm<{ld}, {'BF16' if w.dtype == 'bf16' else 'F32'}, false>"
+    # spmm_bwd runs both gradient passes in one launch unless their two batch-minor
+    # operand tables exceed 2 MiB together (then the two kernels run back to back)
+    big = any(4 * ld * (L.in_ + L.out) > (2 << 20) for L in layers)
+    grad_name = (f"k_segment_spmm<{ld}, F32, false> + k_values_rows<{ld}, false>" if big
+                 else f"k_gradients<{ld}, false>")
+
+    def gelu_parts(H):
+        cdf = 0.5 * (1.0 + torch.erf(H * 0.7071067811865476))
+        return H * cdf, cdf + H * torch.exp(-0.5 * H * H) * 0.3989422804014327
+
+    def calls(st, stream):
+        """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic bytes)."""
+        out = []
+        if kind == "mlp":
+            (h1, h2), (L1, L2) = st["h"], layers
+
+            def f1():
+                csp.spmm_fwd(h1, st["X"], st["H"], stream=stream)
+                a, g = gelu_parts(st["H"])
+                st["A"].copy_(a)
+                st["G"] = g
+
+            def b2():
+                csp.spmm_bwd(h2, st["dY"], st["A"], st["dA"], st["dW2"], stream=stream)
+                torch.mul(st["dA"], st["G"], out=st["dH"])
+
+            out.append(("forward 1", h1, f1, fwd_name, bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
+            out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream), fwd_name,
+                        bytes_fwd(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("backward 2", h2, b2, grad_name, bytes_gradients(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("backward 1", h1, lambda: csp.spmm_bwd(h1, st["dH"], st["X"], st["dX"], st["dW1"],
+                                                               stream=stream), grad_name,
+                        bytes_gradients(L1.nnz, L1.out, L1.in_, B)))
+            return out
+        h, L = st["h"][0], layers[0]
+        sv = 2 if w.dtype == "bf16" else 4
+        out.append(("forward", h, lambda: csp.spmm_fwd(h, st["X"], st["Y"], stream=stream), fwd_name,
+                    bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)))
+        if kind != "inference":
+            out.append(("backward", h, lambda: csp.spmm_bwd(h, st["dY"], st["X"], st["dX"], st["dW"], stream=stream),
+                        grad_name, bytes_gradients(L.nnz, L.out, L.in_, B)))
+        return out
+
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        j = i % R
-        csp.spmm_fwd(handles[j], Xs[j], Ys[j], stream=stream)
-        csp.spmm_bwd(handles[j], dYs[j], Xs[j], dXs[j], dWs[j], stream=stream)
+    def run_calls(st, s):
+        for _, _, fn, _, _ in calls(st, s):
+            fn()
+
+    step_no = [0]
+
+    def after(st):  # the part of a step that cannot be captured (restructure reads back and syncs)
+        if kind == "dst":
+            csp.restructure(st["h"][0], n_prune, seed=w.seed, step=step_no[0], stream=stream)
+            step_no[0] += 1
 
     for i in range(max(args.warmup, R)):  # eager warm-up; also sizes every layer's operand workspace
-        step(i)
+        run_calls(reps[i % R], stream)
+        after(reps[i % R])
     torch.cuda.synchronize()
 
-    # One HIP graph per replica holds one step (two library calls, five kernels),
-    # so the timed loop is K graph launches and host-side Python costs stay out.
     graphs = []
-    if not args.eager:
+    # A restructure rebuilds the task lists (their sizes set launch grids), so a
+    # step that restructures is launched eagerly rather than from a captured graph.
+    use_graphs = not args.eager and kind != "dst"
+    if use_graphs:
         for j in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                s_cap = torch.cuda.current_stream()
-                csp.spmm_fwd(handles[j], Xs[j], Ys[j], stream=s_cap)
-                csp.spmm_bwd(handles[j], dYs[j], Xs[j], dXs[j], dWs[j], stream=s_cap)
+                run_calls(reps[j], torch.cuda.current_stream())
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % R].replay()
+            after(reps[i % R])
         torch.cuda.synchronize()
 
     # timed region: exactly K steps
@@ -266,50 +377,44 @@ def main():
         if graphs:
             graphs[i % R].replay()
         else:
-            step(i)
+            run_calls(reps[i % R], stream)
+        after(reps[i % R])
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # second pass, same work: events around each op and around the main kernels
+    # second pass, same work, eager: HIP events recorded by the library around each main kernel
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
-    for evs in ev:  # instantiate the events
-        for e in evs:
-            e.record(stream)
+    labels = [c[0] for c in calls(reps[0], stream)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in labels]
+          for _ in range(K)]
+    for row in ev:
+        for a, b in row:
+            a.record(stream)
+            b.record(stream)
     torch.cuda.synchronize()
     for i in range(K):
-        j = i % R
-        a = ev[i]
-        a[0].record(stream)
-        csp.sparse_layer_time_next(handles[j], a[1], a[2])
-        csp.spmm_fwd(handles[j], Xs[j], Ys[j], stream=stream)
-        a[3].record(stream)
-        csp.sparse_layer_time_next(handles[j], a[4], a[5])
-        csp.spmm_bwd(handles[j], dYs[j], Xs[j], dXs[j], dWs[j], stream=stream)
+        for (label, h, fn, _, _), (a, b) in zip(calls(reps[i % R], stream), ev[i]):
+            csp.sparse_layer_time_next(h, a, b)
+            fn()
+        after(reps[i % R])
     torch.cuda.synchronize()
-    fwd_op = sum(a[0].elapsed_time(a[3]) for a in ev) / K
-    fwd_k = sum(a[1].elapsed_time(a[2]) for a in ev) / K
-    bwd_k = sum(a[4].elapsed_time(a[5]) for a in ev) / K
-    ld = 1
-    while ld < min(B, 64):
-        ld *= 2
-    kernels = {
-        "forward": {"name": f"k_segment_spmm<{ld}, F32, false>", "us": fwd_k * 1e3, "bytes": b_fwd},
-        "backward": {"name": f"k_gradients<{ld}, false>", "us": bwd_k * 1e3, "bytes": b_bwd},
-    }
-    dom_key = max(kernels, key=lambda k: kernels[k]["us"])
-    dom = kernels[dom_key]
+    per_call = {}
+    for ci, (label, _, _, kname, kbytes) in enumerate(calls(reps[0], stream)):
+        us = sum(ev[i][ci][0].elapsed_time(ev[i][ci][1]) for i in range(K)) / K * 1e3
+        per_call[label] = {"kernel": kname, "us": us, "bytes": kbytes}
+    dom_label = max(per_call, key=lambda k: per_call[k]["us"])
+    dom = per_call[dom_label]
     achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
-    traffic = traffic_for(dom["name"], {"workload": args.workload, "batch": B})
+    traffic = traffic_for(dom["kernel"], {"workload": args.workload, "batch": B})
 
-    # restructure on the same layer (10% of entries), timed separately
-    n_prune = nnz // 10
-    torch.cuda.synchronize()
-    r0 = time.perf_counter()
-    csp.restructure(handles[0], n_prune, seed=w.seed, step=1)
-    restructure_ms = (time.perf_counter() - r0) * 1e3
+    restructure_ms = None
+    if kind in ("linear", "dst"):
+        torch.cuda.synchronize()
+        r0 = time.perf_counter()
+        csp.restructure(reps[0]["h"][0], layers[0].nnz // 10, seed=w.seed, step=12345, stream=stream)
+        restructure_ms = (time.perf_counter() - r0) * 1e3
 
     if args.calibrate_copy:
         n = (args.calibrate_copy << 20) // 4
@@ -322,11 +427,16 @@ def main():
 
     del graphs
     torch.cuda.synchronize()
-    for h in handles:
-        csp.sparse_layer_destroy(h)
+    for st in reps:
+        for h in st["h"]:
+            csp.sparse_layer_destroy(h)
 
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    flops = 3 * 2 * nnz * B
+    value = sbytes / (ms_per_step * 1e-3) / 1e9
+    flops = sum(2 * L.nnz * B * (1 if kind == "inference" else 3) for L in layers)
+    steps_desc = {"linear": "spmm_fwd + spmm_bwd (dX and dW)",
+                  "dst": f"spmm_fwd + spmm_bwd + restructure({n_prune} of {layers[0].nnz})",
+                  "inference": "spmm_fwd",
+                  "mlp": "fwd1, GELU, fwd2, bwd2 (dA, dW2), GELU', bwd1 (dX, dW1)"}[kind]
     rec = {
         "metric": "SpMM fwd+bwd effective GB/s and GFLOP/s (2*nnz*B); % of HBM roofline",
         "value": round(value, 2),
@@ -338,25 +448,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "out": out, "in": in_, "nnz": nnz, "batch": B,
-                   "sparsity": round(1 - nnz / (out * in_), 4), "step": "spmm_fwd + spmm_bwd (dX and dW)",
+        "config": {"workload": args.workload,
+                   "layers": [{"out": L.out, "in": L.in_, "nnz": L.nnz} for L in layers], "batch": B,
+                   "sparsity": round(1 - layers[0].nnz / (layers[0].out * layers[0].in_), 4), "step": steps_desc,
                    "replicas": R, "cache": "warm" if args.warm else "cold",
-                   "launch": "eager" if args.eager else "hip_graph_per_step"},
+                   "launch": "hip_graph_per_step" if use_graphs else "eager"},
         "gflops": round(flops / (ms_per_step * 1e-3) / 1e9, 2),
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": dom["name"], "avg_launch_us": round(dom["us"], 3),
+                     "kernel": dom["kernel"], "call": dom_label, "avg_launch_us": round(dom["us"], 3),
                      "bytes_per_launch": dom["bytes"]},
-        "ops_us": {"forward_call": round(fwd_op * 1e3, 3), "forward_kernel": round(fwd_k * 1e3, 3),
-                   "backward_kernel": round(bwd_k * 1e3, 3)},
-        "restructure_ms": round(restructure_ms, 3),
+        "kernels_us": {k: round(v["us"], 3) for k, v in per_call.items()},
+        "restructure_ms": None if restructure_ms is None else round(restructure_ms, 3),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, L, acts, B)
+        rec["cpu_baseline"] = cpu_baseline(kind, layers, acts, B, n_prune, w.seed)
     print(json.dumps(rec), flush=True)
 
 
