@@ -31,6 +31,7 @@ struct Workspace {
     int32_t *rows_k = nullptr, *cols_k = nullptr;  // nnz: kept entries during restructure
     void *vals_k = nullptr;                        // nnz values
     int32_t *rp_k = nullptr;                       // out + 1: kept row offsets
+    int32_t *rp_new = nullptr;                     // out + 1: row offsets of regrown positions
     uint64_t *acc_a = nullptr, *acc_b = nullptr;   // nnz: accepted regrow positions
     uint32_t *sel = nullptr;                       // small select state / flags (256 words)
     int64_t nkey_cap = 0;

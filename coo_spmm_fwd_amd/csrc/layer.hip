@@ -67,7 +67,7 @@ void free_layer(csp_layer *L)
     if (!L) return;
     void *ptrs[] = {L->rows, L->cols, L->vals, L->row_ptr, L->perm_c, L->rows_by_col, L->col_ptr, L->vals_c,
                     L->ws.key_a, L->ws.key_b, L->ws.idx_a, L->ws.idx_b, L->ws.u_a, L->ws.u_b, L->ws.hist,
-                    L->ws.rows_k, L->ws.cols_k, L->ws.vals_k, L->ws.rp_k, L->ws.acc_a, L->ws.acc_b, L->ws.sel,
+                    L->ws.rows_k, L->ws.cols_k, L->ws.vals_k, L->ws.rp_k, L->ws.rp_new, L->ws.acc_a, L->ws.acc_b, L->ws.sel,
                     L->act.a, L->act.b, L->act.partial,
                     L->row_tasks.desc, L->row_tasks.split, L->row_tasks.seg_first,
                     L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first};
@@ -108,6 +108,7 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&W.cols_k, 4 * n, "kept cols"},
         {&W.vals_k, (size_t)L->esz * n, "kept values"},
         {(void **)&W.rp_k, 4 * (size_t)(out + 1), "kept offsets"},
+        {(void **)&W.rp_new, 4 * (size_t)(out + 1), "regrown offsets"},
         {(void **)&W.acc_a, 8 * n, "regrow positions"},
         {(void **)&W.acc_b, 8 * n, "regrow positions"},
         {(void **)&W.sel, 4 * 1024, "select state"},

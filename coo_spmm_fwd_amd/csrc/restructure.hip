@@ -79,18 +79,39 @@ __global__ void k_sel_init(uint32_t *sel, uint32_t n_prune)
     if (t == 0) sel[kSelState + 2] = n_prune;
 }
 
+// Lanes of the wave whose 8-bit digit equals this lane's (and that take part).
+__device__ inline uint64_t same_digit_lanes(uint32_t d, bool take)
+{
+    uint64_t m = __ballot(take);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const bool on = (d >> bit) & 1u;
+        const uint64_t bb = __ballot(on);
+        m &= on ? bb : ~bb;
+    }
+    return m;
+}
+
+// Digit histogram of the entries whose higher magnitude bits match the
+// prefix found so far.  The top digits of |v| cluster in a few bins, so each
+// wave adds one count per distinct digit (its lowest lane does the LDS atomic).
 template <typename V>
 __global__ __launch_bounds__(256) void k_sel_hist(const V *__restrict__ vals, int64_t n, int shift,
                                                   uint32_t *__restrict__ sel)
 {
     __shared__ uint32_t h[256];
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63;
     h[t] = 0;
     __syncthreads();
     const uint32_t prefix = sel[kSelState], mask = sel[kSelState + 1];
-    for (int64_t k = (int64_t)blockIdx.x * blockDim.x + t; k < n; k += (int64_t)gridDim.x * blockDim.x) {
-        uint32_t key = mag_key<V>(vals[k]);
-        if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & 255u], 1u);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x + (t - lane); base < n; base += stride) {
+        const int64_t k = base + lane;
+        const uint32_t key = k < n ? mag_key<V>(vals[k]) : 0u;
+        const bool take = k < n && (key & mask) == prefix;
+        const uint32_t d = (key >> shift) & 255u;
+        const uint64_t m = same_digit_lanes(d, take);
+        if (take && (m & ((1ull << lane) - 1)) == 0) atomicAdd(&h[d], (uint32_t)__popcll(m));
     }
     __syncthreads();
     if (h[t]) atomicAdd(&sel[kSelHist + t], h[t]);
@@ -263,18 +284,30 @@ __global__ void k_copy_u64(const uint64_t *__restrict__ a, uint64_t *__restrict_
     if (t < n) b[t] = a[t];
 }
 
+// First new position of each row: new_rp[r] = first index with newp >= r*in.
+__global__ void k_new_row_offsets(const uint64_t *__restrict__ newp, int64_t nnew, int64_t out, int64_t in,
+                                  int32_t *__restrict__ new_rp)
+{
+    int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r <= out) new_rp[r] = (int32_t)lower_bound_u64(newp, nnew, (uint64_t)r * (uint64_t)in);
+}
+
+// Kept entry x of row r lands after x kept entries and after the new entries
+// of earlier rows and of row r with a smaller column.
 template <typename V>
 __global__ void k_merge_kept(const int32_t *__restrict__ rows_k, const int32_t *__restrict__ cols_k,
                              const V *__restrict__ vals_k, int64_t nkept, int64_t in,
-                             const uint64_t *__restrict__ newp, int64_t nnew, int32_t *__restrict__ rows,
-                             int32_t *__restrict__ cols, V *__restrict__ vals)
+                             const uint64_t *__restrict__ newp, const int32_t *__restrict__ new_rp,
+                             int32_t *__restrict__ rows, int32_t *__restrict__ cols, V *__restrict__ vals)
 {
     int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (x >= nkept) return;
-    const uint64_t key = (uint64_t)rows_k[x] * (uint64_t)in + (uint64_t)cols_k[x];
-    const int64_t pos = x + lower_bound_u64(newp, nnew, key);
-    rows[pos] = rows_k[x];
-    cols[pos] = cols_k[x];
+    const int32_t r = rows_k[x], c = cols_k[x];
+    const int32_t a = new_rp[r], b = new_rp[r + 1];
+    const uint64_t key = (uint64_t)r * (uint64_t)in + (uint64_t)c;
+    const int64_t pos = x + a + lower_bound_u64(newp + a, b - a, key);
+    rows[pos] = r;
+    cols[pos] = c;
     vals[pos] = vals_k[x];
 }
 
@@ -402,8 +435,10 @@ csp_status restructure_v(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t 
                                : regrow<uint64_t>(L, n_prune, nkept, seed, step, s);
     if (st != CSP_OK) return st;
     if (nkept > 0) {
+        k_new_row_offsets<<<grid_for(L->out + 1), 256, 0, s>>>(W.acc_a, n_prune, L->out, L->in, W.rp_new);
+        CSP_LAUNCHED("k_new_row_offsets");
         k_merge_kept<V><<<grid_for(nkept), 256, 0, s>>>(W.rows_k, W.cols_k, (const V *)W.vals_k, nkept, L->in,
-                                                        W.acc_a, n_prune, L->rows, L->cols, (V *)L->vals);
+                                                        W.acc_a, W.rp_new, L->rows, L->cols, (V *)L->vals);
         CSP_LAUNCHED("k_merge_kept");
     }
     k_merge_new<V><<<grid_for(n_prune), 256, 0, s>>>(W.acc_a, n_prune, L->in, W.cols_k, W.rp_k, regrow_word,

@@ -120,11 +120,23 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_hist(const K *__restrict
     const int t = threadIdx.x;
     h[t] = 0;
     __syncthreads();
+    // One LDS atomic per distinct digit per wave (its lowest lane adds the
+    // count), so runs of equal digits (presorted keys) do not serialize.
     const int64_t base = (int64_t)blockIdx.x * kSortTile;
+    const int lane = t & 63;
 #pragma unroll 4
     for (int j = 0; j < kSortItemsPerLane; ++j) {
-        int64_t idx = base + (int64_t)j * kSortThreads + t;
-        if (idx < n) atomicAdd(&h[(uint32_t)(keys[idx] >> shift) & 255u], 1u);
+        const int64_t idx = base + (int64_t)j * kSortThreads + t;
+        const bool ok = idx < n;
+        const uint32_t d = ok ? (uint32_t)(keys[idx] >> shift) & 255u : 0u;
+        uint64_t m = __ballot(ok);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const bool on = (d >> bit) & 1u;
+            const uint64_t bb = __ballot(on);
+            m &= on ? bb : ~bb;
+        }
+        if (ok && (m & ((1ull << lane) - 1)) == 0) atomicAdd(&h[d], (uint32_t)__popcll(m));
     }
     __syncthreads();
     hist[(int64_t)t * ntiles + blockIdx.x] = h[t];
