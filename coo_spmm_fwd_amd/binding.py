@@ -269,8 +269,9 @@ class _DeviceArray:
 
 
 def sparse_layer_values_tensor(layer: int):
-    """Zero-copy torch view of the layer's canonical values (valid until the layer is destroyed).
-    After writing into it, call sparse_layer_set_values(layer, None)."""
+    """Zero-copy torch view of the layer's canonical values, valid until the next
+    restructure (which may move them) or the layer's destruction.  After writing
+    into it, call sparse_layer_set_values(layer, None)."""
     torch = _torch()
     _, _, dt = sparse_layer_shape(layer)
     nnz = sparse_layer_nnz(layer)

@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoospmm.so")
-SOURCES = ["layer.hip", "build.hip", "sort.hip", "spmm.hip", "restructure.hip"]
+SOURCES = ["layer.hip", "build.hip", "sort.hip", "spmm.hip", "restructure.hip", "occupancy.hip"]
 ARCH = "gfx950"
 
 
@@ -32,7 +32,7 @@ def flags() -> list[str]:
             "-fno-gpu-rdc"]
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
+def build(verbose: bool = False, jobs: int = 6) -> str:
     """Compile each source to an object (in parallel), then link the shared library."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)

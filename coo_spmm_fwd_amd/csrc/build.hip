@@ -7,6 +7,7 @@
 // contiguous segment; a second stable sort by column of the canonical indices
 // gives the column segments.  Offsets come from a binary search per segment.
 #include "common.h"
+#include "device_util.h"
 
 namespace csp {
 namespace {
@@ -65,49 +66,139 @@ __global__ void k_gather_vals(const V *__restrict__ vals, const int32_t *__restr
 
 // Tasks per segment: one for a segment of at most kTaskChunk entries (also
 // for an empty one, which still owns its zero output), else one per chunk.
-__global__ void k_seg_pieces(const int32_t *__restrict__ ptr, int64_t nseg, uint32_t *__restrict__ pieces)
+__device__ __forceinline__ uint32_t seg_pieces(const int32_t *ptr, int64_t i)
 {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nseg) return;
-    int64_t len = (int64_t)ptr[i + 1] - ptr[i];
-    pieces[i] = len <= kTaskChunk ? 1u : (uint32_t)((len + kTaskChunk - 1) / kTaskChunk);
+    const int64_t len = (int64_t)ptr[i + 1] - ptr[i];
+    return len <= kTaskChunk ? 1u : (uint32_t)((len + kTaskChunk - 1) / kTaskChunk);
 }
 
-__global__ void k_emit_tasks(const int32_t *__restrict__ ptr, const int32_t *__restrict__ first, int64_t nseg,
-                             int4 *__restrict__ desc, int64_t cap, int4 *__restrict__ split,
-                             uint32_t *__restrict__ nsplit)
+// Both task lists (rows, then columns) are built by the same three launches:
+// blocks [0, tiles0) work on list 0 and the rest on list 1, one segment per thread.
+constexpr int kTaskThreads = 1024;
+
+struct TaskBuild {
+    const int32_t *ptr[2];
+    int64_t nseg[2];
+    int64_t tiles[2];
+    int4 *desc[2];
+    int4 *split[2];
+    int32_t *seg_first[2];
+    int64_t cap[2];
+    uint32_t *partials[2];  // tiles + 1 words each
+    uint32_t *counts;       // [0], [1] tasks; [2], [3] split segments
+};
+
+__device__ __forceinline__ void task_tile(const TaskBuild &tb, int &l, int64_t &tile)
 {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nseg) return;
-    const int32_t f = first[i], p = first[i + 1] - f, b = ptr[i], e = ptr[i + 1];
-    for (int32_t j = 0; j < p && (int64_t)f + j < cap; ++j) {
+    l = (int64_t)blockIdx.x < tb.tiles[0] ? 0 : 1;
+    tile = l ? (int64_t)blockIdx.x - tb.tiles[0] : (int64_t)blockIdx.x;
+}
+
+__global__ __launch_bounds__(kTaskThreads) void k_tasks_count(TaskBuild tb)
+{
+    __shared__ uint32_t lds[17];
+    int l;
+    int64_t tile;
+    task_tile(tb, l, tile);
+    const int64_t i = tile * kTaskThreads + threadIdx.x;
+    uint32_t total;
+    block_exclusive_scan(i < tb.nseg[l] ? seg_pieces(tb.ptr[l], i) : 0u, lds, &total);
+    if (threadIdx.x == 0) tb.partials[l][tile] = total;
+    if (blockIdx.x == 0 && threadIdx.x < 2) tb.counts[2 + threadIdx.x] = 0;
+}
+
+// Two blocks: block l scans the tile sums of list l in place and stores the
+// list's task count (also as seg_first[nseg]).
+__global__ __launch_bounds__(kTaskThreads) void k_tasks_scan(TaskBuild tb)
+{
+    __shared__ uint32_t lds[17];
+    const int l = blockIdx.x;
+    uint32_t *part = tb.partials[l];
+    const int64_t nb = tb.tiles[l];
+    const int64_t per = ceil_div(nb, kTaskThreads);
+    const int64_t b0 = (int64_t)threadIdx.x * per;
+    uint32_t sum = 0;
+    for (int64_t i = b0; i < b0 + per && i < nb; ++i) sum += part[i];
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(sum, lds, &total);
+    for (int64_t i = b0; i < b0 + per && i < nb; ++i) {
+        const uint32_t v = part[i];
+        part[i] = run;
+        run += v;
+    }
+    if (threadIdx.x == 0) {
+        tb.counts[l] = total;
+        tb.seg_first[l][tb.nseg[l]] = (int32_t)total;
+    }
+}
+
+__global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
+{
+    __shared__ uint32_t lds[17];
+    int l;
+    int64_t tile;
+    task_tile(tb, l, tile);
+    const int64_t i = tile * kTaskThreads + threadIdx.x;
+    const bool live = i < tb.nseg[l];
+    const uint32_t p = live ? seg_pieces(tb.ptr[l], i) : 0u;
+    uint32_t total;
+    const int32_t f = (int32_t)(block_exclusive_scan(p, lds, &total) + tb.partials[l][tile]);
+    if (!live) return;
+    tb.seg_first[l][i] = f;
+    const int32_t b = tb.ptr[l][i], e = tb.ptr[l][i + 1];
+    for (int32_t j = 0; j < (int32_t)p && (int64_t)f + j < tb.cap[l]; ++j) {
         const int32_t kb = b + j * kTaskChunk;
         const int32_t ke = kb + kTaskChunk < e ? kb + kTaskChunk : e;
-        desc[f + j] = make_int4((int32_t)i, kb, ke, p > 1 ? f + j : -1);
+        tb.desc[l][f + j] = make_int4((int32_t)i, kb, ke, p > 1 ? f + j : -1);
     }
-    if (p > 1) split[atomicAdd(nsplit, 1u)] = make_int4((int32_t)i, f, p, 0);
+    if (p > 1) tb.split[l][atomicAdd(&tb.counts[2 + l], 1u)] = make_int4((int32_t)i, f, (int32_t)p, 0);
 }
+
+}  // namespace
 
 // seg_first[0..nseg) = exclusive scan of the per-segment task counts,
 // seg_first[nseg] = the total; then one descriptor per task and one record
 // per split segment (their order is irrelevant: each record is self-contained).
-csp_status build_tasks(TaskList &T, const int32_t *ptr, int64_t nseg, uint32_t *partials, uint32_t *nsplit,
-                       hipStream_t s)
+csp_status build_task_lists(csp_layer *L, hipStream_t s)
 {
-    const unsigned grid = (unsigned)ceil_div(nseg, 256);
-    uint32_t *first = (uint32_t *)T.seg_first;
-    k_seg_pieces<<<grid, 256, 0, s>>>(ptr, nseg, first);
-    CSP_LAUNCHED("k_seg_pieces");
-    csp_status st = exclusive_scan_u32(first, first, nseg, partials, first + nseg, s);
-    if (st != CSP_OK) return st;
-    st = fill_u32(nsplit, 0u, 1, s);
-    if (st != CSP_OK) return st;
-    k_emit_tasks<<<grid, 256, 0, s>>>(ptr, T.seg_first, nseg, T.desc, T.cap, T.split, nsplit);
-    CSP_LAUNCHED("k_emit_tasks");
+    TaskBuild tb;
+    TaskList *T[2] = {&L->row_tasks, &L->col_tasks};
+    const int32_t *ptr[2] = {L->row_ptr, L->col_ptr};
+    const int64_t nseg[2] = {L->out, L->in};
+    uint32_t *part = L->ws.hist;
+    for (int l = 0; l < 2; ++l) {
+        tb.ptr[l] = ptr[l];
+        tb.nseg[l] = nseg[l];
+        tb.tiles[l] = ceil_div(nseg[l], kTaskThreads);
+        tb.desc[l] = T[l]->desc;
+        tb.split[l] = T[l]->split;
+        tb.seg_first[l] = T[l]->seg_first;
+        tb.cap[l] = T[l]->cap;
+        tb.partials[l] = part;
+        part += tb.tiles[l] + 1;
+    }
+    tb.counts = L->ws.sel + kSelCounts;
+    const unsigned grid = (unsigned)(tb.tiles[0] + tb.tiles[1]);
+    k_tasks_count<<<grid, kTaskThreads, 0, s>>>(tb);
+    CSP_LAUNCHED("k_tasks_count");
+    k_tasks_scan<<<2, kTaskThreads, 0, s>>>(tb);
+    CSP_LAUNCHED("k_tasks_scan");
+    k_tasks_emit<<<grid, kTaskThreads, 0, s>>>(tb);
+    CSP_LAUNCHED("k_tasks_emit");
     return CSP_OK;
 }
 
-}  // namespace
+csp_status set_task_counts(csp_layer *L, const uint32_t *counts)
+{
+    L->row_tasks.count = counts[0];
+    L->col_tasks.count = counts[1];
+    L->row_tasks.nsplit = counts[2];
+    L->col_tasks.nsplit = counts[3];
+    if (L->row_tasks.count > L->row_tasks.cap || L->col_tasks.count > L->col_tasks.cap)
+        return set_error(CSP_ERR_HIP, "task list overflow (%lld/%lld, %lld/%lld)", (long long)L->row_tasks.count,
+                         (long long)L->row_tasks.cap, (long long)L->col_tasks.count, (long long)L->col_tasks.cap);
+    return CSP_OK;
+}
 
 csp_status refresh_column_values(csp_layer *L, hipStream_t s)
 {
@@ -143,26 +234,12 @@ csp_status build_index(csp_layer *L, hipStream_t s)
     st = segment_offsets((const int32_t *)L->ws.key_a, nnz, L->col_ptr, L->in, s);
     if (st != CSP_OK) return st;
 
-    // Task lists for the row-order and column-order passes (scan partials in
-    // the now free radix histogram area); the task and split counts are read back.
-    uint32_t *nsplit = L->ws.sel + 512;  // two words outside the select state
-    st = build_tasks(L->row_tasks, L->row_ptr, L->out, L->ws.hist, nsplit, s);
+    st = build_task_lists(L, s);
     if (st != CSP_OK) return st;
-    st = build_tasks(L->col_tasks, L->col_ptr, L->in, L->ws.hist, nsplit + 1, s);
-    if (st != CSP_OK) return st;
-    int32_t counts[4] = {0, 0, 0, 0};
-    CSP_HIP(hipMemcpyAsync(&counts[0], L->row_tasks.seg_first + L->out, 4, hipMemcpyDeviceToHost, s));
-    CSP_HIP(hipMemcpyAsync(&counts[1], L->col_tasks.seg_first + L->in, 4, hipMemcpyDeviceToHost, s));
-    CSP_HIP(hipMemcpyAsync(&counts[2], nsplit, 8, hipMemcpyDeviceToHost, s));
+    uint32_t counts[4] = {0, 0, 0, 0};
+    CSP_HIP(hipMemcpyAsync(counts, L->ws.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));
     CSP_HIP(hipStreamSynchronize(s));
-    L->row_tasks.count = counts[0];
-    L->col_tasks.count = counts[1];
-    L->row_tasks.nsplit = counts[2];
-    L->col_tasks.nsplit = counts[3];
-    if (L->row_tasks.count > L->row_tasks.cap || L->col_tasks.count > L->col_tasks.cap)
-        return set_error(CSP_ERR_HIP, "task list overflow (%lld/%lld, %lld/%lld)", (long long)L->row_tasks.count,
-                         (long long)L->row_tasks.cap, (long long)L->col_tasks.count, (long long)L->col_tasks.cap);
-    return CSP_OK;
+    return set_task_counts(L, counts);
 }
 
 template <typename K>

@@ -33,9 +33,21 @@ struct Workspace {
     int32_t *rp_k = nullptr;                       // out + 1: kept row offsets
     int32_t *rp_new = nullptr;                     // out + 1: row offsets of regrown positions
     uint64_t *acc_a = nullptr, *acc_b = nullptr;   // nnz: accepted regrow positions
-    uint32_t *sel = nullptr;                       // small select state / flags (256 words)
+    uint32_t *sel = nullptr;                       // kSelAllocWords: select state, flags, counts
     int64_t nkey_cap = 0;
     size_t hist_words = 0;
+    // Position bitmaps of the restructure (when they fit, see plan_bitmap):
+    // one bit per weight position, row-major, occ_row_words words per row
+    // (a multiple of 8), occ_rows rows (out padded to a multiple of 64).
+    // occ holds the current layer, occ_next is built by the restructure; each
+    // has its exclusive rank array (occ_words + 1 entries).  tcnt holds the
+    // per-column counts of the transposition tiles.
+    bool bitmap = false;
+    int64_t occ_words = 0, occ_row_words = 0, occ_rows = 0, tcnt_words = 0;
+    uint32_t *occ = nullptr, *occ_next = nullptr, *occ_pref = nullptr, *occ_pref_next = nullptr;
+    uint32_t *tcnt = nullptr;
+    uint64_t *hash = nullptr;  // hash_slots: regrow candidates by position
+    int64_t hash_slots = 0, bm_batch_cap = 0;
 };
 
 struct ActBuffer {
@@ -53,6 +65,11 @@ struct ActBuffer {
 // separate fixup launch that adds the tasks' partial sums in task order, so
 // results do not depend on scheduling and no cross-wave fence is needed.
 constexpr int kTaskChunk = 512;
+
+// Layout of the small state buffer Workspace::sel (uint32 words).
+constexpr int kSelAllocWords = 16384;
+constexpr int kSelCounts = 12288;  // [0] row tasks, [1] column tasks, [2] split rows, [3] split columns,
+                                   // [4] regrown positions taken, [5] the same before the current batch
 
 struct TaskList {
     int4 *desc = nullptr;   // [cap] {segment, first entry, end entry, partial slot or -1}
@@ -130,6 +147,8 @@ csp_status radix_sort_pairs(int key_bytes, const void *keys_in, const int32_t *v
 // Exclusive prefix sum of n uint32 (in place allowed); optional *total on device.
 csp_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *partials, uint32_t *total,
                               hipStream_t s);
+// pref[i] = number of set bits in words[0..i), for i in [0, n] (pref has n + 1 entries).
+csp_status exclusive_scan_popc(const uint32_t *words, uint32_t *pref, int64_t n, uint32_t *partials, hipStream_t s);
 // ptr[i] = first index j with sorted[j] >= i, for i in [0, nseg]  (sorted int32, length n)
 csp_status segment_offsets(const int32_t *sorted, int64_t n, int32_t *ptr, int64_t nseg, hipStream_t s);
 csp_status fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s);
@@ -144,6 +163,11 @@ csp_status build_canonical(csp_layer *L, const int32_t *rows, const int32_t *col
 // Rebuilds row_ptr, perm_c, rows_by_col, col_ptr, vals_c and both task lists
 // from the canonical arrays.  Synchronizes on s (reads back the task counts).
 csp_status build_index(csp_layer *L, hipStream_t s);
+// Both task lists from row_ptr / col_ptr (three launches, no host sync); the
+// counts land in sel[kSelCounts + 0..3] for set_task_counts.
+csp_status build_task_lists(csp_layer *L, hipStream_t s);
+// Takes the counts read back from sel[kSelCounts + 0..3]; checks the capacities.
+csp_status set_task_counts(csp_layer *L, const uint32_t *counts);
 // vals_c[j] = vals[perm_c[j]] after the canonical values changed.
 csp_status refresh_column_values(csp_layer *L, hipStream_t s);
 inline int64_t task_cap(int64_t nseg, int64_t nnz) { return nseg + (nnz + kTaskChunk - 1) / kTaskChunk; }
@@ -159,6 +183,14 @@ csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, vo
 // ---------------------------------------------------------------------------
 // restructure.hip
 // ---------------------------------------------------------------------------
+// occupancy.hip: chooses the bitmap restructure for this shape (fills the
+// Workspace sizes, allocates nothing); scratch words it needs in hist; sets
+// the row-major bitmap from the canonical arrays; the restructure itself.
+bool plan_bitmap(csp_layer *L);
+size_t bitmap_hist_words(const csp_layer *L);
+csp_status occupancy_init(csp_layer *L, hipStream_t s);
+csp_status restructure_bitmap(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,
+                              hipStream_t s);
 csp_status run_restructure(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,
                            hipStream_t s);
 int64_t regrow_batch_cap(const csp_layer *L);

@@ -68,6 +68,7 @@ void free_layer(csp_layer *L)
     void *ptrs[] = {L->rows, L->cols, L->vals, L->row_ptr, L->perm_c, L->rows_by_col, L->col_ptr, L->vals_c,
                     L->ws.key_a, L->ws.key_b, L->ws.idx_a, L->ws.idx_b, L->ws.u_a, L->ws.u_b, L->ws.hist,
                     L->ws.rows_k, L->ws.cols_k, L->ws.vals_k, L->ws.rp_k, L->ws.rp_new, L->ws.acc_a, L->ws.acc_b, L->ws.sel,
+                    L->ws.occ, L->ws.occ_next, L->ws.occ_pref, L->ws.occ_pref_next, L->ws.tcnt, L->ws.hash,
                     L->act.a, L->act.b, L->act.partial,
                     L->row_tasks.desc, L->row_tasks.split, L->row_tasks.seg_first,
                     L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first};
@@ -84,7 +85,9 @@ csp_status alloc_layer(csp_layer *L)
     W.nkey_cap = nnz > 65536 ? nnz : 65536;
     W.hist_words = sort_hist_words(W.nkey_cap);
     const int64_t nseg_max = out > in ? out : in;
-    if (W.hist_words < (size_t)(ceil_div(nseg_max, 4096) + 64)) W.hist_words = (size_t)(ceil_div(nseg_max, 4096) + 64);
+    if (W.hist_words < (size_t)(2 * ceil_div(nseg_max, 1024) + 64)) W.hist_words = (size_t)(2 * ceil_div(nseg_max, 1024) + 64);
+    const bool bitmap = plan_bitmap(L);
+    if (bitmap && W.hist_words < bitmap_hist_words(L)) W.hist_words = bitmap_hist_words(L);
     const size_t cap = (size_t)W.nkey_cap;
     L->row_tasks.cap = task_cap(out, nnz);
     L->col_tasks.cap = task_cap(in, nnz);
@@ -111,7 +114,7 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&W.rp_new, 4 * (size_t)(out + 1), "regrown offsets"},
         {(void **)&W.acc_a, 8 * n, "regrow positions"},
         {(void **)&W.acc_b, 8 * n, "regrow positions"},
-        {(void **)&W.sel, 4 * 1024, "select state"},
+        {(void **)&W.sel, 4 * (size_t)kSelAllocWords, "select state"},
         {(void **)&L->row_tasks.desc, 16 * (size_t)L->row_tasks.cap, "row tasks"},
         {(void **)&L->row_tasks.split, 16 * (size_t)out, "split rows"},
         {(void **)&L->row_tasks.seg_first, 4 * (size_t)(out + 1), "row task offsets"},
@@ -120,6 +123,19 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&L->col_tasks.seg_first, 4 * (size_t)(in + 1), "column task offsets"},
     };
     for (auto &r : reqs) {
+        csp_status st = dalloc(r.p, r.bytes, r.what);
+        if (st != CSP_OK) return st;
+    }
+    if (!bitmap) return CSP_OK;
+    Req breqs[] = {
+        {(void **)&W.occ, 4 * (size_t)W.occ_words, "position bitmap"},
+        {(void **)&W.occ_next, 4 * (size_t)W.occ_words, "position bitmap"},
+        {(void **)&W.occ_pref, 4 * (size_t)(W.occ_words + 1), "bitmap ranks"},
+        {(void **)&W.occ_pref_next, 4 * (size_t)(W.occ_words + 1), "bitmap ranks"},
+        {(void **)&W.tcnt, 4 * (size_t)W.tcnt_words, "transposition counts"},
+        {(void **)&W.hash, 8 * (size_t)W.hash_slots, "regrow hash table"},
+    };
+    for (auto &r : breqs) {
         csp_status st = dalloc(r.p, r.bytes, r.what);
         if (st != CSP_OK) return st;
     }
@@ -169,9 +185,10 @@ csp_status sparse_layer_create(int64_t out_features, int64_t in_features, int64_
     }
     hipStream_t s = (hipStream_t)stream;
     csp_status st = alloc_layer(L);
-    if (st == CSP_OK) st = fill_u32(L->ws.sel, 0u, 1024, s);
+    if (st == CSP_OK) st = fill_u32(L->ws.sel, 0u, kSelAllocWords, s);
     if (st == CSP_OK) st = build_canonical(L, rows, cols, vals, L->ws.sel, s);
     if (st == CSP_OK) st = build_index(L, s);
+    if (st == CSP_OK) st = occupancy_init(L, s);
     uint32_t flags = 0;
     if (st == CSP_OK) {
         hipError_t e = hipMemcpyAsync(&flags, L->ws.sel, sizeof flags, hipMemcpyDeviceToHost, s);

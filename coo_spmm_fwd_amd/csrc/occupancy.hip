@@ -1,0 +1,787 @@
+// occupancy.hip -- prune-and-regrow through position bitmaps ("Beyond Masked
+// Sparsity: SNACK ...", Abstract: connections of the truly sparse layer are
+// restructured during dynamic sparse training while only the stored entries
+// are kept).
+//
+// The layer keeps one bit per weight position, row-major with rows padded to
+// a multiple of 8 words, plus the exclusive rank of every word (set bits
+// before it), as long as that costs at most 1 GiB and out*in < 2^32.  The
+// rule is the one of the sorted path (prune order and regrow stream in
+// regrow.h); what changes is how it is evaluated:
+//  1. prune threshold: a radix select over the magnitude keys, 8 bits per
+//     pass; each pass's blocks redo the digit choice of the earlier passes
+//     from their histograms (eight spread copies, so the hot bins of the top
+//     digit do not serialize the global atomics);
+//  2. prune: per 4096-entry tile, counts of keys below / equal to the
+//     threshold, one block scans them, then every entry knows whether it goes
+//     (a bit per canonical index); the next bitmap is the current one without
+//     those bits (one thread per word: its bits are consecutive entries);
+//  3. regrow: a batch of the stream's candidates is tested against the next
+//     bitmap; a hash table keyed by position keeps the smallest candidate
+//     index per position, so "first occurrence and empty" is a flag per
+//     candidate; a scan over the flags in stream order ranks them and the
+//     first n_prune (minus those taken by earlier batches) set their bit;
+//  4. rebuild: a scan of the next bitmap's bit counts gives every position
+//     its canonical index; one thread per word writes its entries in order,
+//     a kept one with the value at its old index (old bitmap and ranks), a
+//     new one with the regrow value.  The transposed view comes from tiles
+//     of 256 x 256 positions, one wave each: a ballot per column over the
+//     tile's rows gives that column's entries in row order, so with the
+//     scanned per-tile column counts every entry knows its transposed rank;
+//     the task lists follow.
+// Every pass reads or writes whole arrays in order; the only scattered
+// traffic is the candidates' bitmap and hash probes.  The host reads back
+// once at the end (taken count and task counts); only if the first batch fell
+// short does it run further batches and rebuild again.
+#include <cstdlib>
+#include <cstring>
+#include <utility>
+
+#include "common.h"
+#include "device_util.h"
+#include "regrow.h"
+
+namespace csp {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 4096;            // entries per block in the ranked passes
+constexpr int kWaveItems = kTile / 4;  // 1024 consecutive entries per wave, 16 rounds of 64
+constexpr int kCopies = 8;             // spread copies of each select histogram
+constexpr int kHistWords = 256 * kCopies;
+constexpr int kMaxPasses = 4;
+constexpr int kSelT = kMaxPasses * kHistWords;  // threshold key
+constexpr int kSelNeedEq = kSelT + 1;           // entries equal to the threshold that go
+constexpr uint32_t kNoPos = 0xFFFFFFFFu;
+constexpr uint64_t kEmptySlot = ~0ull;
+constexpr int64_t kBatchLimit = int64_t(1) << 21;  // candidates per regrow batch
+constexpr size_t kBitmapBytesLimit = size_t(1) << 30;
+
+static_assert(kSelNeedEq < kSelCounts, "select state overlaps the counts");
+
+// ------------------------------------------------------------ prune threshold
+// One full wave: the digit whose bin holds the need-th entry (1-based) of the
+// histogram h (kCopies copies of 256 bins), and how many entries precede it.
+__device__ inline void pick_digit(const uint32_t *h, uint32_t need, uint32_t &digit, uint32_t &before)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+    for (int k = 0; k < kCopies; ++k) {
+        const uint4 v = *(const uint4 *)(h + k * 256 + lane * 4);
+        c0 += v.x;
+        c1 += v.y;
+        c2 += v.z;
+        c3 += v.w;
+    }
+    const uint32_t own = c0 + c1 + c2 + c3;
+    uint32_t incl = own;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    const uint64_t hit = __ballot(incl >= need);
+    const int L = hit ? __ffsll((unsigned long long)hit) - 1 : 63;
+    uint32_t run = __shfl(incl - own, L, 64);
+    const uint32_t b0 = __shfl(c0, L, 64), b1 = __shfl(c1, L, 64), b2 = __shfl(c2, L, 64);
+    uint32_t d = 4 * L + 3;
+    if (run + b0 >= need) {
+        d = 4 * L;
+    } else {
+        run += b0;
+        if (run + b1 >= need) {
+            d = 4 * L + 1;
+        } else {
+            run += b1;
+            if (run + b2 >= need) d = 4 * L + 2;
+            else run += b2;
+        }
+    }
+    digit = d;
+    before = run;
+}
+
+// One full wave: prefix and mask of the digits fixed by passes [0, npass).
+__device__ inline void select_state(const uint32_t *sel, int npass, int top, uint32_t n_prune, uint32_t &prefix,
+                                    uint32_t &mask, uint32_t &need)
+{
+    prefix = 0;
+    mask = 0;
+    need = n_prune;
+    for (int p = 0; p < npass; ++p) {
+        uint32_t d, before;
+        pick_digit(sel + p * kHistWords, need, d, before);
+        const int shift = top - 8 * p;
+        prefix |= d << shift;
+        mask |= 255u << shift;
+        need -= before;
+    }
+}
+
+// Histogram pass `pass` of the radix select; pass 0 also fills `clear`
+// (the regrow hash table) with empty slots.  Few fat blocks: every block adds
+// its nonzero bins to the global histogram with one atomic each.  Lanes that
+// hit the same bin serialize on the LDS atomic, which costs less than
+// matching digits across the wave first.
+constexpr int kHistThreads = 1024;
+
+template <typename V>
+__global__ __launch_bounds__(kHistThreads) void k_bm_hist(const V *__restrict__ vals, int64_t n, int pass, int top,
+                                                          uint32_t n_prune, uint32_t *sel,
+                                                          uint64_t *__restrict__ clear, int64_t nclear)
+{
+    __shared__ uint32_t h[256];
+    __shared__ uint32_t state[2];
+    const int t = threadIdx.x;
+    if (t < 256) h[t] = 0;
+    if (t < 64) {
+        uint32_t prefix, mask, need;
+        select_state(sel, pass, top, n_prune, prefix, mask, need);
+        if (t == 0) {
+            state[0] = prefix;
+            state[1] = mask;
+        }
+    }
+    const int64_t stride = (int64_t)gridDim.x * kHistThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kHistThreads + t; i < nclear; i += stride) clear[i] = kEmptySlot;
+    __syncthreads();
+    const uint32_t prefix = state[0], mask = state[1];
+    const int shift = top - 8 * pass;
+    constexpr int U = 8;
+    for (int64_t base = (int64_t)blockIdx.x * (kHistThreads * U); base < n; base += stride * U) {
+        uint32_t key[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = base + u * kHistThreads + t;
+            key[u] = mag_key<V>(load_or_first(vals, k, n));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * kHistThreads + t < n && (key[u] & mask) == prefix) atomicAdd(&h[(key[u] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (t < 256 && h[t]) atomicAdd(&sel[pass * kHistWords + (blockIdx.x & (kCopies - 1)) * 256 + t], h[t]);
+}
+
+__global__ __launch_bounds__(64) void k_bm_sel_final(uint32_t *sel, uint32_t n_prune, int passes, int top)
+{
+    uint32_t prefix, mask, need;
+    select_state(sel, passes, top, n_prune, prefix, mask, need);
+    if (threadIdx.x == 0) {
+        sel[kSelT] = prefix;
+        sel[kSelNeedEq] = need;
+    }
+}
+
+// ---------------------------------------------------------------------- prune
+// Per tile: entries with key below the threshold, and equal to it.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void k_bm_prune_count(const V *__restrict__ vals, int64_t n,
+                                                             const uint32_t *__restrict__ sel,
+                                                             uint32_t *__restrict__ tiles)
+{
+    __shared__ uint32_t part[2][4];
+    const uint32_t T = sel[kSelT];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int64_t base = (int64_t)blockIdx.x * kTile;
+    uint32_t lt = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < kTile / kThreads; ++u) {
+        const int64_t k = base + u * kThreads + t;
+        const uint32_t key = mag_key<V>(load_or_first(vals, k, n));
+        lt += k < n && key < T;
+        eq += k < n && key == T;
+    }
+    lt = wave_sum(lt);
+    eq = wave_sum(eq);
+    if (lane == 0) {
+        part[0][w] = lt;
+        part[1][w] = eq;
+    }
+    __syncthreads();
+    if (t == 0) {
+        tiles[2 * blockIdx.x] = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+        tiles[2 * blockIdx.x + 1] = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+    }
+}
+
+// One block of 1024: exclusive scans (in place) of the interleaved per-tile
+// counts; clears the regrow counters.
+__global__ __launch_bounds__(1024) void k_bm_prune_scan(uint32_t *tiles, int64_t nt, uint32_t *sel)
+{
+    __shared__ uint32_t lds[17];
+    const int64_t per = ceil_div(nt, 1024), b0 = (int64_t)threadIdx.x * per;
+    for (int c = 0; c < 2; ++c) {
+        uint32_t sum = 0;
+        for (int64_t i = b0; i < b0 + per && i < nt; ++i) sum += tiles[2 * i + c];
+        uint32_t total;
+        uint32_t run = block_exclusive_scan(sum, lds, &total);
+        for (int64_t i = b0; i < b0 + per && i < nt; ++i) {
+            const uint32_t v = tiles[2 * i + c];
+            tiles[2 * i + c] = run;
+            run += v;
+        }
+    }
+    if (threadIdx.x == 0) {
+        sel[kSelCounts + 4] = 0;
+        sel[kSelCounts + 5] = 0;
+    }
+}
+
+// Entry k goes if its key is below the threshold, or equal to it and fewer
+// than need_eq equal keys precede it; the pruned ones are marked in a bit
+// mask, one bit per canonical index.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void k_bm_prune_mark(const V *__restrict__ vals, int64_t n,
+                                                            const uint32_t *__restrict__ sel,
+                                                            const uint32_t *__restrict__ tiles,
+                                                            uint64_t *__restrict__ pruned)
+{
+    constexpr int R = kWaveItems / kWave;
+    __shared__ uint32_t we[4];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const uint32_t T = sel[kSelT], need_eq = sel[kSelNeedEq];
+    const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)w * kWaveItems;
+    uint32_t key[R];
+    uint32_t eq_w = 0;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t k = base + j * kWave + lane;
+        key[j] = mag_key<V>(load_or_first(vals, k, n));
+        eq_w += (uint32_t)__popcll(__ballot(k < n && key[j] == T));
+    }
+    if (lane == 0) we[w] = eq_w;
+    __syncthreads();
+    uint32_t eq_run = tiles[2 * blockIdx.x + 1];
+    for (int i = 0; i < w; ++i) eq_run += we[i];
+    const uint64_t below = lanes_below();
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const int64_t k = base + j * kWave + lane;
+        const bool valid = k < n;
+        const bool eq = valid && key[j] == T;
+        const uint64_t eqm = __ballot(eq);
+        const uint32_t eqb = eq_run + (uint32_t)__popcll(eqm & below);
+        const uint64_t gm = __ballot((valid && key[j] < T) || (eq && eqb < need_eq));
+        if (lane == 0 && base + j * kWave < n) pruned[(base + j * kWave) >> 6] = gm;
+        eq_run += (uint32_t)__popcll(eqm);
+    }
+}
+
+// One thread per row-major bitmap word: its set bits are canonical entries
+// pref[w], pref[w] + 1, ...; the next bitmap keeps the ones not pruned.
+__global__ __launch_bounds__(kThreads) void k_bm_occ_prune(const uint32_t *__restrict__ occ,
+                                                           const uint32_t *__restrict__ pref, int64_t nw,
+                                                           const uint64_t *__restrict__ pruned,
+                                                           uint32_t *__restrict__ occ_next)
+{
+    const int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (w >= nw) return;
+    const uint32_t o = occ[w];
+    uint32_t k = pref[w], keep = o;
+    for (uint32_t m = o; m; m &= m - 1, ++k)
+        if ((pruned[k >> 6] >> (k & 63)) & 1ull) keep &= ~(m & (0u - m));
+    occ_next[w] = keep;
+}
+
+// --------------------------------------------------------------------- regrow
+__device__ __forceinline__ uint64_t hash_home(uint32_t p, int hbits)
+{
+    return ((uint64_t)p * 0x9E3779B97F4A7C15ull) >> (64 - hbits);
+}
+
+// Slot entry: position in the high word, candidate index in the low word; a
+// slot keeps the smallest index seen for its position (same high word, so
+// the 64-bit minimum is the minimum index).  Linear probing; the table has at
+// least twice as many slots as candidates, so a free slot always exists.
+__device__ inline void hash_insert(uint64_t *tab, int hbits, uint32_t p, uint32_t j)
+{
+    const uint64_t mask = (1ull << hbits) - 1, entry = ((uint64_t)p << 32) | j;
+    uint64_t s = hash_home(p, hbits);
+    for (uint64_t probe = 0; probe <= mask; ++probe, s = (s + 1) & mask) {
+        const uint64_t old = atomicCAS((unsigned long long *)&tab[s], kEmptySlot, entry);
+        if (old == kEmptySlot) return;
+        if ((uint32_t)(old >> 32) == p) {
+            atomicMin((unsigned long long *)&tab[s], (unsigned long long)entry);
+            return;
+        }
+    }
+}
+
+__device__ inline uint32_t hash_first(const uint64_t *tab, int hbits, uint32_t p)
+{
+    const uint64_t mask = (1ull << hbits) - 1;
+    uint64_t s = hash_home(p, hbits);
+    for (uint64_t probe = 0; probe <= mask; ++probe, s = (s + 1) & mask) {
+        const uint64_t e = tab[s];
+        if (e == kEmptySlot) return kNoPos;
+        if ((uint32_t)(e >> 32) == p) return (uint32_t)e;
+    }
+    return kNoPos;
+}
+
+// Candidates [i0, i0 + M) of the stream: occupied positions drop out, the
+// others enter the hash table.  Block 0 also clears the select histograms
+// for the next restructure.
+__global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint64_t step, uint64_t i0, int64_t M,
+                                                             int64_t in, uint64_t npos, const uint32_t *occ,
+                                                             int64_t inw, uint32_t *__restrict__ cand, uint64_t *tab,
+                                                             int hbits, uint32_t *sel)
+{
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < kMaxPasses * kHistWords; i += kThreads) sel[i] = 0;
+    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (j >= M) return;
+    const uint64_t p = regrow_position(seed, step, i0 + (uint64_t)j, npos);
+    const int64_t r = (int64_t)(p / (uint64_t)in), c = (int64_t)p - r * in;
+    const bool taken = (occ[r * inw + (c >> 5)] >> (c & 31)) & 1u;
+    cand[j] = taken ? kNoPos : (uint32_t)p;
+    if (!taken) hash_insert(tab, hbits, (uint32_t)p, (uint32_t)j);
+}
+
+// flag[j] = candidate j is empty and the first of its position in the batch;
+// one bit per candidate (a word per wave), and the count per block.
+__global__ __launch_bounds__(kThreads) void k_bm_cand_count(const uint32_t *__restrict__ cand, int64_t M,
+                                                            const uint64_t *__restrict__ tab, int hbits,
+                                                            uint64_t *__restrict__ flags,
+                                                            uint32_t *__restrict__ tile_cnt)
+{
+    __shared__ uint32_t part[4];
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int64_t j = (int64_t)blockIdx.x * kThreads + t;
+    bool f = false;
+    if (j < M) {
+        const uint32_t p = cand[j];
+        f = p != kNoPos && hash_first(tab, hbits, p) == (uint32_t)j;
+    }
+    const uint64_t m = __ballot(f);
+    if (lane == 0) {
+        if (j < M) flags[j >> 6] = m;
+        part[w] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    if (t == 0) tile_cnt[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
+// One block of 1024: exclusive scan of the block counts; the batch takes
+// min(flags, still needed) and the running total advances.
+__global__ __launch_bounds__(1024) void k_bm_cand_scan(uint32_t *tile_cnt, int64_t nt, uint32_t n_prune,
+                                                       uint32_t *sel)
+{
+    __shared__ uint32_t lds[17];
+    const int64_t per = ceil_div(nt, 1024), b0 = (int64_t)threadIdx.x * per;
+    uint32_t sum = 0;
+    for (int64_t i = b0; i < b0 + per && i < nt; ++i) sum += tile_cnt[i];
+    uint32_t total;
+    uint32_t run = block_exclusive_scan(sum, lds, &total);
+    for (int64_t i = b0; i < b0 + per && i < nt; ++i) {
+        const uint32_t v = tile_cnt[i];
+        tile_cnt[i] = run;
+        run += v;
+    }
+    if (threadIdx.x == 0) {
+        const uint32_t nacc = sel[kSelCounts + 4], need = n_prune - nacc;
+        sel[kSelCounts + 5] = nacc;
+        sel[kSelCounts + 4] = nacc + (total < need ? total : need);
+    }
+}
+
+// Flagged candidates ranked in stream order; those below the still-needed
+// count are taken: their bit is set in the next bitmap.
+__global__ __launch_bounds__(kThreads) void k_bm_cand_take(const uint32_t *__restrict__ cand, int64_t M,
+                                                           const uint64_t *__restrict__ flags,
+                                                           const uint32_t *__restrict__ tile_pre,
+                                                           const uint32_t *__restrict__ sel, uint32_t n_prune,
+                                                           int64_t in, uint32_t *occ, int64_t inw)
+{
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+    const int64_t j = (int64_t)blockIdx.x * kThreads + t;
+    if (j >= M) return;
+    const int64_t q0 = (int64_t)blockIdx.x * (kThreads / 64);
+    uint32_t rank = tile_pre[blockIdx.x];
+    for (int i = 0; i < w; ++i) rank += (uint32_t)__popcll(flags[q0 + i]);
+    const uint64_t fw = flags[j >> 6];
+    if (!((fw >> lane) & 1ull)) return;
+    rank += (uint32_t)__popcll(fw & lanes_below());
+    const uint32_t prev = sel[kSelCounts + 5];
+    if (rank >= n_prune - prev) return;
+    const uint32_t p = cand[j];
+    const int64_t r = (int64_t)(p / (uint64_t)in), c = (int64_t)p - r * in;
+    atomicOr(&occ[r * inw + (c >> 5)], 1u << (c & 31));
+}
+
+// -------------------------------------------------------------------- rebuild
+// Canonical arrays from the next bitmap, one thread per word (its set bits
+// are consecutive canonical indices from pref[w] on).  A position that was
+// occupied before and not pruned keeps its value, read at its old canonical
+// index; any other (regrown, also a just-pruned one) gets the regrow value.
+// The thread of a row's first word also writes row_ptr.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void k_bm_canon(const uint32_t *__restrict__ occ,
+                                                       const uint32_t *__restrict__ pref,
+                                                       const uint32_t *__restrict__ occ_old,
+                                                       const uint32_t *__restrict__ pref_old,
+                                                       const uint64_t *__restrict__ pruned,
+                                                       const V *__restrict__ vals_old, V regrow, uint32_t nw,
+                                                       uint32_t inw, int64_t out, int32_t *__restrict__ rows,
+                                                       int32_t *__restrict__ cols, V *__restrict__ vals,
+                                                       int32_t *__restrict__ row_ptr)
+{
+    const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
+    if (w > nw) return;
+    const uint32_t r = w / inw, cw = w - r * inw;
+    uint32_t pos = pref[w];
+    if (cw == 0 && r <= out) row_ptr[r] = (int32_t)pos;
+    if (w == nw) return;
+    const uint32_t o = occ[w], oo = occ_old[w], ko = pref_old[w];
+    for (uint32_t m = o; m; m &= m - 1, ++pos) {
+        const int b = __ffs(m) - 1;
+        V v = regrow;
+        if ((oo >> b) & 1u) {
+            const uint32_t k = ko + __popc(oo & ((1u << b) - 1u));
+            if (!((pruned[k >> 6] >> (k & 63)) & 1ull)) v = vals_old[k];
+        }
+        rows[pos] = (int32_t)r;
+        cols[pos] = (int32_t)(cw * 32 + b);
+        vals[pos] = v;
+    }
+}
+
+// The transposed view is built in tiles of 1024 rows x 64 columns (two
+// bitmap words per row), one wave each.  Each 64-row slice of a tile's words
+// is turned into column words by 32 x 32 bit transposes across the lanes, so
+// a column's entries in row order are the set bits of its 32 column words.
+constexpr int kTR = 1024, kTC = 64, kTSlices = kTR / 64;
+
+__device__ __forceinline__ uint2 tile_row_words(const uint32_t *__restrict__ occ, int64_t r, int64_t rows_alloc,
+                                                int64_t inw, int64_t cg)
+{
+    const bool ok = r < rows_alloc;
+    const uint2 w = *(const uint2 *)(occ + (ok ? r : 0) * inw + 2 * cg);
+    return ok ? w : make_uint2(0u, 0u);
+}
+
+// Entries per column within each 1024-row chunk: tcnt[c * nrc + chunk].
+__global__ __launch_bounds__(kThreads) void k_bm_tcount(const uint32_t *__restrict__ occ, int64_t inw,
+                                                        int64_t rows_alloc, int64_t nrc, int64_t ncg,
+                                                        uint32_t *__restrict__ tcnt)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wave >= nrc * ncg) return;
+    const int64_t rc = wave % nrc, cg = wave / nrc;
+    uint2 w[kTSlices];
+#pragma unroll
+    for (int sl = 0; sl < kTSlices; ++sl) w[sl] = tile_row_words(occ, rc * kTR + sl * 64 + lane, rows_alloc, inw, cg);
+    uint32_t c0 = 0, c1 = 0;  // lane i: columns i & 31 and 32 + (i & 31), rows of its half-slice
+#pragma unroll
+    for (int sl = 0; sl < kTSlices; ++sl) {
+        if (__ballot((w[sl].x | w[sl].y) != 0u) == 0) continue;
+        c0 += (uint32_t)__popc(transpose32(w[sl].x));
+        c1 += (uint32_t)__popc(transpose32(w[sl].y));
+    }
+    c0 += __shfl_xor(c0, 32, 64);
+    c1 += __shfl_xor(c1, 32, 64);
+    if (lane < 32) {
+        tcnt[(cg * kTC + lane) * nrc + rc] = c0;
+        tcnt[(cg * kTC + 32 + lane) * nrc + rc] = c1;
+    }
+}
+
+// Transposed view, one wave per tile: the tile's output is, per column, a
+// run of consecutive transposed ranks from tscan[c * nrc + rc] (exclusive
+// scan of tcnt).  Lanes walk the tile's entries in that order, so stores are
+// coalesced: output o -> column (search in the column starts) -> row (search
+// in the column's cumulative word counts, then the bit) -> canonical index
+// (the row's first entry in the tile plus its entries to the left).  rc = 0
+// also writes col_ptr.
+template <typename V>
+__global__ __launch_bounds__(64) void k_bm_tgather(const uint32_t *__restrict__ occ,
+                                                   const uint32_t *__restrict__ pref, int64_t inw, int64_t rows_alloc,
+                                                   int64_t nrc, int64_t in, const uint32_t *__restrict__ tscan,
+                                                   const V *__restrict__ vals, int32_t *__restrict__ perm_c,
+                                                   int32_t *__restrict__ rows_by_col, V *__restrict__ vals_c,
+                                                   int32_t *__restrict__ col_ptr)
+{
+    __shared__ uint2 rw[kTR];                     // row words
+    __shared__ uint32_t seg[kTR];                 // canonical index of the row's first entry in the tile
+    __shared__ uint32_t cw[kTC][kTR / 32 + 1];    // column words (padded against bank conflicts)
+    __shared__ uint16_t ccum[kTC][kTR / 32 + 1];  // set bits in the column's earlier words
+    __shared__ uint32_t cstart[kTC + 1];          // tile-local start of each column's run
+    __shared__ uint32_t gout[kTC];                // transposed rank of each run's first entry
+    const int lane = threadIdx.x;
+    const int64_t rc = blockIdx.x % nrc, cg = blockIdx.x / nrc, r0 = rc * kTR;
+#pragma unroll
+    for (int sl = 0; sl < kTSlices; ++sl) {
+        const int64_t r = r0 + sl * 64 + lane;
+        const uint2 w = tile_row_words(occ, r, rows_alloc, inw, cg);
+        rw[sl * 64 + lane] = w;
+        seg[sl * 64 + lane] = pref[(r < rows_alloc ? r : 0) * inw + 2 * cg];
+        cw[lane & 31][2 * sl + (lane >> 5)] = transpose32(w.x);
+        cw[32 + (lane & 31)][2 * sl + (lane >> 5)] = transpose32(w.y);
+    }
+    __syncthreads();
+    uint32_t run = 0;  // lane = column
+    for (int b = 0; b < kTR / 32; ++b) {
+        ccum[lane][b] = (uint16_t)run;
+        run += (uint32_t)__popc(cw[lane][b]);
+    }
+    uint32_t incl = run;  // scan of the column counts over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    const uint32_t total = __shfl(incl, 63, 64);
+    cstart[lane] = incl - run;
+    if (lane == 0) cstart[kTC] = total;
+    const int64_t c_glob = cg * kTC + lane;
+    gout[lane] = tscan[c_glob * nrc + rc];
+    if (rc == 0 && c_glob < in) col_ptr[c_glob] = (int32_t)gout[lane];
+    __syncthreads();
+    constexpr int U = 4;  // outputs in flight per lane
+    for (uint32_t o0 = 0; o0 < total; o0 += 64 * U) {
+        int32_t kk[U], rr[U];
+        uint32_t jj[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t o = o0 + u * 64 + lane;
+            int c = 0;  // last column whose run starts at or before o
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1)
+                if (cstart[c + step] <= o) c += step;
+            const uint32_t q = o < total ? o - cstart[c] : 0u;
+            int b = 0;  // column word holding the q-th entry
+#pragma unroll
+            for (int step = 16; step >= 1; step >>= 1)
+                if (ccum[c][b + step] <= q) b += step;
+            const int ro = b * 32 + nth_set_bit(cw[c][b], q - ccum[c][b]);
+            const uint2 w = rw[ro];
+            const uint32_t left = c < 32 ? (uint32_t)__popc(w.x & ((1u << c) - 1u))
+                                         : (uint32_t)__popc(w.x) + (uint32_t)__popc(w.y & ((1u << (c - 32)) - 1u));
+            kk[u] = o < total ? (int32_t)(seg[ro] + left) : -1;
+            rr[u] = (int32_t)(r0 + ro);
+            jj[u] = gout[c] + q;
+        }
+        V vv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) vv[u] = vals[kk[u] >= 0 ? kk[u] : 0];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (kk[u] >= 0) {
+                perm_c[jj[u]] = kk[u];
+                rows_by_col[jj[u]] = rr[u];
+                vals_c[jj[u]] = vv[u];
+            }
+    }
+}
+
+__global__ void k_bm_occ_set(const int32_t *__restrict__ rows, const int32_t *__restrict__ cols, int64_t n,
+                             uint32_t *occ, int64_t inw)
+{
+    const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= n) return;
+    const int32_t r = rows[k], c = cols[k];
+    atomicOr(&occ[(int64_t)r * inw + (c >> 5)], 1u << (c & 31));
+}
+
+inline unsigned blocks_for(int64_t items, int64_t per_block) { return (unsigned)ceil_div(items, per_block); }
+
+int hash_bits_for(int64_t M)  // smallest b with 2^b >= 2M
+{
+    const int b = bits_for((uint64_t)(2 * M - 1));
+    return b < 1 ? 1 : b;
+}
+
+template <typename V>
+struct BitmapRun {
+    csp_layer *L;
+    int64_t n_prune;
+    uint64_t seed, step, npos;
+    V regrow;
+    hipStream_t s;
+    uint64_t i0 = 0;
+    int64_t nacc = 0;
+
+    int64_t batch_size(int64_t cap) const
+    {
+        const int64_t need = n_prune - nacc, nkept = L->nnz - n_prune;
+        const double free_frac = (double)(npos - (uint64_t)nkept - (uint64_t)nacc) / (double)npos;
+        const double want = (double)need / free_frac * 1.1 + 1024.0;
+        int64_t M = want > (double)cap ? cap : (int64_t)want;
+        return M < 1 ? 1 : M;
+    }
+
+    csp_status batch(int64_t M, int hb)
+    {
+        Workspace &W = L->ws;
+        const unsigned nt = blocks_for(M, kThreads);
+        k_bm_cand_insert<<<nt, kThreads, 0, s>>>(seed, step, i0, M, L->in, npos, W.occ_next, W.occ_row_words, W.u_a,
+                                                 W.hash, hb, W.sel);
+        CSP_LAUNCHED("k_bm_cand_insert");
+        k_bm_cand_count<<<nt, kThreads, 0, s>>>(W.u_a, M, W.hash, hb, (uint64_t *)W.u_b, W.hist);
+        CSP_LAUNCHED("k_bm_cand_count");
+        k_bm_cand_scan<<<1, 1024, 0, s>>>(W.hist, nt, (uint32_t)n_prune, W.sel);
+        CSP_LAUNCHED("k_bm_cand_scan");
+        k_bm_cand_take<<<nt, kThreads, 0, s>>>(W.u_a, M, (const uint64_t *)W.u_b, W.hist, W.sel, (uint32_t)n_prune,
+                                               L->in, W.occ_next, W.occ_row_words);
+        CSP_LAUNCHED("k_bm_cand_take");
+        i0 += (uint64_t)M;
+        return CSP_OK;
+    }
+
+    // Canonical arrays (staged), transposed view and offsets from the next
+    // bitmap, task lists; reads back the counts.
+    csp_status rebuild()
+    {
+        Workspace &W = L->ws;
+        const int64_t nw = W.occ_words, inw = W.occ_row_words, rows_alloc = W.occ_rows;
+        const int64_t nrc = ceil_div(rows_alloc, kTR), ncg = inw / 2, ntiles = nrc * ncg;
+        csp_status st = exclusive_scan_popc(W.occ_next, W.occ_pref_next, nw, W.hist, s);
+        if (st != CSP_OK) return st;
+        k_bm_canon<V><<<blocks_for(nw + 1, kThreads), kThreads, 0, s>>>(
+            W.occ_next, W.occ_pref_next, W.occ, W.occ_pref, (const uint64_t *)W.acc_b, (const V *)L->vals, regrow,
+            (uint32_t)nw, (uint32_t)inw, L->out, W.rows_k, W.cols_k, (V *)W.vals_k, L->row_ptr);
+        CSP_LAUNCHED("k_bm_canon");
+        k_bm_tcount<<<blocks_for(ntiles, 4), kThreads, 0, s>>>(W.occ_next, inw, rows_alloc, nrc, ncg, W.tcnt);
+        CSP_LAUNCHED("k_bm_tcount");
+        st = exclusive_scan_u32(W.tcnt, W.tcnt, ncg * kTC * nrc, W.hist, (uint32_t *)(L->col_ptr + L->in), s);
+        if (st != CSP_OK) return st;
+        k_bm_tgather<V><<<(unsigned)ntiles, 64, 0, s>>>(W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in,
+                                                        W.tcnt, (const V *)W.vals_k, L->perm_c, L->rows_by_col,
+                                                        (V *)L->vals_c, L->col_ptr);
+        CSP_LAUNCHED("k_bm_tgather");
+        st = build_task_lists(L, s);
+        if (st != CSP_OK) return st;
+        uint32_t counts[6] = {0, 0, 0, 0, 0, 0};
+        CSP_HIP(hipMemcpyAsync(counts, W.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));
+        CSP_HIP(hipStreamSynchronize(s));
+        nacc = counts[4];
+        if (nacc != n_prune) return CSP_OK;  // short: another batch, then rebuild again
+        st = set_task_counts(L, counts);
+        if (st != CSP_OK) return st;
+        // The staged canonical arrays and the next bitmap become the layer's.
+        std::swap(L->rows, W.rows_k);
+        std::swap(L->cols, W.cols_k);
+        std::swap(L->vals, W.vals_k);
+        std::swap(W.occ, W.occ_next);
+        std::swap(W.occ_pref, W.occ_pref_next);
+        return CSP_OK;
+    }
+
+    csp_status run()
+    {
+        Workspace &W = L->ws;
+        const int64_t n = L->nnz;
+        const int passes = sizeof(V) == 4 ? 4 : 2, top = sizeof(V) == 4 ? 24 : 8;
+        int64_t cap = W.bm_batch_cap;
+        if (const char *e = std::getenv("COOSPMM_REGROW_BATCH")) {  // test hook: smaller batches
+            long long v = std::atoll(e);
+            if (v >= 1 && v < cap) cap = v;
+        }
+        int64_t M = batch_size(cap);
+        int hb = hash_bits_for(M);
+        const V *vals = (const V *)L->vals;
+        const int64_t hgrid = ceil_div(n, kHistThreads * 8) < 256 ? ceil_div(n, kHistThreads * 8) : 256;
+        for (int p = 0; p < passes; ++p) {
+            k_bm_hist<V><<<(unsigned)hgrid, kHistThreads, 0, s>>>(vals, n, p, top, (uint32_t)n_prune, W.sel,
+                                                                   p == 0 ? W.hash : nullptr,
+                                                                   p == 0 ? (int64_t(1) << hb) : 0);
+            CSP_LAUNCHED("k_bm_hist");
+        }
+        k_bm_sel_final<<<1, 64, 0, s>>>(W.sel, (uint32_t)n_prune, passes, top);
+        CSP_LAUNCHED("k_bm_sel_final");
+        const int64_t nt = ceil_div(n, kTile);
+        k_bm_prune_count<V><<<(unsigned)nt, kThreads, 0, s>>>(vals, n, W.sel, W.hist);
+        CSP_LAUNCHED("k_bm_prune_count");
+        k_bm_prune_scan<<<1, 1024, 0, s>>>(W.hist, nt, W.sel);
+        CSP_LAUNCHED("k_bm_prune_scan");
+        k_bm_prune_mark<V><<<(unsigned)nt, kThreads, 0, s>>>(vals, n, W.sel, W.hist, (uint64_t *)W.acc_b);
+        CSP_LAUNCHED("k_bm_prune_mark");
+        k_bm_occ_prune<<<blocks_for(W.occ_words, kThreads), kThreads, 0, s>>>(W.occ, W.occ_pref, W.occ_words,
+                                                                              (const uint64_t *)W.acc_b, W.occ_next);
+        CSP_LAUNCHED("k_bm_occ_prune");
+        csp_status st = batch(M, hb);
+        if (st != CSP_OK) return st;
+        st = rebuild();
+        if (st != CSP_OK) return st;
+        for (int64_t batches = 1; nacc < n_prune; ++batches) {
+            if (batches >= 4096)
+                return set_error(CSP_ERR_INVALID_ARG, "regrow found only %lld of %lld empty positions in %llu draws",
+                                 (long long)nacc, (long long)n_prune, (unsigned long long)i0);
+            M = batch_size(cap);
+            hb = hash_bits_for(M);
+            st = fill_u32((uint32_t *)W.hash, 0xFFFFFFFFu, int64_t(2) << hb, s);
+            if (st != CSP_OK) return st;
+            st = batch(M, hb);
+            if (st != CSP_OK) return st;
+            st = rebuild();
+            if (st != CSP_OK) return st;
+        }
+        return CSP_OK;
+    }
+};
+
+}  // namespace
+
+bool plan_bitmap(csp_layer *L)
+{
+    Workspace &W = L->ws;
+    W.bitmap = false;
+    const uint64_t npos = (uint64_t)L->out * (uint64_t)L->in;
+    if (npos >= (uint64_t(1) << 32)) return false;
+    if (const char *e = std::getenv("COOSPMM_RESTRUCTURE"))  // test hook: force the sorted path
+        if (std::strcmp(e, "sorted") == 0) return false;
+    const int64_t inw = ceil_div(L->in, 256) * 8, rows_alloc = ceil_div(L->out, 64) * 64;
+    const int64_t nw = rows_alloc * inw, tcnt = inw * 32 * ceil_div(rows_alloc, kTR) + 1;
+    // two bitmaps and their ranks, the transposition counts
+    const size_t bytes = (size_t)nw * 16 + 8 + (size_t)tcnt * 4;
+    if (bytes > kBitmapBytesLimit) return false;
+    W.bitmap = true;
+    W.occ_words = nw;
+    W.occ_row_words = inw;
+    W.occ_rows = rows_alloc;
+    W.tcnt_words = tcnt;
+    W.bm_batch_cap = W.nkey_cap < kBatchLimit ? W.nkey_cap : kBatchLimit;
+    W.hash_slots = int64_t(1) << hash_bits_for(W.bm_batch_cap);
+    return true;
+}
+
+size_t bitmap_hist_words(const csp_layer *L)
+{
+    const Workspace &W = L->ws;
+    if (!W.bitmap) return 0;
+    const int64_t a = 2 * ceil_div(L->nnz, kTile) + 2, b = ceil_div(W.bm_batch_cap, kThreads) + 2,
+                  c = ceil_div(W.occ_words, 4096) + 2, d = ceil_div(W.tcnt_words, 4096) + 2;
+    int64_t m = a > b ? a : b;
+    m = m > c ? m : c;
+    return (size_t)(m > d ? m : d);
+}
+
+csp_status occupancy_init(csp_layer *L, hipStream_t s)
+{
+    Workspace &W = L->ws;
+    if (!W.bitmap) return CSP_OK;
+    csp_status st = fill_u32(W.occ, 0u, W.occ_words, s);
+    if (st != CSP_OK) return st;
+    if (L->nnz > 0) {
+        k_bm_occ_set<<<blocks_for(L->nnz, 256), 256, 0, s>>>(L->rows, L->cols, L->nnz, W.occ, W.occ_row_words);
+        CSP_LAUNCHED("k_bm_occ_set");
+    }
+    return exclusive_scan_popc(W.occ, W.occ_pref, W.occ_words, W.hist, s);  // ranks of the set bits
+}
+
+csp_status restructure_bitmap(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,
+                              hipStream_t s)
+{
+    const uint64_t npos = (uint64_t)L->out * (uint64_t)L->in;
+    if (L->esz == 2) {
+        BitmapRun<uint16_t> r{L, n_prune, seed, step, npos, (uint16_t)regrow_bits, s};
+        return r.run();
+    }
+    BitmapRun<uint32_t> r{L, n_prune, seed, step, npos, regrow_bits, s};
+    return r.run();
+}
+
+}  // namespace csp

@@ -23,53 +23,16 @@
 #include <cstdlib>
 
 #include "common.h"
+#include "device_util.h"
+#include "regrow.h"
 
 namespace csp {
 namespace {
-
-// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds over a
-// 4 x 64-bit counter with a 2 x 64-bit key; each round multiplies two words
-// by fixed odd constants (keeping both halves of the 128-bit products) and
-// the key is advanced by two Weyl increments between rounds.
-struct Philox4x64 {
-    static constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull, kMul1 = 0xCA5A826395121157ull;
-    static constexpr uint64_t kWeyl0 = 0x9E3779B97F4A7C15ull, kWeyl1 = 0xBB67AE8584CAA73Bull;
-    __device__ static uint64_t word(uint64_t seed, uint64_t step, uint64_t i)
-    {
-        uint64_t x0 = i >> 2, x1 = step, x2 = 0, x3 = 0;
-        uint64_t key0 = seed, key1 = 0;
-#pragma unroll
-        for (int r = 0; r < 10; ++r) {
-            const uint64_t p0_hi = __umul64hi(kMul0, x0), p0_lo = kMul0 * x0;
-            const uint64_t p1_hi = __umul64hi(kMul1, x2), p1_lo = kMul1 * x2;
-            const uint64_t y0 = p1_hi ^ x1 ^ key0, y2 = p0_hi ^ x3 ^ key1;
-            x0 = y0;
-            x1 = p1_lo;
-            x2 = y2;
-            x3 = p0_lo;
-            key0 += kWeyl0;
-            key1 += kWeyl1;
-        }
-        switch (i & 3) {
-        case 0: return x0;
-        case 1: return x1;
-        case 2: return x2;
-        default: return x3;
-        }
-    }
-};
 
 constexpr int kSelState = 0;     // sel[0] prefix, sel[1] mask, sel[2] still to select
 constexpr int kSelTotal = 8;     // sel[8] count read back by the host
 constexpr int kSelHist = 16;     // sel[16..272) digit histogram
 constexpr int kSelWords = 1024;
-
-template <typename V>
-__device__ inline uint32_t mag_key(V v);
-template <>
-__device__ inline uint32_t mag_key<uint32_t>(uint32_t v) { return v & 0x7FFFFFFFu; }
-template <>
-__device__ inline uint32_t mag_key<uint16_t>(uint16_t v) { return (uint32_t)v & 0x7FFFu; }
 
 __global__ void k_sel_init(uint32_t *sel, uint32_t n_prune)
 {
@@ -77,19 +40,6 @@ __global__ void k_sel_init(uint32_t *sel, uint32_t n_prune)
     for (int i = t; i < kSelWords; i += blockDim.x) sel[i] = 0;
     __syncthreads();
     if (t == 0) sel[kSelState + 2] = n_prune;
-}
-
-// Lanes of the wave whose 8-bit digit equals this lane's (and that take part).
-__device__ inline uint64_t same_digit_lanes(uint32_t d, bool take)
-{
-    uint64_t m = __ballot(take);
-#pragma unroll
-    for (int bit = 0; bit < 8; ++bit) {
-        const bool on = (d >> bit) & 1u;
-        const uint64_t bb = __ballot(on);
-        m &= on ? bb : ~bb;
-    }
-    return m;
 }
 
 // Digit histogram of the entries whose higher magnitude bits match the
@@ -110,8 +60,8 @@ __global__ __launch_bounds__(256) void k_sel_hist(const V *__restrict__ vals, in
         const uint32_t key = k < n ? mag_key<V>(vals[k]) : 0u;
         const bool take = k < n && (key & mask) == prefix;
         const uint32_t d = (key >> shift) & 255u;
-        const uint64_t m = same_digit_lanes(d, take);
-        if (take && (m & ((1ull << lane) - 1)) == 0) atomicAdd(&h[d], (uint32_t)__popcll(m));
+        const uint64_t m = lanes_with_same_byte(d, take);
+        if (take && (m & lanes_below()) == 0) atomicAdd(&h[d], (uint32_t)__popcll(m));
     }
     __syncthreads();
     if (h[t]) atomicAdd(&sel[kSelHist + t], h[t]);
@@ -220,8 +170,7 @@ __global__ void k_regrow_candidates(uint64_t seed, uint64_t step, uint64_t i0, i
 {
     int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= M) return;
-    const uint64_t u = Philox4x64::word(seed, step, i0 + (uint64_t)j);
-    const uint64_t p = __umul64hi(u, npos);
+    const uint64_t p = regrow_position(seed, step, i0 + (uint64_t)j, npos);
     const int64_t r = (int64_t)(p / (uint64_t)in);
     const int32_t c = (int32_t)(p - (uint64_t)r * (uint64_t)in);
     const int32_t a = rp_k[r], b = rp_k[r + 1];
@@ -459,6 +408,7 @@ csp_status run_restructure(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_
                            hipStream_t s)
 {
     if (n_prune == 0) return CSP_OK;
+    if (L->ws.bitmap) return restructure_bitmap(L, n_prune, seed, step, regrow_bits, s);
     if (L->esz == 2) return restructure_v<uint16_t>(L, n_prune, seed, step, (uint16_t)regrow_bits, s);
     return restructure_v<uint32_t>(L, n_prune, seed, step, regrow_bits, s);
 }

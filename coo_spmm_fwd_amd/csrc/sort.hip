@@ -6,6 +6,7 @@
 // storage of the non-zero connections only) and the re-sort after a
 // restructure.  All work is HBM-bound integer traffic; no host sync here.
 #include "common.h"
+#include "device_util.h"
 
 namespace csp {
 namespace {
@@ -21,38 +22,12 @@ constexpr int kMaxScanPartials = kScanThreads * 64;
 
 int64_t sort_tiles(int64_t n) { return ceil_div(n, kSortTile); }
 
-// ---------------------------------------------------------------- block scan
-// Exclusive scan of one uint32 per thread over a block of blockDim.x threads
-// (a multiple of 64, at most 1024).  Returns the exclusive prefix; *total gets
-// the block sum (all threads).
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *lds16, uint32_t *total)
-{
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) lds16[w] = x;
-    __syncthreads();
-    if (w == 0) {
-        uint32_t t = lane < nw ? lds16[lane] : 0u, s = t;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            uint32_t y = __shfl_up(s, off, 64);
-            if (lane >= off) s += y;
-        }
-        if (lane < nw) lds16[lane] = s - t;
-        if (lane == nw - 1) lds16[16] = s;
-    }
-    __syncthreads();
-    uint32_t r = x - v + lds16[w];
-    *total = lds16[16];
-    __syncthreads();  // lds16 may be reused by the caller
-    return r;
-}
+// The scans read either the items themselves or the number of set bits of
+// each item (kPopc: positions of the set bits of a bitmap in order).
+template <bool kPopc>
+__device__ __forceinline__ uint32_t scan_item(uint32_t v) { return kPopc ? (uint32_t)__popc(v) : v; }
 
+template <bool kPopc>
 __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t *__restrict__ in, int64_t n,
                                                               uint32_t *__restrict__ partials)
 {
@@ -61,7 +36,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_reduce(const uint32_t *__
     uint32_t s = 0;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i)
-        if (base + i < n) s += in[base + i];
+        s += base + i < n ? scan_item<kPopc>(load_or_first(in, base + i, n)) : 0u;
     uint32_t total;
     block_exclusive_scan(s, lds, &total);
     if (threadIdx.x == 0) partials[blockIdx.x] = total;
@@ -85,15 +60,18 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_partials(uint32_t *__rest
     if (threadIdx.x == 0) partials[nb] = total;
 }
 
+// out[i] = exclusive prefix of the items; with `total_at` set the last block
+// also writes the grand total to out[n].
+template <bool kPopc>
 __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const uint32_t *in, uint32_t *out, int64_t n,
-                                                             const uint32_t *__restrict__ partials)
+                                                             const uint32_t *__restrict__ partials, bool total_at)
 {
     __shared__ uint32_t lds[17];
     int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
     uint32_t v[kScanItems], s = 0;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
-        v[i] = base + i < n ? in[base + i] : 0u;
+        v[i] = base + i < n ? scan_item<kPopc>(load_or_first(in, base + i, n)) : 0u;
         s += v[i];
     }
     uint32_t total;
@@ -104,6 +82,7 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const uint32_t *in,
             out[base + i] = run;
             run += v[i];
         }
+    if (total_at && blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) out[n] = partials[gridDim.x];
 }
 
 __global__ void k_copy_total(const uint32_t *src, uint32_t *dst)
@@ -128,7 +107,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_hist(const K *__restrict
     for (int j = 0; j < kSortItemsPerLane; ++j) {
         const int64_t idx = base + (int64_t)j * kSortThreads + t;
         const bool ok = idx < n;
-        const uint32_t d = ok ? (uint32_t)(keys[idx] >> shift) & 255u : 0u;
+        const uint32_t d = ok ? (uint32_t)(load_or_first(keys, idx, n) >> shift) & 255u : 0u;
         uint64_t m = __ballot(ok);
 #pragma unroll
         for (int bit = 0; bit < 8; ++bit) {
@@ -172,8 +151,12 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const K *__restr
     for (int j = 0; j < kSortItemsPerLane; ++j) {
         int64_t idx = base + (int64_t)j * kWave + lane;
         bool valid = idx < n;
-        K k = valid ? keys_in[idx] : K(0);
-        int32_t v = valid ? vals_in[idx] : 0;
+        K k = load_or_first(keys_in, idx, n);
+        int32_t v = load_or_first(vals_in, idx, n);
+        if (!valid) {
+            k = K(0);
+            v = 0;
+        }
         uint32_t d = (uint32_t)(k >> shift) & 255u;
         uint64_t m = __ballot(valid);
 #pragma unroll
@@ -279,6 +262,22 @@ size_t sort_hist_words(int64_t n)
     return (size_t)(nh + ceil_div(scan_n, kScanTile) + 64);
 }
 
+namespace {
+template <bool kPopc>
+csp_status scan_impl(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *partials, bool total_at, hipStream_t s)
+{
+    const int64_t nb = ceil_div(n, kScanTile);
+    if (nb > kMaxScanPartials) return set_error(CSP_ERR_INVALID_ARG, "scan of %lld items exceeds the limit", (long long)n);
+    k_scan_reduce<kPopc><<<dim3((unsigned)nb), dim3(kScanThreads), 0, s>>>(in, n, partials);
+    CSP_LAUNCHED("k_scan_reduce");
+    k_scan_partials<<<1, kScanThreads, 0, s>>>(partials, nb);
+    CSP_LAUNCHED("k_scan_partials");
+    k_scan_apply<kPopc><<<dim3((unsigned)nb), dim3(kScanThreads), 0, s>>>(in, out, n, partials, total_at);
+    CSP_LAUNCHED("k_scan_apply");
+    return CSP_OK;
+}
+}  // namespace
+
 csp_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *partials, uint32_t *total,
                               hipStream_t s)
 {
@@ -289,19 +288,19 @@ csp_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint
         }
         return CSP_OK;
     }
-    const int64_t nb = ceil_div(n, kScanTile);
-    if (nb > kMaxScanPartials) return set_error(CSP_ERR_INVALID_ARG, "scan of %lld items exceeds the limit", (long long)n);
-    k_scan_reduce<<<dim3((unsigned)nb), dim3(kScanThreads), 0, s>>>(in, n, partials);
-    CSP_LAUNCHED("k_scan_reduce");
-    k_scan_partials<<<1, kScanThreads, 0, s>>>(partials, nb);
-    CSP_LAUNCHED("k_scan_partials");
-    k_scan_apply<<<dim3((unsigned)nb), dim3(kScanThreads), 0, s>>>(in, out, n, partials);
-    CSP_LAUNCHED("k_scan_apply");
+    csp_status st = scan_impl<false>(in, out, n, partials, false, s);
+    if (st != CSP_OK) return st;
     if (total) {
-        k_copy_total<<<1, 64, 0, s>>>(partials + nb, total);
+        k_copy_total<<<1, 64, 0, s>>>(partials + ceil_div(n, kScanTile), total);
         CSP_LAUNCHED("k_copy_total");
     }
     return CSP_OK;
+}
+
+csp_status exclusive_scan_popc(const uint32_t *words, uint32_t *pref, int64_t n, uint32_t *partials, hipStream_t s)
+{
+    if (n <= 0) return fill_u32(pref, 0u, 1, s);
+    return scan_impl<true>(words, pref, n, partials, true, s);
 }
 
 csp_status radix_sort_pairs(int key_bytes, const void *keys_in, const int32_t *vals_in, void *keys_out,

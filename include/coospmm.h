@@ -126,8 +126,11 @@ csp_status spmm_bwd(sparse_layer_t layer, const void *dY, const void *X, int64_t
  * nnz is unchanged, and the result is a pure function of (layer contents,
  * n_prune, seed, step, regrow_value).  0 <= n_prune <= nnz, else
  * CSP_ERR_INVALID_ARG.  Synchronizes on "stream" (it reads back how many
- * candidates were accepted; usually once).  regrow_value is rounded to the
- * layer's dtype.
+ * candidates were accepted and the new task counts; usually once).
+ * regrow_value is rounded to the layer's dtype.  The layer may move its
+ * canonical arrays to other buffers of its own: pointers obtained from
+ * sparse_layer_values before the call are stale afterwards, and work captured
+ * in a graph before it must be captured again.
  */
 csp_status restructure(sparse_layer_t layer, int64_t n_prune, uint64_t seed, uint64_t step, float regrow_value,
                        void *stream);
@@ -157,8 +160,9 @@ csp_status sparse_layer_export_index(sparse_layer_t layer, int32_t *row_ptr, int
 /*
  * sparse_layer_values -- device pointer to the layer's canonical values
  * (nnz elements of the layer dtype), for in-place optimizer updates between
- * calls.  Valid until the layer is destroyed; restructure rewrites it in
- * place.  NULL for a NULL layer.  The input-gradient pass reads a
+ * calls.  Valid until the next restructure or the layer's destruction
+ * (restructure may move the values: ask again afterwards).  NULL for a NULL
+ * layer.  The input-gradient pass reads a
  * column-ordered copy of the values: after writing through this pointer,
  * call sparse_layer_set_values(layer, NULL, stream) before the next
  * spmm_bwd_input or spmm_bwd.

@@ -16,6 +16,17 @@ def orc():
     return oracle.default()
 
 
+@pytest.fixture(params=["bitmap", "sorted"])
+def path(request, monkeypatch):
+    """Both restructure implementations: position bitmaps (the default when they
+    fit) and the sorted fallback, chosen when the layer is created."""
+    if request.param == "sorted":
+        monkeypatch.setenv("COOSPMM_RESTRUCTURE", "sorted")
+    else:
+        monkeypatch.delenv("COOSPMM_RESTRUCTURE", raising=False)
+    return request.param
+
+
 def export(h):
     return tuple(host(t) for t in csp.sparse_layer_export(h))
 
@@ -52,7 +63,7 @@ def run_steps(orc, L: W.CooWeights, n_prune, seed, steps, regrow=0.0):
 @pytest.mark.parametrize("out,in_,nnz,n_prune,seed", [
     (6, 7, 12, 3, 1), (6, 7, 42, 5, 2), (6, 7, 40, 40, 3), (20, 30, 200, 20, 5), (1, 50, 10, 4, 6),
     (50, 1, 10, 4, 7), (1000, 700, 35000, 3500, 11), (333, 777, 50000, 1, 12), (30, 30, 900, 5, 13)])
-def test_restructure_matches_oracle(orc, out, in_, nnz, n_prune, seed):
+def test_restructure_matches_oracle(orc, path, out, in_, nnz, n_prune, seed):
     L = W.random_layer(out, in_, nnz, seed=seed)
     if nnz >= 6:   # plant magnitude ties and signed zeros
         L.vals[1] = -L.vals[0]
@@ -62,13 +73,13 @@ def test_restructure_matches_oracle(orc, out, in_, nnz, n_prune, seed):
     csp.sparse_layer_destroy(h)
 
 
-def test_restructure_zero_prune_is_identity(orc):
+def test_restructure_zero_prune_is_identity(orc, path):
     L = W.random_layer(100, 90, 900, seed=3)
     h, rows, cols, vals = run_steps(orc, L, 0, 1, steps=1)
     csp.sparse_layer_destroy(h)
 
 
-def test_restructure_multi_batch_path(orc, monkeypatch):
+def test_restructure_multi_batch_path(orc, path, monkeypatch):
     """Tiny candidate batches force several regrow rounds; the result must not change."""
     monkeypatch.setenv("COOSPMM_REGROW_BATCH", "37")
     L = W.random_layer(200, 150, 15000, seed=17)
@@ -76,7 +87,7 @@ def test_restructure_multi_batch_path(orc, monkeypatch):
     csp.sparse_layer_destroy(h)
 
 
-def test_restructure_bf16(orc):
+def test_restructure_bf16(orc, path):
     L = W.random_layer(300, 200, 6000, seed=19, dtype="bf16")
     h = csp.sparse_layer_create(300, 200, dev(L.rows), dev(L.cols), dev(L.vals))
     try:
@@ -85,6 +96,49 @@ def test_restructure_bf16(orc):
         rr, cr, vr, _ = orc.restructure(300, 200, c["rows"], c["cols"], c["vals"], 600, 9, 2, regrow_bits)
         csp.restructure(h, 600, 9, 2, 0.125)
         check_state(orc, h, 300, 200, rr, cr, vr)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_restructure_wide_layer_sorted_path(orc):
+    """out*in >= 2^32: positions need 64 bits, so the layer takes the sorted path by itself."""
+    L = W.random_layer(70000, 70000, 30000, seed=41)
+    h, *_ = run_steps(orc, L, 3000, 5, steps=2, regrow=-1.0)
+    csp.sparse_layer_destroy(h)
+
+
+def test_restructure_multi_batch_bf16(orc, path, monkeypatch):
+    """Short batches on a bf16 layer: several rounds, each rebuilding the view until all are taken."""
+    monkeypatch.setenv("COOSPMM_REGROW_BATCH", "300")
+    L = W.random_layer(64, 96, 5000, seed=43, dtype="bf16")
+    h = csp.sparse_layer_create(64, 96, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(64, 96, L.rows, L.cols, L.vals)
+        rows, cols, vals = c["rows"], c["cols"], c["vals"]
+        regrow_bits = W.f32_to_bf16_bits(np.array([2.0], np.float32))[0]
+        for step in range(3):
+            rows, cols, vals, _ = orc.restructure(64, 96, rows, cols, vals, 900, 21, step, regrow_bits)
+            csp.restructure(h, 900, 21, step, 2.0)
+            check_state(orc, h, 64, 96, rows, cols, vals)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_values_view_after_restructure(orc, path):
+    """A values view taken after a restructure sees the new values, and in-place
+    updates through it reach every pass."""
+    L = W.random_layer(400, 300, 12000, seed=47)
+    h, rows, cols, vals = run_steps(orc, L, 1200, 3, steps=1, regrow=0.25)
+    try:
+        v = csp.sparse_layer_values_tensor(h)
+        assert np.array_equal(bits(host(v.clone())), bits(vals))
+        v.mul_(3.0)
+        csp.sparse_layer_set_values(h, None)
+        newv = host(v.clone())
+        dY = W.random_dense((5, 400), 8)
+        dX = host(csp.spmm_bwd_input(h, dev(dY)))
+        ref, S = orc.spmm_bwd_input(400, 300, rows, cols, newv, dY)
+        assert_within(dX, ref, S, FP32_REL, "dX after restructure and in-place update")
     finally:
         csp.sparse_layer_destroy(h)
 
@@ -101,7 +155,7 @@ def test_restructure_rejects_bad_count():
         csp.sparse_layer_destroy(h)
 
 
-def test_products_after_restructure(orc):
+def test_products_after_restructure(orc, path):
     """After restructure the products use the new structure (offsets and transposed view rebuilt)."""
     L = W.random_layer(700, 500, 20000, seed=23)
     h, rows, cols, vals = run_steps(orc, L, 2000, 8, steps=2)
