@@ -122,8 +122,8 @@ __device__ inline void select_state(const uint32_t *sel, int npass, int top, uin
 // Histogram pass `pass` of the radix select; pass 0 also fills `clear`
 // (the regrow hash table) with empty slots.  Few fat blocks: every block adds
 // its nonzero bins to the global histogram with one atomic each.  Lanes that
-// hit the same bin serialize on the LDS atomic, which costs less than
-// matching digits across the wave first.
+// hit the same bin serialize on the LDS atomic (four copies, by lane, cut
+// that by four), which costs less than matching digits across the wave.
 constexpr int kHistThreads = 1024;
 
 template <typename V>
@@ -131,10 +131,10 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(const V *__restrict__ 
                                                           uint32_t n_prune, uint32_t *sel,
                                                           uint64_t *__restrict__ clear, int64_t nclear)
 {
-    __shared__ uint32_t h[256];
+    __shared__ uint32_t h[4][256];  // lane & 3 picks the copy: a quarter of the lanes per address
     __shared__ uint32_t state[2];
     const int t = threadIdx.x;
-    if (t < 256) h[t] = 0;
+    h[t >> 8][t & 255] = 0;
     if (t < 64) {
         uint32_t prefix, mask, need;
         select_state(sel, pass, top, n_prune, prefix, mask, need);
@@ -158,10 +158,14 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(const V *__restrict__ 
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            if (base + u * kHistThreads + t < n && (key[u] & mask) == prefix) atomicAdd(&h[(key[u] >> shift) & 255u], 1u);
+            if (base + u * kHistThreads + t < n && (key[u] & mask) == prefix)
+                atomicAdd(&h[t & 3][(key[u] >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (t < 256 && h[t]) atomicAdd(&sel[pass * kHistWords + (blockIdx.x & (kCopies - 1)) * 256 + t], h[t]);
+    if (t < 256) {
+        const uint32_t c = h[0][t] + h[1][t] + h[2][t] + h[3][t];
+        if (c) atomicAdd(&sel[pass * kHistWords + (blockIdx.x & (kCopies - 1)) * 256 + t], c);
+    }
 }
 
 __global__ __launch_bounds__(64) void k_bm_sel_final(uint32_t *sel, uint32_t n_prune, int passes, int top)
@@ -278,10 +282,18 @@ __global__ __launch_bounds__(kThreads) void k_bm_occ_prune(const uint32_t *__res
 {
     const int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (w >= nw) return;
-    const uint32_t o = occ[w];
-    uint32_t k = pref[w], keep = o;
-    for (uint32_t m = o; m; m &= m - 1, ++k)
-        if ((pruned[k >> 6] >> (k & 63)) & 1ull) keep &= ~(m & (0u - m));
+    const uint32_t o = occ[w], k0 = pref[w];
+    uint32_t keep = o;
+    if (o) {
+        // the word's entries k0 .. k0 + popc - 1 span at most two mask words
+        const uint32_t k1 = k0 + (uint32_t)__popc(o) - 1u;
+        const uint64_t lo = pruned[k0 >> 6], hi = pruned[k1 >> 6];
+        uint32_t k = k0;
+        for (uint32_t m = o; m; m &= m - 1, ++k) {
+            const uint64_t pw = (k >> 6) == (k0 >> 6) ? lo : hi;
+            if ((pw >> (k & 63)) & 1ull) keep &= ~(m & (0u - m));
+        }
+    }
     occ_next[w] = keep;
 }
 
@@ -295,17 +307,18 @@ __device__ __forceinline__ uint64_t hash_home(uint32_t p, int hbits)
 // slot keeps the smallest index seen for its position (same high word, so
 // the 64-bit minimum is the minimum index).  Linear probing; the table has at
 // least twice as many slots as candidates, so a free slot always exists.
-__device__ inline void hash_insert(uint64_t *tab, int hbits, uint32_t p, uint32_t j)
+// Finishes an insertion whose attempt at slot s found `old` there.
+__device__ inline void hash_insert_from(uint64_t *tab, int hbits, uint32_t p, uint32_t j, uint64_t s, uint64_t old)
 {
     const uint64_t mask = (1ull << hbits) - 1, entry = ((uint64_t)p << 32) | j;
-    uint64_t s = hash_home(p, hbits);
-    for (uint64_t probe = 0; probe <= mask; ++probe, s = (s + 1) & mask) {
-        const uint64_t old = atomicCAS((unsigned long long *)&tab[s], kEmptySlot, entry);
+    for (uint64_t probe = 0; probe <= mask; ++probe) {
         if (old == kEmptySlot) return;
         if ((uint32_t)(old >> 32) == p) {
             atomicMin((unsigned long long *)&tab[s], (unsigned long long)entry);
             return;
         }
+        s = (s + 1) & mask;
+        old = atomicCAS((unsigned long long *)&tab[s], kEmptySlot, entry);
     }
 }
 
@@ -321,9 +334,10 @@ __device__ inline uint32_t hash_first(const uint64_t *tab, int hbits, uint32_t p
     return kNoPos;
 }
 
-// Candidates [i0, i0 + M) of the stream: occupied positions drop out, the
-// others enter the hash table.  Block 0 also clears the select histograms
-// for the next restructure.
+// Candidates [i0, i0 + M) of the stream (i0 a multiple of 4), four per
+// thread (one Philox block): occupied positions drop out, the others enter
+// the hash table.  Block 0 also clears the select histograms for the next
+// restructure.
 __global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint64_t step, uint64_t i0, int64_t M,
                                                              int64_t in, uint64_t npos, const uint32_t *occ,
                                                              int64_t inw, uint32_t *__restrict__ cand, uint64_t *tab,
@@ -331,13 +345,33 @@ __global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint
 {
     if (blockIdx.x == 0)
         for (int i = threadIdx.x; i < kMaxPasses * kHistWords; i += kThreads) sel[i] = 0;
-    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (j >= M) return;
-    const uint64_t p = regrow_position(seed, step, i0 + (uint64_t)j, npos);
-    const int64_t r = (int64_t)(p / (uint64_t)in), c = (int64_t)p - r * in;
-    const bool taken = (occ[r * inw + (c >> 5)] >> (c & 31)) & 1u;
-    cand[j] = taken ? kNoPos : (uint32_t)p;
-    if (!taken) hash_insert(tab, hbits, (uint32_t)p, (uint32_t)j);
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x, j0 = 4 * t;
+    if (j0 >= M) return;
+    uint64_t u[4];
+    Philox4x64::block(seed, step, (i0 >> 2) + (uint64_t)t, u);
+    uint32_t p[4];
+    bool free_[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint64_t pq = __umul64hi(u[q], npos);
+        const int64_t r = (int64_t)(pq / (uint64_t)in), c = (int64_t)pq - r * in;
+        p[q] = (uint32_t)pq;
+        free_[q] = j0 + q < M && !((occ[r * inw + (c >> 5)] >> (c & 31)) & 1u);
+    }
+    uint64_t home[4], old[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // the four first attempts go out together
+        home[q] = hash_home(p[q], hbits);
+        old[q] = free_[q] ? atomicCAS((unsigned long long *)&tab[home[q]], kEmptySlot,
+                                      ((uint64_t)p[q] << 32) | (uint64_t)(j0 + q))
+                          : kEmptySlot;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (j0 + q >= M) break;
+        cand[j0 + q] = free_[q] ? p[q] : kNoPos;
+        if (free_[q]) hash_insert_from(tab, hbits, p[q], (uint32_t)(j0 + q), home[q], old[q]);
+    }
 }
 
 // flag[j] = candidate j is empty and the first of its position in the batch;
@@ -449,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void k_bm_canon(const uint32_t *__restric
 }
 
 // The transposed view is built in tiles of 1024 rows x 64 columns (two
-// bitmap words per row), one wave each.  Each 64-row slice of a tile's words
+// bitmap words per row), one block each.  Each 64-row slice of a tile's words
 // is turned into column words by 32 x 32 bit transposes across the lanes, so
 // a column's entries in row order are the set bits of its 32 column words.
 constexpr int kTR = 1024, kTC = 64, kTSlices = kTR / 64;
@@ -463,33 +497,38 @@ __device__ __forceinline__ uint2 tile_row_words(const uint32_t *__restrict__ occ
 }
 
 // Entries per column within each 1024-row chunk: tcnt[c * nrc + chunk].
+// One block per tile, wave w takes slices w, w + 4, ...
 __global__ __launch_bounds__(kThreads) void k_bm_tcount(const uint32_t *__restrict__ occ, int64_t inw,
-                                                        int64_t rows_alloc, int64_t nrc, int64_t ncg,
-                                                        uint32_t *__restrict__ tcnt)
+                                                        int64_t rows_alloc, int64_t nrc, uint32_t *__restrict__ tcnt)
 {
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wave >= nrc * ncg) return;
-    const int64_t rc = wave % nrc, cg = wave / nrc;
-    uint2 w[kTSlices];
+    __shared__ uint32_t part[4][kTC];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t rc = blockIdx.x % nrc, cg = blockIdx.x / nrc;
+    uint2 wd[kTSlices / 4];
 #pragma unroll
-    for (int sl = 0; sl < kTSlices; ++sl) w[sl] = tile_row_words(occ, rc * kTR + sl * 64 + lane, rows_alloc, inw, cg);
+    for (int i = 0; i < kTSlices / 4; ++i)
+        wd[i] = tile_row_words(occ, rc * kTR + (4 * i + w) * 64 + lane, rows_alloc, inw, cg);
     uint32_t c0 = 0, c1 = 0;  // lane i: columns i & 31 and 32 + (i & 31), rows of its half-slice
 #pragma unroll
-    for (int sl = 0; sl < kTSlices; ++sl) {
-        if (__ballot((w[sl].x | w[sl].y) != 0u) == 0) continue;
-        c0 += (uint32_t)__popc(transpose32(w[sl].x));
-        c1 += (uint32_t)__popc(transpose32(w[sl].y));
+    for (int i = 0; i < kTSlices / 4; ++i) {
+        if (__ballot((wd[i].x | wd[i].y) != 0u) == 0) continue;
+        c0 += (uint32_t)__popc(transpose32(wd[i].x));
+        c1 += (uint32_t)__popc(transpose32(wd[i].y));
     }
     c0 += __shfl_xor(c0, 32, 64);
     c1 += __shfl_xor(c1, 32, 64);
     if (lane < 32) {
-        tcnt[(cg * kTC + lane) * nrc + rc] = c0;
-        tcnt[(cg * kTC + 32 + lane) * nrc + rc] = c1;
+        part[w][lane] = c0;
+        part[w][32 + lane] = c1;
+    }
+    __syncthreads();
+    if (threadIdx.x < kTC) {
+        const int c = threadIdx.x;
+        tcnt[(cg * kTC + c) * nrc + rc] = part[0][c] + part[1][c] + part[2][c] + part[3][c];
     }
 }
 
-// Transposed view, one wave per tile: the tile's output is, per column, a
+// Transposed view, one block per tile: the tile's output is, per column, a
 // run of consecutive transposed ranks from tscan[c * nrc + rc] (exclusive
 // scan of tcnt).  Lanes walk the tile's entries in that order, so stores are
 // coalesced: output o -> column (search in the column starts) -> row (search
@@ -497,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void k_bm_tcount(const uint32_t *__restri
 // (the row's first entry in the tile plus its entries to the left).  rc = 0
 // also writes col_ptr.
 template <typename V>
-__global__ __launch_bounds__(64) void k_bm_tgather(const uint32_t *__restrict__ occ,
+__global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restrict__ occ,
                                                    const uint32_t *__restrict__ pref, int64_t inw, int64_t rows_alloc,
                                                    int64_t nrc, int64_t in, const uint32_t *__restrict__ tscan,
                                                    const V *__restrict__ vals, int32_t *__restrict__ perm_c,
@@ -510,10 +549,11 @@ __global__ __launch_bounds__(64) void k_bm_tgather(const uint32_t *__restrict__ 
     __shared__ uint16_t ccum[kTC][kTR / 32 + 1];  // set bits in the column's earlier words
     __shared__ uint32_t cstart[kTC + 1];          // tile-local start of each column's run
     __shared__ uint32_t gout[kTC];                // transposed rank of each run's first entry
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t rc = blockIdx.x % nrc, cg = blockIdx.x / nrc, r0 = rc * kTR;
 #pragma unroll
-    for (int sl = 0; sl < kTSlices; ++sl) {
+    for (int i = 0; i < kTSlices / 4; ++i) {
+        const int sl = 4 * i + wv;
         const int64_t r = r0 + sl * 64 + lane;
         const uint2 w = tile_row_words(occ, r, rows_alloc, inw, cg);
         rw[sl * 64 + lane] = w;
@@ -522,31 +562,37 @@ __global__ __launch_bounds__(64) void k_bm_tgather(const uint32_t *__restrict__ 
         cw[32 + (lane & 31)][2 * sl + (lane >> 5)] = transpose32(w.y);
     }
     __syncthreads();
-    uint32_t run = 0;  // lane = column
-    for (int b = 0; b < kTR / 32; ++b) {
-        ccum[lane][b] = (uint16_t)run;
-        run += (uint32_t)__popc(cw[lane][b]);
-    }
-    uint32_t incl = run;  // scan of the column counts over the wave
+    __shared__ uint32_t total_s;
+    if (wv == 0) {
+        uint32_t run = 0;  // lane = column
+        for (int b = 0; b < kTR / 32; ++b) {
+            ccum[lane][b] = (uint16_t)run;
+            run += (uint32_t)__popc(cw[lane][b]);
+        }
+        uint32_t incl = run;  // scan of the column counts over the wave
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        cstart[lane] = incl - run;
+        if (lane == 63) {
+            cstart[kTC] = incl;
+            total_s = incl;
+        }
+        const int64_t c_glob = cg * kTC + lane;
+        gout[lane] = tscan[c_glob * nrc + rc];
+        if (rc == 0 && c_glob < in) col_ptr[c_glob] = (int32_t)gout[lane];
     }
-    const uint32_t total = __shfl(incl, 63, 64);
-    cstart[lane] = incl - run;
-    if (lane == 0) cstart[kTC] = total;
-    const int64_t c_glob = cg * kTC + lane;
-    gout[lane] = tscan[c_glob * nrc + rc];
-    if (rc == 0 && c_glob < in) col_ptr[c_glob] = (int32_t)gout[lane];
     __syncthreads();
-    constexpr int U = 4;  // outputs in flight per lane
-    for (uint32_t o0 = 0; o0 < total; o0 += 64 * U) {
+    const uint32_t total = total_s;
+    constexpr int U = 4;  // outputs in flight per thread (their value loads overlap)
+    for (uint32_t o0 = 0; o0 < total; o0 += kThreads * U) {
         int32_t kk[U], rr[U];
         uint32_t jj[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t o = o0 + u * 64 + lane;
+            const uint32_t o = o0 + u * kThreads + t;
             int c = 0;  // last column whose run starts at or before o
 #pragma unroll
             for (int step = 32; step >= 1; step >>= 1)
@@ -610,14 +656,15 @@ struct BitmapRun {
         const double free_frac = (double)(npos - (uint64_t)nkept - (uint64_t)nacc) / (double)npos;
         const double want = (double)need / free_frac * 1.1 + 1024.0;
         int64_t M = want > (double)cap ? cap : (int64_t)want;
-        return M < 1 ? 1 : M;
+        M -= M % 4;  // whole Philox blocks, so every batch starts at a multiple of 4
+        return M < 4 ? 4 : M;
     }
 
     csp_status batch(int64_t M, int hb)
     {
         Workspace &W = L->ws;
         const unsigned nt = blocks_for(M, kThreads);
-        k_bm_cand_insert<<<nt, kThreads, 0, s>>>(seed, step, i0, M, L->in, npos, W.occ_next, W.occ_row_words, W.u_a,
+        k_bm_cand_insert<<<blocks_for(M, 4 * kThreads), kThreads, 0, s>>>(seed, step, i0, M, L->in, npos, W.occ_next, W.occ_row_words, W.u_a,
                                                  W.hash, hb, W.sel);
         CSP_LAUNCHED("k_bm_cand_insert");
         k_bm_cand_count<<<nt, kThreads, 0, s>>>(W.u_a, M, W.hash, hb, (uint64_t *)W.u_b, W.hist);
@@ -644,11 +691,11 @@ struct BitmapRun {
             W.occ_next, W.occ_pref_next, W.occ, W.occ_pref, (const uint64_t *)W.acc_b, (const V *)L->vals, regrow,
             (uint32_t)nw, (uint32_t)inw, L->out, W.rows_k, W.cols_k, (V *)W.vals_k, L->row_ptr);
         CSP_LAUNCHED("k_bm_canon");
-        k_bm_tcount<<<blocks_for(ntiles, 4), kThreads, 0, s>>>(W.occ_next, inw, rows_alloc, nrc, ncg, W.tcnt);
+        k_bm_tcount<<<(unsigned)ntiles, kThreads, 0, s>>>(W.occ_next, inw, rows_alloc, nrc, W.tcnt);
         CSP_LAUNCHED("k_bm_tcount");
         st = exclusive_scan_u32(W.tcnt, W.tcnt, ncg * kTC * nrc, W.hist, (uint32_t *)(L->col_ptr + L->in), s);
         if (st != CSP_OK) return st;
-        k_bm_tgather<V><<<(unsigned)ntiles, 64, 0, s>>>(W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in,
+        k_bm_tgather<V><<<(unsigned)ntiles, kThreads, 0, s>>>(W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in,
                                                         W.tcnt, (const V *)W.vals_k, L->perm_c, L->rows_by_col,
                                                         (V *)L->vals_c, L->col_ptr);
         CSP_LAUNCHED("k_bm_tgather");

@@ -20,9 +20,10 @@ namespace csp {
 struct Philox4x64 {
     static constexpr uint64_t kMul0 = 0xD2E7470EE14C6C93ull, kMul1 = 0xCA5A826395121157ull;
     static constexpr uint64_t kWeyl0 = 0x9E3779B97F4A7C15ull, kWeyl1 = 0xBB67AE8584CAA73Bull;
-    __device__ static uint64_t word(uint64_t seed, uint64_t step, uint64_t i)
+    // The four words of block b (counter (b, step, 0, 0), key (seed, 0)).
+    __device__ static void block(uint64_t seed, uint64_t step, uint64_t b, uint64_t out[4])
     {
-        uint64_t x0 = i >> 2, x1 = step, x2 = 0, x3 = 0;
+        uint64_t x0 = b, x1 = step, x2 = 0, x3 = 0;
         uint64_t key0 = seed, key1 = 0;
 #pragma unroll
         for (int r = 0; r < 10; ++r) {
@@ -36,12 +37,17 @@ struct Philox4x64 {
             key0 += kWeyl0;
             key1 += kWeyl1;
         }
-        switch (i & 3) {
-        case 0: return x0;
-        case 1: return x1;
-        case 2: return x2;
-        default: return x3;
-        }
+        out[0] = x0;
+        out[1] = x1;
+        out[2] = x2;
+        out[3] = x3;
+    }
+    // Word i of the stream: word (i mod 4) of block (i div 4).
+    __device__ static uint64_t word(uint64_t seed, uint64_t step, uint64_t i)
+    {
+        uint64_t w[4];
+        block(seed, step, i >> 2, w);
+        return w[i & 3];
     }
 };
 
