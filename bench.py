@@ -195,6 +195,66 @@ def cpu_baseline(kind, layers, acts, B, n_prune=0, seed=0, budget_s=12.0):
 
 
 # ------------------------------------------------------------------ steps
+def dense_baselines(kind, layers, uploaded, X, dY, B, ours_ms, steps=20):
+    """The same step with torch's dense matmul (hipBLASLt) on the same shapes: a dense layer, and
+    Dense+Mask (the weight multiplied by its 0/1 mask before use, the weight gradient masked after).
+    Warm (one copy).  A restructure has no dense counterpart here, so a DST step is compared on its
+    products only.  Also checks that the dense forward agrees with the layer's."""
+    import torch
+    dev = X.device
+    dt = X.dtype
+    Ws, Ms = [], []
+    for L, (r, c, v) in zip(layers, uploaded):
+        Wd = torch.zeros((L.out, L.in_), dtype=dt, device=dev)
+        Wd[r.long(), c.long()] = v
+        Ws.append(Wd)
+        Ms.append((Wd != 0).to(dt))
+
+    def gelu_parts(H):
+        cdf = 0.5 * (1.0 + torch.erf(H * 0.7071067811865476))
+        return H * cdf, cdf + H * torch.exp(-0.5 * H * H) * 0.3989422804014327
+
+    def step(masked):
+        W = [w * m for w, m in zip(Ws, Ms)] if masked else Ws
+        if kind == "inference":
+            return X @ W[0].t()
+        if kind == "mlp":
+            H = X @ W[0].t()
+            A, G = gelu_parts(H)
+            Y = A @ W[1].t()
+            dA = dY @ W[1]
+            dW2 = dY.t() @ A
+            dH = dA * G
+            dX = dH @ W[0]
+            dW1 = dH.t() @ X
+            if masked:
+                dW1, dW2 = dW1 * Ms[0], dW2 * Ms[1]
+            return Y
+        Y = X @ W[0].t()
+        dX = dY @ W[0]
+        dWd = dY.t() @ X
+        if masked:
+            dWd = dWd * Ms[0]
+        return Y
+
+    res = {}
+    for name, masked in (("dense", False), ("dense_mask", True)):
+        for _ in range(3):
+            step(masked)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            step(masked)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms_per_step": round(ms, 5), "ratio": round(ms / ours_ms, 2)}
+    res["note"] = ("torch dense matmul (hipBLASLt) on the same shapes and dtype, warm; ratio = their step "
+                   "time / ours" + (" (products only: no restructure on the dense side)" if kind == "dst" else ""))
+    return res, Ws
+
+
 def workload_kind(w) -> str:
     if w.dtype == "bf16":
         return "inference"
@@ -230,6 +290,7 @@ def main():
     ap.add_argument("--warm", action="store_true", help="reuse one replica (cache-resident data)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
     ap.add_argument("--eager", action="store_true", help="launch each call from Python instead of graph replay")
+    ap.add_argument("--no-baselines", action="store_true", help="skip the dense and Dense+Mask torch baselines")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (reference for HBM byte counters)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -417,6 +478,27 @@ def main():
             csp.restructure(reps[0]["h"][0], layers[0].nnz // 10, seed=w.seed, step=12345 + k, stream=stream)
             restructure_ms = (time.perf_counter() - r0) * 1e3
 
+    baselines = None
+    if not args.no_baselines:
+        ours_ms = ms_per_step
+        if kind == "dst":  # products only, eager like the timed steps
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.steps):
+                run_calls(reps[i % R], stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ours_ms = e0.elapsed_time(e1) / args.steps
+        X0, dY0 = reps[0]["X"], reps[0]["dY"]
+        current = [csp.sparse_layer_export(h) for h in reps[0]["h"]]  # after any restructures
+        baselines, Ws = dense_baselines(kind, layers, current, X0, dY0, B, ours_ms)
+        if kind != "mlp":  # the dense forward must agree with the layer's
+            Yd = (X0.float() @ Ws[0].float().t())
+            Ys = csp.spmm_fwd(reps[0]["h"][0], X0).float()
+            baselines["forward_max_abs_diff"] = float((Yd - Ys).abs().max())
+        baselines["ours_ms_per_step"] = round(ours_ms, 5)
+        del Ws
+
     if args.calibrate_copy:
         n = (args.calibrate_copy << 20) // 4
         src = torch.randn(n, device=dev)
@@ -466,6 +548,8 @@ def main():
         "restructure_ms": None if restructure_ms is None else round(restructure_ms, 3),
         "wall_s": round(wall, 3),
     }
+    if baselines is not None:
+        rec["dense_baselines"] = baselines
     if not args.no_cpu:
         rec["cpu_baseline"] = cpu_baseline(kind, layers, acts, B, n_prune, w.seed)
     print(json.dumps(rec), flush=True)
