@@ -161,6 +161,14 @@ def cpu_baseline(kind, layers, acts, B, n_prune=0, seed=0, budget_s=12.0):
             L = layers[0]
             orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, X)
             return
+        if kind == "stack":
+            from coo_spmm_fwd_amd.workloads import f32_to_bf16_bits
+            A = X
+            for li, L in enumerate(layers):
+                H, _ = orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, A)
+                if li + 1 < len(layers):
+                    A = f32_to_bf16_bits(orc.gelu(H).astype(np.float32))
+            return
         if kind == "mlp":
             L1, L2 = layers
             H, _ = orc.spmm_fwd(L1.out, L1.in_, L1.rows, L1.cols, L1.vals, X)
@@ -218,6 +226,13 @@ def dense_baselines(kind, layers, uploaded, X, dY, B, ours_ms, steps=20):
         W = [w * m for w, m in zip(Ws, Ms)] if masked else Ws
         if kind == "inference":
             return X @ W[0].t()
+        if kind == "stack":
+            A = X
+            for li, w in enumerate(W):
+                A = A @ w.t()
+                if li + 1 < len(W):
+                    A = torch.nn.functional.gelu(A)
+            return A
         if kind == "mlp":
             H = X @ W[0].t()
             A, G = gelu_parts(H)
@@ -257,7 +272,7 @@ def dense_baselines(kind, layers, uploaded, X, dY, B, ours_ms, steps=20):
 
 def workload_kind(w) -> str:
     if w.dtype == "bf16":
-        return "inference"
+        return "stack" if len(w.layers) > 1 else "inference"
     if len(w.layers) == 2:
         return "mlp"
     if w.prune_frac > 0:
@@ -272,7 +287,7 @@ def step_bytes(kind, layers, B, n_prune=0):
     for L in layers:
         sv = 2 if L.dtype == "bf16" else 4
         tot += bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)
-        if kind != "inference":
+        if kind not in ("inference", "stack"):
             tot += bytes_dx(L.nnz, L.out, L.in_, B) + bytes_dw(L.nnz, L.out, L.in_, B)
     if kind == "dst":
         tot += 36 * layers[0].nnz
@@ -323,7 +338,11 @@ def main():
     n_prune = int(w.prune_frac * layers[0].nnz) if kind == "dst" else 0
     sbytes = step_bytes(kind, layers, B, n_prune)
     # bytes one step touches in one replica: both index orders, both value orders, dW, dense operands
-    touched = sum(L.nnz * 28 + 4 * B * (3 * L.in_ + 2 * L.out) for L in layers)
+    if kind in ("inference", "stack"):  # forward only: column index, value, task list, X and Y
+        sv = 2 if w.dtype == "bf16" else 4
+        touched = sum(L.nnz * (4 + sv) + 16 * (L.out + L.nnz // 512) + sv * B * (L.in_ + L.out) for L in layers)
+    else:
+        touched = sum(L.nnz * 28 + 4 * B * (3 * L.in_ + 2 * L.out) for L in layers)
     R = 1 if args.warm else max(2, -(-2 * MALL_BYTES // touched) + 1)
 
     def t(a):
@@ -336,7 +355,9 @@ def main():
     for j in range(R):
         st = {"h": [csp.sparse_layer_create(L.out, L.in_, *u) for L, u in zip(layers, uploaded)],
               "X": t(acts[B]["X"]), "dY": t(acts[B]["dY"])}
-        if kind == "mlp":
+        if kind == "stack":
+            st.update(acts=[torch.empty((B, L.out), device=dev, dtype=torch.bfloat16) for L in layers])
+        elif kind == "mlp":
             L1, L2 = layers
             st.update(H=torch.empty((B, L1.out), device=dev), A=torch.empty((B, L1.out), device=dev),
                       Y=torch.empty((B, L2.out), device=dev), dA=torch.empty((B, L1.out), device=dev),
@@ -366,6 +387,17 @@ def main():
     def calls(st, stream):
         """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic bytes)."""
         out = []
+        if kind == "stack":
+            for li, (h, L) in enumerate(zip(st["h"], layers)):
+                src = st["X"] if li == 0 else st["acts"][li - 1]
+
+                def f(h=h, src=src, dst=st["acts"][li], last=li + 1 == len(layers)):
+                    csp.spmm_fwd(h, src, dst, stream=stream)
+                    if not last:
+                        dst.copy_(torch.nn.functional.gelu(dst))
+
+                out.append((f"forward {li + 1}", h, f, fwd_name, bytes_fwd(L.nnz, L.out, L.in_, B, sv=2, sx=2)))
+            return out
         if kind == "mlp":
             (h1, h2), (L1, L2) = st["h"], layers
 
@@ -492,7 +524,7 @@ def main():
         X0, dY0 = reps[0]["X"], reps[0]["dY"]
         current = [csp.sparse_layer_export(h) for h in reps[0]["h"]]  # after any restructures
         baselines, Ws = dense_baselines(kind, layers, current, X0, dY0, B, ours_ms)
-        if kind != "mlp":  # the dense forward must agree with the layer's
+        if kind not in ("mlp", "stack"):  # the dense forward must agree with the layer's
             Yd = (X0.float() @ Ws[0].float().t())
             Ys = csp.spmm_fwd(reps[0]["h"][0], X0).float()
             baselines["forward_max_abs_diff"] = float((Yd - Ys).abs().max())
@@ -515,8 +547,9 @@ def main():
             csp.sparse_layer_destroy(h)
 
     value = sbytes / (ms_per_step * 1e-3) / 1e9
-    flops = sum(2 * L.nnz * B * (1 if kind == "inference" else 3) for L in layers)
-    steps_desc = {"linear": "spmm_fwd + spmm_bwd (dX and dW)",
+    flops = sum(2 * L.nnz * B * (1 if kind in ("inference", "stack") else 3) for L in layers)
+    steps_desc = {"stack": f"{len(layers)} x spmm_fwd with GELU between (one token batch through the stack)",
+                  "linear": "spmm_fwd + spmm_bwd (dX and dW)",
                   "dst": f"spmm_fwd + spmm_bwd + restructure({n_prune} of {layers[0].nnz})",
                   "inference": "spmm_fwd",
                   "mlp": "fwd1, GELU, fwd2, bwd2 (dA, dW2), GELU', bwd1 (dX, dW1)"}[kind]

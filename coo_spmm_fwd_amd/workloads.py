@@ -71,6 +71,8 @@ WORKLOADS = {
                  "fwd"),
         Workload("dst8192_b64_s95", ((8192, 8192),), 0.05, (64,), 0.02, "f32", "uniform", 5,
                  "fwd+dX+dW then restructure", steps=10, prune_frac=0.10),
+        Workload("stack16384x4_zipf_s99_bf16", ((16384, 16384),) * 4, 0.01, (1, 4), 0.02, "bf16", "zipf", 6,
+                 "fwd of four layers, GELU between, one graph per token", gelu=True),
     )
 }
 
