@@ -380,10 +380,6 @@ def main():
     grad_name = (f"k_segment_spmm<{ld}, F32, false> + k_values_rows<{ld}, false>" if big
                  else f"k_gradients<{ld}, false>")
 
-    def gelu_parts(H):
-        cdf = 0.5 * (1.0 + torch.erf(H * 0.7071067811865476))
-        return H * cdf, cdf + H * torch.exp(-0.5 * H * H) * 0.3989422804014327
-
     def calls(st, stream):
         """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic bytes)."""
         out = []
@@ -392,24 +388,22 @@ def main():
                 src = st["X"] if li == 0 else st["acts"][li - 1]
 
                 def f(h=h, src=src, dst=st["acts"][li], last=li + 1 == len(layers)):
-                    csp.spmm_fwd(h, src, dst, stream=stream)
-                    if not last:
-                        dst.copy_(torch.nn.functional.gelu(dst))
+                    # GELU fused into the producing layer's epilogue
+                    csp.spmm_fwd_act(h, src, act="none" if last else "gelu", Y=dst, stream=stream)
 
                 out.append((f"forward {li + 1}", h, f, fwd_name, bytes_fwd(L.nnz, L.out, L.in_, B, sv=2, sx=2)))
             return out
         if kind == "mlp":
             (h1, h2), (L1, L2) = st["h"], layers
 
+            # GELU in the first layer's forward epilogue (A = GELU(H), H kept), GELU' in the
+            # second layer's input-gradient epilogue (dH = (dY W2) * GELU'(H))
             def f1():
-                csp.spmm_fwd(h1, st["X"], st["H"], stream=stream)
-                a, g = gelu_parts(st["H"])
-                st["A"].copy_(a)
-                st["G"] = g
+                csp.spmm_fwd_act(h1, st["X"], act="gelu", Y=st["A"], H=st["H"], stream=stream)
 
             def b2():
-                csp.spmm_bwd(h2, st["dY"], st["A"], st["dA"], st["dW2"], stream=stream)
-                torch.mul(st["dA"], st["G"], out=st["dH"])
+                csp.spmm_bwd_act(h2, st["dY"], st["A"], st["H"], act="gelu", dX=st["dH"], dW=st["dW2"],
+                                 stream=stream)
 
             out.append(("forward 1", h1, f1, fwd_name, bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
             out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream), fwd_name,
@@ -552,7 +546,7 @@ def main():
                   "linear": "spmm_fwd + spmm_bwd (dX and dW)",
                   "dst": f"spmm_fwd + spmm_bwd + restructure({n_prune} of {layers[0].nnz})",
                   "inference": "spmm_fwd",
-                  "mlp": "fwd1, GELU, fwd2, bwd2 (dA, dW2), GELU', bwd1 (dX, dW1)"}[kind]
+                  "mlp": "fwd1 with GELU epilogue, fwd2, bwd2 (dA * GELU'(H) epilogue, dW2), bwd1 (dX, dW1)"}[kind]
     rec = {
         "metric": "SpMM fwd+bwd effective GB/s and GFLOP/s (2*nnz*B); % of HBM roofline",
         "value": round(value, 2),

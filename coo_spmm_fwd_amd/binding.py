@@ -17,7 +17,9 @@ LIB_PATH = os.path.join(HERE, "libcoospmm.so")
 CSP_F32, CSP_BF16 = 0, 1
 STATUS = {0: "CSP_OK", -1: "CSP_ERR_INVALID_ARG", -2: "CSP_ERR_INDEX_RANGE", -3: "CSP_ERR_DUPLICATE",
           -4: "CSP_ERR_NO_MEMORY", -5: "CSP_ERR_HIP", -6: "CSP_ERR_DTYPE"}
+CSP_ACT_NONE, CSP_ACT_GELU = 0, 1
 EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_bwd_input", "spmm_bwd_values", "spmm_bwd",
+            "spmm_fwd_act", "spmm_bwd_input_act", "spmm_bwd_act",
             "restructure", "sparse_layer_nnz", "sparse_layer_shape", "sparse_layer_export",
             "sparse_layer_export_index", "sparse_layer_values", "sparse_layer_set_values", "sparse_layer_time_next",
             "sparse_layer_last_error"]
@@ -54,6 +56,12 @@ def load(path: str = LIB_PATH):
     L.spmm_bwd_values.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p]
     L.spmm_bwd.restype = c_int
     L.spmm_bwd.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_void_p]
+    L.spmm_fwd_act.restype = c_int
+    L.spmm_fwd_act.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_void_p, c_void_p]
+    L.spmm_bwd_input_act.restype = c_int
+    L.spmm_bwd_input_act.argtypes = [c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p]
+    L.spmm_bwd_act.restype = c_int
+    L.spmm_bwd_act.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p, c_void_p]
     L.restructure.restype = c_int
     L.restructure.argtypes = [c_void_p, c_int64, c_uint64, c_uint64, c_float, c_void_p]
     L.sparse_layer_nnz.restype = c_int64
@@ -207,6 +215,62 @@ def spmm_bwd(layer: int, dY, X, dX=None, dW=None, stream=None):
     dxp = _dev(dX, "dX", _torch_dtype(dt), (B, in_))
     wp = _dev(dW, "dW", _torch().float32, (nnz,))
     _check(load().spmm_bwd(c_void_p(layer), gp, xp, B, dxp, wp, _stream(stream)))
+    return dX, dW
+
+
+def _act_code(act) -> int:
+    codes = {None: CSP_ACT_NONE, "none": CSP_ACT_NONE, "gelu": CSP_ACT_GELU, CSP_ACT_NONE: CSP_ACT_NONE,
+             CSP_ACT_GELU: CSP_ACT_GELU}
+    if act not in codes:
+        raise ValueError(f"unknown activation {act!r}")
+    return codes[act]
+
+
+def spmm_fwd_act(layer: int, X, bias=None, act="gelu", Y=None, H=None, stream=None):
+    """Y = act(X W^T + bias); H (optional output) receives the pre-activation X W^T + bias."""
+    out, in_, dt = sparse_layer_shape(layer)
+    B = int(X.shape[0])
+    td = _torch_dtype(dt)
+    xp = _dev(X, "X", td, (B, in_))
+    bp = None if bias is None else _dev(bias, "bias", td, (out,))
+    if Y is None:
+        Y = _torch().empty((B, out), dtype=X.dtype, device=X.device)
+    yp = _dev(Y, "Y", td, (B, out))
+    hp = None if H is None else _dev(H, "H", td, (B, out))
+    _check(load().spmm_fwd_act(c_void_p(layer), xp, B, bp, _act_code(act), yp, hp, _stream(stream)))
+    return Y
+
+
+def spmm_bwd_input_act(layer: int, dY, H_in, act="gelu", dX=None, stream=None):
+    """dX = (dY W) * act'(H_in): the input gradient through the activation that produced the layer's input."""
+    out, in_, dt = sparse_layer_shape(layer)
+    B = int(dY.shape[0])
+    td = _torch_dtype(dt)
+    gp = _dev(dY, "dY", td, (B, out))
+    hp = None if H_in is None else _dev(H_in, "H_in", td, (B, in_))
+    if dX is None:
+        dX = _torch().empty((B, in_), dtype=dY.dtype, device=dY.device)
+    xp = _dev(dX, "dX", td, (B, in_))
+    _check(load().spmm_bwd_input_act(c_void_p(layer), gp, B, _act_code(act), hp, xp, _stream(stream)))
+    return dX
+
+
+def spmm_bwd_act(layer: int, dY, X, H_in, act="gelu", dX=None, dW=None, stream=None):
+    """spmm_bwd with dX = (dY W) * act'(H_in); dW as in spmm_bwd_values."""
+    out, in_, dt = sparse_layer_shape(layer)
+    nnz = sparse_layer_nnz(layer)
+    B = int(X.shape[0])
+    td = _torch_dtype(dt)
+    gp = _dev(dY, "dY", td, (B, out))
+    xp = _dev(X, "X", td, (B, in_))
+    hp = None if H_in is None else _dev(H_in, "H_in", td, (B, in_))
+    if dX is None:
+        dX = _torch().empty((B, in_), dtype=X.dtype, device=X.device)
+    if dW is None:
+        dW = _torch().empty((nnz,), dtype=_torch().float32, device=X.device)
+    dxp = _dev(dX, "dX", td, (B, in_))
+    wp = _dev(dW, "dW", _torch().float32, (nnz,))
+    _check(load().spmm_bwd_act(c_void_p(layer), gp, xp, B, _act_code(act), hp, dxp, wp, _stream(stream)))
     return dX, dW
 
 

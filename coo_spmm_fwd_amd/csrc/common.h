@@ -175,10 +175,19 @@ inline int64_t task_cap(int64_t nseg, int64_t nnz) { return nseg + (nnz + kTaskC
 // ---------------------------------------------------------------------------
 // spmm.hip : the three products
 // ---------------------------------------------------------------------------
-csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, hipStream_t s);
-csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, hipStream_t s);
+// Forward epilogue: y = sum + bias (bias optional), pre = y (optional), out = GELU(y) if gelu else y.
+struct FwdEpilogue {
+    const void *bias = nullptr;
+    void *pre = nullptr;
+    int gelu = 0;
+};
+// fe == nullptr: plain forward.  act_in != nullptr: the input gradient is
+// multiplied by GELU'(act_in[b, c]) (act_in [B, in], layer dtype).
+csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s);
+csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s);
 csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s);
-csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, hipStream_t s);
+csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
+                      hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // restructure.hip

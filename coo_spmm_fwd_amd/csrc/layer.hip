@@ -220,24 +220,50 @@ csp_status spmm_fwd(sparse_layer_t L, const void *X, int64_t B, void *Y, void *s
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
     DeviceGuard g(L->device);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
-    return launch_fwd(L, X, B, Y, (hipStream_t)stream);
+    return launch_fwd(L, X, B, Y, nullptr, (hipStream_t)stream);
+}
+
+csp_status spmm_fwd_act(sparse_layer_t L, const void *X, int64_t B, const void *bias, csp_act act, void *Y, void *H,
+                        void *stream)
+{
+    if (!L || !X || !Y) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_fwd_act");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+    if (H && H == Y) return set_error(CSP_ERR_INVALID_ARG, "H must not overlap Y");
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    FwdEpilogue fe;
+    fe.bias = bias;
+    fe.pre = H;
+    fe.gelu = act == CSP_ACT_GELU;
+    return launch_fwd(L, X, B, Y, &fe, (hipStream_t)stream);
 }
 
 csp_status spmm_bwd_input(sparse_layer_t L, const void *dY, int64_t B, void *dX, void *stream)
 {
     if (!L || !dY || !dX) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_input");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
-    if (L->dtype != CSP_F32) return set_error(CSP_ERR_DTYPE, "spmm_bwd_input supports fp32 layers only");
     DeviceGuard g(L->device);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
-    return launch_bwd_input(L, dY, B, dX, (hipStream_t)stream);
+    return launch_bwd_input(L, dY, B, dX, nullptr, (hipStream_t)stream);
+}
+
+csp_status spmm_bwd_input_act(sparse_layer_t L, const void *dY, int64_t B, csp_act act, const void *H_in, void *dX,
+                              void *stream)
+{
+    if (!L || !dY || !dX) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_input_act");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+    if (act == CSP_ACT_GELU && !H_in) return set_error(CSP_ERR_INVALID_ARG, "CSP_ACT_GELU needs H_in");
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    return launch_bwd_input(L, dY, B, dX, act == CSP_ACT_GELU ? H_in : nullptr, (hipStream_t)stream);
 }
 
 csp_status spmm_bwd_values(sparse_layer_t L, const void *dY, const void *X, int64_t B, float *dW, void *stream)
 {
     if (!L || !dY || !X || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_values");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
-    if (L->dtype != CSP_F32) return set_error(CSP_ERR_DTYPE, "spmm_bwd_values supports fp32 layers only");
     DeviceGuard g(L->device);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     return launch_bwd_values(L, dY, X, B, dW, (hipStream_t)stream);
@@ -247,10 +273,21 @@ csp_status spmm_bwd(sparse_layer_t L, const void *dY, const void *X, int64_t B, 
 {
     if (!L || !dY || !X || !dX || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
-    if (L->dtype != CSP_F32) return set_error(CSP_ERR_DTYPE, "spmm_bwd supports fp32 layers only");
     DeviceGuard g(L->device);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
-    return launch_bwd(L, dY, X, B, dX, dW, (hipStream_t)stream);
+    return launch_bwd(L, dY, X, B, dX, dW, nullptr, (hipStream_t)stream);
+}
+
+csp_status spmm_bwd_act(sparse_layer_t L, const void *dY, const void *X, int64_t B, csp_act act, const void *H_in,
+                        void *dX, float *dW, void *stream)
+{
+    if (!L || !dY || !X || !dX || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_act");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+    if (act == CSP_ACT_GELU && !H_in) return set_error(CSP_ERR_INVALID_ARG, "CSP_ACT_GELU needs H_in");
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    return launch_bwd(L, dY, X, B, dX, dW, act == CSP_ACT_GELU ? H_in : nullptr, (hipStream_t)stream);
 }
 
 csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_t step, float regrow_value,

@@ -137,6 +137,45 @@ __global__ __launch_bounds__(256) void k_batch_minor(const T *__restrict__ X1, I
     }
 }
 
+// ------------------------------------------------------------- epilogues
+// What happens to a segment sum before it is stored:
+//   kEpiNone      out = sum;
+//   kEpiForward   y = sum + bias[seg] (bias optional); pre[b, seg] = y (optional);
+//                 out = GELU(y) when gelu is set, else y;
+//   kEpiActGrad   out = sum * GELU'(act_in[b, seg]): the input gradient of this
+//                 layer times the derivative of the activation whose input was
+//                 act_in (the previous layer's pre-activation).
+// GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)); GELU'(x) = Phi(x) + x * phi(x).
+enum : int { kEpiNone = 0, kEpiForward = 1, kEpiActGrad = 2 };
+
+struct Epi {
+    const void *bias = nullptr;    // [n_seg], layer dtype
+    void *pre = nullptr;           // [B, n_seg], layer dtype
+    const void *act_in = nullptr;  // [B, n_seg], layer dtype
+    int gelu = 0;
+};
+
+__device__ inline float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ inline float gelu_grad_f(float x)
+{
+    return 0.5f * (1.0f + erff(x * 0.70710678118654752f)) + x * 0.39894228040143268f * expf(-0.5f * x * x);
+}
+
+template <int E, class D>
+__device__ inline typename D::T finish_out(float acc, int64_t b, int64_t seg, int64_t n_seg, const Epi &ep)
+{
+    using T = typename D::T;
+    if constexpr (E == kEpiNone) {
+        return D::from_f(acc);
+    } else if constexpr (E == kEpiForward) {
+        const float y = acc + (ep.bias ? D::load((const T *)ep.bias, seg) : 0.f);
+        if (ep.pre) ((T *)ep.pre)[b * n_seg + seg] = D::from_f(y);
+        return D::from_f(ep.gelu ? gelu_f(y) : y);
+    } else {
+        return D::from_f(acc * gelu_grad_f(D::load((const T *)ep.act_in, b * n_seg + seg)));
+    }
+}
+
 // Lane map.  Each lane owns VW consecutive batch values of an entry (one
 // 16-byte load when VW = 4), LPE = LD/VW lanes cover one entry, and the
 // wave steps through S = 64/LPE entries at a time.  A pass loads 256 of the
@@ -235,11 +274,11 @@ __device__ inline Task load_task(const int4 *__restrict__ desc, int64_t t)
 // Input gradient: column tasks over (rows_by_col, column-ordered value
 // copy, dY).  A split segment's task stores its partial sums instead
 // (slot >= 0); the fixup launch finishes the segment.
-template <int LD, class D, bool kWide>
+template <int LD, class D, bool kWide, int E>
 __device__ __attribute__((always_inline)) inline void segment_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ idx,
                                     const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
                                     int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
-                                    typename D::T *__restrict__ out)
+                                    typename D::T *__restrict__ out, const Epi &ep)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
@@ -305,32 +344,33 @@ __device__ __attribute__((always_inline)) inline void segment_task(const int4 *_
             for (int w = 0; w < VW; ++w) {
                 const int64_t b = (int64_t)ch * LD + q * VW + w;
                 if (b >= B) continue;
-                if (T.slot < 0) out[b * n_seg + T.seg] = D::from_f(acc[w]);
+                if (T.slot < 0) out[b * n_seg + T.seg] = finish_out<E, D>(acc[w], b, T.seg, n_seg, ep);
                 else partial[((int64_t)T.slot * nch + ch) * LD + q * VW + w] = acc[w];
             }
         }
     }
 }
 
-template <int LD, class D, bool kWide>
+template <int LD, class D, bool kWide, int E>
 __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
                                                       const int32_t *__restrict__ idx,
                                                       const typename D::T *__restrict__ vals,
                                                       const typename D::T *__restrict__ opT, int64_t n_op,
                                                       int64_t n_seg, int64_t B, int nch,
-                                                      float *__restrict__ partial, typename D::T *__restrict__ out)
+                                                      float *__restrict__ partial, typename D::T *__restrict__ out,
+                                                      Epi ep)
 {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    segment_task<LD, D, kWide>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out);
+    segment_task<LD, D, kWide, E>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
 }
 
 // Finish split segments: out[b, seg] = sum over the segment's tasks, in task
 // order, of their partial sums.  One thread per (split segment, batch index).
-template <class D>
+template <class D, int E>
 __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ split, int64_t nsplit,
                                                      const float *__restrict__ partial, int64_t B, int ld, int nch,
-                                                     int64_t n_seg, typename D::T *__restrict__ out)
+                                                     int64_t n_seg, typename D::T *__restrict__ out, Epi ep)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nsplit * B) return;
@@ -349,7 +389,7 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
         for (int j = 0; j < 8; ++j) tot += v[j];
     }
     for (; p < r.z; ++p) tot += src[p * stride];
-    out[bg * n_seg + r.x] = D::from_f(tot);
+    out[bg * n_seg + r.x] = finish_out<E, D>(tot, bg, r.x, n_seg, ep);
 }
 
 // ----------------------------------------------- value gradient, row order
@@ -358,10 +398,10 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
 // lane of the entry's group writes the same value to the same word, so no
 // lane test is needed -- and each 64-entry block leaves as one coalesced row
 // in canonical order.
-template <int LD, bool kWide>
+template <int LD, class D, bool kWide>
 __device__ __attribute__((always_inline)) inline void values_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ cols,
-                                   const float *__restrict__ XT, const float *__restrict__ dYT, int64_t in,
-                                   int64_t out, int nch, float *__restrict__ dW)
+                                   const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
+                                   int64_t in, int64_t out, int nch, float *__restrict__ dW)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
@@ -372,7 +412,7 @@ __device__ __attribute__((always_inline)) inline void values_task(const int4 *__
     for (int ch = 0; ch < nch; ++ch) {
         float dy[VW];
         load_vec<VW>(dYT + ((int64_t)ch * out + T.seg) * LD + q * VW, dy);
-        const float *xt = XT + (int64_t)ch * in * LD + q * VW;
+        const typename D::T *xt = XT + (int64_t)ch * in * LD + q * VW;
         for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
             const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
             int32_t ci[kPerLane];
@@ -412,15 +452,16 @@ __device__ __attribute__((always_inline)) inline void values_task(const int4 *__
     }
 }
 
-template <int LD, bool kWide>
+template <int LD, class D, bool kWide>
 __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ desc, int64_t ntasks,
-                                                     const int32_t *__restrict__ cols, const float *__restrict__ XT,
-                                                     const float *__restrict__ dYT, int64_t in, int64_t out,
+                                                     const int32_t *__restrict__ cols,
+                                                     const typename D::T *__restrict__ XT,
+                                                     const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
                                                      int nch, float *__restrict__ dW)
 {
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    values_task<LD, kWide>(desc, t, cols, XT, dYT, in, out, nch, dW);
+    values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, nch, dW);
 }
 
 // --------------------------------------------------- both gradients
@@ -428,15 +469,16 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
 // latency chains overlap: even/odd blocks alternate between input-gradient
 // column tasks and value-gradient row tasks, the longer list's surplus
 // blocks come last.
-template <int LD, bool kWide>
+template <int LD, class D, bool kWide, int E>
 __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_desc, int64_t ncol_tasks,
                                                    const int4 *__restrict__ row_desc, int64_t nrow_tasks,
                                                    const int32_t *__restrict__ rows_by_col,
-                                                   const float *__restrict__ vals_c, const int32_t *__restrict__ cols,
-                                                   const float *__restrict__ XT, const float *__restrict__ dYT,
-                                                   int64_t in, int64_t out, int64_t B, int nch,
-                                                   float *__restrict__ partial, float *__restrict__ dX,
-                                                   float *__restrict__ dW)
+                                                   const typename D::T *__restrict__ vals_c,
+                                                   const int32_t *__restrict__ cols,
+                                                   const typename D::T *__restrict__ XT,
+                                                   const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
+                                                   int64_t B, int nch, float *__restrict__ partial,
+                                                   typename D::T *__restrict__ dX, float *__restrict__ dW, Epi ep)
 {
     const int64_t ncb = (ncol_tasks + 3) / 4, nrb = (nrow_tasks + 3) / 4;
     const int64_t m = ncb < nrb ? ncb : nrb;
@@ -453,9 +495,9 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
     const int64_t t = blk * 4 + (threadIdx.x >> 6);
     if (col) {
         if (t < ncol_tasks)
-            segment_task<LD, F32, kWide>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, nch, partial, dX);
+            segment_task<LD, D, kWide, E>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, nch, partial, dX, ep);
     } else if (t < nrow_tasks) {
-        values_task<LD, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW);
+        values_task<LD, D, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW);
     }
 }
 
@@ -543,20 +585,21 @@ csp_status batch_minor(csp_layer *L, int64_t B, const void *X1, int64_t n1, void
 // Operands whose chunk holds 2^30 or more elements need 64-bit offsets.
 inline bool wide_operand(int64_t n, int ld) { return n * (int64_t)ld >= (int64_t(1) << 30); }
 
-template <class D>
-csp_status split_fixup(csp_layer *L, const TaskList &TL, int64_t B, int64_t n_seg, void *out, hipStream_t s)
+template <class D, int E>
+csp_status split_fixup(csp_layer *L, const TaskList &TL, int64_t B, int64_t n_seg, void *out, const Epi &ep,
+                       hipStream_t s)
 {
     if (TL.nsplit == 0) return CSP_OK;
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
-    k_split_fixup<D><<<(unsigned)ceil_div(TL.nsplit * B, 256), 256, 0, s>>>(TL.split, TL.nsplit, L->act.partial, B, ld,
-                                                                          nch, n_seg, (typename D::T *)out);
+    k_split_fixup<D, E><<<(unsigned)ceil_div(TL.nsplit * B, 256), 256, 0, s>>>(
+        TL.split, TL.nsplit, L->act.partial, B, ld, nch, n_seg, (typename D::T *)out, ep);
     CSP_LAUNCHED("k_split_fixup");
     return CSP_OK;
 }
 
-template <class D>
-csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, hipStream_t s)
+template <class D, int E>
+csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const Epi &ep, hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
@@ -564,66 +607,48 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, hipStr
     const TaskList &TL = L->row_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
-#define CSP_FWD(LDV, W)                                                                                          \
-    k_segment_spmm<LDV, D, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, \
-                                                   L->in, L->out, B, nch, L->act.partial, (T *)Y)
+#define CSP_FWD(LDV, W)                                                                                             \
+    k_segment_spmm<LDV, D, W, E><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, \
+                                                      L->in, L->out, B, nch, L->act.partial, (T *)Y, ep)
     CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_FWD);
 #undef CSP_FWD
     CSP_LAUNCHED("k_segment_spmm (forward)");
     timing_mark(L, false, s);
-    return split_fixup<D>(L, TL, B, L->out, Y, s);
+    return split_fixup<D, E>(L, TL, B, L->out, Y, ep, s);
 }
 
-}  // namespace
-
-csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, hipStream_t s)
+template <class D, int E>
+csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX, const Epi &ep, hipStream_t s)
 {
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
-    st = batch_minor(L, B, X, L->in, L->act.a, nullptr, 0, nullptr, s);
-    if (st != CSP_OK) return st;
-    const void *xt = B == 1 ? X : L->act.a;
-    return L->dtype == CSP_BF16 ? fwd_dispatch<BF16>(L, xt, B, Y, s) : fwd_dispatch<F32>(L, xt, B, Y, s);
-}
-
-csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, hipStream_t s)
-{
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
-    st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
-    if (st != CSP_OK) return st;
-    const float *dyt = (const float *)(B == 1 ? dY : L->act.a);
+    using T = typename D::T;
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->col_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
-#define CSP_DX(LDV, W)                                                                                           \
-    k_segment_spmm<LDV, F32, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, (const float *)L->vals_c, \
-                                                     dyt, L->out, L->in, B, nch, L->act.partial, (float *)dX)
+#define CSP_DX(LDV, W)                                                                                        \
+    k_segment_spmm<LDV, D, W, E><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, (const T *)L->vals_c, \
+                                                      (const T *)dYT, L->out, L->in, B, nch, L->act.partial,    \
+                                                      (T *)dX, ep)
     CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_DX);
 #undef CSP_DX
     CSP_LAUNCHED("k_segment_spmm (input gradient)");
     timing_mark(L, false, s);
-    return split_fixup<F32>(L, TL, B, L->in, dX, s);
+    return split_fixup<D, E>(L, TL, B, L->in, dX, ep, s);
 }
 
-csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s)
+template <class D>
+csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, float *dW, hipStream_t s)
 {
-    if (L->nnz == 0) return CSP_OK;
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
-    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
-    if (st != CSP_OK) return st;
-    const float *xt = (const float *)(B == 1 ? X : L->act.a);
-    const float *dyt = (const float *)(B == 1 ? dY : L->act.b);
+    using T = typename D::T;
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->row_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
-#define CSP_DW(LDV, W) \
-    k_values_rows<LDV, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, xt, dyt, L->in, L->out, nch, dW)
+#define CSP_DW(LDV, W)                                                                                            \
+    k_values_rows<LDV, D, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, (const T *)XT, (const T *)dYT, L->in, \
+                                                  L->out, nch, dW)
     CSP_LD_SWITCH(ld, wide_operand(L->in > L->out ? L->in : L->out, ld), CSP_DW);
 #undef CSP_DW
     CSP_LAUNCHED("k_values_rows");
@@ -631,14 +656,11 @@ csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_
     return CSP_OK;
 }
 
-csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, hipStream_t s)
+template <class D, int E>
+csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, void *dX, float *dW, const Epi &ep,
+                        hipStream_t s)
 {
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
-    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
-    if (st != CSP_OK) return st;
-    const float *xt = (const float *)(B == 1 ? X : L->act.a);
-    const float *dyt = (const float *)(B == 1 ? dY : L->act.b);
+    using T = typename D::T;
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
     const TaskList &CT = L->col_tasks, &RT = L->row_tasks;
@@ -648,37 +670,112 @@ csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, vo
     // interleaved passes gather from both batch-minor tables at once; when the
     // tables together exceed about half an XCD's 4 MiB L2 they evict each
     // other, so the passes run as two launches instead.
-    const int64_t table_bytes = (int64_t)sizeof(float) * ld * (L->in + L->out);
+    const int64_t table_bytes = (int64_t)L->esz * ld * (L->in + L->out);
     if (table_bytes > (int64_t(2) << 20)) {
         const unsigned gx = (unsigned)ceil_div(CT.count, 4), gw = (unsigned)ceil_div(nrow, 4);
         timing_mark(L, true, s);
-#define CSP_DX2(LDV, W)                                                                                        \
-    k_segment_spmm<LDV, F32, W><<<gx, 256, 0, s>>>(CT.desc, CT.count, L->rows_by_col, (const float *)L->vals_c, \
-                                                   dyt, L->out, L->in, B, nch, L->act.partial, (float *)dX)
+#define CSP_DX2(LDV, W)                                                                                     \
+    k_segment_spmm<LDV, D, W, E><<<gx, 256, 0, s>>>(CT.desc, CT.count, L->rows_by_col, (const T *)L->vals_c, \
+                                                    (const T *)dYT, L->out, L->in, B, nch, L->act.partial,    \
+                                                    (T *)dX, ep)
         CSP_LD_SWITCH(ld, wide, CSP_DX2);
 #undef CSP_DX2
         CSP_LAUNCHED("k_segment_spmm (input gradient)");
         if (gw > 0) {
-#define CSP_DW2(LDV, W) \
-    k_values_rows<LDV, W><<<gw, 256, 0, s>>>(RT.desc, nrow, L->cols, xt, dyt, L->in, L->out, nch, dW)
+#define CSP_DW2(LDV, W)                                                                                           \
+    k_values_rows<LDV, D, W><<<gw, 256, 0, s>>>(RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
+                                                nch, dW)
             CSP_LD_SWITCH(ld, wide, CSP_DW2);
 #undef CSP_DW2
             CSP_LAUNCHED("k_values_rows");
         }
         timing_mark(L, false, s);
-        return split_fixup<F32>(L, CT, B, L->in, dX, s);
+        return split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
     }
     const unsigned grid = (unsigned)(ceil_div(CT.count, 4) + ceil_div(nrow, 4));
     timing_mark(L, true, s);
-#define CSP_BOTH(LDV, W)                                                                                            \
-    k_gradients<LDV, W><<<grid, 256, 0, s>>>(CT.desc, CT.count, RT.desc, nrow, L->rows_by_col,                    \
-                                             (const float *)L->vals_c, L->cols, xt, dyt, L->in, L->out, B, nch,   \
-                                             L->act.partial, (float *)dX, dW)
+#define CSP_BOTH(LDV, W)                                                                                         \
+    k_gradients<LDV, D, W, E><<<grid, 256, 0, s>>>(CT.desc, CT.count, RT.desc, nrow, L->rows_by_col,           \
+                                                   (const T *)L->vals_c, L->cols, (const T *)XT, (const T *)dYT, \
+                                                   L->in, L->out, B, nch, L->act.partial, (T *)dX, dW, ep)
     CSP_LD_SWITCH(ld, wide, CSP_BOTH);
 #undef CSP_BOTH
     CSP_LAUNCHED("k_gradients");
     timing_mark(L, false, s);
-    return split_fixup<F32>(L, CT, B, L->in, dX, s);
+    return split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
+}
+
+Epi make_epi(const FwdEpilogue *fe)
+{
+    Epi ep;
+    if (fe) {
+        ep.bias = fe->bias;
+        ep.pre = fe->pre;
+        ep.gelu = fe->gelu;
+    }
+    return ep;
+}
+
+}  // namespace
+
+csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s)
+{
+    csp_status st = ensure_act(L, B);
+    if (st != CSP_OK) return st;
+    st = batch_minor(L, B, X, L->in, L->act.a, nullptr, 0, nullptr, s);
+    if (st != CSP_OK) return st;
+    const void *xt = B == 1 ? X : L->act.a;
+    const Epi ep = make_epi(fe);
+    if (L->dtype == CSP_BF16)
+        return fe ? fwd_dispatch<BF16, kEpiForward>(L, xt, B, Y, ep, s) : fwd_dispatch<BF16, kEpiNone>(L, xt, B, Y, ep, s);
+    return fe ? fwd_dispatch<F32, kEpiForward>(L, xt, B, Y, ep, s) : fwd_dispatch<F32, kEpiNone>(L, xt, B, Y, ep, s);
+}
+
+csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s)
+{
+    csp_status st = ensure_act(L, B);
+    if (st != CSP_OK) return st;
+    st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
+    if (st != CSP_OK) return st;
+    const void *dyt = B == 1 ? dY : L->act.a;
+    Epi ep;
+    ep.act_in = act_in;
+    if (L->dtype == CSP_BF16)
+        return act_in ? bwd_input_dispatch<BF16, kEpiActGrad>(L, dyt, B, dX, ep, s)
+                      : bwd_input_dispatch<BF16, kEpiNone>(L, dyt, B, dX, ep, s);
+    return act_in ? bwd_input_dispatch<F32, kEpiActGrad>(L, dyt, B, dX, ep, s)
+                  : bwd_input_dispatch<F32, kEpiNone>(L, dyt, B, dX, ep, s);
+}
+
+csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s)
+{
+    if (L->nnz == 0) return CSP_OK;
+    csp_status st = ensure_act(L, B);
+    if (st != CSP_OK) return st;
+    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
+    if (st != CSP_OK) return st;
+    const void *xt = B == 1 ? X : L->act.a;
+    const void *dyt = B == 1 ? dY : L->act.b;
+    return L->dtype == CSP_BF16 ? bwd_values_dispatch<BF16>(L, xt, dyt, B, dW, s)
+                                : bwd_values_dispatch<F32>(L, xt, dyt, B, dW, s);
+}
+
+csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
+                      hipStream_t s)
+{
+    csp_status st = ensure_act(L, B);
+    if (st != CSP_OK) return st;
+    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
+    if (st != CSP_OK) return st;
+    const void *xt = B == 1 ? X : L->act.a;
+    const void *dyt = B == 1 ? dY : L->act.b;
+    Epi ep;
+    ep.act_in = act_in;
+    if (L->dtype == CSP_BF16)
+        return act_in ? bwd_dispatch<BF16, kEpiActGrad>(L, xt, dyt, B, dX, dW, ep, s)
+                      : bwd_dispatch<BF16, kEpiNone>(L, xt, dyt, B, dX, dW, ep, s);
+    return act_in ? bwd_dispatch<F32, kEpiActGrad>(L, xt, dyt, B, dX, dW, ep, s)
+                  : bwd_dispatch<F32, kEpiNone>(L, xt, dyt, B, dX, dW, ep, s);
 }
 
 }  // namespace csp

@@ -51,6 +51,12 @@ typedef enum {
     CSP_BF16 = 1 /* bf16 values and activations, fp32 accumulation, bf16 output */
 } csp_dtype;
 
+/* Activation of the fused epilogues: GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt 2)). */
+typedef enum {
+    CSP_ACT_NONE = 0,
+    CSP_ACT_GELU = 1
+} csp_act;
+
 /*
  * sparse_layer_create -- build a layer from COO triples (the page's COO
  * weight storage, Abstract).
@@ -85,8 +91,8 @@ csp_status spmm_fwd(sparse_layer_t layer, const void *X, int64_t B, void *Y, voi
  * spmm_bwd_input -- gradient with respect to the layer input (Abstract:
  * gradients are backpropagated on the sparse storage):
  *     dX[b, c] = sum over stored k with col_k = c of v_k * dY[b, row_k]
- * i.e. dX = dY W.  dY [B, out], dX [B, in], fp32 layers only (CSP_ERR_DTYPE
- * for bf16).
+ * i.e. dX = dY W.  dY [B, out], dX [B, in], both in the layer's dtype
+ * (bf16 layers: bf16 in and out, fp32 accumulation).
  */
 csp_status spmm_bwd_input(sparse_layer_t layer, const void *dY, int64_t B, void *dX, void *stream);
 
@@ -95,7 +101,8 @@ csp_status spmm_bwd_input(sparse_layer_t layer, const void *dY, int64_t B, void 
  * sampled dense-dense product:
  *     dW[k] = sum_b dY[b, row_k] * X[b, col_k]   for every stored k
  * dW [nnz] is fp32 and in canonical (row, col) order (the order of
- * sparse_layer_export and sparse_layer_values).  fp32 layers only.
+ * sparse_layer_export and sparse_layer_values).  dY and X have the layer's
+ * dtype (bf16 products are exact in fp32); dW is fp32 for either dtype.
  */
 csp_status spmm_bwd_values(sparse_layer_t layer, const void *dY, const void *X, int64_t B, float *dW,
                            void *stream);
@@ -103,11 +110,41 @@ csp_status spmm_bwd_values(sparse_layer_t layer, const void *dY, const void *X, 
 /*
  * spmm_bwd -- both gradients of one backward step in a single pass over the
  * transposed view: dX as in spmm_bwd_input and dW as in spmm_bwd_values, with
- * each gathered dY row used for both.  Same layouts and results (within the
- * fp32 tolerance of each) as the two separate calls; fp32 layers only.
+ * each gathered dY row used for both.  Same layouts, dtypes and results
+ * (within the tolerance of each) as the two separate calls.
  */
 csp_status spmm_bwd(sparse_layer_t layer, const void *dY, const void *X, int64_t B, void *dX, float *dW,
                     void *stream);
+
+/*
+ * Fused epilogues for a stack of layers with an activation between them (the
+ * page reports end-to-end GPT-2 training with truly sparse layers, Abstract;
+ * its MLP block is linear -> GELU -> linear).  The activation is applied where
+ * the segment sum is stored, so it costs no extra pass over the activations.
+ *
+ * spmm_fwd_act -- Y = act(X W^T + bias), computed in fp32 from the fp32 sum:
+ *   bias [out] in the layer dtype, or NULL for none;
+ *   act  CSP_ACT_NONE or CSP_ACT_GELU (else CSP_ERR_INVALID_ARG);
+ *   H    [B, out] in the layer dtype, or NULL: receives the pre-activation
+ *        X W^T + bias (what the backward needs); must not overlap Y.
+ */
+csp_status spmm_fwd_act(sparse_layer_t layer, const void *X, int64_t B, const void *bias, csp_act act, void *Y,
+                        void *H, void *stream);
+
+/*
+ * spmm_bwd_input_act -- the input gradient times the derivative of the
+ * activation that produced this layer's input:
+ *     dX = (dY W) * act'(H_in)   (elementwise; GELU'(x) = Phi(x) + x phi(x))
+ * H_in [B, in] is that activation's input (the previous layer's H), layer
+ * dtype; required for CSP_ACT_GELU, ignored for CSP_ACT_NONE (then this is
+ * spmm_bwd_input).
+ */
+csp_status spmm_bwd_input_act(sparse_layer_t layer, const void *dY, int64_t B, csp_act act, const void *H_in,
+                              void *dX, void *stream);
+
+/* spmm_bwd_act -- spmm_bwd with the input gradient of spmm_bwd_input_act; dW is unchanged. */
+csp_status spmm_bwd_act(sparse_layer_t layer, const void *dY, const void *X, int64_t B, csp_act act,
+                        const void *H_in, void *dX, float *dW, void *stream);
 
 /*
  * restructure -- one prune-and-regrow step of dynamic sparse training

@@ -1,0 +1,102 @@
+"""Fused epilogues against the oracle: forward with bias and GELU (and the pre-activation output),
+input gradient times GELU' of the previous layer's pre-activation, in fp32 and bf16, including
+rows and columns long enough to be split across tasks (their sums finish in the fixup launch).
+
+Tolerances.  The oracle's pre-activation y and S = sum |terms| + |bias| are fp64.  GELU' lies in
+[-0.17, 1.13], so an fp32 sum within 1e-5 * S moves GELU(y) by at most 1.13e-5 * S; the fp32
+evaluation of erf adds at most a few ulp of |y| <= S: 1.3e-5 * S.  The same bound covers
+sum * GELU'(h) for the input gradient.  bf16 outputs: 1.2e-2 * S."""
+import numpy as np
+import pytest
+
+import oracle
+from coo_spmm_fwd_amd import binding as csp
+from coo_spmm_fwd_amd import workloads as W
+from tests.gpu_util import as_f64, assert_within, dev, host
+
+pytestmark = pytest.mark.gpu
+ACT_REL = {"f32": 1.3e-5, "bf16": 1.2e-2}
+PRE_REL = {"f32": 1e-5, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
+
+
+def bf16_or_f32(x, dtype):
+    x = np.asarray(x, np.float32)
+    return W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("out,in_,nnz,B", [(500, 700, 20000, 1), (500, 700, 20000, 16), (3, 5000, 9000, 8),
+                                           (900, 300, 30000, 70)])
+def test_forward_bias_gelu(orc, dtype, out, in_, nnz, B):
+    L = W.random_layer(out, in_, nnz, seed=out + in_, dtype=dtype, std=0.3)
+    h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        X = W.random_dense((B, in_), 3, dtype=dtype)
+        bias = bf16_or_f32(W.random_dense((out,), 4) * 0.5, dtype)
+        ref, S = orc.spmm_fwd(out, in_, L.rows, L.cols, L.vals, X)
+        y_ref = ref + as_f64(bias)[None, :]
+        S = S + np.abs(as_f64(bias))[None, :]
+        H = dev(np.zeros((B, out), np.uint16 if dtype == "bf16" else np.float32))
+        Y = host(csp.spmm_fwd_act(h, dev(X), bias=dev(bias), act="gelu", H=H))
+        assert_within(host(H), y_ref, S, PRE_REL[dtype], "pre-activation")
+        assert_within(Y, orc.gelu(y_ref), S, ACT_REL[dtype], "GELU output")
+        # no bias, no activation: the plain forward
+        Y0 = host(csp.spmm_fwd_act(h, dev(X), act="none"))
+        assert_within(Y0, ref, S, PRE_REL[dtype], "epilogue without bias or activation")
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("out,in_,nnz,B", [(700, 500, 20000, 1), (700, 500, 20000, 16), (5000, 3, 9000, 8),
+                                           (300, 900, 30000, 70)])
+def test_input_gradient_times_gelu_grad(orc, dtype, out, in_, nnz, B):
+    L = W.random_layer(out, in_, nnz, seed=out * 3 + in_, dtype=dtype, std=0.3)
+    h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(out, in_, L.rows, L.cols, L.vals)
+        X = W.random_dense((B, in_), 5, dtype=dtype)
+        dY = W.random_dense((B, out), 6, dtype=dtype)
+        Hin = bf16_or_f32(W.random_dense((B, in_), 7) * 2.0, dtype)
+        g = orc.gelu_grad(as_f64(Hin))
+        ref, S = orc.spmm_bwd_input(out, in_, L.rows, L.cols, L.vals, dY)
+        dX = host(csp.spmm_bwd_input_act(h, dev(dY), dev(Hin), act="gelu"))
+        assert_within(dX, ref * g, S, ACT_REL[dtype], "dX * GELU'")
+        dX2, dW = (host(t) for t in csp.spmm_bwd_act(h, dev(dY), dev(X), dev(Hin), act="gelu"))
+        assert_within(dX2, ref * g, S, ACT_REL[dtype], "fused dX * GELU'")
+        refw, Sw = orc.spmm_bwd_values(out, in_, c["rows"], c["cols"], dY, X)
+        assert_within(dW, refw, Sw, 1e-5, "fused dW")
+        dX3 = host(csp.spmm_bwd_input_act(h, dev(dY), None, act="none"))
+        assert_within(dX3, ref, S, PRE_REL[dtype], "act none is the plain input gradient")
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_epilogue_argument_errors():
+    L = W.random_layer(40, 30, 200, seed=2)
+    h = csp.sparse_layer_create(40, 30, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        X = dev(W.random_dense((2, 30), 1))
+        dY = dev(W.random_dense((2, 40), 2))
+        lib = csp.load()
+        import ctypes
+        st = lib.spmm_fwd_act(ctypes.c_void_p(h), ctypes.c_void_p(X.data_ptr()), 2, None, 7,
+                              ctypes.c_void_p(dY.data_ptr()), None, None)
+        assert st == -1 and "activation" in csp.sparse_layer_last_error()
+        Y = dY.clone()
+        with pytest.raises(csp.CspError) as e:
+            csp.spmm_fwd_act(h, X, act="gelu", Y=Y, H=Y)
+        assert e.value.status == -1
+        with pytest.raises(csp.CspError) as e:
+            csp.spmm_bwd_input_act(h, dY, None, act="gelu")
+        assert e.value.status == -1
+        with pytest.raises(csp.CspError) as e:
+            csp.spmm_bwd_act(h, dY, X, None, act="gelu")
+        assert e.value.status == -1
+    finally:
+        csp.sparse_layer_destroy(h)

@@ -143,16 +143,29 @@ def test_bf16_forward(orc):
         check_canonical(layer)
         for B in (1, 2, 4, 7, 64, 70):
             check_ops(orc, layer, B, seed=60 + B, rel=BF16_REL, ops=("fwd",))
-        X = dev(W.random_dense((4, 1100), 1, dtype="bf16"))
-        with pytest.raises(csp.CspError) as e:
-            csp.spmm_bwd_input(layer.h, dev(W.random_dense((4, 900), 2, dtype="bf16")))
-        assert e.value.status == -6
-        with pytest.raises(csp.CspError) as e:
-            csp.spmm_bwd_values(layer.h, dev(W.random_dense((4, 900), 2, dtype="bf16")), X)
-        assert e.value.status == -6
-        with pytest.raises(csp.CspError) as e:
-            csp.spmm_bwd(layer.h, dev(W.random_dense((4, 900), 2, dtype="bf16")), X)
-        assert e.value.status == -6
+    finally:
+        layer.close()
+
+
+def test_bf16_training(orc):
+    """bf16 backward: dX in bf16 (1e-2 * S), dW in fp32 from exact bf16 products (fp32 bound)."""
+    layer = Layer(orc, W.random_layer(700, 900, 30000, seed=18, dtype="bf16"))
+    L, c = layer.L, layer.canon
+    try:
+        for B in (1, 3, 16, 64, 70):
+            X = W.random_dense((B, L.in_), 80 + B, dtype="bf16")
+            dY = W.random_dense((B, L.out), 90 + B, dtype="bf16")
+            refx, Sx = orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dY)
+            refw, Sw = orc.spmm_bwd_values(L.out, L.in_, c["rows"], c["cols"], dY, X)
+            dX = host(csp.spmm_bwd_input(layer.h, dev(dY)))
+            assert dX.dtype == np.uint16
+            assert_within(dX, refx, Sx, BF16_REL, f"bf16 dX B={B}")
+            dW = host(csp.spmm_bwd_values(layer.h, dev(dY), dev(X)))
+            assert dW.dtype == np.float32
+            assert_within(dW, refw, Sw, FP32_REL, f"bf16 dW B={B}")
+            dX2, dW2 = (host(t) for t in csp.spmm_bwd(layer.h, dev(dY), dev(X)))
+            assert_within(dX2, refx, Sx, BF16_REL, f"bf16 fused dX B={B}")
+            assert_within(dW2, refw, Sw, FP32_REL, f"bf16 fused dW B={B}")
     finally:
         layer.close()
 
