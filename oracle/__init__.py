@@ -77,6 +77,10 @@ class Oracle:
                                          c_int64, c_uint64, c_uint64, c_uint32, c_void_p, c_void_p, c_void_p,
                                          c_void_p]
         L.oracle_gelu.restype = None
+        L.oracle_restructure_grad.restype = c_int
+        L.oracle_restructure_grad.argtypes = [c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_int,
+                                              c_int64, c_void_p, c_void_p, c_int64, c_uint32, c_void_p, c_void_p,
+                                              c_void_p]
         L.oracle_gelu.argtypes = [c_int64, c_void_p, c_void_p]
         L.oracle_gelu_grad.restype = None
         L.oracle_gelu_grad.argtypes = [c_int64, c_void_p, c_void_p]
@@ -188,6 +192,30 @@ class Oracle:
         if st != OK:
             raise ValueError(f"oracle_restructure failed with status {st}")
         return r, c, v, int(draws[0])
+
+    def restructure_grad(self, out, in_, rows_c, cols_c, vals_c, n_prune, dY, X, regrow_value=0.0):
+        """Prune as restructure; regrow the n_prune empty positions with the largest |(dY^T X)[r, c]|
+        (fp32 fused-multiply-add chain in batch order; ties to the smaller position)."""
+        rows_c, cols_c = self._i32(rows_c), self._i32(cols_c)
+        vals_c, dt = self._words(vals_c)
+        dY, dty = self._words(dY)
+        X, dtx = self._words(X)
+        assert dt == dty == dtx
+        B = X.shape[0]
+        assert X.shape == (B, in_) and dY.shape == (B, out)
+        nnz = rows_c.shape[0]
+        if dt == F32:
+            bits = int(np.array([regrow_value], np.float32).view(np.uint32)[0])
+        else:
+            bits = int(np.asarray(regrow_value, dtype=np.uint16))  # caller passes bf16 bits
+        r = np.empty(nnz, np.int32)
+        c = np.empty(nnz, np.int32)
+        v = np.empty(nnz, vals_c.dtype)
+        st = self.lib.oracle_restructure_grad(out, in_, nnz, _ptr(rows_c), _ptr(cols_c), _ptr(vals_c), dt, n_prune,
+                                              _ptr(dY), _ptr(X), B, bits, _ptr(r), _ptr(c), _ptr(v))
+        if st != OK:
+            raise ValueError(f"oracle_restructure_grad failed with status {st}")
+        return r, c, v
 
     # -- GELU -----------------------------------------------------------
     def gelu(self, x):

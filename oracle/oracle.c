@@ -30,7 +30,9 @@
  * <dY, X W^T> = <dY W, X> = <dW, v>, finite differences, special cases
  * (permutation W, single nnz, empty layer), brute-force sorting for the
  * canonical order, restructure invariants plus an independent set-based
- * re-implementation driven by numpy's own Philox generator, Philox blocks
+ * re-implementation driven by numpy's own Philox generator, the
+ * gradient-informed regrow against integer-valued brute force (exact scores,
+ * many ties) plus its ranking invariants, Philox blocks
  * against numpy.random.Philox, bf16 decoding against torch, and GELU against
  * scipy's erf.  Every exported function is pinned; none is "parity unpinned".
  *
@@ -408,6 +410,139 @@ int oracle_restructure(int64_t out, int64_t in, int64_t nnz, const int32_t *rows
     free(pruned);
     free(occ);
     free(all);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Gradient-informed restructure (the regrow variant ranked next after   */
+/* random regrow; the page's Abstract speaks of restructuring the        */
+/* connections during dynamic sparse training and fixes no regrow rule). */
+/* Prune exactly as oracle_restructure.  Then every position that is     */
+/* empty after the prune gets the score                                  */
+/*     g(r, c) = | sum_b dY[b, r] * X[b, c] |                            */
+/* -- the magnitude of the dense weight gradient at that position -- in  */
+/* fp32, as a fused-multiply-add chain in batch order:                   */
+/*     s = 0; for b = 0..B-1: s = fmaf(dY[b, r], X[b, c], s)             */
+/* (bf16 inputs widen exactly to fp32 first).  The n_prune empty         */
+/* positions with the largest scores are regrown, ordered by (bit        */
+/* pattern of |s| descending, position r * in + c ascending); regrown    */
+/* entries take regrow_bits.  Kept and new entries return to canonical   */
+/* order.  Input must be canonical.                                      */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    uint32_t key;
+    int64_t pos;
+} scored_t;
+
+static int cmp_scored(const void *pa, const void *pb)
+{
+    const scored_t *x = (const scored_t *)pa, *y = (const scored_t *)pb;
+    if (x->key != y->key) return x->key > y->key ? -1 : 1; /* larger score first */
+    if (x->pos != y->pos) {
+        int before = x->pos < y->pos;
+        if (MUTANT(8)) before = !before; /* mutant 8: ties go to the larger position */
+        return before ? -1 : 1;
+    }
+    return 0;
+}
+
+static float word_to_float(const void *base, int dtype, int64_t i)
+{
+    return (float)word_to_double(base, dtype, i); /* exact: every word is an fp32 or bf16 value */
+}
+
+int oracle_restructure_grad(int64_t out, int64_t in, int64_t nnz, const int32_t *rows_c, const int32_t *cols_c,
+                            const void *vals_c, int dtype, int64_t n_prune, const void *dY, const void *X, int64_t B,
+                            uint32_t regrow_bits, int32_t *rows_new, int32_t *cols_new, void *vals_new)
+{
+    if (n_prune < 0 || n_prune > nnz || out <= 0 || in <= 0 || B <= 0) return OR_ERR_ARG;
+    int64_t npos = out * in;
+    int eb = elem_bytes(dtype);
+
+    /* 1. prune, as in oracle_restructure */
+    absent_t *ord = (absent_t *)malloc((size_t)(nnz ? nnz : 1) * sizeof *ord);
+    unsigned char *pruned = (unsigned char *)calloc((size_t)(nnz ? nnz : 1), 1);
+    unsigned char *occ = (unsigned char *)calloc((size_t)((npos + 7) / 8), 1);
+    triple_t *all = (triple_t *)malloc((size_t)(nnz ? nnz : 1) * sizeof *all);
+    scored_t *cand = (scored_t *)malloc((size_t)npos * sizeof *cand);
+    float *dyf = (float *)malloc((size_t)(B * out) * sizeof *dyf);
+    float *xf = (float *)malloc((size_t)(B * in) * sizeof *xf);
+    if (!ord || !pruned || !occ || !all || !cand || !dyf || !xf) {
+        free(ord);
+        free(pruned);
+        free(occ);
+        free(all);
+        free(cand);
+        free(dyf);
+        free(xf);
+        return OR_ERR_NOMEM;
+    }
+    for (int64_t k = 0; k < nnz; ++k) {
+        ord[k].key = magnitude_key(vals_c, dtype, k);
+        ord[k].idx = k;
+    }
+    qsort(ord, (size_t)nnz, sizeof *ord, cmp_absent);
+    for (int64_t j = 0; j < n_prune; ++j) pruned[ord[j].idx] = 1;
+
+    /* 2. kept entries and their positions */
+    int64_t m = 0;
+    for (int64_t k = 0; k < nnz; ++k) {
+        if (pruned[k]) continue;
+        int64_t p = (int64_t)rows_c[k] * in + cols_c[k];
+        occ[p >> 3] |= (unsigned char)(1u << (p & 7));
+        all[m].a = rows_c[k];
+        all[m].b = cols_c[k];
+        all[m].idx = k;
+        ++m;
+    }
+
+    /* 3. scores of the empty positions, best n_prune of them */
+    for (int64_t i = 0; i < B * out; ++i) dyf[i] = word_to_float(dY, dtype, i);
+    for (int64_t i = 0; i < B * in; ++i) xf[i] = word_to_float(X, dtype, i);
+    int64_t ncand = 0;
+    for (int64_t r = 0; r < out; ++r)
+        for (int64_t c = 0; c < in; ++c) {
+            int64_t p = r * in + c;
+            if ((occ[p >> 3] >> (p & 7)) & 1) continue;
+            float sc = 0.0f;
+            for (int64_t b = 0; b < B; ++b) sc = fmaf(dyf[b * out + r], xf[b * in + c], sc);
+            if (!MUTANT(9)) sc = fabsf(sc); /* mutant 9: ranks the signed sum */
+            uint32_t key;
+            memcpy(&key, &sc, 4);
+            if (MUTANT(9)) key ^= (key >> 31) ? 0xFFFFFFFFu : 0x80000000u; /* order of the signed value */
+            cand[ncand].key = key;
+            cand[ncand].pos = p;
+            ++ncand;
+        }
+    qsort(cand, (size_t)ncand, sizeof *cand, cmp_scored);
+    for (int64_t j = 0; j < n_prune; ++j) {
+        all[m].a = cand[j].pos / in;
+        all[m].b = cand[j].pos % in;
+        all[m].idx = -1;
+        ++m;
+    }
+
+    /* 4. back to canonical order */
+    qsort(all, (size_t)m, sizeof *all, cmp_triple);
+    for (int64_t k = 0; k < m; ++k) {
+        rows_new[k] = (int32_t)all[k].a;
+        cols_new[k] = (int32_t)all[k].b;
+        char *dst = (char *)vals_new + k * eb;
+        if (all[k].idx >= 0)
+            memcpy(dst, (const char *)vals_c + all[k].idx * eb, (size_t)eb);
+        else if (dtype == OR_BF16) {
+            uint16_t h = (uint16_t)regrow_bits;
+            memcpy(dst, &h, 2);
+        } else
+            memcpy(dst, &regrow_bits, 4);
+    }
+    free(ord);
+    free(pruned);
+    free(occ);
+    free(all);
+    free(cand);
+    free(dyf);
+    free(xf);
     return OR_OK;
 }
 

@@ -321,6 +321,60 @@ def pin_restructure(orc):
     assert not np.array_equal(a[1], d[1])
 
 
+# ------------------------------------------------ gradient-informed regrow
+def brute_restructure_grad(out, in_, rows_c, cols_c, vals_c, n_prune, dY, X, regrow_value):
+    """Set-based reading of the gradient-informed restructure with exact integer scores:
+    the same prune, then the empty positions ranked by |(dY^T X)[r, c]| (computed exactly in
+    int64, so no summation order matters), ties to the smaller position."""
+    mag = vals_c.view(np.uint32) & 0x7FFFFFFF
+    order = sorted(range(len(rows_c)), key=lambda k: (int(mag[k]), k))
+    pruned = set(order[:n_prune])
+    kept = [(int(rows_c[k]), int(cols_c[k]), float(vals_c[k])) for k in range(len(rows_c)) if k not in pruned]
+    occ = {r * in_ + c for r, c, _ in kept}
+    G = np.abs(dY.astype(np.int64).T @ X.astype(np.int64))  # [out, in], exact
+    empty = [p for p in range(out * in_) if p not in occ]
+    empty.sort(key=lambda p: (-int(G[p // in_, p % in_]), p))
+    new = [(p // in_, p % in_, regrow_value) for p in empty[:n_prune]]
+    allt = sorted(kept + new)
+    return (np.array([t[0] for t in allt], np.int32), np.array([t[1] for t in allt], np.int32),
+            np.array([t[2] for t in allt], np.float32))
+
+
+def pin_restructure_grad(orc):
+    """Gradient-informed regrow: equals the exact brute force on integer-valued operands (every score
+    exact, many ties), and on random operands the regrown positions outscore every position left empty."""
+    rng = np.random.default_rng(17)
+    for out, in_, nnz, n_prune, B in [(7, 9, 25, 6, 4), (12, 5, 30, 12, 3), (1, 40, 12, 5, 2), (30, 1, 12, 5, 6)]:
+        L = _layer(out, in_, nnz, 70 + out)
+        c = orc.canonicalize(out, in_, L.rows, L.cols, L.vals)
+        dY = rng.integers(-2, 3, size=(B, out)).astype(np.float32)
+        X = rng.integers(-2, 3, size=(B, in_)).astype(np.float32)
+        r2, c2, v2 = orc.restructure_grad(out, in_, c["rows"], c["cols"], c["vals"], n_prune, dY, X, -0.5)
+        br, bc, bv = brute_restructure_grad(out, in_, c["rows"], c["cols"], c["vals"], n_prune, dY, X, -0.5)
+        assert np.array_equal(r2, br) and np.array_equal(c2, bc), (out, in_, nnz, n_prune)
+        assert np.array_equal(v2.view(np.uint32), bv.view(np.uint32))
+    # random operands: ranking invariant against numpy's fp64 scores (within fp32 rounding)
+    out, in_, nnz, n_prune, B = 40, 50, 400, 60, 8
+    L = _layer(out, in_, nnz, 5)
+    c = orc.canonicalize(out, in_, L.rows, L.cols, L.vals)
+    dY = rng.standard_normal((B, out)).astype(np.float32)
+    X = rng.standard_normal((B, in_)).astype(np.float32)
+    r2, c2, v2 = orc.restructure_grad(out, in_, c["rows"], c["cols"], c["vals"], n_prune, dY, X, 0.0)
+    keys = r2.astype(np.int64) * in_ + c2
+    assert len(keys) == nnz and np.all(np.diff(keys) > 0)
+    mag = c["vals"].view(np.uint32) & 0x7FFFFFFF
+    order = sorted(range(nnz), key=lambda k: (int(mag[k]), k))
+    kept = {int(c["rows"][k]) * in_ + int(c["cols"][k]) for k in order[n_prune:]}
+    new = [int(k) for k in keys if int(k) not in kept]
+    assert len(new) == n_prune
+    G = np.abs(dY.astype(np.float64).T @ X.astype(np.float64))
+    S = np.abs(dY.astype(np.float64)).T @ np.abs(X.astype(np.float64))
+    left = [p for p in range(out * in_) if p not in kept and p not in set(new)]
+    lo = min(G[p // in_, p % in_] + 1e-6 * S[p // in_, p % in_] for p in new)
+    hi = max(G[p // in_, p % in_] - 1e-6 * S[p // in_, p % in_] for p in left)
+    assert lo >= hi
+
+
 # ---------------------------------------------------------------- GELU
 def pin_gelu(orc):
     from scipy.special import erf
@@ -334,4 +388,4 @@ def pin_gelu(orc):
 
 ALL_PINS = [pin_dense_tiny, pin_integer_exact, pin_zero_sparsity, pin_adjoint, pin_finite_differences,
             pin_special_cases, pin_bf16, pin_canonicalize, pin_philox, pin_position_map, pin_restructure,
-            pin_gelu]
+            pin_restructure_grad, pin_gelu]

@@ -18,6 +18,8 @@ MUTANTS = {
     5: "regrow position map is off by one",
     6: "prune removes the largest magnitudes",
     7: "regrow ignores occupied positions",
+    8: "gradient regrow breaks score ties towards the larger position",
+    9: "gradient regrow ranks the signed sum instead of its magnitude",
 }
 
 
