@@ -496,13 +496,18 @@ def main():
     achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
     traffic = traffic_for(dom["kernel"], {"workload": args.workload, "batch": B})
 
-    restructure_ms = None
+    restructure_ms = restructure_grad_ms = None
     if kind in ("linear", "dst"):  # one restructure of 10% of the entries (second call: steady state)
         for k in range(2):
             torch.cuda.synchronize()
             r0 = time.perf_counter()
             csp.restructure(reps[0]["h"][0], layers[0].nnz // 10, seed=w.seed, step=12345 + k, stream=stream)
             restructure_ms = (time.perf_counter() - r0) * 1e3
+        for k in range(2):  # the gradient-informed variant, scored with this batch's dY and X
+            torch.cuda.synchronize()
+            r0 = time.perf_counter()
+            csp.restructure_grad(reps[0]["h"][0], layers[0].nnz // 10, reps[0]["dY"], reps[0]["X"], stream=stream)
+            restructure_grad_ms = (time.perf_counter() - r0) * 1e3
 
     baselines = None
     if not args.no_baselines:
@@ -573,6 +578,7 @@ def main():
                      "bytes_per_launch": dom["bytes"]},
         "kernels_us": {k: round(v["us"], 3) for k, v in per_call.items()},
         "restructure_ms": None if restructure_ms is None else round(restructure_ms, 3),
+        "restructure_grad_ms": None if restructure_grad_ms is None else round(restructure_grad_ms, 3),
         "wall_s": round(wall, 3),
     }
     if baselines is not None:

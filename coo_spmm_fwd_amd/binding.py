@@ -19,7 +19,7 @@ STATUS = {0: "CSP_OK", -1: "CSP_ERR_INVALID_ARG", -2: "CSP_ERR_INDEX_RANGE", -3:
           -4: "CSP_ERR_NO_MEMORY", -5: "CSP_ERR_HIP", -6: "CSP_ERR_DTYPE"}
 CSP_ACT_NONE, CSP_ACT_GELU = 0, 1
 EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_bwd_input", "spmm_bwd_values", "spmm_bwd",
-            "spmm_fwd_act", "spmm_bwd_input_act", "spmm_bwd_act",
+            "spmm_fwd_act", "spmm_bwd_input_act", "spmm_bwd_act", "restructure_grad",
             "restructure", "sparse_layer_nnz", "sparse_layer_shape", "sparse_layer_export",
             "sparse_layer_export_index", "sparse_layer_values", "sparse_layer_set_values", "sparse_layer_time_next",
             "sparse_layer_last_error"]
@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH):
     L.spmm_bwd_act.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p, c_void_p]
     L.restructure.restype = c_int
     L.restructure.argtypes = [c_void_p, c_int64, c_uint64, c_uint64, c_float, c_void_p]
+    L.restructure_grad.restype = c_int
+    L.restructure_grad.argtypes = [c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_float, c_void_p]
     L.sparse_layer_nnz.restype = c_int64
     L.sparse_layer_nnz.argtypes = [c_void_p]
     L.sparse_layer_shape.restype = c_int
@@ -278,6 +280,17 @@ def restructure(layer: int, n_prune: int, seed: int, step: int, regrow_value: fl
     """Prune n_prune smallest-|v| entries and regrow as many at empty positions (synchronizes)."""
     _check(load().restructure(c_void_p(layer), int(n_prune), int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
                               float(regrow_value), _stream(stream)))
+
+
+def restructure_grad(layer: int, n_prune: int, dY, X, regrow_value: float = 0.0, stream=None):
+    """Prune n_prune smallest-|v| entries and regrow as many at the empty positions with the largest
+    |(dY^T X)[r, c]| (fp32 multiply-add chain in batch order; synchronizes)."""
+    out, in_, dt = sparse_layer_shape(layer)
+    B = int(X.shape[0])
+    td = _torch_dtype(dt)
+    gp = _dev(dY, "dY", td, (B, out))
+    xp = _dev(X, "X", td, (B, in_))
+    _check(load().restructure_grad(c_void_p(layer), int(n_prune), gp, xp, B, float(regrow_value), _stream(stream)))
 
 
 def sparse_layer_export(layer: int, stream=None):

@@ -47,6 +47,7 @@ struct Workspace {
     uint32_t *occ = nullptr, *occ_next = nullptr, *occ_pref = nullptr, *occ_pref_next = nullptr;
     uint32_t *tcnt = nullptr;
     uint64_t *hash = nullptr;  // hash_slots: regrow candidates by position
+    uint32_t *score = nullptr; // occ_words * 32: gradient regrow score keys (first use)
     int64_t hash_slots = 0, bm_batch_cap = 0;
 };
 
@@ -200,6 +201,9 @@ size_t bitmap_hist_words(const csp_layer *L);
 csp_status occupancy_init(csp_layer *L, hipStream_t s);
 csp_status restructure_bitmap(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,
                               hipStream_t s);
+// Prune as restructure; regrow the empty positions with the largest |dY^T X|.
+csp_status restructure_gradient(csp_layer *L, int64_t n_prune, const void *dY, const void *X, int64_t B,
+                                uint32_t regrow_bits, hipStream_t s);
 csp_status run_restructure(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,
                            hipStream_t s);
 int64_t regrow_batch_cap(const csp_layer *L);

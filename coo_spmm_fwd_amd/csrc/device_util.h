@@ -46,6 +46,24 @@ __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t *lds16, uin
     return r;
 }
 
+// Element types of the layer: fp32, and bf16 held as its 16-bit pattern
+// (widened exactly by a 16-bit shift; narrowed round-to-nearest-even).
+struct F32 {
+    using T = float;
+    __device__ static float load(const float *p, int64_t i) { return p[i]; }
+    __device__ static float from_f(float v) { return v; }
+};
+struct BF16 {
+    using T = uint16_t;
+    __device__ static float load(const uint16_t *p, int64_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
+    __device__ static uint16_t from_f(float f)  // round to nearest even
+    {
+        uint32_t u = __float_as_uint(f);
+        if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+        u += 0x7FFFu + ((u >> 16) & 1u);
+        return (uint16_t)(u >> 16);
+    }
+};
 // Lanes of the wave whose 8-bit value d equals this lane's, among the lanes
 // with `take` set (eight ballots, one per bit).
 __device__ __forceinline__ uint64_t lanes_with_same_byte(uint32_t d, bool take)

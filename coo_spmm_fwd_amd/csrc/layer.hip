@@ -68,7 +68,7 @@ void free_layer(csp_layer *L)
     void *ptrs[] = {L->rows, L->cols, L->vals, L->row_ptr, L->perm_c, L->rows_by_col, L->col_ptr, L->vals_c,
                     L->ws.key_a, L->ws.key_b, L->ws.idx_a, L->ws.idx_b, L->ws.u_a, L->ws.u_b, L->ws.hist,
                     L->ws.rows_k, L->ws.cols_k, L->ws.vals_k, L->ws.rp_k, L->ws.rp_new, L->ws.acc_a, L->ws.acc_b, L->ws.sel,
-                    L->ws.occ, L->ws.occ_next, L->ws.occ_pref, L->ws.occ_pref_next, L->ws.tcnt, L->ws.hash,
+                    L->ws.occ, L->ws.occ_next, L->ws.occ_pref, L->ws.occ_pref_next, L->ws.tcnt, L->ws.hash, L->ws.score,
                     L->act.a, L->act.b, L->act.partial,
                     L->row_tasks.desc, L->row_tasks.split, L->row_tasks.seg_first,
                     L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first};
@@ -304,6 +304,25 @@ csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_
     if (st == CSP_OK && n_prune > 0) {
         hipError_t e = hipStreamSynchronize(s);
         if (e != hipSuccess) st = hip_error(e, "restructure");
+    }
+    return st;
+}
+
+csp_status restructure_grad(sparse_layer_t L, int64_t n_prune, const void *dY, const void *X, int64_t B,
+                            float regrow_value, void *stream)
+{
+    if (!L || !dY || !X) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to restructure_grad");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    if (n_prune < 0 || n_prune > L->nnz)
+        return set_error(CSP_ERR_INVALID_ARG, "n_prune %lld outside [0, nnz = %lld]", (long long)n_prune,
+                         (long long)L->nnz);
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    hipStream_t s = (hipStream_t)stream;
+    csp_status st = restructure_gradient(L, n_prune, dY, X, B, regrow_word(L, regrow_value), s);
+    if (st == CSP_OK && n_prune > 0) {
+        hipError_t e = hipStreamSynchronize(s);
+        if (e != hipSuccess) st = hip_error(e, "restructure_grad");
     }
     return st;
 }

@@ -119,6 +119,22 @@ __device__ inline void select_state(const uint32_t *sel, int npass, int top, uin
     }
 }
 
+// Key sources of the radix select: the prune order reads the magnitude keys
+// of the values (smallest first); the gradient-informed regrow reads score
+// keys and wants the largest first, so it selects on their complement.
+template <typename V>
+struct MagKeys {
+    const V *v;
+    __device__ __forceinline__ uint32_t operator()(int64_t k, int64_t n) const
+    {
+        return mag_key<V>(load_or_first(v, k, n));
+    }
+};
+struct InvKeys {
+    const uint32_t *w;
+    __device__ __forceinline__ uint32_t operator()(int64_t k, int64_t n) const { return ~load_or_first(w, k, n); }
+};
+
 // Histogram pass `pass` of the radix select; pass 0 also fills `clear`
 // (the regrow hash table) with empty slots.  Few fat blocks: every block adds
 // its nonzero bins to the global histogram with one atomic each.  Lanes that
@@ -126,8 +142,8 @@ __device__ inline void select_state(const uint32_t *sel, int npass, int top, uin
 // that by four), which costs less than matching digits across the wave.
 constexpr int kHistThreads = 1024;
 
-template <typename V>
-__global__ __launch_bounds__(kHistThreads) void k_bm_hist(const V *__restrict__ vals, int64_t n, int pass, int top,
+template <class K>
+__global__ __launch_bounds__(kHistThreads) void k_bm_hist(K keyof, int64_t n, int pass, int top,
                                                           uint32_t n_prune, uint32_t *sel,
                                                           uint64_t *__restrict__ clear, int64_t nclear)
 {
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(kHistThreads) void k_bm_hist(const V *__restrict__ 
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t k = base + u * kHistThreads + t;
-            key[u] = mag_key<V>(load_or_first(vals, k, n));
+            key[u] = keyof(k, n);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -180,8 +196,8 @@ __global__ __launch_bounds__(64) void k_bm_sel_final(uint32_t *sel, uint32_t n_p
 
 // ---------------------------------------------------------------------- prune
 // Per tile: entries with key below the threshold, and equal to it.
-template <typename V>
-__global__ __launch_bounds__(kThreads) void k_bm_prune_count(const V *__restrict__ vals, int64_t n,
+template <class K>
+__global__ __launch_bounds__(kThreads) void k_bm_prune_count(K keyof, int64_t n,
                                                              const uint32_t *__restrict__ sel,
                                                              uint32_t *__restrict__ tiles)
 {
@@ -193,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void k_bm_prune_count(const V *__restrict
 #pragma unroll
     for (int u = 0; u < kTile / kThreads; ++u) {
         const int64_t k = base + u * kThreads + t;
-        const uint32_t key = mag_key<V>(load_or_first(vals, k, n));
+        const uint32_t key = keyof(k, n);
         lt += k < n && key < T;
         eq += k < n && key == T;
     }
@@ -211,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void k_bm_prune_count(const V *__restrict
 }
 
 // One block of 1024: exclusive scans (in place) of the interleaved per-tile
-// counts; clears the regrow counters.
+// counts; clears the regrow counters and the select histograms.
 __global__ __launch_bounds__(1024) void k_bm_prune_scan(uint32_t *tiles, int64_t nt, uint32_t *sel)
 {
     __shared__ uint32_t lds[17];
@@ -231,13 +247,15 @@ __global__ __launch_bounds__(1024) void k_bm_prune_scan(uint32_t *tiles, int64_t
         sel[kSelCounts + 4] = 0;
         sel[kSelCounts + 5] = 0;
     }
+    // the select is done: clear its histograms for the next one
+    for (int i = threadIdx.x; i < kMaxPasses * kHistWords; i += 1024) sel[i] = 0;
 }
 
 // Entry k goes if its key is below the threshold, or equal to it and fewer
 // than need_eq equal keys precede it; the pruned ones are marked in a bit
 // mask, one bit per canonical index.
-template <typename V>
-__global__ __launch_bounds__(kThreads) void k_bm_prune_mark(const V *__restrict__ vals, int64_t n,
+template <class K>
+__global__ __launch_bounds__(kThreads) void k_bm_prune_mark(K keyof, int64_t n,
                                                             const uint32_t *__restrict__ sel,
                                                             const uint32_t *__restrict__ tiles,
                                                             uint64_t *__restrict__ pruned)
@@ -252,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void k_bm_prune_mark(const V *__restrict_
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         const int64_t k = base + j * kWave + lane;
-        key[j] = mag_key<V>(load_or_first(vals, k, n));
+        key[j] = keyof(k, n);
         eq_w += (uint32_t)__popcll(__ballot(k < n && key[j] == T));
     }
     if (lane == 0) we[w] = eq_w;
@@ -336,15 +354,13 @@ __device__ inline uint32_t hash_first(const uint64_t *tab, int hbits, uint32_t p
 
 // Candidates [i0, i0 + M) of the stream (i0 a multiple of 4), four per
 // thread (one Philox block): occupied positions drop out, the others enter
-// the hash table.  Block 0 also clears the select histograms for the next
-// restructure.
+// the hash table.
 __global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint64_t step, uint64_t i0, int64_t M,
                                                              int64_t in, uint64_t npos, const uint32_t *occ,
                                                              int64_t inw, uint32_t *__restrict__ cand, uint64_t *tab,
                                                              int hbits, uint32_t *sel)
 {
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < kMaxPasses * kHistWords; i += kThreads) sel[i] = 0;
+    (void)sel;
     const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x, j0 = 4 * t;
     if (j0 >= M) return;
     uint64_t u[4];
@@ -443,6 +459,83 @@ __global__ __launch_bounds__(kThreads) void k_bm_cand_take(const uint32_t *__res
     const uint32_t p = cand[j];
     const int64_t r = (int64_t)(p / (uint64_t)in), c = (int64_t)p - r * in;
     atomicOr(&occ[r * inw + (c >> 5)], 1u << (c & 31));
+}
+
+// ------------------------------------------------- gradient-informed regrow
+// Score key of every padded bitmap position: 0 unless the position is inside
+// the layer and empty after the prune, else 1 + bit pattern of |s| with
+//     s = 0; for b = 0..B-1: s = fma(dY[b, r], X[b, c], s)     (fp32)
+// -- the fused-multiply-add chain in batch order, so the integer decision
+// "which positions come back" is the same on any implementation that keeps
+// this order.  Block = 64 rows x 64 columns; thread = 4 rows x 4 columns
+// (register tile); dY and X tiles of 64 batch rows at a time in LDS.
+template <class D>
+__global__ __launch_bounds__(kThreads) void k_bm_scores(const typename D::T *__restrict__ dY,
+                                                        const typename D::T *__restrict__ X, int64_t B, int64_t out,
+                                                        int64_t in, const uint32_t *__restrict__ occ, int64_t inw,
+                                                        uint32_t *__restrict__ keys)
+{
+    __shared__ float ty[64][64 + 1];  // [b][row]
+    __shared__ float tx[64][64 + 1];  // [b][col]
+    const int t = threadIdx.x, tr = t >> 4, tc = t & 15;  // 16 x 16 threads, 4 x 4 each
+    const int64_t ncb = inw / 2;                           // 64-column blocks
+    const int64_t r0 = (int64_t)(blockIdx.x / ncb) * 64, c0 = (int64_t)(blockIdx.x % ncb) * 64;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int64_t b0 = 0; b0 < B; b0 += 64) {
+        const int nb = B - b0 < 64 ? (int)(B - b0) : 64;
+        __syncthreads();
+        for (int e = t; e < 64 * 64; e += kThreads) {
+            const int bb = e >> 6, k = e & 63;
+            const bool okb = bb < nb;
+            const int64_t r = r0 + k, c = c0 + k;
+            ty[bb][k] = okb && r < out ? D::load(dY, (b0 + bb) * out + r) : 0.f;
+            tx[bb][k] = okb && c < in ? D::load(X, (b0 + bb) * in + c) : 0.f;
+        }
+        __syncthreads();
+        for (int bb = 0; bb < nb; ++bb) {
+            float y[4], x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) y[i] = ty[bb][tr * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] = tx[bb][tc * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __fmaf_rn(y[i], x[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + tr * 4 + i;
+        const int64_t c = c0 + tc * 4;  // four consecutive columns in one bitmap word
+        const uint32_t w = occ[r * inw + (c >> 5)];
+        uint4 k4;
+        uint32_t kv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool live = r < out && c + j < in && !((w >> ((c + j) & 31)) & 1u);
+            kv[j] = live ? (__float_as_uint(fabsf(acc[i][j])) + 1u) : 0u;
+        }
+        k4.x = kv[0];
+        k4.y = kv[1];
+        k4.z = kv[2];
+        k4.w = kv[3];
+        *(uint4 *)(keys + r * inw * 32 + c) = k4;
+    }
+}
+
+// Adds the chosen positions (bit mask in bitmap word order) to the next
+// bitmap; records that all n_prune are taken.
+__global__ __launch_bounds__(kThreads) void k_bm_or(uint32_t *__restrict__ occ, const uint32_t *__restrict__ chosen,
+                                                    int64_t nw, uint32_t *sel, uint32_t n_prune)
+{
+    const int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (w < nw) occ[w] |= chosen[w];
+    if (w == 0) sel[kSelCounts + 4] = n_prune;
 }
 
 // -------------------------------------------------------------------- rebuild
@@ -717,11 +810,71 @@ struct BitmapRun {
         return CSP_OK;
     }
 
+    // Radix select of the `count` smallest keys of keyof over [0, n), then a
+    // bit per index of the chosen ones (ties go to the smaller index) in mask;
+    // `clear` (optional) is filled with empty hash slots by the first pass.
+    template <class K>
+    csp_status select(K keyof, int64_t n, int64_t count, int passes, int top, uint64_t *mask, uint64_t *clear,
+                      int64_t nclear)
+    {
+        Workspace &W = L->ws;
+        const int64_t hgrid = ceil_div(n, kHistThreads * 8) < 256 ? ceil_div(n, kHistThreads * 8) : 256;
+        for (int p = 0; p < passes; ++p) {
+            k_bm_hist<K><<<(unsigned)hgrid, kHistThreads, 0, s>>>(keyof, n, p, top, (uint32_t)count, W.sel,
+                                                                   p == 0 ? clear : nullptr, p == 0 ? nclear : 0);
+            CSP_LAUNCHED("k_bm_hist");
+        }
+        k_bm_sel_final<<<1, 64, 0, s>>>(W.sel, (uint32_t)count, passes, top);
+        CSP_LAUNCHED("k_bm_sel_final");
+        const int64_t nt = ceil_div(n, kTile);
+        k_bm_prune_count<K><<<(unsigned)nt, kThreads, 0, s>>>(keyof, n, W.sel, W.hist);
+        CSP_LAUNCHED("k_bm_prune_count");
+        k_bm_prune_scan<<<1, 1024, 0, s>>>(W.hist, nt, W.sel);
+        CSP_LAUNCHED("k_bm_prune_scan");
+        k_bm_prune_mark<K><<<(unsigned)nt, kThreads, 0, s>>>(keyof, n, W.sel, W.hist, mask);
+        CSP_LAUNCHED("k_bm_prune_mark");
+        return CSP_OK;
+    }
+
+    // Prune: mark the n_prune entries first in the prune order, and start the
+    // next bitmap as the current one without them.
+    csp_status prune(uint64_t *clear, int64_t nclear)
+    {
+        Workspace &W = L->ws;
+        const int passes = sizeof(V) == 4 ? 4 : 2, top = sizeof(V) == 4 ? 24 : 8;
+        csp_status st = select(MagKeys<V>{(const V *)L->vals}, L->nnz, n_prune, passes, top, (uint64_t *)W.acc_b,
+                               clear, nclear);
+        if (st != CSP_OK) return st;
+        k_bm_occ_prune<<<blocks_for(W.occ_words, kThreads), kThreads, 0, s>>>(W.occ, W.occ_pref, W.occ_words,
+                                                                              (const uint64_t *)W.acc_b, W.occ_next);
+        CSP_LAUNCHED("k_bm_occ_prune");
+        return CSP_OK;
+    }
+
+    // Gradient-informed regrow: the n_prune empty positions with the largest
+    // score keys (ties to the smaller position) join the next bitmap.
+    template <class D>
+    csp_status regrow_by_gradient(const void *dY, const void *X, int64_t B)
+    {
+        Workspace &W = L->ws;
+        const int64_t npad = W.occ_words * 32;  // padded positions, bitmap order
+        const int64_t rblk = ceil_div(W.occ_rows, 64), cblk = W.occ_row_words / 2;
+        k_bm_scores<D><<<(unsigned)(rblk * cblk), kThreads, 0, s>>>((const typename D::T *)dY,
+                                                                     (const typename D::T *)X, B, L->out, L->in,
+                                                                     W.occ_next, W.occ_row_words, W.score);
+        CSP_LAUNCHED("k_bm_scores");
+        uint64_t *chosen = (uint64_t *)W.occ_pref_next;  // scratch until the rebuild
+        csp_status st = select(InvKeys{W.score}, npad, n_prune, 4, 24, chosen, nullptr, 0);
+        if (st != CSP_OK) return st;
+        k_bm_or<<<blocks_for(W.occ_words, kThreads), kThreads, 0, s>>>(W.occ_next, (const uint32_t *)chosen,
+                                                                       W.occ_words, W.sel, (uint32_t)n_prune);
+        CSP_LAUNCHED("k_bm_or");
+        return rebuild();
+    }
+
     csp_status run()
     {
         Workspace &W = L->ws;
-        const int64_t n = L->nnz;
-        const int passes = sizeof(V) == 4 ? 4 : 2, top = sizeof(V) == 4 ? 24 : 8;
         int64_t cap = W.bm_batch_cap;
         if (const char *e = std::getenv("COOSPMM_REGROW_BATCH")) {  // test hook: smaller batches
             long long v = std::atoll(e);
@@ -729,27 +882,9 @@ struct BitmapRun {
         }
         int64_t M = batch_size(cap);
         int hb = hash_bits_for(M);
-        const V *vals = (const V *)L->vals;
-        const int64_t hgrid = ceil_div(n, kHistThreads * 8) < 256 ? ceil_div(n, kHistThreads * 8) : 256;
-        for (int p = 0; p < passes; ++p) {
-            k_bm_hist<V><<<(unsigned)hgrid, kHistThreads, 0, s>>>(vals, n, p, top, (uint32_t)n_prune, W.sel,
-                                                                   p == 0 ? W.hash : nullptr,
-                                                                   p == 0 ? (int64_t(1) << hb) : 0);
-            CSP_LAUNCHED("k_bm_hist");
-        }
-        k_bm_sel_final<<<1, 64, 0, s>>>(W.sel, (uint32_t)n_prune, passes, top);
-        CSP_LAUNCHED("k_bm_sel_final");
-        const int64_t nt = ceil_div(n, kTile);
-        k_bm_prune_count<V><<<(unsigned)nt, kThreads, 0, s>>>(vals, n, W.sel, W.hist);
-        CSP_LAUNCHED("k_bm_prune_count");
-        k_bm_prune_scan<<<1, 1024, 0, s>>>(W.hist, nt, W.sel);
-        CSP_LAUNCHED("k_bm_prune_scan");
-        k_bm_prune_mark<V><<<(unsigned)nt, kThreads, 0, s>>>(vals, n, W.sel, W.hist, (uint64_t *)W.acc_b);
-        CSP_LAUNCHED("k_bm_prune_mark");
-        k_bm_occ_prune<<<blocks_for(W.occ_words, kThreads), kThreads, 0, s>>>(W.occ, W.occ_pref, W.occ_words,
-                                                                              (const uint64_t *)W.acc_b, W.occ_next);
-        CSP_LAUNCHED("k_bm_occ_prune");
-        csp_status st = batch(M, hb);
+        csp_status st = prune(W.hash, int64_t(1) << hb);
+        if (st != CSP_OK) return st;
+        st = batch(M, hb);
         if (st != CSP_OK) return st;
         st = rebuild();
         if (st != CSP_OK) return st;
@@ -800,10 +935,12 @@ size_t bitmap_hist_words(const csp_layer *L)
     const Workspace &W = L->ws;
     if (!W.bitmap) return 0;
     const int64_t a = 2 * ceil_div(L->nnz, kTile) + 2, b = ceil_div(W.bm_batch_cap, kThreads) + 2,
-                  c = ceil_div(W.occ_words, 4096) + 2, d = ceil_div(W.tcnt_words, 4096) + 2;
+                  c = ceil_div(W.occ_words, 4096) + 2, d = ceil_div(W.tcnt_words, 4096) + 2,
+                  e = 2 * ceil_div(W.occ_words * 32, kTile) + 2;  // tiles of the gradient regrow select
     int64_t m = a > b ? a : b;
     m = m > c ? m : c;
-    return (size_t)(m > d ? m : d);
+    m = m > d ? m : d;
+    return (size_t)(m > e ? m : e);
 }
 
 csp_status occupancy_init(csp_layer *L, hipStream_t s)
@@ -817,6 +954,33 @@ csp_status occupancy_init(csp_layer *L, hipStream_t s)
         CSP_LAUNCHED("k_bm_occ_set");
     }
     return exclusive_scan_popc(W.occ, W.occ_pref, W.occ_words, W.hist, s);  // ranks of the set bits
+}
+
+csp_status restructure_gradient(csp_layer *L, int64_t n_prune, const void *dY, const void *X, int64_t B,
+                                uint32_t regrow_bits, hipStream_t s)
+{
+    Workspace &W = L->ws;
+    if (!W.bitmap)
+        return set_error(CSP_ERR_INVALID_ARG, "gradient-informed restructure needs the position bitmaps "
+                                              "(out * in < 2^32 and bitmaps within 1 GiB)");
+    if (n_prune == 0) return CSP_OK;
+    if (!W.score) {  // score keys of every padded position, allocated at the first call
+        if (hipMalloc((void **)&W.score, 4 * (size_t)W.occ_words * 32) != hipSuccess) {
+            (void)hipGetLastError();
+            W.score = nullptr;
+            return set_error(CSP_ERR_NO_MEMORY, "cannot allocate %zu bytes of regrow scores",
+                             4 * (size_t)W.occ_words * 32);
+        }
+    }
+    const uint64_t npos = (uint64_t)L->out * (uint64_t)L->in;
+    if (L->esz == 2) {
+        BitmapRun<uint16_t> r{L, n_prune, 0, 0, npos, (uint16_t)regrow_bits, s};
+        csp_status st = r.prune(nullptr, 0);
+        return st != CSP_OK ? st : r.template regrow_by_gradient<BF16>(dY, X, B);
+    }
+    BitmapRun<uint32_t> r{L, n_prune, 0, 0, npos, regrow_bits, s};
+    csp_status st = r.prune(nullptr, 0);
+    return st != CSP_OK ? st : r.template regrow_by_gradient<F32>(dY, X, B);
 }
 
 csp_status restructure_bitmap(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,

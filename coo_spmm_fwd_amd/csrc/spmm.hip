@@ -24,27 +24,12 @@
 // dense contraction; the bound is HBM for the COO stream and L1/L2 for the
 // operand gathers.
 #include "common.h"
+#include "device_util.h"
 
 namespace csp {
 namespace {
 
-// ----------------------------------------------------------------- dtype glue
-struct F32 {
-    using T = float;
-    __device__ static float load(const float *p, int64_t i) { return p[i]; }
-    __device__ static float from_f(float v) { return v; }
-};
-struct BF16 {
-    using T = uint16_t;
-    __device__ static float load(const uint16_t *p, int64_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
-    __device__ static uint16_t from_f(float f)  // round to nearest even
-    {
-        uint32_t u = __float_as_uint(f);
-        if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-        u += 0x7FFFu + ((u >> 16) & 1u);
-        return (uint16_t)(u >> 16);
-    }
-};
+
 
 inline int pow2_ld(int64_t B)
 {

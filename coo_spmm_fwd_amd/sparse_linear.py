@@ -52,7 +52,9 @@ class SparseLinear(torch.nn.Module):
 
     rows, cols: int32 device tensors of the stored positions (any order, no
     duplicates); vals: float32 or bfloat16 device tensor of their values.  No
-    bias (a dense add outside the layer).  bf16 layers run forward only.
+    bias (a dense add outside the layer).  On a bf16 layer the input gradient
+    flows through autograd but the values take no gradient (the library's
+    value gradient is fp32: call spmm_bwd_values for it).
     """
 
     def __init__(self, rows, cols, vals, out_features: int, in_features: int):
@@ -84,6 +86,14 @@ class SparseLinear(torch.nn.Module):
         """One prune-and-regrow step (the n_prune smallest |v| go, as many empty positions are drawn)."""
         self._sync_values()
         csp.restructure(self.handle, int(n_prune), int(seed), int(step), float(regrow_value))
+        self.values.data = csp.sparse_layer_values_tensor(self.handle)
+        self._seen_version = self.values._version
+
+    @torch.no_grad()
+    def restructure_by_gradient(self, n_prune: int, dY, X, regrow_value: float = 0.0):
+        """Prune the n_prune smallest |v|; regrow the empty positions where |dY^T X| is largest."""
+        self._sync_values()
+        csp.restructure_grad(self.handle, int(n_prune), dY.contiguous(), X.contiguous(), float(regrow_value))
         self.values.data = csp.sparse_layer_values_tensor(self.handle)
         self._seen_version = self.values._version
 

@@ -172,6 +172,29 @@ csp_status spmm_bwd_act(sparse_layer_t layer, const void *dY, const void *X, int
 csp_status restructure(sparse_layer_t layer, int64_t n_prune, uint64_t seed, uint64_t step, float regrow_value,
                        void *stream);
 
+/*
+ * restructure_grad -- prune-and-regrow with gradient-informed regrowth (the
+ * page's Abstract restructures connections during dynamic sparse training and
+ * fixes no regrow rule; this variant ranks the empty positions by the
+ * magnitude of the dense weight gradient, the quantity the value gradient
+ * computes at the stored positions only).
+ *  1. prune exactly as restructure (the n_prune smallest |v|);
+ *  2. every position (r, c) empty after the prune gets the score |s| with
+ *         s = 0; for b = 0 .. B-1: s = fmaf(dY[b, r], X[b, c], s)
+ *     in fp32 (bf16 operands widen exactly), a fused-multiply-add chain in
+ *     batch order so that the result is reproducible bit for bit;
+ *  3. the n_prune empty positions with the largest scores are regrown with
+ *     value regrow_value, ties (equal fp32 scores) to the smaller r * in + c;
+ *  4. canonical order, offsets and the transposed view are rebuilt.
+ * dY [B, out] and X [B, in] have the layer's dtype.  Layers whose position
+ * bitmaps do not fit (out * in >= 2^32, or more than 1 GiB) return
+ * CSP_ERR_INVALID_ARG.  The first call allocates the score workspace
+ * (4 bytes per position).  Synchronizes on "stream"; pointers from
+ * sparse_layer_values are stale afterwards, as after restructure.
+ */
+csp_status restructure_grad(sparse_layer_t layer, int64_t n_prune, const void *dY, const void *X, int64_t B,
+                            float regrow_value, void *stream);
+
 /* Number of stored entries; -1 for NULL. */
 int64_t sparse_layer_nnz(sparse_layer_t layer);
 /* Shape and dtype; returns CSP_ERR_INVALID_ARG for NULL arguments. */

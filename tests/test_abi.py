@@ -62,6 +62,7 @@ def test_calls_reject_null_layer(lib):
     assert lib.spmm_bwd_input_act(None, c_void_p(16), 4, 1, c_void_p(16), c_void_p(16), None) == -1
     assert lib.spmm_bwd_act(None, c_void_p(16), c_void_p(16), 4, 1, c_void_p(16), c_void_p(16), c_void_p(16),
                             None) == -1
+    assert lib.restructure_grad(None, 1, c_void_p(16), c_void_p(16), 4, ctypes.c_float(0.0), None) == -1
     assert lib.restructure(None, 0, 1, 1, 0.0, None) == -1
     assert lib.sparse_layer_nnz(None) == -1
     assert lib.sparse_layer_values(None) is None

@@ -143,6 +143,57 @@ def test_values_view_after_restructure(orc, path):
         csp.sparse_layer_destroy(h)
 
 
+@pytest.mark.parametrize("out,in_,nnz,n_prune,B,dtype,integer", [
+    (6, 7, 12, 3, 2, "f32", True), (40, 30, 300, 40, 3, "f32", True), (1000, 700, 35000, 3500, 16, "f32", False),
+    (333, 777, 50000, 700, 70, "f32", False), (300, 200, 6000, 600, 4, "bf16", False),
+    (1, 3000, 500, 50, 5, "f32", False), (3000, 1, 500, 50, 5, "f32", False)])
+def test_restructure_grad_matches_oracle(orc, out, in_, nnz, n_prune, B, dtype, integer):
+    """Gradient-informed regrow, bit-exact against the oracle over three steps (integer operands give
+    exact scores with many ties, so the tie rule is exercised)."""
+    L = W.random_layer(out, in_, nnz, seed=out + 7 * in_, dtype=dtype)
+    h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(out, in_, L.rows, L.cols, L.vals)
+        rows, cols, vals = c["rows"], c["cols"], c["vals"]
+        regrow = W.f32_to_bf16_bits(np.array([0.5], np.float32))[0] if dtype == "bf16" else 0.5
+        for step in range(3):
+            dY = W.random_dense((B, out), 100 + step, dtype=dtype, integer=integer)
+            X = W.random_dense((B, in_), 200 + step, dtype=dtype, integer=integer)
+            rows, cols, vals = orc.restructure_grad(out, in_, rows, cols, vals, n_prune, dY, X, regrow)
+            csp.restructure_grad(h, n_prune, dev(dY), dev(X), 0.5)
+            check_state(orc, h, out, in_, rows, cols, vals)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_restructure_grad_full_size(orc):
+    """4096 x 4096 at 95%, B = 16: one gradient-informed step of 10%, bit-exact."""
+    w, layers, acts = W.build("linear4096_b16_s95")
+    L = layers[0]
+    h = csp.sparse_layer_create(L.out, L.in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        c = orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals)
+        X, dY = acts[16]["X"], acts[16]["dY"]
+        n_prune = L.nnz // 10
+        r0 = orc.restructure_grad(L.out, L.in_, c["rows"], c["cols"], c["vals"], n_prune, dY, X, 0.0)
+        csp.restructure_grad(h, n_prune, dev(dY), dev(X), 0.0)
+        check_state(orc, h, L.out, L.in_, *r0)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_restructure_grad_needs_bitmaps(monkeypatch):
+    monkeypatch.setenv("COOSPMM_RESTRUCTURE", "sorted")
+    L = W.random_layer(50, 40, 300, seed=3)
+    h = csp.sparse_layer_create(50, 40, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        with pytest.raises(csp.CspError) as e:
+            csp.restructure_grad(h, 10, dev(W.random_dense((2, 50), 1)), dev(W.random_dense((2, 40), 2)))
+        assert e.value.status == -1 and "bitmap" in str(e.value)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
 def test_restructure_rejects_bad_count():
     L = W.random_layer(10, 10, 20, seed=1)
     h = csp.sparse_layer_create(10, 10, dev(L.rows), dev(L.cols), dev(L.vals))
