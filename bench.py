@@ -130,7 +130,7 @@ def ingest_counters(fetch_dir, write_dir, workload, batch, copy_mib=256):
     f_scale = copy_bytes / (cf * 1024) if cf else None
     w_scale = copy_bytes / (cw * 1024) if cw else None
     rec = {}
-    for name in (f"k_gradients<{ld}, false>", f"k_segment_spmm<{ld}, F32, false>"):
+    for name in (f"k_gradients<{ld}, csp::F32, false, 0>", f"k_segment_spmm<{ld}, csp::F32, false, 0>"):
         m = lambda n, name=name: name in n
         kf, nf = _per_dispatch(fetch, "FETCH_SIZE", m)
         kw, nw = _per_dispatch(write, "WRITE_SIZE", m)
@@ -373,12 +373,21 @@ def main():
     ld = 1
     while ld < min(B, 64):
         ld *= 2
-    fwd_name = f"k_segment_spmm<{ld}, {'BF16' if w.dtype == 'bf16' else 'F32'}, false>"
+    # kernel names as the profiler prints them (template arguments: batch width, element type,
+    # 64-bit offsets, epilogue 0 none / 1 forward bias+activation / 2 input gradient times act')
+    dt_name = "csp::BF16" if w.dtype == "bf16" else "csp::F32"
+
+    def fwd_name(epi=0):
+        return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}>"
+
     # spmm_bwd runs both gradient passes in one launch unless their two batch-minor
     # operand tables exceed 2 MiB together (then the two kernels run back to back)
-    big = any(4 * ld * (L.in_ + L.out) > (2 << 20) for L in layers)
-    grad_name = (f"k_segment_spmm<{ld}, F32, false> + k_values_rows<{ld}, false>" if big
-                 else f"k_gradients<{ld}, false>")
+    big = any((2 if w.dtype == "bf16" else 4) * ld * (L.in_ + L.out) > (2 << 20) for L in layers)
+
+    def grad_name(epi=0):
+        if big:
+            return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}> + k_values_rows<{ld}, {dt_name}, false>"
+        return f"k_gradients<{ld}, {dt_name}, false, {epi}>"
 
     def calls(st, stream):
         """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic bytes)."""
@@ -391,7 +400,7 @@ def main():
                     # GELU fused into the producing layer's epilogue
                     csp.spmm_fwd_act(h, src, act="none" if last else "gelu", Y=dst, stream=stream)
 
-                out.append((f"forward {li + 1}", h, f, fwd_name, bytes_fwd(L.nnz, L.out, L.in_, B, sv=2, sx=2)))
+                out.append((f"forward {li + 1}", h, f, fwd_name(1), bytes_fwd(L.nnz, L.out, L.in_, B, sv=2, sx=2)))
             return out
         if kind == "mlp":
             (h1, h2), (L1, L2) = st["h"], layers
@@ -405,21 +414,21 @@ def main():
                 csp.spmm_bwd_act(h2, st["dY"], st["A"], st["H"], act="gelu", dX=st["dH"], dW=st["dW2"],
                                  stream=stream)
 
-            out.append(("forward 1", h1, f1, fwd_name, bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
-            out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream), fwd_name,
+            out.append(("forward 1", h1, f1, fwd_name(1), bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
+            out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream), fwd_name(),
                         bytes_fwd(L2.nnz, L2.out, L2.in_, B)))
-            out.append(("backward 2", h2, b2, grad_name, bytes_gradients(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("backward 2", h2, b2, grad_name(2), bytes_gradients(L2.nnz, L2.out, L2.in_, B)))
             out.append(("backward 1", h1, lambda: csp.spmm_bwd(h1, st["dH"], st["X"], st["dX"], st["dW1"],
-                                                               stream=stream), grad_name,
+                                                               stream=stream), grad_name(),
                         bytes_gradients(L1.nnz, L1.out, L1.in_, B)))
             return out
         h, L = st["h"][0], layers[0]
         sv = 2 if w.dtype == "bf16" else 4
-        out.append(("forward", h, lambda: csp.spmm_fwd(h, st["X"], st["Y"], stream=stream), fwd_name,
+        out.append(("forward", h, lambda: csp.spmm_fwd(h, st["X"], st["Y"], stream=stream), fwd_name(),
                     bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)))
         if kind != "inference":
             out.append(("backward", h, lambda: csp.spmm_bwd(h, st["dY"], st["X"], st["dX"], st["dW"], stream=stream),
-                        grad_name, bytes_gradients(L.nnz, L.out, L.in_, B)))
+                        grad_name(), bytes_gradients(L.nnz, L.out, L.in_, B)))
         return out
 
     stream = torch.cuda.current_stream()
@@ -481,12 +490,27 @@ def main():
             a.record(stream)
             b.record(stream)
     torch.cuda.synchronize()
+    # Hold the GPU with a spin kernel while the K steps are queued, so that they run back to back
+    # as in the timed region instead of each waiting for its launch from the host.
+    if kind != "dst" and hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2.0e9 * min(0.2, 1e-4 * K * len(labels))))
     for i in range(K):
         for (label, h, fn, _, _), (a, b) in zip(calls(reps[i % R], stream), ev[i]):
             csp.sparse_layer_time_next(h, a, b)
             fn()
         after(reps[i % R])
     torch.cuda.synchronize()
+    # The cost of a bracket itself: the same event pairs with nothing between them, queued the
+    # same way (reported beside the kernel times, which include the event records around them).
+    empty = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2.0e9 * 0.01))
+    for a, b in empty:
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    bracket_us = sum(a.elapsed_time(b) for a, b in empty) / K * 1e3
     per_call = {}
     for ci, (label, _, _, kname, kbytes) in enumerate(calls(reps[0], stream)):
         us = sum(ev[i][ci][0].elapsed_time(ev[i][ci][1]) for i in range(K)) / K * 1e3
@@ -575,6 +599,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": dom["kernel"], "call": dom_label, "avg_launch_us": round(dom["us"], 3),
+                     "empty_event_bracket_us": round(bracket_us, 3),
                      "bytes_per_launch": dom["bytes"]},
         "kernels_us": {k: round(v["us"], 3) for k, v in per_call.items()},
         "restructure_ms": None if restructure_ms is None else round(restructure_ms, 3),
