@@ -244,6 +244,17 @@ __device__ inline void block_fence()
     asm volatile("" ::: "memory");
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i mod 8), each XCD with its own L2.  Renumbering them so that XCD x
+// takes one contiguous range of tasks keeps neighbouring segments -- whose
+// outputs share cache lines -- on one XCD, so each output line is written
+// back whole by one L2 instead of in pieces by several.
+__device__ __forceinline__ int64_t xcd_block()
+{
+    const int64_t nb = gridDim.x, b = blockIdx.x, x = b & 7, per = nb >> 3, extra = nb & 7;
+    return x * per + (x < extra ? x : extra) + (b >> 3);
+}
+
 struct Task {
     int32_t seg, kb, n, slot;
 };
@@ -345,7 +356,7 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
                                                       float *__restrict__ partial, typename D::T *__restrict__ out,
                                                       Epi ep)
 {
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
     segment_task<LD, D, kWide, E>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
 }
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
                                                      const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
                                                      int nch, float *__restrict__ dW)
 {
-    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
     values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, nch, dW);
 }
@@ -467,6 +478,8 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
 {
     const int64_t ncb = (ncol_tasks + 3) / 4, nrb = (nrow_tasks + 3) / 4;
     const int64_t m = ncb < nrb ? ncb : nrb;
+    // Plain dispatch order here: with the two task kinds interleaved, renumbering by XCD
+    // measured 6% more HBM traffic for this kernel (and 6% less for the single-kind ones).
     const int64_t bid = blockIdx.x;
     bool col;
     int64_t blk;
