@@ -385,15 +385,24 @@ def main():
     # 64-bit offsets, epilogue 0 none / 1 forward bias+activation / 2 input gradient times act')
     dt_name = "csp::BF16" if w.dtype == "bf16" else "csp::F32"
 
-    def fwd_name(epi=0):
+    esz = 2 if w.dtype == "bf16" else 4
+    lds_on = os.environ.get("COOSPMM_LDS_TABLES", "1")[:1] != "0"
+
+    def lds_fits(n):
+        """The library gathers from an LDS copy of an operand of n columns (2 <= B <= 64, <= 64 KiB)."""
+        return lds_on and 2 <= B <= 64 and n * ld * esz <= (64 << 10)
+
+    def fwd_name(L, epi=0):
+        if lds_fits(L.in_):
+            return f"k_segment_lds<{ld}, {dt_name}, {epi}>"
         return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}>"
 
-    # spmm_bwd runs both gradient passes in one launch unless their two batch-minor
-    # operand tables exceed 2 MiB together (then the two kernels run back to back)
-    big = any((2 if w.dtype == "bf16" else 4) * ld * (L.in_ + L.out) > (2 << 20) for L in layers)
-
-    def grad_name(epi=0):
-        if big:
+    def grad_name(L, epi=0):
+        if lds_fits(max(L.in_, L.out)):
+            return f"k_gradients_lds<{ld}, {dt_name}, {epi}>"
+        # spmm_bwd runs both gradient passes in one launch unless their two batch-minor
+        # operand tables exceed 2 MiB together (then the two kernels run back to back)
+        if esz * ld * (L.in_ + L.out) > (2 << 20):
             return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}> + k_values_rows<{ld}, {dt_name}, false>"
         return f"k_gradients<{ld}, {dt_name}, false, {epi}>"
 
@@ -408,7 +417,7 @@ def main():
                     # GELU fused into the producing layer's epilogue
                     csp.spmm_fwd_act(h, src, act="none" if last else "gelu", Y=dst, stream=stream)
 
-                out.append((f"forward {li + 1}", h, f, fwd_name(1), bytes_fwd(L.nnz, L.out, L.in_, B, sv=2, sx=2)))
+                out.append((f"forward {li + 1}", h, f, fwd_name(L, 1), bytes_fwd(L.nnz, L.out, L.in_, B, sv=2, sx=2)))
             return out
         if kind == "mlp":
             (h1, h2), (L1, L2) = st["h"], layers
@@ -422,21 +431,21 @@ def main():
                 csp.spmm_bwd_act(h2, st["dY"], st["A"], st["H"], act="gelu", dX=st["dH"], dW=st["dW2"],
                                  stream=stream)
 
-            out.append(("forward 1", h1, f1, fwd_name(1), bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
-            out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream), fwd_name(),
+            out.append(("forward 1", h1, f1, fwd_name(L1, 1), bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
+            out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream), fwd_name(L2),
                         bytes_fwd(L2.nnz, L2.out, L2.in_, B)))
-            out.append(("backward 2", h2, b2, grad_name(2), bytes_gradients(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("backward 2", h2, b2, grad_name(L2, 2), bytes_gradients(L2.nnz, L2.out, L2.in_, B)))
             out.append(("backward 1", h1, lambda: csp.spmm_bwd(h1, st["dH"], st["X"], st["dX"], st["dW1"],
-                                                               stream=stream), grad_name(),
+                                                               stream=stream), grad_name(L1),
                         bytes_gradients(L1.nnz, L1.out, L1.in_, B)))
             return out
         h, L = st["h"][0], layers[0]
         sv = 2 if w.dtype == "bf16" else 4
-        out.append(("forward", h, lambda: csp.spmm_fwd(h, st["X"], st["Y"], stream=stream), fwd_name(),
+        out.append(("forward", h, lambda: csp.spmm_fwd(h, st["X"], st["Y"], stream=stream), fwd_name(L),
                     bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)))
         if kind != "inference":
             out.append(("backward", h, lambda: csp.spmm_bwd(h, st["dY"], st["X"], st["dX"], st["dW"], stream=stream),
-                        grad_name(), bytes_gradients(L.nnz, L.out, L.in_, B)))
+                        grad_name(L), bytes_gradients(L.nnz, L.out, L.in_, B)))
         return out
 
     stream = torch.cuda.current_stream()

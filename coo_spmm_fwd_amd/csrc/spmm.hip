@@ -23,6 +23,8 @@
 // gradient) use DPP row operations.  No MFMA: an unstructured gather is not a
 // dense contraction; the bound is HBM for the COO stream and L1/L2 for the
 // operand gathers.
+#include <cstdlib>
+
 #include "common.h"
 #include "device_util.h"
 
@@ -271,7 +273,7 @@ __device__ inline Task load_task(const int4 *__restrict__ desc, int64_t t)
 // copy, dY).  A split segment's task stores its partial sums instead
 // (slot >= 0); the fixup launch finishes the segment.
 template <int LD, class D, bool kWide, int E>
-__device__ __attribute__((always_inline)) inline void segment_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ idx,
+__device__ __attribute__((always_inline)) inline void segment_task_body(const Task &T, const int32_t *__restrict__ idx,
                                     const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
                                     int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
                                     typename D::T *__restrict__ out, const Epi &ep)
@@ -279,7 +281,6 @@ __device__ __attribute__((always_inline)) inline void segment_task(const int4 *_
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
     const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
-    const Task T = load_task(desc, t);
 
     for (int ch = 0; ch < nch; ++ch) {
         const typename D::T *op = opT + (int64_t)ch * n_op * LD + q * VW;
@@ -348,6 +349,15 @@ __device__ __attribute__((always_inline)) inline void segment_task(const int4 *_
 }
 
 template <int LD, class D, bool kWide, int E>
+__device__ __attribute__((always_inline)) inline void segment_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ idx,
+                                    const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
+                                    int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
+                                    typename D::T *__restrict__ out, const Epi &ep)
+{
+    segment_task_body<LD, D, kWide, E>(load_task(desc, t), idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
+}
+
+template <int LD, class D, bool kWide, int E>
 __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
                                                       const int32_t *__restrict__ idx,
                                                       const typename D::T *__restrict__ vals,
@@ -394,20 +404,31 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
 // lane of the entry's group writes the same value to the same word, so no
 // lane test is needed -- and each 64-entry block leaves as one coalesced row
 // in canonical order.
-template <int LD, class D, bool kWide>
-__device__ __attribute__((always_inline)) inline void values_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ cols,
+// kRowMajorDy: dY is the caller's row-major [B, out] (small-table path, one
+// chunk); the entry's batch values then come from B scattered words, padded
+// with zeros past B.
+template <int LD, class D, bool kWide, int NW = 4, bool kRowMajorDy = false>
+__device__ __attribute__((always_inline)) inline void values_task_body(const Task &T, const int32_t *__restrict__ cols,
                                    const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
-                                   int64_t in, int64_t out, int nch, float *__restrict__ dW)
+                                   int64_t in, int64_t out, int64_t B, int nch, float *__restrict__ dW)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
-    __shared__ float stage[4][kWave];
+    __shared__ float stage[NW][kWave];
     const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
     float *lds = stage[threadIdx.x >> 6];
-    const Task T = load_task(desc, t);
     for (int ch = 0; ch < nch; ++ch) {
         float dy[VW];
-        load_vec<VW>(dYT + ((int64_t)ch * out + T.seg) * LD + q * VW, dy);
+        if constexpr (kRowMajorDy) {
+#pragma unroll
+            for (int w = 0; w < VW; ++w) {
+                const int64_t b = q * VW + w;
+                const float v = D::load(dYT, (b < B ? b : 0) * out + T.seg);
+                dy[w] = b < B ? v : 0.f;
+            }
+        } else {
+            load_vec<VW>(dYT + ((int64_t)ch * out + T.seg) * LD + q * VW, dy);
+        }
         const typename D::T *xt = XT + (int64_t)ch * in * LD + q * VW;
         for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
             const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
@@ -446,6 +467,14 @@ __device__ __attribute__((always_inline)) inline void values_task(const int4 *__
             }
         }
     }
+}
+
+template <int LD, class D, bool kWide>
+__device__ __attribute__((always_inline)) inline void values_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ cols,
+                                   const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
+                                   int64_t in, int64_t out, int nch, float *__restrict__ dW)
+{
+    values_task_body<LD, D, kWide>(load_task(desc, t), cols, XT, dYT, in, out, 0, nch, dW);
 }
 
 template <int LD, class D, bool kWide>
@@ -497,6 +526,119 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
     } else if (t < nrow_tasks) {
         values_task<LD, D, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW);
     }
+}
+
+// --------------------------------------------- small operand tables in LDS
+// When the operand a pass gathers from is small (2 <= B <= 64, so one chunk,
+// and n * ld * esz <= kLdsTableBytes), each workgroup of kLdsWaves waves
+// first copies it from the caller's row-major [B, n] into LDS in the
+// batch-minor layout [n][ld] (pad slots zero), then runs its tasks against
+// that copy.  No copy launch precedes the product, and the gathers become LDS
+// reads instead of one L2 line request each.  The tasks are the same code as
+// with the global table, so results are bitwise the same.  The gain is the
+// copy launch: with B = 1 there is none to save, and with tables above 64 KiB
+// the per-workgroup fill and the lower occupancy cost more than the L2
+// gathers they replace (measured on 16384-column layers at B = 1 and 4).
+constexpr int kLdsWaves = 16;
+constexpr int kLdsThreads = kLdsWaves * kWave;
+constexpr size_t kLdsTableBytes = size_t(64) << 10;
+
+// tab[c * LD + b] = src[b * n + c] for b < B, 0 for B <= b < LD.  Loads are
+// unconditional (row 0 stands in for pad rows) so they all issue together.
+template <int LD, class D>
+__device__ inline void fill_table(const typename D::T *__restrict__ src, int64_t n, int64_t B, typename D::T *tab)
+{
+    using T = typename D::T;
+    if constexpr (LD == 1) {
+        for (int64_t i = threadIdx.x; i < n; i += kLdsThreads) tab[i] = src[i];
+    } else {
+        constexpr int W = LD * (int)sizeof(T) / 4;  // 32-bit words per column
+        for (int64_t c = threadIdx.x; c < n; c += kLdsThreads) {
+            uint32_t w[W];
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+                for (int b = 0; b < LD; ++b) {
+                    const uint32_t x = __float_as_uint(src[(b < B ? b : 0) * n + c]);
+                    w[b] = b < B ? x : 0u;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < W; ++k) {
+                    const int b0 = 2 * k, b1 = 2 * k + 1;
+                    const uint32_t x0 = src[(b0 < B ? b0 : 0) * n + c], x1 = src[(b1 < B ? b1 : 0) * n + c];
+                    w[k] = (b0 < B ? x0 : 0u) | ((b1 < B ? x1 : 0u) << 16);
+                }
+            }
+            uint32_t *dst = reinterpret_cast<uint32_t *>(tab + c * LD);
+            if constexpr (W % 4 == 0) {
+#pragma unroll
+                for (int k = 0; k < W / 4; ++k)
+                    reinterpret_cast<uint4 *>(dst)[k] = make_uint4(w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]);
+            } else if constexpr (W == 2) {
+                *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+            } else {
+                dst[0] = w[0];
+            }
+        }
+    }
+}
+
+// Forward (row tasks over X) or input gradient (column tasks over dY).
+template <int LD, class D, int E>
+__global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restrict__ desc, int64_t ntasks,
+                                                             const int32_t *__restrict__ idx,
+                                                             const typename D::T *__restrict__ vals,
+                                                             const typename D::T *__restrict__ op, int64_t n_op,
+                                                             int64_t n_seg, int64_t B, float *__restrict__ partial,
+                                                             typename D::T *__restrict__ out, Epi ep)
+{
+    extern __shared__ __align__(16) unsigned char lds_table[];
+    auto *tab = reinterpret_cast<typename D::T *>(lds_table);
+    const int64_t t = xcd_block() * kLdsWaves + (threadIdx.x >> 6);
+    const bool has = t < ntasks;
+    const Task T = load_task(desc, has ? t : 0);  // in flight during the fill
+    fill_table<LD, D>(op, n_op, B, tab);
+    __syncthreads();
+    if (has) segment_task_body<LD, D, false, E>(T, idx, vals, tab, n_op, n_seg, B, 1, partial, out, ep);
+}
+
+// Both gradients: workgroups alternate between input-gradient column tasks
+// (table: dY) and value-gradient row tasks (table: X), as in k_gradients.
+template <int LD, class D, int E>
+__global__ __launch_bounds__(kLdsThreads) void k_gradients_lds(const int4 *__restrict__ col_desc, int64_t ncol_tasks,
+                                                               const int4 *__restrict__ row_desc, int64_t nrow_tasks,
+                                                               const int32_t *__restrict__ rows_by_col,
+                                                               const typename D::T *__restrict__ vals_c,
+                                                               const int32_t *__restrict__ cols,
+                                                               const typename D::T *__restrict__ X,
+                                                               const typename D::T *__restrict__ dY, int64_t in,
+                                                               int64_t out, int64_t B, float *__restrict__ partial,
+                                                               typename D::T *__restrict__ dX, float *__restrict__ dW,
+                                                               Epi ep)
+{
+    extern __shared__ __align__(16) unsigned char lds_table[];
+    auto *tab = reinterpret_cast<typename D::T *>(lds_table);
+    const int64_t ncb = (ncol_tasks + kLdsWaves - 1) / kLdsWaves, nrb = (nrow_tasks + kLdsWaves - 1) / kLdsWaves;
+    const int64_t m = ncb < nrb ? ncb : nrb;
+    const int64_t bid = blockIdx.x;
+    bool col;
+    int64_t blk;
+    if (bid < 2 * m) {
+        col = (bid & 1) == 0;
+        blk = bid >> 1;
+    } else {
+        col = ncb > nrb;
+        blk = m + (bid - 2 * m);
+    }
+    const int64_t t = blk * kLdsWaves + (threadIdx.x >> 6);
+    const bool has = t < (col ? ncol_tasks : nrow_tasks);
+    const Task T = load_task(col ? col_desc : row_desc, has ? t : 0);
+    if (col) fill_table<LD, D>(dY, out, B, tab);
+    else fill_table<LD, D>(X, in, B, tab);
+    __syncthreads();
+    if (!has) return;
+    if (col) segment_task_body<LD, D, false, E>(T, rows_by_col, vals_c, tab, out, in, B, 1, partial, dX, ep);
+    else values_task_body<LD, D, false, kLdsWaves, true>(T, cols, tab, dY, in, out, B, 1, dW);
 }
 
 // ------------------------------------------------------------ host side
@@ -594,6 +736,97 @@ csp_status split_fixup(csp_layer *L, const TaskList &TL, int64_t B, int64_t n_se
         TL.split, TL.nsplit, L->act.partial, B, ld, nch, n_seg, (typename D::T *)out, ep);
     CSP_LAUNCHED("k_split_fixup");
     return CSP_OK;
+}
+
+// Small-table path (see fill_table) for a pass that gathers from an operand
+// of n columns.  COOSPMM_LDS_TABLES=0 forces the global-table path (A/B runs
+// and tests of both paths).
+inline bool lds_table_fits(const csp_layer *L, int64_t B, int64_t n)
+{
+    if (B < 2 || B > 64 || (size_t)n * (size_t)pow2_ld(B) * (size_t)L->esz > kLdsTableBytes) return false;
+    const char *e = std::getenv("COOSPMM_LDS_TABLES");
+    return !(e && e[0] == '0');
+}
+
+// The kernel's dynamic LDS limit is raised to the table size once per kernel
+// (the value-gradient stage array is static LDS on top of it).
+template <auto Kern>
+csp_status allow_lds(size_t)
+{
+    static bool done = false;
+    if (!done) {
+        CSP_HIP(hipFuncSetAttribute(reinterpret_cast<const void *>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)kLdsTableBytes));
+        done = true;
+    }
+    return CSP_OK;
+}
+
+#define CSP_LD_SWITCH_LDS(ld, MACRO) \
+    switch (ld) {                    \
+    case 1: MACRO(1); break;         \
+    case 2: MACRO(2); break;         \
+    case 4: MACRO(4); break;         \
+    case 8: MACRO(8); break;         \
+    case 16: MACRO(16); break;       \
+    case 32: MACRO(32); break;       \
+    default: MACRO(64); break;       \
+    }
+
+// One segment pass (forward: rows over X; input gradient: columns over dY)
+// from a row-major operand through an LDS table.
+template <class D, int E>
+csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t *idx, const void *vals, const void *op,
+                                int64_t n_op, int64_t n_seg, int64_t B, void *out, const Epi &ep, hipStream_t s)
+{
+    using T = typename D::T;
+    const int ld = pow2_ld(B);
+    const unsigned grid = (unsigned)ceil_div(TL.count, kLdsWaves);
+    const size_t lds = (size_t)n_op * ld * L->esz;
+    csp_status st = CSP_OK;
+    timing_mark(L, true, s);
+#define CSP_SEGL(LDV)                                                                                            \
+    if ((st = allow_lds<k_segment_lds<LDV, D, E>>(lds)) == CSP_OK)                                              \
+        k_segment_lds<LDV, D, E><<<grid, kLdsThreads, lds, s>>>(TL.desc, TL.count, idx, (const T *)vals,          \
+                                                                (const T *)op, n_op, n_seg, B, L->act.partial, \
+                                                                (T *)out, ep)
+    CSP_LD_SWITCH_LDS(ld, CSP_SEGL);
+#undef CSP_SEGL
+    if (st != CSP_OK) return st;
+    CSP_LAUNCHED("k_segment_lds");
+    timing_mark(L, false, s);
+    return split_fixup<D, E>(L, TL, B, n_seg, out, ep, s);
+}
+
+// Both gradients (or only the value gradient when with_dx is false) from
+// row-major X and dY through LDS tables.
+template <class D, int E>
+csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, int64_t B, void *dX, float *dW,
+                                  bool with_dx, const Epi &ep, hipStream_t s)
+{
+    using T = typename D::T;
+    const int ld = pow2_ld(B);
+    const TaskList &CT = L->col_tasks, &RT = L->row_tasks;
+    const int64_t ncol = with_dx ? CT.count : 0;
+    const int64_t nrow = L->nnz > 0 ? RT.count : 0;  // no value-gradient work for an empty layer
+    const unsigned grid = (unsigned)(ceil_div(ncol, kLdsWaves) + ceil_div(nrow, kLdsWaves));
+    if (grid == 0) return CSP_OK;
+    // the value gradient alone needs only the X table
+    const int64_t n_tab = with_dx && L->out > L->in ? L->out : L->in;
+    const size_t lds = (size_t)n_tab * ld * L->esz;
+    csp_status st = CSP_OK;
+    timing_mark(L, true, s);
+#define CSP_GRADL(LDV)                                                                                          \
+    if ((st = allow_lds<k_gradients_lds<LDV, D, E>>(lds)) == CSP_OK)                                           \
+        k_gradients_lds<LDV, D, E><<<grid, kLdsThreads, lds, s>>>(                                              \
+            CT.desc, ncol, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)X,          \
+            (const T *)dY, L->in, L->out, B, L->act.partial, (T *)dX, dW, ep)
+    CSP_LD_SWITCH_LDS(ld, CSP_GRADL);
+#undef CSP_GRADL
+    if (st != CSP_OK) return st;
+    CSP_LAUNCHED("k_gradients_lds");
+    timing_mark(L, false, s);
+    return with_dx ? split_fixup<D, E>(L, CT, B, L->in, dX, ep, s) : CSP_OK;
 }
 
 template <class D, int E>
@@ -720,10 +953,18 @@ csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const Fwd
 {
     csp_status st = ensure_act(L, B);
     if (st != CSP_OK) return st;
+    const Epi ep = make_epi(fe);
+    if (lds_table_fits(L, B, L->in)) {
+        const TaskList &RT = L->row_tasks;
+        if (L->dtype == CSP_BF16)
+            return fe ? segment_lds_dispatch<BF16, kEpiForward>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s)
+                      : segment_lds_dispatch<BF16, kEpiNone>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s);
+        return fe ? segment_lds_dispatch<F32, kEpiForward>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s)
+                  : segment_lds_dispatch<F32, kEpiNone>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s);
+    }
     st = batch_minor(L, B, X, L->in, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
     const void *xt = B == 1 ? X : L->act.a;
-    const Epi ep = make_epi(fe);
     if (L->dtype == CSP_BF16)
         return fe ? fwd_dispatch<BF16, kEpiForward>(L, xt, B, Y, ep, s) : fwd_dispatch<BF16, kEpiNone>(L, xt, B, Y, ep, s);
     return fe ? fwd_dispatch<F32, kEpiForward>(L, xt, B, Y, ep, s) : fwd_dispatch<F32, kEpiNone>(L, xt, B, Y, ep, s);
@@ -733,11 +974,21 @@ csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, c
 {
     csp_status st = ensure_act(L, B);
     if (st != CSP_OK) return st;
+    Epi ep;
+    ep.act_in = act_in;
+    if (lds_table_fits(L, B, L->out)) {
+        const TaskList &CT = L->col_tasks;
+        const int32_t *rc = L->rows_by_col;
+        const void *vc = L->vals_c;
+        if (L->dtype == CSP_BF16)
+            return act_in ? segment_lds_dispatch<BF16, kEpiActGrad>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s)
+                          : segment_lds_dispatch<BF16, kEpiNone>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s);
+        return act_in ? segment_lds_dispatch<F32, kEpiActGrad>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s)
+                      : segment_lds_dispatch<F32, kEpiNone>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s);
+    }
     st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
     const void *dyt = B == 1 ? dY : L->act.a;
-    Epi ep;
-    ep.act_in = act_in;
     if (L->dtype == CSP_BF16)
         return act_in ? bwd_input_dispatch<BF16, kEpiActGrad>(L, dyt, B, dX, ep, s)
                       : bwd_input_dispatch<BF16, kEpiNone>(L, dyt, B, dX, ep, s);
@@ -750,6 +1001,11 @@ csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_
     if (L->nnz == 0) return CSP_OK;
     csp_status st = ensure_act(L, B);
     if (st != CSP_OK) return st;
+    if (lds_table_fits(L, B, L->in)) {
+        const Epi ep;
+        return L->dtype == CSP_BF16 ? gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, nullptr, dW, false, ep, s)
+                                    : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, nullptr, dW, false, ep, s);
+    }
     st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
     if (st != CSP_OK) return st;
     const void *xt = B == 1 ? X : L->act.a;
@@ -763,12 +1019,19 @@ csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, vo
 {
     csp_status st = ensure_act(L, B);
     if (st != CSP_OK) return st;
+    Epi ep;
+    ep.act_in = act_in;
+    if (lds_table_fits(L, B, L->in > L->out ? L->in : L->out)) {
+        if (L->dtype == CSP_BF16)
+            return act_in ? gradients_lds_dispatch<BF16, kEpiActGrad>(L, X, dY, B, dX, dW, true, ep, s)
+                          : gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, dX, dW, true, ep, s);
+        return act_in ? gradients_lds_dispatch<F32, kEpiActGrad>(L, X, dY, B, dX, dW, true, ep, s)
+                      : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, dX, dW, true, ep, s);
+    }
     st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
     if (st != CSP_OK) return st;
     const void *xt = B == 1 ? X : L->act.a;
     const void *dyt = B == 1 ? dY : L->act.b;
-    Epi ep;
-    ep.act_in = act_in;
     if (L->dtype == CSP_BF16)
         return act_in ? bwd_dispatch<BF16, kEpiActGrad>(L, xt, dyt, B, dX, dW, ep, s)
                       : bwd_dispatch<BF16, kEpiNone>(L, xt, dyt, B, dX, dW, ep, s);
