@@ -392,9 +392,16 @@ def main():
         """The library gathers from an LDS copy of an operand of n columns (2 <= B <= 64, <= 64 KiB)."""
         return lds_on and 2 <= B <= 64 and n * ld * esz <= (64 << 10)
 
+    grouped_on = os.environ.get("COOSPMM_GROUPED_SPLITS", "1")[:1] != "0"
+
     def fwd_name(L, epi=0):
         if lds_fits(L.in_):
             return f"k_segment_lds<{ld}, {dt_name}, {epi}>"
+        # split rows (over 512 entries) finish inside the pass when no row can exceed 64 tasks
+        import numpy as np
+        longest = int(np.bincount(L.rows, minlength=L.out).max()) if L.nnz else 0
+        if grouped_on and B <= 64 and longest > 512 and L.in_ <= 64 * 512:
+            return f"k_segment_grouped<{ld}, {dt_name}, false, {epi}>"
         return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}>"
 
     def grad_name(L, epi=0):

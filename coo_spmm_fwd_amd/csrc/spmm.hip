@@ -272,7 +272,9 @@ __device__ inline Task load_task(const int4 *__restrict__ desc, int64_t t)
 // Input gradient: column tasks over (rows_by_col, column-ordered value
 // copy, dY).  A split segment's task stores its partial sums instead
 // (slot >= 0); the fixup launch finishes the segment.
-template <int LD, class D, bool kWide, int E>
+// kStore: 0 = by the task's slot (store the output, or the partial sums of a
+// split task), 1 = always the output, 2 = always the partial sums.
+template <int LD, class D, bool kWide, int E, int kStore = 0>
 __device__ __attribute__((always_inline)) inline void segment_task_body(const Task &T, const int32_t *__restrict__ idx,
                                     const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
                                     int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
@@ -341,8 +343,10 @@ __device__ __attribute__((always_inline)) inline void segment_task_body(const Ta
             for (int w = 0; w < VW; ++w) {
                 const int64_t b = (int64_t)ch * LD + q * VW + w;
                 if (b >= B) continue;
-                if (T.slot < 0) out[b * n_seg + T.seg] = finish_out<E, D>(acc[w], b, T.seg, n_seg, ep);
-                else partial[((int64_t)T.slot * nch + ch) * LD + q * VW + w] = acc[w];
+                if (kStore == 1 || (kStore == 0 && T.slot < 0))
+                    out[b * n_seg + T.seg] = finish_out<E, D>(acc[w], b, T.seg, n_seg, ep);
+                else
+                    partial[((int64_t)T.slot * nch + ch) * LD + q * VW + w] = acc[w];
             }
         }
     }
@@ -369,6 +373,50 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
     const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
     segment_task<LD, D, kWide, E>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
+}
+
+// Segment pass with split segments finished in the kernel (one batch chunk,
+// every segment at most kGroupMaxTasks tasks).  Workgroups [0, nsplit) each
+// take one split segment: its 16 waves run the segment's tasks (wave w: tasks
+// w, w + 16, ...), put their sums in LDS, and after a barrier one lane per
+// batch index adds them in task order -- the order the fixup launch uses, so
+// results are bitwise those of the split-plus-fixup path.  Split segments come
+// first so that long rows start at once.  The remaining workgroups take 16
+// consecutive tasks each and skip the split ones.
+constexpr int kGroupWaves = 16;
+constexpr int kGroupMaxTasks = 64;
+
+template <int LD, class D, bool kWide, int E>
+__global__ __launch_bounds__(kGroupWaves * kWave) void k_segment_grouped(
+    const int4 *__restrict__ desc, int64_t ntasks, const int4 *__restrict__ split, int64_t nsplit,
+    const int32_t *__restrict__ idx, const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
+    int64_t n_op, int64_t n_seg, int64_t B, typename D::T *__restrict__ out, Epi ep)
+{
+    __shared__ float part[kGroupMaxTasks][LD];
+    const int wave = threadIdx.x >> 6;
+    const int64_t g = blockIdx.x;
+    if (g < nsplit) {
+        const int4 r = split[g];  // {segment, first task, task count, 0}
+        const int32_t seg = uniform(r.x), first = uniform(r.y), cnt = uniform(r.z);
+        // a split task's slot is its task index, so its partial sums land in part[slot - first]
+        float *base = &part[0][0] - (int64_t)first * LD;
+        for (int32_t j = wave; j < cnt; j += kGroupWaves)
+            segment_task_body<LD, D, kWide, E, 2>(load_task(desc, first + j), idx, vals, opT, n_op, n_seg, B, 1,
+                                                  base, out, ep);
+        __syncthreads();
+        if (threadIdx.x < B) {
+            const int64_t b = threadIdx.x;
+            float tot = 0.f;
+            for (int32_t j = 0; j < cnt; ++j) tot += part[j][b];
+            out[b * n_seg + seg] = finish_out<E, D>(tot, b, seg, n_seg, ep);
+        }
+        return;
+    }
+    const int64_t t = (g - nsplit) * kGroupWaves + wave;
+    if (t >= ntasks) return;
+    const Task T = load_task(desc, t);
+    if (T.slot >= 0) return;  // part of a split segment: finished by its own workgroup
+    segment_task_body<LD, D, kWide, E, 1>(T, idx, vals, opT, n_op, n_seg, B, 1, nullptr, out, ep);
 }
 
 // Finish split segments: out[b, seg] = sum over the segment's tasks, in task
@@ -829,6 +877,36 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
     return with_dx ? split_fixup<D, E>(L, CT, B, L->in, dX, ep, s) : CSP_OK;
 }
 
+// Split segments finished inside the segment pass (k_segment_grouped) when
+// there are any, one batch chunk covers B, and no segment can have more than
+// kGroupMaxTasks tasks (its length is at most max_len, the other dimension).
+// COOSPMM_GROUPED_SPLITS=0 keeps the split-plus-fixup path.
+inline bool grouped_splits(const TaskList &TL, int64_t B, int64_t max_len, int64_t n_op)
+{
+    if (TL.nsplit == 0 || B > 64 || ceil_div(max_len, kTaskChunk) > kGroupMaxTasks) return false;
+    if (wide_operand(n_op, pow2_ld(B))) return false;
+    const char *e = std::getenv("COOSPMM_GROUPED_SPLITS");
+    return !(e && e[0] == '0');
+}
+
+template <class D, int E>
+csp_status grouped_dispatch(csp_layer *L, const TaskList &TL, const int32_t *idx, const void *vals, const void *opT,
+                            int64_t n_op, int64_t n_seg, int64_t B, void *out, const Epi &ep, hipStream_t s)
+{
+    using T = typename D::T;
+    const int ld = pow2_ld(B);
+    const unsigned grid = (unsigned)(TL.nsplit + ceil_div(TL.count, kGroupWaves));
+    timing_mark(L, true, s);
+#define CSP_GRP(LDV)                                                                                            \
+    k_segment_grouped<LDV, D, false, E><<<grid, kGroupWaves * kWave, 0, s>>>(                                   \
+        TL.desc, TL.count, TL.split, TL.nsplit, idx, (const T *)vals, (const T *)opT, n_op, n_seg, B, (T *)out, ep)
+    CSP_LD_SWITCH_LDS(ld, CSP_GRP);
+#undef CSP_GRP
+    CSP_LAUNCHED("k_segment_grouped");
+    timing_mark(L, false, s);
+    return CSP_OK;
+}
+
 template <class D, int E>
 csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const Epi &ep, hipStream_t s)
 {
@@ -836,6 +914,8 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->row_tasks;
+    if (grouped_splits(TL, B, L->in, L->in))
+        return grouped_dispatch<D, E>(L, TL, L->cols, L->vals, XT, L->in, L->out, B, Y, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
 #define CSP_FWD(LDV, W)                                                                                             \
@@ -855,6 +935,8 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
     const int ld = pow2_ld(B);
     const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->col_tasks;
+    if (grouped_splits(TL, B, L->out, L->out))
+        return grouped_dispatch<D, E>(L, TL, L->rows_by_col, L->vals_c, dYT, L->out, L->in, B, dX, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
 #define CSP_DX(LDV, W)                                                                                        \
