@@ -130,7 +130,7 @@ def ingest_counters(fetch_dir, write_dir, workload, batch, copy_mib=256):
     f_scale = copy_bytes / (cf * 1024) if cf else None
     w_scale = copy_bytes / (cw * 1024) if cw else None
     rec = {}
-    for name in (f"k_gradients<{ld}, csp::F32, false, 0>", f"k_segment_spmm<{ld}, csp::F32, false, 0>"):
+    for name in (f"k_gradients<{ld}, csp::F32, false, 0, 1>", f"k_segment_spmm<{ld}, csp::F32, false, 0, 1>"):
         m = lambda n, name=name: name in n
         kf, nf = _per_dispatch(fetch, "FETCH_SIZE", m)
         kw, nw = _per_dispatch(write, "WRITE_SIZE", m)
@@ -393,25 +393,38 @@ def main():
         return lds_on and 2 <= B <= 64 and n * ld * esz <= (64 << 10)
 
     grouped_on = os.environ.get("COOSPMM_GROUPED_SPLITS", "1")[:1] != "0"
+    import numpy as np
 
+    # longest row and column of each layer (segments over 512 entries are split into tasks);
+    # computed once here, outside every timed loop
+    seg_max = {}
+    for L in layers:
+        seg_max[id(L)] = tuple(int(np.bincount(a, minlength=n).max()) if L.nnz else 0
+                               for a, n in ((L.rows, L.out), (L.cols, L.in_)))
+
+    def longest(L, rows):
+        return seg_max[id(L)][0 if rows else 1]
+
+    # The last template argument of the segment kernels is 1 when the pass's task list has no
+    # split segment (every task stores its output), else 0.
     def fwd_name(L, epi=0):
+        ks = int(longest(L, True) <= 512)
         if lds_fits(L.in_):
-            return f"k_segment_lds<{ld}, {dt_name}, {epi}>"
-        # split rows (over 512 entries) finish inside the pass when no row can exceed 64 tasks
-        import numpy as np
-        longest = int(np.bincount(L.rows, minlength=L.out).max()) if L.nnz else 0
-        if grouped_on and B <= 64 and longest > 512 and L.in_ <= 64 * 512:
+            return f"k_segment_lds<{ld}, {dt_name}, {epi}, {ks}>"
+        # split rows finish inside the pass when no row can exceed 64 tasks
+        if grouped_on and B <= 64 and not ks and L.in_ <= 64 * 512:
             return f"k_segment_grouped<{ld}, {dt_name}, false, {epi}>"
-        return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}>"
+        return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}, {ks}>"
 
     def grad_name(L, epi=0):
+        ks = int(longest(L, False) <= 512)
         if lds_fits(max(L.in_, L.out)):
-            return f"k_gradients_lds<{ld}, {dt_name}, {epi}>"
+            return f"k_gradients_lds<{ld}, {dt_name}, {epi}, {ks}>"
         # spmm_bwd runs both gradient passes in one launch unless their two batch-minor
         # operand tables exceed 2 MiB together (then the two kernels run back to back)
         if esz * ld * (L.in_ + L.out) > (2 << 20):
-            return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}> + k_values_rows<{ld}, {dt_name}, false>"
-        return f"k_gradients<{ld}, {dt_name}, false, {epi}>"
+            return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}, {ks}> + k_values_rows<{ld}, {dt_name}, false>"
+        return f"k_gradients<{ld}, {dt_name}, false, {epi}, {ks}>"
 
     def calls(st, stream):
         """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic bytes)."""

@@ -352,16 +352,18 @@ __device__ __attribute__((always_inline)) inline void segment_task_body(const Ta
     }
 }
 
-template <int LD, class D, bool kWide, int E>
+template <int LD, class D, bool kWide, int E, int kStore = 0>
 __device__ __attribute__((always_inline)) inline void segment_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ idx,
                                     const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
                                     int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
                                     typename D::T *__restrict__ out, const Epi &ep)
 {
-    segment_task_body<LD, D, kWide, E>(load_task(desc, t), idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
+    segment_task_body<LD, D, kWide, E, kStore>(load_task(desc, t), idx, vals, opT, n_op, n_seg, B, nch, partial, out,
+                                               ep);
 }
 
-template <int LD, class D, bool kWide, int E>
+// kStore = 1 when the list has no split segments (every task stores its output).
+template <int LD, class D, bool kWide, int E, int kStore>
 __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
                                                       const int32_t *__restrict__ idx,
                                                       const typename D::T *__restrict__ vals,
@@ -372,7 +374,7 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
 {
     const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    segment_task<LD, D, kWide, E>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
+    segment_task<LD, D, kWide, E, kStore>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
 }
 
 // Segment pass with split segments finished in the kernel (one batch chunk,
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
 // latency chains overlap: even/odd blocks alternate between input-gradient
 // column tasks and value-gradient row tasks, the longer list's surplus
 // blocks come last.
-template <int LD, class D, bool kWide, int E>
+template <int LD, class D, bool kWide, int E, int kStore>
 __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_desc, int64_t ncol_tasks,
                                                    const int4 *__restrict__ row_desc, int64_t nrow_tasks,
                                                    const int32_t *__restrict__ rows_by_col,
@@ -570,7 +572,8 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
     const int64_t t = blk * 4 + (threadIdx.x >> 6);
     if (col) {
         if (t < ncol_tasks)
-            segment_task<LD, D, kWide, E>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, nch, partial, dX, ep);
+            segment_task<LD, D, kWide, E, kStore>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, nch, partial, dX,
+                                                  ep);
     } else if (t < nrow_tasks) {
         values_task<LD, D, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW);
     }
@@ -632,7 +635,7 @@ __device__ inline void fill_table(const typename D::T *__restrict__ src, int64_t
 }
 
 // Forward (row tasks over X) or input gradient (column tasks over dY).
-template <int LD, class D, int E>
+template <int LD, class D, int E, int kStore>
 __global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restrict__ desc, int64_t ntasks,
                                                              const int32_t *__restrict__ idx,
                                                              const typename D::T *__restrict__ vals,
@@ -647,12 +650,12 @@ __global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restr
     const Task T = load_task(desc, has ? t : 0);  // in flight during the fill
     fill_table<LD, D>(op, n_op, B, tab);
     __syncthreads();
-    if (has) segment_task_body<LD, D, false, E>(T, idx, vals, tab, n_op, n_seg, B, 1, partial, out, ep);
+    if (has) segment_task_body<LD, D, false, E, kStore>(T, idx, vals, tab, n_op, n_seg, B, 1, partial, out, ep);
 }
 
 // Both gradients: workgroups alternate between input-gradient column tasks
 // (table: dY) and value-gradient row tasks (table: X), as in k_gradients.
-template <int LD, class D, int E>
+template <int LD, class D, int E, int kStore>
 __global__ __launch_bounds__(kLdsThreads) void k_gradients_lds(const int4 *__restrict__ col_desc, int64_t ncol_tasks,
                                                                const int4 *__restrict__ row_desc, int64_t nrow_tasks,
                                                                const int32_t *__restrict__ rows_by_col,
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(kLdsThreads) void k_gradients_lds(const int4 *__res
     else fill_table<LD, D>(X, in, B, tab);
     __syncthreads();
     if (!has) return;
-    if (col) segment_task_body<LD, D, false, E>(T, rows_by_col, vals_c, tab, out, in, B, 1, partial, dX, ep);
+    if (col) segment_task_body<LD, D, false, E, kStore>(T, rows_by_col, vals_c, tab, out, in, B, 1, partial, dX, ep);
     else values_task_body<LD, D, false, kLdsWaves, true>(T, cols, tab, dY, in, out, B, 1, dW);
 }
 
@@ -833,13 +836,18 @@ csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t 
     const size_t lds = (size_t)n_op * ld * L->esz;
     csp_status st = CSP_OK;
     timing_mark(L, true, s);
-#define CSP_SEGL(LDV)                                                                                            \
-    if ((st = allow_lds<k_segment_lds<LDV, D, E>>(lds)) == CSP_OK)                                              \
-        k_segment_lds<LDV, D, E><<<grid, kLdsThreads, lds, s>>>(TL.desc, TL.count, idx, (const T *)vals,          \
-                                                                (const T *)op, n_op, n_seg, B, L->act.partial, \
-                                                                (T *)out, ep)
+    const bool ks = TL.nsplit == 0;  // no split segments: every task stores its output
+#define CSP_SEGL_ARGS TL.desc, TL.count, idx, (const T *)vals, (const T *)op, n_op, n_seg, B, L->act.partial, (T *)out, ep
+#define CSP_SEGL(LDV)                                                                                        \
+    if (ks) {                                                                                                \
+        if ((st = allow_lds<k_segment_lds<LDV, D, E, 1>>(lds)) == CSP_OK)                                   \
+            k_segment_lds<LDV, D, E, 1><<<grid, kLdsThreads, lds, s>>>(CSP_SEGL_ARGS);                      \
+    } else if ((st = allow_lds<k_segment_lds<LDV, D, E, 0>>(lds)) == CSP_OK) {                               \
+        k_segment_lds<LDV, D, E, 0><<<grid, kLdsThreads, lds, s>>>(CSP_SEGL_ARGS);                          \
+    }
     CSP_LD_SWITCH_LDS(ld, CSP_SEGL);
 #undef CSP_SEGL
+#undef CSP_SEGL_ARGS
     if (st != CSP_OK) return st;
     CSP_LAUNCHED("k_segment_lds");
     timing_mark(L, false, s);
@@ -864,13 +872,20 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
     const size_t lds = (size_t)n_tab * ld * L->esz;
     csp_status st = CSP_OK;
     timing_mark(L, true, s);
-#define CSP_GRADL(LDV)                                                                                          \
-    if ((st = allow_lds<k_gradients_lds<LDV, D, E>>(lds)) == CSP_OK)                                           \
-        k_gradients_lds<LDV, D, E><<<grid, kLdsThreads, lds, s>>>(                                              \
-            CT.desc, ncol, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)X,          \
-            (const T *)dY, L->in, L->out, B, L->act.partial, (T *)dX, dW, ep)
+    const bool ks = CT.nsplit == 0 || !with_dx;
+#define CSP_GRADL_ARGS                                                                                   \
+    CT.desc, ncol, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)X, (const T *)dY, \
+        L->in, L->out, B, L->act.partial, (T *)dX, dW, ep
+#define CSP_GRADL(LDV)                                                                                       \
+    if (ks) {                                                                                                \
+        if ((st = allow_lds<k_gradients_lds<LDV, D, E, 1>>(lds)) == CSP_OK)                                 \
+            k_gradients_lds<LDV, D, E, 1><<<grid, kLdsThreads, lds, s>>>(CSP_GRADL_ARGS);                   \
+    } else if ((st = allow_lds<k_gradients_lds<LDV, D, E, 0>>(lds)) == CSP_OK) {                             \
+        k_gradients_lds<LDV, D, E, 0><<<grid, kLdsThreads, lds, s>>>(CSP_GRADL_ARGS);                       \
+    }
     CSP_LD_SWITCH_LDS(ld, CSP_GRADL);
 #undef CSP_GRADL
+#undef CSP_GRADL_ARGS
     if (st != CSP_OK) return st;
     CSP_LAUNCHED("k_gradients_lds");
     timing_mark(L, false, s);
@@ -918,11 +933,15 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
         return grouped_dispatch<D, E>(L, TL, L->cols, L->vals, XT, L->in, L->out, B, Y, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
-#define CSP_FWD(LDV, W)                                                                                             \
-    k_segment_spmm<LDV, D, W, E><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, \
-                                                      L->in, L->out, B, nch, L->act.partial, (T *)Y, ep)
+    const bool ks = TL.nsplit == 0;
+#define CSP_FWD_ARGS \
+    TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, nch, L->act.partial, (T *)Y, ep
+#define CSP_FWD(LDV, W)                                                             \
+    if (ks) k_segment_spmm<LDV, D, W, E, 1><<<grid, 256, 0, s>>>(CSP_FWD_ARGS);    \
+    else k_segment_spmm<LDV, D, W, E, 0><<<grid, 256, 0, s>>>(CSP_FWD_ARGS)
     CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_FWD);
 #undef CSP_FWD
+#undef CSP_FWD_ARGS
     CSP_LAUNCHED("k_segment_spmm (forward)");
     timing_mark(L, false, s);
     return split_fixup<D, E>(L, TL, B, L->out, Y, ep, s);
@@ -939,12 +958,16 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
         return grouped_dispatch<D, E>(L, TL, L->rows_by_col, L->vals_c, dYT, L->out, L->in, B, dX, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     timing_mark(L, true, s);
-#define CSP_DX(LDV, W)                                                                                        \
-    k_segment_spmm<LDV, D, W, E><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->rows_by_col, (const T *)L->vals_c, \
-                                                      (const T *)dYT, L->out, L->in, B, nch, L->act.partial,    \
-                                                      (T *)dX, ep)
+    const bool ks = TL.nsplit == 0;
+#define CSP_DX_ARGS                                                                                                 \
+    TL.desc, TL.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, nch, L->act.partial, \
+        (T *)dX, ep
+#define CSP_DX(LDV, W)                                                            \
+    if (ks) k_segment_spmm<LDV, D, W, E, 1><<<grid, 256, 0, s>>>(CSP_DX_ARGS);   \
+    else k_segment_spmm<LDV, D, W, E, 0><<<grid, 256, 0, s>>>(CSP_DX_ARGS)
     CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_DX);
 #undef CSP_DX
+#undef CSP_DX_ARGS
     CSP_LAUNCHED("k_segment_spmm (input gradient)");
     timing_mark(L, false, s);
     return split_fixup<D, E>(L, TL, B, L->in, dX, ep, s);
@@ -987,12 +1010,16 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
     if (table_bytes > (int64_t(2) << 20)) {
         const unsigned gx = (unsigned)ceil_div(CT.count, 4), gw = (unsigned)ceil_div(nrow, 4);
         timing_mark(L, true, s);
-#define CSP_DX2(LDV, W)                                                                                     \
-    k_segment_spmm<LDV, D, W, E><<<gx, 256, 0, s>>>(CT.desc, CT.count, L->rows_by_col, (const T *)L->vals_c, \
-                                                    (const T *)dYT, L->out, L->in, B, nch, L->act.partial,    \
-                                                    (T *)dX, ep)
+        const bool ks = CT.nsplit == 0;
+#define CSP_DX2_ARGS                                                                                                \
+    CT.desc, CT.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, nch, L->act.partial, \
+        (T *)dX, ep
+#define CSP_DX2(LDV, W)                                                         \
+    if (ks) k_segment_spmm<LDV, D, W, E, 1><<<gx, 256, 0, s>>>(CSP_DX2_ARGS);  \
+    else k_segment_spmm<LDV, D, W, E, 0><<<gx, 256, 0, s>>>(CSP_DX2_ARGS)
         CSP_LD_SWITCH(ld, wide, CSP_DX2);
 #undef CSP_DX2
+#undef CSP_DX2_ARGS
         CSP_LAUNCHED("k_segment_spmm (input gradient)");
         if (gw > 0) {
 #define CSP_DW2(LDV, W)                                                                                           \
@@ -1007,12 +1034,16 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
     }
     const unsigned grid = (unsigned)(ceil_div(CT.count, 4) + ceil_div(nrow, 4));
     timing_mark(L, true, s);
-#define CSP_BOTH(LDV, W)                                                                                         \
-    k_gradients<LDV, D, W, E><<<grid, 256, 0, s>>>(CT.desc, CT.count, RT.desc, nrow, L->rows_by_col,           \
-                                                   (const T *)L->vals_c, L->cols, (const T *)XT, (const T *)dYT, \
-                                                   L->in, L->out, B, nch, L->act.partial, (T *)dX, dW, ep)
+    const bool ks = CT.nsplit == 0;
+#define CSP_BOTH_ARGS                                                                                            \
+    CT.desc, CT.count, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)XT, (const T *)dYT, \
+        L->in, L->out, B, nch, L->act.partial, (T *)dX, dW, ep
+#define CSP_BOTH(LDV, W)                                                        \
+    if (ks) k_gradients<LDV, D, W, E, 1><<<grid, 256, 0, s>>>(CSP_BOTH_ARGS);  \
+    else k_gradients<LDV, D, W, E, 0><<<grid, 256, 0, s>>>(CSP_BOTH_ARGS)
     CSP_LD_SWITCH(ld, wide, CSP_BOTH);
 #undef CSP_BOTH
+#undef CSP_BOTH_ARGS
     CSP_LAUNCHED("k_gradients");
     timing_mark(L, false, s);
     return split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
