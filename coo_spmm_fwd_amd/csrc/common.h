@@ -51,9 +51,14 @@ struct Workspace {
     int64_t hash_slots = 0, bm_batch_cap = 0;
 };
 
+// Batch rows per slice of a product call: one batch-minor chunk.  The
+// operand workspace is sized for one slice at create; larger batches run
+// slice after slice.
+constexpr int64_t kSliceRows = 64;
+
 struct ActBuffer {
-    // Batch-minor copies of dense operands ([chunk][n][ld]) and split-segment
-    // partial sums, grown on demand with the batch size.
+    // Batch-minor copies of dense operands ([n][ld], ld <= kSliceRows) and
+    // split-segment partial sums, allocated at create for one slice.
     void *a = nullptr, *b = nullptr;
     size_t bytes = 0;
     float *partial = nullptr;

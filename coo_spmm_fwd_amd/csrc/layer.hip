@@ -91,6 +91,11 @@ csp_status alloc_layer(csp_layer *L)
     const size_t cap = (size_t)W.nkey_cap;
     L->row_tasks.cap = task_cap(out, nnz);
     L->col_tasks.cap = task_cap(in, nnz);
+    const size_t act_bytes = (size_t)L->esz * kSliceRows * (size_t)nseg_max;
+    const size_t tcap = (size_t)(L->row_tasks.cap > L->col_tasks.cap ? L->row_tasks.cap : L->col_tasks.cap);
+    const size_t partial_bytes = sizeof(float) * kSliceRows * tcap;
+    L->act.bytes = act_bytes;
+    L->act.partial_bytes = partial_bytes;
     struct Req { void **p; size_t bytes; const char *what; } reqs[] = {
         {(void **)&L->rows, 4 * n, "rows"},
         {(void **)&L->cols, 4 * n, "cols"},
@@ -121,6 +126,10 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&L->col_tasks.desc, 16 * (size_t)L->col_tasks.cap, "column tasks"},
         {(void **)&L->col_tasks.split, 16 * (size_t)in, "split columns"},
         {(void **)&L->col_tasks.seg_first, 4 * (size_t)(in + 1), "column task offsets"},
+        // batch-minor operand copies for one slice of up to 64 batch rows, and the split partial sums
+        {&L->act.a, act_bytes, "operand copy"},
+        {&L->act.b, act_bytes, "operand copy"},
+        {(void **)&L->act.partial, partial_bytes, "split partial sums"},
     };
     for (auto &r : reqs) {
         csp_status st = dalloc(r.p, r.bytes, r.what);

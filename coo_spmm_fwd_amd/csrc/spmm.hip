@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
 template <int LD, class D, bool kWide, int NW = 4, bool kRowMajorDy = false>
 __device__ __attribute__((always_inline)) inline void values_task_body(const Task &T, const int32_t *__restrict__ cols,
                                    const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
-                                   int64_t in, int64_t out, int64_t B, int nch, float *__restrict__ dW)
+                                   int64_t in, int64_t out, int64_t B, int nch, float *__restrict__ dW, bool acc)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
@@ -511,7 +511,7 @@ __device__ __attribute__((always_inline)) inline void values_task_body(const Tas
                 const float r = lds[lane];
                 const int32_t e = p0 + u * kWave + lane;
                 if (e < T.n) {
-                    if (ch == 0) dW[T.kb + e] = r;
+                    if (ch == 0 && !acc) dW[T.kb + e] = r;
                     else dW[T.kb + e] += r;
                 }
             }
@@ -522,9 +522,9 @@ __device__ __attribute__((always_inline)) inline void values_task_body(const Tas
 template <int LD, class D, bool kWide>
 __device__ __attribute__((always_inline)) inline void values_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ cols,
                                    const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
-                                   int64_t in, int64_t out, int nch, float *__restrict__ dW)
+                                   int64_t in, int64_t out, int nch, float *__restrict__ dW, bool acc)
 {
-    values_task_body<LD, D, kWide>(load_task(desc, t), cols, XT, dYT, in, out, 0, nch, dW);
+    values_task_body<LD, D, kWide>(load_task(desc, t), cols, XT, dYT, in, out, 0, nch, dW, acc);
 }
 
 template <int LD, class D, bool kWide>
@@ -532,11 +532,11 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
                                                      const int32_t *__restrict__ cols,
                                                      const typename D::T *__restrict__ XT,
                                                      const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
-                                                     int nch, float *__restrict__ dW)
+                                                     int nch, float *__restrict__ dW, int acc)
 {
     const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, nch, dW);
+    values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, nch, dW, acc != 0);
 }
 
 // --------------------------------------------------- both gradients
@@ -553,7 +553,8 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
                                                    const typename D::T *__restrict__ XT,
                                                    const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
                                                    int64_t B, int nch, float *__restrict__ partial,
-                                                   typename D::T *__restrict__ dX, float *__restrict__ dW, Epi ep)
+                                                   typename D::T *__restrict__ dX, float *__restrict__ dW, Epi ep,
+                                                   int acc)
 {
     const int64_t ncb = (ncol_tasks + 3) / 4, nrb = (nrow_tasks + 3) / 4;
     const int64_t m = ncb < nrb ? ncb : nrb;
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
             segment_task<LD, D, kWide, E, kStore>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, nch, partial, dX,
                                                   ep);
     } else if (t < nrow_tasks) {
-        values_task<LD, D, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW);
+        values_task<LD, D, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW, acc != 0);
     }
 }
 
@@ -665,7 +666,7 @@ __global__ __launch_bounds__(kLdsThreads) void k_gradients_lds(const int4 *__res
                                                                const typename D::T *__restrict__ dY, int64_t in,
                                                                int64_t out, int64_t B, float *__restrict__ partial,
                                                                typename D::T *__restrict__ dX, float *__restrict__ dW,
-                                                               Epi ep)
+                                                               Epi ep, int acc)
 {
     extern __shared__ __align__(16) unsigned char lds_table[];
     auto *tab = reinterpret_cast<typename D::T *>(lds_table);
@@ -689,47 +690,10 @@ __global__ __launch_bounds__(kLdsThreads) void k_gradients_lds(const int4 *__res
     __syncthreads();
     if (!has) return;
     if (col) segment_task_body<LD, D, false, E, kStore>(T, rows_by_col, vals_c, tab, out, in, B, 1, partial, dX, ep);
-    else values_task_body<LD, D, false, kLdsWaves, true>(T, cols, tab, dY, in, out, B, 1, dW);
+    else values_task_body<LD, D, false, kLdsWaves, true>(T, cols, tab, dY, in, out, B, 1, dW, acc != 0);
 }
 
 // ------------------------------------------------------------ host side
-size_t batch_minor_bytes(const csp_layer *L, int64_t B, int64_t n)
-{
-    const int ld = pow2_ld(B);
-    return (size_t)ceil_div(B, ld) * (size_t)n * (size_t)ld * (size_t)L->esz;
-}
-
-csp_status ensure_act(csp_layer *L, int64_t B)
-{
-    const int ld = pow2_ld(B);
-    const int64_t nch = ceil_div(B, ld);
-    const size_t bytes = batch_minor_bytes(L, B, L->in > L->out ? L->in : L->out);
-    const int64_t tcap = L->row_tasks.cap > L->col_tasks.cap ? L->row_tasks.cap : L->col_tasks.cap;
-    const size_t pbytes = (size_t)tcap * (size_t)nch * (size_t)ld * sizeof(float);
-    if (L->act.bytes < bytes) {
-        if (L->act.a) CSP_HIP(hipFree(L->act.a));
-        if (L->act.b) CSP_HIP(hipFree(L->act.b));
-        L->act.a = L->act.b = nullptr;
-        L->act.bytes = 0;
-        if (hipMalloc(&L->act.a, bytes) != hipSuccess || hipMalloc(&L->act.b, bytes) != hipSuccess) {
-            (void)hipGetLastError();
-            return set_error(CSP_ERR_NO_MEMORY, "cannot allocate %zu bytes of operand workspace", bytes);
-        }
-        L->act.bytes = bytes;
-    }
-    if (L->act.partial_bytes < pbytes) {
-        if (L->act.partial) CSP_HIP(hipFree(L->act.partial));
-        L->act.partial = nullptr;
-        L->act.partial_bytes = 0;
-        if (hipMalloc(&L->act.partial, pbytes) != hipSuccess) {
-            (void)hipGetLastError();
-            return set_error(CSP_ERR_NO_MEMORY, "cannot allocate %zu bytes of partial sums", pbytes);
-        }
-        L->act.partial_bytes = pbytes;
-    }
-    return CSP_OK;
-}
-
 // Batch-minor copies of up to two operands (B == 1 needs none: [1, n] already is).
 csp_status batch_minor(csp_layer *L, int64_t B, const void *X1, int64_t n1, void *O1, const void *X2, int64_t n2,
                        void *O2, hipStream_t s)
@@ -858,7 +822,7 @@ csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t 
 // row-major X and dY through LDS tables.
 template <class D, int E>
 csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, int64_t B, void *dX, float *dW,
-                                  bool with_dx, const Epi &ep, hipStream_t s)
+                                  bool with_dx, bool acc, const Epi &ep, hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
@@ -875,7 +839,7 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
     const bool ks = CT.nsplit == 0 || !with_dx;
 #define CSP_GRADL_ARGS                                                                                   \
     CT.desc, ncol, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)X, (const T *)dY, \
-        L->in, L->out, B, L->act.partial, (T *)dX, dW, ep
+        L->in, L->out, B, L->act.partial, (T *)dX, dW, ep, (int)acc
 #define CSP_GRADL(LDV)                                                                                       \
     if (ks) {                                                                                                \
         if ((st = allow_lds<k_gradients_lds<LDV, D, E, 1>>(lds)) == CSP_OK)                                 \
@@ -974,7 +938,8 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
 }
 
 template <class D>
-csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, float *dW, hipStream_t s)
+csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, float *dW, bool acc,
+                               hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
@@ -984,7 +949,7 @@ csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, in
     timing_mark(L, true, s);
 #define CSP_DW(LDV, W)                                                                                            \
     k_values_rows<LDV, D, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, (const T *)XT, (const T *)dYT, L->in, \
-                                                  L->out, nch, dW)
+                                                  L->out, nch, dW, (int)acc)
     CSP_LD_SWITCH(ld, wide_operand(L->in > L->out ? L->in : L->out, ld), CSP_DW);
 #undef CSP_DW
     CSP_LAUNCHED("k_values_rows");
@@ -993,8 +958,8 @@ csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, in
 }
 
 template <class D, int E>
-csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, void *dX, float *dW, const Epi &ep,
-                        hipStream_t s)
+csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, void *dX, float *dW, bool acc,
+                        const Epi &ep, hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
@@ -1024,7 +989,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         if (gw > 0) {
 #define CSP_DW2(LDV, W)                                                                                           \
     k_values_rows<LDV, D, W><<<gw, 256, 0, s>>>(RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
-                                                nch, dW)
+                                                nch, dW, (int)acc)
             CSP_LD_SWITCH(ld, wide, CSP_DW2);
 #undef CSP_DW2
             CSP_LAUNCHED("k_values_rows");
@@ -1037,7 +1002,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
     const bool ks = CT.nsplit == 0;
 #define CSP_BOTH_ARGS                                                                                            \
     CT.desc, CT.count, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)XT, (const T *)dYT, \
-        L->in, L->out, B, nch, L->act.partial, (T *)dX, dW, ep
+        L->in, L->out, B, nch, L->act.partial, (T *)dX, dW, ep, (int)acc
 #define CSP_BOTH(LDV, W)                                                        \
     if (ks) k_gradients<LDV, D, W, E, 1><<<grid, 256, 0, s>>>(CSP_BOTH_ARGS);  \
     else k_gradients<LDV, D, W, E, 0><<<grid, 256, 0, s>>>(CSP_BOTH_ARGS)
@@ -1060,12 +1025,9 @@ Epi make_epi(const FwdEpilogue *fe)
     return ep;
 }
 
-}  // namespace
-
-csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s)
+csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s)
 {
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
+    csp_status st = CSP_OK;
     const Epi ep = make_epi(fe);
     if (lds_table_fits(L, B, L->in)) {
         const TaskList &RT = L->row_tasks;
@@ -1083,10 +1045,9 @@ csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const Fwd
     return fe ? fwd_dispatch<F32, kEpiForward>(L, xt, B, Y, ep, s) : fwd_dispatch<F32, kEpiNone>(L, xt, B, Y, ep, s);
 }
 
-csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s)
+csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s)
 {
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
+    csp_status st = CSP_OK;
     Epi ep;
     ep.act_in = act_in;
     if (lds_table_fits(L, B, L->out)) {
@@ -1109,47 +1070,112 @@ csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, c
                   : bwd_input_dispatch<F32, kEpiNone>(L, dyt, B, dX, ep, s);
 }
 
-csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s)
+csp_status bwd_values_slice(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, bool acc, hipStream_t s)
 {
-    if (L->nnz == 0) return CSP_OK;
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
+    csp_status st = CSP_OK;
     if (lds_table_fits(L, B, L->in)) {
         const Epi ep;
-        return L->dtype == CSP_BF16 ? gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, nullptr, dW, false, ep, s)
-                                    : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, nullptr, dW, false, ep, s);
+        return L->dtype == CSP_BF16 ? gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, nullptr, dW, false, acc, ep, s)
+                                    : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, nullptr, dW, false, acc, ep, s);
     }
     st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
     if (st != CSP_OK) return st;
     const void *xt = B == 1 ? X : L->act.a;
     const void *dyt = B == 1 ? dY : L->act.b;
-    return L->dtype == CSP_BF16 ? bwd_values_dispatch<BF16>(L, xt, dyt, B, dW, s)
-                                : bwd_values_dispatch<F32>(L, xt, dyt, B, dW, s);
+    return L->dtype == CSP_BF16 ? bwd_values_dispatch<BF16>(L, xt, dyt, B, dW, acc, s)
+                                : bwd_values_dispatch<F32>(L, xt, dyt, B, dW, acc, s);
 }
 
-csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
-                      hipStream_t s)
+csp_status bwd_slice(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
+                     bool acc, hipStream_t s)
 {
-    csp_status st = ensure_act(L, B);
-    if (st != CSP_OK) return st;
+    csp_status st = CSP_OK;
     Epi ep;
     ep.act_in = act_in;
     if (lds_table_fits(L, B, L->in > L->out ? L->in : L->out)) {
         if (L->dtype == CSP_BF16)
-            return act_in ? gradients_lds_dispatch<BF16, kEpiActGrad>(L, X, dY, B, dX, dW, true, ep, s)
-                          : gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, dX, dW, true, ep, s);
-        return act_in ? gradients_lds_dispatch<F32, kEpiActGrad>(L, X, dY, B, dX, dW, true, ep, s)
-                      : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, dX, dW, true, ep, s);
+            return act_in ? gradients_lds_dispatch<BF16, kEpiActGrad>(L, X, dY, B, dX, dW, true, acc, ep, s)
+                          : gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, dX, dW, true, acc, ep, s);
+        return act_in ? gradients_lds_dispatch<F32, kEpiActGrad>(L, X, dY, B, dX, dW, true, acc, ep, s)
+                      : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, dX, dW, true, acc, ep, s);
     }
     st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
     if (st != CSP_OK) return st;
     const void *xt = B == 1 ? X : L->act.a;
     const void *dyt = B == 1 ? dY : L->act.b;
     if (L->dtype == CSP_BF16)
-        return act_in ? bwd_dispatch<BF16, kEpiActGrad>(L, xt, dyt, B, dX, dW, ep, s)
-                      : bwd_dispatch<BF16, kEpiNone>(L, xt, dyt, B, dX, dW, ep, s);
-    return act_in ? bwd_dispatch<F32, kEpiActGrad>(L, xt, dyt, B, dX, dW, ep, s)
-                  : bwd_dispatch<F32, kEpiNone>(L, xt, dyt, B, dX, dW, ep, s);
+        return act_in ? bwd_dispatch<BF16, kEpiActGrad>(L, xt, dyt, B, dX, dW, acc, ep, s)
+                      : bwd_dispatch<BF16, kEpiNone>(L, xt, dyt, B, dX, dW, acc, ep, s);
+    return act_in ? bwd_dispatch<F32, kEpiActGrad>(L, xt, dyt, B, dX, dW, acc, ep, s)
+                  : bwd_dispatch<F32, kEpiNone>(L, xt, dyt, B, dX, dW, acc, ep, s);
+}
+
+}  // namespace
+
+// Batches above kSliceB run as consecutive slices of kSliceB rows of the
+// row-major operands (one batch-minor chunk each), so the operand workspace
+// sized at create serves every batch and no call allocates.  The value
+// gradient of a later slice is added to the earlier ones in slice order.
+constexpr int64_t kSliceB = kSliceRows;
+
+namespace {
+inline const void *rows_at(const void *p, int64_t r, int64_t n, int esz)
+{
+    return p ? (const char *)p + r * n * esz : nullptr;
+}
+inline void *rows_at(void *p, int64_t r, int64_t n, int esz) { return p ? (char *)p + r * n * esz : nullptr; }
+}  // namespace
+
+csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s)
+{
+    for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
+        const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
+        FwdEpilogue f{};
+        if (fe) {
+            f = *fe;
+            f.pre = rows_at(f.pre, b0, L->out, L->esz);
+        }
+        const csp_status st = fwd_slice(L, rows_at(X, b0, L->in, L->esz), bs, rows_at(Y, b0, L->out, L->esz),
+                                        fe ? &f : nullptr, s);
+        if (st != CSP_OK) return st;
+    }
+    return CSP_OK;
+}
+
+csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s)
+{
+    for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
+        const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
+        const csp_status st = bwd_input_slice(L, rows_at(dY, b0, L->out, L->esz), bs, rows_at(dX, b0, L->in, L->esz),
+                                              rows_at(act_in, b0, L->in, L->esz), s);
+        if (st != CSP_OK) return st;
+    }
+    return CSP_OK;
+}
+
+csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s)
+{
+    if (L->nnz == 0) return CSP_OK;
+    for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
+        const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
+        const csp_status st = bwd_values_slice(L, rows_at(dY, b0, L->out, L->esz), rows_at(X, b0, L->in, L->esz), bs, dW,
+                                               b0 > 0, s);
+        if (st != CSP_OK) return st;
+    }
+    return CSP_OK;
+}
+
+csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
+                      hipStream_t s)
+{
+    for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
+        const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
+        const csp_status st = bwd_slice(L, rows_at(dY, b0, L->out, L->esz), rows_at(X, b0, L->in, L->esz), bs,
+                                        rows_at(dX, b0, L->in, L->esz), dW, rows_at(act_in, b0, L->in, L->esz),
+                                        b0 > 0, s);
+        if (st != CSP_OK) return st;
+    }
+    return CSP_OK;
 }
 
 }  // namespace csp

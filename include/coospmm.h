@@ -69,7 +69,11 @@ typedef enum {
  * nnz = 0 is valid.  Synchronizes on "stream" once, to read the validation
  * result; returns CSP_ERR_INDEX_RANGE or CSP_ERR_DUPLICATE without creating a
  * layer when the triples are invalid.  On success *out_layer owns device
- * memory until sparse_layer_destroy.
+ * memory until sparse_layer_destroy: the COO arrays and their index, the
+ * restructure state, and the product workspace -- two batch-minor operand
+ * copies of max(out, in) * 64 elements and 64 fp32 partial sums per task --
+ * so that no product call allocates (batches above 64 rows run as
+ * consecutive slices of 64 rows).
  */
 csp_status sparse_layer_create(int64_t out_features, int64_t in_features, int64_t nnz, const int32_t *rows,
                                const int32_t *cols, const void *vals, csp_dtype dtype, void *stream,
@@ -84,6 +88,9 @@ void sparse_layer_destroy(sparse_layer_t layer);
  *     Y[b, r] = sum over stored k with row_k = r of v_k * X[b, col_k]
  * i.e. Y = X W^T.  X [B, in] and Y [B, out] have the layer's dtype.  A row
  * with no stored entry gives exactly 0.  fp32 accumulation in any order.
+ * This and the other product calls (spmm_bwd_input, spmm_bwd_values,
+ * spmm_bwd and their _act forms) are asynchronous on "stream", allocate
+ * nothing, set no memory with memset, and may be captured in a HIP graph.
  */
 csp_status spmm_fwd(sparse_layer_t layer, const void *X, int64_t B, void *Y, void *stream);
 

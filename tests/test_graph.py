@@ -47,3 +47,44 @@ def test_graph_replay_matches_eager(B):
     finally:
         torch.cuda.synchronize()
         csp.sparse_layer_destroy(h)
+
+
+@pytest.mark.parametrize("B", [16, 130])
+def test_first_calls_captured(orc, B):
+    """A fresh layer's very first product calls are captured: nothing in them allocates (the workspace is
+    sized at create; B = 130 runs as three slices of at most 64 rows).  Replays match the oracle, and a
+    layer used eagerly afterwards gives the same bits."""
+    import numpy as np
+
+    from tests.gpu_util import FP32_REL, assert_within, host
+    L = W.random_layer(900, 700, 40000, seed=77 + B)
+    h = csp.sparse_layer_create(L.out, L.in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        Xh, dYh = W.random_dense((B, L.in_), 3), W.random_dense((B, L.out), 4)
+        X, dY = dev(Xh), dev(dYh)
+        Y = torch.empty((B, L.out), device="cuda")
+        dX = torch.empty((B, L.in_), device="cuda")
+        dW = torch.empty((L.nnz,), device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = torch.cuda.current_stream()
+            csp.spmm_fwd(h, X, Y, stream=s)
+            csp.spmm_bwd(h, dY, X, dX, dW, stream=s)
+        for rep in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            c = orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals)
+            ref, S = orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, Xh)
+            assert_within(host(Y), ref, S, FP32_REL, f"captured forward, replay {rep}")
+            refx, Sx = orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dYh)
+            assert_within(host(dX), refx, Sx, FP32_REL, f"captured dX, replay {rep}")
+            refw, Sw = orc.spmm_bwd_values(L.out, L.in_, c["rows"], c["cols"], dYh, Xh)
+            assert_within(host(dW), refw, Sw, FP32_REL, f"captured dW, replay {rep}")
+        Ye = host(csp.spmm_fwd(h, X))
+        dXe, dWe = (host(t) for t in csp.spmm_bwd(h, dY, X))
+        assert np.array_equal(Ye, host(Y)) and np.array_equal(dXe, host(dX)) and np.array_equal(dWe, host(dW))
+        del g
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h)
