@@ -15,9 +15,10 @@ its data from HBM rather than from cache.
 Printed: one JSON line.  `value` is the effective bandwidth of the step:
 algorithmic bytes of forward + input gradient + value gradient (byte models
 below) over the measured step time.  `roofline` covers the dominant kernel,
-timed with HIP events that the library records immediately around it, in a
-second pass with the same work.  `cpu_baseline` times the CPU oracle (plain C
-loops, fp64 accumulation, one core) on the same workload.
+timed with a pair of HIP events that the library attaches to that kernel's
+dispatch (so they carry its own start and end), in a second pass with the
+same work.  `cpu_baseline` times the CPU oracle (plain C loops, fp64
+accumulation, one core) on the same workload.
 """
 from __future__ import annotations
 
@@ -518,7 +519,8 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # second pass, same work, eager: HIP events recorded by the library around each main kernel
+    # second pass, same work, eager: the library attaches a pair of HIP events to each call's main
+    # kernel dispatch (sparse_layer_time_next), so each pair carries that kernel's own start and end
     K = args.steps
     labels = [c[0] for c in calls(reps[0], stream)]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in labels]
@@ -538,17 +540,6 @@ def main():
             fn()
         after(reps[i % R])
     torch.cuda.synchronize()
-    # The cost of a bracket itself: the same event pairs with nothing between them, queued the
-    # same way (reported beside the kernel times, which include the event records around them).
-    empty = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    torch.cuda.synchronize()
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(2.0e9 * 0.01))
-    for a, b in empty:
-        a.record(stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    bracket_us = sum(a.elapsed_time(b) for a, b in empty) / K * 1e3
     per_call = {}
     for ci, (label, _, _, kname, kbytes) in enumerate(calls(reps[0], stream)):
         us = sum(ev[i][ci][0].elapsed_time(ev[i][ci][1]) for i in range(K)) / K * 1e3
@@ -637,7 +628,6 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": dom["kernel"], "call": dom_label, "avg_launch_us": round(dom["us"], 3),
-                     "empty_event_bracket_us": round(bracket_us, 3),
                      "bytes_per_launch": dom["bytes"]},
         "kernels_us": {k: round(v["us"], 3) for k, v in per_call.items()},
         "restructure_ms": None if restructure_ms is None else round(restructure_ms, 3),

@@ -106,15 +106,6 @@ struct csp_layer {
 
 namespace csp {
 
-// Records the layer's pending timing events around one main-kernel launch
-// (before = true: just before it, then false: just after it, clearing the request).
-inline void timing_mark(csp_layer *L, bool before, hipStream_t s)
-{
-    hipEvent_t &e = before ? L->time_before : L->time_after;
-    if (e) (void)hipEventRecord(e, s);
-    if (!before) L->time_before = L->time_after = nullptr;
-}
-
 // Error reporting (layer.hip).
 csp_status set_error(csp_status st, const char *fmt, ...);
 csp_status hip_error(hipError_t e, const char *what);

@@ -25,6 +25,8 @@
 // operand gathers.
 #include <cstdlib>
 
+#include <hip/hip_ext.h>
+
 #include "common.h"
 #include "device_util.h"
 
@@ -721,6 +723,27 @@ csp_status batch_minor(csp_layer *L, int64_t B, const void *X1, int64_t n1, void
     return CSP_OK;
 }
 
+// Launch of a product call's main kernel.  When the caller has asked for the
+// next main kernel to be timed (sparse_layer_time_next), the launch goes
+// through hipExtLaunchKernel with the request's events attached to the
+// dispatch itself, so they carry the kernel's own start and end times; mark
+// says which of the two this launch carries (a pass of two kernels puts the
+// start on the first and the end on the second).
+enum : int { kTimeStart = 1, kTimeStop = 2, kTimeBoth = 3 };
+
+template <typename... KArgs, typename... Args>
+inline void launch_main(csp_layer *L, int mark, void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem,
+                        hipStream_t s, Args... args)
+{
+    hipEvent_t a = (mark & kTimeStart) ? L->time_before : nullptr;
+    hipEvent_t b = (mark & kTimeStop) ? L->time_after : nullptr;
+    if (a || b)
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, a, b, 0u, static_cast<KArgs>(args)...);
+    else
+        kernel<<<grid, block, shmem, s>>>(static_cast<KArgs>(args)...);
+    if (mark & kTimeStop) L->time_before = L->time_after = nullptr;
+}
+
 #define CSP_LD_SWITCH_W(ld, MACRO, W) \
     switch (ld) {                     \
     case 1: MACRO(1, W); break;       \
@@ -799,22 +822,20 @@ csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t 
     const unsigned grid = (unsigned)ceil_div(TL.count, kLdsWaves);
     const size_t lds = (size_t)n_op * ld * L->esz;
     csp_status st = CSP_OK;
-    timing_mark(L, true, s);
     const bool ks = TL.nsplit == 0;  // no split segments: every task stores its output
 #define CSP_SEGL_ARGS TL.desc, TL.count, idx, (const T *)vals, (const T *)op, n_op, n_seg, B, L->act.partial, (T *)out, ep
 #define CSP_SEGL(LDV)                                                                                        \
     if (ks) {                                                                                                \
         if ((st = allow_lds<k_segment_lds<LDV, D, E, 1>>(lds)) == CSP_OK)                                   \
-            k_segment_lds<LDV, D, E, 1><<<grid, kLdsThreads, lds, s>>>(CSP_SEGL_ARGS);                      \
+            launch_main(L, kTimeBoth, k_segment_lds<LDV, D, E, 1>, grid, kLdsThreads, lds, s, CSP_SEGL_ARGS);                      \
     } else if ((st = allow_lds<k_segment_lds<LDV, D, E, 0>>(lds)) == CSP_OK) {                               \
-        k_segment_lds<LDV, D, E, 0><<<grid, kLdsThreads, lds, s>>>(CSP_SEGL_ARGS);                          \
+        launch_main(L, kTimeBoth, k_segment_lds<LDV, D, E, 0>, grid, kLdsThreads, lds, s, CSP_SEGL_ARGS);                          \
     }
     CSP_LD_SWITCH_LDS(ld, CSP_SEGL);
 #undef CSP_SEGL
 #undef CSP_SEGL_ARGS
     if (st != CSP_OK) return st;
     CSP_LAUNCHED("k_segment_lds");
-    timing_mark(L, false, s);
     return split_fixup<D, E>(L, TL, B, n_seg, out, ep, s);
 }
 
@@ -835,7 +856,6 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
     const int64_t n_tab = with_dx && L->out > L->in ? L->out : L->in;
     const size_t lds = (size_t)n_tab * ld * L->esz;
     csp_status st = CSP_OK;
-    timing_mark(L, true, s);
     const bool ks = CT.nsplit == 0 || !with_dx;
 #define CSP_GRADL_ARGS                                                                                   \
     CT.desc, ncol, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)X, (const T *)dY, \
@@ -843,16 +863,15 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
 #define CSP_GRADL(LDV)                                                                                       \
     if (ks) {                                                                                                \
         if ((st = allow_lds<k_gradients_lds<LDV, D, E, 1>>(lds)) == CSP_OK)                                 \
-            k_gradients_lds<LDV, D, E, 1><<<grid, kLdsThreads, lds, s>>>(CSP_GRADL_ARGS);                   \
+            launch_main(L, kTimeBoth, k_gradients_lds<LDV, D, E, 1>, grid, kLdsThreads, lds, s, CSP_GRADL_ARGS);                   \
     } else if ((st = allow_lds<k_gradients_lds<LDV, D, E, 0>>(lds)) == CSP_OK) {                             \
-        k_gradients_lds<LDV, D, E, 0><<<grid, kLdsThreads, lds, s>>>(CSP_GRADL_ARGS);                       \
+        launch_main(L, kTimeBoth, k_gradients_lds<LDV, D, E, 0>, grid, kLdsThreads, lds, s, CSP_GRADL_ARGS);                       \
     }
     CSP_LD_SWITCH_LDS(ld, CSP_GRADL);
 #undef CSP_GRADL
 #undef CSP_GRADL_ARGS
     if (st != CSP_OK) return st;
     CSP_LAUNCHED("k_gradients_lds");
-    timing_mark(L, false, s);
     return with_dx ? split_fixup<D, E>(L, CT, B, L->in, dX, ep, s) : CSP_OK;
 }
 
@@ -875,14 +894,12 @@ csp_status grouped_dispatch(csp_layer *L, const TaskList &TL, const int32_t *idx
     using T = typename D::T;
     const int ld = pow2_ld(B);
     const unsigned grid = (unsigned)(TL.nsplit + ceil_div(TL.count, kGroupWaves));
-    timing_mark(L, true, s);
 #define CSP_GRP(LDV)                                                                                            \
-    k_segment_grouped<LDV, D, false, E><<<grid, kGroupWaves * kWave, 0, s>>>(                                   \
+    launch_main(L, kTimeBoth, k_segment_grouped<LDV, D, false, E>, grid, kGroupWaves * kWave, 0, s,                                    \
         TL.desc, TL.count, TL.split, TL.nsplit, idx, (const T *)vals, (const T *)opT, n_op, n_seg, B, (T *)out, ep)
     CSP_LD_SWITCH_LDS(ld, CSP_GRP);
 #undef CSP_GRP
     CSP_LAUNCHED("k_segment_grouped");
-    timing_mark(L, false, s);
     return CSP_OK;
 }
 
@@ -896,18 +913,16 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
     if (grouped_splits(TL, B, L->in, L->in))
         return grouped_dispatch<D, E>(L, TL, L->cols, L->vals, XT, L->in, L->out, B, Y, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
-    timing_mark(L, true, s);
     const bool ks = TL.nsplit == 0;
 #define CSP_FWD_ARGS \
     TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, nch, L->act.partial, (T *)Y, ep
 #define CSP_FWD(LDV, W)                                                             \
-    if (ks) k_segment_spmm<LDV, D, W, E, 1><<<grid, 256, 0, s>>>(CSP_FWD_ARGS);    \
-    else k_segment_spmm<LDV, D, W, E, 0><<<grid, 256, 0, s>>>(CSP_FWD_ARGS)
+    if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_FWD_ARGS);    \
+    else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_FWD_ARGS)
     CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_FWD);
 #undef CSP_FWD
 #undef CSP_FWD_ARGS
     CSP_LAUNCHED("k_segment_spmm (forward)");
-    timing_mark(L, false, s);
     return split_fixup<D, E>(L, TL, B, L->out, Y, ep, s);
 }
 
@@ -921,19 +936,17 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
     if (grouped_splits(TL, B, L->out, L->out))
         return grouped_dispatch<D, E>(L, TL, L->rows_by_col, L->vals_c, dYT, L->out, L->in, B, dX, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
-    timing_mark(L, true, s);
     const bool ks = TL.nsplit == 0;
 #define CSP_DX_ARGS                                                                                                 \
     TL.desc, TL.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, nch, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX(LDV, W)                                                            \
-    if (ks) k_segment_spmm<LDV, D, W, E, 1><<<grid, 256, 0, s>>>(CSP_DX_ARGS);   \
-    else k_segment_spmm<LDV, D, W, E, 0><<<grid, 256, 0, s>>>(CSP_DX_ARGS)
+    if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_DX_ARGS);   \
+    else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_DX_ARGS)
     CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_DX);
 #undef CSP_DX
 #undef CSP_DX_ARGS
     CSP_LAUNCHED("k_segment_spmm (input gradient)");
-    timing_mark(L, false, s);
     return split_fixup<D, E>(L, TL, B, L->in, dX, ep, s);
 }
 
@@ -946,14 +959,12 @@ csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, in
     const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->row_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
-    timing_mark(L, true, s);
 #define CSP_DW(LDV, W)                                                                                            \
-    k_values_rows<LDV, D, W><<<grid, 256, 0, s>>>(TL.desc, TL.count, L->cols, (const T *)XT, (const T *)dYT, L->in, \
+    launch_main(L, kTimeBoth, k_values_rows<LDV, D, W>, grid, 256, 0, s, TL.desc, TL.count, L->cols, (const T *)XT, (const T *)dYT, L->in, \
                                                   L->out, nch, dW, (int)acc)
     CSP_LD_SWITCH(ld, wide_operand(L->in > L->out ? L->in : L->out, ld), CSP_DW);
 #undef CSP_DW
     CSP_LAUNCHED("k_values_rows");
-    timing_mark(L, false, s);
     return CSP_OK;
 }
 
@@ -974,43 +985,40 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
     const int64_t table_bytes = (int64_t)L->esz * ld * (L->in + L->out);
     if (table_bytes > (int64_t(2) << 20)) {
         const unsigned gx = (unsigned)ceil_div(CT.count, 4), gw = (unsigned)ceil_div(nrow, 4);
-        timing_mark(L, true, s);
+        const int m1 = gw > 0 ? kTimeStart : kTimeBoth;  // the value-gradient kernel carries the end
         const bool ks = CT.nsplit == 0;
 #define CSP_DX2_ARGS                                                                                                \
     CT.desc, CT.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, nch, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX2(LDV, W)                                                         \
-    if (ks) k_segment_spmm<LDV, D, W, E, 1><<<gx, 256, 0, s>>>(CSP_DX2_ARGS);  \
-    else k_segment_spmm<LDV, D, W, E, 0><<<gx, 256, 0, s>>>(CSP_DX2_ARGS)
+    if (ks) launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 1>, gx, 256, 0, s, CSP_DX2_ARGS);  \
+    else launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 0>, gx, 256, 0, s, CSP_DX2_ARGS)
         CSP_LD_SWITCH(ld, wide, CSP_DX2);
 #undef CSP_DX2
 #undef CSP_DX2_ARGS
         CSP_LAUNCHED("k_segment_spmm (input gradient)");
         if (gw > 0) {
 #define CSP_DW2(LDV, W)                                                                                           \
-    k_values_rows<LDV, D, W><<<gw, 256, 0, s>>>(RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
+    launch_main(L, kTimeStop, k_values_rows<LDV, D, W>, gw, 256, 0, s, RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
                                                 nch, dW, (int)acc)
             CSP_LD_SWITCH(ld, wide, CSP_DW2);
 #undef CSP_DW2
             CSP_LAUNCHED("k_values_rows");
         }
-        timing_mark(L, false, s);
         return split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
     }
     const unsigned grid = (unsigned)(ceil_div(CT.count, 4) + ceil_div(nrow, 4));
-    timing_mark(L, true, s);
     const bool ks = CT.nsplit == 0;
 #define CSP_BOTH_ARGS                                                                                            \
     CT.desc, CT.count, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)XT, (const T *)dYT, \
         L->in, L->out, B, nch, L->act.partial, (T *)dX, dW, ep, (int)acc
 #define CSP_BOTH(LDV, W)                                                        \
-    if (ks) k_gradients<LDV, D, W, E, 1><<<grid, 256, 0, s>>>(CSP_BOTH_ARGS);  \
-    else k_gradients<LDV, D, W, E, 0><<<grid, 256, 0, s>>>(CSP_BOTH_ARGS)
+    if (ks) launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_BOTH_ARGS);  \
+    else launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_BOTH_ARGS)
     CSP_LD_SWITCH(ld, wide, CSP_BOTH);
 #undef CSP_BOTH
 #undef CSP_BOTH_ARGS
     CSP_LAUNCHED("k_gradients");
-    timing_mark(L, false, s);
     return split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
 }
 

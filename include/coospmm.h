@@ -247,11 +247,14 @@ csp_status sparse_layer_set_values(sparse_layer_t layer, const void *vals, void 
 
 /*
  * sparse_layer_time_next -- profiling aid: the next product call on this
- * layer (spmm_fwd, spmm_bwd_input, spmm_bwd_values or spmm_bwd) records
- * ev_before on its stream immediately before launching its main kernel and
- * ev_after immediately after, then forgets the request.  The events are
+ * layer (spmm_fwd, spmm_bwd_input, spmm_bwd_values, spmm_bwd or their _act
+ * forms) attaches ev_before and ev_after to the dispatch of its main kernel
+ * (hipExtLaunchKernel), so hipEventElapsedTime(ev_before, ev_after) is that
+ * kernel's own duration; then the request is forgotten.  When the pass has
+ * two main kernels (input gradient and value gradient as separate launches
+ * for large operand tables) the pair spans both.  The events are
  * caller-owned hipEvent_t handles passed as void*.  Operand copies and other
- * helper kernels of the call fall outside the bracket.
+ * helper kernels of the call fall outside.  Not for use under graph capture.
  */
 csp_status sparse_layer_time_next(sparse_layer_t layer, void *ev_before, void *ev_after);
 
