@@ -413,7 +413,7 @@ def main():
         if lds_fits(L.in_):
             return f"k_segment_lds<{ld}, {dt_name}, {epi}, {ks}>"
         # split rows finish inside the pass when no row can exceed 64 tasks
-        if grouped_on and B <= 64 and not ks and L.in_ <= 64 * 512:
+        if grouped_on and B <= 8 and not ks and L.in_ <= 64 * 512:
             return f"k_segment_grouped<{ld}, {dt_name}, false, {epi}>"
         return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}, {ks}>"
 

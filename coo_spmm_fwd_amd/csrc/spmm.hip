@@ -876,12 +876,15 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
 }
 
 // Split segments finished inside the segment pass (k_segment_grouped) when
-// there are any, one batch chunk covers B, and no segment can have more than
-// kGroupMaxTasks tasks (its length is at most max_len, the other dimension).
+// there are any, B <= 8, and no segment can have more than kGroupMaxTasks
+// tasks (its length is at most max_len, the other dimension).  Up to B = 8
+// the kernel keeps 8 waves per SIMD, two 16-wave workgroups per CU; at larger
+// widths its registers leave one workgroup per CU and the split-plus-fixup
+// path was faster (B = 64: 56 against 43 us for the pass).
 // COOSPMM_GROUPED_SPLITS=0 keeps the split-plus-fixup path.
 inline bool grouped_splits(const TaskList &TL, int64_t B, int64_t max_len, int64_t n_op)
 {
-    if (TL.nsplit == 0 || B > 64 || ceil_div(max_len, kTaskChunk) > kGroupMaxTasks) return false;
+    if (TL.nsplit == 0 || B > 8 || ceil_div(max_len, kTaskChunk) > kGroupMaxTasks) return false;
     if (wide_operand(n_op, pow2_ld(B))) return false;
     const char *e = std::getenv("COOSPMM_GROUPED_SPLITS");
     return !(e && e[0] == '0');

@@ -1,7 +1,7 @@
 """Split segments finished inside the segment pass (k_segment_grouped).
 
 A row (forward) or column (input gradient) longer than 512 entries is cut
-into tasks.  When the gathered operand takes the global-table path, B <= 64,
+into tasks.  When the gathered operand takes the global-table path, B <= 8,
 and no segment can have more than 64 tasks (the other dimension is at most
 32768), one 16-wave workgroup runs all tasks of a split segment and adds
 their sums in LDS, in task order, instead of the separate fixup launch doing
@@ -10,7 +10,8 @@ those of COOSPMM_GROUPED_SPLITS=0 (split-plus-fixup path), and within the
 oracle's bounds.
 
 Cases: power-law rows and columns (many split segments of different task
-counts next to unsplit ones and empty ones), B = 1, 3 (pad slots), 16 and 64,
+counts next to unsplit ones and empty ones), B = 1, 3 (pad slots), 8, and 16
+and 64 (above the limit: both settings take the split-plus-fixup path),
 fp32 and bf16, the epilogues (bias + GELU forward, input gradient times
 GELU'), a row of 32768 entries (exactly 64 tasks) and a layer with 32769
 columns (more than 64 tasks possible: the fixup path stays).
@@ -66,6 +67,7 @@ CASES = [
     # (name, builder, B, dtype)
     ("zipf_rows_b1_bf16", lambda d: zipf_layer(4096, 16384, 300000, 11, d), 1, "bf16"),
     ("zipf_rows_b3", lambda d: zipf_layer(4096, 16384, 300000, 12, d), 3, "f32"),
+    ("zipf_rows_b8", lambda d: zipf_layer(2048, 8192, 200000, 19, d), 8, "f32"),
     ("zipf_rows_b16", lambda d: zipf_layer(2048, 8192, 200000, 13, d), 16, "f32"),
     ("zipf_rows_b64", lambda d: zipf_layer(1024, 4096, 100000, 14, d), 64, "f32"),
     ("zipf_cols_b1", lambda d: zipf_layer(16384, 4096, 300000, 15, d, transpose=True), 1, "f32"),
