@@ -132,6 +132,12 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_scan(TaskBuild tb)
     }
 }
 
+// kPrefix: the tile sums are still raw (k_tasks_scan skipped); each block
+// adds up those of the tiles before it, and the last tile of a list stores
+// the list's task count as k_tasks_scan would.  Used up to kPrefixTaskTiles
+// tiles per list.
+constexpr int64_t kPrefixTaskTiles = 1024;
+template <bool kPrefix>
 __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
 {
     __shared__ uint32_t lds[17];
@@ -141,8 +147,19 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
     const int64_t i = tile * kTaskThreads + threadIdx.x;
     const bool live = i < tb.nseg[l];
     const uint32_t p = live ? seg_pieces(tb.ptr[l], i) : 0u;
-    uint32_t total;
-    const int32_t f = (int32_t)(block_exclusive_scan(p, lds, &total) + tb.partials[l][tile]);
+    uint32_t before, total;
+    if constexpr (kPrefix) {
+        uint32_t v = 0;
+        for (int64_t j = threadIdx.x; j < tile; j += kTaskThreads) v += tb.partials[l][j];
+        block_exclusive_scan(v, lds, &before);
+    } else {
+        before = tb.partials[l][tile];
+    }
+    const int32_t f = (int32_t)(block_exclusive_scan(p, lds, &total) + before);
+    if (kPrefix && tile == tb.tiles[l] - 1 && threadIdx.x == 0) {
+        tb.counts[l] = before + total;
+        tb.seg_first[l][tb.nseg[l]] = (int32_t)(before + total);
+    }
     if (!live) return;
     tb.seg_first[l][i] = f;
     const int32_t b = tb.ptr[l][i], e = tb.ptr[l][i + 1];
@@ -181,9 +198,13 @@ csp_status build_task_lists(csp_layer *L, hipStream_t s)
     const unsigned grid = (unsigned)(tb.tiles[0] + tb.tiles[1]);
     k_tasks_count<<<grid, kTaskThreads, 0, s>>>(tb);
     CSP_LAUNCHED("k_tasks_count");
-    k_tasks_scan<<<2, kTaskThreads, 0, s>>>(tb);
-    CSP_LAUNCHED("k_tasks_scan");
-    k_tasks_emit<<<grid, kTaskThreads, 0, s>>>(tb);
+    if (tb.tiles[0] <= kPrefixTaskTiles && tb.tiles[1] <= kPrefixTaskTiles) {
+        k_tasks_emit<true><<<grid, kTaskThreads, 0, s>>>(tb);
+    } else {
+        k_tasks_scan<<<2, kTaskThreads, 0, s>>>(tb);
+        CSP_LAUNCHED("k_tasks_scan");
+        k_tasks_emit<false><<<grid, kTaskThreads, 0, s>>>(tb);
+    }
     CSP_LAUNCHED("k_tasks_emit");
     return CSP_OK;
 }

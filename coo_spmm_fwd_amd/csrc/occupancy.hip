@@ -254,16 +254,37 @@ __global__ __launch_bounds__(1024) void k_bm_prune_scan(uint32_t *tiles, int64_t
 // Entry k goes if its key is below the threshold, or equal to it and fewer
 // than need_eq equal keys precede it; the pruned ones are marked in a bit
 // mask, one bit per canonical index.
-template <class K>
+// kPrefix: tiles holds the raw per-tile counts (k_bm_prune_scan skipped) and
+// each block adds up the equal counts of the tiles before it; block 0 then
+// also does the scan kernel's clean-up.  Used up to kPrefixTiles tiles.
+constexpr int64_t kPrefixTiles = 2048;
+template <class K, bool kPrefix>
 __global__ __launch_bounds__(kThreads) void k_bm_prune_mark(K keyof, int64_t n,
-                                                            const uint32_t *__restrict__ sel,
+                                                            uint32_t *__restrict__ sel,
                                                             const uint32_t *__restrict__ tiles,
                                                             uint64_t *__restrict__ pruned)
 {
     constexpr int R = kWaveItems / kWave;
     __shared__ uint32_t we[4];
+    __shared__ uint32_t wb[4];
     const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const uint32_t T = sel[kSelT], need_eq = sel[kSelNeedEq];
+    uint32_t eq_before = 0;
+    if constexpr (kPrefix) {
+        uint32_t v = 0;
+        for (int64_t j = t; j < (int64_t)blockIdx.x; j += kThreads) v += tiles[2 * j + 1];
+        v = wave_sum(v);
+        if (lane == 0) wb[w] = v;
+        __syncthreads();
+        eq_before = wb[0] + wb[1] + wb[2] + wb[3];
+        if (blockIdx.x == 0) {  // what k_bm_prune_scan does after its scan
+            if (t == 0) {
+                sel[kSelCounts + 4] = 0;
+                sel[kSelCounts + 5] = 0;
+            }
+            for (int i = t; i < kMaxPasses * kHistWords; i += kThreads) sel[i] = 0;
+        }
+    }
     const int64_t base = (int64_t)blockIdx.x * kTile + (int64_t)w * kWaveItems;
     uint32_t key[R];
     uint32_t eq_w = 0;
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_bm_prune_mark(K keyof, int64_t n,
     }
     if (lane == 0) we[w] = eq_w;
     __syncthreads();
-    uint32_t eq_run = tiles[2 * blockIdx.x + 1];
+    uint32_t eq_run = kPrefix ? eq_before : tiles[2 * blockIdx.x + 1];
     for (int i = 0; i < w; ++i) eq_run += we[i];
     const uint64_t below = lanes_below();
 #pragma unroll
@@ -829,9 +850,13 @@ struct BitmapRun {
         const int64_t nt = ceil_div(n, kTile);
         k_bm_prune_count<K><<<(unsigned)nt, kThreads, 0, s>>>(keyof, n, W.sel, W.hist);
         CSP_LAUNCHED("k_bm_prune_count");
-        k_bm_prune_scan<<<1, 1024, 0, s>>>(W.hist, nt, W.sel);
-        CSP_LAUNCHED("k_bm_prune_scan");
-        k_bm_prune_mark<K><<<(unsigned)nt, kThreads, 0, s>>>(keyof, n, W.sel, W.hist, mask);
+        if (nt <= kPrefixTiles) {
+            k_bm_prune_mark<K, true><<<(unsigned)nt, kThreads, 0, s>>>(keyof, n, W.sel, W.hist, mask);
+        } else {
+            k_bm_prune_scan<<<1, 1024, 0, s>>>(W.hist, nt, W.sel);
+            CSP_LAUNCHED("k_bm_prune_scan");
+            k_bm_prune_mark<K, false><<<(unsigned)nt, kThreads, 0, s>>>(keyof, n, W.sel, W.hist, mask);
+        }
         CSP_LAUNCHED("k_bm_prune_mark");
         return CSP_OK;
     }

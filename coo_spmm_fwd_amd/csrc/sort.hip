@@ -85,6 +85,39 @@ __global__ __launch_bounds__(kScanThreads) void k_scan_apply(const uint32_t *in,
     if (total_at && blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) out[n] = partials[gridDim.x];
 }
 
+// k_scan_partials and k_scan_apply in one launch for up to kFusedScanBlocks
+// blocks: each block first adds up the reduce sums of the blocks before it.
+// The last block writes the grand total to out[n] (total_at) and to *total.
+constexpr int64_t kFusedScanBlocks = 1024;
+template <bool kPopc>
+__global__ __launch_bounds__(kScanThreads) void k_scan_apply_prefix(const uint32_t *in, uint32_t *out, int64_t n,
+                                                                    const uint32_t *__restrict__ partials,
+                                                                    bool total_at, uint32_t *total_out)
+{
+    __shared__ uint32_t lds[17];
+    const int64_t base = (int64_t)blockIdx.x * kScanTile + (int64_t)threadIdx.x * kScanItems;
+    uint32_t v[kScanItems], s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        v[i] = base + i < n ? scan_item<kPopc>(load_or_first(in, base + i, n)) : 0u;
+        s += v[i];
+    }
+    uint32_t before = 0, total;
+    for (int64_t j = threadIdx.x; j < (int64_t)blockIdx.x; j += kScanThreads) before += partials[j];
+    block_exclusive_scan(before, lds, &before);
+    uint32_t run = block_exclusive_scan(s, lds, &total) + before;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i)
+        if (base + i < n) {
+            out[base + i] = run;
+            run += v[i];
+        }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+        if (total_at) out[n] = before + total;
+        if (total_out) *total_out = before + total;
+    }
+}
+
 __global__ void k_copy_total(const uint32_t *src, uint32_t *dst)
 {
     if (threadIdx.x == 0 && blockIdx.x == 0) *dst = *src;
@@ -263,17 +296,32 @@ size_t sort_hist_words(int64_t n)
 }
 
 namespace {
+// Block sums, then either (up to kFusedScanBlocks blocks) one launch that
+// scans with each block's prefix summed in place, or a one-block scan of the
+// sums and the apply launch.  The grand total goes to out[n] (total_at) and
+// to *total (optional).
 template <bool kPopc>
-csp_status scan_impl(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *partials, bool total_at, hipStream_t s)
+csp_status scan_impl(const uint32_t *in, uint32_t *out, int64_t n, uint32_t *partials, bool total_at,
+                     uint32_t *total, hipStream_t s)
 {
     const int64_t nb = ceil_div(n, kScanTile);
     if (nb > kMaxScanPartials) return set_error(CSP_ERR_INVALID_ARG, "scan of %lld items exceeds the limit", (long long)n);
     k_scan_reduce<kPopc><<<dim3((unsigned)nb), dim3(kScanThreads), 0, s>>>(in, n, partials);
     CSP_LAUNCHED("k_scan_reduce");
+    if (nb <= kFusedScanBlocks) {
+        k_scan_apply_prefix<kPopc><<<dim3((unsigned)nb), dim3(kScanThreads), 0, s>>>(in, out, n, partials, total_at,
+                                                                                      total);
+        CSP_LAUNCHED("k_scan_apply_prefix");
+        return CSP_OK;
+    }
     k_scan_partials<<<1, kScanThreads, 0, s>>>(partials, nb);
     CSP_LAUNCHED("k_scan_partials");
     k_scan_apply<kPopc><<<dim3((unsigned)nb), dim3(kScanThreads), 0, s>>>(in, out, n, partials, total_at);
     CSP_LAUNCHED("k_scan_apply");
+    if (total) {
+        k_copy_total<<<1, 64, 0, s>>>(partials + nb, total);
+        CSP_LAUNCHED("k_copy_total");
+    }
     return CSP_OK;
 }
 }  // namespace
@@ -288,19 +336,13 @@ csp_status exclusive_scan_u32(const uint32_t *in, uint32_t *out, int64_t n, uint
         }
         return CSP_OK;
     }
-    csp_status st = scan_impl<false>(in, out, n, partials, false, s);
-    if (st != CSP_OK) return st;
-    if (total) {
-        k_copy_total<<<1, 64, 0, s>>>(partials + ceil_div(n, kScanTile), total);
-        CSP_LAUNCHED("k_copy_total");
-    }
-    return CSP_OK;
+    return scan_impl<false>(in, out, n, partials, false, total, s);
 }
 
 csp_status exclusive_scan_popc(const uint32_t *words, uint32_t *pref, int64_t n, uint32_t *partials, hipStream_t s)
 {
     if (n <= 0) return fill_u32(pref, 0u, 1, s);
-    return scan_impl<true>(words, pref, n, partials, true, s);
+    return scan_impl<true>(words, pref, n, partials, true, nullptr, s);
 }
 
 csp_status radix_sort_pairs(int key_bytes, const void *keys_in, const int32_t *vals_in, void *keys_out,
