@@ -279,77 +279,75 @@ __device__ inline Task load_task(const int4 *__restrict__ desc, int64_t t)
 template <int LD, class D, bool kWide, int E, int kStore = 0>
 __device__ __attribute__((always_inline)) inline void segment_task_body(const Task &T, const int32_t *__restrict__ idx,
                                     const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
-                                    int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
+                                    int64_t n_op, int64_t n_seg, int64_t B, float *__restrict__ partial,
                                     typename D::T *__restrict__ out, const Epi &ep)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
     const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
 
-    for (int ch = 0; ch < nch; ++ch) {
-        const typename D::T *op = opT + (int64_t)ch * n_op * LD + q * VW;
-        float acc[VW];
+    const typename D::T *op = opT + q * VW;
+    float acc[VW];
 #pragma unroll
-        for (int w = 0; w < VW; ++w) acc[w] = 0.f;
-        for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
-            const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
-            int32_t ci[kPerLane];
-            float vv[kPerLane];
+    for (int w = 0; w < VW; ++w) acc[w] = 0.f;
+    for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
+        const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
+        int32_t ci[kPerLane];
+        float vv[kPerLane];
 #pragma unroll
-            for (int u = 0; u < kPerLane; ++u) {
-                const int e = u * kWave + lane;
-                const bool ok = e < m;
-                const int32_t ec = T.kb + p0 + (ok ? e : m - 1);
-                const int32_t c = idx[ec];
-                const float v = D::load(vals, ec);
-                ci[u] = ok ? c : 0;
-                vv[u] = ok ? v : 0.f;
+        for (int u = 0; u < kPerLane; ++u) {
+            const int e = u * kWave + lane;
+            const bool ok = e < m;
+            const int32_t ec = T.kb + p0 + (ok ? e : m - 1);
+            const int32_t c = idx[ec];
+            const float v = D::load(vals, ec);
+            ci[u] = ok ? c : 0;
+            vv[u] = ok ? v : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPerLane; ++u) {
+            if (M::exit_before(u)) {
+                block_fence();
+                if (u * kWave >= m) break;
             }
 #pragma unroll
-            for (int u = 0; u < kPerLane; ++u) {
-                if (M::exit_before(u)) {
-                    block_fence();
-                    if (u * kWave >= m) break;
-                }
+            for (int i0 = 0; i0 < IT; i0 += M::G) {
+                if (i0 > 0) block_fence();
+                float x[M::G][VW], v[M::G];
 #pragma unroll
-                for (int i0 = 0; i0 < IT; i0 += M::G) {
-                    if (i0 > 0) block_fence();
-                    float x[M::G][VW], v[M::G];
+                for (int j = 0; j < M::G; ++j) {
+                    const int l = (i0 + j) * S + s;
+                    const int32_t c = entry_i<S>(ci[u], l);
+                    v[j] = entry_f<S>(vv[u], l);
+                    load_vec<VW>(op + row_off<kWide>(c, LD), x[j]);
+                }
+                if ((u + 1) * kWave <= m) {
+#pragma unroll
+                    for (int j = 0; j < M::G; ++j)
+#pragma unroll
+                        for (int w = 0; w < VW; ++w) acc[w] += v[j] * x[j][w];
+                } else {  // block holding the end of the task
 #pragma unroll
                     for (int j = 0; j < M::G; ++j) {
-                        const int l = (i0 + j) * S + s;
-                        const int32_t c = entry_i<S>(ci[u], l);
-                        v[j] = entry_f<S>(vv[u], l);
-                        load_vec<VW>(op + row_off<kWide>(c, LD), x[j]);
-                    }
-                    if ((u + 1) * kWave <= m) {
+                        const bool ok = u * kWave + (i0 + j) * S + s < m;
 #pragma unroll
-                        for (int j = 0; j < M::G; ++j)
-#pragma unroll
-                            for (int w = 0; w < VW; ++w) acc[w] += v[j] * x[j][w];
-                    } else {  // block holding the end of the task
-#pragma unroll
-                        for (int j = 0; j < M::G; ++j) {
-                            const bool ok = u * kWave + (i0 + j) * S + s < m;
-#pragma unroll
-                            for (int w = 0; w < VW; ++w) acc[w] += v[j] * (ok ? x[j][w] : 0.f);
-                        }
+                        for (int w = 0; w < VW; ++w) acc[w] += v[j] * (ok ? x[j][w] : 0.f);
                     }
                 }
             }
         }
+    }
 #pragma unroll
-        for (int w = 0; w < VW; ++w) acc[w] = slot_sum<LPE>(acc[w]);
-        if (s == 0) {
+    for (int w = 0; w < VW; ++w) acc[w] = slot_sum<LPE>(acc[w]);
+    if (s == 0) {
 #pragma unroll
-            for (int w = 0; w < VW; ++w) {
-                const int64_t b = (int64_t)ch * LD + q * VW + w;
-                if (b >= B) continue;
-                if (kStore == 1 || (kStore == 0 && T.slot < 0))
-                    out[b * n_seg + T.seg] = finish_out<E, D>(acc[w], b, T.seg, n_seg, ep);
-                else
-                    partial[((int64_t)T.slot * nch + ch) * LD + q * VW + w] = acc[w];
-            }
+        for (int w = 0; w < VW; ++w) {
+            const int64_t b = q * VW + w;
+            if (b >= B) continue;
+            if (kStore == 1 || (kStore == 0 && T.slot < 0))
+                out[b * n_seg + T.seg] = finish_out<E, D>(acc[w], b, T.seg, n_seg, ep);
+            else
+                partial[(int64_t)T.slot * LD + q * VW + w] = acc[w];
         }
     }
 }
@@ -357,11 +355,10 @@ __device__ __attribute__((always_inline)) inline void segment_task_body(const Ta
 template <int LD, class D, bool kWide, int E, int kStore = 0>
 __device__ __attribute__((always_inline)) inline void segment_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ idx,
                                     const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
-                                    int64_t n_op, int64_t n_seg, int64_t B, int nch, float *__restrict__ partial,
+                                    int64_t n_op, int64_t n_seg, int64_t B, float *__restrict__ partial,
                                     typename D::T *__restrict__ out, const Epi &ep)
 {
-    segment_task_body<LD, D, kWide, E, kStore>(load_task(desc, t), idx, vals, opT, n_op, n_seg, B, nch, partial, out,
-                                               ep);
+    segment_task_body<LD, D, kWide, E, kStore>(load_task(desc, t), idx, vals, opT, n_op, n_seg, B, partial, out, ep);
 }
 
 // kStore = 1 when the list has no split segments (every task stores its output).
@@ -370,13 +367,13 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
                                                       const int32_t *__restrict__ idx,
                                                       const typename D::T *__restrict__ vals,
                                                       const typename D::T *__restrict__ opT, int64_t n_op,
-                                                      int64_t n_seg, int64_t B, int nch,
+                                                      int64_t n_seg, int64_t B,
                                                       float *__restrict__ partial, typename D::T *__restrict__ out,
                                                       Epi ep)
 {
     const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    segment_task<LD, D, kWide, E, kStore>(desc, t, idx, vals, opT, n_op, n_seg, B, nch, partial, out, ep);
+    segment_task<LD, D, kWide, E, kStore>(desc, t, idx, vals, opT, n_op, n_seg, B, partial, out, ep);
 }
 
 // Segment pass with split segments finished in the kernel (one batch chunk,
@@ -405,7 +402,7 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void k_segment_grouped(
         // a split task's slot is its task index, so its partial sums land in part[slot - first]
         float *base = &part[0][0] - (int64_t)first * LD;
         for (int32_t j = wave; j < cnt; j += kGroupWaves)
-            segment_task_body<LD, D, kWide, E, 2>(load_task(desc, first + j), idx, vals, opT, n_op, n_seg, B, 1,
+            segment_task_body<LD, D, kWide, E, 2>(load_task(desc, first + j), idx, vals, opT, n_op, n_seg, B,
                                                   base, out, ep);
         __syncthreads();
         if (threadIdx.x < B) {
@@ -420,23 +417,22 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void k_segment_grouped(
     if (t >= ntasks) return;
     const Task T = load_task(desc, t);
     if (T.slot >= 0) return;  // part of a split segment: finished by its own workgroup
-    segment_task_body<LD, D, kWide, E, 1>(T, idx, vals, opT, n_op, n_seg, B, 1, nullptr, out, ep);
+    segment_task_body<LD, D, kWide, E, 1>(T, idx, vals, opT, n_op, n_seg, B, nullptr, out, ep);
 }
 
 // Finish split segments: out[b, seg] = sum over the segment's tasks, in task
 // order, of their partial sums.  One thread per (split segment, batch index).
 template <class D, int E>
 __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ split, int64_t nsplit,
-                                                     const float *__restrict__ partial, int64_t B, int ld, int nch,
+                                                     const float *__restrict__ partial, int64_t B, int ld,
                                                      int64_t n_seg, typename D::T *__restrict__ out, Epi ep)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= nsplit * B) return;
     const int64_t q = i / B, bg = i - q * B;
     const int4 r = split[q];
-    const int64_t ch = bg / ld, bl = bg - ch * ld;
-    const float *src = partial + ((int64_t)r.y * nch + ch) * ld + bl;
-    const int64_t stride = (int64_t)nch * ld;
+    const float *src = partial + (int64_t)r.y * ld + bg;
+    const int64_t stride = ld;
     float tot = 0.f;
     int32_t p = 0;
     for (; p + 8 <= r.z; p += 8) {  // eight independent loads in flight, added in task order
@@ -462,60 +458,58 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
 template <int LD, class D, bool kWide, int NW = 4, bool kRowMajorDy = false>
 __device__ __attribute__((always_inline)) inline void values_task_body(const Task &T, const int32_t *__restrict__ cols,
                                    const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
-                                   int64_t in, int64_t out, int64_t B, int nch, float *__restrict__ dW, bool acc)
+                                   int64_t in, int64_t out, int64_t B, float *__restrict__ dW, bool acc)
 {
     using M = Map<LD>;
     constexpr int VW = M::VW, LPE = M::LPE, S = M::S, IT = M::IT;
     __shared__ float stage[NW][kWave];
     const int lane = threadIdx.x & 63, s = lane / LPE, q = lane % LPE;
     float *lds = stage[threadIdx.x >> 6];
-    for (int ch = 0; ch < nch; ++ch) {
-        float dy[VW];
-        if constexpr (kRowMajorDy) {
+    float dy[VW];
+    if constexpr (kRowMajorDy) {
 #pragma unroll
-            for (int w = 0; w < VW; ++w) {
-                const int64_t b = q * VW + w;
-                const float v = D::load(dYT, (b < B ? b : 0) * out + T.seg);
-                dy[w] = b < B ? v : 0.f;
-            }
-        } else {
-            load_vec<VW>(dYT + ((int64_t)ch * out + T.seg) * LD + q * VW, dy);
+        for (int w = 0; w < VW; ++w) {
+            const int64_t b = q * VW + w;
+            const float v = D::load(dYT, (b < B ? b : 0) * out + T.seg);
+            dy[w] = b < B ? v : 0.f;
         }
-        const typename D::T *xt = XT + (int64_t)ch * in * LD + q * VW;
-        for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
-            const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
-            int32_t ci[kPerLane];
+    } else {
+        load_vec<VW>(dYT + (int64_t)T.seg * LD + q * VW, dy);
+    }
+    const typename D::T *xt = XT + q * VW;
+    for (int32_t p0 = 0; p0 < T.n; p0 += kPass) {
+        const int32_t m = T.n - p0 < kPass ? T.n - p0 : kPass;
+        int32_t ci[kPerLane];
 #pragma unroll
-            for (int u = 0; u < kPerLane; ++u) {
-                const int e = u * kWave + lane;
-                const int32_t c = cols[T.kb + p0 + (e < m ? e : m - 1)];
-                ci[u] = e < m ? c : 0;
+        for (int u = 0; u < kPerLane; ++u) {
+            const int e = u * kWave + lane;
+            const int32_t c = cols[T.kb + p0 + (e < m ? e : m - 1)];
+            ci[u] = e < m ? c : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kPerLane; ++u) {
+            if (M::exit_before(u)) block_fence();
+            if (u * kWave >= m) break;
+#pragma unroll
+            for (int i0 = 0; i0 < IT; i0 += M::G) {
+                if (i0 > 0) block_fence();
+                float x[M::G][VW];
+#pragma unroll
+                for (int j = 0; j < M::G; ++j)
+                    load_vec<VW>(xt + row_off<kWide>(entry_i<S>(ci[u], (i0 + j) * S + s), LD), x[j]);
+#pragma unroll
+                for (int j = 0; j < M::G; ++j) {
+                    float p = 0.f;
+#pragma unroll
+                    for (int w = 0; w < VW; ++w) p += dy[w] * x[j][w];
+                    lds[(i0 + j) * S + s] = group_sum<LPE>(p);
+                }
             }
-#pragma unroll
-            for (int u = 0; u < kPerLane; ++u) {
-                if (M::exit_before(u)) block_fence();
-                if (u * kWave >= m) break;
-#pragma unroll
-                for (int i0 = 0; i0 < IT; i0 += M::G) {
-                    if (i0 > 0) block_fence();
-                    float x[M::G][VW];
-#pragma unroll
-                    for (int j = 0; j < M::G; ++j)
-                        load_vec<VW>(xt + row_off<kWide>(entry_i<S>(ci[u], (i0 + j) * S + s), LD), x[j]);
-#pragma unroll
-                    for (int j = 0; j < M::G; ++j) {
-                        float p = 0.f;
-#pragma unroll
-                        for (int w = 0; w < VW; ++w) p += dy[w] * x[j][w];
-                        lds[(i0 + j) * S + s] = group_sum<LPE>(p);
-                    }
-                }
-                const float r = lds[lane];
-                const int32_t e = p0 + u * kWave + lane;
-                if (e < T.n) {
-                    if (ch == 0 && !acc) dW[T.kb + e] = r;
-                    else dW[T.kb + e] += r;
-                }
+            const float r = lds[lane];
+            const int32_t e = p0 + u * kWave + lane;
+            if (e < T.n) {
+                if (!acc) dW[T.kb + e] = r;
+                else dW[T.kb + e] += r;
             }
         }
     }
@@ -524,9 +518,9 @@ __device__ __attribute__((always_inline)) inline void values_task_body(const Tas
 template <int LD, class D, bool kWide>
 __device__ __attribute__((always_inline)) inline void values_task(const int4 *__restrict__ desc, int64_t t, const int32_t *__restrict__ cols,
                                    const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
-                                   int64_t in, int64_t out, int nch, float *__restrict__ dW, bool acc)
+                                   int64_t in, int64_t out, float *__restrict__ dW, bool acc)
 {
-    values_task_body<LD, D, kWide>(load_task(desc, t), cols, XT, dYT, in, out, 0, nch, dW, acc);
+    values_task_body<LD, D, kWide>(load_task(desc, t), cols, XT, dYT, in, out, 0, dW, acc);
 }
 
 template <int LD, class D, bool kWide>
@@ -534,11 +528,11 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
                                                      const int32_t *__restrict__ cols,
                                                      const typename D::T *__restrict__ XT,
                                                      const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
-                                                     int nch, float *__restrict__ dW, int acc)
+                                                     float *__restrict__ dW, int acc)
 {
     const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, nch, dW, acc != 0);
+    values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, dW, acc != 0);
 }
 
 // --------------------------------------------------- both gradients
@@ -554,7 +548,7 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
                                                    const int32_t *__restrict__ cols,
                                                    const typename D::T *__restrict__ XT,
                                                    const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
-                                                   int64_t B, int nch, float *__restrict__ partial,
+                                                   int64_t B, float *__restrict__ partial,
                                                    typename D::T *__restrict__ dX, float *__restrict__ dW, Epi ep,
                                                    int acc)
 {
@@ -575,10 +569,9 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
     const int64_t t = blk * 4 + (threadIdx.x >> 6);
     if (col) {
         if (t < ncol_tasks)
-            segment_task<LD, D, kWide, E, kStore>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, nch, partial, dX,
-                                                  ep);
+            segment_task<LD, D, kWide, E, kStore>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, partial, dX, ep);
     } else if (t < nrow_tasks) {
-        values_task<LD, D, kWide>(row_desc, t, cols, XT, dYT, in, out, nch, dW, acc != 0);
+        values_task<LD, D, kWide>(row_desc, t, cols, XT, dYT, in, out, dW, acc != 0);
     }
 }
 
@@ -653,7 +646,7 @@ __global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restr
     const Task T = load_task(desc, has ? t : 0);  // in flight during the fill
     fill_table<LD, D>(op, n_op, B, tab);
     __syncthreads();
-    if (has) segment_task_body<LD, D, false, E, kStore>(T, idx, vals, tab, n_op, n_seg, B, 1, partial, out, ep);
+    if (has) segment_task_body<LD, D, false, E, kStore>(T, idx, vals, tab, n_op, n_seg, B, partial, out, ep);
 }
 
 // Both gradients: workgroups alternate between input-gradient column tasks
@@ -691,8 +684,8 @@ __global__ __launch_bounds__(kLdsThreads) void k_gradients_lds(const int4 *__res
     else fill_table<LD, D>(X, in, B, tab);
     __syncthreads();
     if (!has) return;
-    if (col) segment_task_body<LD, D, false, E, kStore>(T, rows_by_col, vals_c, tab, out, in, B, 1, partial, dX, ep);
-    else values_task_body<LD, D, false, kLdsWaves, true>(T, cols, tab, dY, in, out, B, 1, dW, acc != 0);
+    if (col) segment_task_body<LD, D, false, E, kStore>(T, rows_by_col, vals_c, tab, out, in, B, partial, dX, ep);
+    else values_task_body<LD, D, false, kLdsWaves, true>(T, cols, tab, dY, in, out, B, dW, acc != 0);
 }
 
 // ------------------------------------------------------------ host side
@@ -769,9 +762,8 @@ csp_status split_fixup(csp_layer *L, const TaskList &TL, int64_t B, int64_t n_se
 {
     if (TL.nsplit == 0) return CSP_OK;
     const int ld = pow2_ld(B);
-    const int nch = (int)ceil_div(B, ld);
     k_split_fixup<D, E><<<(unsigned)ceil_div(TL.nsplit * B, 256), 256, 0, s>>>(
-        TL.split, TL.nsplit, L->act.partial, B, ld, nch, n_seg, (typename D::T *)out, ep);
+        TL.split, TL.nsplit, L->act.partial, B, ld, n_seg, (typename D::T *)out, ep);
     CSP_LAUNCHED("k_split_fixup");
     return CSP_OK;
 }
@@ -911,14 +903,13 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->row_tasks;
     if (grouped_splits(TL, B, L->in, L->in))
         return grouped_dispatch<D, E>(L, TL, L->cols, L->vals, XT, L->in, L->out, B, Y, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     const bool ks = TL.nsplit == 0;
 #define CSP_FWD_ARGS \
-    TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, nch, L->act.partial, (T *)Y, ep
+    TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, L->act.partial, (T *)Y, ep
 #define CSP_FWD(LDV, W)                                                             \
     if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_FWD_ARGS);    \
     else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_FWD_ARGS)
@@ -934,14 +925,13 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->col_tasks;
     if (grouped_splits(TL, B, L->out, L->out))
         return grouped_dispatch<D, E>(L, TL, L->rows_by_col, L->vals_c, dYT, L->out, L->in, B, dX, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     const bool ks = TL.nsplit == 0;
 #define CSP_DX_ARGS                                                                                                 \
-    TL.desc, TL.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, nch, L->act.partial, \
+    TL.desc, TL.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX(LDV, W)                                                            \
     if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_DX_ARGS);   \
@@ -959,12 +949,11 @@ csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, in
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    const int nch = (int)ceil_div(B, ld);
     const TaskList &TL = L->row_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
 #define CSP_DW(LDV, W)                                                                                            \
     launch_main(L, kTimeBoth, k_values_rows<LDV, D, W>, grid, 256, 0, s, TL.desc, TL.count, L->cols, (const T *)XT, (const T *)dYT, L->in, \
-                                                  L->out, nch, dW, (int)acc)
+                                                  L->out, dW, (int)acc)
     CSP_LD_SWITCH(ld, wide_operand(L->in > L->out ? L->in : L->out, ld), CSP_DW);
 #undef CSP_DW
     CSP_LAUNCHED("k_values_rows");
@@ -977,7 +966,6 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    const int nch = (int)ceil_div(B, ld);
     const TaskList &CT = L->col_tasks, &RT = L->row_tasks;
     const int64_t nrow = L->nnz > 0 ? RT.count : 0;  // no value-gradient work for an empty layer
     const bool wide = wide_operand(L->in > L->out ? L->in : L->out, ld);
@@ -991,7 +979,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         const int m1 = gw > 0 ? kTimeStart : kTimeBoth;  // the value-gradient kernel carries the end
         const bool ks = CT.nsplit == 0;
 #define CSP_DX2_ARGS                                                                                                \
-    CT.desc, CT.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, nch, L->act.partial, \
+    CT.desc, CT.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX2(LDV, W)                                                         \
     if (ks) launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 1>, gx, 256, 0, s, CSP_DX2_ARGS);  \
@@ -1003,7 +991,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         if (gw > 0) {
 #define CSP_DW2(LDV, W)                                                                                           \
     launch_main(L, kTimeStop, k_values_rows<LDV, D, W>, gw, 256, 0, s, RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
-                                                nch, dW, (int)acc)
+                                                dW, (int)acc)
             CSP_LD_SWITCH(ld, wide, CSP_DW2);
 #undef CSP_DW2
             CSP_LAUNCHED("k_values_rows");
@@ -1014,7 +1002,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
     const bool ks = CT.nsplit == 0;
 #define CSP_BOTH_ARGS                                                                                            \
     CT.desc, CT.count, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)XT, (const T *)dYT, \
-        L->in, L->out, B, nch, L->act.partial, (T *)dX, dW, ep, (int)acc
+        L->in, L->out, B, L->act.partial, (T *)dX, dW, ep, (int)acc
 #define CSP_BOTH(LDV, W)                                                        \
     if (ks) launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_BOTH_ARGS);  \
     else launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_BOTH_ARGS)
