@@ -373,42 +373,31 @@ __device__ inline uint32_t hash_first(const uint64_t *tab, int hbits, uint32_t p
     return kNoPos;
 }
 
-// Candidates [i0, i0 + M) of the stream (i0 a multiple of 4), four per
-// thread (one Philox block): occupied positions drop out, the others enter
-// the hash table.
+// Candidates [i0, i0 + M) of the stream (i0 a multiple of 4), one per
+// thread: each thread computes its candidate's Philox block (four threads
+// share one; recomputing it is cheaper than waiting on fewer, longer chains)
+// and keeps its word.  Occupied positions drop out, the others enter the
+// hash table.
 __global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint64_t step, uint64_t i0, int64_t M,
                                                              int64_t in, uint64_t npos, const uint32_t *occ,
                                                              int64_t inw, uint32_t *__restrict__ cand, uint64_t *tab,
-                                                             int hbits, uint32_t *sel)
+                                                             int hbits)
 {
-    (void)sel;
-    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x, j0 = 4 * t;
-    if (j0 >= M) return;
+    const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (j >= M) return;
     uint64_t u[4];
-    Philox4x64::block(seed, step, (i0 >> 2) + (uint64_t)t, u);
-    uint32_t p[4];
-    bool free_[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const uint64_t pq = __umul64hi(u[q], npos);
-        const int64_t r = (int64_t)(pq / (uint64_t)in), c = (int64_t)pq - r * in;
-        p[q] = (uint32_t)pq;
-        free_[q] = j0 + q < M && !((occ[r * inw + (c >> 5)] >> (c & 31)) & 1u);
-    }
-    uint64_t home[4], old[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {  // the four first attempts go out together
-        home[q] = hash_home(p[q], hbits);
-        old[q] = free_[q] ? atomicCAS((unsigned long long *)&tab[home[q]], kEmptySlot,
-                                      ((uint64_t)p[q] << 32) | (uint64_t)(j0 + q))
-                          : kEmptySlot;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (j0 + q >= M) break;
-        cand[j0 + q] = free_[q] ? p[q] : kNoPos;
-        if (free_[q]) hash_insert_from(tab, hbits, p[q], (uint32_t)(j0 + q), home[q], old[q]);
-    }
+    Philox4x64::block(seed, step, (i0 >> 2) + (uint64_t)(j >> 2), u);
+    const int q = (int)(j & 3);
+    const uint64_t uq = q == 0 ? u[0] : q == 1 ? u[1] : q == 2 ? u[2] : u[3];
+    const uint64_t pq = __umul64hi(uq, npos);
+    const int64_t r = (int64_t)(pq / (uint64_t)in), c = (int64_t)pq - r * in;
+    const uint32_t p = (uint32_t)pq;
+    const bool free_ = !((occ[r * inw + (c >> 5)] >> (c & 31)) & 1u);
+    cand[j] = free_ ? p : kNoPos;
+    if (!free_) return;
+    const uint64_t home = hash_home(p, hbits);
+    const uint64_t old = atomicCAS((unsigned long long *)&tab[home], kEmptySlot, ((uint64_t)p << 32) | (uint64_t)j);
+    hash_insert_from(tab, hbits, p, (uint32_t)j, home, old);
 }
 
 // flag[j] = candidate j is empty and the first of its position in the batch;
@@ -778,8 +767,8 @@ struct BitmapRun {
     {
         Workspace &W = L->ws;
         const unsigned nt = blocks_for(M, kThreads);
-        k_bm_cand_insert<<<blocks_for(M, 4 * kThreads), kThreads, 0, s>>>(seed, step, i0, M, L->in, npos, W.occ_next, W.occ_row_words, W.u_a,
-                                                 W.hash, hb, W.sel);
+        k_bm_cand_insert<<<blocks_for(M, kThreads), kThreads, 0, s>>>(seed, step, i0, M, L->in, npos, W.occ_next,
+                                                                      W.occ_row_words, W.u_a, W.hash, hb);
         CSP_LAUNCHED("k_bm_cand_insert");
         k_bm_cand_count<<<nt, kThreads, 0, s>>>(W.u_a, M, W.hash, hb, (uint64_t *)W.u_b, W.hist);
         CSP_LAUNCHED("k_bm_cand_count");
