@@ -477,29 +477,32 @@ __global__ __launch_bounds__(kThreads) void k_bm_cand_take(const uint32_t *__res
 //     s = 0; for b = 0..B-1: s = fma(dY[b, r], X[b, c], s)     (fp32)
 // -- the fused-multiply-add chain in batch order, so the integer decision
 // "which positions come back" is the same on any implementation that keeps
-// this order.  Block = 64 rows x 64 columns; thread = 4 rows x 4 columns
-// (register tile); dY and X tiles of 64 batch rows at a time in LDS.
+// this order.  Block = 128 rows x 128 columns; thread = 8 rows x 8 columns
+// (64 independent chains in registers, one LDS word per four FMAs); dY and X
+// tiles of kScoreB batch rows at a time in LDS.
+constexpr int kScoreTile = 128;
+constexpr int kScoreB = 32;
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_bm_scores(const typename D::T *__restrict__ dY,
                                                         const typename D::T *__restrict__ X, int64_t B, int64_t out,
                                                         int64_t in, const uint32_t *__restrict__ occ, int64_t inw,
-                                                        uint32_t *__restrict__ keys)
+                                                        int64_t rows_alloc, uint32_t *__restrict__ keys)
 {
-    __shared__ float ty[64][64 + 1];  // [b][row]
-    __shared__ float tx[64][64 + 1];  // [b][col]
-    const int t = threadIdx.x, tr = t >> 4, tc = t & 15;  // 16 x 16 threads, 4 x 4 each
-    const int64_t ncb = inw / 2;                           // 64-column blocks
-    const int64_t r0 = (int64_t)(blockIdx.x / ncb) * 64, c0 = (int64_t)(blockIdx.x % ncb) * 64;
-    float acc[4][4];
+    __shared__ __align__(16) float ty[kScoreB][kScoreTile + 4];  // [b][row]
+    __shared__ __align__(16) float tx[kScoreB][kScoreTile + 4];  // [b][col]
+    const int t = threadIdx.x, tr = t >> 4, tc = t & 15;         // 16 x 16 threads, 8 x 8 each
+    const int64_t ncb = inw * 32 / kScoreTile;                    // column blocks
+    const int64_t r0 = (int64_t)(blockIdx.x / ncb) * kScoreTile, c0 = (int64_t)(blockIdx.x % ncb) * kScoreTile;
+    float acc[8][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-    for (int64_t b0 = 0; b0 < B; b0 += 64) {
-        const int nb = B - b0 < 64 ? (int)(B - b0) : 64;
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int64_t b0 = 0; b0 < B; b0 += kScoreB) {
+        const int nb = B - b0 < kScoreB ? (int)(B - b0) : kScoreB;
         __syncthreads();
-        for (int e = t; e < 64 * 64; e += kThreads) {
-            const int bb = e >> 6, k = e & 63;
+        for (int e = t; e < kScoreB * kScoreTile; e += kThreads) {
+            const int bb = e / kScoreTile, k = e % kScoreTile;
             const bool okb = bb < nb;
             const int64_t r = r0 + k, c = c0 + k;
             ty[bb][k] = okb && r < out ? D::load(dY, (b0 + bb) * out + r) : 0.f;
@@ -507,34 +510,33 @@ __global__ __launch_bounds__(kThreads) void k_bm_scores(const typename D::T *__r
         }
         __syncthreads();
         for (int bb = 0; bb < nb; ++bb) {
-            float y[4], x[4];
+            const float4 y0 = *reinterpret_cast<const float4 *>(&ty[bb][tr * 8]);
+            const float4 y1 = *reinterpret_cast<const float4 *>(&ty[bb][tr * 8 + 4]);
+            const float4 x0 = *reinterpret_cast<const float4 *>(&tx[bb][tc * 8]);
+            const float4 x1 = *reinterpret_cast<const float4 *>(&tx[bb][tc * 8 + 4]);
+            const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = ty[bb][tr * 4 + i];
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x[j] = tx[bb][tc * 4 + j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = __fmaf_rn(y[i], x[j], acc[i][j]);
+                for (int j = 0; j < 8; ++j) acc[i][j] = __fmaf_rn(y[i], x[j], acc[i][j]);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t r = r0 + tr * 4 + i;
-        const int64_t c = c0 + tc * 4;  // four consecutive columns in one bitmap word
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + tr * 8 + i;
+        if (r >= rows_alloc) break;
+        const int64_t c = c0 + tc * 8;  // eight consecutive columns in one bitmap word
         const uint32_t w = occ[r * inw + (c >> 5)];
-        uint4 k4;
-        uint32_t kv[4];
+        uint32_t kv[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 8; ++j) {
             const bool live = r < out && c + j < in && !((w >> ((c + j) & 31)) & 1u);
             kv[j] = live ? (__float_as_uint(fabsf(acc[i][j])) + 1u) : 0u;
         }
-        k4.x = kv[0];
-        k4.y = kv[1];
-        k4.z = kv[2];
-        k4.w = kv[3];
-        *(uint4 *)(keys + r * inw * 32 + c) = k4;
+        uint4 *dst = reinterpret_cast<uint4 *>(keys + r * inw * 32 + c);
+        dst[0] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+        dst[1] = make_uint4(kv[4], kv[5], kv[6], kv[7]);
     }
 }
 
@@ -872,10 +874,11 @@ struct BitmapRun {
     {
         Workspace &W = L->ws;
         const int64_t npad = W.occ_words * 32;  // padded positions, bitmap order
-        const int64_t rblk = ceil_div(W.occ_rows, 64), cblk = W.occ_row_words / 2;
+        const int64_t rblk = ceil_div(W.occ_rows, kScoreTile), cblk = W.occ_row_words * 32 / kScoreTile;
         k_bm_scores<D><<<(unsigned)(rblk * cblk), kThreads, 0, s>>>((const typename D::T *)dY,
                                                                      (const typename D::T *)X, B, L->out, L->in,
-                                                                     W.occ_next, W.occ_row_words, W.score);
+                                                                     W.occ_next, W.occ_row_words, W.occ_rows,
+                                                                     W.score);
         CSP_LAUNCHED("k_bm_scores");
         uint64_t *chosen = (uint64_t *)W.occ_pref_next;  // scratch until the rebuild
         csp_status st = select(InvKeys{W.score}, npad, n_prune, 4, 24, chosen, nullptr, 0);
