@@ -389,8 +389,11 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     lds_on = os.environ.get("COOSPMM_LDS_TABLES", "1")[:1] != "0"
 
-    def lds_fits(n):
-        """The library gathers from an LDS copy of an operand of n columns (2 <= B <= 64, <= 64 KiB)."""
+    def lds_fits(n, segment=False):
+        """The library gathers from an LDS copy of an operand of n columns (2 <= B <= 64,
+        <= 64 KiB; the segment passes also need every segment to be at most 64 tasks)."""
+        if segment and -(-n // 512) > 64:
+            return False
         return lds_on and 2 <= B <= 64 and n * ld * esz <= (64 << 10)
 
     grouped_on = os.environ.get("COOSPMM_GROUPED_SPLITS", "1")[:1] != "0"
@@ -410,8 +413,8 @@ def main():
     # split segment (every task stores its output), else 0.
     def fwd_name(L, epi=0):
         ks = int(longest(L, True) <= 512)
-        if lds_fits(L.in_):
-            return f"k_segment_lds<{ld}, {dt_name}, {epi}, {ks}>"
+        if lds_fits(L.in_, segment=True):
+            return f"k_segment_lds<{ld}, {dt_name}, {epi}>"
         # split rows finish inside the pass when no row can exceed 64 tasks
         if grouped_on and B <= 8 and not ks and L.in_ <= 64 * 512:
             return f"k_segment_grouped<{ld}, {dt_name}, false, {epi}>"

@@ -63,6 +63,7 @@ struct ActBuffer {
     size_t bytes = 0;
     float *partial = nullptr;
     size_t partial_bytes = 0;
+    int cus = 0;  // compute units of the layer's device (sizes persistent grids)
 };
 
 // Segments (rows for the row-order passes, columns for the transposed ones)

@@ -193,6 +193,11 @@ csp_status sparse_layer_create(int64_t out_features, int64_t in_features, int64_
         return set_error(CSP_ERR_HIP, "hipGetDevice failed");
     }
     hipStream_t s = (hipStream_t)stream;
+    if (hipDeviceGetAttribute(&L->act.cus, hipDeviceAttributeMultiprocessorCount, L->device) != hipSuccess ||
+        L->act.cus <= 0) {
+        delete L;
+        return set_error(CSP_ERR_HIP, "cannot query the compute-unit count");
+    }
     csp_status st = alloc_layer(L);
     if (st == CSP_OK) st = fill_u32(L->ws.sel, 0u, kSelAllocWords, s);
     if (st == CSP_OK) st = build_canonical(L, rows, cols, vals, L->ws.sel, s);

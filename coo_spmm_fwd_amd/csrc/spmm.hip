@@ -597,7 +597,17 @@ __device__ inline void fill_table(const typename D::T *__restrict__ src, int64_t
 {
     using T = typename D::T;
     if constexpr (LD == 1) {
-        for (int64_t i = threadIdx.x; i < n; i += kLdsThreads) tab[i] = src[i];
+        // A plain copy: 16-byte pieces when the source is 16-byte aligned.
+        int64_t head = 0;
+        if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+            constexpr int P = 16 / (int)sizeof(T);
+            const int64_t np = n / P;
+            const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
+            uint4 *t4 = reinterpret_cast<uint4 *>(tab);
+            for (int64_t i = threadIdx.x; i < np; i += kLdsThreads) t4[i] = s4[i];
+            head = np * P;
+        }
+        for (int64_t i = head + threadIdx.x; i < n; i += kLdsThreads) tab[i] = src[i];
     } else {
         constexpr int W = LD * (int)sizeof(T) / 4;  // 32-bit words per column
         for (int64_t c = threadIdx.x; c < n; c += kLdsThreads) {
@@ -630,23 +640,61 @@ __device__ inline void fill_table(const typename D::T *__restrict__ src, int64_t
     }
 }
 
-// Forward (row tasks over X) or input gradient (column tasks over dY).
-template <int LD, class D, int E, int kStore>
+// Forward (row tasks over X) or input gradient (column tasks over dY) with
+// the operand table in LDS.  The grid is persistent (about two workgroups per
+// CU), so each workgroup fills the table once.  It then takes every grid-th
+// split segment (its 16 waves run the segment's tasks and add their sums in
+// LDS in task order, as in k_segment_grouped), and after those each wave
+// takes every (16 * grid)-th task, skipping split ones.  Fixed strides need
+// no shared counter: one counter on one address, taken by every workgroup,
+// costs more in serialised atomics than the balance it buys.  Which wave runs
+// a task does not change its arithmetic, so the outputs are bitwise those of
+// the global-table kernels.
+template <int LD, class D, int E>
 __global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restrict__ desc, int64_t ntasks,
+                                                             const int4 *__restrict__ split, int64_t nsplit,
                                                              const int32_t *__restrict__ idx,
                                                              const typename D::T *__restrict__ vals,
                                                              const typename D::T *__restrict__ op, int64_t n_op,
-                                                             int64_t n_seg, int64_t B, float *__restrict__ partial,
-                                                             typename D::T *__restrict__ out, Epi ep)
+                                                             int64_t n_seg, int64_t B, typename D::T *__restrict__ out,
+                                                             Epi ep)
 {
     extern __shared__ __align__(16) unsigned char lds_table[];
+    __shared__ float part[kGroupMaxTasks][LD];
     auto *tab = reinterpret_cast<typename D::T *>(lds_table);
-    const int64_t t = xcd_block() * kLdsWaves + (threadIdx.x >> 6);
-    const bool has = t < ntasks;
-    const Task T = load_task(desc, has ? t : 0);  // in flight during the fill
+    const int wave = threadIdx.x >> 6;
     fill_table<LD, D>(op, n_op, B, tab);
     __syncthreads();
-    if (has) segment_task_body<LD, D, false, E, kStore>(T, idx, vals, tab, n_op, n_seg, B, partial, out, ep);
+    // Split segments first, a whole workgroup each.
+    for (int64_t g = blockIdx.x; g < nsplit; g += gridDim.x) {
+        const int4 r = split[g];  // {segment, first task, task count, 0}
+        const int32_t seg = uniform(r.x), first = uniform(r.y), cnt = uniform(r.z);
+        float *base = &part[0][0] - (int64_t)first * LD;  // slot = task index
+        for (int32_t j = wave; j < cnt; j += kLdsWaves)
+            segment_task_body<LD, D, false, E, 2>(load_task(desc, first + j), idx, vals, tab, n_op, n_seg, B, base,
+                                                  out, ep);
+        __syncthreads();
+        if (threadIdx.x < B) {
+            const int64_t b = threadIdx.x;
+            float tot = 0.f;
+            for (int32_t j = 0; j < cnt; ++j) tot += part[j][b];
+            out[b * n_seg + seg] = finish_out<E, D>(tot, b, seg, n_seg, ep);
+        }
+        __syncthreads();  // partial sums consumed before the next group writes them
+    }
+    // Then the unsplit tasks, each wave on its own stride (no barrier: a
+    // wave that drew short tasks moves on at once).  The next descriptor is
+    // loaded before the current task runs, so its latency hides behind it.
+    const int64_t nw = (int64_t)gridDim.x * kLdsWaves;
+    int64_t t = (int64_t)blockIdx.x * kLdsWaves + wave;
+    if (t >= ntasks) return;
+    int4 d = desc[t];
+    for (; t < ntasks; t += nw) {
+        const int4 dn = desc[t + nw < ntasks ? t + nw : t];
+        const Task T{uniform(d.x), uniform(d.y), uniform(d.z) - uniform(d.y), uniform(d.w)};
+        if (T.slot < 0) segment_task_body<LD, D, false, E, 1>(T, idx, vals, tab, n_op, n_seg, B, nullptr, out, ep);
+        d = dn;
+    }
 }
 
 // Both gradients: workgroups alternate between input-gradient column tasks
@@ -768,14 +816,26 @@ csp_status split_fixup(csp_layer *L, const TaskList &TL, int64_t B, int64_t n_se
     return CSP_OK;
 }
 
-// Small-table path (see fill_table) for a pass that gathers from an operand
-// of n columns.  COOSPMM_LDS_TABLES=0 forces the global-table path (A/B runs
-// and tests of both paths).
+// Small-table paths (see fill_table) for a pass that gathers from an operand
+// of n columns, 2 <= B <= 64.  At B = 1 the operand is a single row that
+// stays cached near the CUs anyway and no copy launch is saved, so filling
+// tables costs more than it returns (measured: 1 us slower on a 16384-column
+// bf16 layer).  The segment pass (k_segment_lds) also needs every segment to
+// be at most kGroupMaxTasks tasks; its segments are at most n long.
+// COOSPMM_LDS_TABLES=0 forces the global-table paths (A/B runs and tests).
+inline bool lds_tables_enabled()
+{
+    const char *e = std::getenv("COOSPMM_LDS_TABLES");
+    return !(e && e[0] == '0');
+}
 inline bool lds_table_fits(const csp_layer *L, int64_t B, int64_t n)
 {
     if (B < 2 || B > 64 || (size_t)n * (size_t)pow2_ld(B) * (size_t)L->esz > kLdsTableBytes) return false;
-    const char *e = std::getenv("COOSPMM_LDS_TABLES");
-    return !(e && e[0] == '0');
+    return lds_tables_enabled();
+}
+inline bool lds_segment_fits(const csp_layer *L, int64_t B, int64_t n)
+{
+    return ceil_div(n, kTaskChunk) <= kGroupMaxTasks && lds_table_fits(L, B, n);
 }
 
 // The kernel's dynamic LDS limit is raised to the table size once per kernel
@@ -804,31 +864,31 @@ csp_status allow_lds(size_t)
     }
 
 // One segment pass (forward: rows over X; input gradient: columns over dY)
-// from a row-major operand through an LDS table.
+// from a row-major operand through an LDS table: a persistent grid of at
+// most two workgroups per CU (one when the batch is wider than 8 and the
+// kernel's registers allow no more), each taking every grid-th group of
+// tasks.  Split segments finish inside the pass, so no fixup launch follows.
 template <class D, int E>
 csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t *idx, const void *vals, const void *op,
                                 int64_t n_op, int64_t n_seg, int64_t B, void *out, const Epi &ep, hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    const unsigned grid = (unsigned)ceil_div(TL.count, kLdsWaves);
+    const int64_t ngroups = TL.nsplit + ceil_div(TL.count, kLdsWaves);
+    const int64_t cap = (int64_t)L->act.cus * (ld <= 8 ? 2 : 1);
+    const unsigned grid = (unsigned)(ngroups < cap ? ngroups : cap);
+    if (grid == 0) return CSP_OK;
     const size_t lds = (size_t)n_op * ld * L->esz;
     csp_status st = CSP_OK;
-    const bool ks = TL.nsplit == 0;  // no split segments: every task stores its output
-#define CSP_SEGL_ARGS TL.desc, TL.count, idx, (const T *)vals, (const T *)op, n_op, n_seg, B, L->act.partial, (T *)out, ep
-#define CSP_SEGL(LDV)                                                                                        \
-    if (ks) {                                                                                                \
-        if ((st = allow_lds<k_segment_lds<LDV, D, E, 1>>(lds)) == CSP_OK)                                   \
-            launch_main(L, kTimeBoth, k_segment_lds<LDV, D, E, 1>, grid, kLdsThreads, lds, s, CSP_SEGL_ARGS);                      \
-    } else if ((st = allow_lds<k_segment_lds<LDV, D, E, 0>>(lds)) == CSP_OK) {                               \
-        launch_main(L, kTimeBoth, k_segment_lds<LDV, D, E, 0>, grid, kLdsThreads, lds, s, CSP_SEGL_ARGS);                          \
-    }
+#define CSP_SEGL(LDV)                                                                                              \
+    if ((st = allow_lds<k_segment_lds<LDV, D, E>>(lds)) == CSP_OK)                                                \
+        launch_main(L, kTimeBoth, k_segment_lds<LDV, D, E>, grid, kLdsThreads, lds, s, TL.desc, TL.count, TL.split, \
+                    TL.nsplit, idx, (const T *)vals, (const T *)op, n_op, n_seg, B, (T *)out, ep)
     CSP_LD_SWITCH_LDS(ld, CSP_SEGL);
 #undef CSP_SEGL
-#undef CSP_SEGL_ARGS
     if (st != CSP_OK) return st;
     CSP_LAUNCHED("k_segment_lds");
-    return split_fixup<D, E>(L, TL, B, n_seg, out, ep, s);
+    return CSP_OK;
 }
 
 // Both gradients (or only the value gradient when with_dx is false) from
@@ -1028,7 +1088,7 @@ csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdE
 {
     csp_status st = CSP_OK;
     const Epi ep = make_epi(fe);
-    if (lds_table_fits(L, B, L->in)) {
+    if (lds_segment_fits(L, B, L->in)) {
         const TaskList &RT = L->row_tasks;
         if (L->dtype == CSP_BF16)
             return fe ? segment_lds_dispatch<BF16, kEpiForward>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s)
@@ -1049,7 +1109,7 @@ csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, co
     csp_status st = CSP_OK;
     Epi ep;
     ep.act_in = act_in;
-    if (lds_table_fits(L, B, L->out)) {
+    if (lds_segment_fits(L, B, L->out)) {
         const TaskList &CT = L->col_tasks;
         const int32_t *rc = L->rows_by_col;
         const void *vc = L->vals_c;

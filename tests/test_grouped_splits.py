@@ -1,20 +1,26 @@
-"""Split segments finished inside the segment pass (k_segment_grouped).
+"""Split segments finished inside the segment pass.
 
 A row (forward) or column (input gradient) longer than 512 entries is cut
-into tasks.  When the gathered operand takes the global-table path, B <= 8,
-and no segment can have more than 64 tasks (the other dimension is at most
-32768), one 16-wave workgroup runs all tasks of a split segment and adds
-their sums in LDS, in task order, instead of the separate fixup launch doing
-it.  The order of the additions is the fixup's, so results must be bitwise
-those of COOSPMM_GROUPED_SPLITS=0 (split-plus-fixup path), and within the
-oracle's bounds.
+into tasks.  Three paths add up the tasks of such a segment, all in task
+order:
+- the split-plus-fixup path: tasks store partial sums, a fixup launch adds
+  them (global tables, COOSPMM_GROUPED_SPLITS=0);
+- k_segment_grouped: with global tables, B <= 8 and at most 64 tasks per
+  segment (the other dimension is at most 32768), one 16-wave workgroup
+  runs all tasks of a split segment and adds their sums in LDS;
+- k_segment_lds: when the gathered operand fits an LDS table (2 <= B <= 64,
+  at most 64 KiB), the persistent small-table kernel does the same for its
+  split segments.
+Results must be bitwise equal across the three, and within the oracle's
+bounds.
 
 Cases: power-law rows and columns (many split segments of different task
 counts next to unsplit ones and empty ones), B = 1, 3 (pad slots), 8, and 16
 and 64 (above the limit: both settings take the split-plus-fixup path),
 fp32 and bf16, the epilogues (bias + GELU forward, input gradient times
 GELU'), a row of 32768 entries (exactly 64 tasks) and a layer with 32769
-columns (more than 64 tasks possible: the fixup path stays).
+columns (more than 64 tasks possible: the fixup path stays), and layers
+whose operand tables fit LDS exactly (64 KiB) with split rows or columns.
 """
 import os
 from contextlib import contextmanager
@@ -31,16 +37,17 @@ pytestmark = pytest.mark.gpu
 
 
 @contextmanager
-def grouped(on: bool):
-    old = os.environ.get("COOSPMM_GROUPED_SPLITS")
-    os.environ["COOSPMM_GROUPED_SPLITS"] = "1" if on else "0"
+def env(**kv):
+    old = {k: os.environ.get(k) for k in kv}
+    os.environ.update(kv)
     try:
         yield
     finally:
-        if old is None:
-            os.environ.pop("COOSPMM_GROUPED_SPLITS", None)
-        else:
-            os.environ["COOSPMM_GROUPED_SPLITS"] = old
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def zipf_layer(out, in_, nnz, seed, dtype, transpose=False):
@@ -73,6 +80,11 @@ CASES = [
     ("zipf_cols_b1", lambda d: zipf_layer(16384, 4096, 300000, 15, d, transpose=True), 1, "f32"),
     ("zipf_cols_b4_bf16", lambda d: zipf_layer(16384, 4096, 300000, 16, d, transpose=True), 4, "bf16"),
     ("row_of_64_tasks", lambda d: full_row_layer(8, 32768, 5000, 17, d), 1, "f32"),
+    # LDS tables: X of 16384 bf16 columns at B = 2 is exactly 64 KiB (a 32-task row); X of 4096
+    # fp32 columns at B = 4 is 64 KiB; dY of 16384 bf16 columns at B = 2 is 64 KiB (long columns)
+    ("row_of_32_tasks_lds_b2_bf16", lambda d: full_row_layer(8, 16384, 5000, 20, d), 2, "bf16"),
+    ("zipf_rows_lds_b4", lambda d: zipf_layer(1024, 4096, 150000, 21, d), 4, "f32"),
+    ("zipf_cols_lds_b2_bf16", lambda d: zipf_layer(16384, 2048, 200000, 22, d, transpose=True), 2, "bf16"),
     ("over_64_tasks_fixup", lambda d: full_row_layer(8, 32769, 5000, 18, d), 2, "f32"),
 ]
 
@@ -98,12 +110,15 @@ def test_grouped_splits_bitwise_and_oracle(orc, name, builder, B, dtype):
             r["dx_act"] = host(csp.spmm_bwd_input_act(h, dY, Hin, act="gelu"))
             return r
 
-        with grouped(True):
+        with env(COOSPMM_GROUPED_SPLITS="1", COOSPMM_LDS_TABLES="0"):
             on = run()
-        with grouped(False):
+        with env(COOSPMM_GROUPED_SPLITS="0", COOSPMM_LDS_TABLES="0"):
             off = run()
+        with env(COOSPMM_GROUPED_SPLITS="1", COOSPMM_LDS_TABLES="1"):
+            lds = run()
         for k in on:
             assert np.array_equal(on[k].view(np.uint8), off[k].view(np.uint8)), f"{k}: grouped result differs"
+            assert np.array_equal(lds[k].view(np.uint8), off[k].view(np.uint8)), f"{k}: LDS-table result differs"
         rel = BF16_REL if dtype == "bf16" else FP32_REL
         ref, S = orc.spmm_fwd(out, in_, L.rows, L.cols, L.vals, Xh)
         assert_within(on["fwd"], ref, S, rel, f"{name} forward")

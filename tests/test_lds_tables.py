@@ -3,7 +3,9 @@
 When the operand a pass gathers from is small in its batch-minor layout
 (2 <= B <= 64 and n * ld * element size <= 64 KiB, ld = B rounded up to a
 power of two), the library copies it into LDS inside the product kernel
-instead of launching the batch-minor copy and gathering from L2.  The task code and its
+instead of launching the batch-minor copy and gathering from L2 (for the
+segment passes, forward and input gradient, in a persistent grid of about
+two workgroups per CU, split segments finished in the same launch).  The task code and its
 arithmetic order are those of the global-table path, so every output must be
 bitwise the same as with COOSPMM_LDS_TABLES=0 (which forces the global
 tables).  Parity with the oracle uses the usual bounds (fp32 1e-5 * S, bf16
