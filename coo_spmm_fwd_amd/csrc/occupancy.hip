@@ -390,8 +390,8 @@ __global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint
     const int q = (int)(j & 3);
     const uint64_t uq = q == 0 ? u[0] : q == 1 ? u[1] : q == 2 ? u[2] : u[3];
     const uint64_t pq = __umul64hi(uq, npos);
-    const int64_t r = (int64_t)(pq / (uint64_t)in), c = (int64_t)pq - r * in;
-    const uint32_t p = (uint32_t)pq;
+    const uint32_t p = (uint32_t)pq;  // npos < 2^32 on the bitmap path: 32-bit division suffices
+    const int64_t r = (int64_t)(p / (uint32_t)in), c = (int64_t)p - r * in;
     const bool free_ = !((occ[r * inw + (c >> 5)] >> (c & 31)) & 1u);
     cand[j] = free_ ? p : kNoPos;
     if (!free_) return;
@@ -574,16 +574,41 @@ __global__ __launch_bounds__(kThreads) void k_bm_canon(const uint32_t *__restric
     if (cw == 0 && r <= out) row_ptr[r] = (int32_t)pos;
     if (w == nw) return;
     const uint32_t o = occ[w], oo = occ_old[w], ko = pref_old[w];
-    for (uint32_t m = o; m; m &= m - 1, ++pos) {
-        const int b = __ffs(m) - 1;
-        V v = regrow;
-        if ((oo >> b) & 1u) {
-            const uint32_t k = ko + __popc(oo & ((1u << b) - 1u));
-            if (!((pruned[k >> 6] >> (k & 63)) & 1ull)) v = vals_old[k];
+    // The word's old entries are canonical indices ko .. ko + nold - 1: their
+    // prune bits lie in at most two mask words, loaded once.
+    const uint32_t nold = (uint32_t)__popc(oo), k0 = ko & ~63u;
+    uint64_t p0 = 0, p1 = 0;
+    if (nold) {
+        p0 = pruned[ko >> 6];
+        if (((ko + nold - 1) >> 6) != (ko >> 6)) p1 = pruned[(ko >> 6) + 1];
+    }
+    // Four set bits per pass, so their value loads are in flight together.
+    constexpr int P = 4;
+    for (uint32_t m = o; m;) {
+        int b[P];
+        uint32_t k[P];
+        bool has[P], keep[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            has[j] = m != 0;
+            b[j] = has[j] ? __ffs(m) - 1 : 0;
+            m &= m - 1;
+            k[j] = ko + (uint32_t)__popc(oo & ((1u << b[j]) - 1u));
+            const uint32_t off = k[j] - k0;
+            const bool gone = off < 64 ? (p0 >> off) & 1ull : (p1 >> ((off - 64) & 63)) & 1ull;
+            keep[j] = has[j] && ((oo >> b[j]) & 1u) && !gone;
         }
-        rows[pos] = (int32_t)r;
-        cols[pos] = (int32_t)(cw * 32 + b);
-        vals[pos] = v;
+        V v[P];
+#pragma unroll
+        for (int j = 0; j < P; ++j) v[j] = keep[j] ? vals_old[k[j]] : regrow;
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            if (has[j]) {
+                rows[pos + j] = (int32_t)r;
+                cols[pos + j] = (int32_t)(cw * 32 + b[j]);
+                vals[pos + j] = v[j];
+            }
+        pos += P;  // only read again when the word had P more bits
     }
 }
 
@@ -691,29 +716,42 @@ __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restr
     }
     __syncthreads();
     const uint32_t total = total_s;
-    constexpr int U = 4;  // outputs in flight per thread (their value loads overlap)
+    // Outputs in flight per thread.  Each search step is taken for all of
+    // them together, without branches, so their LDS reads issue back to back
+    // instead of as U dependent chains.
+    constexpr int U = 4;
     for (uint32_t o0 = 0; o0 < total; o0 += kThreads * U) {
+        uint32_t o[U], q[U];
+        int c[U], b[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            o[u] = o0 + u * kThreads + t;
+            c[u] = 0;  // last column whose run starts at or before o
+            b[u] = 0;  // column word holding the q-th entry of that column
+        }
+#pragma unroll
+        for (int step = 32; step >= 1; step >>= 1)
+#pragma unroll
+            for (int u = 0; u < U; ++u) c[u] += cstart[c[u] + step] <= o[u] ? step : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) q[u] = o[u] < total ? o[u] - cstart[c[u]] : 0u;
+#pragma unroll
+        for (int step = 16; step >= 1; step >>= 1)
+#pragma unroll
+            for (int u = 0; u < U; ++u) b[u] += ccum[c[u]][b[u] + step] <= q[u] ? step : 0;
         int32_t kk[U], rr[U];
         uint32_t jj[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t o = o0 + u * kThreads + t;
-            int c = 0;  // last column whose run starts at or before o
-#pragma unroll
-            for (int step = 32; step >= 1; step >>= 1)
-                if (cstart[c + step] <= o) c += step;
-            const uint32_t q = o < total ? o - cstart[c] : 0u;
-            int b = 0;  // column word holding the q-th entry
-#pragma unroll
-            for (int step = 16; step >= 1; step >>= 1)
-                if (ccum[c][b + step] <= q) b += step;
-            const int ro = b * 32 + nth_set_bit(cw[c][b], q - ccum[c][b]);
+            const int ro = b[u] * 32 + nth_set_bit(cw[c[u]][b[u]], q[u] - ccum[c[u]][b[u]]);
             const uint2 w = rw[ro];
-            const uint32_t left = c < 32 ? (uint32_t)__popc(w.x & ((1u << c) - 1u))
-                                         : (uint32_t)__popc(w.x) + (uint32_t)__popc(w.y & ((1u << (c - 32)) - 1u));
-            kk[u] = o < total ? (int32_t)(seg[ro] + left) : -1;
+            // entries of the row left of column c within the tile's two words
+            const uint32_t below = (1u << (c[u] & 31)) - 1u;
+            const uint32_t mx = c[u] < 32 ? below : ~0u, my = c[u] < 32 ? 0u : below;
+            const uint32_t left = (uint32_t)__popc(w.x & mx) + (uint32_t)__popc(w.y & my);
+            kk[u] = o[u] < total ? (int32_t)(seg[ro] + left) : -1;
             rr[u] = (int32_t)(r0 + ro);
-            jj[u] = gout[c] + q;
+            jj[u] = gout[c[u]] + q[u];
         }
         V vv[U];
 #pragma unroll
