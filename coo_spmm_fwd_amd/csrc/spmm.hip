@@ -321,17 +321,19 @@ __device__ __attribute__((always_inline)) inline void segment_task_body(const Ta
                     v[j] = entry_f<S>(vv[u], l);
                     load_vec<VW>(op + row_off<kWide>(c, LD), x[j]);
                 }
+                // explicit fused multiply-adds, so that no path that shares
+                // this arithmetic depends on the compiler contracting them
                 if ((u + 1) * kWave <= m) {
 #pragma unroll
                     for (int j = 0; j < M::G; ++j)
 #pragma unroll
-                        for (int w = 0; w < VW; ++w) acc[w] += v[j] * x[j][w];
+                        for (int w = 0; w < VW; ++w) acc[w] = __builtin_fmaf(v[j], x[j][w], acc[w]);
                 } else {  // block holding the end of the task
 #pragma unroll
                     for (int j = 0; j < M::G; ++j) {
                         const bool ok = u * kWave + (i0 + j) * S + s < m;
 #pragma unroll
-                        for (int w = 0; w < VW; ++w) acc[w] += v[j] * (ok ? x[j][w] : 0.f);
+                        for (int w = 0; w < VW; ++w) acc[w] = __builtin_fmaf(v[j], ok ? x[j][w] : 0.f, acc[w]);
                     }
                 }
             }
