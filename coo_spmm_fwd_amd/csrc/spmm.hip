@@ -501,9 +501,9 @@ __device__ __attribute__((always_inline)) inline void values_task_body(const Tas
                     load_vec<VW>(xt + row_off<kWide>(entry_i<S>(ci[u], (i0 + j) * S + s), LD), x[j]);
 #pragma unroll
                 for (int j = 0; j < M::G; ++j) {
-                    float p = 0.f;
+                    float p = 0.f;  // fused multiply-adds in batch order
 #pragma unroll
-                    for (int w = 0; w < VW; ++w) p += dy[w] * x[j][w];
+                    for (int w = 0; w < VW; ++w) p = __builtin_fmaf(dy[w], x[j][w], p);
                     lds[(i0 + j) * S + s] = group_sum<LPE>(p);
                 }
             }
