@@ -6,6 +6,8 @@
 // with a flat key row*in + col (one LSD radix sort), so each output row is a
 // contiguous segment; a second stable sort by column of the canonical indices
 // gives the column segments.  Offsets come from a binary search per segment.
+#include <cstdlib>
+
 #include "common.h"
 #include "device_util.h"
 
@@ -72,26 +74,99 @@ __device__ __forceinline__ uint32_t seg_pieces(const int32_t *ptr, int64_t i)
     return len <= kTaskChunk ? 1u : (uint32_t)((len + kTaskChunk - 1) / kTaskChunk);
 }
 
-// Both task lists (rows, then columns) are built by the same three launches:
-// blocks [0, tiles0) work on list 0 and the rest on list 1, one segment per thread.
+// The three task lists (plain rows, plain columns, packed rows) are built by
+// the same launches: blocks [0, tiles0) work on list 0, the next tiles1 on
+// list 1 and the rest on list 2.  Lists 0 and 1 take one segment per
+// thread; list 2 takes one window of kPackSegs rows per thread.
 constexpr int kTaskThreads = 1024;
+constexpr int kLists = 3;
 
 struct TaskBuild {
-    const int32_t *ptr[2];
-    int64_t nseg[2];
-    int64_t tiles[2];
-    int4 *desc[2];
-    int4 *split[2];
-    int32_t *seg_first[2];
-    int64_t cap[2];
-    uint32_t *partials[2];  // tiles + 1 words each
-    uint32_t *counts;       // [0], [1] tasks; [2], [3] split segments
+    const int32_t *ptr[kLists];
+    int64_t nseg[kLists];
+    int64_t tiles[kLists];
+    int4 *desc[kLists];
+    int4 *split[kLists];
+    int32_t *seg_first[kLists];  // list 2: none
+    int64_t cap[kLists];
+    uint32_t *partials[kLists];  // tiles + 1 words each
+    uint32_t *counts;            // [0], [1], [6] tasks; [2], [3], [7] split segments
+    int64_t rows2;               // rows of list 2 (its nseg counts windows)
+    int32_t pack_limit;          // entries of a task of several rows, at most kPackEntries
 };
+__device__ __forceinline__ int task_count_word(int l) { return l < 2 ? l : 6; }
+__device__ __forceinline__ int split_count_word(int l) { return l < 2 ? 2 + l : 7; }
 
 __device__ __forceinline__ void task_tile(const TaskBuild &tb, int &l, int64_t &tile)
 {
-    l = (int64_t)blockIdx.x < tb.tiles[0] ? 0 : 1;
-    tile = l ? (int64_t)blockIdx.x - tb.tiles[0] : (int64_t)blockIdx.x;
+    tile = blockIdx.x;
+    l = 0;
+    while (l < kLists - 1 && tile >= tb.tiles[l]) tile -= tb.tiles[l++];
+}
+
+// Greedy packing of the rows [s0, s1) of one window, in order.  A row longer
+// than kTaskChunk closes the open task and is cut into kTaskChunk pieces (a
+// split row, as in the plain list).  Any other row joins the open task unless
+// that would take the task past pack_limit (<= kPackEntries) entries; then
+// the open task is closed first.  Empty rows join like any other (the task
+// stores their zero outputs).  Returns the number of tasks; with kEmit, also writes them from
+// descriptor f on: {first row, first entry, end entry, -(rows)} for a packed
+// task (-1: one row, as in the plain list) and {row, first entry, end entry,
+// task index} for each piece of a split row, plus the split records.
+template <bool kEmit>
+__device__ uint32_t pack_window(const TaskBuild &tb, const int32_t *ptr, int64_t s0, int64_t s1, int32_t f)
+{
+    uint32_t n = 0;
+    int64_t open = -1;
+    int32_t open_kb = 0, cnt = 0;
+    int32_t b = ptr[s0];
+    for (int64_t r = s0; r < s1; ++r) {
+        const int32_t e = ptr[r + 1], len = e - b;
+        if (len > kTaskChunk) {
+            if (cnt) {
+                if (kEmit && f + n < tb.cap[2]) tb.desc[2][f + n] = make_int4((int32_t)open, open_kb, b, -cnt);
+                ++n;
+                cnt = 0;
+            }
+            const uint32_t p = (uint32_t)((len + kTaskChunk - 1) / kTaskChunk);
+            if (kEmit) {
+                for (uint32_t j = 0; j < p && (int64_t)f + n + j < tb.cap[2]; ++j) {
+                    const int32_t kb = b + (int32_t)j * kTaskChunk;
+                    const int32_t ke = kb + kTaskChunk < e ? kb + kTaskChunk : e;
+                    tb.desc[2][f + n + j] = make_int4((int32_t)r, kb, ke, (int32_t)(f + n + j));
+                }
+                tb.split[2][atomicAdd(&tb.counts[7], 1u)] = make_int4((int32_t)r, (int32_t)(f + n), (int32_t)p, 0);
+            }
+            n += p;
+        } else {
+            if (cnt && e - open_kb > tb.pack_limit) {
+                if (kEmit && f + n < tb.cap[2]) tb.desc[2][f + n] = make_int4((int32_t)open, open_kb, b, -cnt);
+                ++n;
+                cnt = 0;
+            }
+            if (!cnt) {
+                open = r;
+                open_kb = b;
+            }
+            ++cnt;
+        }
+        b = e;
+    }
+    if (cnt) {
+        if (kEmit && f + n < tb.cap[2]) tb.desc[2][f + n] = make_int4((int32_t)open, open_kb, b, -cnt);
+        ++n;
+    }
+    return n;
+}
+
+// Tasks of work item i of list l: a segment of lists 0 and 1, a window of
+// kPackSegs rows of list 2 (nseg[2] counts windows, rows2 rows).
+__device__ __forceinline__ uint32_t item_tasks(const TaskBuild &tb, int l, int64_t i)
+{
+    if (i >= tb.nseg[l]) return 0u;
+    if (l < 2) return seg_pieces(tb.ptr[l], i);
+    const int64_t s0 = i * kPackSegs, s1 = s0 + kPackSegs < tb.rows2 ? s0 + kPackSegs : tb.rows2;
+    return pack_window<false>(tb, tb.ptr[2], s0, s1, 0);
 }
 
 __global__ __launch_bounds__(kTaskThreads) void k_tasks_count(TaskBuild tb)
@@ -102,13 +177,13 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_count(TaskBuild tb)
     task_tile(tb, l, tile);
     const int64_t i = tile * kTaskThreads + threadIdx.x;
     uint32_t total;
-    block_exclusive_scan(i < tb.nseg[l] ? seg_pieces(tb.ptr[l], i) : 0u, lds, &total);
+    block_exclusive_scan(item_tasks(tb, l, i), lds, &total);
     if (threadIdx.x == 0) tb.partials[l][tile] = total;
-    if (blockIdx.x == 0 && threadIdx.x < 2) tb.counts[2 + threadIdx.x] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < kLists) tb.counts[split_count_word(threadIdx.x)] = 0;
 }
 
-// Two blocks: block l scans the tile sums of list l in place and stores the
-// list's task count (also as seg_first[nseg]).
+// kLists blocks: block l scans the tile sums of list l in place and stores
+// the list's task count (lists 0 and 1 also as seg_first[nseg]).
 __global__ __launch_bounds__(kTaskThreads) void k_tasks_scan(TaskBuild tb)
 {
     __shared__ uint32_t lds[17];
@@ -127,8 +202,8 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_scan(TaskBuild tb)
         run += v;
     }
     if (threadIdx.x == 0) {
-        tb.counts[l] = total;
-        tb.seg_first[l][tb.nseg[l]] = (int32_t)total;
+        tb.counts[task_count_word(l)] = total;
+        if (l < 2) tb.seg_first[l][tb.nseg[l]] = (int32_t)total;
     }
 }
 
@@ -146,7 +221,7 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
     task_tile(tb, l, tile);
     const int64_t i = tile * kTaskThreads + threadIdx.x;
     const bool live = i < tb.nseg[l];
-    const uint32_t p = live ? seg_pieces(tb.ptr[l], i) : 0u;
+    const uint32_t p = item_tasks(tb, l, i);
     uint32_t before, total;
     if constexpr (kPrefix) {
         uint32_t v = 0;
@@ -157,10 +232,15 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
     }
     const int32_t f = (int32_t)(block_exclusive_scan(p, lds, &total) + before);
     if (kPrefix && tile == tb.tiles[l] - 1 && threadIdx.x == 0) {
-        tb.counts[l] = before + total;
-        tb.seg_first[l][tb.nseg[l]] = (int32_t)(before + total);
+        tb.counts[task_count_word(l)] = before + total;
+        if (l < 2) tb.seg_first[l][tb.nseg[l]] = (int32_t)(before + total);
     }
     if (!live) return;
+    if (l == 2) {
+        const int64_t s0 = i * kPackSegs, s1 = s0 + kPackSegs < tb.rows2 ? s0 + kPackSegs : tb.rows2;
+        pack_window<true>(tb, tb.ptr[2], s0, s1, f);
+        return;
+    }
     tb.seg_first[l][i] = f;
     const int32_t b = tb.ptr[l][i], e = tb.ptr[l][i + 1];
     for (int32_t j = 0; j < (int32_t)p && (int64_t)f + j < tb.cap[l]; ++j) {
@@ -173,17 +253,29 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
 
 }  // namespace
 
-// seg_first[0..nseg) = exclusive scan of the per-segment task counts,
-// seg_first[nseg] = the total; then one descriptor per task and one record
-// per split segment (their order is irrelevant: each record is self-contained).
+// Rows are packed only while the layer still has about as many tasks as the
+// device has wave slots (32 per CU): packing a layer with fewer entries per
+// slot would only lengthen each wave's chain of dependent loads.
+// COOSPMM_PACK_LIMIT overrides the entry limit (1 turns packing off).
+int32_t pack_limit(const csp_layer *L)
+{
+    int64_t lim = L->nnz / ((int64_t)(L->act.cus > 0 ? L->act.cus : 256) * 32);
+    if (const char *e = std::getenv("COOSPMM_PACK_LIMIT")) lim = std::atoll(e);
+    return (int32_t)(lim < 1 ? 1 : lim > kPackEntries ? kPackEntries : lim);
+}
+
+// Lists 0 and 1: seg_first[0..nseg) = exclusive scan of the per-segment task
+// counts, seg_first[nseg] = the total; then one descriptor per task and one
+// record per split segment (their order is irrelevant: each record is
+// self-contained).  List 2 packs windows of rows (pack_window).
 csp_status build_task_lists(csp_layer *L, hipStream_t s)
 {
     TaskBuild tb;
-    TaskList *T[2] = {&L->row_tasks, &L->col_tasks};
-    const int32_t *ptr[2] = {L->row_ptr, L->col_ptr};
-    const int64_t nseg[2] = {L->out, L->in};
+    TaskList *T[kLists] = {&L->row_tasks, &L->col_tasks, &L->row_packed};
+    const int32_t *ptr[kLists] = {L->row_ptr, L->col_ptr, L->row_ptr};
+    const int64_t nseg[kLists] = {L->out, L->in, ceil_div(L->out, kPackSegs)};
     uint32_t *part = L->ws.hist;
-    for (int l = 0; l < 2; ++l) {
+    for (int l = 0; l < kLists; ++l) {
         tb.ptr[l] = ptr[l];
         tb.nseg[l] = nseg[l];
         tb.tiles[l] = ceil_div(nseg[l], kTaskThreads);
@@ -194,14 +286,16 @@ csp_status build_task_lists(csp_layer *L, hipStream_t s)
         tb.partials[l] = part;
         part += tb.tiles[l] + 1;
     }
+    tb.rows2 = L->out;
+    tb.pack_limit = pack_limit(L);
     tb.counts = L->ws.sel + kSelCounts;
-    const unsigned grid = (unsigned)(tb.tiles[0] + tb.tiles[1]);
+    const unsigned grid = (unsigned)(tb.tiles[0] + tb.tiles[1] + tb.tiles[2]);
     k_tasks_count<<<grid, kTaskThreads, 0, s>>>(tb);
     CSP_LAUNCHED("k_tasks_count");
-    if (tb.tiles[0] <= kPrefixTaskTiles && tb.tiles[1] <= kPrefixTaskTiles) {
+    if (tb.tiles[0] <= kPrefixTaskTiles && tb.tiles[1] <= kPrefixTaskTiles && tb.tiles[2] <= kPrefixTaskTiles) {
         k_tasks_emit<true><<<grid, kTaskThreads, 0, s>>>(tb);
     } else {
-        k_tasks_scan<<<2, kTaskThreads, 0, s>>>(tb);
+        k_tasks_scan<<<kLists, kTaskThreads, 0, s>>>(tb);
         CSP_LAUNCHED("k_tasks_scan");
         k_tasks_emit<false><<<grid, kTaskThreads, 0, s>>>(tb);
     }
@@ -215,6 +309,11 @@ csp_status set_task_counts(csp_layer *L, const uint32_t *counts)
     L->col_tasks.count = counts[1];
     L->row_tasks.nsplit = counts[2];
     L->col_tasks.nsplit = counts[3];
+    L->row_packed.count = counts[6];
+    L->row_packed.nsplit = counts[7];
+    if (L->row_packed.count > L->row_packed.cap)
+        return set_error(CSP_ERR_HIP, "packed task list overflow (%lld/%lld)", (long long)L->row_packed.count,
+                         (long long)L->row_packed.cap);
     if (L->row_tasks.count > L->row_tasks.cap || L->col_tasks.count > L->col_tasks.cap)
         return set_error(CSP_ERR_HIP, "task list overflow (%lld/%lld, %lld/%lld)", (long long)L->row_tasks.count,
                          (long long)L->row_tasks.cap, (long long)L->col_tasks.count, (long long)L->col_tasks.cap);
@@ -257,7 +356,7 @@ csp_status build_index(csp_layer *L, hipStream_t s)
 
     st = build_task_lists(L, s);
     if (st != CSP_OK) return st;
-    uint32_t counts[4] = {0, 0, 0, 0};
+    uint32_t counts[kSelCountWords] = {};
     CSP_HIP(hipMemcpyAsync(counts, L->ws.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));
     CSP_HIP(hipStreamSynchronize(s));
     return set_task_counts(L, counts);

@@ -73,10 +73,21 @@ struct ActBuffer {
 // results do not depend on scheduling and no cross-wave fence is needed.
 constexpr int kTaskChunk = 512;
 
+// Packed row list (forward passes at batch widths of at most 4, one entry
+// per lane).  Consecutive whole rows of at most kTaskChunk entries each are
+// packed into one task, up to kPackEntries entries and at most the kPackSegs
+// rows of one aligned row window; rows longer than kTaskChunk are split as
+// in the plain list.  kPackEntries leaves room for the 8-entry alignment of
+// the window the packed task body loads (kb rounded down to a multiple of 8).
+constexpr int kPackSegs = 64;
+constexpr int kPackEntries = kTaskChunk - 7;
+
 // Layout of the small state buffer Workspace::sel (uint32 words).
 constexpr int kSelAllocWords = 16384;
 constexpr int kSelCounts = 12288;  // [0] row tasks, [1] column tasks, [2] split rows, [3] split columns,
-                                   // [4] regrown positions taken, [5] the same before the current batch
+                                   // [4] regrown positions taken, [5] the same before the current batch,
+                                   // [6] packed row tasks, [7] split rows of the packed list
+constexpr int kSelCountWords = 8;  // words read back after a task-list build
 
 struct TaskList {
     int4 *desc = nullptr;   // [cap] {segment, first entry, end entry, partial slot or -1}
@@ -100,6 +111,7 @@ struct csp_layer {
     int32_t *perm_c = nullptr, *rows_by_col = nullptr, *col_ptr = nullptr;
     void *vals_c = nullptr;  // values in transposed (col, row) order: vals_c[j] = vals[perm_c[j]]
     csp::TaskList row_tasks, col_tasks;
+    csp::TaskList row_packed;  // whole rows packed per task (forward at B <= 4); seg_first unused
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request
@@ -161,10 +173,13 @@ csp_status build_canonical(csp_layer *L, const int32_t *rows, const int32_t *col
 // Rebuilds row_ptr, perm_c, rows_by_col, col_ptr, vals_c and both task lists
 // from the canonical arrays.  Synchronizes on s (reads back the task counts).
 csp_status build_index(csp_layer *L, hipStream_t s);
-// Both task lists from row_ptr / col_ptr (three launches, no host sync); the
-// counts land in sel[kSelCounts + 0..3] for set_task_counts.
+// The three task lists from row_ptr / col_ptr (plain rows, plain columns,
+// packed rows; two or three launches, no host sync); the counts land in
+// sel[kSelCounts + 0..3, 6..7] for set_task_counts.
 csp_status build_task_lists(csp_layer *L, hipStream_t s);
-// Takes the counts read back from sel[kSelCounts + 0..3]; checks the capacities.
+// Entry limit of a packed task of several rows for this layer.
+int32_t pack_limit(const csp_layer *L);
+// Takes the kSelCountWords counts read back from sel[kSelCounts]; checks the capacities.
 csp_status set_task_counts(csp_layer *L, const uint32_t *counts);
 // vals_c[j] = vals[perm_c[j]] after the canonical values changed.
 csp_status refresh_column_values(csp_layer *L, hipStream_t s);

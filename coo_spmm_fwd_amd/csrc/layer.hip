@@ -71,7 +71,8 @@ void free_layer(csp_layer *L)
                     L->ws.occ, L->ws.occ_next, L->ws.occ_pref, L->ws.occ_pref_next, L->ws.tcnt, L->ws.hash, L->ws.score,
                     L->act.a, L->act.b, L->act.partial,
                     L->row_tasks.desc, L->row_tasks.split, L->row_tasks.seg_first,
-                    L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first};
+                    L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first,
+                    L->row_packed.desc, L->row_packed.split};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete L;
@@ -80,17 +81,22 @@ void free_layer(csp_layer *L)
 csp_status alloc_layer(csp_layer *L)
 {
     const int64_t nnz = L->nnz, out = L->out, in = L->in;
-    const size_t n = (size_t)(nnz > 0 ? nnz : 1);
+    // Entry arrays carry 8 spare elements: the packed forward loads whole
+    // 8-entry groups, and the last group of a layer may reach 7 past its end.
+    const size_t n = (size_t)nnz + 8;
     Workspace &W = L->ws;
     W.nkey_cap = nnz > 65536 ? nnz : 65536;
     W.hist_words = sort_hist_words(W.nkey_cap);
     const int64_t nseg_max = out > in ? out : in;
-    if (W.hist_words < (size_t)(2 * ceil_div(nseg_max, 1024) + 64)) W.hist_words = (size_t)(2 * ceil_div(nseg_max, 1024) + 64);
+    // scan partials of the three task lists
+    const size_t task_words = (size_t)(2 * ceil_div(nseg_max, 1024) + ceil_div(out, 1024 * (int64_t)kPackSegs) + 64);
+    if (W.hist_words < task_words) W.hist_words = task_words;
     const bool bitmap = plan_bitmap(L);
     if (bitmap && W.hist_words < bitmap_hist_words(L)) W.hist_words = bitmap_hist_words(L);
     const size_t cap = (size_t)W.nkey_cap;
     L->row_tasks.cap = task_cap(out, nnz);
     L->col_tasks.cap = task_cap(in, nnz);
+    L->row_packed.cap = L->row_tasks.cap;  // packing only merges whole-row tasks
     const size_t act_bytes = (size_t)L->esz * kSliceRows * (size_t)nseg_max;
     const size_t tcap = (size_t)(L->row_tasks.cap > L->col_tasks.cap ? L->row_tasks.cap : L->col_tasks.cap);
     const size_t partial_bytes = sizeof(float) * kSliceRows * tcap;
@@ -126,6 +132,8 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&L->col_tasks.desc, 16 * (size_t)L->col_tasks.cap, "column tasks"},
         {(void **)&L->col_tasks.split, 16 * (size_t)in, "split columns"},
         {(void **)&L->col_tasks.seg_first, 4 * (size_t)(in + 1), "column task offsets"},
+        {(void **)&L->row_packed.desc, 16 * (size_t)L->row_packed.cap, "packed row tasks"},
+        {(void **)&L->row_packed.split, 16 * (size_t)out, "split rows (packed list)"},
         // batch-minor operand copies for one slice of up to 64 batch rows, and the split partial sums
         {&L->act.a, act_bytes, "operand copy"},
         {&L->act.b, act_bytes, "operand copy"},

@@ -844,7 +844,7 @@ struct BitmapRun {
         CSP_LAUNCHED("k_bm_tgather");
         st = build_task_lists(L, s);
         if (st != CSP_OK) return st;
-        uint32_t counts[6] = {0, 0, 0, 0, 0, 0};
+        uint32_t counts[kSelCountWords] = {};
         CSP_HIP(hipMemcpyAsync(counts, W.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));
         CSP_HIP(hipStreamSynchronize(s));
         nacc = counts[4];

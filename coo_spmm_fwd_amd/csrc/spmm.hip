@@ -363,9 +363,161 @@ __device__ __attribute__((always_inline)) inline void segment_task(const int4 *_
     segment_task_body<LD, D, kWide, E, kStore>(load_task(desc, t), idx, vals, opT, n_op, n_seg, B, partial, out, ep);
 }
 
+// ---------------------------------------------- packed rows (B <= 4)
+// One task of whole segments seg .. seg + nseg - 1 (nseg = -slot >= 2),
+// holding the entries [kb, kb + n), n <= kPackEntries, of a narrow batch
+// (LD <= 4: one entry per lane, its LD batch values in registers).  The wave
+// covers the 512-entry window that starts at kb rounded down to a multiple of
+// 8; lane l takes its eight consecutive entries with vector loads and gathers
+// their operand rows together.  A byte per window entry in LDS marks the
+// first entry of each non-empty segment (bit 7) and the last one (segment
+// number + 1 in bits 0-6); lane j < nseg sets the marks of segment j.  Each
+// lane then adds its entries with fused multiply-adds, restarting at every
+// first entry: the sum of a segment that starts and ends in the lane is
+// final; the lane's leading part and its trailing sum go through one
+// segmented scan over the lanes, which gives each lane the sum of the
+// segment's earlier entries (carry).  Final sums are put in LDS by segment
+// (over the marks, which are read by then), and lane j finishes segment j:
+// epilogue and store, zero for an empty one.  The addition order is fixed by
+// the task list, so results are repeatable, but it differs from the
+// one-segment task body's.
+template <int LD, class D, bool kWide, int E, int NW>
+__device__ __attribute__((always_inline)) inline void packed_task_body(const Task &T, const int32_t *__restrict__ seg_ptr,
+                                    const int32_t *__restrict__ idx, const typename D::T *__restrict__ vals,
+                                    const typename D::T *__restrict__ opT, int64_t n_seg, int64_t B,
+                                    typename D::T *__restrict__ out, const Epi &ep)
+{
+    static_assert(LD <= 4, "one entry per lane");
+    constexpr int VW = LD;
+    using Tv = typename D::T;
+    // Per wave: 64 x 8 mark bytes, later 64 x VW sums (at least 512 bytes).
+    __shared__ float pk_w[NW][kWave * (VW < 2 ? 2 : VW)];
+    const int lane = threadIdx.x & 63;
+    float *res = pk_w[threadIdx.x >> 6];
+    uint2 *marks2 = reinterpret_cast<uint2 *>(res);
+    uint8_t *marks = reinterpret_cast<uint8_t *>(res);
+    const int32_t nseg = -T.slot, kb = T.kb, ke = T.kb + T.n;
+    const int32_t a0 = kb & ~7, g0 = a0 + lane * 8;
+    // The window's entries, clamped to the first group when the lane's group
+    // holds none of the task (every load stays inside the padded entry arrays).
+    const bool any = g0 < ke && g0 + 8 > kb;
+    const int32_t g = any ? g0 : a0;
+    marks2[lane] = make_uint2(0u, 0u);
+    const int32_t sb = seg_ptr[T.seg + (lane < nseg ? lane : nseg)];
+    const int32_t se = seg_ptr[T.seg + (lane < nseg ? lane + 1 : nseg)];
+    int32_t ci[8];
+    float vv[8];
+    {
+        const int4 i0 = *reinterpret_cast<const int4 *>(idx + g), i1 = *reinterpret_cast<const int4 *>(idx + g + 4);
+        ci[0] = i0.x; ci[1] = i0.y; ci[2] = i0.z; ci[3] = i0.w;
+        ci[4] = i1.x; ci[5] = i1.y; ci[6] = i1.z; ci[7] = i1.w;
+        if constexpr (sizeof(Tv) == 4) {
+            const float4 v0 = *reinterpret_cast<const float4 *>(vals + g),
+                         v1 = *reinterpret_cast<const float4 *>(vals + g + 4);
+            vv[0] = v0.x; vv[1] = v0.y; vv[2] = v0.z; vv[3] = v0.w;
+            vv[4] = v1.x; vv[5] = v1.y; vv[6] = v1.z; vv[7] = v1.w;
+        } else {
+            const uint4 v = *reinterpret_cast<const uint4 *>(vals + g);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                vv[2 * k] = __uint_as_float(w4[k] << 16);
+                vv[2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+            }
+        }
+    }
+    bool ok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        ok[i] = g0 + i >= kb && g0 + i < ke;
+        if (!ok[i]) ci[i] = 0;
+    }
+    float x[8][VW];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_vec<VW>(opT + row_off<kWide>(ci[i], LD), x[i]);
+    // marks (the clearing stores above come first in this wave's LDS order)
+    if (lane < nseg && se > sb) {
+        const int32_t rs = sb - a0, re = se - 1 - a0;
+        if (rs == re) {
+            marks[rs] = (uint8_t)(0x80 | (lane + 1));
+        } else {
+            marks[rs] = 0x80;
+            marks[re] = (uint8_t)(lane + 1);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint2 mk = marks2[lane];
+    __builtin_amdgcn_wave_barrier();  // every lane's marks are read before sums overwrite them
+    auto put = [&](uint32_t j, const float (&v)[VW]) {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) res[j * VW + w] = v[w];
+    };
+    float r[VW], lead[VW];
+#pragma unroll
+    for (int w = 0; w < VW; ++w) r[w] = lead[w] = 0.f;
+    bool seen = false;
+    int32_t lead_end = -1;  // segment whose last entry ends the lane's leading part
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t m = ((i < 4 ? mk.x : mk.y) >> (8 * (i & 3))) & 0xFFu;
+        if (m & 0x80u) {
+            if (!seen) {
+#pragma unroll
+                for (int w = 0; w < VW; ++w) lead[w] = r[w];
+            }
+            seen = true;
+#pragma unroll
+            for (int w = 0; w < VW; ++w) r[w] = 0.f;
+        }
+#pragma unroll
+        for (int w = 0; w < VW; ++w) r[w] = ok[i] ? __builtin_fmaf(vv[i], x[i][w], r[w]) : r[w];
+        if (m & 0x7Fu) {
+            if (seen) put((m & 0x7Fu) - 1, r);
+            else lead_end = (int32_t)(m & 0x7Fu) - 1;
+        }
+    }
+    if (!seen) {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) lead[w] = r[w];
+    }
+    // Segmented inclusive scan of the trailing sums r over the lanes: a lane
+    // adds the lanes back to the last one that holds a segment start.
+    const uint64_t heads = __ballot(seen);
+    const uint64_t upto = heads & (lane == 63 ? ~0ull : ((2ull << lane) - 1ull));
+    const int st = upto ? 63 - __builtin_clzll(upto) : 0;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) {
+            const float y = __shfl_up(r[w], d, kWave);
+            if (lane - d >= st) r[w] += y;
+        }
+    }
+    float carry[VW];  // the segment's sum over the lanes before this one
+#pragma unroll
+    for (int w = 0; w < VW; ++w) carry[w] = __shfl_up(r[w], 1, kWave);
+    if (lead_end >= 0) {
+        float f[VW];
+#pragma unroll
+        for (int w = 0; w < VW; ++w) f[w] = carry[w] + lead[w];
+        put((uint32_t)lead_end, f);
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < nseg) {
+        const bool has = se > sb;
+#pragma unroll
+        for (int w = 0; w < VW; ++w) {
+            const float y = has ? res[lane * VW + w] : 0.f;
+            if (w < B) out[(int64_t)w * n_seg + T.seg + lane] = finish_out<E, D>(y, w, T.seg + lane, n_seg, ep);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();  // sums read before the next task clears the marks
+}
+
 // kStore = 1 when the list has no split segments (every task stores its output).
 template <int LD, class D, bool kWide, int E, int kStore>
 __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
+                                                      const int32_t *__restrict__ seg_ptr,
                                                       const int32_t *__restrict__ idx,
                                                       const typename D::T *__restrict__ vals,
                                                       const typename D::T *__restrict__ opT, int64_t n_op,
@@ -375,7 +527,14 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
 {
     const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
     if (t >= ntasks) return;
-    segment_task<LD, D, kWide, E, kStore>(desc, t, idx, vals, opT, n_op, n_seg, B, partial, out, ep);
+    const Task T = load_task(desc, t);
+    if constexpr (LD <= 4) {
+        if (T.slot < -1) {
+            packed_task_body<LD, D, kWide, E, 4>(T, seg_ptr, idx, vals, opT, n_seg, B, out, ep);
+            return;
+        }
+    }
+    segment_task_body<LD, D, kWide, E, kStore>(T, idx, vals, opT, n_op, n_seg, B, partial, out, ep);
 }
 
 // Segment pass with split segments finished in the kernel (one batch chunk,
@@ -392,8 +551,9 @@ constexpr int kGroupMaxTasks = 64;
 template <int LD, class D, bool kWide, int E>
 __global__ __launch_bounds__(kGroupWaves * kWave) void k_segment_grouped(
     const int4 *__restrict__ desc, int64_t ntasks, const int4 *__restrict__ split, int64_t nsplit,
-    const int32_t *__restrict__ idx, const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT,
-    int64_t n_op, int64_t n_seg, int64_t B, typename D::T *__restrict__ out, Epi ep)
+    const int32_t *__restrict__ seg_ptr, const int32_t *__restrict__ idx, const typename D::T *__restrict__ vals,
+    const typename D::T *__restrict__ opT, int64_t n_op, int64_t n_seg, int64_t B, typename D::T *__restrict__ out,
+    Epi ep)
 {
     __shared__ float part[kGroupMaxTasks][LD];
     const int wave = threadIdx.x >> 6;
@@ -419,6 +579,12 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void k_segment_grouped(
     if (t >= ntasks) return;
     const Task T = load_task(desc, t);
     if (T.slot >= 0) return;  // part of a split segment: finished by its own workgroup
+    if constexpr (LD <= 4) {
+        if (T.slot < -1) {
+            packed_task_body<LD, D, kWide, E, kGroupWaves>(T, seg_ptr, idx, vals, opT, n_seg, B, out, ep);
+            return;
+        }
+    }
     segment_task_body<LD, D, kWide, E, 1>(T, idx, vals, opT, n_op, n_seg, B, nullptr, out, ep);
 }
 
@@ -655,6 +821,7 @@ __device__ inline void fill_table(const typename D::T *__restrict__ src, int64_t
 template <int LD, class D, int E>
 __global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restrict__ desc, int64_t ntasks,
                                                              const int4 *__restrict__ split, int64_t nsplit,
+                                                             const int32_t *__restrict__ seg_ptr,
                                                              const int32_t *__restrict__ idx,
                                                              const typename D::T *__restrict__ vals,
                                                              const typename D::T *__restrict__ op, int64_t n_op,
@@ -694,7 +861,10 @@ __global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restr
     for (; t < ntasks; t += nw) {
         const int4 dn = desc[t + nw < ntasks ? t + nw : t];
         const Task T{uniform(d.x), uniform(d.y), uniform(d.z) - uniform(d.y), uniform(d.w)};
-        if (T.slot < 0) segment_task_body<LD, D, false, E, 1>(T, idx, vals, tab, n_op, n_seg, B, nullptr, out, ep);
+        if constexpr (LD <= 4) {
+            if (T.slot < -1) packed_task_body<LD, D, false, E, kLdsWaves>(T, seg_ptr, idx, vals, tab, n_seg, B, out, ep);
+        }
+        if (T.slot == -1) segment_task_body<LD, D, false, E, 1>(T, idx, vals, tab, n_op, n_seg, B, nullptr, out, ep);
         d = dn;
     }
 }
@@ -871,8 +1041,9 @@ csp_status allow_lds(size_t)
 // kernel's registers allow no more), each taking every grid-th group of
 // tasks.  Split segments finish inside the pass, so no fixup launch follows.
 template <class D, int E>
-csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t *idx, const void *vals, const void *op,
-                                int64_t n_op, int64_t n_seg, int64_t B, void *out, const Epi &ep, hipStream_t s)
+csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t *seg_ptr, const int32_t *idx,
+                                const void *vals, const void *op, int64_t n_op, int64_t n_seg, int64_t B, void *out,
+                                const Epi &ep, hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
@@ -885,7 +1056,7 @@ csp_status segment_lds_dispatch(csp_layer *L, const TaskList &TL, const int32_t 
 #define CSP_SEGL(LDV)                                                                                              \
     if ((st = allow_lds<k_segment_lds<LDV, D, E>>(lds)) == CSP_OK)                                                \
         launch_main(L, kTimeBoth, k_segment_lds<LDV, D, E>, grid, kLdsThreads, lds, s, TL.desc, TL.count, TL.split, \
-                    TL.nsplit, idx, (const T *)vals, (const T *)op, n_op, n_seg, B, (T *)out, ep)
+                    TL.nsplit, seg_ptr, idx, (const T *)vals, (const T *)op, n_op, n_seg, B, (T *)out, ep)
     CSP_LD_SWITCH_LDS(ld, CSP_SEGL);
 #undef CSP_SEGL
     if (st != CSP_OK) return st;
@@ -929,6 +1100,16 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
     return with_dx ? split_fixup<D, E>(L, CT, B, L->in, dX, ep, s) : CSP_OK;
 }
 
+// The forward's task list: the packed one when a lane holds one entry
+// (B <= 4), where a task of one short row would leave most lanes idle.
+// COOSPMM_PACKED=0 keeps the plain list.
+inline const TaskList &fwd_tasks(const csp_layer *L, int64_t B)
+{
+    if (pow2_ld(B) > 4) return L->row_tasks;
+    const char *e = std::getenv("COOSPMM_PACKED");
+    return e && e[0] == '0' ? L->row_tasks : L->row_packed;
+}
+
 // Split segments finished inside the segment pass (k_segment_grouped) when
 // there are any, B <= 8, and no segment can have more than kGroupMaxTasks
 // tasks (its length is at most max_len, the other dimension).  Up to B = 8
@@ -945,15 +1126,16 @@ inline bool grouped_splits(const TaskList &TL, int64_t B, int64_t max_len, int64
 }
 
 template <class D, int E>
-csp_status grouped_dispatch(csp_layer *L, const TaskList &TL, const int32_t *idx, const void *vals, const void *opT,
-                            int64_t n_op, int64_t n_seg, int64_t B, void *out, const Epi &ep, hipStream_t s)
+csp_status grouped_dispatch(csp_layer *L, const TaskList &TL, const int32_t *seg_ptr, const int32_t *idx,
+                            const void *vals, const void *opT, int64_t n_op, int64_t n_seg, int64_t B, void *out,
+                            const Epi &ep, hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
     const unsigned grid = (unsigned)(TL.nsplit + ceil_div(TL.count, kGroupWaves));
 #define CSP_GRP(LDV)                                                                                            \
     launch_main(L, kTimeBoth, k_segment_grouped<LDV, D, false, E>, grid, kGroupWaves * kWave, 0, s,                                    \
-        TL.desc, TL.count, TL.split, TL.nsplit, idx, (const T *)vals, (const T *)opT, n_op, n_seg, B, (T *)out, ep)
+        TL.desc, TL.count, TL.split, TL.nsplit, seg_ptr, idx, (const T *)vals, (const T *)opT, n_op, n_seg, B, (T *)out, ep)
     CSP_LD_SWITCH_LDS(ld, CSP_GRP);
 #undef CSP_GRP
     CSP_LAUNCHED("k_segment_grouped");
@@ -965,13 +1147,13 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    const TaskList &TL = L->row_tasks;
+    const TaskList &TL = fwd_tasks(L, B);
     if (grouped_splits(TL, B, L->in, L->in))
-        return grouped_dispatch<D, E>(L, TL, L->cols, L->vals, XT, L->in, L->out, B, Y, ep, s);
+        return grouped_dispatch<D, E>(L, TL, L->row_ptr, L->cols, L->vals, XT, L->in, L->out, B, Y, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     const bool ks = TL.nsplit == 0;
 #define CSP_FWD_ARGS \
-    TL.desc, TL.count, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, L->act.partial, (T *)Y, ep
+    TL.desc, TL.count, L->row_ptr, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, L->act.partial, (T *)Y, ep
 #define CSP_FWD(LDV, W)                                                             \
     if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_FWD_ARGS);    \
     else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_FWD_ARGS)
@@ -989,11 +1171,11 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
     const int ld = pow2_ld(B);
     const TaskList &TL = L->col_tasks;
     if (grouped_splits(TL, B, L->out, L->out))
-        return grouped_dispatch<D, E>(L, TL, L->rows_by_col, L->vals_c, dYT, L->out, L->in, B, dX, ep, s);
+        return grouped_dispatch<D, E>(L, TL, L->col_ptr, L->rows_by_col, L->vals_c, dYT, L->out, L->in, B, dX, ep, s);
     const unsigned grid = (unsigned)ceil_div(TL.count, 4);
     const bool ks = TL.nsplit == 0;
 #define CSP_DX_ARGS                                                                                                 \
-    TL.desc, TL.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
+    TL.desc, TL.count, L->col_ptr, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX(LDV, W)                                                            \
     if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_DX_ARGS);   \
@@ -1041,7 +1223,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         const int m1 = gw > 0 ? kTimeStart : kTimeBoth;  // the value-gradient kernel carries the end
         const bool ks = CT.nsplit == 0;
 #define CSP_DX2_ARGS                                                                                                \
-    CT.desc, CT.count, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
+    CT.desc, CT.count, L->col_ptr, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX2(LDV, W)                                                         \
     if (ks) launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 1>, gx, 256, 0, s, CSP_DX2_ARGS);  \
@@ -1091,12 +1273,14 @@ csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdE
     csp_status st = CSP_OK;
     const Epi ep = make_epi(fe);
     if (lds_segment_fits(L, B, L->in)) {
-        const TaskList &RT = L->row_tasks;
+        const TaskList &RT = fwd_tasks(L, B);
+        const int32_t *rp = L->row_ptr, *ci = L->cols;
+        const void *v = L->vals;
         if (L->dtype == CSP_BF16)
-            return fe ? segment_lds_dispatch<BF16, kEpiForward>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s)
-                      : segment_lds_dispatch<BF16, kEpiNone>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s);
-        return fe ? segment_lds_dispatch<F32, kEpiForward>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s)
-                  : segment_lds_dispatch<F32, kEpiNone>(L, RT, L->cols, L->vals, X, L->in, L->out, B, Y, ep, s);
+            return fe ? segment_lds_dispatch<BF16, kEpiForward>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s)
+                      : segment_lds_dispatch<BF16, kEpiNone>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s);
+        return fe ? segment_lds_dispatch<F32, kEpiForward>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s)
+                  : segment_lds_dispatch<F32, kEpiNone>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s);
     }
     st = batch_minor(L, B, X, L->in, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
@@ -1113,13 +1297,13 @@ csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, co
     ep.act_in = act_in;
     if (lds_segment_fits(L, B, L->out)) {
         const TaskList &CT = L->col_tasks;
-        const int32_t *rc = L->rows_by_col;
+        const int32_t *cp = L->col_ptr, *rc = L->rows_by_col;
         const void *vc = L->vals_c;
         if (L->dtype == CSP_BF16)
-            return act_in ? segment_lds_dispatch<BF16, kEpiActGrad>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s)
-                          : segment_lds_dispatch<BF16, kEpiNone>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s);
-        return act_in ? segment_lds_dispatch<F32, kEpiActGrad>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s)
-                      : segment_lds_dispatch<F32, kEpiNone>(L, CT, rc, vc, dY, L->out, L->in, B, dX, ep, s);
+            return act_in ? segment_lds_dispatch<BF16, kEpiActGrad>(L, CT, cp, rc, vc, dY, L->out, L->in, B, dX, ep, s)
+                          : segment_lds_dispatch<BF16, kEpiNone>(L, CT, cp, rc, vc, dY, L->out, L->in, B, dX, ep, s);
+        return act_in ? segment_lds_dispatch<F32, kEpiActGrad>(L, CT, cp, rc, vc, dY, L->out, L->in, B, dX, ep, s)
+                      : segment_lds_dispatch<F32, kEpiNone>(L, CT, cp, rc, vc, dY, L->out, L->in, B, dX, ep, s);
     }
     st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
