@@ -87,6 +87,8 @@ struct TaskBuild {
     int64_t tiles[kLists];
     int4 *desc[kLists];
     int4 *split[kLists];
+    int4 *split_cls[kLists];     // class c at c * cls_stride
+    int64_t cls_stride[kLists];
     int32_t *seg_first[kLists];  // list 2: none
     int64_t cap[kLists];
     uint32_t *partials[kLists];  // tiles + 1 words each
@@ -96,6 +98,15 @@ struct TaskBuild {
 };
 __device__ __forceinline__ int task_count_word(int l) { return l < 2 ? l : 6; }
 __device__ __forceinline__ int split_count_word(int l) { return l < 2 ? 2 + l : 7; }
+
+// One split segment's record, in the list's split array and in its class.
+__device__ __forceinline__ void emit_split(const TaskBuild &tb, int l, int4 rec, uint32_t p)
+{
+    tb.split[l][atomicAdd(&tb.counts[split_count_word(l)], 1u)] = rec;
+    const int c = split_class(p);
+    const uint32_t k = atomicAdd(&tb.counts[kSelClassWords + kSplitClasses * l + c], 1u);
+    tb.split_cls[l][c * tb.cls_stride[l] + k] = rec;
+}
 
 __device__ __forceinline__ void task_tile(const TaskBuild &tb, int &l, int64_t &tile)
 {
@@ -135,7 +146,7 @@ __device__ uint32_t pack_window(const TaskBuild &tb, const int32_t *ptr, int64_t
                     const int32_t ke = kb + kTaskChunk < e ? kb + kTaskChunk : e;
                     tb.desc[2][f + n + j] = make_int4((int32_t)r, kb, ke, (int32_t)(f + n + j));
                 }
-                tb.split[2][atomicAdd(&tb.counts[7], 1u)] = make_int4((int32_t)r, (int32_t)(f + n), (int32_t)p, 0);
+                emit_split(tb, 2, make_int4((int32_t)r, (int32_t)(f + n), (int32_t)p, 0), p);
             }
             n += p;
         } else {
@@ -180,6 +191,7 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_count(TaskBuild tb)
     block_exclusive_scan(item_tasks(tb, l, i), lds, &total);
     if (threadIdx.x == 0) tb.partials[l][tile] = total;
     if (blockIdx.x == 0 && threadIdx.x < kLists) tb.counts[split_count_word(threadIdx.x)] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < kLists * kSplitClasses) tb.counts[kSelClassWords + threadIdx.x] = 0;
 }
 
 // kLists blocks: block l scans the tile sums of list l in place and stores
@@ -248,7 +260,7 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
         const int32_t ke = kb + kTaskChunk < e ? kb + kTaskChunk : e;
         tb.desc[l][f + j] = make_int4((int32_t)i, kb, ke, p > 1 ? f + j : -1);
     }
-    if (p > 1) tb.split[l][atomicAdd(&tb.counts[2 + l], 1u)] = make_int4((int32_t)i, f, (int32_t)p, 0);
+    if (p > 1) emit_split(tb, l, make_int4((int32_t)i, f, (int32_t)p, 0), p);
 }
 
 }  // namespace
@@ -281,6 +293,8 @@ csp_status build_task_lists(csp_layer *L, hipStream_t s)
         tb.tiles[l] = ceil_div(nseg[l], kTaskThreads);
         tb.desc[l] = T[l]->desc;
         tb.split[l] = T[l]->split;
+        tb.split_cls[l] = T[l]->split_cls;
+        tb.cls_stride[l] = l == 1 ? L->in : L->out;
         tb.seg_first[l] = T[l]->seg_first;
         tb.cap[l] = T[l]->cap;
         tb.partials[l] = part;
@@ -311,6 +325,9 @@ csp_status set_task_counts(csp_layer *L, const uint32_t *counts)
     L->col_tasks.nsplit = counts[3];
     L->row_packed.count = counts[6];
     L->row_packed.nsplit = counts[7];
+    TaskList *T[3] = {&L->row_tasks, &L->col_tasks, &L->row_packed};
+    for (int l = 0; l < 3; ++l)
+        for (int c = 0; c < kSplitClasses; ++c) T[l]->ncls[c] = counts[kSelClassWords + kSplitClasses * l + c];
     if (L->row_packed.count > L->row_packed.cap)
         return set_error(CSP_ERR_HIP, "packed task list overflow (%lld/%lld)", (long long)L->row_packed.count,
                          (long long)L->row_packed.cap);

@@ -86,12 +86,23 @@ constexpr int kPackEntries = kTaskChunk - 7;
 constexpr int kSelAllocWords = 16384;
 constexpr int kSelCounts = 12288;  // [0] row tasks, [1] column tasks, [2] split rows, [3] split columns,
                                    // [4] regrown positions taken, [5] the same before the current batch,
-                                   // [6] packed row tasks, [7] split rows of the packed list
-constexpr int kSelCountWords = 8;  // words read back after a task-list build
+                                   // [6] packed row tasks, [7] split rows of the packed list,
+                                   // [8 + 4 l + c] split segments of list l (rows, columns,
+                                   // packed rows) in size class c
+constexpr int kSplitClasses = 4;
+constexpr int kSelClassWords = 8;
+constexpr int kSelCountWords = kSelClassWords + 3 * kSplitClasses;  // words read back after a build
+
+// Split segments are also kept by size class (their task count p): class 0
+// p > 8, class 1 5..8, class 2 3..4, class 3 p = 2, so that one 16-wave
+// workgroup can finish 1, 2, 4 or 8 of them (kGroupWaves >> c waves each).
+__host__ __device__ inline int split_class(uint32_t p) { return p > 8 ? 0 : p > 4 ? 1 : p > 2 ? 2 : 3; }
 
 struct TaskList {
     int4 *desc = nullptr;   // [cap] {segment, first entry, end entry, partial slot or -1}
     int4 *split = nullptr;  // [nseg] {segment, first task, task count, 0} of split segments
+    int4 *split_cls = nullptr;  // [kSplitClasses][nseg] the same records by size class
+    int64_t ncls[kSplitClasses] = {};  // records per class
     int32_t *seg_first = nullptr;  // [nseg + 1] first task of each segment
     int64_t count = 0;      // tasks in use
     int64_t nsplit = 0;     // split segments in use

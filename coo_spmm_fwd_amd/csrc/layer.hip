@@ -72,7 +72,8 @@ void free_layer(csp_layer *L)
                     L->act.a, L->act.b, L->act.partial,
                     L->row_tasks.desc, L->row_tasks.split, L->row_tasks.seg_first,
                     L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first,
-                    L->row_packed.desc, L->row_packed.split};
+                    L->row_packed.desc, L->row_packed.split,
+                    L->row_tasks.split_cls, L->col_tasks.split_cls, L->row_packed.split_cls};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete L;
@@ -134,6 +135,9 @@ csp_status alloc_layer(csp_layer *L)
         {(void **)&L->col_tasks.seg_first, 4 * (size_t)(in + 1), "column task offsets"},
         {(void **)&L->row_packed.desc, 16 * (size_t)L->row_packed.cap, "packed row tasks"},
         {(void **)&L->row_packed.split, 16 * (size_t)out, "split rows (packed list)"},
+        {(void **)&L->row_tasks.split_cls, 16 * (size_t)kSplitClasses * out, "split rows by class"},
+        {(void **)&L->col_tasks.split_cls, 16 * (size_t)kSplitClasses * in, "split columns by class"},
+        {(void **)&L->row_packed.split_cls, 16 * (size_t)kSplitClasses * out, "split rows by class (packed list)"},
         // batch-minor operand copies for one slice of up to 64 batch rows, and the split partial sums
         {&L->act.a, act_bytes, "operand copy"},
         {&L->act.b, act_bytes, "operand copy"},

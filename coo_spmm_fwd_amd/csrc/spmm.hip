@@ -538,44 +538,63 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
 }
 
 // Segment pass with split segments finished in the kernel (one batch chunk,
-// every segment at most kGroupMaxTasks tasks).  Workgroups [0, nsplit) each
-// take one split segment: its 16 waves run the segment's tasks (wave w: tasks
-// w, w + 16, ...), put their sums in LDS, and after a barrier one lane per
-// batch index adds them in task order -- the order the fixup launch uses, so
-// results are bitwise those of the split-plus-fixup path.  Split segments come
-// first so that long rows start at once.  The remaining workgroups take 16
-// consecutive tasks each and skip the split ones.
+// every segment at most kGroupMaxTasks tasks).  The first workgroups take
+// the split segments by size class (split_class): a class-c workgroup holds
+// 2^c segments of kGroupWaves >> c waves each, so a segment of few tasks does
+// not hold a whole 16-wave workgroup.  A segment's waves run its tasks (wave
+// j: tasks j, j + waves, ...) and put their sums in LDS; after a barrier one
+// thread per (segment, batch index) adds them in task order -- the order the
+// fixup launch uses, so results are bitwise those of the split-plus-fixup
+// path.  Split segments come first so that long rows start at once.  The
+// remaining workgroups take 16 consecutive tasks each and skip the split ones.
 constexpr int kGroupWaves = 16;
 constexpr int kGroupMaxTasks = 64;
 
 template <int LD, class D, bool kWide, int E>
 __global__ __launch_bounds__(kGroupWaves * kWave) void k_segment_grouped(
-    const int4 *__restrict__ desc, int64_t ntasks, const int4 *__restrict__ split, int64_t nsplit,
-    const int32_t *__restrict__ seg_ptr, const int32_t *__restrict__ idx, const typename D::T *__restrict__ vals,
-    const typename D::T *__restrict__ opT, int64_t n_op, int64_t n_seg, int64_t B, typename D::T *__restrict__ out,
-    Epi ep)
+    const int4 *__restrict__ desc, int64_t ntasks, const int4 *__restrict__ split_cls, int64_t cls_stride,
+    int4 ncls, const int32_t *__restrict__ seg_ptr, const int32_t *__restrict__ idx,
+    const typename D::T *__restrict__ vals, const typename D::T *__restrict__ opT, int64_t n_op, int64_t n_seg,
+    int64_t B, typename D::T *__restrict__ out, Epi ep)
 {
     __shared__ float part[kGroupMaxTasks][LD];
     const int wave = threadIdx.x >> 6;
-    const int64_t g = blockIdx.x;
-    if (g < nsplit) {
-        const int4 r = split[g];  // {segment, first task, task count, 0}
-        const int32_t seg = uniform(r.x), first = uniform(r.y), cnt = uniform(r.z);
-        // a split task's slot is its task index, so its partial sums land in part[slot - first]
-        float *base = &part[0][0] - (int64_t)first * LD;
-        for (int32_t j = wave; j < cnt; j += kGroupWaves)
-            segment_task_body<LD, D, kWide, E, 2>(load_task(desc, first + j), idx, vals, opT, n_op, n_seg, B,
-                                                  base, out, ep);
+    int64_t g = blockIdx.x;
+    const int64_t nc[kSplitClasses] = {ncls.x, ncls.y, ncls.z, ncls.w};
+    int c = 0;
+    for (; c < kSplitClasses; ++c) {
+        const int64_t nwg = (nc[c] + (1 << c) - 1) >> c;
+        if (g < nwg) break;
+        g -= nwg;
+    }
+    if (c < kSplitClasses) {
+        const int wps = kGroupWaves >> c;  // waves per segment (a class-0 segment may have 64 tasks)
+        const int sl = wave / wps, wj = wave % wps;
+        const int4 *recs = split_cls + c * cls_stride;
+        const int64_t ri = (g << c) + sl;
+        if (ri < nc[c]) {
+            const int4 r = recs[ri];  // {segment, first task, task count, 0}
+            const int32_t first = uniform(r.y), cnt = uniform(r.z);
+            // a split task's slot is its task index, so its partial sums land in part[sl * wps + slot - first]
+            float *base = &part[sl * wps][0] - (int64_t)first * LD;
+            for (int32_t j = wj; j < cnt; j += wps)
+                segment_task_body<LD, D, kWide, E, 2>(load_task(desc, first + j), idx, vals, opT, n_op, n_seg, B,
+                                                      base, out, ep);
+        }
         __syncthreads();
-        if (threadIdx.x < B) {
-            const int64_t b = threadIdx.x;
-            float tot = 0.f;
-            for (int32_t j = 0; j < cnt; ++j) tot += part[j][b];
-            out[b * n_seg + seg] = finish_out<E, D>(tot, b, seg, n_seg, ep);
+        if (threadIdx.x < (B << c)) {
+            const int s2 = (int)(threadIdx.x / B);
+            const int64_t b = threadIdx.x - (int64_t)s2 * B, r2 = (g << c) + s2;
+            if (r2 < nc[c]) {
+                const int4 r = recs[r2];
+                float tot = 0.f;
+                for (int32_t j = 0; j < r.z; ++j) tot += part[s2 * wps + j][b];
+                out[b * n_seg + r.x] = finish_out<E, D>(tot, b, r.x, n_seg, ep);
+            }
         }
         return;
     }
-    const int64_t t = (g - nsplit) * kGroupWaves + wave;
+    const int64_t t = g * kGroupWaves + wave;
     if (t >= ntasks) return;
     const Task T = load_task(desc, t);
     if (T.slot >= 0) return;  // part of a split segment: finished by its own workgroup
@@ -1132,10 +1151,14 @@ csp_status grouped_dispatch(csp_layer *L, const TaskList &TL, const int32_t *seg
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
-    const unsigned grid = (unsigned)(TL.nsplit + ceil_div(TL.count, kGroupWaves));
+    int64_t nsw = 0;  // workgroups of the split segments, by class
+    for (int c = 0; c < kSplitClasses; ++c) nsw += (TL.ncls[c] + (1 << c) - 1) >> c;
+    const unsigned grid = (unsigned)(nsw + ceil_div(TL.count, kGroupWaves));
+    const int4 ncls = make_int4((int)TL.ncls[0], (int)TL.ncls[1], (int)TL.ncls[2], (int)TL.ncls[3]);
+    const int64_t stride = TL.nsplit > 0 ? n_seg : 0;
 #define CSP_GRP(LDV)                                                                                            \
     launch_main(L, kTimeBoth, k_segment_grouped<LDV, D, false, E>, grid, kGroupWaves * kWave, 0, s,                                    \
-        TL.desc, TL.count, TL.split, TL.nsplit, seg_ptr, idx, (const T *)vals, (const T *)opT, n_op, n_seg, B, (T *)out, ep)
+        TL.desc, TL.count, TL.split_cls, stride, ncls, seg_ptr, idx, (const T *)vals, (const T *)opT, n_op, n_seg, B, (T *)out, ep)
     CSP_LD_SWITCH_LDS(ld, CSP_GRP);
 #undef CSP_GRP
     CSP_LAUNCHED("k_segment_grouped");
