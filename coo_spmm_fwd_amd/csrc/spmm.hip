@@ -259,6 +259,13 @@ __device__ __forceinline__ int64_t xcd_block()
     return x * per + (x < extra ? x : extra) + (b >> 3);
 }
 
+// Waves per workgroup of the product kernels that run one task per wave
+// (k_segment_spmm, k_values_rows, k_gradients).
+#ifndef CSP_PRODUCT_WAVES
+#define CSP_PRODUCT_WAVES 4
+#endif
+constexpr int kPW = CSP_PRODUCT_WAVES;
+
 struct Task {
     int32_t seg, kb, n, slot;
 };
@@ -516,7 +523,7 @@ __device__ __attribute__((always_inline)) inline void packed_task_body(const Tas
 
 // kStore = 1 when the list has no split segments (every task stores its output).
 template <int LD, class D, bool kWide, int E, int kStore>
-__global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
+__global__ __launch_bounds__(kPW * kWave) void k_segment_spmm(const int4 *__restrict__ desc, int64_t ntasks,
                                                       const int32_t *__restrict__ seg_ptr,
                                                       const int32_t *__restrict__ idx,
                                                       const typename D::T *__restrict__ vals,
@@ -525,12 +532,12 @@ __global__ __launch_bounds__(256) void k_segment_spmm(const int4 *__restrict__ d
                                                       float *__restrict__ partial, typename D::T *__restrict__ out,
                                                       Epi ep)
 {
-    const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
+    const int64_t t = xcd_block() * kPW + (threadIdx.x >> 6);
     if (t >= ntasks) return;
     const Task T = load_task(desc, t);
     if constexpr (LD <= 4) {
         if (T.slot < -1) {
-            packed_task_body<LD, D, kWide, E, 4>(T, seg_ptr, idx, vals, opT, n_seg, B, out, ep);
+            packed_task_body<LD, D, kWide, E, kPW>(T, seg_ptr, idx, vals, opT, n_seg, B, out, ep);
             return;
         }
     }
@@ -642,7 +649,7 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
 // kRowMajorDy: dY is the caller's row-major [B, out] (small-table path, one
 // chunk); the entry's batch values then come from B scattered words, padded
 // with zeros past B.
-template <int LD, class D, bool kWide, int NW = 4, bool kRowMajorDy = false>
+template <int LD, class D, bool kWide, int NW = kPW, bool kRowMajorDy = false>
 __device__ __attribute__((always_inline)) inline void values_task_body(const Task &T, const int32_t *__restrict__ cols,
                                    const typename D::T *__restrict__ XT, const typename D::T *__restrict__ dYT,
                                    int64_t in, int64_t out, int64_t B, float *__restrict__ dW, bool acc)
@@ -711,13 +718,13 @@ __device__ __attribute__((always_inline)) inline void values_task(const int4 *__
 }
 
 template <int LD, class D, bool kWide>
-__global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ desc, int64_t ntasks,
+__global__ __launch_bounds__(kPW * kWave) void k_values_rows(const int4 *__restrict__ desc, int64_t ntasks,
                                                      const int32_t *__restrict__ cols,
                                                      const typename D::T *__restrict__ XT,
                                                      const typename D::T *__restrict__ dYT, int64_t in, int64_t out,
                                                      float *__restrict__ dW, int acc)
 {
-    const int64_t t = xcd_block() * 4 + (threadIdx.x >> 6);
+    const int64_t t = xcd_block() * kPW + (threadIdx.x >> 6);
     if (t >= ntasks) return;
     values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, dW, acc != 0);
 }
@@ -728,7 +735,7 @@ __global__ __launch_bounds__(256) void k_values_rows(const int4 *__restrict__ de
 // column tasks and value-gradient row tasks, the longer list's surplus
 // blocks come last.
 template <int LD, class D, bool kWide, int E, int kStore>
-__global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_desc, int64_t ncol_tasks,
+__global__ __launch_bounds__(kPW * kWave) void k_gradients(const int4 *__restrict__ col_desc, int64_t ncol_tasks,
                                                    const int4 *__restrict__ row_desc, int64_t nrow_tasks,
                                                    const int32_t *__restrict__ rows_by_col,
                                                    const typename D::T *__restrict__ vals_c,
@@ -739,7 +746,7 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
                                                    typename D::T *__restrict__ dX, float *__restrict__ dW, Epi ep,
                                                    int acc)
 {
-    const int64_t ncb = (ncol_tasks + 3) / 4, nrb = (nrow_tasks + 3) / 4;
+    const int64_t ncb = (ncol_tasks + kPW - 1) / kPW, nrb = (nrow_tasks + kPW - 1) / kPW;
     const int64_t m = ncb < nrb ? ncb : nrb;
     // Plain dispatch order here: with the two task kinds interleaved, renumbering by XCD
     // measured 6% more HBM traffic for this kernel (and 6% less for the single-kind ones).
@@ -753,7 +760,7 @@ __global__ __launch_bounds__(256) void k_gradients(const int4 *__restrict__ col_
         col = ncb > nrb;
         blk = m + (bid - 2 * m);
     }
-    const int64_t t = blk * 4 + (threadIdx.x >> 6);
+    const int64_t t = blk * kPW + (threadIdx.x >> 6);
     if (col) {
         if (t < ncol_tasks)
             segment_task<LD, D, kWide, E, kStore>(col_desc, t, rows_by_col, vals_c, dYT, out, in, B, partial, dX, ep);
@@ -1173,13 +1180,13 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
     const TaskList &TL = fwd_tasks(L, B);
     if (grouped_splits(TL, B, L->in, L->in))
         return grouped_dispatch<D, E>(L, TL, L->row_ptr, L->cols, L->vals, XT, L->in, L->out, B, Y, ep, s);
-    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    const unsigned grid = (unsigned)ceil_div(TL.count, kPW);
     const bool ks = TL.nsplit == 0;
 #define CSP_FWD_ARGS \
     TL.desc, TL.count, L->row_ptr, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, L->act.partial, (T *)Y, ep
 #define CSP_FWD(LDV, W)                                                             \
-    if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_FWD_ARGS);    \
-    else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_FWD_ARGS)
+    if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, kPW * kWave, 0, s, CSP_FWD_ARGS);    \
+    else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, kPW * kWave, 0, s, CSP_FWD_ARGS)
     CSP_LD_SWITCH(ld, wide_operand(L->in, ld), CSP_FWD);
 #undef CSP_FWD
 #undef CSP_FWD_ARGS
@@ -1195,14 +1202,14 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
     const TaskList &TL = L->col_tasks;
     if (grouped_splits(TL, B, L->out, L->out))
         return grouped_dispatch<D, E>(L, TL, L->col_ptr, L->rows_by_col, L->vals_c, dYT, L->out, L->in, B, dX, ep, s);
-    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    const unsigned grid = (unsigned)ceil_div(TL.count, kPW);
     const bool ks = TL.nsplit == 0;
 #define CSP_DX_ARGS                                                                                                 \
     TL.desc, TL.count, L->col_ptr, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX(LDV, W)                                                            \
-    if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_DX_ARGS);   \
-    else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_DX_ARGS)
+    if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, kPW * kWave, 0, s, CSP_DX_ARGS);   \
+    else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, kPW * kWave, 0, s, CSP_DX_ARGS)
     CSP_LD_SWITCH(ld, wide_operand(L->out, ld), CSP_DX);
 #undef CSP_DX
 #undef CSP_DX_ARGS
@@ -1217,9 +1224,9 @@ csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, in
     using T = typename D::T;
     const int ld = pow2_ld(B);
     const TaskList &TL = L->row_tasks;
-    const unsigned grid = (unsigned)ceil_div(TL.count, 4);
+    const unsigned grid = (unsigned)ceil_div(TL.count, kPW);
 #define CSP_DW(LDV, W)                                                                                            \
-    launch_main(L, kTimeBoth, k_values_rows<LDV, D, W>, grid, 256, 0, s, TL.desc, TL.count, L->cols, (const T *)XT, (const T *)dYT, L->in, \
+    launch_main(L, kTimeBoth, k_values_rows<LDV, D, W>, grid, kPW * kWave, 0, s, TL.desc, TL.count, L->cols, (const T *)XT, (const T *)dYT, L->in, \
                                                   L->out, dW, (int)acc)
     CSP_LD_SWITCH(ld, wide_operand(L->in > L->out ? L->in : L->out, ld), CSP_DW);
 #undef CSP_DW
@@ -1242,22 +1249,22 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
     // other, so the passes run as two launches instead.
     const int64_t table_bytes = (int64_t)L->esz * ld * (L->in + L->out);
     if (table_bytes > (int64_t(2) << 20)) {
-        const unsigned gx = (unsigned)ceil_div(CT.count, 4), gw = (unsigned)ceil_div(nrow, 4);
+        const unsigned gx = (unsigned)ceil_div(CT.count, kPW), gw = (unsigned)ceil_div(nrow, kPW);
         const int m1 = gw > 0 ? kTimeStart : kTimeBoth;  // the value-gradient kernel carries the end
         const bool ks = CT.nsplit == 0;
 #define CSP_DX2_ARGS                                                                                                \
     CT.desc, CT.count, L->col_ptr, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
         (T *)dX, ep
 #define CSP_DX2(LDV, W)                                                         \
-    if (ks) launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 1>, gx, 256, 0, s, CSP_DX2_ARGS);  \
-    else launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 0>, gx, 256, 0, s, CSP_DX2_ARGS)
+    if (ks) launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 1>, gx, kPW * kWave, 0, s, CSP_DX2_ARGS);  \
+    else launch_main(L, m1, k_segment_spmm<LDV, D, W, E, 0>, gx, kPW * kWave, 0, s, CSP_DX2_ARGS)
         CSP_LD_SWITCH(ld, wide, CSP_DX2);
 #undef CSP_DX2
 #undef CSP_DX2_ARGS
         CSP_LAUNCHED("k_segment_spmm (input gradient)");
         if (gw > 0) {
 #define CSP_DW2(LDV, W)                                                                                           \
-    launch_main(L, kTimeStop, k_values_rows<LDV, D, W>, gw, 256, 0, s, RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
+    launch_main(L, kTimeStop, k_values_rows<LDV, D, W>, gw, kPW * kWave, 0, s, RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
                                                 dW, (int)acc)
             CSP_LD_SWITCH(ld, wide, CSP_DW2);
 #undef CSP_DW2
@@ -1265,14 +1272,14 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         }
         return split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
     }
-    const unsigned grid = (unsigned)(ceil_div(CT.count, 4) + ceil_div(nrow, 4));
+    const unsigned grid = (unsigned)(ceil_div(CT.count, kPW) + ceil_div(nrow, kPW));
     const bool ks = CT.nsplit == 0;
 #define CSP_BOTH_ARGS                                                                                            \
     CT.desc, CT.count, RT.desc, nrow, L->rows_by_col, (const T *)L->vals_c, L->cols, (const T *)XT, (const T *)dYT, \
         L->in, L->out, B, L->act.partial, (T *)dX, dW, ep, (int)acc
 #define CSP_BOTH(LDV, W)                                                        \
-    if (ks) launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 1>, grid, 256, 0, s, CSP_BOTH_ARGS);  \
-    else launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 0>, grid, 256, 0, s, CSP_BOTH_ARGS)
+    if (ks) launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 1>, grid, kPW * kWave, 0, s, CSP_BOTH_ARGS);  \
+    else launch_main(L, kTimeBoth, k_gradients<LDV, D, W, E, 0>, grid, kPW * kWave, 0, s, CSP_BOTH_ARGS)
     CSP_LD_SWITCH(ld, wide, CSP_BOTH);
 #undef CSP_BOTH
 #undef CSP_BOTH_ARGS
