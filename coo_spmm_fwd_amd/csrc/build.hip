@@ -77,7 +77,7 @@ __device__ __forceinline__ uint32_t seg_pieces(const int32_t *ptr, int64_t i)
 // The three task lists (plain rows, plain columns, packed rows) are built by
 // the same launches: blocks [0, tiles0) work on list 0, the next tiles1 on
 // list 1 and the rest on list 2.  Lists 0 and 1 take one segment per
-// thread; list 2 takes one window of kPackSegs rows per thread.
+// thread; list 2 takes one window of kPackSegs rows per workgroup.
 constexpr int kTaskThreads = 1024;
 constexpr int kLists = 3;
 
@@ -115,43 +115,55 @@ __device__ __forceinline__ void task_tile(const TaskBuild &tb, int &l, int64_t &
     while (l < kLists - 1 && tile >= tb.tiles[l]) tile -= tb.tiles[l++];
 }
 
-// Greedy packing of the rows [s0, s1) of one window, in order.  A row longer
-// than kTaskChunk closes the open task and is cut into kTaskChunk pieces (a
-// split row, as in the plain list).  Any other row joins the open task unless
-// that would take the task past pack_limit (<= kPackEntries) entries; then
-// the open task is closed first.  Empty rows join like any other (the task
-// stores their zero outputs).  Returns the number of tasks; with kEmit, also writes them from
-// descriptor f on: {first row, first entry, end entry, -(rows)} for a packed
-// task (-1: one row, as in the plain list) and {row, first entry, end entry,
-// task index} for each piece of a split row, plus the split records.
+// Greedy packing of the rows [s0, s1) of one window (kPackSegs rows), in
+// order, by one wave: lane j loads the bounds of row s0 + j, and every lane
+// walks the window reading them with readlane (no memory access inside the
+// walk).  A row longer than kTaskChunk closes the open task and is cut into
+// kTaskChunk pieces (a split row, as in the plain list).  Any other row joins
+// the open task unless that would take the task past pack_limit
+// (<= kPackEntries) entries; then the open task is closed first.  Empty rows
+// join like any other (the task stores their zero outputs).  Returns the
+// number of tasks; with kEmit, lane 0 also writes them from descriptor f on:
+// {first row, first entry, end entry, -(rows)} for a packed task (-1: one
+// row, as in the plain list) and {row, first entry, end entry, task index}
+// for each piece of a split row, plus the split records.
 template <bool kEmit>
-__device__ uint32_t pack_window(const TaskBuild &tb, const int32_t *ptr, int64_t s0, int64_t s1, int32_t f)
+__device__ uint32_t pack_window(const TaskBuild &tb, int64_t s0, int64_t s1, int32_t f)
 {
+    const int lane = threadIdx.x & 63;
+    const int nr = (int)(s1 - s0);  // 1 .. kPackSegs
+    // fields used in the walk, read once (the build struct may sit in private memory)
+    const int32_t *ptr = tb.ptr[2];
+    int4 *const desc = tb.desc[2];
+    const int64_t cap = tb.cap[2];
+    const int32_t lim = tb.pack_limit;
+    const int32_t ej = ptr[s0 + (lane < nr ? lane + 1 : nr)];  // end of row s0 + lane
+    const bool w0 = kEmit && lane == 0;
     uint32_t n = 0;
-    int64_t open = -1;
-    int32_t open_kb = 0, cnt = 0;
-    int32_t b = ptr[s0];
-    for (int64_t r = s0; r < s1; ++r) {
-        const int32_t e = ptr[r + 1], len = e - b;
+    int32_t open = -1, open_kb = 0, cnt = 0;
+    int32_t b = __builtin_amdgcn_readfirstlane(ptr[s0]);
+    for (int j = 0; j < nr; ++j) {
+        const int32_t r = (int32_t)(s0 + j);
+        const int32_t e = __builtin_amdgcn_readlane(ej, j), len = e - b;
         if (len > kTaskChunk) {
             if (cnt) {
-                if (kEmit && f + n < tb.cap[2]) tb.desc[2][f + n] = make_int4((int32_t)open, open_kb, b, -cnt);
+                if (w0 && f + n < cap) desc[f + n] = make_int4(open, open_kb, b, -cnt);
                 ++n;
                 cnt = 0;
             }
             const uint32_t p = (uint32_t)((len + kTaskChunk - 1) / kTaskChunk);
-            if (kEmit) {
-                for (uint32_t j = 0; j < p && (int64_t)f + n + j < tb.cap[2]; ++j) {
-                    const int32_t kb = b + (int32_t)j * kTaskChunk;
+            if (w0) {
+                for (uint32_t k = 0; k < p && (int64_t)f + n + k < cap; ++k) {
+                    const int32_t kb = b + (int32_t)k * kTaskChunk;
                     const int32_t ke = kb + kTaskChunk < e ? kb + kTaskChunk : e;
-                    tb.desc[2][f + n + j] = make_int4((int32_t)r, kb, ke, (int32_t)(f + n + j));
+                    desc[f + n + k] = make_int4(r, kb, ke, (int32_t)(f + n + k));
                 }
-                emit_split(tb, 2, make_int4((int32_t)r, (int32_t)(f + n), (int32_t)p, 0), p);
+                emit_split(tb, 2, make_int4(r, (int32_t)(f + n), (int32_t)p, 0), p);
             }
             n += p;
         } else {
-            if (cnt && e - open_kb > tb.pack_limit) {
-                if (kEmit && f + n < tb.cap[2]) tb.desc[2][f + n] = make_int4((int32_t)open, open_kb, b, -cnt);
+            if (cnt && e - open_kb > lim) {
+                if (w0 && f + n < cap) desc[f + n] = make_int4(open, open_kb, b, -cnt);
                 ++n;
                 cnt = 0;
             }
@@ -164,20 +176,32 @@ __device__ uint32_t pack_window(const TaskBuild &tb, const int32_t *ptr, int64_t
         b = e;
     }
     if (cnt) {
-        if (kEmit && f + n < tb.cap[2]) tb.desc[2][f + n] = make_int4((int32_t)open, open_kb, b, -cnt);
+        if (w0 && f + n < cap) desc[f + n] = make_int4(open, open_kb, b, -cnt);
         ++n;
     }
     return n;
 }
 
-// Tasks of work item i of list l: a segment of lists 0 and 1, a window of
-// kPackSegs rows of list 2 (nseg[2] counts windows, rows2 rows).
+// Work item of a thread: a segment of lists 0 and 1 (item = thread), a
+// window of kPackSegs rows of list 2 (item = the block's first wave; nseg[2]
+// counts windows, rows2 rows).  The walk is scalar work, and a compute unit
+// has one scalar unit for all its waves, so one window per workgroup spreads
+// the walks over the compute units (16 windows per workgroup measured 12 us
+// per launch on a 4096-row layer).  item_tasks returns the item's task count
+// in the lane that owns it (every lane of lists 0 and 1, lane 0 of the
+// list-2 wave) and 0 elsewhere.
+__device__ __forceinline__ int64_t item_index(const TaskBuild &tb, int l, int64_t tile)
+{
+    if (l < 2) return tile * kTaskThreads + threadIdx.x;
+    return threadIdx.x < 64 ? tile : tb.nseg[2];
+}
 __device__ __forceinline__ uint32_t item_tasks(const TaskBuild &tb, int l, int64_t i)
 {
     if (i >= tb.nseg[l]) return 0u;
     if (l < 2) return seg_pieces(tb.ptr[l], i);
     const int64_t s0 = i * kPackSegs, s1 = s0 + kPackSegs < tb.rows2 ? s0 + kPackSegs : tb.rows2;
-    return pack_window<false>(tb, tb.ptr[2], s0, s1, 0);
+    const uint32_t n = pack_window<false>(tb, s0, s1, 0);
+    return (threadIdx.x & 63) == 0 ? n : 0u;
 }
 
 __global__ __launch_bounds__(kTaskThreads) void k_tasks_count(TaskBuild tb)
@@ -186,7 +210,7 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_count(TaskBuild tb)
     int l;
     int64_t tile;
     task_tile(tb, l, tile);
-    const int64_t i = tile * kTaskThreads + threadIdx.x;
+    const int64_t i = item_index(tb, l, tile);
     uint32_t total;
     block_exclusive_scan(item_tasks(tb, l, i), lds, &total);
     if (threadIdx.x == 0) tb.partials[l][tile] = total;
@@ -231,7 +255,7 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
     int l;
     int64_t tile;
     task_tile(tb, l, tile);
-    const int64_t i = tile * kTaskThreads + threadIdx.x;
+    const int64_t i = item_index(tb, l, tile);
     const bool live = i < tb.nseg[l];
     const uint32_t p = item_tasks(tb, l, i);
     uint32_t before, total;
@@ -248,9 +272,9 @@ __global__ __launch_bounds__(kTaskThreads) void k_tasks_emit(TaskBuild tb)
         if (l < 2) tb.seg_first[l][tb.nseg[l]] = (int32_t)(before + total);
     }
     if (!live) return;
-    if (l == 2) {
+    if (l == 2) {  // the window's first descriptor is its lane 0's offset
         const int64_t s0 = i * kPackSegs, s1 = s0 + kPackSegs < tb.rows2 ? s0 + kPackSegs : tb.rows2;
-        pack_window<true>(tb, tb.ptr[2], s0, s1, f);
+        pack_window<true>(tb, s0, s1, __builtin_amdgcn_readfirstlane(f));
         return;
     }
     tb.seg_first[l][i] = f;
@@ -280,17 +304,19 @@ int32_t pack_limit(const csp_layer *L)
 // counts, seg_first[nseg] = the total; then one descriptor per task and one
 // record per split segment (their order is irrelevant: each record is
 // self-contained).  List 2 packs windows of rows (pack_window).
-csp_status build_task_lists(csp_layer *L, hipStream_t s)
+csp_status build_task_lists(csp_layer *L, hipStream_t s, bool with_packed)
 {
+    L->packed_pending = with_packed;
+    if (!with_packed) L->packed_valid = false;  // the list no longer matches the layer
     TaskBuild tb;
     TaskList *T[kLists] = {&L->row_tasks, &L->col_tasks, &L->row_packed};
     const int32_t *ptr[kLists] = {L->row_ptr, L->col_ptr, L->row_ptr};
-    const int64_t nseg[kLists] = {L->out, L->in, ceil_div(L->out, kPackSegs)};
+    const int64_t nseg[kLists] = {L->out, L->in, with_packed ? ceil_div(L->out, kPackSegs) : 0};
     uint32_t *part = L->ws.hist;
     for (int l = 0; l < kLists; ++l) {
         tb.ptr[l] = ptr[l];
         tb.nseg[l] = nseg[l];
-        tb.tiles[l] = ceil_div(nseg[l], kTaskThreads);
+        tb.tiles[l] = l < 2 ? ceil_div(nseg[l], kTaskThreads) : nseg[l];  // list 2: a window per workgroup
         tb.desc[l] = T[l]->desc;
         tb.split[l] = T[l]->split;
         tb.split_cls[l] = T[l]->split_cls;
@@ -325,6 +351,7 @@ csp_status set_task_counts(csp_layer *L, const uint32_t *counts)
     L->col_tasks.nsplit = counts[3];
     L->row_packed.count = counts[6];
     L->row_packed.nsplit = counts[7];
+    L->packed_valid = L->packed_pending;
     TaskList *T[3] = {&L->row_tasks, &L->col_tasks, &L->row_packed};
     for (int l = 0; l < 3; ++l)
         for (int c = 0; c < kSplitClasses; ++c) T[l]->ncls[c] = counts[kSelClassWords + kSplitClasses * l + c];
@@ -371,7 +398,7 @@ csp_status build_index(csp_layer *L, hipStream_t s)
     st = segment_offsets((const int32_t *)L->ws.key_a, nnz, L->col_ptr, L->in, s);
     if (st != CSP_OK) return st;
 
-    st = build_task_lists(L, s);
+    st = build_task_lists(L, s, !L->created || L->narrow_seen);
     if (st != CSP_OK) return st;
     uint32_t counts[kSelCountWords] = {};
     CSP_HIP(hipMemcpyAsync(counts, L->ws.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));

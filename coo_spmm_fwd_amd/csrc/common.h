@@ -123,6 +123,11 @@ struct csp_layer {
     void *vals_c = nullptr;  // values in transposed (col, row) order: vals_c[j] = vals[perm_c[j]]
     csp::TaskList row_tasks, col_tasks;
     csp::TaskList row_packed;  // whole rows packed per task (forward at B <= 4); seg_first unused
+    // The packed list is built at create, and again by a restructure only
+    // once a forward at B <= 4 has been asked for (narrow_seen); a forward
+    // after a restructure that skipped it uses the plain row list.
+    bool packed_valid = false, packed_pending = false, narrow_seen = false;
+    bool created = false;  // set once sparse_layer_create has finished
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request
@@ -187,7 +192,7 @@ csp_status build_index(csp_layer *L, hipStream_t s);
 // The three task lists from row_ptr / col_ptr (plain rows, plain columns,
 // packed rows; two or three launches, no host sync); the counts land in
 // sel[kSelCounts + 0..3, 6..7] for set_task_counts.
-csp_status build_task_lists(csp_layer *L, hipStream_t s);
+csp_status build_task_lists(csp_layer *L, hipStream_t s, bool with_packed);
 // Entry limit of a packed task of several rows for this layer.
 int32_t pack_limit(const csp_layer *L);
 // Takes the kSelCountWords counts read back from sel[kSelCounts]; checks the capacities.

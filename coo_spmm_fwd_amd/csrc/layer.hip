@@ -90,7 +90,7 @@ csp_status alloc_layer(csp_layer *L)
     W.hist_words = sort_hist_words(W.nkey_cap);
     const int64_t nseg_max = out > in ? out : in;
     // scan partials of the three task lists
-    const size_t task_words = (size_t)(2 * ceil_div(nseg_max, 1024) + ceil_div(out, 1024 * (int64_t)kPackSegs) + 64);
+    const size_t task_words = (size_t)(2 * ceil_div(nseg_max, 1024) + ceil_div(out, (int64_t)kPackSegs) + 64);
     if (W.hist_words < task_words) W.hist_words = task_words;
     const bool bitmap = plan_bitmap(L);
     if (bitmap && W.hist_words < bitmap_hist_words(L)) W.hist_words = bitmap_hist_words(L);
@@ -228,6 +228,7 @@ csp_status sparse_layer_create(int64_t out_features, int64_t in_features, int64_
         free_layer(L);
         return st;
     }
+    L->created = true;
     *out_layer = L;
     return CSP_OK;
 }

@@ -842,7 +842,7 @@ struct BitmapRun {
                                                         W.tcnt, (const V *)W.vals_k, L->perm_c, L->rows_by_col,
                                                         (V *)L->vals_c, L->col_ptr);
         CSP_LAUNCHED("k_bm_tgather");
-        st = build_task_lists(L, s);
+        st = build_task_lists(L, s, L->narrow_seen);
         if (st != CSP_OK) return st;
         uint32_t counts[kSelCountWords] = {};
         CSP_HIP(hipMemcpyAsync(counts, W.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));

@@ -1127,13 +1127,15 @@ csp_status gradients_lds_dispatch(csp_layer *L, const void *X, const void *dY, i
 }
 
 // The forward's task list: the packed one when a lane holds one entry
-// (B <= 4), where a task of one short row would leave most lanes idle.
-// COOSPMM_PACKED=0 keeps the plain list.
-inline const TaskList &fwd_tasks(const csp_layer *L, int64_t B)
+// (B <= 4), where a task of one short row would leave most lanes idle, and
+// the packed list is current (see csp_layer::narrow_seen).  COOSPMM_PACKED=0
+// keeps the plain list.
+inline const TaskList &fwd_tasks(csp_layer *L, int64_t B)
 {
     if (pow2_ld(B) > 4) return L->row_tasks;
+    L->narrow_seen = true;  // later restructures rebuild the packed list
     const char *e = std::getenv("COOSPMM_PACKED");
-    return e && e[0] == '0' ? L->row_tasks : L->row_packed;
+    return (e && e[0] == '0') || !L->packed_valid ? L->row_tasks : L->row_packed;
 }
 
 // Split segments finished inside the segment pass (k_segment_grouped) when

@@ -167,3 +167,33 @@ def test_packed_forward(orc, layout, B, dtype):
                 assert_within(packed["fwd"], ref, S, rel, f"{layout} B={B} forward")
         finally:
             csp.sparse_layer_destroy(h)
+
+
+@pytest.mark.gpu
+def test_packed_list_across_restructures(orc):
+    """The packed list is rebuilt by a restructure only after a narrow forward was asked for; in
+    between the forward uses the plain list.  Every state must give the oracle's exact sums."""
+    n, in_ = lengths_for("mixed_short")
+    L = layer_from_lengths(n, in_, 5, "f32", integer=True)
+    out = L.out
+    with env(COOSPMM_PACK_LIMIT="505"):
+        h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))
+        try:
+            Xh = W.random_dense((1, in_), 77, integer=True)
+            X = dev(Xh)
+
+            def check(tag):
+                r, c, v = (host(t) for t in csp.sparse_layer_export(h))
+                ref, _ = orc.spmm_fwd(out, in_, r, c, v, Xh)
+                got = host(csp.spmm_fwd(h, X))
+                assert np.array_equal(got, ref.astype(np.float32)), tag
+                with env(COOSPMM_PACKED="0"):
+                    plain = host(csp.spmm_fwd(h, X))
+                assert np.array_equal(plain.view(np.uint32), got.view(np.uint32)), tag
+
+            csp.restructure(h, 5000, seed=9, step=1)   # no narrow forward yet: packed list not rebuilt
+            check("after a restructure that skipped the packed list")
+            csp.restructure(h, 5000, seed=9, step=2)   # narrow forward seen: rebuilt
+            check("after a restructure that rebuilt it")
+        finally:
+            csp.sparse_layer_destroy(h)
