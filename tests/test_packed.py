@@ -11,7 +11,8 @@ a segmented scan over the lanes.
 
 Checks, on layouts made to hit the packing rule's edges (runs of empty rows,
 single-entry rows, rows of 504..513 and 1024/1025 entries, a lone non-empty
-row, an empty layer, power-law rows):
+row, an empty layer, 70000 short rows (over 1024 packing windows), power-law
+rows):
 - integer-valued inputs (every sum exact in fp32): the packed result equals
   the oracle exactly, and the plain list's result bit for bit, also through
   the bias + GELU epilogue and its pre-activation output;
@@ -70,6 +71,8 @@ def lengths_for(name: str) -> tuple[np.ndarray, int]:
         return n, 400
     if name == "empty_layer":
         return np.zeros(1000, np.int64), 100
+    if name == "tall":  # more than 1024 packing windows: the task-list build takes its separate scan launch
+        return rng.integers(0, 6, size=70000), 64
     raise KeyError(name)
 
 
@@ -97,7 +100,7 @@ def zipf_layer(dtype, integer, seed=31):
     return W.CooWeights(2048, 16384, rows, cols, W.f32_to_bf16_bits(v) if dtype == "bf16" else v, dtype)
 
 
-LAYOUTS = ["mixed_short", "single_entry", "empty_runs", "edge_lengths", "one_row", "empty_layer", "zipf"]
+LAYOUTS = ["mixed_short", "single_entry", "empty_runs", "edge_lengths", "one_row", "empty_layer", "tall", "zipf"]
 CASES = [(lay, B, dt) for lay in LAYOUTS for B in (1, 2, 3, 4) for dt in ("f32", "bf16")
          if not (dt == "bf16" and B in (2, 3))]
 
@@ -119,6 +122,8 @@ def test_layouts_hit_the_packing_edges():
     assert set(n.tolist()) == {0, 1}
     n, _ = lengths_for("mixed_short")
     assert (n > 512).sum() == 2 and (n == 0).sum() > 100
+    n, _ = lengths_for("tall")
+    assert -(-len(n) // 64) > 1024
 
 
 @pytest.mark.gpu
