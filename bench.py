@@ -362,8 +362,8 @@ def main():
         ingest_counters(*args.ingest_counters, workload=args.workload, batch=args.batch)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each MI355X runs its own layer; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(each MI355X runs its own layer). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
