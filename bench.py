@@ -632,7 +632,8 @@ def main():
         baselines["ours_ms_per_step"] = round(ours_ms, 5)
         del Ws
 
-    ceiling = practical_ceiling(dom["bytes"], stream)
+    # not in counter runs: the calibration copy must be the run's only large copy
+    ceiling = None if args.calibrate_copy else practical_ceiling(dom["bytes"], stream)
 
     if args.calibrate_copy:
         n = (args.calibrate_copy << 20) // 4

@@ -14,15 +14,18 @@
 //
 // Work split.  One wavefront runs one task: up to kTaskChunk consecutive
 // entries of one segment (a row for the forward pass and the value gradient,
-// a column for the input gradient).  Lane = (slot s, batch b) with S = 64/ld
-// slots.  A pass first loads 256 of the task's index/value words with
-// coalesced loads (4 per lane), then hands them to the slots with cross-lane
-// reads (v_readlane when S = 1, ds_bpermute otherwise), so all of the pass's
-// operand gathers can be in flight together.  Slots are summed at the end of
-// the task with cross-lane adds; per-entry sums over the batch (value
-// gradient) use DPP row operations.  No MFMA: an unstructured gather is not a
+// a column for the input gradient).  A lane holds VW = min(4, ld) batch
+// values of one entry, LPE = ld/VW lanes cover an entry, and the wave steps
+// through S = 64/LPE entries at a time (see Map).  A pass first loads 256 of
+// the task's index/value words with coalesced loads (4 per lane), then hands
+// them to the entry slots with ds_bpermute, so a run of the pass's operand
+// gathers can be in flight together.  Slots are summed at the end of the task
+// with cross-lane adds; per-entry sums over the batch (value gradient) use
+// DPP row operations.  At ld <= 4 the forward runs from a packed row list
+// whose tasks may hold several whole short rows (packed_task_body: a
+// segmented scan over the lanes).  No MFMA: an unstructured gather is not a
 // dense contraction; the bound is HBM for the COO stream and L1/L2 for the
-// operand gathers.
+// operand gathers (one L2 request per stored entry and gathered table).
 #include <cstdlib>
 
 #include <hip/hip_ext.h>
