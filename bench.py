@@ -591,8 +591,10 @@ def main():
     torch.cuda.synchronize()
     per_call = {}
     for ci, (label, _, _, kname, kbytes) in enumerate(calls(reps[0], stream)):
-        us = sum(ev[i][ci][0].elapsed_time(ev[i][ci][1]) for i in range(K)) / K * 1e3
-        per_call[label] = {"kernel": kname, "us": us, "bytes": kbytes}
+        ts = sorted(ev[i][ci][0].elapsed_time(ev[i][ci][1]) * 1e3 for i in range(K))
+        us = sum(ts) / K
+        med = ts[K // 2] if K % 2 else 0.5 * (ts[K // 2 - 1] + ts[K // 2])
+        per_call[label] = {"kernel": kname, "us": us, "median_us": med, "bytes": kbytes}
     dom_label = max(per_call, key=lambda k: per_call[k]["us"])
     dom = per_call[dom_label]
     achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
@@ -680,6 +682,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": dom["kernel"], "call": dom_label, "avg_launch_us": round(dom["us"], 3),
+                     "median_launch_us": round(dom["median_us"], 3),
                      "bytes_per_launch": dom["bytes"], "ceiling": ceiling},
         "kernels_us": {k: round(v["us"], 3) for k, v in per_call.items()},
         "restructure_ms": None if restructure_ms is None else round(restructure_ms, 3),
