@@ -104,7 +104,9 @@ csp_status spmm_fwd(sparse_layer_t layer, const void *X, int64_t B, void *Y, voi
 csp_status spmm_bwd_input(sparse_layer_t layer, const void *dY, int64_t B, void *dX, void *stream);
 
 /*
- * spmm_bwd_values -- gradient with respect to the stored values only, a
+ * spmm_bwd_values -- gradient with respect to the stored values only
+ * (Abstract: the layer backpropagates its gradients entirely on the sparse
+ * storage, so the weight gradient exists only at the stored connections), a
  * sampled dense-dense product:
  *     dW[k] = sum_b dY[b, row_k] * X[b, col_k]   for every stored k
  * dW [nnz] is fp32 and in canonical (row, col) order (the order of

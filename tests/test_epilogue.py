@@ -1,6 +1,8 @@
 """Fused epilogues against the oracle: forward with bias and GELU (and the pre-activation output),
 input gradient times GELU' of the previous layer's pre-activation, in fp32 and bf16, including
-rows and columns long enough to be split across tasks (their sums finish in the fixup launch).
+rows and columns long enough to be split across tasks (their sums finish in the fixup launch or
+inside the pass), and B = 32 (the batch-width-32 fused gradients kernel that the MLP training
+step runs).
 
 Tolerances.  The oracle's pre-activation y and S = sum |terms| + |bias| are fp64.  GELU' lies in
 [-0.17, 1.13], so an fp32 sum within 1e-5 * S moves GELU(y) by at most 1.13e-5 * S; the fp32
@@ -31,7 +33,8 @@ def bf16_or_f32(x, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("out,in_,nnz,B", [(500, 700, 20000, 1), (500, 700, 20000, 16), (3, 5000, 9000, 8),
-                                           (900, 300, 30000, 70)])
+                                           (900, 300, 30000, 70), (500, 700, 20000, 32), (3, 5000, 9000, 1),
+                                           (2, 20000, 30000, 1)])
 def test_forward_bias_gelu(orc, dtype, out, in_, nnz, B):
     L = W.random_layer(out, in_, nnz, seed=out + in_, dtype=dtype, std=0.3)
     h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))
@@ -54,7 +57,7 @@ def test_forward_bias_gelu(orc, dtype, out, in_, nnz, B):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("out,in_,nnz,B", [(700, 500, 20000, 1), (700, 500, 20000, 16), (5000, 3, 9000, 8),
-                                           (300, 900, 30000, 70)])
+                                           (300, 900, 30000, 70), (700, 500, 20000, 32), (5000, 3, 9000, 1)])
 def test_input_gradient_times_gelu_grad(orc, dtype, out, in_, nnz, B):
     L = W.random_layer(out, in_, nnz, seed=out * 3 + in_, dtype=dtype, std=0.3)
     h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))

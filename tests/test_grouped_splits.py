@@ -124,6 +124,11 @@ def test_grouped_splits_bitwise_and_oracle(orc, name, builder, B, dtype):
         assert_within(on["fwd"], ref, S, rel, f"{name} forward")
         refx, Sx = orc.spmm_bwd_input(out, in_, L.rows, L.cols, L.vals, dYh)
         assert_within(on["dx"], refx, Sx, rel, f"{name} input gradient")
+        # the fused forward: pre-activation y = X W^T + bias and GELU(y), bias counted in S
+        yb = ref + as_f64(bh)[None, :]
+        Sb = S + np.abs(as_f64(bh))[None, :]
+        assert_within(on["pre"], yb, Sb, rel, f"{name} pre-activation")
+        assert_within(on["fwd_act"], orc.gelu(yb), Sb, 1.3e-5 if dtype == "f32" else 1.2e-2, f"{name} GELU")
         g = orc.gelu_grad(as_f64(Hh))
         assert_within(on["dx_act"], refx * g, Sx, 1.3e-5 if dtype == "f32" else 1.2e-2, f"{name} dX * GELU'")
     finally:

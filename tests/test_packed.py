@@ -29,7 +29,7 @@ import torch
 
 from coo_spmm_fwd_amd import binding as csp
 from coo_spmm_fwd_amd import workloads as W
-from tests.gpu_util import BF16_REL, FP32_REL, assert_within, dev, host
+from tests.gpu_util import BF16_REL, FP32_REL, as_f64, assert_within, dev, host
 
 
 @contextmanager
@@ -170,6 +170,11 @@ def test_packed_forward(orc, layout, B, dtype):
                     assert np.array_equal(plain[k].view(np.uint8), packed[k].view(np.uint8)), f"{k}: plain list"
             else:
                 assert_within(packed["fwd"], ref, S, rel, f"{layout} B={B} forward")
+                yb = ref + as_f64(bh)[None, :]
+                Sb = S + np.abs(as_f64(bh))[None, :]
+                assert_within(packed["pre"], yb, Sb, rel, f"{layout} B={B} pre-activation")
+                assert_within(packed["act"], orc.gelu(yb), Sb, 1.3e-5 if dtype == "f32" else 1.2e-2,
+                              f"{layout} B={B} GELU")
         finally:
             csp.sparse_layer_destroy(h)
 

@@ -262,8 +262,9 @@ def test_full_size_zipf_bf16_inference(orc):
         layer.close()
 
 
-def test_full_size_mlp_pair(orc):
-    """768 -> 3072 (GELU) -> 768: every op compared on the GPU's own inputs to that op."""
+def test_full_size_mlp_pair_plain(orc):
+    """768 -> 3072 (GELU) -> 768 through the plain calls (GELU in the harness): every op compared on
+    the GPU's own inputs to that op."""
     from scipy.special import erf
     w, layers, acts = W.build("mlp768x3072_s90")
     l1, l2 = Layer(orc, layers[0]), Layer(orc, layers[1])
@@ -294,6 +295,45 @@ def test_full_size_mlp_pair(orc):
             dX = host(csp.spmm_bwd_input(l1.h, dev(dH)))
             ref, S = orc.spmm_bwd_input(3072, 768, l1.L.rows, l1.L.cols, l1.L.vals, dH)
             assert_within(dX, ref, S, FP32_REL, f"mlp dX1 B={B}")
+    finally:
+        l1.close()
+        l2.close()
+
+
+ACT_REL = 1.3e-5   # fused GELU / GELU' outputs (derivation in tests/test_epilogue.py)
+
+
+def test_full_size_mlp_pair_fused(orc):
+    """The MLP pair exactly as the training step runs it, at the full 768 -> 3072 -> 768 size and
+    B in {1, 4, 32}: spmm_fwd_act (GELU epilogue, pre-activation H kept), spmm_fwd,
+    spmm_bwd_act (dH = (dY W2) * GELU'(H) and dW2 in one call), spmm_bwd (dX, dW1).  Each output
+    is compared with the oracle on the GPU's own inputs to that call; the activations go through
+    the oracle's fp64 GELU and GELU'."""
+    w, layers, acts = W.build("mlp768x3072_s90")
+    l1, l2 = Layer(orc, layers[0]), Layer(orc, layers[1])
+    L1, L2 = l1.L, l2.L
+    try:
+        for B in w.batches:
+            X, dY = acts[B]["X"], acts[B]["dY"]
+            Hd = torch.empty((B, L1.out), device="cuda")
+            A = host(csp.spmm_fwd_act(l1.h, dev(X), act="gelu", H=Hd))
+            H = host(Hd)
+            ref, S = orc.spmm_fwd(L1.out, L1.in_, L1.rows, L1.cols, L1.vals, X)
+            assert_within(H, ref, S, FP32_REL, f"mlp fused fwd1 pre-activation B={B}")
+            assert_within(A, orc.gelu(ref), S, ACT_REL, f"mlp fused fwd1 GELU B={B}")
+            Y = host(csp.spmm_fwd(l2.h, dev(A)))
+            ref, S = orc.spmm_fwd(L2.out, L2.in_, L2.rows, L2.cols, L2.vals, A)
+            assert_within(Y, ref, S, FP32_REL, f"mlp fused fwd2 B={B}")
+            dH, dW2 = (host(t) for t in csp.spmm_bwd_act(l2.h, dev(dY), dev(A), dev(H), act="gelu"))
+            refa, Sa = orc.spmm_bwd_input(L2.out, L2.in_, L2.rows, L2.cols, L2.vals, dY)
+            assert_within(dH, refa * orc.gelu_grad(H.astype(np.float64)), Sa, ACT_REL, f"mlp fused dH B={B}")
+            refw, Sw = orc.spmm_bwd_values(L2.out, L2.in_, l2.canon["rows"], l2.canon["cols"], dY, A)
+            assert_within(dW2, refw, Sw, FP32_REL, f"mlp fused dW2 B={B}")
+            dX, dW1 = (host(t) for t in csp.spmm_bwd(l1.h, dev(dH), dev(X)))
+            ref, S = orc.spmm_bwd_input(L1.out, L1.in_, L1.rows, L1.cols, L1.vals, dH)
+            assert_within(dX, ref, S, FP32_REL, f"mlp fused dX1 B={B}")
+            ref, S = orc.spmm_bwd_values(L1.out, L1.in_, l1.canon["rows"], l1.canon["cols"], dH, X)
+            assert_within(dW1, ref, S, FP32_REL, f"mlp fused dW1 B={B}")
     finally:
         l1.close()
         l2.close()
