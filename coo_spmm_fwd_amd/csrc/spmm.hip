@@ -94,38 +94,50 @@ __device__ inline float slot_sum(float v)
 }
 
 // ------------------------------------------------------- batch-minor copy
-// One or two operands [B, n] -> [chunk][n][ld]; reads coalesced, writes
-// scattered (the small writes merge in L2).  The pad slots of the last chunk
-// (batch index >= B) are written as zeros, so consumers never mask them.
-template <typename T, typename I>
-__global__ __launch_bounds__(256) void k_batch_minor(const T *__restrict__ X1, I n1, T *__restrict__ O1,
-                                                     const T *__restrict__ X2, I n2, T *__restrict__ O2, I B,
-                                                     int ld_log2, I pad)
+// One or two operands [B, n] -> [n][LD] (B <= LD <= 64, pad slots b >= B
+// written as zeros, so consumers never mask them).  A workgroup transposes a
+// tile of kBmCols columns through LDS: reads go along the operand's rows
+// (coalesced, all of a thread's loads in flight together), and the tile's
+// output [kBmCols][LD] is one contiguous run (coalesced writes).  The LDS rows
+// are LD + 1 elements long, so the column-wise writes spread over the banks.
+constexpr int kBmCols = 32;
+constexpr int kBmThreads = 256;
+
+template <typename T, int LD>
+__global__ __launch_bounds__(kBmThreads) void k_batch_minor(const T *__restrict__ X1, int64_t n1, T *__restrict__ O1,
+                                                          const T *__restrict__ X2, int64_t n2, T *__restrict__ O2,
+                                                          int64_t B)
 {
-    const I ld = I(1) << ld_log2;
-    const I tot1 = B * n1, tot = tot1 + B * n2;
-    const I last = (B + pad) / ld - 1;  // chunk holding the pad slots
-    const I all = tot + pad * (n1 + n2);
-    for (I i = (I)blockIdx.x * blockDim.x + threadIdx.x; i < all; i += (I)gridDim.x * blockDim.x) {
-        if (i < tot) {
-            const bool first = i < tot1;
-            const I j = first ? i : i - tot1;
-            const I n = first ? n1 : n2;
-            const I b = j / n, c = j - b * n;
-            const I ch = b >> ld_log2, bl = b & (ld - 1);
-            const I dst = (((ch * n) + c) << ld_log2) + bl;
-            if (first) O1[dst] = X1[j];
-            else O2[dst] = X2[j];
-        } else {
-            I j = i - tot;
-            const bool first = j < pad * n1;
-            if (!first) j -= pad * n1;
-            const I c = j / pad, k = j - c * pad;
-            const I n = first ? n1 : n2;
-            const I dst = (((last * n) + c) << ld_log2) + (ld - pad + k);
-            if (first) O1[dst] = T(0);
-            else O2[dst] = T(0);
-        }
+    constexpr int N = LD * kBmCols;                         // elements of a tile
+    constexpr int E = (N + kBmThreads - 1) / kBmThreads;    // per thread
+    __shared__ T tile[kBmCols * (LD + 1)];
+    const int64_t tiles1 = (n1 + kBmCols - 1) / kBmCols;
+    const bool first = blockIdx.x < tiles1;
+    const T *__restrict__ X = first ? X1 : X2;
+    T *__restrict__ O = first ? O1 : O2;
+    const int64_t n = first ? n1 : n2;
+    const int64_t c0 = (first ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - tiles1) * kBmCols;
+    const int cols = n - c0 < kBmCols ? (int)(n - c0) : kBmCols;
+    T v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {  // every load of the thread issued before the first LDS store
+        const int i = threadIdx.x + e * kBmThreads;
+        const int b = i / kBmCols, c = i % kBmCols;
+        const bool ok = i < N && b < B && c < cols;
+        const T x = X[ok ? (int64_t)b * n + c0 + c : 0];
+        v[e] = ok ? x : T(0);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = threadIdx.x + e * kBmThreads;
+        if (i < N) tile[(i % kBmCols) * (LD + 1) + i / kBmCols] = v[e];
+    }
+    __syncthreads();
+    T *__restrict__ dst = O + c0 * LD;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int i = threadIdx.x + e * kBmThreads;
+        if (i < cols * LD) dst[i] = tile[(i / LD) * (LD + 1) + i % LD];
     }
 }
 
@@ -944,23 +956,24 @@ csp_status batch_minor(csp_layer *L, int64_t B, const void *X1, int64_t n1, void
 {
     if (B == 1) return CSP_OK;
     const int ld = pow2_ld(B);
-    int ld_log2 = 0;
-    while ((1 << ld_log2) < ld) ++ld_log2;
     if (!X2) n2 = 0;
-    const int64_t tot = B * (n1 + n2) + (ceil_div(B, ld) * ld - B) * (n1 + n2);
-    int64_t blocks = ceil_div(tot, 256);
-    if (blocks > 8192) blocks = 8192;
-    const int64_t pad = ceil_div(B, ld) * ld - B;
-    const bool small = tot + pad * (n1 + n2) < (int64_t(1) << 31);
-#define CSP_BM(T, I)                                                                                           \
-    k_batch_minor<T, I><<<(unsigned)blocks, 256, 0, s>>>((const T *)X1, (I)n1, (T *)O1, (const T *)X2, (I)n2, \
-                                                         (T *)O2, (I)B, ld_log2, (I)pad)
-    if (L->esz == 4) {
-        if (small) CSP_BM(float, int32_t); else CSP_BM(float, int64_t);
-    } else {
-        if (small) CSP_BM(uint16_t, int32_t); else CSP_BM(uint16_t, int64_t);
+    const int64_t blocks = ceil_div(n1, kBmCols) + ceil_div(n2, kBmCols);
+#define CSP_BMT(T, LDV)                                                                                        \
+    k_batch_minor<T, LDV><<<(unsigned)blocks, kBmThreads, 0, s>>>((const T *)X1, n1, (T *)O1, (const T *)X2, n2, \
+                                                                  (T *)O2, B)
+#define CSP_BM(LDV)                               \
+    if (L->esz == 4) CSP_BMT(float, LDV);         \
+    else CSP_BMT(uint16_t, LDV)
+    switch (ld) {
+    case 2: CSP_BM(2); break;
+    case 4: CSP_BM(4); break;
+    case 8: CSP_BM(8); break;
+    case 16: CSP_BM(16); break;
+    case 32: CSP_BM(32); break;
+    default: CSP_BM(64); break;
     }
 #undef CSP_BM
+#undef CSP_BMT
     CSP_LAUNCHED("k_batch_minor");
     return CSP_OK;
 }
