@@ -1,25 +1,35 @@
 """Throughput of the truly sparse COO layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--warm]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--batch B] [--warm]
 
 One step is one training pass of the layer over one batch: spmm_fwd, then
-spmm_bwd (input gradient and value gradient in one launch sequence).  The
-default workload is the single sparse linear layer 4096 x 4096 at 95%
-unstructured sparsity (838,861 stored fp32 entries), batch 16.
+spmm_bwd (input gradient and value gradient).  The default workload is the
+dynamic-sparse-training layer 8192 x 8192 at 95% unstructured sparsity
+(3,355,443 stored fp32 entries), batch 64; its full training step (products,
+an SGD update of the stored values, the refresh of their column-ordered copy
+and a prune-and-regrow restructure of 10% of the entries) is timed beside the
+products step.
 
 Inputs are resident in HBM before timing starts.  Unless --warm is given,
-steps cycle through enough replicas of the layer and its dense operands
-(together more than twice the 256 MiB last-level cache) that each step reads
-its data from HBM rather than from cache.
+every step, from the first warm-up step to the last step of the per-kernel
+timing pass, runs on replica g mod R of the layer and its dense operands (g
+counts steps), with R chosen so that the other R - 1 replicas between two uses
+of one replica touch more than twice the 256 MiB last-level cache: each step
+reads its data from HBM.
 
-Printed: one JSON line.  `value` is the effective bandwidth of the step:
-algorithmic bytes of forward + input gradient + value gradient (byte models
-below) over the measured step time.  `roofline` covers the dominant kernel,
-timed with a pair of HIP events that the library attaches to that kernel's
-dispatch (so they carry its own start and end), in a second pass with the
-same work; its `ceiling` holds a same-byte device copy and the launch floor
-measured on the same stream.  `cpu_baseline` times the CPU oracle (plain C
-loops, fp64 accumulation, one core) on the same workload.
+Printed: one JSON line.  `value` is the effective bandwidth of the products
+step: algorithmic bytes of forward + input gradient + value gradient (byte
+models below; the input gradient reads the layer's column-ordered value copy,
+so it is charged 8 bytes per entry, and the copy's refresh belongs to the
+training step that changes the values) over the measured step time.
+`roofline` covers the dominant kernel, timed with a pair of HIP events that
+the library attaches to that kernel's dispatch, in a second pass over the
+same replicas; its `ceiling` holds a same-byte device copy and the launch
+floor measured on the same stream.  `cpu_baseline` times the CPU oracle (plain
+C loops, fp64 accumulation, one core) and, beside it, the same loops in fp32
+on every host core.  `page_ratios` holds the pages' three ratio metrics
+(kernel at 95%, training and inference at 90%) against torch's dense and
+Dense+Mask layers on the same GPU, under the same cold protocol.
 """
 from __future__ import annotations
 
@@ -37,6 +47,9 @@ HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCE = os.path.join(ROOT, "coo_spmm_fwd_amd", "csrc", "spmm.hip")
+DEFAULT_WORKLOAD = "dst8192_b64_s95"
+RATIO_WORKLOAD_90 = "linear4096_b16_s90"
+SGD_LR = 1e-3
 
 
 # ------------------------------------------------------------------ byte models
@@ -46,8 +59,15 @@ def bytes_fwd(nnz, out, in_, B, sv=4, sx=4):
 
 
 def bytes_dx(nnz, out, in_, B):
-    """Input gradient: gathered value + permutation + row index per entry, column offsets, dY, dX."""
+    """Input gradient, permuted-read model: gathered value + permutation + row index per entry,
+    column offsets, dY read once, dX written once."""
     return nnz * (4 + 4 + 4) + 4 * (in_ + 1) + 4 * B * (in_ + out)
+
+
+def bytes_dx_mirror(nnz, out, in_, B, sv=4, sx=4):
+    """Input gradient over the column-ordered value copy: row index + copied value per entry,
+    column offsets, dY read once, dX written once."""
+    return nnz * (4 + sv) + 4 * (in_ + 1) + sx * B * (in_ + out)
 
 
 def bytes_dw(nnz, out, in_, B):
@@ -62,20 +82,32 @@ def bytes_gradients(nnz, out, in_, B):
     return nnz * 16 + 4 * (in_ + 1) + 4 * (out + 1) + 4 * B * (2 * in_ + out)
 
 
+def bytes_restructure(nnz):
+    """Prune-and-regrow with re-sort: read the 12-byte triples, write canonical and transposed arrays."""
+    return 36 * nnz
+
+
+def bytes_sgd_refresh(nnz):
+    """SGD on the stored values (read value and dW, write value) and the column-ordered copy's refresh
+    (read the permutation, gather the value, write the copy)."""
+    return 12 * nnz + 12 * nnz
+
+
 def source_sha() -> str:
     with open(KERNEL_SOURCE, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_for(kernel: str, launch_args: dict):
+def traffic_for(label: str, launch_args: dict):
     """HBM bytes per launch from committed counter runs, if taken on the current kernel source."""
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    e = rec.get(kernel)
-    if not e or e.get("source_sha") != source_sha() or e.get("args") != launch_args:
+    key = f"{launch_args['workload']}/B={launch_args['batch']}/{label}"
+    e = rec.get(key)
+    if not e or e.get("source_sha") != source_sha():
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -111,17 +143,12 @@ def _per_dispatch(rows, counter, match):
     return sum(per.values()) / len(per), len(per)
 
 
-def ingest_counters(fetch_dir, write_dir, workload, batch, copy_mib=256):
-    """Scale each counter by what it reads for a plain copy of known size, then store bytes per launch."""
-    from coo_spmm_fwd_amd import workloads as W
-    w = W.WORKLOADS[workload]
-    B = batch or w.batches[0]
-    ld = 1
-    while ld < min(B, 64):
-        ld *= 2
+def ingest_counters(fetch_dir, write_dir, workload, batch, label, kernel, copy_mib=256):
+    """Scale each counter by what it reads for a plain copy of known size, then store the bytes per
+    launch of `kernel` (a run made with --only, so one op's kernel) under workload/B/label."""
     fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
     copy_bytes = copy_mib << 20
-    # the calibration copy is the only copy dispatch of that size (grid of copy_bytes / 2048 work-items)
+    # the calibration copy is the only copy dispatch of that size (the largest copy grid of the run)
     big = [r for r in fetch + write if COPY_KERNEL_KEY in r.get("Kernel_Name", "")]
     gmax = max((int(r["Grid_Size"]) for r in big), default=0)
     is_copy = lambda n: COPY_KERNEL_KEY in n
@@ -129,31 +156,49 @@ def ingest_counters(fetch_dir, write_dir, workload, batch, copy_mib=256):
     write_c = [r for r in write if is_copy(r.get("Kernel_Name", "")) and int(r["Grid_Size"]) == gmax]
     cf, _ = _per_dispatch(fetch_c, "FETCH_SIZE", lambda n: True)
     cw, _ = _per_dispatch(write_c, "WRITE_SIZE", lambda n: True)
-    f_scale = copy_bytes / (cf * 1024) if cf else None
-    w_scale = copy_bytes / (cw * 1024) if cw else None
-    rec = {}
-    for name in (f"k_gradients<{ld}, csp::F32, false, 0, 1>", f"k_segment_spmm<{ld}, csp::F32, false, 0, 1>"):
-        m = lambda n, name=name: name in n
-        kf, nf = _per_dispatch(fetch, "FETCH_SIZE", m)
-        kw, nw = _per_dispatch(write, "WRITE_SIZE", m)
-        if kf is None or kw is None or f_scale is None or w_scale is None:
-            continue
-        fb, wb = kf * 1024 * f_scale, kw * 1024 * w_scale
-        rec[name] = {"source_sha": source_sha(), "args": {"workload": workload, "batch": B},
-                     "fetch_kib_raw": kf, "write_kib_raw": kw, "dispatches": [nf, nw],
-                     "copy_scale": {"fetch": f_scale, "write": w_scale, "copy_bytes": copy_bytes},
-                     "hbm_bytes_per_launch": round(fb + wb)}
+    if not cf or not cw:
+        raise SystemExit("no calibration copy in the counter runs (run them with --calibrate-copy)")
+    f_scale, w_scale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    m = lambda n: kernel in n
+    kf, nf = _per_dispatch(fetch, "FETCH_SIZE", m)
+    kw, nw = _per_dispatch(write, "WRITE_SIZE", m)
+    if kf is None or kw is None:
+        raise SystemExit(f"kernel {kernel!r} not in the counter runs")
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[f"{workload}/B={batch}/{label}"] = {
+        "kernel": kernel, "source_sha": source_sha(), "fetch_kib_raw": kf, "write_kib_raw": kw,
+        "dispatches": [nf, nw], "copy_scale": {"fetch": f_scale, "write": w_scale, "copy_bytes": copy_bytes},
+        "hbm_bytes_per_launch": round(kf * 1024 * f_scale + kw * 1024 * w_scale)}
     os.makedirs(os.path.dirname(PROFILE_TRAFFIC), exist_ok=True)
     with open(PROFILE_TRAFFIC, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps(rec, indent=1))
 
 
-# ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(kind, layers, acts, B, n_prune=0, seed=0, budget_s=12.0):
-    """The oracle as written (fp64 loops, one core) on the same step, repeated until ~budget_s."""
+# ------------------------------------------------------------------ CPU baselines
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(kind, layers, acts, B, sbytes, n_prune=0, seed=0, budget_s=10.0):
+    """The oracle as written (fp64 loops, one core) on the products step of the same workload and
+    batch, repeated until ~budget_s; beside it the same loops in fp32 over every host core
+    (oracle/parallel.c, median of 5 after one warm-up) and, for a training workload, the oracle's
+    restructure once."""
     import numpy as np
     import oracle
+    from oracle import parallel
     orc = oracle.default()
     X, dY = acts[B]["X"], acts[B]["dY"]
     canon = [orc.canonicalize(L.out, L.in_, L.rows, L.cols, L.vals) for L in layers]
@@ -186,9 +231,6 @@ def cpu_baseline(kind, layers, acts, B, n_prune=0, seed=0, budget_s=12.0):
         orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, X)
         orc.spmm_bwd_input(L.out, L.in_, L.rows, L.cols, L.vals, dY)
         orc.spmm_bwd_values(L.out, L.in_, canon[0]["rows"], canon[0]["cols"], dY, X)
-        if kind == "dst":
-            c = canon[0]
-            orc.restructure(L.out, L.in_, c["rows"], c["cols"], c["vals"], n_prune, seed, 1)
 
     reps, t_all = 0, 0.0
     while True:
@@ -199,34 +241,79 @@ def cpu_baseline(kind, layers, acts, B, n_prune=0, seed=0, budget_s=12.0):
         if t_all >= budget_s or reps >= 100:
             break
     step_s = t_all / reps
-    nbytes = step_bytes(kind, layers, B, n_prune)
-    return {"value": round(nbytes / step_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full step(s) of the same workload and batch on one core, {step_s * 1e3:.1f} ms per step"}
+    rec = {"value": round(sbytes / step_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{reps} full products step(s) of the same workload and batch on one core, "
+                     f"{step_s * 1e3:.1f} ms per step", "cpu_model": cpu_model()}
+    if kind == "dst":
+        c = canon[0]
+        t0 = time.perf_counter()
+        orc.restructure(layers[0].out, layers[0].in_, c["rows"], c["cols"], c["vals"], n_prune, seed, 1)
+        rec["restructure_ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+    if kind in ("linear", "dst", "inference") and layers[0].dtype == "f32":
+        par = parallel.Parallel()
+        L, c = layers[0], canon[0]
+
+        def par_step():
+            par.spmm_fwd(c, L.out, L.in_, X)
+            if kind != "inference":
+                par.spmm_bwd_input(c, L.out, L.in_, dY)
+                par.spmm_bwd_values(c, L.out, L.in_, dY, X)
+
+        par_step()
+        ts = []
+        for _ in range(5):
+            t0 = time.perf_counter()
+            par_step()
+            ts.append(time.perf_counter() - t0)
+        med = sorted(ts)[2]
+        rec["all_cores"] = {"value": round(sbytes / med / 1e9, 3), "unit": "GB/s", "cores": par.threads,
+                            "affinity_cores": len(os.sched_getaffinity(0)), "kind": "fp32 loops, OpenMP",
+                            "sample": f"median of 5 products steps after one warm-up, {med * 1e3:.2f} ms per step"}
+    return rec
 
 
-# ------------------------------------------------------------------ steps
-def dense_baselines(kind, layers, uploaded, X, dY, B, ours_ms, steps=20):
-    """The same step with torch's dense matmul (hipBLASLt) on the same shapes: a dense layer, and
-    Dense+Mask (the weight multiplied by its 0/1 mask before use, the weight gradient masked after).
-    Warm (one copy).  A restructure has no dense counterpart here, so a DST step is compared on its
-    products only.  Also checks that the dense forward agrees with the layer's."""
+# ------------------------------------------------------------------ cold replica cycle
+class Cycle:
+    """Step g runs on replica g mod R, through warm-up, graph uploads, timed steps and the timing
+    pass, so a step's previous use of its replica lies R - 1 steps back."""
+
+    def __init__(self, R):
+        self.R, self.g = R, 0
+
+    def next(self):
+        r = self.g % self.R
+        self.g += 1
+        return r
+
+
+def replicas_for(touched, warm):
+    return 1 if warm else max(2, -(-2 * MALL_BYTES // touched) + 1)
+
+
+# ------------------------------------------------------------------ dense references
+def dense_layers(layers, uploaded, dt, dev):
     import torch
-    dev = X.device
-    dt = X.dtype
     Ws, Ms = [], []
     for L, (r, c, v) in zip(layers, uploaded):
         Wd = torch.zeros((L.out, L.in_), dtype=dt, device=dev)
-        Wd[r.long(), c.long()] = v
+        Wd[r.long(), c.long()] = v.to(dt)
         Ws.append(Wd)
         Ms.append((Wd != 0).to(dt))
+    return Ws, Ms
+
+
+def dense_step_fn(kind, masked, forward_only=False):
+    """The step with torch's dense matmul (hipBLASLt): a dense layer, or Dense+Mask (the weight
+    multiplied by its 0/1 mask before use, the weight gradient masked after)."""
+    import torch
 
     def gelu_parts(H):
         cdf = 0.5 * (1.0 + torch.erf(H * 0.7071067811865476))
         return H * cdf, cdf + H * torch.exp(-0.5 * H * H) * 0.3989422804014327
 
-    def step(masked):
+    def step(Ws, Ms, X, dY):
         W = [w * m for w, m in zip(Ws, Ms)] if masked else Ws
-        if kind == "inference":
+        if kind in ("inference",) or forward_only:
             return X @ W[0].t()
         if kind == "stack":
             A = X
@@ -253,23 +340,40 @@ def dense_baselines(kind, layers, uploaded, X, dY, B, ours_ms, steps=20):
         if masked:
             dWd = dWd * Ms[0]
         return Y
+    return step
 
+
+def time_dense(kind, layers, uploaded, X, dY, steps, warm, forward_only=False):
+    """ms per step of the dense and Dense+Mask steps, each cycling through enough copies of its
+    weights (and masks) that a copy's reuse distance passes twice the last-level cache."""
+    import torch
+    dt, dev = X.dtype, X.device
+    W0, M0 = dense_layers(layers, uploaded, dt, dev)
     res = {}
+    esz = X.element_size()
     for name, masked in (("dense", False), ("dense_mask", True)):
-        for _ in range(3):
-            step(masked)
+        per = sum(w.numel() for w in W0) * esz * (2 if masked else 1)
+        R = replicas_for(per, warm)
+        copies = [([w.clone() for w in W0], [m.clone() for m in M0] if masked else M0) for _ in range(R)]
+        fn = dense_step_fn(kind, masked, forward_only)
+        cyc = Cycle(R)
+        for _ in range(max(3, R)):
+            Ws, Ms = copies[cyc.next()]
+            fn(Ws, Ms, X, dY)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
         for _ in range(steps):
-            step(masked)
+            Ws, Ms = copies[cyc.next()]
+            fn(Ws, Ms, X, dY)
         e1.record()
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / steps
-        res[name] = {"ms_per_step": round(ms, 5), "ratio": round(ms / ours_ms, 2)}
-    res["note"] = ("torch dense matmul (hipBLASLt) on the same shapes and dtype, warm; ratio = their step "
-                   "time / ours" + (" (products only: no restructure on the dense side)" if kind == "dst" else ""))
-    return res, Ws
+        res[name] = {"ms_per_step": round(e0.elapsed_time(e1) / steps, 5), "copies": R}
+        del copies
+    Yd = (X.float() @ W0[0].float().t()) if kind not in ("mlp", "stack") else None
+    del W0, M0
+    torch.cuda.empty_cache()
+    return res, Yd
 
 
 def practical_ceiling(nbytes, stream, launches=100):
@@ -324,92 +428,78 @@ def workload_kind(w) -> str:
         return "mlp"
     if w.prune_frac > 0:
         return "dst"
+    if w.ops == "fwd":
+        return "inference"
     return "linear"
 
 
-def step_bytes(kind, layers, B, n_prune=0):
-    """Algorithmic bytes of one step: forward + input gradient + value gradient of every layer
-    (forward only for inference), plus 36 B per entry for a restructure."""
+def step_bytes(kind, layers, B):
+    """Algorithmic bytes of one products step: forward + input gradient (over the column-ordered value
+    copy) + value gradient of every layer, forward only for inference."""
     tot = 0
     for L in layers:
         sv = 2 if L.dtype == "bf16" else 4
         tot += bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)
         if kind not in ("inference", "stack"):
-            tot += bytes_dx(L.nnz, L.out, L.in_, B) + bytes_dw(L.nnz, L.out, L.in_, B)
-    if kind == "dst":
-        tot += 36 * layers[0].nnz
+            tot += bytes_dx_mirror(L.nnz, L.out, L.in_, B, sv=sv, sx=sv) + bytes_dw(L.nnz, L.out, L.in_, B)
     return tot
 
 
-# ------------------------------------------------------------------ main
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="linear4096_b16_s95")
-    ap.add_argument("--batch", type=int, default=None)
-    ap.add_argument("--warm", action="store_true", help="reuse one replica (cache-resident data)")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timing")
-    ap.add_argument("--eager", action="store_true", help="launch each call from Python instead of graph replay")
-    ap.add_argument("--no-baselines", action="store_true", help="skip the dense and Dense+Mask torch baselines")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="also run a plain device copy of MIB MiB (reference for HBM byte counters)")
-    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_counters.json")
-    args = ap.parse_args()
-    if args.ingest_counters:
-        ingest_counters(*args.ingest_counters, workload=args.workload, batch=args.batch)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              "(each MI355X runs its own layer). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+# ------------------------------------------------------------------ one workload, measured
+class Bench:
+    """A workload's replicas on the GPU, its step as library calls, the cold replica cycle, graph
+    replay of the timed steps and the per-kernel timing pass."""
 
-    import torch
-    from coo_spmm_fwd_amd import binding as csp
-    from coo_spmm_fwd_amd import workloads as W
+    def __init__(self, name, B=None, warm=False, only=None, steps=100, eager=False):
+        import numpy as np
+        import torch
+        from coo_spmm_fwd_amd import binding as csp
+        from coo_spmm_fwd_amd import workloads as W
+        self.csp, self.torch = csp, torch
+        self.name, self.only = name, only
+        w, layers, acts = W.build(name)
+        self.w, self.layers, self.acts = w, layers, acts
+        self.kind = kind = workload_kind(w)
+        self.B = B = B or (max(w.batches) if kind == "mlp" else w.batches[0])
+        if B not in acts:
+            acts[B] = dict(X=W.random_dense((B, layers[0].in_), 11, dtype=w.dtype),
+                           dY=W.random_dense((B, layers[-1].out), 12, dtype=w.dtype))
+        self.dev = dev = torch.device("cuda", 0)
+        self.esz = esz = 2 if w.dtype == "bf16" else 4
+        # bytes one step touches in one replica
+        if kind in ("inference", "stack"):  # forward only: column index, value, task list, X and Y
+            touched = sum(L.nnz * (4 + esz) + 16 * (L.out + L.nnz // 512) + esz * B * (L.in_ + L.out)
+                          for L in layers)
+        else:  # both index orders, both value orders, dW, dense operands and their batch-minor copies
+            touched = sum(L.nnz * 28 + 4 * B * (3 * L.in_ + 2 * L.out) for L in layers)
+        self.touched = touched
+        # S consecutive steps per captured graph (S divides the timed steps); the cycle's length is a
+        # multiple of S, so the graphs partition it
+        self.S = 1 if eager else next(d for d in (10, 8, 5, 4, 2, 1) if steps % d == 0)
+        self.R = replicas_for(touched, warm)
+        if self.R > 1:
+            self.R = -(-self.R // self.S) * self.S
+        self.uploaded = [(self.t(L.rows), self.t(L.cols), self.t(L.vals)) for L in layers]
+        self.reps = [self.make_replica() for _ in range(self.R)]
+        self.ld = 1
+        while self.ld < min(B, 64):
+            self.ld *= 2
+        # longest row and column of each layer (segments over 512 entries are split into tasks)
+        self.seg_max = {id(L): tuple(int(np.bincount(a, minlength=n).max()) if L.nnz else 0
+                                     for a, n in ((L.rows, L.out), (L.cols, L.in_))) for L in layers}
+        self.cycle = Cycle(self.R)
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-
-    w, layers, acts = W.build(args.workload)
-    kind = workload_kind(w)
-    B = args.batch or (max(w.batches) if kind == "mlp" else w.batches[0])
-    if B not in acts:
-        acts[B] = dict(X=W.random_dense((B, layers[0].in_), 11, dtype=w.dtype),
-                       dY=W.random_dense((B, layers[-1].out), 12, dtype=w.dtype))
-    n_prune = int(w.prune_frac * layers[0].nnz) if kind == "dst" else 0
-    sbytes = step_bytes(kind, layers, B, n_prune)
-    # bytes one step touches in one replica: both index orders, both value orders, dW, dense operands
-    if kind in ("inference", "stack"):  # forward only: column index, value, task list, X and Y
-        sv = 2 if w.dtype == "bf16" else 4
-        touched = sum(L.nnz * (4 + sv) + 16 * (L.out + L.nnz // 512) + sv * B * (L.in_ + L.out) for L in layers)
-    else:
-        touched = sum(L.nnz * 28 + 4 * B * (3 * L.in_ + 2 * L.out) for L in layers)
-    R = 1 if args.warm else max(2, -(-2 * MALL_BYTES // touched) + 1)
-    # Steps per captured graph: a graph launch costs ~18 us of host time and ~7 us on the GPU, more
-    # than a small step itself, so several consecutive steps (over consecutive replicas) share one
-    # graph, as a launch-bound training or serving loop would capture them.  Exactly K steps are timed.
-    S = next(d for d in (10, 8, 5, 4, 2, 1) if args.steps % d == 0)
-    if args.eager or workload_kind(w) == "dst":
-        S = 1
-    if not args.warm:
-        R = -(-R // S) * S
-
-    def t(a):
+    def t(self, a):
+        torch = self.torch
         if a.dtype.name == "uint16":
-            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
+            return torch.from_numpy(a.view("int16")).view(torch.bfloat16).to(self.dev)
+        return torch.from_numpy(a).to(self.dev)
 
-    uploaded = [(t(L.rows), t(L.cols), t(L.vals)) for L in layers]
-    reps = []
-    for j in range(R):
-        st = {"h": [csp.sparse_layer_create(L.out, L.in_, *u) for L, u in zip(layers, uploaded)],
-              "X": t(acts[B]["X"]), "dY": t(acts[B]["dY"])}
+    def make_replica(self):
+        torch, csp, B, kind, dev = self.torch, self.csp, self.B, self.kind, self.dev
+        layers = self.layers
+        st = {"h": [csp.sparse_layer_create(L.out, L.in_, *u) for L, u in zip(layers, self.uploaded)],
+              "X": self.t(self.acts[B]["X"]), "dY": self.t(self.acts[B]["dY"])}
         if kind == "stack":
             st.update(acts=[torch.empty((B, L.out), device=dev, dtype=torch.bfloat16) for L in layers])
         elif kind == "mlp":
@@ -423,74 +513,66 @@ def main():
             st.update(Y=torch.empty((B, L.out), device=dev, dtype=st["X"].dtype))
             if kind != "inference":
                 st.update(dX=torch.empty((B, L.in_), device=dev), dW=torch.empty((L.nnz,), device=dev))
-        reps.append(st)
+        return st
 
-    ld = 1
-    while ld < min(B, 64):
-        ld *= 2
     # kernel names as the profiler prints them (template arguments: batch width, element type,
-    # 64-bit offsets, epilogue 0 none / 1 forward bias+activation / 2 input gradient times act')
-    dt_name = "csp::BF16" if w.dtype == "bf16" else "csp::F32"
-
-    esz = 2 if w.dtype == "bf16" else 4
-    lds_on = os.environ.get("COOSPMM_LDS_TABLES", "1")[:1] != "0"
-
-    def lds_fits(n, segment=False):
-        """The library gathers from an LDS copy of an operand of n columns (2 <= B <= 64,
-        <= 64 KiB; the segment passes also need every segment to be at most 64 tasks)."""
+    # 64-bit offsets, epilogue 0 none / 1 forward bias+activation / 2 input gradient times act',
+    # and 1 when the pass's task list has no split segment)
+    def lds_fits(self, n, segment=False):
+        lds_on = os.environ.get("COOSPMM_LDS_TABLES", "1")[:1] != "0"
         if segment and -(-n // 512) > 64:
             return False
-        return lds_on and 2 <= B <= 64 and n * ld * esz <= (64 << 10)
+        return lds_on and 2 <= self.B <= 64 and n * self.ld * self.esz <= (64 << 10)
 
-    grouped_on = os.environ.get("COOSPMM_GROUPED_SPLITS", "1")[:1] != "0"
-    import numpy as np
+    def dt_name(self):
+        return "csp::BF16" if self.w.dtype == "bf16" else "csp::F32"
 
-    # longest row and column of each layer (segments over 512 entries are split into tasks);
-    # computed once here, outside every timed loop
-    seg_max = {}
-    for L in layers:
-        seg_max[id(L)] = tuple(int(np.bincount(a, minlength=n).max()) if L.nnz else 0
-                               for a, n in ((L.rows, L.out), (L.cols, L.in_)))
-
-    def longest(L, rows):
-        return seg_max[id(L)][0 if rows else 1]
-
-    # The last template argument of the segment kernels is 1 when the pass's task list has no
-    # split segment (every task stores its output), else 0.
-    def fwd_name(L, epi=0):
-        ks = int(longest(L, True) <= 512)
-        if lds_fits(L.in_, segment=True):
-            return f"k_segment_lds<{ld}, {dt_name}, {epi}>"
-        # split rows finish inside the pass when no row can exceed 64 tasks
+    def fwd_name(self, L, epi=0):
+        ld, dt, B = self.ld, self.dt_name(), self.B
+        ks = int(self.seg_max[id(L)][0] <= 512)
+        grouped_on = os.environ.get("COOSPMM_GROUPED_SPLITS", "1")[:1] != "0"
+        if self.lds_fits(L.in_, segment=True):
+            return f"k_segment_lds<{ld}, {dt}, {epi}>"
         if grouped_on and B <= 8 and not ks and L.in_ <= 64 * 512:
-            return f"k_segment_grouped<{ld}, {dt_name}, false, {epi}>"
-        return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}, {ks}>"
+            return f"k_segment_grouped<{ld}, {dt}, false, {epi}>"
+        return f"k_segment_spmm<{ld}, {dt}, false, {epi}, {ks}>"
 
-    def grad_name(L, epi=0):
-        ks = int(longest(L, False) <= 512)
-        if lds_fits(max(L.in_, L.out)):
-            return f"k_gradients_lds<{ld}, {dt_name}, {epi}, {ks}>"
-        # spmm_bwd runs both gradient passes in one launch unless their two batch-minor
-        # operand tables exceed 2 MiB together (then the two kernels run back to back)
-        if esz * ld * (L.in_ + L.out) > (2 << 20):
-            return f"k_segment_spmm<{ld}, {dt_name}, false, {epi}, {ks}> + k_values_rows<{ld}, {dt_name}, false>"
-        return f"k_gradients<{ld}, {dt_name}, false, {epi}, {ks}>"
+    def dx_name(self, L, epi=0):
+        ks = int(self.seg_max[id(L)][1] <= 512)
+        return f"k_segment_spmm<{self.ld}, {self.dt_name()}, false, {epi}, {ks}>"
 
-    def calls(st, stream):
-        """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic bytes)."""
+    def dw_name(self, L):
+        return f"k_values_rows<{self.ld}, {self.dt_name()}, false>"
+
+    def grad_fused(self, L):
+        """spmm_bwd runs both gradient passes in one launch (k_gradients / k_gradients_lds) unless their
+        two batch-minor operand tables exceed 2 MiB together (then two kernels back to back)."""
+        return self.lds_fits(max(L.in_, L.out)) or self.esz * self.ld * (L.in_ + L.out) <= (2 << 20)
+
+    def grad_name(self, L, epi=0):
+        ks = int(self.seg_max[id(L)][1] <= 512)
+        if self.lds_fits(max(L.in_, L.out)):
+            return f"k_gradients_lds<{self.ld}, {self.dt_name()}, {epi}, {ks}>"
+        return f"k_gradients<{self.ld}, {self.dt_name()}, false, {epi}, {ks}>"
+
+    def calls(self, st, stream, split=False):
+        """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic
+        bytes).  split: time the two gradients of a single layer as separate calls when spmm_bwd would
+        run them as two kernels anyway (one main kernel per call)."""
+        csp, kind, B = self.csp, self.kind, self.B
         out = []
         if kind == "stack":
-            for li, (h, L) in enumerate(zip(st["h"], layers)):
+            for li, (h, L) in enumerate(zip(st["h"], self.layers)):
                 src = st["X"] if li == 0 else st["acts"][li - 1]
 
-                def f(h=h, src=src, dst=st["acts"][li], last=li + 1 == len(layers)):
+                def f(h=h, src=src, dst=st["acts"][li], last=li + 1 == len(self.layers)):
                     # GELU fused into the producing layer's epilogue
                     csp.spmm_fwd_act(h, src, act="none" if last else "gelu", Y=dst, stream=stream)
 
-                out.append((f"forward {li + 1}", h, f, fwd_name(L, 1), bytes_fwd(L.nnz, L.out, L.in_, B, sv=2, sx=2)))
+                out.append((f"forward {li + 1}", h, f, self.fwd_name(L, 1), bytes_fwd(L.nnz, L.out, L.in_, B, 2, 2)))
             return out
         if kind == "mlp":
-            (h1, h2), (L1, L2) = st["h"], layers
+            (h1, h2), (L1, L2) = st["h"], self.layers
 
             # GELU in the first layer's forward epilogue (A = GELU(H), H kept), GELU' in the
             # second layer's input-gradient epilogue (dH = (dY W2) * GELU'(H))
@@ -501,164 +583,290 @@ def main():
                 csp.spmm_bwd_act(h2, st["dY"], st["A"], st["H"], act="gelu", dX=st["dH"], dW=st["dW2"],
                                  stream=stream)
 
-            out.append(("forward 1", h1, f1, fwd_name(L1, 1), bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
-            out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream), fwd_name(L2),
-                        bytes_fwd(L2.nnz, L2.out, L2.in_, B)))
-            out.append(("backward 2", h2, b2, grad_name(L2, 2), bytes_gradients(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("forward 1", h1, f1, self.fwd_name(L1, 1), bytes_fwd(L1.nnz, L1.out, L1.in_, B)))
+            out.append(("forward 2", h2, lambda: csp.spmm_fwd(h2, st["A"], st["Y"], stream=stream),
+                        self.fwd_name(L2), bytes_fwd(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("backward 2", h2, b2, self.grad_name(L2, 2), bytes_gradients(L2.nnz, L2.out, L2.in_, B)))
             out.append(("backward 1", h1, lambda: csp.spmm_bwd(h1, st["dH"], st["X"], st["dX"], st["dW1"],
-                                                               stream=stream), grad_name(L1),
+                                                               stream=stream), self.grad_name(L1),
                         bytes_gradients(L1.nnz, L1.out, L1.in_, B)))
             return out
-        h, L = st["h"][0], layers[0]
-        sv = 2 if w.dtype == "bf16" else 4
-        out.append(("forward", h, lambda: csp.spmm_fwd(h, st["X"], st["Y"], stream=stream), fwd_name(L),
-                    bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)))
-        if kind != "inference":
-            out.append(("backward", h, lambda: csp.spmm_bwd(h, st["dY"], st["X"], st["dX"], st["dW"], stream=stream),
-                        grad_name(L), bytes_gradients(L.nnz, L.out, L.in_, B)))
-        return out
+        h, L = st["h"][0], self.layers[0]
+        sv = self.esz
+        ops = {
+            "fwd": ("forward", h, lambda: csp.spmm_fwd(h, st["X"], st["Y"], stream=stream), self.fwd_name(L),
+                    bytes_fwd(L.nnz, L.out, L.in_, B, sv=sv, sx=sv)),
+            "dx": ("input gradient", h, lambda: csp.spmm_bwd_input(h, st["dY"], st["dX"], stream=stream),
+                   self.dx_name(L), bytes_dx_mirror(L.nnz, L.out, L.in_, B)),
+            "dw": ("value gradient", h, lambda: csp.spmm_bwd_values(h, st["dY"], st["X"], st["dW"], stream=stream),
+                   self.dw_name(L), bytes_dw(L.nnz, L.out, L.in_, B)),
+        }
+        if self.only:
+            return [ops[self.only]]
+        out.append(ops["fwd"])
+        if kind == "inference":
+            return out
+        if split and not self.grad_fused(L):
+            return out + [ops["dx"], ops["dw"]]
+        bw = ("backward", h, lambda: csp.spmm_bwd(h, st["dY"], st["X"], st["dX"], st["dW"], stream=stream),
+              self.grad_name(L) if self.grad_fused(L) else f"{self.dx_name(L)} + {self.dw_name(L)}",
+              bytes_gradients(L.nnz, L.out, L.in_, B) if self.grad_fused(L)
+              else bytes_dx_mirror(L.nnz, L.out, L.in_, B) + bytes_dw(L.nnz, L.out, L.in_, B))
+        return out + [bw]
 
-    stream = torch.cuda.current_stream()
-
-    def run_calls(st, s):
-        for _, _, fn, _, _ in calls(st, s):
+    def run_step(self, st, stream):
+        for _, _, fn, _, _ in self.calls(st, stream):
             fn()
 
-    step_no = [0]
-
-    def after(st):  # the part of a step that cannot be captured (restructure reads back and syncs)
-        if kind == "dst":
-            csp.restructure(st["h"][0], n_prune, seed=w.seed, step=step_no[0], stream=stream)
-            step_no[0] += 1
-
-    for i in range(max(args.warmup, R)):  # eager warm-up; also sizes every layer's operand workspace
-        run_calls(reps[i % R], stream)
-        after(reps[i % R])
-    torch.cuda.synchronize()
-
-    graphs = []
-    # A restructure rebuilds the task lists (their sizes set launch grids), so a
-    # step that restructures is launched eagerly rather than from a captured graph.
-    use_graphs = not args.eager and kind != "dst"
-    if use_graphs:  # graph j runs steps over replicas jS .. jS + S - 1
-        for j in range(max(1, R // S)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for t in range(S):
-                    run_calls(reps[(j * S + t) % R], torch.cuda.current_stream())
-            graphs.append(g)
-        for i in range(-(-args.warmup // S)):
-            graphs[i % len(graphs)].replay()
+    def measure(self, steps, warmup, eager=False):
+        """Warm-up, graph capture (S consecutive steps per graph), one upload replay of every graph,
+        then exactly `steps` timed steps; all on the replica cycle.  Returns ms per step."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for _ in range(max(warmup, 1)):
+            self.run_step(self.reps[self.cycle.next()], stream)
         torch.cuda.synchronize()
+        S = self.S
+        graphs = []
+        if not eager:
+            o = self.cycle.g % self.R
+            for j in range(max(1, self.R // S)):  # graph j: the next S steps of the cycle
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for t in range(S):
+                        self.run_step(self.reps[(o + j * S + t) % self.R], torch.cuda.current_stream())
+                graphs.append(g)
+            for g in graphs:  # upload replay of every graph, continuing the cycle
+                g.replay()
+                self.cycle.g += S
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        e0.record(stream)
+        if graphs:
+            for i in range(steps // S):
+                graphs[i % len(graphs)].replay()
+                self.cycle.g += S
+        else:
+            for _ in range(steps):
+                self.run_step(self.reps[self.cycle.next()], stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - wall0
+        del graphs
+        return e0.elapsed_time(e1) / steps
 
-    # timed region: exactly K steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    if graphs:
-        for i in range(args.steps // S):
-            graphs[i % len(graphs)].replay()
-    else:
-        for i in range(args.steps):
-            run_calls(reps[i % R], stream)
-            after(reps[i % R])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
+    def kernel_pass(self, K):
+        """Same work, eager, continuing the cycle: the library attaches a pair of HIP events to each
+        call's main kernel dispatch (sparse_layer_time_next), so each pair carries that kernel's own
+        start and end.  The steps are queued behind a spin kernel so they run back to back."""
+        torch, csp = self.torch, self.csp
+        stream = torch.cuda.current_stream()
+        labels = [c[0] for c in self.calls(self.reps[0], stream, split=True)]
+        ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in labels]
+              for _ in range(K)]
+        for row in ev:
+            for a, b in row:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(2.0e9 * min(0.2, 1e-4 * K * len(labels))))
+        for i in range(K):
+            st = self.reps[self.cycle.next()]
+            for (label, h, fn, _, _), (a, b) in zip(self.calls(st, stream, split=True), ev[i]):
+                csp.sparse_layer_time_next(h, a, b)
+                fn()
+        torch.cuda.synchronize()
+        per = {}
+        for ci, (label, _, _, kname, kbytes) in enumerate(self.calls(self.reps[0], stream, split=True)):
+            # (kernel names and byte models do not depend on the replica)
+            ts = sorted(ev[i][ci][0].elapsed_time(ev[i][ci][1]) * 1e3 for i in range(K))
+            med = ts[K // 2] if K % 2 else 0.5 * (ts[K // 2 - 1] + ts[K // 2])
+            per[label] = {"kernel": kname, "us": sum(ts) / K, "median_us": med, "bytes": kbytes}
+        return per
 
-    # second pass, same work, eager: the library attaches a pair of HIP events to each call's main
-    # kernel dispatch (sparse_layer_time_next), so each pair carries that kernel's own start and end
-    K = args.steps
-    labels = [c[0] for c in calls(reps[0], stream)]
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in labels]
-          for _ in range(K)]
-    for row in ev:
-        for a, b in row:
-            a.record(stream)
-            b.record(stream)
-    torch.cuda.synchronize()
-    # Hold the GPU with a spin kernel while the K steps are queued, so that they run back to back
-    # as in the timed region instead of each waiting for its launch from the host.
-    if kind != "dst" and hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(2.0e9 * min(0.2, 1e-4 * K * len(labels))))
-    for i in range(K):
-        for (label, h, fn, _, _), (a, b) in zip(calls(reps[i % R], stream), ev[i]):
-            csp.sparse_layer_time_next(h, a, b)
-            fn()
-        after(reps[i % R])
-    torch.cuda.synchronize()
-    per_call = {}
-    for ci, (label, _, _, kname, kbytes) in enumerate(calls(reps[0], stream)):
-        ts = sorted(ev[i][ci][0].elapsed_time(ev[i][ci][1]) * 1e3 for i in range(K))
-        us = sum(ts) / K
-        med = ts[K // 2] if K % 2 else 0.5 * (ts[K // 2 - 1] + ts[K // 2])
-        per_call[label] = {"kernel": kname, "us": us, "median_us": med, "bytes": kbytes}
+    def dst_steps(self, n, n_prune):
+        """The full training step of the DST workload, eager, on the replica cycle: forward, both
+        gradients, SGD on the stored values (harness), refresh of the column-ordered copy, restructure
+        (which reads back once).  Events bracket the step and the restructure call on the stream."""
+        torch, csp = self.torch, self.csp
+        stream = torch.cuda.current_stream()
+        t_step, t_rs = [], []
+        for k in range(-1, n):  # step -1 is an untimed warm-up (first calls of the harness's torch kernels)
+            st = self.reps[self.cycle.next()]
+            h = st["h"][0]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+            csp.spmm_fwd(h, st["X"], st["Y"], stream=stream)
+            csp.spmm_bwd(h, st["dY"], st["X"], st["dX"], st["dW"], stream=stream)
+            v = csp.sparse_layer_values_tensor(h)
+            v.sub_(SGD_LR * st["dW"])
+            csp.sparse_layer_set_values(h, None, stream=stream)
+            e[1].record(stream)
+            csp.restructure(h, n_prune, seed=self.w.seed, step=1000 + k, stream=stream)
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            if k >= 0:
+                t_step.append(e[0].elapsed_time(e[2]))
+                t_rs.append(e[1].elapsed_time(e[2]))
+        # the gradient-informed regrow, scored with this batch's dY and X (one call)
+        st = self.reps[self.cycle.next()]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        csp.restructure_grad(st["h"][0], n_prune, st["dY"], st["X"], stream=stream)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        return sum(t_step) / n, sum(t_rs) / n, e[0].elapsed_time(e[1])
+
+    def destroy(self):
+        self.torch.cuda.synchronize()
+        for st in self.reps:
+            for h in st["h"]:
+                self.csp.sparse_layer_destroy(h)
+        self.reps = []
+
+
+def page_ratios(main, per_call, steps, warm):
+    """The pages' ratio metrics on this GPU (their own figures are context, on unnamed hardware):
+    the SpMM kernel at 95% sparsity against Dense+Mask (forward of this run's 95% layer), and one
+    sparse layer at 90% sparsity, training step and inference (forward), against dense and
+    Dense+Mask.  Ours and theirs run under the same cold protocol."""
+    import torch
+    out = {}
+    if main.kind in ("linear", "dst") and abs(main.w.density - 0.05) < 1e-9:
+        st = main.reps[0]
+        cur = [main.csp.sparse_layer_export(h) for h in st["h"]]
+        dn, Yd = time_dense(main.kind, main.layers, cur, st["X"], st["dY"], steps, warm, forward_only=True)
+        fwd_us = per_call["forward"]["us"]
+        Ys = main.csp.spmm_fwd(st["h"][0], st["X"]).float()
+        diff = float((Yd - Ys).abs().max())
+        out["kernel_95"] = {"workload": main.name, "ours_forward_kernel_us": round(fwd_us, 3),
+                            "dense_forward_us": round(dn["dense"]["ms_per_step"] * 1e3, 3),
+                            "dense_mask_forward_us": round(dn["dense_mask"]["ms_per_step"] * 1e3, 3),
+                            "vs_dense": round(dn["dense"]["ms_per_step"] * 1e3 / fwd_us, 2),
+                            "vs_dense_mask": round(dn["dense_mask"]["ms_per_step"] * 1e3 / fwd_us, 2),
+                            "forward_max_abs_diff": diff, "pages": "up to 7x vs Dense+Mask"}
+    for label, forward_only in (("training_90", False), ("inference_90", True)):
+        b = Bench(RATIO_WORKLOAD_90, warm=warm, only="fwd" if forward_only else None, steps=steps)
+        ms = b.measure(steps, 5)
+        st = b.reps[0]
+        cur = [b.csp.sparse_layer_export(h) for h in st["h"]]
+        dn, _ = time_dense(b.kind, b.layers, cur, st["X"], st["dY"], steps, warm, forward_only=forward_only)
+        out[label] = {"workload": RATIO_WORKLOAD_90, "batch": b.B, "ours_ms_per_step": round(ms, 5),
+                      "dense_ms_per_step": dn["dense"]["ms_per_step"],
+                      "dense_mask_ms_per_step": dn["dense_mask"]["ms_per_step"],
+                      "vs_dense": round(dn["dense"]["ms_per_step"] / ms, 2),
+                      "vs_dense_mask": round(dn["dense_mask"]["ms_per_step"] / ms, 2),
+                      "pages": "training 8x / 3.7x, inference 4x / 2x vs Dense+Mask / dense"}
+        b.destroy()
+        del b
+        torch.cuda.empty_cache()
+    out["note"] = ("torch dense matmul (hipBLASLt) on the same shapes and dtype; Dense+Mask multiplies the "
+                   "weight by its 0/1 mask before use and the weight gradient after; each side cycles through "
+                   "enough copies to read HBM; ratio = their time / ours")
+    return out
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--batch", type=int, default=None)
+    ap.add_argument("--warm", action="store_true", help="reuse one replica (cache-resident data)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baselines")
+    ap.add_argument("--eager", action="store_true", help="launch each call from Python instead of graph replay")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the dense baselines, page ratios, DST step, ceiling and CPU baselines")
+    ap.add_argument("--only", choices=("fwd", "dx", "dw"), default=None,
+                    help="run only this product call of a single-layer workload (for per-kernel counter runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (reference for HBM byte counters)")
+    ap.add_argument("--ingest-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "LABEL", "KERNEL"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of one --only op into "
+                         "profiles/traffic_counters.json under workload/B/LABEL")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(each MI355X runs its own layer). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.ingest_counters:
+        from coo_spmm_fwd_amd import workloads as W
+        w = W.WORKLOADS[args.workload]
+        ingest_counters(*args.ingest_counters[:2], workload=args.workload, batch=args.batch or w.batches[0],
+                        label=args.ingest_counters[2], kernel=args.ingest_counters[3])
+        return
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    extras = not (args.no_extras or args.only)
+
+    main_b = Bench(args.workload, args.batch, args.warm, args.only, args.steps, args.eager)
+    kind, layers, B = main_b.kind, main_b.layers, main_b.B
+    sbytes = step_bytes(kind, layers, B)
+    if args.only:
+        sbytes = main_b.calls(main_b.reps[0], None)[0][4]
+    ms_per_step = main_b.measure(args.steps, args.warmup, eager=args.eager)
+    reuse_bytes = (main_b.R - 1) * main_b.touched
+    per_call = main_b.kernel_pass(args.steps)
     dom_label = max(per_call, key=lambda k: per_call[k]["us"])
     dom = per_call[dom_label]
     achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
-    traffic = traffic_for(dom["kernel"], {"workload": args.workload, "batch": B})
+    traffic = traffic_for(dom_label, {"workload": args.workload, "batch": B})
+    stream = torch.cuda.current_stream()
 
-    restructure_ms = restructure_grad_ms = None
-    if kind in ("linear", "dst"):  # one restructure of 10% of the entries (second call: steady state)
-        for k in range(2):
-            torch.cuda.synchronize()
-            r0 = time.perf_counter()
-            csp.restructure(reps[0]["h"][0], layers[0].nnz // 10, seed=w.seed, step=12345 + k, stream=stream)
-            restructure_ms = (time.perf_counter() - r0) * 1e3
-        for k in range(2):  # the gradient-informed variant, scored with this batch's dY and X
-            torch.cuda.synchronize()
-            r0 = time.perf_counter()
-            csp.restructure_grad(reps[0]["h"][0], layers[0].nnz // 10, reps[0]["dY"], reps[0]["X"], stream=stream)
-            restructure_grad_ms = (time.perf_counter() - r0) * 1e3
+    dst = None
+    if kind == "dst" and extras:
+        n_prune = int(main_b.w.prune_frac * layers[0].nnz)
+        step_ms, rs_ms, rsg_ms = main_b.dst_steps(5, n_prune)
+        nnz = layers[0].nnz
+        rbytes = bytes_restructure(nnz)
+        dbytes = sbytes + bytes_sgd_refresh(nnz) + rbytes
+        dst = {"step": f"spmm_fwd + spmm_bwd + SGD on the values (harness, lr {SGD_LR}) + refresh of the "
+                       f"column-ordered copy + restructure({n_prune} of {nnz}), eager, on the replica cycle",
+               "ms_per_step": round(step_ms, 4), "bytes_per_step": dbytes,
+               "gbs": round(dbytes / (step_ms * 1e-3) / 1e9, 2),
+               "restructure_ms": round(rs_ms, 4), "restructure_bytes": rbytes,
+               "restructure_gbs": round(rbytes / (rs_ms * 1e-3) / 1e9, 2),
+               "restructure_frac": round(rbytes / (rs_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+               "restructure_grad_ms": round(rsg_ms, 4),
+               "note": "GPU time between events on the stream; the restructure reads back its accepted count "
+                       "once, so its bracket includes that round trip"}
 
-    baselines = None
-    if not args.no_baselines:
-        ours_ms = ms_per_step
-        if kind == "dst":  # products only, eager like the timed steps
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for i in range(args.steps):
-                run_calls(reps[i % R], stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ours_ms = e0.elapsed_time(e1) / args.steps
-        X0, dY0 = reps[0]["X"], reps[0]["dY"]
-        current = [csp.sparse_layer_export(h) for h in reps[0]["h"]]  # after any restructures
-        baselines, Ws = dense_baselines(kind, layers, current, X0, dY0, B, ours_ms)
-        if kind not in ("mlp", "stack"):  # the dense forward must agree with the layer's
-            Yd = (X0.float() @ Ws[0].float().t())
-            Ys = csp.spmm_fwd(reps[0]["h"][0], X0).float()
-            baselines["forward_max_abs_diff"] = float((Yd - Ys).abs().max())
-        baselines["ours_ms_per_step"] = round(ours_ms, 5)
-        del Ws
-
-    # not in counter runs: the calibration copy must be the run's only large copy
-    ceiling = None if args.calibrate_copy else practical_ceiling(dom["bytes"], stream)
+    ratios = page_ratios(main_b, per_call, min(args.steps, 20), args.warm) if extras else None
+    ceiling = practical_ceiling(dom["bytes"], stream) if extras and not args.calibrate_copy else None
 
     if args.calibrate_copy:
         n = (args.calibrate_copy << 20) // 4
-        src = torch.randn(n, device=dev)
-        dst = torch.empty_like(src)
+        src = torch.randn(n, device="cuda")
+        dst_t = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            dst_t.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst_t
 
-    del graphs
-    torch.cuda.synchronize()
-    for st in reps:
-        for h in st["h"]:
-            csp.sparse_layer_destroy(h)
+    wall = main_b.wall
+    R, S = main_b.R, main_b.S
+    main_b.destroy()
 
     value = sbytes / (ms_per_step * 1e-3) / 1e9
-    flops = sum(2 * L.nnz * B * (1 if kind in ("inference", "stack") else 3) for L in layers)
+    n_ops = 1 if (kind in ("inference", "stack") or args.only) else 3
+    flops = sum(2 * L.nnz * B * n_ops for L in layers)
     steps_desc = {"stack": f"{len(layers)} x spmm_fwd with GELU between (one token batch through the stack)",
                   "linear": "spmm_fwd + spmm_bwd (dX and dW)",
-                  "dst": f"spmm_fwd + spmm_bwd + restructure({n_prune} of {layers[0].nnz})",
+                  "dst": "spmm_fwd + spmm_bwd (dX and dW); the full training step is under dst_step",
                   "inference": "spmm_fwd",
                   "mlp": "fwd1 with GELU epilogue, fwd2, bwd2 (dA * GELU'(H) epilogue, dW2), bwd1 (dX, dW1)"}[kind]
+    if args.only:
+        steps_desc = {"fwd": "spmm_fwd", "dx": "spmm_bwd_input", "dw": "spmm_bwd_values"}[args.only] + " only"
+    w = main_b.w
     rec = {
         "metric": "SpMM fwd+bwd effective GB/s and GFLOP/s (2*nnz*B); % of HBM roofline",
         "value": round(value, 2),
@@ -676,7 +884,9 @@ def main():
                    "layers": [{"out": L.out, "in": L.in_, "nnz": L.nnz} for L in layers], "batch": B,
                    "sparsity": round(1 - layers[0].nnz / (layers[0].out * layers[0].in_), 4), "step": steps_desc,
                    "replicas": R, "cache": "warm" if args.warm else "cold",
-                   "launch": f"hip_graph, {S} steps per graph" if use_graphs else "eager"},
+                   "reuse_distance_bytes": reuse_bytes,
+                   "launch": f"hip_graph, {S} steps per graph" if not args.eager else "eager",
+                   "bytes_per_step": sbytes},
         "gflops": round(flops / (ms_per_step * 1e-3) / 1e9, 2),
         "hbm_frac": round(value / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -685,14 +895,15 @@ def main():
                      "median_launch_us": round(dom["median_us"], 3),
                      "bytes_per_launch": dom["bytes"], "ceiling": ceiling},
         "kernels_us": {k: round(v["us"], 3) for k, v in per_call.items()},
-        "restructure_ms": None if restructure_ms is None else round(restructure_ms, 3),
-        "restructure_grad_ms": None if restructure_grad_ms is None else round(restructure_grad_ms, 3),
         "wall_s": round(wall, 3),
     }
-    if baselines is not None:
-        rec["dense_baselines"] = baselines
-    if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(kind, layers, acts, B, n_prune, w.seed)
+    if dst is not None:
+        rec["dst_step"] = dst
+    if ratios is not None:
+        rec["page_ratios"] = ratios
+    if extras and not args.no_cpu:
+        n_prune = int(w.prune_frac * layers[0].nnz) if kind == "dst" else 0
+        rec["cpu_baseline"] = cpu_baseline(kind, layers, main_b.acts, B, sbytes, n_prune, w.seed)
     print(json.dumps(rec), flush=True)
 
 

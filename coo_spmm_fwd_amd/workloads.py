@@ -73,6 +73,9 @@ WORKLOADS = {
                  "fwd+dX+dW then restructure", steps=10, prune_frac=0.10),
         Workload("stack16384x4_zipf_s99_bf16", ((16384, 16384),) * 4, 0.01, (1, 4), 0.02, "bf16", "zipf", 6,
                  "fwd of four layers, GELU between, one graph per token", gelu=True),
+        # the pages' single-layer comparisons at 90% sparsity (training step and inference) on the
+        # 4096-square shape
+        Workload("linear4096_b16_s90", ((4096, 4096),), 0.10, (16,), 0.02, "f32", "uniform", 7, "fwd+dX+dW"),
     )
 }
 

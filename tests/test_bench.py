@@ -1,5 +1,6 @@
 """bench.py's contract pieces that run without a GPU: the byte models behind
-`value` and `roofline.achieved`, and the refusal of more than one GPU."""
+`value` and `roofline.achieved`, the cold replica cycle, and the refusal of more
+than one GPU."""
 import os
 import subprocess
 import sys
@@ -43,3 +44,36 @@ def test_refuses_more_than_one_gpu():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_mirror_and_restructure_bytes():
+    """The input gradient over the column-ordered value copy moves 8 B per entry (row index and copied
+    value); restructure 36 B per entry; the products step of the 8192-square B=64 layer adds up the
+    three per-op models."""
+    nnz, out, in_, B = 3355443, 8192, 8192, 64
+    assert bench.bytes_dx_mirror(nnz, out, in_, B) == nnz * 8 + 4 * 8193 + 4 * 64 * 16384
+    assert bench.bytes_restructure(nnz) == 120_795_948
+
+    class L:
+        pass
+    lay = L()
+    lay.nnz, lay.out, lay.in_, lay.dtype = nnz, out, in_, "f32"
+    assert bench.step_bytes("dst", [lay], B) == (bench.bytes_fwd(nnz, out, in_, B) + bench.bytes_dx_mirror(nnz, out, in_, B)
+                                                 + bench.bytes_dw(nnz, out, in_, B))
+    assert bench.step_bytes("inference", [lay], B) == bench.bytes_fwd(nnz, out, in_, B)
+
+
+def test_cold_cycle_reuse_distance():
+    """Every step, whatever the warm-up and step counts, reuses its replica R - 1 steps later, and R
+    is chosen so that R - 1 replicas exceed twice the last-level cache."""
+    for touched in (10 << 20, 94 << 20, 300 << 20):
+        R = bench.replicas_for(touched, warm=False)
+        assert (R - 1) * touched >= 2 * bench.MALL_BYTES
+        cyc = bench.Cycle(R)
+        last = {}
+        for g in range(5 * R + 3):
+            r = cyc.next()
+            if r in last:
+                assert g - last[r] == R
+            last[r] = g
+    assert bench.replicas_for(94 << 20, warm=True) == 1
