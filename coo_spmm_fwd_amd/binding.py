@@ -18,7 +18,7 @@ CSP_F32, CSP_BF16 = 0, 1
 STATUS = {0: "CSP_OK", -1: "CSP_ERR_INVALID_ARG", -2: "CSP_ERR_INDEX_RANGE", -3: "CSP_ERR_DUPLICATE",
           -4: "CSP_ERR_NO_MEMORY", -5: "CSP_ERR_HIP", -6: "CSP_ERR_DTYPE"}
 CSP_ACT_NONE, CSP_ACT_GELU = 0, 1
-EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_bwd_input", "spmm_bwd_values", "spmm_bwd",
+EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_fwd_static", "spmm_bwd_input", "spmm_bwd_values", "spmm_bwd",
             "spmm_fwd_act", "spmm_bwd_input_act", "spmm_bwd_act", "restructure_grad",
             "restructure", "sparse_layer_nnz", "sparse_layer_shape", "sparse_layer_export",
             "sparse_layer_export_index", "sparse_layer_values", "sparse_layer_set_values", "sparse_layer_time_next",
@@ -50,6 +50,8 @@ def load(path: str = LIB_PATH):
     L.sparse_layer_destroy.argtypes = [c_void_p]
     L.spmm_fwd.restype = c_int
     L.spmm_fwd.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]
+    L.spmm_fwd_static.restype = c_int
+    L.spmm_fwd_static.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]
     L.spmm_bwd_input.restype = c_int
     L.spmm_bwd_input.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_void_p]
     L.spmm_bwd_values.restype = c_int
@@ -174,6 +176,19 @@ def spmm_fwd(layer: int, X, Y=None, stream=None):
         Y = _torch().empty((B, out), dtype=X.dtype, device=X.device)
     yp = _dev(Y, "Y", _torch_dtype(dt), (B, out))
     _check(load().spmm_fwd(c_void_p(layer), xp, B, yp, _stream(stream)))
+    return Y
+
+
+def spmm_fwd_static(layer: int, X, Y=None, stream=None):
+    """Y[B, out] = X[B, in] W^T with the call's workspace in the library's static per-GPU array
+    (no allocation by the library; calls overlapping on one GPU race)."""
+    out, in_, dt = sparse_layer_shape(layer)
+    B = int(X.shape[0])
+    xp = _dev(X, "X", _torch_dtype(dt), (B, in_))
+    if Y is None:
+        Y = _torch().empty((B, out), dtype=X.dtype, device=X.device)
+    yp = _dev(Y, "Y", _torch_dtype(dt), (B, out))
+    _check(load().spmm_fwd_static(c_void_p(layer), xp, B, yp, _stream(stream)))
     return Y
 
 

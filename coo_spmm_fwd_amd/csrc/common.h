@@ -210,9 +210,19 @@ struct FwdEpilogue {
     void *pre = nullptr;
     int gelu = 0;
 };
+// Workspace of a forward call: the batch-minor copy of the operand slice and
+// the split tasks' partial sums.  launch_fwd uses the layer's own workspace
+// unless one is passed.
+struct FwdWork {
+    void *operand = nullptr;
+    float *partial = nullptr;
+};
 // fe == nullptr: plain forward.  act_in != nullptr: the input gradient is
 // multiplied by GELU'(act_in[b, c]) (act_in [B, in], layer dtype).
-csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s);
+csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s,
+                      const FwdWork *work = nullptr);
+// Bytes of each FwdWork buffer a forward of B rows needs (its largest slice).
+csp_status fwd_work_bytes(csp_layer *L, int64_t B, size_t *operand_bytes, size_t *partial_bytes);
 csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s);
 csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s);
 csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "common.h"
@@ -163,6 +164,33 @@ csp_status alloc_layer(csp_layer *L)
     return CSP_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Static workspace of spmm_fwd_static: one array per GPU, held until the
+// process ends.  In host code the array's name stands for a host-side symbol;
+// its device address on each GPU comes from hipGetSymbolAddress, taken once per
+// device with that device current, and only that address reaches kernels.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+void *g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+csp_status scratch_on(int dev, void **ptr)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return set_error(CSP_ERR_HIP, "device %d is beyond the static workspace table (%d devices)", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_error(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return set_error(CSP_ERR_HIP, "hipGetSymbolAddress(scratch) gave no address");
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return CSP_OK;
+}
+
 uint32_t regrow_word(const csp_layer *L, float v)
 {
     uint32_t u;
@@ -264,6 +292,29 @@ csp_status spmm_fwd_act(sparse_layer_t L, const void *X, int64_t B, const void *
     fe.pre = H;
     fe.gelu = act == CSP_ACT_GELU;
     return launch_fwd(L, X, B, Y, &fe, (hipStream_t)stream);
+}
+
+csp_status spmm_fwd_static(sparse_layer_t L, const void *X, int64_t B, void *Y, void *stream)
+{
+    if (!L || !X || !Y) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_fwd_static");
+    if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
+    DeviceGuard g(L->device);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    size_t ob = 0, pb = 0;
+    csp_status st = fwd_work_bytes(L, B, &ob, &pb);
+    if (st != CSP_OK) return st;
+    const size_t ob_al = (ob + 255) & ~size_t(255);
+    if (ob_al + pb > kScratchBytes)
+        return set_error(CSP_ERR_INVALID_ARG,
+                         "spmm_fwd_static needs %zu bytes of workspace for this layer and batch; its static "
+                         "array holds %zu (use spmm_fwd)", ob_al + pb, kScratchBytes);
+    void *base = nullptr;
+    st = scratch_on(L->device, &base);
+    if (st != CSP_OK) return st;
+    FwdWork wk;
+    wk.operand = base;
+    wk.partial = reinterpret_cast<float *>(static_cast<unsigned char *>(base) + ob_al);
+    return launch_fwd(L, X, B, Y, nullptr, (hipStream_t)stream, &wk);
 }
 
 csp_status spmm_bwd_input(sparse_layer_t L, const void *dY, int64_t B, void *dX, void *stream)

@@ -1020,12 +1020,12 @@ inline bool wide_operand(int64_t n, int ld) { return n * (int64_t)ld >= (int64_t
 
 template <class D, int E>
 csp_status split_fixup(csp_layer *L, const TaskList &TL, int64_t B, int64_t n_seg, void *out, const Epi &ep,
-                       hipStream_t s)
+                       hipStream_t s, float *partial = nullptr)
 {
     if (TL.nsplit == 0) return CSP_OK;
     const int ld = pow2_ld(B);
     k_split_fixup<D, E><<<(unsigned)ceil_div(TL.nsplit * B, 256), 256, 0, s>>>(
-        TL.split, TL.nsplit, L->act.partial, B, ld, n_seg, (typename D::T *)out, ep);
+        TL.split, TL.nsplit, partial ? partial : L->act.partial, B, ld, n_seg, (typename D::T *)out, ep);
     CSP_LAUNCHED("k_split_fixup");
     return CSP_OK;
 }
@@ -1191,7 +1191,8 @@ csp_status grouped_dispatch(csp_layer *L, const TaskList &TL, const int32_t *seg
 }
 
 template <class D, int E>
-csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const Epi &ep, hipStream_t s)
+csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const Epi &ep, hipStream_t s,
+                        float *partial)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
@@ -1201,7 +1202,7 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
     const unsigned grid = (unsigned)ceil_div(TL.count, kPW);
     const bool ks = TL.nsplit == 0;
 #define CSP_FWD_ARGS \
-    TL.desc, TL.count, L->row_ptr, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, L->act.partial, (T *)Y, ep
+    TL.desc, TL.count, L->row_ptr, L->cols, (const T *)L->vals, (const T *)XT, L->in, L->out, B, partial, (T *)Y, ep
 #define CSP_FWD(LDV, W)                                                             \
     if (ks) launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 1>, grid, kPW * kWave, 0, s, CSP_FWD_ARGS);    \
     else launch_main(L, kTimeBoth, k_segment_spmm<LDV, D, W, E, 0>, grid, kPW * kWave, 0, s, CSP_FWD_ARGS)
@@ -1209,7 +1210,7 @@ csp_status fwd_dispatch(csp_layer *L, const void *XT, int64_t B, void *Y, const 
 #undef CSP_FWD
 #undef CSP_FWD_ARGS
     CSP_LAUNCHED("k_segment_spmm (forward)");
-    return split_fixup<D, E>(L, TL, B, L->out, Y, ep, s);
+    return split_fixup<D, E>(L, TL, B, L->out, Y, ep, s, partial);
 }
 
 template <class D, int E>
@@ -1316,7 +1317,8 @@ Epi make_epi(const FwdEpilogue *fe)
     return ep;
 }
 
-csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s)
+csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s,
+                     const FwdWork &wk)
 {
     csp_status st = CSP_OK;
     const Epi ep = make_epi(fe);
@@ -1330,12 +1332,26 @@ csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdE
         return fe ? segment_lds_dispatch<F32, kEpiForward>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s)
                   : segment_lds_dispatch<F32, kEpiNone>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s);
     }
-    st = batch_minor(L, B, X, L->in, L->act.a, nullptr, 0, nullptr, s);
+    st = batch_minor(L, B, X, L->in, wk.operand, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
-    const void *xt = B == 1 ? X : L->act.a;
+    const void *xt = B == 1 ? X : wk.operand;
+    float *pt = wk.partial;
     if (L->dtype == CSP_BF16)
-        return fe ? fwd_dispatch<BF16, kEpiForward>(L, xt, B, Y, ep, s) : fwd_dispatch<BF16, kEpiNone>(L, xt, B, Y, ep, s);
-    return fe ? fwd_dispatch<F32, kEpiForward>(L, xt, B, Y, ep, s) : fwd_dispatch<F32, kEpiNone>(L, xt, B, Y, ep, s);
+        return fe ? fwd_dispatch<BF16, kEpiForward>(L, xt, B, Y, ep, s, pt) : fwd_dispatch<BF16, kEpiNone>(L, xt, B, Y, ep, s, pt);
+    return fe ? fwd_dispatch<F32, kEpiForward>(L, xt, B, Y, ep, s, pt) : fwd_dispatch<F32, kEpiNone>(L, xt, B, Y, ep, s, pt);
+}
+
+// Workspace one forward slice of B rows needs: the batch-minor operand copy
+// (none for B = 1 or the LDS-table path) and the split tasks' partial sums
+// (none without split rows or when they finish inside the pass).
+void fwd_slice_work(csp_layer *L, int64_t B, size_t *operand_bytes, size_t *partial_bytes)
+{
+    *operand_bytes = *partial_bytes = 0;
+    if (lds_segment_fits(L, B, L->in)) return;
+    const int ld = pow2_ld(B);
+    if (B > 1) *operand_bytes = (size_t)L->esz * ld * (size_t)L->in;
+    const TaskList &TL = fwd_tasks(L, B);
+    if (TL.nsplit > 0 && !grouped_splits(TL, B, L->in, L->in)) *partial_bytes = sizeof(float) * ld * (size_t)TL.count;
 }
 
 csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s)
@@ -1419,8 +1435,30 @@ inline const void *rows_at(const void *p, int64_t r, int64_t n, int esz)
 inline void *rows_at(void *p, int64_t r, int64_t n, int esz) { return p ? (char *)p + r * n * esz : nullptr; }
 }  // namespace
 
-csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s)
+csp_status fwd_work_bytes(csp_layer *L, int64_t B, size_t *operand_bytes, size_t *partial_bytes)
 {
+    *operand_bytes = *partial_bytes = 0;
+    // the slices are kSliceB rows, then the remainder
+    const int64_t sizes[2] = {B < kSliceB ? B : kSliceB, B > kSliceB ? (B - 1) % kSliceB + 1 : 0};
+    for (int64_t bs : sizes) {
+        if (bs <= 0) continue;
+        size_t o = 0, p = 0;
+        fwd_slice_work(L, bs, &o, &p);
+        if (o > *operand_bytes) *operand_bytes = o;
+        if (p > *partial_bytes) *partial_bytes = p;
+    }
+    return CSP_OK;
+}
+
+csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s,
+                      const FwdWork *work)
+{
+    FwdWork wk;
+    if (work) wk = *work;
+    else {
+        wk.operand = L->act.a;
+        wk.partial = L->act.partial;
+    }
     for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
         const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
         FwdEpilogue f{};
@@ -1429,7 +1467,7 @@ csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const Fwd
             f.pre = rows_at(f.pre, b0, L->out, L->esz);
         }
         const csp_status st = fwd_slice(L, rows_at(X, b0, L->in, L->esz), bs, rows_at(Y, b0, L->out, L->esz),
-                                        fe ? &f : nullptr, s);
+                                        fe ? &f : nullptr, s, wk);
         if (st != CSP_OK) return st;
     }
     return CSP_OK;

@@ -95,6 +95,28 @@ void sparse_layer_destroy(sparse_layer_t layer);
 csp_status spmm_fwd(sparse_layer_t layer, const void *X, int64_t B, void *Y, void *stream);
 
 /*
+ * spmm_fwd_static -- spmm_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same kernels, arguments and results (bit for bit) as
+ * spmm_fwd, but the call's workspace -- the batch-minor copy of X and the
+ * partial sums of rows split over several tasks -- lives in one static device
+ * array of 16 MiB per GPU (held until the process ends) instead of the
+ * layer's own workspace.  The call allocates and frees nothing.  Its largest
+ * batch slice (at most 64 rows) needs esz * ld * in bytes for the copy of X
+ * (ld = the slice's rows rounded up to a power of two; esz = 4 for fp32, 2 for
+ * bf16; none for one row, or when the forward reads X through the on-chip
+ * table path) and, when some row is split over several tasks and finished in
+ * a separate pass, 4 * ld bytes per task of the layer's row task list; a layer
+ * and batch that need more than 16 MiB get CSP_ERR_INVALID_ARG before any
+ * launch (use spmm_fwd).  Nothing in the array
+ * needs to start at zero.  All calls on one GPU share its array: calls that
+ * overlap on one GPU (two streams, or two host threads) race and give wrong
+ * results; serialize them.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) once.
+ */
+csp_status spmm_fwd_static(sparse_layer_t layer, const void *X, int64_t B, void *Y, void *stream);
+
+/*
  * spmm_bwd_input -- gradient with respect to the layer input (Abstract:
  * gradients are backpropagated on the sparse storage):
  *     dX[b, c] = sum over stored k with col_k = c of v_k * dY[b, row_k]
