@@ -128,6 +128,10 @@ struct csp_layer {
     // after a restructure that skipped it uses the plain row list.
     bool packed_valid = false, packed_pending = false, narrow_seen = false;
     bool created = false;  // set once sparse_layer_create has finished
+    // Set when a restructure fails part way: its offsets, transposed view and
+    // task lists may then describe a layer that was never completed, so every
+    // later call but destroy refuses the layer.
+    bool broken = false;
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request

@@ -191,6 +191,22 @@ csp_status scratch_on(int dev, void **ptr)
     return CSP_OK;
 }
 
+// Every call that reads or changes the layer's contents refuses a layer left
+// incomplete by a failed restructure.
+csp_status check_usable(const csp_layer *L)
+{
+    if (L->broken)
+        return set_error(CSP_ERR_INVALID_ARG,
+                         "the layer was left incomplete by a failed restructure; destroy it and create it again");
+    return CSP_OK;
+}
+
+#define CSP_USABLE(L)                                     \
+    do {                                                  \
+        const csp_status u_ = ::csp::check_usable(L);     \
+        if (u_ != CSP_OK) return u_;                      \
+    } while (0)
+
 uint32_t regrow_word(const csp_layer *L, float v)
 {
     uint32_t u;
@@ -274,6 +290,7 @@ csp_status spmm_fwd(sparse_layer_t L, const void *X, int64_t B, void *Y, void *s
     if (!L || !X || !Y) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_fwd");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     return launch_fwd(L, X, B, Y, nullptr, (hipStream_t)stream);
 }
@@ -286,6 +303,7 @@ csp_status spmm_fwd_act(sparse_layer_t L, const void *X, int64_t B, const void *
     if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
     if (H && H == Y) return set_error(CSP_ERR_INVALID_ARG, "H must not overlap Y");
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     FwdEpilogue fe;
     fe.bias = bias;
@@ -299,6 +317,7 @@ csp_status spmm_fwd_static(sparse_layer_t L, const void *X, int64_t B, void *Y, 
     if (!L || !X || !Y) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_fwd_static");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     size_t ob = 0, pb = 0;
     csp_status st = fwd_work_bytes(L, B, &ob, &pb);
@@ -322,6 +341,7 @@ csp_status spmm_bwd_input(sparse_layer_t L, const void *dY, int64_t B, void *dX,
     if (!L || !dY || !dX) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_input");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     return launch_bwd_input(L, dY, B, dX, nullptr, (hipStream_t)stream);
 }
@@ -334,6 +354,7 @@ csp_status spmm_bwd_input_act(sparse_layer_t L, const void *dY, int64_t B, csp_a
     if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
     if (act == CSP_ACT_GELU && !H_in) return set_error(CSP_ERR_INVALID_ARG, "CSP_ACT_GELU needs H_in");
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     return launch_bwd_input(L, dY, B, dX, act == CSP_ACT_GELU ? H_in : nullptr, (hipStream_t)stream);
 }
@@ -343,6 +364,7 @@ csp_status spmm_bwd_values(sparse_layer_t L, const void *dY, const void *X, int6
     if (!L || !dY || !X || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_values");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     return launch_bwd_values(L, dY, X, B, dW, (hipStream_t)stream);
 }
@@ -352,6 +374,7 @@ csp_status spmm_bwd(sparse_layer_t L, const void *dY, const void *X, int64_t B, 
     if (!L || !dY || !X || !dX || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd");
     if (B <= 0 || B > kIndexLimit) return set_error(CSP_ERR_INVALID_ARG, "batch %lld outside [1, 2^31)", (long long)B);
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     return launch_bwd(L, dY, X, B, dX, dW, nullptr, (hipStream_t)stream);
 }
@@ -364,6 +387,7 @@ csp_status spmm_bwd_act(sparse_layer_t L, const void *dY, const void *X, int64_t
     if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
     if (act == CSP_ACT_GELU && !H_in) return set_error(CSP_ERR_INVALID_ARG, "CSP_ACT_GELU needs H_in");
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     return launch_bwd(L, dY, X, B, dX, dW, act == CSP_ACT_GELU ? H_in : nullptr, (hipStream_t)stream);
 }
@@ -376,6 +400,7 @@ csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_
         return set_error(CSP_ERR_INVALID_ARG, "n_prune %lld outside [0, nnz = %lld]", (long long)n_prune,
                          (long long)L->nnz);
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
     csp_status st = run_restructure(L, n_prune, seed, step, regrow_word(L, regrow_value), s);
@@ -383,6 +408,7 @@ csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_
         hipError_t e = hipStreamSynchronize(s);
         if (e != hipSuccess) st = hip_error(e, "restructure");
     }
+    if (st != CSP_OK) L->broken = true;
     return st;
 }
 
@@ -395,6 +421,7 @@ csp_status restructure_grad(sparse_layer_t L, int64_t n_prune, const void *dY, c
         return set_error(CSP_ERR_INVALID_ARG, "n_prune %lld outside [0, nnz = %lld]", (long long)n_prune,
                          (long long)L->nnz);
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
     csp_status st = restructure_gradient(L, n_prune, dY, X, B, regrow_word(L, regrow_value), s);
@@ -402,6 +429,7 @@ csp_status restructure_grad(sparse_layer_t L, int64_t n_prune, const void *dY, c
         hipError_t e = hipStreamSynchronize(s);
         if (e != hipSuccess) st = hip_error(e, "restructure_grad");
     }
+    if (st != CSP_OK) L->broken = true;
     return st;
 }
 
@@ -420,6 +448,7 @@ csp_status sparse_layer_export(sparse_layer_t L, int32_t *rows, int32_t *cols, v
 {
     if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     hipStream_t s = (hipStream_t)stream;
     const size_t n = (size_t)L->nnz;
     if (n == 0) return CSP_OK;
@@ -434,6 +463,7 @@ csp_status sparse_layer_export_index(sparse_layer_t L, int32_t *row_ptr, int32_t
 {
     if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     hipStream_t s = (hipStream_t)stream;
     const size_t n = (size_t)L->nnz;
     if (row_ptr) CSP_HIP(hipMemcpyAsync(row_ptr, L->row_ptr, 4 * (size_t)(L->out + 1), hipMemcpyDeviceToDevice, s));
@@ -449,6 +479,7 @@ csp_status sparse_layer_set_values(sparse_layer_t L, const void *vals, void *str
     if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
     if (L->nnz == 0) return CSP_OK;
     DeviceGuard g(L->device);
+    CSP_USABLE(L);
     hipStream_t s = (hipStream_t)stream;
     if (vals)
         CSP_HIP(hipMemcpyAsync(L->vals, vals, (size_t)L->esz * (size_t)L->nnz, hipMemcpyDeviceToDevice, s));

@@ -272,3 +272,26 @@ def test_dst_loop_full_size(orc):
         check_state(orc, h, L.out, L.in_, r0[0], r0[1], r0[2])
     finally:
         csp.sparse_layer_destroy(h)
+
+
+def test_failed_restructure_marks_layer_unusable(path, monkeypatch):
+    """A regrow that cannot place every pruned entry within its batch limit (forced from the host
+    with four-draw batches: about 4096 * 4 * 0.85 < 30000 candidates land on empty positions)
+    returns an error; the layer is then half rebuilt, so every call but destroy refuses it."""
+    monkeypatch.setenv("COOSPMM_REGROW_BATCH", "4")
+    L = W.random_layer(200, 200, 36000, seed=53)
+    h = csp.sparse_layer_create(200, 200, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        with pytest.raises(csp.CspError, match="regrow found only"):
+            csp.restructure(h, 30000, 3, 0)
+        X = dev(W.random_dense((2, 200), 1))
+        refused = [lambda: csp.spmm_fwd(h, X), lambda: csp.spmm_fwd_static(h, X),
+                   lambda: csp.spmm_bwd_input(h, X), lambda: csp.spmm_bwd(h, X, X),
+                   lambda: csp.sparse_layer_export(h), lambda: csp.sparse_layer_export_index(h),
+                   lambda: csp.sparse_layer_set_values(h, None), lambda: csp.restructure(h, 10, 3, 1),
+                   lambda: csp.restructure_grad(h, 10, X, X)]
+        for call in refused:
+            with pytest.raises(csp.CspError, match="failed restructure"):
+                call()
+    finally:
+        csp.sparse_layer_destroy(h)
