@@ -352,25 +352,44 @@ def sparse_layer_set_values(layer: int, vals, stream=None):
     _check(load().sparse_layer_set_values(c_void_p(layer), vp, _stream(stream)))
 
 
-class _DeviceArray:
-    """Minimal __cuda_array_interface__ holder for a library-owned device array."""
+class LayerOwner:
+    """Owns a layer handle and destroys it when the last reference goes away.  Zero-copy views of
+    the layer's device arrays hold a reference to it, so the layer outlives every view (an optimizer
+    may keep a parameter after its module is gone)."""
 
-    def __init__(self, ptr: int, n: int, typestr: str):
+    def __init__(self, handle: int, destroy=None):
+        self.handle = handle
+        self._destroy = destroy if destroy is not None else sparse_layer_destroy
+
+    def __del__(self):
+        h, self.handle = self.handle, None
+        if h:
+            self._destroy(h)
+
+
+class _DeviceArray:
+    """Minimal __cuda_array_interface__ holder for a library-owned device array; `owner` (a
+    LayerOwner, or None) is kept alive as long as this object, and torch keeps this object alive as
+    long as a tensor made from it."""
+
+    def __init__(self, ptr: int, n: int, typestr: str, owner=None):
+        self.owner = owner
         self.__cuda_array_interface__ = {"shape": (n,), "typestr": typestr, "data": (ptr, False),
                                          "strides": None, "version": 2}
 
 
-def sparse_layer_values_tensor(layer: int):
+def sparse_layer_values_tensor(layer: int, owner=None):
     """Zero-copy torch view of the layer's canonical values, valid until the next
-    restructure (which may move them) or the layer's destruction.  After writing
-    into it, call sparse_layer_set_values(layer, None)."""
+    restructure (which may move them).  With `owner` (the layer's LayerOwner) the
+    view keeps the layer alive; without it the caller must keep the layer until the
+    view is gone.  After writing into it, call sparse_layer_set_values(layer, None)."""
     torch = _torch()
     _, _, dt = sparse_layer_shape(layer)
     nnz = sparse_layer_nnz(layer)
     ptr = sparse_layer_values(layer)
     if nnz == 0:
         return torch.empty(0, dtype=_torch_dtype(dt), device="cuda")
-    t = torch.as_tensor(_DeviceArray(ptr, nnz, "<u2" if dt == CSP_BF16 else "<f4"), device="cuda")
+    t = torch.as_tensor(_DeviceArray(ptr, nnz, "<u2" if dt == CSP_BF16 else "<f4", owner), device="cuda")
     return t.view(torch.bfloat16) if dt == CSP_BF16 else t
 
 

@@ -60,10 +60,15 @@ class SparseLinear(torch.nn.Module):
     def __init__(self, rows, cols, vals, out_features: int, in_features: int):
         super().__init__()
         self.out_features, self.in_features = int(out_features), int(in_features)
-        self.handle = csp.sparse_layer_create(self.out_features, self.in_features, rows, cols, vals)
-        self.values = torch.nn.Parameter(csp.sparse_layer_values_tensor(self.handle),
+        # the owner destroys the layer once neither the module nor any view of its values is left
+        self._owner = csp.LayerOwner(csp.sparse_layer_create(self.out_features, self.in_features, rows, cols, vals))
+        self.values = torch.nn.Parameter(csp.sparse_layer_values_tensor(self.handle, self._owner),
                                          requires_grad=vals.dtype == torch.float32)
         self._seen_version = self.values._version
+
+    @property
+    def handle(self) -> int:
+        return self._owner.handle
 
     @property
     def nnz(self) -> int:
@@ -86,7 +91,7 @@ class SparseLinear(torch.nn.Module):
         """One prune-and-regrow step (the n_prune smallest |v| go, as many empty positions are drawn)."""
         self._sync_values()
         csp.restructure(self.handle, int(n_prune), int(seed), int(step), float(regrow_value))
-        self.values.data = csp.sparse_layer_values_tensor(self.handle)
+        self.values.data = csp.sparse_layer_values_tensor(self.handle, self._owner)
         self._seen_version = self.values._version
 
     @torch.no_grad()
@@ -94,7 +99,7 @@ class SparseLinear(torch.nn.Module):
         """Prune the n_prune smallest |v|; regrow the empty positions where |dY^T X| is largest."""
         self._sync_values()
         csp.restructure_grad(self.handle, int(n_prune), dY.contiguous(), X.contiguous(), float(regrow_value))
-        self.values.data = csp.sparse_layer_values_tensor(self.handle)
+        self.values.data = csp.sparse_layer_values_tensor(self.handle, self._owner)
         self._seen_version = self.values._version
 
     def coo(self):
@@ -108,12 +113,6 @@ class SparseLinear(torch.nn.Module):
         W = torch.zeros(self.out_features, self.in_features, dtype=v.dtype, device=v.device)
         W[r.long(), c.long()] = v
         return W
-
-    def __del__(self):
-        h = getattr(self, "handle", None)
-        if h:
-            self.handle = None
-            csp.sparse_layer_destroy(h)
 
     def extra_repr(self) -> str:
         return f"in_features={self.in_features}, out_features={self.out_features}, nnz={self.nnz}"

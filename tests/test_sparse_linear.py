@@ -1,5 +1,8 @@
 """SparseLinear (torch module + autograd) against the oracle: forward, both gradients through
 autograd, an optimizer step through the zero-copy values parameter, and a restructure."""
+import gc
+import weakref
+
 import numpy as np
 import pytest
 import torch
@@ -12,6 +15,47 @@ from tests.gpu_util import FP32_REL, assert_within, bits, dev, host
 def test_module_imports_without_gpu():
     from coo_spmm_fwd_amd.sparse_linear import SparseLinear
     assert "truly sparse" in SparseLinear.__doc__ or "COO" in SparseLinear.__doc__
+
+
+def test_layer_owner_outlives_its_views():
+    """The owner destroys its layer exactly once, only after the last view that holds it is gone
+    (a stand-in destroy callback: no library call)."""
+    from coo_spmm_fwd_amd import binding as csp
+    destroyed = []
+    owner = csp.LayerOwner(1234, destroy=destroyed.append)
+    views = [csp._DeviceArray(0x1000, 4, "<f4", owner), csp._DeviceArray(0x1000, 4, "<f4", owner)]
+    del owner
+    gc.collect()
+    assert destroyed == []
+    views.pop()
+    assert destroyed == []
+    views.pop()
+    gc.collect()
+    assert destroyed == [1234]
+
+
+@pytest.mark.gpu
+def test_values_parameter_outlives_module():
+    """An optimizer may hold the values parameter after the module is gone: the view keeps the
+    layer alive, still reads and writes its buffer, and the layer goes with the last view."""
+    from coo_spmm_fwd_amd.sparse_linear import SparseLinear
+    L = W.random_layer(300, 200, 9000, seed=57)
+    m = SparseLinear(dev(L.rows), dev(L.cols), dev(L.vals), 300, 200)
+    m.restructure(900, 2, 0)                      # the parameter now views a buffer made by the restructure
+    v = m.values
+    want = host(v.detach()).copy()
+    owner = weakref.ref(m._owner)
+    del m
+    gc.collect()
+    assert owner() is not None
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(host(v.detach())), bits(want))
+    with torch.no_grad():
+        v.mul_(2.0)
+    assert np.array_equal(bits(host(v.detach())), bits(want * np.float32(2.0)))
+    del v
+    gc.collect()
+    assert owner() is None
 
 
 @pytest.mark.gpu
