@@ -98,6 +98,17 @@ constexpr int kSelCountWords = kSelClassWords + 3 * kSplitClasses;  // words rea
 // workgroup can finish 1, 2, 4 or 8 of them (kGroupWaves >> c waves each).
 __host__ __device__ inline int split_class(uint32_t p) { return p > 8 ? 0 : p > 4 ? 1 : p > 2 ? 2 : 3; }
 
+// Value-gradient tiles (fp32 layers, batch chunks of 33..64): the layer is
+// cut into tiles of kTileRows rows x kTileCols columns; one workgroup stages a
+// tile's operand columns in LDS and computes the value gradient of the tile's
+// entries.  tile_ptr[r * (ncb + 1) + k] is the first entry of row r whose
+// column is at least k * kTileCols (k = ncb: the row's end); tile_rows holds,
+// per tile, its local rows ordered by their entry count in the tile (most
+// first, ties by row), so that the four rows a wave runs side by side have
+// similar lengths.
+constexpr int kTileCols = 512;
+constexpr int kTileRows = 512;
+
 struct TaskList {
     int4 *desc = nullptr;   // [cap] {segment, first entry, end entry, partial slot or -1}
     int4 *split = nullptr;  // [nseg] {segment, first task, task count, 0} of split segments
@@ -132,6 +143,10 @@ struct csp_layer {
     // task lists may then describe a layer that was never completed, so every
     // later call but destroy refuses the layer.
     bool broken = false;
+    // value-gradient tiles (allocated at create for fp32 layers with in >= 2 * kTileCols; else null)
+    int32_t *tile_ptr = nullptr;
+    int16_t *tile_rows = nullptr;
+    int64_t tile_ncb = 0, tile_nrb = 0;
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request
@@ -203,6 +218,9 @@ int32_t pack_limit(const csp_layer *L);
 csp_status set_task_counts(csp_layer *L, const uint32_t *counts);
 // vals_c[j] = vals[perm_c[j]] after the canonical values changed.
 csp_status refresh_column_values(csp_layer *L, hipStream_t s);
+// Value-gradient tiles from row_ptr and cols (two launches, no host sync);
+// nothing to do for a layer without tiles.
+csp_status build_tiles(csp_layer *L, hipStream_t s);
 inline int64_t task_cap(int64_t nseg, int64_t nnz) { return nseg + (nnz + kTaskChunk - 1) / kTaskChunk; }
 
 // ---------------------------------------------------------------------------

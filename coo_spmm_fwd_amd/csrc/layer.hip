@@ -74,7 +74,8 @@ void free_layer(csp_layer *L)
                     L->row_tasks.desc, L->row_tasks.split, L->row_tasks.seg_first,
                     L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first,
                     L->row_packed.desc, L->row_packed.split,
-                    L->row_tasks.split_cls, L->col_tasks.split_cls, L->row_packed.split_cls};
+                    L->row_tasks.split_cls, L->col_tasks.split_cls, L->row_packed.split_cls,
+                    L->tile_ptr, L->tile_rows};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete L;
@@ -146,6 +147,14 @@ csp_status alloc_layer(csp_layer *L)
     };
     for (auto &r : reqs) {
         csp_status st = dalloc(r.p, r.bytes, r.what);
+        if (st != CSP_OK) return st;
+    }
+    if (L->esz == 4 && in >= 2 * kTileCols) {
+        L->tile_ncb = ceil_div(in, kTileCols);
+        L->tile_nrb = ceil_div(out, kTileRows);
+        csp_status st = dalloc((void **)&L->tile_ptr, 4 * (size_t)out * (size_t)(L->tile_ncb + 1), "tile offsets");
+        if (st == CSP_OK)
+            st = dalloc((void **)&L->tile_rows, 2 * (size_t)(L->tile_nrb * L->tile_ncb) * kTileRows, "tile row order");
         if (st != CSP_OK) return st;
     }
     if (!bitmap) return CSP_OK;
@@ -258,6 +267,7 @@ csp_status sparse_layer_create(int64_t out_features, int64_t in_features, int64_
     if (st == CSP_OK) st = fill_u32(L->ws.sel, 0u, kSelAllocWords, s);
     if (st == CSP_OK) st = build_canonical(L, rows, cols, vals, L->ws.sel, s);
     if (st == CSP_OK) st = build_index(L, s);
+    if (st == CSP_OK) st = build_tiles(L, s);
     if (st == CSP_OK) st = occupancy_init(L, s);
     uint32_t flags = 0;
     if (st == CSP_OK) {
@@ -404,6 +414,7 @@ csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
     csp_status st = run_restructure(L, n_prune, seed, step, regrow_word(L, regrow_value), s);
+    if (st == CSP_OK && n_prune > 0) st = build_tiles(L, s);
     if (st == CSP_OK && n_prune > 0) {
         hipError_t e = hipStreamSynchronize(s);
         if (e != hipSuccess) st = hip_error(e, "restructure");
@@ -425,6 +436,7 @@ csp_status restructure_grad(sparse_layer_t L, int64_t n_prune, const void *dY, c
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
     csp_status st = restructure_gradient(L, n_prune, dY, X, B, regrow_word(L, regrow_value), s);
+    if (st == CSP_OK && n_prune > 0) st = build_tiles(L, s);
     if (st == CSP_OK && n_prune > 0) {
         hipError_t e = hipStreamSynchronize(s);
         if (e != hipSuccess) st = hip_error(e, "restructure_grad");

@@ -744,6 +744,185 @@ __global__ __launch_bounds__(kPW * kWave) void k_values_rows(const int4 *__restr
     values_task<LD, D, kWide>(desc, t, cols, XT, dYT, in, out, dW, acc != 0);
 }
 
+// ------------------------------------------ value gradient, LDS tiles
+// fp32, one batch chunk of width 64 (B of 33..64; the pad slots of the
+// batch-minor tables are zero).  The task-list kernel above pulls one 256-byte
+// operand row through its CU's vector-memory path per stored entry, and at
+// this width that path bounds it.  Here one workgroup of kTileWaves waves
+// takes a tile of kTileRows rows x kTileCols columns (tile_ptr, tile_rows):
+// it copies the tile's operand rows XT[c][0..63] (128 KiB) into LDS once, and
+// every entry of the tile reads its row from there.
+// A wave runs four rows side by side, one per 16-lane DPP row: lane q holds
+// batch values 4q .. 4q + 3 of dY[row] and of each gathered X row.  A row's
+// entries in the tile come in windows of 16 (lane q loads entry q of the
+// window; the first kTilePF windows of the next four rows are loaded while
+// the current ones run), and step t of a window broadcasts entry t's LDS
+// offset to the 16 lanes (row_newbcast).  Each lane keeps the 16 partial dot
+// products of a window; one transposing reduction over the 16 lanes then
+// leaves the sum of entry q in lane q, stored with one coalesced write.
+// The partial products are the task kernel's fused multiply-add chains, and
+// the reduction adds the same pairs as its 16-lane sum (lanes xor 1, then xor
+// 2, then the two quads of each half, then the two halves -- the task kernel
+// pairs the quads and halves by mirroring, which meets the same sums because
+// they are equal across a quad or half), so the results are bitwise the same.
+constexpr int kTileWaves = 16;
+constexpr int kTilePF = 3;
+
+template <int T>
+__device__ __forceinline__ int row_bcast(int v)
+{
+    return __builtin_amdgcn_mov_dpp(v, 0x150 + T, 0xF, 0xF, true);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Steps T .. T + 3 of a window: four LDS gathers in flight, then their dot products.
+template <int T>
+__device__ __forceinline__ void tile_dots(const char *tab, int coff, int q16, const float (&dy)[4], float (&p)[16])
+{
+    const int a0 = row_bcast<T>(coff) + q16, a1 = row_bcast<T + 1>(coff) + q16;
+    const int a2 = row_bcast<T + 2>(coff) + q16, a3 = row_bcast<T + 3>(coff) + q16;
+    const float4 x0 = *reinterpret_cast<const float4 *>(tab + a0);
+    const float4 x1 = *reinterpret_cast<const float4 *>(tab + a1);
+    const float4 x2 = *reinterpret_cast<const float4 *>(tab + a2);
+    const float4 x3 = *reinterpret_cast<const float4 *>(tab + a3);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    const float4 xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = 0.f;  // fused multiply-adds in batch order
+        v = __builtin_fmaf(dy[0], xs[i].x, v);
+        v = __builtin_fmaf(dy[1], xs[i].y, v);
+        v = __builtin_fmaf(dy[2], xs[i].z, v);
+        v = __builtin_fmaf(dy[3], xs[i].w, v);
+        p[T + i] = v;
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+}
+
+// On exit lane q of each 16-lane row holds the sum over the row's lanes of p[q].
+// Each stage keeps the entries whose index bit matches the lane's bit and adds
+// the partner lane's partial sums of the same entries.
+__device__ __forceinline__ float tile_reduce16(const float (&p)[16], int q)
+{
+    const bool b0 = q & 1, b1 = q & 2, b2 = q & 4, b3 = q & 8;
+    float a[8], b[4], c[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float keep = b0 ? p[2 * k + 1] : p[2 * k], send = b0 ? p[2 * k] : p[2 * k + 1];
+        a[k] = keep + dpp_mov<0xB1>(send);  // lane xor 1
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float keep = b1 ? a[2 * k + 1] : a[2 * k], send = b1 ? a[2 * k] : a[2 * k + 1];
+        b[k] = keep + dpp_mov<0x4E>(send);  // lane xor 2
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float keep = b2 ? b[2 * k + 1] : b[2 * k], send = b2 ? b[2 * k] : b[2 * k + 1];
+        c[k] = keep + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(send), 0x1F | (4 << 10)));  // xor 4
+    }
+    const float keep = b3 ? c[1] : c[0], send = b3 ? c[0] : c[1];
+    return keep + dpp_mov<0x128>(send);  // row_ror 8: lane xor 8 within the 16
+}
+
+__global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int32_t *__restrict__ tile_ptr,
+                                                                     const int16_t *__restrict__ tile_rows,
+                                                                     int64_t ncb, const int32_t *__restrict__ cols,
+                                                                     const float *__restrict__ XT,
+                                                                     const float *__restrict__ dYT, int64_t in,
+                                                                     int64_t out, float *__restrict__ dW, int acc)
+{
+    constexpr int G = kTileRows / (4 * kTileWaves);  // groups of four rows per wave
+    static_assert(4 * G <= kWave, "one lane per row of the wave");
+    constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);  // 16-byte pieces per thread
+    __shared__ float4 tab[kTileCols * 16];
+    const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
+    const int64_t c0 = cb * kTileCols, r0 = rb * kTileRows;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
+    // lane l < 4G: row (group l / 4, slot l % 4) of the wave, and its entries in the tile
+    int mybeg = 0, myend = 0, myrow = 0;
+    if (lane < 4 * G) {
+        myrow = tile_rows[blockIdx.x * (int64_t)kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
+        const int64_t r = r0 + myrow;
+        if (r < out) {
+            mybeg = tile_ptr[r * (ncb + 1) + cb];
+            myend = tile_ptr[r * (ncb + 1) + cb + 1];
+        }
+    }
+    const int64_t ncols = in - c0 < kTileCols ? in - c0 : kTileCols;
+    const float4 *x4 = reinterpret_cast<const float4 *>(XT);
+    float4 fl[FILL];
+#pragma unroll
+    for (int j = 0; j < FILL; ++j) {  // every fill load in flight before the first LDS store
+        const int i = threadIdx.x + kTileWaves * kWave * j, c = i >> 4;
+        fl[j] = x4[(c0 + (c < ncols ? c : 0)) * 16 + (i & 15)];
+    }
+    int cbeg, cn, nbeg = 0, nn = 0;
+    int ci[kTilePF], ni[kTilePF] = {};
+    float4 cdy, ndy = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto fetch = [&](int i, int &beg, int &n, int (&ii)[kTilePF], float4 &dy) {
+        beg = __shfl(mybeg, 4 * i + g);
+        n = __shfl(myend, 4 * i + g) - beg;
+        const int64_t r = r0 + __shfl(myrow, 4 * i + g);
+        dy = reinterpret_cast<const float4 *>(dYT)[(r < out ? r : 0) * 16 + q];
+#pragma unroll
+        for (int j = 0; j < kTilePF; ++j) {
+            const int e = 16 * j + q;
+            ii[j] = cols[e < n ? beg + e : 0];
+        }
+    };
+    fetch(0, cbeg, cn, ci, cdy);
+#pragma unroll
+    for (int j = 0; j < FILL; ++j) {
+        const int i = threadIdx.x + kTileWaves * kWave * j;
+        tab[i] = (i >> 4) < ncols ? fl[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    const char *base = reinterpret_cast<const char *>(tab);
+    for (int i = 0; i < G; ++i) {
+        if (i + 1 < G) fetch(i + 1, nbeg, nn, ni, ndy);
+        const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
+                             max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
+        const float dy[4] = {cdy.x, cdy.y, cdy.z, cdy.w};
+        for (int k = 0; k < nmax; k += 16) {
+            const int e = k + q;
+            int c;
+            if (k < 16 * kTilePF) {
+                const int j = k >> 4;
+                c = j == 0 ? ci[0] : (j == 1 ? ci[1] : ci[2]);
+            } else {  // a row with more than 16 * kTilePF entries in the tile
+                c = cols[e < cn ? cbeg + e : 0];
+            }
+            const uint32_t rel = (uint32_t)((int64_t)c - c0);
+            const int coff = e < cn && rel < (uint32_t)kTileCols ? (int)rel * 256 : 0;
+            float p[16];
+            tile_dots<0>(base, coff, q16, dy, p);
+            if (k + 4 < nmax) tile_dots<4>(base, coff, q16, dy, p);
+            else p[4] = p[5] = p[6] = p[7] = 0.f;
+            if (k + 8 < nmax) tile_dots<8>(base, coff, q16, dy, p);
+            else p[8] = p[9] = p[10] = p[11] = 0.f;
+            if (k + 12 < nmax) tile_dots<12>(base, coff, q16, dy, p);
+            else p[12] = p[13] = p[14] = p[15] = 0.f;
+            const float r = tile_reduce16(p, q);
+            if (e < cn) {
+                if (!acc) dW[cbeg + e] = r;
+                else dW[cbeg + e] += r;
+            }
+        }
+        cbeg = nbeg;
+        cn = nn;
+        cdy = ndy;
+#pragma unroll
+        for (int j = 0; j < kTilePF; ++j) ci[j] = ni[j];
+    }
+}
+
 // --------------------------------------------------- both gradients
 // The two gradients are independent; one launch runs both so that their
 // latency chains overlap: even/odd blocks alternate between input-gradient
@@ -1236,12 +1415,35 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
     return split_fixup<D, E>(L, TL, B, L->in, dX, ep, s);
 }
 
+// The tile kernel for the value gradient: fp32 layers that have tiles, a
+// batch chunk of width 64, and at least one tile per compute unit (fewer
+// would leave CUs idle; the task list then spreads better).  The variable
+// COOSPMM_VALUE_TILES=0 turns it off (a test hook: the results are the same).
+inline bool value_tiles_usable(const csp_layer *L, int ld)
+{
+    if (!L->tile_ptr || ld != 64 || L->tile_nrb * L->tile_ncb < L->act.cus) return false;
+    const char *e = std::getenv("COOSPMM_VALUE_TILES");
+    return !(e && e[0] == '0');
+}
+
+csp_status launch_value_tiles(csp_layer *L, int mark, const float *XT, const float *dYT, float *dW, bool acc,
+                              hipStream_t s)
+{
+    launch_main(L, mark, k_values_tiles, dim3((unsigned)(L->tile_nrb * L->tile_ncb)), dim3(kTileWaves * kWave), 0u,
+                s, L->tile_ptr, L->tile_rows, L->tile_ncb, L->cols, XT, dYT, L->in, L->out, dW, (int)acc);
+    CSP_LAUNCHED("k_values_tiles");
+    return CSP_OK;
+}
+
 template <class D>
 csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, float *dW, bool acc,
                                hipStream_t s)
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
+    if constexpr (sizeof(T) == 4)
+        if (value_tiles_usable(L, ld))
+            return launch_value_tiles(L, kTimeBoth, (const float *)XT, (const float *)dYT, dW, acc, s);
     const TaskList &TL = L->row_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, kPW);
 #define CSP_DW(LDV, W)                                                                                            \
@@ -1281,7 +1483,12 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
 #undef CSP_DX2
 #undef CSP_DX2_ARGS
         CSP_LAUNCHED("k_segment_spmm (input gradient)");
-        if (gw > 0) {
+        bool tiled = false;
+        if constexpr (sizeof(T) == 4) tiled = gw > 0 && value_tiles_usable(L, ld);
+        if (tiled) {
+            const csp_status st = launch_value_tiles(L, kTimeStop, (const float *)XT, (const float *)dYT, dW, acc, s);
+            if (st != CSP_OK) return st;
+        } else if (gw > 0) {
 #define CSP_DW2(LDV, W)                                                                                           \
     launch_main(L, kTimeStop, k_values_rows<LDV, D, W>, gw, kPW * kWave, 0, s, RT.desc, nrow, L->cols, (const T *)XT, (const T *)dYT, L->in, L->out, \
                                                 dW, (int)acc)
