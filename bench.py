@@ -159,11 +159,17 @@ def ingest_counters(fetch_dir, write_dir, workload, batch, label, kernel, copy_m
     if not cf or not cw:
         raise SystemExit("no calibration copy in the counter runs (run them with --calibrate-copy)")
     f_scale, w_scale = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    m = lambda n: kernel in n
-    kf, nf = _per_dispatch(fetch, "FETCH_SIZE", m)
-    kw, nw = _per_dispatch(write, "WRITE_SIZE", m)
-    if kf is None or kw is None:
-        raise SystemExit(f"kernel {kernel!r} not in the counter runs")
+    # a call of several launches ("a + b") moves the sum of its kernels' bytes
+    kf = kw = 0.0
+    nf, nw = [], []
+    for name in (k.strip() for k in kernel.split(" + ")):
+        f1, n1 = _per_dispatch(fetch, "FETCH_SIZE", lambda n, k=name: k in n)
+        w1, n2 = _per_dispatch(write, "WRITE_SIZE", lambda n, k=name: k in n)
+        if f1 is None or w1 is None:
+            raise SystemExit(f"kernel {name!r} not in the counter runs")
+        kf, kw = kf + f1, kw + w1
+        nf.append(n1)
+        nw.append(n2)
     try:
         with open(PROFILE_TRAFFIC) as f:
             rec = json.load(f)
@@ -527,8 +533,19 @@ class Bench:
     def dt_name(self):
         return "csp::BF16" if self.w.dtype == "bf16" else "csp::F32"
 
+    def tiled(self, L, which):
+        """The library's LDS-tile path for this layer and call (fp32, a 64-wide batch chunk, at least one
+        512 x 512 tile per compute unit; the environment switches turn it off)."""
+        import torch
+        env = "COOSPMM_VALUE_TILES" if which == "values" else "COOSPMM_SEGMENT_TILES"
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        return (self.esz == 4 and self.ld == 64 and os.environ.get(env, "1")[:1] != "0"
+                and -(-L.out // 512) * -(-L.in_ // 512) >= cus)
+
     def fwd_name(self, L, epi=0):
         ld, dt, B = self.ld, self.dt_name(), self.B
+        if self.tiled(L, "segments"):
+            return f"k_segment_tiles + k_tile_reduce<{epi}>"
         ks = int(self.seg_max[id(L)][0] <= 512)
         grouped_on = os.environ.get("COOSPMM_GROUPED_SPLITS", "1")[:1] != "0"
         if self.lds_fits(L.in_, segment=True):
@@ -538,10 +555,14 @@ class Bench:
         return f"k_segment_spmm<{ld}, {dt}, false, {epi}, {ks}>"
 
     def dx_name(self, L, epi=0):
+        if self.tiled(L, "segments"):
+            return f"k_segment_tiles + k_tile_reduce<{epi}>"
         ks = int(self.seg_max[id(L)][1] <= 512)
         return f"k_segment_spmm<{self.ld}, {self.dt_name()}, false, {epi}, {ks}>"
 
     def dw_name(self, L):
+        if self.tiled(L, "values"):
+            return "k_values_tiles"
         return f"k_values_rows<{self.ld}, {self.dt_name()}, false>"
 
     def grad_fused(self, L):

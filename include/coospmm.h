@@ -97,11 +97,15 @@ csp_status spmm_fwd(sparse_layer_t layer, const void *X, int64_t B, void *Y, voi
 /*
  * spmm_fwd_static -- spmm_fwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
- * allocation).  Same kernels, arguments and results (bit for bit) as
- * spmm_fwd, but the call's workspace -- the batch-minor copy of X and the
- * partial sums of rows split over several tasks -- lives in one static device
- * array of 16 MiB per GPU (held until the process ends) instead of the
- * layer's own workspace.  The call allocates and frees nothing.  Its largest
+ * allocation).  Same arguments as spmm_fwd, and its task-list kernels, but the
+ * call's workspace -- the batch-minor copy of X and the partial sums of rows
+ * split over several tasks -- lives in one static device array of 16 MiB per
+ * GPU (held until the process ends) instead of the layer's own workspace.
+ * Results are bit for bit those of spmm_fwd except where spmm_fwd takes its
+ * LDS-tile path (fp32 layers with at least one 512 x 512 tile per compute
+ * unit, batch slices of 33..64 rows), whose per-tile partial sums do not fit
+ * the array: there both are within the fp32 bound of the exact sum and agree
+ * to rounding.  The call allocates and frees nothing.  Its largest
  * batch slice (at most 64 rows) needs esz * ld * in bytes for the copy of X
  * (ld = the slice's rows rounded up to a power of two; esz = 4 for fp32, 2 for
  * bf16; none for one row, or when the forward reads X through the on-chip

@@ -1,8 +1,9 @@
 """spmm_fwd_static -- the forward for callers that cannot allocate -- through the C ABI: its output
-equals spmm_fwd's bit for bit (same kernels, its workspace in the library's static per-GPU array)
-and the oracle's within 1e-5 * S, over two calls in a row (the second with a smaller input) and a
-third on another layer; a layer and batch whose workspace exceeds the array are refused on the host
-before any launch."""
+equals spmm_fwd's bit for bit (same task-list kernels, its workspace in the library's static per-GPU
+array) and the oracle's within 1e-5 * S, over two calls in a row (the second with a smaller input)
+and a third on another layer; on a layer where spmm_fwd takes the LDS-tile path it equals the
+task-list path bit for bit and the tile path to rounding; a layer and batch whose workspace exceeds
+the array are refused on the host before any launch."""
 import ctypes
 
 import numpy as np
@@ -74,5 +75,28 @@ def test_static_forward_refuses_oversized_workspace():
         Y2 = torch.empty(1, 10, device="cuda")
         assert call_static(h, X[:1].contiguous(), 1, Y2) == 0   # one row needs no copy
         assert torch.equal(Y2, csp.spmm_fwd(h, X[:1].contiguous()))
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_static_forward_on_a_tiled_layer(orc, monkeypatch):
+    """8192 x 8192 at 5%, B = 64: spmm_fwd runs the LDS tiles there (their partial sums do not fit the
+    static array), the static variant the task list.  It must equal spmm_fwd with the tiles switched
+    off bit for bit, and the tiled output within twice the fp32 bound."""
+    L = W.random_layer(8192, 8192, 3_355_443, seed=44)
+    h = csp.sparse_layer_create(L.out, L.in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        Xh = W.random_dense((64, L.in_), 45)
+        X = dev(Xh)
+        Y = torch.full((64, L.out), float("nan"), device="cuda")
+        assert call_static(h, X, 64, Y) == 0, csp.sparse_layer_last_error()
+        got = host(Y)
+        monkeypatch.setenv("COOSPMM_SEGMENT_TILES", "0")
+        plain = host(csp.spmm_fwd(h, X))
+        monkeypatch.delenv("COOSPMM_SEGMENT_TILES")
+        tiled = host(csp.spmm_fwd(h, X))
+        assert np.array_equal(got.view(np.uint32), plain.view(np.uint32)), "differs from the task-list forward"
+        _, S = orc.spmm_fwd(L.out, L.in_, L.rows, L.cols, L.vals, Xh)
+        assert_within(got, tiled.astype(np.float64), S, 2 * FP32_REL, "static against the tiled forward")
     finally:
         csp.sparse_layer_destroy(h)
