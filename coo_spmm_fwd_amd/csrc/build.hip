@@ -364,55 +364,41 @@ csp_status set_task_counts(csp_layer *L, const uint32_t *counts)
     return CSP_OK;
 }
 
-// ----------------------------------------------------- value-gradient tiles
-// tile_ptr[r * (ncb + 1) + k] = first entry of row r whose column is at least
-// k * kTileCols, in one pass over the canonical entries: entry p of row r in
-// column block b sets the slots k of (b', b], b' the block of the row's
-// previous entry (-1 at the row's first entry); the row's end fills the slots
-// after the block of its last entry (all of them for an empty row).  Every
-// slot is written exactly once.  Threads t < ceil(nnz / 4) take entries
-// 4t .. 4t + 3 (vector loads, the previous entry read as well); thread
-// ceil(nnz / 4) + r takes the end of row r.
-__global__ void k_tile_ptr(const int32_t *__restrict__ rows, const int32_t *__restrict__ cols,
-                           const int32_t *__restrict__ row_ptr, int64_t nnz, int64_t out, int64_t ncb,
-                           int32_t *__restrict__ tile_ptr)
+// ------------------------------------------------------------- LDS tiles
+// ptr[s * (ncb + 1) + k] = first entry of segment s whose index is at least
+// k * kTileCols, one wave per segment: entry e of block b sets the slots k of
+// (b', b], b' the block of the segment's previous entry (-1 at its first
+// entry), then the slots after the last entry's block (all of them for an
+// empty segment) get the segment's end.  Every slot is written exactly once.
+__global__ __launch_bounds__(256) void k_tile_ptr(const int32_t *__restrict__ seg_ptr, const int32_t *__restrict__ idx,
+                                                  int64_t nseg, int64_t ncb, int32_t *__restrict__ tile_ptr)
 {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x, nq = (nnz + 3) / 4;
-    if (t < nq) {
-        const int64_t i0 = 4 * t;
-        int32_t r[5], c[5];  // [0]: the entry before i0 (row -1 if none)
-        r[0] = i0 > 0 ? rows[i0 - 1] : -1;
-        c[0] = i0 > 0 ? cols[i0 - 1] : 0;
-        if (i0 + 4 <= nnz) {  // entry arrays are 16-byte aligned and padded
-            const int4 rr = *reinterpret_cast<const int4 *>(rows + i0), cc = *reinterpret_cast<const int4 *>(cols + i0);
-            r[1] = rr.x; r[2] = rr.y; r[3] = rr.z; r[4] = rr.w;
-            c[1] = cc.x; c[2] = cc.y; c[3] = cc.z; c[4] = cc.w;
-        } else {
-            for (int j = 0; j < 4; ++j) {
-                r[j + 1] = i0 + j < nnz ? rows[i0 + j] : -1;
-                c[j + 1] = i0 + j < nnz ? cols[i0 + j] : 0;
-            }
-        }
-#pragma unroll
-        for (int j = 1; j <= 4; ++j) {
-            if (r[j] < 0) break;
-            const int64_t b = c[j] / kTileCols, prev = r[j - 1] == r[j] ? c[j - 1] / kTileCols : -1;
-            for (int64_t k = prev + 1; k <= b; ++k) tile_ptr[(int64_t)r[j] * (ncb + 1) + k] = (int32_t)(i0 + j - 1);
-        }
-    } else if (t < nq + out) {
-        const int64_t r = t - nq;
-        const int32_t beg = row_ptr[r], end = row_ptr[r + 1];
-        const int64_t last = end > beg ? cols[end - 1] / kTileCols : -1;
-        for (int64_t k = last + 1; k <= ncb; ++k) tile_ptr[r * (ncb + 1) + k] = end;
+    const int64_t sg = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (sg >= nseg) return;
+    const int lane = threadIdx.x & 63;
+    const int32_t beg = seg_ptr[sg], end = seg_ptr[sg + 1];
+    int32_t *t = tile_ptr + sg * (ncb + 1);
+    int32_t carry = -1;  // block of the entry before the current chunk
+    for (int32_t base = beg; base < end; base += kWave) {
+        const int32_t e = base + lane;
+        const int32_t b = e < end ? idx[e] / kTileCols : (int32_t)ncb;
+        const int32_t up = __shfl_up(b, 1, kWave);
+        const int32_t prev = lane == 0 ? carry : up;
+        if (e < end)
+            for (int32_t k = prev + 1; k <= b; ++k) t[k] = e;
+        carry = __shfl(b, kWave - 1, kWave);
     }
+    const int32_t last = end > beg ? idx[end - 1] / kTileCols : -1;
+    for (int64_t k = last + 1 + lane; k <= ncb; k += kWave) t[k] = end;
 }
 
-// One block per tile (tile = row block * ncb + column block): its local rows
-// by entry count in the tile, most first (counts of kTileRows - 2 and more
-// share a bin; rows past the layer count -1 and come last), by a counting
-// sort.  Rows of equal count land in any order: the order only pairs rows for
-// the waves of the tile kernel, whose sums do not depend on it.
-__global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restrict__ tile_ptr, int64_t out,
+// One block per tile (tile = row block * ncb + column block): its local
+// segments by entry count in the tile, most first (counts of kTileRows - 2 and
+// more share a bin; segments past the view count -1 and come last), by a
+// counting sort.  Segments of equal count land in any order: the order only
+// pairs segments for the waves of the tile kernels, whose sums do not depend
+// on it.
+__global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restrict__ tile_ptr, int64_t nseg,
                                                          int64_t ncb, int16_t *__restrict__ tile_rows)
 {
     static_assert(kTileRows % kWave == 0 && kTileRows <= 1024, "one thread per row and per bin");
@@ -421,7 +407,7 @@ __global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restri
     const int64_t tile = blockIdx.x, rb = tile / ncb, cb = tile - rb * ncb;
     const int l = threadIdx.x;
     const int64_t r = rb * kTileRows + l;
-    const int32_t c = r < out ? tile_ptr[r * (ncb + 1) + cb + 1] - tile_ptr[r * (ncb + 1) + cb] : -1;
+    const int32_t c = r < nseg ? tile_ptr[r * (ncb + 1) + cb + 1] - tile_ptr[r * (ncb + 1) + cb] : -1;
     const int bin = (c < kTileRows - 2 ? c : kTileRows - 2) + 1;  // 0 .. kTileRows - 1
     bin_n[l] = 0;
     __syncthreads();
@@ -438,14 +424,17 @@ __global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restri
 
 csp_status build_tiles(csp_layer *L, hipStream_t s)
 {
-    if (!L->tile_ptr) return CSP_OK;
-    const int64_t n = ceil_div(L->nnz, 4) + L->out;
-    k_tile_ptr<<<(unsigned)ceil_div(n, 256), 256, 0, s>>>(L->rows, L->cols, L->row_ptr, L->nnz, L->out, L->tile_ncb,
-                                                          L->tile_ptr);
-    CSP_LAUNCHED("k_tile_ptr");
-    k_tile_rows<<<(unsigned)(L->tile_nrb * L->tile_ncb), kTileRows, 0, s>>>(L->tile_ptr, L->out, L->tile_ncb,
-                                                                           L->tile_rows);
-    CSP_LAUNCHED("k_tile_rows");
+    if (!L->tile_partial) return CSP_OK;
+    const Tiles *T[2] = {&L->tiles_r, &L->tiles_c};
+    const int32_t *seg_ptr[2] = {L->row_ptr, L->col_ptr}, *idx[2] = {L->cols, L->rows_by_col};
+    for (int v = 0; v < 2; ++v) {
+        k_tile_ptr<<<(unsigned)ceil_div(T[v]->nseg, 4), 256, 0, s>>>(seg_ptr[v], idx[v], T[v]->nseg, T[v]->ncb,
+                                                                     T[v]->ptr);
+        CSP_LAUNCHED("k_tile_ptr");
+        k_tile_rows<<<(unsigned)(T[v]->nrb * T[v]->ncb), kTileRows, 0, s>>>(T[v]->ptr, T[v]->nseg, T[v]->ncb,
+                                                                             T[v]->rows);
+        CSP_LAUNCHED("k_tile_rows");
+    }
     return CSP_OK;
 }
 

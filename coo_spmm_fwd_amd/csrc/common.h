@@ -98,16 +98,23 @@ constexpr int kSelCountWords = kSelClassWords + 3 * kSplitClasses;  // words rea
 // workgroup can finish 1, 2, 4 or 8 of them (kGroupWaves >> c waves each).
 __host__ __device__ inline int split_class(uint32_t p) { return p > 8 ? 0 : p > 4 ? 1 : p > 2 ? 2 : 3; }
 
-// Value-gradient tiles (fp32 layers, batch chunks of 33..64): the layer is
-// cut into tiles of kTileRows rows x kTileCols columns; one workgroup stages a
-// tile's operand columns in LDS and computes the value gradient of the tile's
-// entries.  tile_ptr[r * (ncb + 1) + k] is the first entry of row r whose
-// column is at least k * kTileCols (k = ncb: the row's end); tile_rows holds,
-// per tile, its local rows ordered by their entry count in the tile (most
-// first, ties by row), so that the four rows a wave runs side by side have
-// similar lengths.
+// LDS tiles (fp32 layers, batch chunks of 33..64).  A view of the layer -- the
+// rows over the X columns, or the columns (transposed view) over the dY
+// columns -- is cut into tiles of kTileRows segments x kTileCols operand
+// columns; one workgroup stages a tile's operand rows in LDS once and runs
+// the tile's entries against them.  ptr[s * (ncb + 1) + k] is the first entry
+// of segment s whose index is at least k * kTileCols (k = ncb: the segment's
+// end); rows holds, per tile, its local segments ordered by their entry count
+// in the tile (most first), so that the four segments a wave runs side by
+// side have similar lengths.
 constexpr int kTileCols = 512;
 constexpr int kTileRows = 512;
+
+struct Tiles {
+    int32_t *ptr = nullptr;   // [nseg][ncb + 1]
+    int16_t *rows = nullptr;  // [nrb * ncb][kTileRows], tile = row block * ncb + column block
+    int64_t nseg = 0, nop = 0, ncb = 0, nrb = 0;
+};
 
 struct TaskList {
     int4 *desc = nullptr;   // [cap] {segment, first entry, end entry, partial slot or -1}
@@ -143,10 +150,12 @@ struct csp_layer {
     // task lists may then describe a layer that was never completed, so every
     // later call but destroy refuses the layer.
     bool broken = false;
-    // value-gradient tiles (allocated at create for fp32 layers with in >= 2 * kTileCols; else null)
-    int32_t *tile_ptr = nullptr;
-    int16_t *tile_rows = nullptr;
-    int64_t tile_ncb = 0, tile_nrb = 0;
+    // LDS tiles of the row view (value gradient, forward) and of the column
+    // view (input gradient), and the partial sums of the segment passes:
+    // [ncb][nseg][64] floats for the larger view.  Allocated at create for
+    // fp32 layers with at least one tile per compute unit in both views.
+    csp::Tiles tiles_r, tiles_c;
+    float *tile_partial = nullptr;
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request
@@ -218,8 +227,8 @@ int32_t pack_limit(const csp_layer *L);
 csp_status set_task_counts(csp_layer *L, const uint32_t *counts);
 // vals_c[j] = vals[perm_c[j]] after the canonical values changed.
 csp_status refresh_column_values(csp_layer *L, hipStream_t s);
-// Value-gradient tiles from row_ptr and cols (two launches, no host sync);
-// nothing to do for a layer without tiles.
+// Tiles of both views from row_ptr / cols and col_ptr / rows_by_col (four
+// launches, no host sync); nothing to do for a layer without tiles.
 csp_status build_tiles(csp_layer *L, hipStream_t s);
 inline int64_t task_cap(int64_t nseg, int64_t nnz) { return nseg + (nnz + kTaskChunk - 1) / kTaskChunk; }
 

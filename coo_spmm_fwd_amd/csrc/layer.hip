@@ -75,7 +75,7 @@ void free_layer(csp_layer *L)
                     L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first,
                     L->row_packed.desc, L->row_packed.split,
                     L->row_tasks.split_cls, L->col_tasks.split_cls, L->row_packed.split_cls,
-                    L->tile_ptr, L->tile_rows};
+                    L->tiles_r.ptr, L->tiles_r.rows, L->tiles_c.ptr, L->tiles_c.rows, L->tile_partial};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete L;
@@ -149,12 +149,24 @@ csp_status alloc_layer(csp_layer *L)
         csp_status st = dalloc(r.p, r.bytes, r.what);
         if (st != CSP_OK) return st;
     }
-    if (L->esz == 4 && in >= 2 * kTileCols) {
-        L->tile_ncb = ceil_div(in, kTileCols);
-        L->tile_nrb = ceil_div(out, kTileRows);
-        csp_status st = dalloc((void **)&L->tile_ptr, 4 * (size_t)out * (size_t)(L->tile_ncb + 1), "tile offsets");
-        if (st == CSP_OK)
-            st = dalloc((void **)&L->tile_rows, 2 * (size_t)(L->tile_nrb * L->tile_ncb) * kTileRows, "tile row order");
+    // LDS tiles: fp32, and at least one tile per compute unit (fewer would leave units idle)
+    if (L->esz == 4 && ceil_div(out, kTileRows) * ceil_div(in, kTileCols) >= L->act.cus) {
+        Tiles *T[2] = {&L->tiles_r, &L->tiles_c};
+        const int64_t nseg[2] = {out, in}, nop[2] = {in, out};
+        size_t partial = 0;
+        for (int v = 0; v < 2; ++v) {
+            T[v]->nseg = nseg[v];
+            T[v]->nop = nop[v];
+            T[v]->ncb = ceil_div(nop[v], kTileCols);
+            T[v]->nrb = ceil_div(nseg[v], kTileRows);
+            csp_status st = dalloc((void **)&T[v]->ptr, 4 * (size_t)nseg[v] * (size_t)(T[v]->ncb + 1), "tile offsets");
+            if (st == CSP_OK)
+                st = dalloc((void **)&T[v]->rows, 2 * (size_t)(T[v]->nrb * T[v]->ncb) * kTileRows, "tile row order");
+            if (st != CSP_OK) return st;
+            const size_t p = sizeof(float) * kSliceRows * (size_t)T[v]->ncb * (size_t)nseg[v];
+            partial = p > partial ? p : partial;
+        }
+        csp_status st = dalloc((void **)&L->tile_partial, partial, "tile partial sums");
         if (st != CSP_OK) return st;
     }
     if (!bitmap) return CSP_OK;

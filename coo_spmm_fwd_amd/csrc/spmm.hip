@@ -749,7 +749,7 @@ __global__ __launch_bounds__(kPW * kWave) void k_values_rows(const int4 *__restr
 // batch-minor tables are zero).  The task-list kernel above pulls one 256-byte
 // operand row through its CU's vector-memory path per stored entry, and at
 // this width that path bounds it.  Here one workgroup of kTileWaves waves
-// takes a tile of kTileRows rows x kTileCols columns (tile_ptr, tile_rows):
+// takes a tile of kTileRows rows x kTileCols columns (Tiles of the row view):
 // it copies the tile's operand rows XT[c][0..63] (128 KiB) into LDS once, and
 // every entry of the tile reads its row from there.
 // A wave runs four rows side by side, one per 16-lane DPP row: lane q holds
@@ -920,6 +920,203 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int32
         cdy = ndy;
 #pragma unroll
         for (int j = 0; j < kTilePF; ++j) ci[j] = ni[j];
+    }
+}
+
+// ------------------------------------------- segment sums, LDS tiles
+// fp32, batch chunks of width 64: the same tiles for the forward (row view:
+// segments are rows, entries their columns, operand X) and the input gradient
+// (column view: segments are columns, entries their rows in the transposed
+// order with the column-ordered values, operand dY).  The workgroup of a tile
+// stages the operand rows of its kTileCols column block in LDS and adds, for
+// each of its segments, the entries that fall in the block; the result is one
+// partial sum per (column block, segment, batch slot) in P[cb][seg][64]
+// (float4 stores of 256-byte runs), and k_tile_reduce adds the column blocks
+// in order.  A wave runs four segments side by side as in k_values_tiles: lane
+// q of a 16-lane row accumulates batch slots 4q .. 4q + 3 of its segment, one
+// fused multiply-add chain per slot in entry order.
+template <int T>
+__device__ __forceinline__ float row_bcast_f(float v)
+{
+    return __int_as_float(row_bcast<T>(__float_as_int(v)));
+}
+
+template <int T>
+__device__ __forceinline__ void tile_steps(const char *tab, int coff, float v, int q16, float (&acc)[4])
+{
+    const int a0 = row_bcast<T>(coff) + q16, a1 = row_bcast<T + 1>(coff) + q16;
+    const int a2 = row_bcast<T + 2>(coff) + q16, a3 = row_bcast<T + 3>(coff) + q16;
+    const float4 x0 = *reinterpret_cast<const float4 *>(tab + a0);
+    const float4 x1 = *reinterpret_cast<const float4 *>(tab + a1);
+    const float4 x2 = *reinterpret_cast<const float4 *>(tab + a2);
+    const float4 x3 = *reinterpret_cast<const float4 *>(tab + a3);
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    const float v0 = row_bcast_f<T>(v), v1 = row_bcast_f<T + 1>(v), v2 = row_bcast_f<T + 2>(v),
+                v3 = row_bcast_f<T + 3>(v);
+    acc[0] = __builtin_fmaf(v0, x0.x, acc[0]); acc[1] = __builtin_fmaf(v0, x0.y, acc[1]);
+    acc[2] = __builtin_fmaf(v0, x0.z, acc[2]); acc[3] = __builtin_fmaf(v0, x0.w, acc[3]);
+    acc[0] = __builtin_fmaf(v1, x1.x, acc[0]); acc[1] = __builtin_fmaf(v1, x1.y, acc[1]);
+    acc[2] = __builtin_fmaf(v1, x1.z, acc[2]); acc[3] = __builtin_fmaf(v1, x1.w, acc[3]);
+    acc[0] = __builtin_fmaf(v2, x2.x, acc[0]); acc[1] = __builtin_fmaf(v2, x2.y, acc[1]);
+    acc[2] = __builtin_fmaf(v2, x2.z, acc[2]); acc[3] = __builtin_fmaf(v2, x2.w, acc[3]);
+    acc[0] = __builtin_fmaf(v3, x3.x, acc[0]); acc[1] = __builtin_fmaf(v3, x3.y, acc[1]);
+    acc[2] = __builtin_fmaf(v3, x3.z, acc[2]); acc[3] = __builtin_fmaf(v3, x3.w, acc[3]);
+    __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+}
+
+__global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int32_t *__restrict__ tile_ptr,
+                                                                      const int16_t *__restrict__ tile_rows,
+                                                                      int64_t ncb, const int32_t *__restrict__ idx,
+                                                                      const float *__restrict__ vals,
+                                                                      const float *__restrict__ opT, int64_t n_op,
+                                                                      int64_t n_seg, float *__restrict__ P)
+{
+    constexpr int G = kTileRows / (4 * kTileWaves);
+    constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);
+    __shared__ float4 tab[(kTileCols + 1) * 16];  // the block's operand rows, then a row of zeros
+    const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
+    const int64_t c0 = cb * kTileCols, r0 = rb * kTileRows;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
+    int mybeg = 0, myend = 0, myrow = 0;
+    if (lane < 4 * G) {
+        myrow = tile_rows[blockIdx.x * (int64_t)kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
+        const int64_t r = r0 + myrow;
+        if (r < n_seg) {
+            mybeg = tile_ptr[r * (ncb + 1) + cb];
+            myend = tile_ptr[r * (ncb + 1) + cb + 1];
+        }
+    }
+    const int64_t ncols = n_op - c0 < kTileCols ? n_op - c0 : kTileCols;
+    const float4 *o4 = reinterpret_cast<const float4 *>(opT);
+    float4 fl[FILL];
+#pragma unroll
+    for (int j = 0; j < FILL; ++j) {
+        const int i = threadIdx.x + kTileWaves * kWave * j, c = i >> 4;
+        fl[j] = o4[(c0 + (c < ncols ? c : 0)) * 16 + (i & 15)];
+    }
+    int cbeg, cn, nbeg = 0, nn = 0;
+    int ci[kTilePF], ni[kTilePF] = {};
+    float cv[kTilePF], nv[kTilePF] = {};
+    auto fetch = [&](int i, int &beg, int &n, int (&ii)[kTilePF], float (&vv)[kTilePF]) {
+        beg = __shfl(mybeg, 4 * i + g);
+        n = __shfl(myend, 4 * i + g) - beg;
+#pragma unroll
+        for (int j = 0; j < kTilePF; ++j) {
+            const int e = 16 * j + q;
+            const int p = e < n ? beg + e : 0;
+            ii[j] = idx[p];
+            vv[j] = vals[p];
+        }
+    };
+    fetch(0, cbeg, cn, ci, cv);
+#pragma unroll
+    for (int j = 0; j < FILL; ++j) {
+        const int i = threadIdx.x + kTileWaves * kWave * j;
+        tab[i] = (i >> 4) < ncols ? fl[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (threadIdx.x < 16) tab[kTileCols * 16 + threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    const char *base = reinterpret_cast<const char *>(tab);
+    for (int i = 0; i < G; ++i) {
+        if (i + 1 < G) fetch(i + 1, nbeg, nn, ni, nv);
+        const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
+                             max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < nmax; k += 16) {
+            const int e = k + q;
+            int c;
+            float v;
+            if (k < 16 * kTilePF) {
+                const int j = k >> 4;
+                c = j == 0 ? ci[0] : (j == 1 ? ci[1] : ci[2]);
+                v = j == 0 ? cv[0] : (j == 1 ? cv[1] : cv[2]);
+            } else {  // a segment with more than 16 * kTilePF entries in the tile
+                const int p = e < cn ? cbeg + e : 0;
+                c = idx[p];
+                v = vals[p];
+            }
+            const uint32_t rel = (uint32_t)((int64_t)c - c0);
+            const bool ok = e < cn && rel < (uint32_t)kTileCols;
+            // steps past the segment's entries read the zero row (an inf or NaN in
+            // the block's first row must not reach the sum through a zero weight)
+            const int coff = ok ? (int)rel * 256 : kTileCols * 256;
+            const float vv = ok ? v : 0.f;
+            tile_steps<0>(base, coff, vv, q16, acc);
+            if (k + 4 >= nmax) continue;
+            tile_steps<4>(base, coff, vv, q16, acc);
+            if (k + 8 >= nmax) continue;
+            tile_steps<8>(base, coff, vv, q16, acc);
+            if (k + 12 >= nmax) continue;
+            tile_steps<12>(base, coff, vv, q16, acc);
+        }
+        const int64_t r = r0 + __shfl(myrow, 4 * i + g);
+        if (r < n_seg)
+            reinterpret_cast<float4 *>(P)[(cb * n_seg + r) * 16 + q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        cbeg = nbeg;
+        cn = nn;
+#pragma unroll
+        for (int j = 0; j < kTilePF; ++j) {
+            ci[j] = ni[j];
+            cv[j] = nv[j];
+        }
+    }
+}
+
+// out[b, seg] = epilogue(sum over column blocks cb, in order, of P[cb][seg][b]).
+// A block takes kReduceSegs segments: thread t adds the float4 t (and t + 256)
+// of their 64-slot runs over the column blocks (eight loads in flight), the
+// sums are turned around in LDS, and each batch row leaves as one run of
+// kReduceSegs values.
+constexpr int kReduceSegs = 32;
+template <int E>
+__global__ __launch_bounds__(256) void k_tile_reduce(const float *__restrict__ P, int64_t ncb, int64_t n_seg, int64_t B,
+                                                     float *__restrict__ out, Epi ep)
+{
+    constexpr int PER = kReduceSegs * 16 / 256;  // float4 per thread
+    __shared__ float t[kReduceSegs][65];
+    const int64_t s0 = (int64_t)blockIdx.x * kReduceSegs;
+    const int nsg = (int)(n_seg - s0 < kReduceSegs ? n_seg - s0 : kReduceSegs);
+    const float4 *src = reinterpret_cast<const float4 *>(P) + s0 * 16;
+    const int64_t stride = n_seg * 16;
+    float4 a[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    int64_t cb = 0;
+    for (; cb + 8 <= ncb; cb += 8) {
+        float4 x[8][PER];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                const int f = threadIdx.x + 256 * i;
+                x[j][i] = (f >> 4) < nsg ? src[(cb + j) * stride + f] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int i = 0; i < PER; ++i) {
+                a[i].x += x[j][i].x; a[i].y += x[j][i].y; a[i].z += x[j][i].z; a[i].w += x[j][i].w;
+            }
+    }
+    for (; cb < ncb; ++cb)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int f = threadIdx.x + 256 * i;
+            const float4 x = (f >> 4) < nsg ? src[cb * stride + f] : make_float4(0.f, 0.f, 0.f, 0.f);
+            a[i].x += x.x; a[i].y += x.y; a[i].z += x.z; a[i].w += x.w;
+        }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int f = threadIdx.x + 256 * i, sl = f >> 4, b0 = (f & 15) * 4;
+        t[sl][b0] = a[i].x; t[sl][b0 + 1] = a[i].y; t[sl][b0 + 2] = a[i].z; t[sl][b0 + 3] = a[i].w;
+    }
+    __syncthreads();
+    const int sl = threadIdx.x % kReduceSegs;
+#pragma unroll
+    for (int i = 0; i < 64 * kReduceSegs / 256; ++i) {
+        const int64_t b = threadIdx.x / kReduceSegs + (256 / kReduceSegs) * i;
+        if (b < B && sl < nsg) out[b * n_seg + s0 + sl] = finish_out<E, F32>(t[sl][b], b, s0 + sl, n_seg, ep);
     }
 }
 
@@ -1421,7 +1618,7 @@ csp_status bwd_input_dispatch(csp_layer *L, const void *dYT, int64_t B, void *dX
 // COOSPMM_VALUE_TILES=0 turns it off (a test hook: the results are the same).
 inline bool value_tiles_usable(const csp_layer *L, int ld)
 {
-    if (!L->tile_ptr || ld != 64 || L->tile_nrb * L->tile_ncb < L->act.cus) return false;
+    if (!L->tile_partial || ld != 64) return false;
     const char *e = std::getenv("COOSPMM_VALUE_TILES");
     return !(e && e[0] == '0');
 }
@@ -1429,9 +1626,35 @@ inline bool value_tiles_usable(const csp_layer *L, int ld)
 csp_status launch_value_tiles(csp_layer *L, int mark, const float *XT, const float *dYT, float *dW, bool acc,
                               hipStream_t s)
 {
-    launch_main(L, mark, k_values_tiles, dim3((unsigned)(L->tile_nrb * L->tile_ncb)), dim3(kTileWaves * kWave), 0u,
-                s, L->tile_ptr, L->tile_rows, L->tile_ncb, L->cols, XT, dYT, L->in, L->out, dW, (int)acc);
+    const Tiles &T = L->tiles_r;
+    launch_main(L, mark, k_values_tiles, dim3((unsigned)(T.nrb * T.ncb)), dim3(kTileWaves * kWave), 0u, s, T.ptr,
+                T.rows, T.ncb, L->cols, XT, dYT, L->in, L->out, dW, (int)acc);
     CSP_LAUNCHED("k_values_tiles");
+    return CSP_OK;
+}
+
+// The tile kernels for the segment sums (forward: row view; input gradient:
+// column view) at batch chunks of width 64.  The sums are added in another
+// order than the task kernel's (per tile, then the tiles in column-block
+// order), so they agree with it to rounding, not bitwise.  The variable
+// COOSPMM_SEGMENT_TILES=0 turns them off (a test hook).
+inline bool segment_tiles_usable(const csp_layer *L, int ld)
+{
+    if (!L->tile_partial || ld != 64) return false;
+    const char *e = std::getenv("COOSPMM_SEGMENT_TILES");
+    return !(e && e[0] == '0');
+}
+
+template <int E>
+csp_status launch_segment_tiles(csp_layer *L, int mark, const Tiles &T, const int32_t *idx, const float *vals,
+                                const float *opT, int64_t B, float *out, const Epi &ep, hipStream_t s)
+{
+    launch_main(L, mark & kTimeStart, k_segment_tiles, dim3((unsigned)(T.nrb * T.ncb)), dim3(kTileWaves * kWave), 0u,
+                s, T.ptr, T.rows, T.ncb, idx, vals, opT, T.nop, T.nseg, L->tile_partial);
+    CSP_LAUNCHED("k_segment_tiles");
+    launch_main(L, mark & kTimeStop, k_tile_reduce<E>, dim3((unsigned)ceil_div(T.nseg, kReduceSegs)), dim3(256), 0u, s,
+                (const float *)L->tile_partial, T.ncb, T.nseg, B, out, ep);
+    CSP_LAUNCHED("k_tile_reduce");
     return CSP_OK;
 }
 
@@ -1473,6 +1696,13 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         const unsigned gx = (unsigned)ceil_div(CT.count, kPW), gw = (unsigned)ceil_div(nrow, kPW);
         const int m1 = gw > 0 ? kTimeStart : kTimeBoth;  // the value-gradient kernel carries the end
         const bool ks = CT.nsplit == 0;
+        bool dx_tiled = false;
+        if constexpr (sizeof(T) == 4) dx_tiled = segment_tiles_usable(L, ld);
+        if (dx_tiled) {
+            const csp_status st = launch_segment_tiles<E>(L, m1, L->tiles_c, L->rows_by_col, (const float *)L->vals_c,
+                                                          (const float *)dYT, B, (float *)dX, ep, s);
+            if (st != CSP_OK) return st;
+        } else {
 #define CSP_DX2_ARGS                                                                                                \
     CT.desc, CT.count, L->col_ptr, L->rows_by_col, (const T *)L->vals_c, (const T *)dYT, L->out, L->in, B, L->act.partial, \
         (T *)dX, ep
@@ -1483,6 +1713,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
 #undef CSP_DX2
 #undef CSP_DX2_ARGS
         CSP_LAUNCHED("k_segment_spmm (input gradient)");
+        }
         bool tiled = false;
         if constexpr (sizeof(T) == 4) tiled = gw > 0 && value_tiles_usable(L, ld);
         if (tiled) {
@@ -1496,7 +1727,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
 #undef CSP_DW2
             CSP_LAUNCHED("k_values_rows");
         }
-        return split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
+        return dx_tiled ? CSP_OK : split_fixup<D, E>(L, CT, B, L->in, dX, ep, s);
     }
     const unsigned grid = (unsigned)(ceil_div(CT.count, kPW) + ceil_div(nrow, kPW));
     const bool ks = CT.nsplit == 0;
@@ -1543,6 +1774,13 @@ csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdE
     if (st != CSP_OK) return st;
     const void *xt = B == 1 ? X : wk.operand;
     float *pt = wk.partial;
+    // LDS tiles need the layer's own partial-sum buffer (not a caller's workspace)
+    if (L->dtype == CSP_F32 && wk.operand == L->act.a && segment_tiles_usable(L, pow2_ld(B))) {
+        const Tiles &T = L->tiles_r;
+        const float *v = (const float *)L->vals, *x = (const float *)xt;
+        return fe ? launch_segment_tiles<kEpiForward>(L, kTimeBoth, T, L->cols, v, x, B, (float *)Y, ep, s)
+                  : launch_segment_tiles<kEpiNone>(L, kTimeBoth, T, L->cols, v, x, B, (float *)Y, ep, s);
+    }
     if (L->dtype == CSP_BF16)
         return fe ? fwd_dispatch<BF16, kEpiForward>(L, xt, B, Y, ep, s, pt) : fwd_dispatch<BF16, kEpiNone>(L, xt, B, Y, ep, s, pt);
     return fe ? fwd_dispatch<F32, kEpiForward>(L, xt, B, Y, ep, s, pt) : fwd_dispatch<F32, kEpiNone>(L, xt, B, Y, ep, s, pt);
@@ -1579,6 +1817,12 @@ csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, co
     st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
     const void *dyt = B == 1 ? dY : L->act.a;
+    if (L->dtype == CSP_F32 && segment_tiles_usable(L, pow2_ld(B))) {
+        const Tiles &T = L->tiles_c;
+        const float *v = (const float *)L->vals_c, *g = (const float *)dyt;
+        return act_in ? launch_segment_tiles<kEpiActGrad>(L, kTimeBoth, T, L->rows_by_col, v, g, B, (float *)dX, ep, s)
+                      : launch_segment_tiles<kEpiNone>(L, kTimeBoth, T, L->rows_by_col, v, g, B, (float *)dX, ep, s);
+    }
     if (L->dtype == CSP_BF16)
         return act_in ? bwd_input_dispatch<BF16, kEpiActGrad>(L, dyt, B, dX, ep, s)
                       : bwd_input_dispatch<BF16, kEpiNone>(L, dyt, B, dX, ep, s);

@@ -1,17 +1,22 @@
-"""Value gradient through LDS tiles (fp32 layers, batch chunks 33..64 wide) against the task-list
-kernel it replaces and against fp64 sums.
+"""The LDS-tile kernels of fp32 layers at batch chunks 33..64 wide, against the oracle and against
+the task-list kernels they replace.
 
-The two kernels run the same fused multiply-add chains and add the same pairs, so their results
-must be bitwise equal.  Covered here: tiles cut by the layer's edges (out and in not multiples of
-the tile), rows longer than the windows loaded ahead (up to 1400 entries, 512 in one tile), empty
-rows, batches of one and two chunks (the second chunk accumulates), spmm_bwd_values and spmm_bwd,
-and a restructure (the tiles are rebuilt).  Parity with the oracle at the 8192-square full size is
-in test_parity; here sampled entries are checked against fp64 sums computed in the test.
+Value gradient: the tile kernel runs the task kernel's fused multiply-add chains and adds the same
+pairs, so the two must agree bitwise.  Forward and input gradient: the tiles add a segment's
+entries per column block and then the blocks in order, so they agree with the oracle within the
+fp32 bound (and the fused epilogues within theirs), not bitwise with the task kernel.
+
+The layer has tiles cut by its edges (out and in not multiples of 512), rows longer than the
+windows loaded ahead (up to 1400 entries, 512 in one tile), empty rows, and batches of one and two
+chunks (the second chunk of the value gradient accumulates).  A restructure rebuilds the tiles of
+both views.  An infinite operand value in the first column of a block must not reach the sums of
+rows that do not hold that column.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from coo_spmm_fwd_amd import binding as csp
 from coo_spmm_fwd_amd import workloads as W
 from tests.gpu_util import FP32_REL, assert_within, bits, dev, host
@@ -34,6 +39,14 @@ def tiled_layer(seed):
         vals.append(rng.standard_normal(span).astype(np.float32))
     return (np.concatenate(rows).astype(np.int32), np.concatenate(cols).astype(np.int32),
             np.concatenate(vals).astype(np.float32))
+
+
+ACT_REL = 1.3e-5   # fused GELU / GELU' outputs (derivation in tests/test_epilogue.py)
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.default()
 
 
 def both(monkeypatch, fn):
@@ -85,5 +98,93 @@ def test_value_tiles_after_restructure(monkeypatch):
             a, b = both(monkeypatch, lambda: csp.spmm_bwd_values(h, dY, X))
             assert np.array_equal(bits(host(a)), bits(host(b))), f"differs after restructure {step}"
             check_sample(h, b, X, dY, 71 + step)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+@pytest.mark.parametrize("B", [33, 64, 100])
+def test_segment_tiles_against_oracle(orc, B):
+    """Forward (plain and with bias + GELU), input gradient (plain, times GELU', and inside
+    spmm_bwd) through the tiles, each against the oracle on the same inputs."""
+    rows, cols, vals = tiled_layer(73)
+    h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
+    try:
+        X = W.random_dense((B, IN), 74 + B)
+        dY = W.random_dense((B, OUT), 75 + B)
+        bias = W.random_dense((OUT,), 76)
+        ref, S = orc.spmm_fwd(OUT, IN, rows, cols, vals, X)
+        assert_within(host(csp.spmm_fwd(h, dev(X))), ref, S, FP32_REL, f"tiled forward B={B}")
+        Hd = torch.empty((B, OUT), device="cuda")
+        A = host(csp.spmm_fwd_act(h, dev(X), bias=dev(bias), act="gelu", H=Hd))
+        pre, Sp = ref + bias.astype(np.float64), S + np.abs(bias.astype(np.float64))
+        assert_within(host(Hd), pre, Sp, FP32_REL, f"tiled forward pre-activation B={B}")
+        assert_within(A, orc.gelu(pre), Sp, ACT_REL, f"tiled forward GELU B={B}")
+        refx, Sx = orc.spmm_bwd_input(OUT, IN, rows, cols, vals, dY)
+        assert_within(host(csp.spmm_bwd_input(h, dev(dY))), refx, Sx, FP32_REL, f"tiled input gradient B={B}")
+        dX, _ = csp.spmm_bwd(h, dev(dY), dev(X))
+        assert_within(host(dX), refx, Sx, FP32_REL, f"tiled input gradient in spmm_bwd B={B}")
+        Hin = W.random_dense((B, IN), 77 + B)
+        g = orc.gelu_grad(Hin.astype(np.float64))
+        dXa = host(csp.spmm_bwd_input_act(h, dev(dY), dev(Hin), act="gelu"))
+        assert_within(dXa, refx * g, Sx, ACT_REL, f"tiled input gradient times GELU' B={B}")
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_segment_tiles_close_to_task_kernels(orc, monkeypatch):
+    """The tiled sums and the task-list sums of the same call differ only by rounding: each is
+    within the fp32 bound of the exact sum, so they are within twice that bound of each other."""
+    rows, cols, vals = tiled_layer(79)
+    h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
+    try:
+        X = W.random_dense((64, IN), 80)
+        dY = W.random_dense((64, OUT), 81)
+        out = {}
+        for flag in ("0", "1"):
+            monkeypatch.setenv("COOSPMM_SEGMENT_TILES", flag)
+            out[flag] = (host(csp.spmm_fwd(h, dev(X))), host(csp.spmm_bwd_input(h, dev(dY))))
+        _, Sf = orc.spmm_fwd(OUT, IN, rows, cols, vals, X)
+        _, Sx = orc.spmm_bwd_input(OUT, IN, rows, cols, vals, dY)
+        for k, S in enumerate((Sf, Sx)):
+            assert_within(out["1"][k], out["0"][k].astype(np.float64), S, 2 * FP32_REL,
+                          f"output {k}: tiled against task-list sums")
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_segment_tiles_after_restructure(orc):
+    rows, cols, vals = tiled_layer(83)
+    h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
+    try:
+        X = W.random_dense((64, IN), 84)
+        dY = W.random_dense((64, OUT), 85)
+        for step in range(2):
+            csp.restructure(h, csp.sparse_layer_nnz(h) // 10, seed=86, step=step, regrow_value=0.25)
+            r, c, v = (host(t) for t in csp.sparse_layer_export(h))
+            ref, S = orc.spmm_fwd(OUT, IN, r, c, v, X)
+            assert_within(host(csp.spmm_fwd(h, dev(X))), ref, S, FP32_REL, f"forward after restructure {step}")
+            ref, S = orc.spmm_bwd_input(OUT, IN, r, c, v, dY)
+            assert_within(host(csp.spmm_bwd_input(h, dev(dY))), ref, S, FP32_REL,
+                          f"input gradient after restructure {step}")
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
+def test_segment_tiles_keep_infinity_out_of_other_rows(orc):
+    """An inf in X at the first column of a column block: rows without that column stay finite and
+    match the oracle; the steps past a row's entries read a zero row, not the block's first one."""
+    rows, cols, vals = tiled_layer(87)
+    h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
+    try:
+        X = W.random_dense((64, IN), 88)
+        X[:, 512] = np.inf
+        Y = host(csp.spmm_fwd(h, dev(X)))
+        has = np.zeros(OUT, bool)
+        has[rows[cols == 512]] = True
+        assert np.all(np.isfinite(Y[:, ~has])), "an inf reached rows that do not hold its column"
+        Xf = X.copy()
+        Xf[:, 512] = 0.0
+        ref, S = orc.spmm_fwd(OUT, IN, rows, cols, vals, Xf)
+        assert_within(Y[:, ~has], ref[:, ~has], S[:, ~has], FP32_REL, "rows without the inf column")
     finally:
         csp.sparse_layer_destroy(h)
