@@ -88,3 +88,42 @@ def test_first_calls_captured(orc, B):
     finally:
         torch.cuda.synchronize()
         csp.sparse_layer_destroy(h)
+
+
+@pytest.mark.parametrize("B", [64, 100])
+def test_graph_replay_tiled_layer(B):
+    """An 8192-square fp32 layer takes the LDS tiles at batch chunks of 33..64 (forward and input
+    gradient: a tile pass and the reduce of its partial sums; value gradient: the tile pass): every
+    replay of the captured calls equals the eager result bit for bit (B = 100: two slices)."""
+    L = W.random_layer(8192, 8192, 8192 * 8192 // 100, seed=41 + B)
+    h = csp.sparse_layer_create(L.out, L.in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        X = dev(W.random_dense((B, L.in_), 3))
+        dY = dev(W.random_dense((B, L.out), 4))
+        Y_ref = csp.spmm_fwd(h, X)
+        dX_ref, dW_ref = csp.spmm_bwd(h, dY, X)
+        torch.cuda.synchronize()
+        Y = torch.full_like(Y_ref, float("nan"))
+        dX = torch.full_like(dX_ref, float("nan"))
+        dW = torch.full_like(dW_ref, float("nan"))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = torch.cuda.current_stream()
+            csp.spmm_fwd(h, X, Y, stream=s)
+            csp.spmm_bwd(h, dY, X, dX, dW, stream=s)
+        for rep in range(3):
+            Y.fill_(float("nan"))
+            dX.fill_(float("nan"))
+            dW.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Y, Y_ref), rep
+            assert torch.equal(dX, dX_ref), rep
+            assert torch.equal(dW, dW_ref), rep
+            csp.spmm_bwd(h, dev(W.random_dense((B, L.out), 20 + rep)), X)   # eager work between replays
+            torch.cuda.synchronize()
+        del g
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h)
