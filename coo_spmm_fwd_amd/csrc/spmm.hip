@@ -768,6 +768,25 @@ __global__ __launch_bounds__(kPW * kWave) void k_values_rows(const int4 *__restr
 constexpr int kTileWaves = 16;
 constexpr int kTilePF = 3;
 
+// Tile (row block rb, column block cb) of a tile kernel's workgroup.  The
+// logical tile order runs in panels of kTilePanel row blocks, column block by
+// column block within a panel, and xcd_block gives each XCD a contiguous run
+// of it: an XCD takes a compact block of tiles (4 row blocks x 8 column blocks
+// at 8192 x 8192).  Its rows' entry runs, ~100 bytes per row and tile, then
+// share their cache lines only with tiles in the same L2; ordered by column
+// block alone (each XCD taking every eighth block) each run's lines were
+// fetched once per XCD that needed a piece of them, 2.3 times the entry bytes.
+// The price is each operand block filled once per XCD that needs it (8 MiB of
+// fills rather than 2 at 8192 x 8192).
+constexpr int kTilePanel = 4;
+__device__ __forceinline__ void tile_of(int64_t ncb, int64_t nrb, int64_t &rb, int64_t &cb)
+{
+    const int64_t L = xcd_block(), panel = L / (kTilePanel * ncb), within = L - panel * kTilePanel * ncb;
+    const int64_t rows = nrb - panel * kTilePanel < kTilePanel ? nrb - panel * kTilePanel : kTilePanel;
+    cb = within / rows;
+    rb = panel * kTilePanel + within % rows;
+}
+
 template <int T>
 __device__ __forceinline__ int row_bcast(int v)
 {
@@ -842,13 +861,14 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int32
     static_assert(4 * G <= kWave, "one lane per row of the wave");
     constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);  // 16-byte pieces per thread
     __shared__ float4 tab[kTileCols * 16];
-    const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
-    const int64_t c0 = cb * kTileCols, r0 = rb * kTileRows;
+    int64_t rb, cb;
+    tile_of(ncb, gridDim.x / ncb, rb, cb);
+    const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
     // lane l < 4G: row (group l / 4, slot l % 4) of the wave, and its entries in the tile
     int mybeg = 0, myend = 0, myrow = 0;
     if (lane < 4 * G) {
-        myrow = tile_rows[blockIdx.x * (int64_t)kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
+        myrow = tile_rows[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
         const int64_t r = r0 + myrow;
         if (r < out) {
             mybeg = tile_ptr[r * (ncb + 1) + cb];
@@ -975,12 +995,13 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int3
     constexpr int G = kTileRows / (4 * kTileWaves);
     constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);
     __shared__ float4 tab[(kTileCols + 1) * 16];  // the block's operand rows, then a row of zeros
-    const int64_t cb = blockIdx.x % ncb, rb = blockIdx.x / ncb;
-    const int64_t c0 = cb * kTileCols, r0 = rb * kTileRows;
+    int64_t rb, cb;
+    tile_of(ncb, gridDim.x / ncb, rb, cb);
+    const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
     int mybeg = 0, myend = 0, myrow = 0;
     if (lane < 4 * G) {
-        myrow = tile_rows[blockIdx.x * (int64_t)kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
+        myrow = tile_rows[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
         const int64_t r = r0 + myrow;
         if (r < n_seg) {
             mybeg = tile_ptr[r * (ncb + 1) + cb];
