@@ -428,13 +428,16 @@ csp_status build_tiles(csp_layer *L, hipStream_t s)
     const Tiles *T[2] = {&L->tiles_r, &L->tiles_c};
     const int32_t *seg_ptr[2] = {L->row_ptr, L->col_ptr}, *idx[2] = {L->cols, L->rows_by_col};
     for (int v = 0; v < 2; ++v) {
-        k_tile_ptr<<<(unsigned)ceil_div(T[v]->nseg, 4), 256, 0, s>>>(seg_ptr[v], idx[v], T[v]->nseg, T[v]->ncb,
-                                                                     T[v]->ptr);
-        CSP_LAUNCHED("k_tile_ptr");
+        if (!L->tile_ptr_ready) {
+            k_tile_ptr<<<(unsigned)ceil_div(T[v]->nseg, 4), 256, 0, s>>>(seg_ptr[v], idx[v], T[v]->nseg, T[v]->ncb,
+                                                                         T[v]->ptr);
+            CSP_LAUNCHED("k_tile_ptr");
+        }
         k_tile_rows<<<(unsigned)(T[v]->nrb * T[v]->ncb), kTileRows, 0, s>>>(T[v]->ptr, T[v]->nseg, T[v]->ncb,
                                                                              T[v]->rows);
         CSP_LAUNCHED("k_tile_rows");
     }
+    L->tile_ptr_ready = false;
     return CSP_OK;
 }
 

@@ -156,6 +156,7 @@ struct csp_layer {
     // fp32 layers with at least one tile per compute unit in both views.
     csp::Tiles tiles_r, tiles_c;
     float *tile_partial = nullptr;
+    bool tile_ptr_ready = false;  // a bitmap rebuild wrote both views' tile offsets
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request

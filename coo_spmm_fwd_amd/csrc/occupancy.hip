@@ -227,21 +227,43 @@ __global__ __launch_bounds__(kThreads) void k_bm_prune_count(K keyof, int64_t n,
 }
 
 // One block of 1024: exclusive scans (in place) of the interleaved per-tile
-// counts; clears the regrow counters and the select histograms.
+// counts; clears the regrow counters and the select histograms.  A thread
+// takes a run of tiles and reads it in groups of kScanGroup pairs, all loads
+// of a group in flight together (a run read one load after another left the
+// block waiting on dozens of serial loads over the 67 M positions of the
+// gradient-informed regrow).
+constexpr int kScanGroup = 16;
 __global__ __launch_bounds__(1024) void k_bm_prune_scan(uint32_t *tiles, int64_t nt, uint32_t *sel)
 {
     __shared__ uint32_t lds[17];
     const int64_t per = ceil_div(nt, 1024), b0 = (int64_t)threadIdx.x * per;
-    for (int c = 0; c < 2; ++c) {
-        uint32_t sum = 0;
-        for (int64_t i = b0; i < b0 + per && i < nt; ++i) sum += tiles[2 * i + c];
-        uint32_t total;
-        uint32_t run = block_exclusive_scan(sum, lds, &total);
-        for (int64_t i = b0; i < b0 + per && i < nt; ++i) {
-            const uint32_t v = tiles[2 * i + c];
-            tiles[2 * i + c] = run;
-            run += v;
+    const int64_t e0 = b0 < nt ? b0 : nt, e1 = b0 + per < nt ? b0 + per : nt;
+    uint2 *pairs = reinterpret_cast<uint2 *>(tiles);  // (below, equal) of tile i
+    uint32_t s0 = 0, s1 = 0;
+    for (int64_t i = e0; i < e1; i += kScanGroup) {
+        uint2 v[kScanGroup];
+#pragma unroll
+        for (int g = 0; g < kScanGroup; ++g) v[g] = i + g < e1 ? pairs[i + g] : make_uint2(0u, 0u);
+#pragma unroll
+        for (int g = 0; g < kScanGroup; ++g) {
+            s0 += v[g].x;
+            s1 += v[g].y;
         }
+    }
+    uint32_t t0, t1;
+    uint32_t r0 = block_exclusive_scan(s0, lds, &t0);
+    uint32_t r1 = block_exclusive_scan(s1, lds, &t1);
+    for (int64_t i = e0; i < e1; i += kScanGroup) {
+        uint2 v[kScanGroup];
+#pragma unroll
+        for (int g = 0; g < kScanGroup; ++g) v[g] = i + g < e1 ? pairs[i + g] : make_uint2(0u, 0u);
+#pragma unroll
+        for (int g = 0; g < kScanGroup; ++g)
+            if (i + g < e1) {
+                pairs[i + g] = make_uint2(r0, r1);
+                r0 += v[g].x;
+                r1 += v[g].y;
+            }
     }
     if (threadIdx.x == 0) {
         sel[kSelCounts + 4] = 0;
@@ -565,13 +587,21 @@ __global__ __launch_bounds__(kThreads) void k_bm_canon(const uint32_t *__restric
                                                        const V *__restrict__ vals_old, V regrow, uint32_t nw,
                                                        uint32_t inw, int64_t out, int32_t *__restrict__ rows,
                                                        int32_t *__restrict__ cols, V *__restrict__ vals,
-                                                       int32_t *__restrict__ row_ptr)
+                                                       int32_t *__restrict__ row_ptr, int32_t *__restrict__ tptr,
+                                                       int64_t ncb)
 {
     const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
     if (w > nw) return;
     const uint32_t r = w / inw, cw = w - r * inw;
     uint32_t pos = pref[w];
     if (cw == 0 && r <= out) row_ptr[r] = (int32_t)pos;
+    // Tile offsets of the row view (when the layer has tiles): the first entry
+    // of row r at column 512 k or later is the rank of the row's word 16 k,
+    // and the row's end is the next row's start.
+    if (tptr) {
+        if (cw == 0 && r >= 1 && r - 1 < out) tptr[(int64_t)(r - 1) * (ncb + 1) + ncb] = (int32_t)pos;
+        if (r < out && (cw & 15u) == 0 && (int64_t)(cw >> 4) < ncb) tptr[(int64_t)r * (ncb + 1) + (cw >> 4)] = (int32_t)pos;
+    }
     if (w == nw) return;
     const uint32_t o = occ[w], oo = occ_old[w], ko = pref_old[w];
     // The word's old entries are canonical indices ko .. ko + nold - 1: their
@@ -617,6 +647,7 @@ __global__ __launch_bounds__(kThreads) void k_bm_canon(const uint32_t *__restric
 // is turned into column words by 32 x 32 bit transposes across the lanes, so
 // a column's entries in row order are the set bits of its 32 column words.
 constexpr int kTR = 1024, kTC = 64, kTSlices = kTR / 64;
+static_assert(kTR == 2 * kTileCols && kTileCols == 16 * 32, "a transposition chunk holds two tile blocks of 16 column words");
 
 __device__ __forceinline__ uint2 tile_row_words(const uint32_t *__restrict__ occ, int64_t r, int64_t rows_alloc,
                                                 int64_t inw, int64_t cg)
@@ -671,7 +702,8 @@ __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restr
                                                    int64_t nrc, int64_t in, const uint32_t *__restrict__ tscan,
                                                    const V *__restrict__ vals, int32_t *__restrict__ perm_c,
                                                    int32_t *__restrict__ rows_by_col, V *__restrict__ vals_c,
-                                                   int32_t *__restrict__ col_ptr)
+                                                   int32_t *__restrict__ col_ptr, int32_t *__restrict__ tptr,
+                                                   int64_t nrb)
 {
     __shared__ uint2 rw[kTR];                     // row words
     __shared__ uint32_t seg[kTR];                 // canonical index of the row's first entry in the tile
@@ -713,6 +745,18 @@ __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restr
         const int64_t c_glob = cg * kTC + lane;
         gout[lane] = tscan[c_glob * nrc + rc];
         if (rc == 0 && c_glob < in) col_ptr[c_glob] = (int32_t)gout[lane];
+        // Tile offsets of the column view (when the layer has tiles), in
+        // 512-row blocks: this chunk's two blocks start at the column's first
+        // entry in the chunk and after its entries in the chunk's first 512
+        // rows (its first 16 column words); the last chunk also writes the
+        // column's end.
+        if (tptr && c_glob < in) {
+            int32_t *tp = tptr + c_glob * (nrb + 1);
+            const int64_t k0 = 2 * rc;
+            if (k0 < nrb) tp[k0] = (int32_t)gout[lane];
+            if (k0 + 1 < nrb) tp[k0 + 1] = (int32_t)(gout[lane] + ccum[lane][16]);
+            if (rc == nrc - 1) tp[nrb] = (int32_t)(gout[lane] + run);
+        }
     }
     __syncthreads();
     const uint32_t total = total_s;
@@ -832,7 +876,8 @@ struct BitmapRun {
         if (st != CSP_OK) return st;
         k_bm_canon<V><<<blocks_for(nw + 1, kThreads), kThreads, 0, s>>>(
             W.occ_next, W.occ_pref_next, W.occ, W.occ_pref, (const uint64_t *)W.acc_b, (const V *)L->vals, regrow,
-            (uint32_t)nw, (uint32_t)inw, L->out, W.rows_k, W.cols_k, (V *)W.vals_k, L->row_ptr);
+            (uint32_t)nw, (uint32_t)inw, L->out, W.rows_k, W.cols_k, (V *)W.vals_k, L->row_ptr, L->tiles_r.ptr,
+            L->tiles_r.ncb);
         CSP_LAUNCHED("k_bm_canon");
         k_bm_tcount<<<(unsigned)ntiles, kThreads, 0, s>>>(W.occ_next, inw, rows_alloc, nrc, W.tcnt);
         CSP_LAUNCHED("k_bm_tcount");
@@ -840,8 +885,9 @@ struct BitmapRun {
         if (st != CSP_OK) return st;
         k_bm_tgather<V><<<(unsigned)ntiles, kThreads, 0, s>>>(W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in,
                                                         W.tcnt, (const V *)W.vals_k, L->perm_c, L->rows_by_col,
-                                                        (V *)L->vals_c, L->col_ptr);
+                                                        (V *)L->vals_c, L->col_ptr, L->tiles_c.ptr, L->tiles_c.ncb);
         CSP_LAUNCHED("k_bm_tgather");
+        L->tile_ptr_ready = L->tiles_r.ptr != nullptr;  // build_tiles then only orders the tiles' rows
         st = build_task_lists(L, s, L->narrow_seen);
         if (st != CSP_OK) return st;
         uint32_t counts[kSelCountWords] = {};

@@ -188,3 +188,34 @@ def test_segment_tiles_keep_infinity_out_of_other_rows(orc):
         assert_within(Y[:, ~has], ref[:, ~has], S[:, ~has], FP32_REL, "rows without the inf column")
     finally:
         csp.sparse_layer_destroy(h)
+
+
+def test_restructured_tiles_match_a_fresh_layer():
+    """After a bitmap restructure (random and gradient-informed regrow) the tiles' offsets come from
+    the rebuild's ranks, not from a pass over the new entries.  The forward, input gradient and value
+    gradient must then equal, bit for bit, those of a fresh layer created from the restructured
+    layer's entries (whose tile offsets come from that pass): a wrong offset would move or drop
+    entries of a tile."""
+    rows, cols, vals = tiled_layer(99)
+    h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
+    try:
+        X = dev(W.random_dense((64, IN), 100))
+        dY = dev(W.random_dense((64, OUT), 101))
+        for kind in ("random", "gradient"):
+            n_prune = csp.sparse_layer_nnz(h) // 10
+            if kind == "random":
+                csp.restructure(h, n_prune, seed=102, step=0, regrow_value=0.5)
+            else:
+                csp.restructure_grad(h, n_prune, dY, X, 0.25)
+            r, c, v = csp.sparse_layer_export(h)
+            h2 = csp.sparse_layer_create(OUT, IN, r, c, v)
+            try:
+                for name, fn in (("forward", lambda k: csp.spmm_fwd(k, X)),
+                                 ("input gradient", lambda k: csp.spmm_bwd_input(k, dY)),
+                                 ("value gradient", lambda k: csp.spmm_bwd_values(k, dY, X))):
+                    a, b = host(fn(h)), host(fn(h2))
+                    assert np.array_equal(bits(a), bits(b)), f"{name} after {kind} restructure"
+            finally:
+                csp.sparse_layer_destroy(h2)
+    finally:
+        csp.sparse_layer_destroy(h)
