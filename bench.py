@@ -741,6 +741,51 @@ class Bench:
         torch.cuda.synchronize()
         return sum(t_step) / n, sum(t_rs) / n, e[0].elapsed_time(e[1])
 
+    def dst_graph_steps(self, n, n_prune):
+        """The same full training step with restructure_async in place of restructure, captured per
+        replica in two HIP graphs (products + SGD + refresh of the column-ordered copy; the restructure)
+        and replayed on the replica cycle.  Events between the two replays time the restructure on its
+        own: no launch gaps, no host round trip.  Each replica draws its candidates from its own device
+        step counter.  The first pass over the replicas uploads the graphs (untimed); afterwards every
+        replica is synchronized (sparse_layer_sync), which would report a short regrow."""
+        torch, csp = self.torch, self.csp
+        stream = torch.cuda.current_stream()
+        caps = []
+        for r, st in enumerate(self.reps):
+            h = st["h"][0]
+            csp.sparse_layer_sync(h)
+            v = csp.sparse_layer_values_tensor(h)  # stays the layer's buffer under restructure_async
+            step = torch.tensor([5000 + 100 * r], dtype=torch.int64, device=self.dev)
+            torch.cuda.synchronize()
+            ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(ga):
+                s = torch.cuda.current_stream()
+                csp.spmm_fwd(h, st["X"], st["Y"], stream=s)
+                csp.spmm_bwd(h, st["dY"], st["X"], st["dX"], st["dW"], stream=s)
+                v.sub_(SGD_LR * st["dW"])
+                csp.sparse_layer_set_values(h, None, stream=s)
+            with torch.cuda.graph(gb):
+                csp.restructure_async(h, n_prune, seed=self.w.seed, step_dev=step, stream=torch.cuda.current_stream())
+            caps.append((ga, gb, step, v))
+        t_step, t_rs = [], []
+        for k in range(len(caps) + n):
+            ga, gb = caps[self.cycle.next()][:2]
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            ga.replay()
+            e[1].record(stream)
+            gb.replay()
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            if k >= len(caps):
+                t_step.append(e[0].elapsed_time(e[2]))
+                t_rs.append(e[1].elapsed_time(e[2]))
+        for st in self.reps:
+            csp.sparse_layer_sync(st["h"][0])
+        del caps
+        torch.cuda.synchronize()
+        return sum(t_step) / n, sum(t_rs) / n
+
     def destroy(self):
         self.torch.cuda.synchronize()
         for st in self.reps:
@@ -847,6 +892,7 @@ def main():
     if kind == "dst" and extras:
         n_prune = int(main_b.w.prune_frac * layers[0].nnz)
         step_ms, rs_ms, rsg_ms = main_b.dst_steps(5, n_prune)
+        gstep_ms, grs_ms = main_b.dst_graph_steps(10, n_prune)
         nnz = layers[0].nnz
         rbytes = bytes_restructure(nnz)
         dbytes = sbytes + bytes_sgd_refresh(nnz) + rbytes
@@ -858,6 +904,12 @@ def main():
                "restructure_gbs": round(rbytes / (rs_ms * 1e-3) / 1e9, 2),
                "restructure_frac": round(rbytes / (rs_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                "restructure_grad_ms": round(rsg_ms, 4),
+               "graph": {"step": "the same step with restructure_async (no host read-back), captured per replica "
+                                 "in two HIP graphs and replayed on the replica cycle",
+                         "ms_per_step": round(gstep_ms, 4), "gbs": round(dbytes / (gstep_ms * 1e-3) / 1e9, 2),
+                         "restructure_ms": round(grs_ms, 4),
+                         "restructure_gbs": round(rbytes / (grs_ms * 1e-3) / 1e9, 2),
+                         "restructure_frac": round(rbytes / (grs_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
                "note": "GPU time between events on the stream; the restructure reads back its accepted count "
                        "once, so its bracket includes that round trip"}
 

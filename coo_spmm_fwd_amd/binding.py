@@ -22,7 +22,7 @@ EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_fwd
             "spmm_fwd_act", "spmm_bwd_input_act", "spmm_bwd_act", "restructure_grad",
             "restructure", "sparse_layer_nnz", "sparse_layer_shape", "sparse_layer_export",
             "sparse_layer_export_index", "sparse_layer_values", "sparse_layer_set_values", "sparse_layer_time_next",
-            "sparse_layer_last_error"]
+            "sparse_layer_last_error", "restructure_async", "sparse_layer_sync"]
 
 
 class CspError(RuntimeError):
@@ -66,6 +66,10 @@ def load(path: str = LIB_PATH):
     L.spmm_bwd_act.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p, c_void_p]
     L.restructure.restype = c_int
     L.restructure.argtypes = [c_void_p, c_int64, c_uint64, c_uint64, c_float, c_void_p]
+    L.restructure_async.restype = c_int
+    L.restructure_async.argtypes = [c_void_p, c_int64, c_uint64, c_void_p, c_float, c_void_p]
+    L.sparse_layer_sync.restype = c_int
+    L.sparse_layer_sync.argtypes = [c_void_p, c_void_p]
     L.restructure_grad.restype = c_int
     L.restructure_grad.argtypes = [c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_float, c_void_p]
     L.sparse_layer_nnz.restype = c_int64
@@ -295,6 +299,20 @@ def restructure(layer: int, n_prune: int, seed: int, step: int, regrow_value: fl
     """Prune n_prune smallest-|v| entries and regrow as many at empty positions (synchronizes)."""
     _check(load().restructure(c_void_p(layer), int(n_prune), int(seed) & (2**64 - 1), int(step) & (2**64 - 1),
                               float(regrow_value), _stream(stream)))
+
+
+def restructure_async(layer: int, n_prune: int, seed: int, step_dev, regrow_value: float = 0.0, stream=None):
+    """restructure with the step read from (and advanced in) step_dev, a one-element int64 GPU
+    tensor; no host synchronization (capturable).  See the C header for what stays pending."""
+    torch = _torch()
+    sp = _dev(step_dev, "step_dev", torch.int64, (1,))
+    _check(load().restructure_async(c_void_p(layer), int(n_prune), int(seed) & (2**64 - 1), sp,
+                                    float(regrow_value), _stream(stream)))
+
+
+def sparse_layer_sync(layer: int, stream=None):
+    """Finish the bookkeeping of earlier restructure_async calls (synchronizes)."""
+    _check(load().sparse_layer_sync(c_void_p(layer), _stream(stream)))
 
 
 def restructure_grad(layer: int, n_prune: int, dY, X, regrow_value: float = 0.0, stream=None):

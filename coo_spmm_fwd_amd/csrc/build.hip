@@ -364,6 +364,26 @@ csp_status set_task_counts(csp_layer *L, const uint32_t *counts)
     return CSP_OK;
 }
 
+csp_status tasks_ready(csp_layer *L, hipStream_t s)
+{
+    if (!L->counts_stale) return CSP_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+        return set_error(CSP_ERR_INVALID_ARG, "this call needs the task lists that restructure_async left pending: "
+                                              "call sparse_layer_sync before capturing it");
+    uint32_t counts[kSelCountWords + 1] = {};  // the counts, then the short-regrow flag
+    static_assert(kSelAsyncShort == kSelCounts + kSelCountWords, "the flag follows the counts");
+    CSP_HIP(hipMemcpyAsync(counts, L->ws.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));
+    CSP_HIP(hipStreamSynchronize(s));
+    L->counts_stale = false;
+    if (counts[kSelCountWords]) {
+        L->broken = true;
+        return set_error(CSP_ERR_INVALID_ARG, "a restructure_async found fewer empty positions than it pruned in "
+                                              "its batch of candidates; the layer is incomplete");
+    }
+    return set_task_counts(L, counts);
+}
+
 // ------------------------------------------------------------- LDS tiles
 // ptr[s * (ncb + 1) + k] = first entry of segment s whose index is at least
 // k * kTileCols, one wave per segment: entry e of block b sets the slots k of

@@ -92,6 +92,7 @@ constexpr int kSelCounts = 12288;  // [0] row tasks, [1] column tasks, [2] split
 constexpr int kSplitClasses = 4;
 constexpr int kSelClassWords = 8;
 constexpr int kSelCountWords = kSelClassWords + 3 * kSplitClasses;  // words read back after a build
+constexpr int kSelAsyncShort = kSelCounts + kSelCountWords;  // set when a restructure_async regrew too few
 
 // Split segments are also kept by size class (their task count p): class 0
 // p > 8, class 1 5..8, class 2 3..4, class 3 p = 2, so that one 16-wave
@@ -157,6 +158,9 @@ struct csp_layer {
     csp::Tiles tiles_r, tiles_c;
     float *tile_partial = nullptr;
     bool tile_ptr_ready = false;  // a bitmap rebuild wrote both views' tile offsets
+    // Set by restructure_async: the host's task counts are those of the layer
+    // before it, until tasks_ready reads back the new ones.
+    bool counts_stale = false;
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request
@@ -226,6 +230,10 @@ csp_status build_task_lists(csp_layer *L, hipStream_t s, bool with_packed);
 int32_t pack_limit(const csp_layer *L);
 // Takes the kSelCountWords counts read back from sel[kSelCounts]; checks the capacities.
 csp_status set_task_counts(csp_layer *L, const uint32_t *counts);
+// After restructure_async: reads back the task counts (a synchronization on
+// s; refused on a stream that is being captured) and the short-regrow flag
+// (which leaves the layer refused).  Nothing to do otherwise.
+csp_status tasks_ready(csp_layer *L, hipStream_t s);
 // vals_c[j] = vals[perm_c[j]] after the canonical values changed.
 csp_status refresh_column_values(csp_layer *L, hipStream_t s);
 // Tiles of both views from row_ptr / cols and col_ptr / rows_by_col (four
@@ -271,6 +279,12 @@ size_t bitmap_hist_words(const csp_layer *L);
 csp_status occupancy_init(csp_layer *L, hipStream_t s);
 csp_status restructure_bitmap(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,
                               hipStream_t s);
+// The same step with one batch of candidates and no host synchronization
+// (restructure_async); the Philox step is read from and advanced at step_dev.
+csp_status restructure_bitmap_async(csp_layer *L, int64_t n_prune, uint64_t seed, const uint64_t *step_dev,
+                                    uint32_t regrow_bits, hipStream_t s);
+// Candidates of that one batch; 0 when it would not fit the workspace.
+int64_t async_batch(const csp_layer *L, int64_t n_prune);
 // Prune as restructure; regrow the empty positions with the largest |dY^T X|.
 csp_status restructure_gradient(csp_layer *L, int64_t n_prune, const void *dY, const void *X, int64_t B,
                                 uint32_t regrow_bits, hipStream_t s);

@@ -342,7 +342,9 @@ csp_status spmm_fwd_static(sparse_layer_t L, const void *X, int64_t B, void *Y, 
     CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     size_t ob = 0, pb = 0;
-    csp_status st = fwd_work_bytes(L, B, &ob, &pb);
+    csp_status st = tasks_ready(L, (hipStream_t)stream);  // the workspace size depends on the task lists
+    if (st != CSP_OK) return st;
+    st = fwd_work_bytes(L, B, &ob, &pb);
     if (st != CSP_OK) return st;
     const size_t ob_al = (ob + 255) & ~size_t(255);
     if (ob_al + pb > kScratchBytes)
@@ -425,7 +427,9 @@ csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_
     CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
-    csp_status st = run_restructure(L, n_prune, seed, step, regrow_word(L, regrow_value), s);
+    csp_status st = tasks_ready(L, s);  // a pending restructure_async must have completed in full
+    if (st != CSP_OK) return st;
+    st = run_restructure(L, n_prune, seed, step, regrow_word(L, regrow_value), s);
     if (st == CSP_OK && n_prune > 0) st = build_tiles(L, s);
     if (st == CSP_OK && n_prune > 0) {
         hipError_t e = hipStreamSynchronize(s);
@@ -447,7 +451,9 @@ csp_status restructure_grad(sparse_layer_t L, int64_t n_prune, const void *dY, c
     CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
-    csp_status st = restructure_gradient(L, n_prune, dY, X, B, regrow_word(L, regrow_value), s);
+    csp_status st = tasks_ready(L, s);
+    if (st != CSP_OK) return st;
+    st = restructure_gradient(L, n_prune, dY, X, B, regrow_word(L, regrow_value), s);
     if (st == CSP_OK && n_prune > 0) st = build_tiles(L, s);
     if (st == CSP_OK && n_prune > 0) {
         hipError_t e = hipStreamSynchronize(s);
@@ -455,6 +461,40 @@ csp_status restructure_grad(sparse_layer_t L, int64_t n_prune, const void *dY, c
     }
     if (st != CSP_OK) L->broken = true;
     return st;
+}
+
+csp_status restructure_async(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_t *step_dev, float regrow_value,
+                             void *stream)
+{
+    if (!L || !step_dev) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to restructure_async");
+    if (n_prune < 0 || n_prune > L->nnz)
+        return set_error(CSP_ERR_INVALID_ARG, "n_prune %lld outside [0, nnz = %lld]", (long long)n_prune,
+                         (long long)L->nnz);
+    if (!L->ws.bitmap)
+        return set_error(CSP_ERR_INVALID_ARG, "restructure_async needs the position bitmaps (out * in < 2^32 and "
+                                              "bitmaps within 1 GiB); use restructure");
+    if (n_prune > 0 && async_batch(L, n_prune) == 0)
+        return set_error(CSP_ERR_INVALID_ARG, "restructure_async: %lld regrow candidates do not fit one batch; use "
+                                              "restructure", (long long)n_prune);
+    DeviceGuard g(L->device);
+    CSP_USABLE(L);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    if (n_prune == 0) return CSP_OK;
+    hipStream_t s = (hipStream_t)stream;
+    csp_status st = restructure_bitmap_async(L, n_prune, seed, step_dev, regrow_word(L, regrow_value), s);
+    if (st == CSP_OK) st = build_tiles(L, s);
+    if (st == CSP_OK) L->counts_stale = true;
+    else L->broken = true;
+    return st;
+}
+
+csp_status sparse_layer_sync(sparse_layer_t L, void *stream)
+{
+    if (!L) return set_error(CSP_ERR_INVALID_ARG, "NULL layer");
+    DeviceGuard g(L->device);
+    CSP_USABLE(L);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    return tasks_ready(L, (hipStream_t)stream);
 }
 
 int64_t sparse_layer_nnz(sparse_layer_t L) { return L ? L->nnz : -1; }

@@ -400,15 +400,17 @@ __device__ inline uint32_t hash_first(const uint64_t *tab, int hbits, uint32_t p
 // share one; recomputing it is cheaper than waiting on fewer, longer chains)
 // and keeps its word.  Occupied positions drop out, the others enter the
 // hash table.
-__global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint64_t step, uint64_t i0, int64_t M,
-                                                             int64_t in, uint64_t npos, const uint32_t *occ,
+// step_dev (restructure_async): the step is read from device memory instead.
+__global__ __launch_bounds__(kThreads) void k_bm_cand_insert(uint64_t seed, uint64_t step,
+                                                             const uint64_t *__restrict__ step_dev, uint64_t i0,
+                                                             int64_t M, int64_t in, uint64_t npos, const uint32_t *occ,
                                                              int64_t inw, uint32_t *__restrict__ cand, uint64_t *tab,
                                                              int hbits)
 {
     const int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     if (j >= M) return;
     uint64_t u[4];
-    Philox4x64::block(seed, step, (i0 >> 2) + (uint64_t)(j >> 2), u);
+    Philox4x64::block(seed, step_dev ? *step_dev : step, (i0 >> 2) + (uint64_t)(j >> 2), u);
     const int q = (int)(j & 3);
     const uint64_t uq = q == 0 ? u[0] : q == 1 ? u[1] : q == 2 ? u[2] : u[3];
     const uint64_t pq = __umul64hi(uq, npos);
@@ -827,6 +829,33 @@ int hash_bits_for(int64_t M)  // smallest b with 2^b >= 2M
     return b < 1 ? 1 : b;
 }
 
+// End of restructure_async: the step counter moves on, and a sticky flag
+// records a regrow that took fewer than n_prune positions in its one batch
+// (read back by the next synchronizing call, which then refuses the layer).
+__global__ void k_bm_async_end(uint64_t *step_dev, uint32_t *sel, uint32_t n_prune)
+{
+    if (threadIdx.x != 0) return;
+    *step_dev += 1;
+    if (sel[kSelCounts + 4] != n_prune) sel[kSelAsyncShort] = 1u;
+}
+
+// Plain copy of n 32-bit words (16-byte pieces, then the tail).
+__global__ __launch_bounds__(kThreads) void k_copy_words(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst,
+                                                         int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x, n4 = n >> 2;
+    if (i < n4) reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(src)[i];
+    if (i < (n & 3)) dst[4 * n4 + i] = src[4 * n4 + i];
+}
+
+csp_status copy_words(const void *src, void *dst, int64_t n, hipStream_t s)
+{
+    if (n <= 0) return CSP_OK;
+    k_copy_words<<<blocks_for(ceil_div(n, 4), kThreads), kThreads, 0, s>>>((const uint32_t *)src, (uint32_t *)dst, n);
+    CSP_LAUNCHED("k_copy_words");
+    return CSP_OK;
+}
+
 template <typename V>
 struct BitmapRun {
     csp_layer *L;
@@ -836,6 +865,7 @@ struct BitmapRun {
     hipStream_t s;
     uint64_t i0 = 0;
     int64_t nacc = 0;
+    const uint64_t *step_dev = nullptr;  // restructure_async: the step lives on the device
 
     int64_t batch_size(int64_t cap) const
     {
@@ -851,8 +881,8 @@ struct BitmapRun {
     {
         Workspace &W = L->ws;
         const unsigned nt = blocks_for(M, kThreads);
-        k_bm_cand_insert<<<blocks_for(M, kThreads), kThreads, 0, s>>>(seed, step, i0, M, L->in, npos, W.occ_next,
-                                                                      W.occ_row_words, W.u_a, W.hash, hb);
+        k_bm_cand_insert<<<blocks_for(M, kThreads), kThreads, 0, s>>>(seed, step, step_dev, i0, M, L->in, npos,
+                                                                      W.occ_next, W.occ_row_words, W.u_a, W.hash, hb);
         CSP_LAUNCHED("k_bm_cand_insert");
         k_bm_cand_count<<<nt, kThreads, 0, s>>>(W.u_a, M, W.hash, hb, (uint64_t *)W.u_b, W.hist);
         CSP_LAUNCHED("k_bm_cand_count");
@@ -865,9 +895,11 @@ struct BitmapRun {
         return CSP_OK;
     }
 
-    // Canonical arrays (staged), transposed view and offsets from the next
-    // bitmap, task lists; reads back the counts.
-    csp_status rebuild()
+    // Canonical arrays, transposed view and offsets from the next bitmap, task
+    // lists.  rows_out and cols_out take the canonical rows and columns (the
+    // staged arrays, or the layer's own: nothing of the old ones is read);
+    // the values always go to the staged array (the old ones are read).
+    csp_status rebuild_device(int32_t *rows_out, int32_t *cols_out)
     {
         Workspace &W = L->ws;
         const int64_t nw = W.occ_words, inw = W.occ_row_words, rows_alloc = W.occ_rows;
@@ -876,7 +908,7 @@ struct BitmapRun {
         if (st != CSP_OK) return st;
         k_bm_canon<V><<<blocks_for(nw + 1, kThreads), kThreads, 0, s>>>(
             W.occ_next, W.occ_pref_next, W.occ, W.occ_pref, (const uint64_t *)W.acc_b, (const V *)L->vals, regrow,
-            (uint32_t)nw, (uint32_t)inw, L->out, W.rows_k, W.cols_k, (V *)W.vals_k, L->row_ptr, L->tiles_r.ptr,
+            (uint32_t)nw, (uint32_t)inw, L->out, rows_out, cols_out, (V *)W.vals_k, L->row_ptr, L->tiles_r.ptr,
             L->tiles_r.ncb);
         CSP_LAUNCHED("k_bm_canon");
         k_bm_tcount<<<(unsigned)ntiles, kThreads, 0, s>>>(W.occ_next, inw, rows_alloc, nrc, W.tcnt);
@@ -888,7 +920,16 @@ struct BitmapRun {
                                                         (V *)L->vals_c, L->col_ptr, L->tiles_c.ptr, L->tiles_c.ncb);
         CSP_LAUNCHED("k_bm_tgather");
         L->tile_ptr_ready = L->tiles_r.ptr != nullptr;  // build_tiles then only orders the tiles' rows
-        st = build_task_lists(L, s, L->narrow_seen);
+        return build_task_lists(L, s, L->narrow_seen);
+    }
+
+    // Eager rebuild: staged arrays, then the read-back of the taken count and
+    // the task counts; the staged arrays and bitmap become the layer's by
+    // pointer swaps.
+    csp_status rebuild()
+    {
+        Workspace &W = L->ws;
+        csp_status st = rebuild_device(W.rows_k, W.cols_k);
         if (st != CSP_OK) return st;
         uint32_t counts[kSelCountWords] = {};
         CSP_HIP(hipMemcpyAsync(counts, W.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));
@@ -971,6 +1012,26 @@ struct BitmapRun {
                                                                        W.occ_words, W.sel, (uint32_t)n_prune);
         CSP_LAUNCHED("k_bm_or");
         return rebuild();
+    }
+
+    // restructure_async: one batch of candidates sized with a wide margin,
+    // the rebuild writing the layer's own arrays (values and bitmaps copied
+    // back from their staged halves instead of swapped, so the buffers a
+    // captured graph holds stay the layer's), no read-back.
+    csp_status run_async(int64_t M)
+    {
+        Workspace &W = L->ws;
+        const int hb = hash_bits_for(M);
+        csp_status st = prune(W.hash, int64_t(1) << hb);
+        if (st == CSP_OK) st = batch(M, hb);
+        if (st == CSP_OK) st = rebuild_device(L->rows, L->cols);
+        if (st == CSP_OK) st = copy_words(W.vals_k, L->vals, ceil_div(L->nnz * (int64_t)sizeof(V), 4), s);
+        if (st == CSP_OK) st = copy_words(W.occ_next, W.occ, W.occ_words, s);
+        if (st == CSP_OK) st = copy_words(W.occ_pref_next, W.occ_pref, W.occ_words + 1, s);
+        if (st != CSP_OK) return st;
+        k_bm_async_end<<<1, 64, 0, s>>>(const_cast<uint64_t *>(step_dev), W.sel, (uint32_t)n_prune);
+        CSP_LAUNCHED("k_bm_async_end");
+        return CSP_OK;
     }
 
     csp_status run()
@@ -1082,6 +1143,41 @@ csp_status restructure_gradient(csp_layer *L, int64_t n_prune, const void *dY, c
     BitmapRun<uint32_t> r{L, n_prune, 0, 0, npos, regrow_bits, s};
     csp_status st = r.prune(nullptr, 0);
     return st != CSP_OK ? st : r.template regrow_by_gradient<F32>(dY, X, B);
+}
+
+// Candidates restructure_async draws in its one batch: the expected need
+// (n_prune over the empty fraction) times 1.5, plus 4096, so that falling
+// short (fewer empty, first-seen positions than n_prune) takes a deviation of
+// hundreds of standard deviations at the layer sizes of interest; 0 when the
+// batch would exceed the workspace.
+int64_t async_batch(const csp_layer *L, int64_t n_prune)
+{
+    const Workspace &W = L->ws;
+    const uint64_t npos = (uint64_t)L->out * (uint64_t)L->in;
+    const double free_frac = (double)(npos - (uint64_t)(L->nnz - n_prune)) / (double)npos;
+    const double want = (double)n_prune / free_frac * 1.5 + 4096.0;
+    if (want > (double)W.bm_batch_cap) return 0;
+    int64_t M = (int64_t)want;
+    return M + (4 - M % 4) % 4;  // whole Philox blocks
+}
+
+csp_status restructure_bitmap_async(csp_layer *L, int64_t n_prune, uint64_t seed, const uint64_t *step_dev,
+                                    uint32_t regrow_bits, hipStream_t s)
+{
+    const int64_t M = async_batch(L, n_prune);
+    if (M == 0)
+        return set_error(CSP_ERR_INVALID_ARG, "restructure_async: %lld regrow candidates do not fit one batch "
+                                              "(%lld); use restructure", (long long)n_prune,
+                         (long long)L->ws.bm_batch_cap);
+    const uint64_t npos = (uint64_t)L->out * (uint64_t)L->in;
+    if (L->esz == 2) {
+        BitmapRun<uint16_t> r{L, n_prune, seed, 0, npos, (uint16_t)regrow_bits, s};
+        r.step_dev = step_dev;
+        return r.run_async(M);
+    }
+    BitmapRun<uint32_t> r{L, n_prune, seed, 0, npos, regrow_bits, s};
+    r.step_dev = step_dev;
+    return r.run_async(M);
 }
 
 csp_status restructure_bitmap(csp_layer *L, int64_t n_prune, uint64_t seed, uint64_t step, uint32_t regrow_bits,

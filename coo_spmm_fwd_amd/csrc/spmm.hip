@@ -1688,6 +1688,8 @@ csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, in
     if constexpr (sizeof(T) == 4)
         if (value_tiles_usable(L, ld))
             return launch_value_tiles(L, kTimeBoth, (const float *)XT, (const float *)dYT, dW, acc, s);
+    const csp_status st = tasks_ready(L, s);
+    if (st != CSP_OK) return st;
     const TaskList &TL = L->row_tasks;
     const unsigned grid = (unsigned)ceil_div(TL.count, kPW);
 #define CSP_DW(LDV, W)                                                                                            \
@@ -1705,6 +1707,15 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
 {
     using T = typename D::T;
     const int ld = pow2_ld(B);
+    const int64_t table_bytes = (int64_t)L->esz * ld * (L->in + L->out);
+    bool both_tiled = false;  // then the task counts are not read (beyond being nonzero with entries)
+    if constexpr (sizeof(T) == 4)
+        both_tiled = table_bytes > (int64_t(2) << 20) && L->nnz > 0 && segment_tiles_usable(L, ld) &&
+                     value_tiles_usable(L, ld);
+    if (!both_tiled) {
+        const csp_status st = tasks_ready(L, s);
+        if (st != CSP_OK) return st;
+    }
     const TaskList &CT = L->col_tasks, &RT = L->row_tasks;
     const int64_t nrow = L->nnz > 0 ? RT.count : 0;  // no value-gradient work for an empty layer
     const bool wide = wide_operand(L->in > L->out ? L->in : L->out, ld);
@@ -1712,7 +1723,6 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
     // interleaved passes gather from both batch-minor tables at once; when the
     // tables together exceed about half an XCD's 4 MiB L2 they evict each
     // other, so the passes run as two launches instead.
-    const int64_t table_bytes = (int64_t)L->esz * ld * (L->in + L->out);
     if (table_bytes > (int64_t(2) << 20)) {
         const unsigned gx = (unsigned)ceil_div(CT.count, kPW), gw = (unsigned)ceil_div(nrow, kPW);
         const int m1 = gw > 0 ? kTimeStart : kTimeBoth;  // the value-gradient kernel carries the end
@@ -1782,6 +1792,7 @@ csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdE
     csp_status st = CSP_OK;
     const Epi ep = make_epi(fe);
     if (lds_segment_fits(L, B, L->in)) {
+        if ((st = tasks_ready(L, s)) != CSP_OK) return st;
         const TaskList &RT = fwd_tasks(L, B);
         const int32_t *rp = L->row_ptr, *ci = L->cols;
         const void *v = L->vals;
@@ -1791,12 +1802,14 @@ csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdE
         return fe ? segment_lds_dispatch<F32, kEpiForward>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s)
                   : segment_lds_dispatch<F32, kEpiNone>(L, RT, rp, ci, v, X, L->in, L->out, B, Y, ep, s);
     }
+    const bool tiled = L->dtype == CSP_F32 && wk.operand == L->act.a && segment_tiles_usable(L, pow2_ld(B));
+    if (!tiled && (st = tasks_ready(L, s)) != CSP_OK) return st;
     st = batch_minor(L, B, X, L->in, wk.operand, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
     const void *xt = B == 1 ? X : wk.operand;
     float *pt = wk.partial;
     // LDS tiles need the layer's own partial-sum buffer (not a caller's workspace)
-    if (L->dtype == CSP_F32 && wk.operand == L->act.a && segment_tiles_usable(L, pow2_ld(B))) {
+    if (tiled) {
         const Tiles &T = L->tiles_r;
         const float *v = (const float *)L->vals, *x = (const float *)xt;
         return fe ? launch_segment_tiles<kEpiForward>(L, kTimeBoth, T, L->cols, v, x, B, (float *)Y, ep, s)
@@ -1826,6 +1839,7 @@ csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, co
     Epi ep;
     ep.act_in = act_in;
     if (lds_segment_fits(L, B, L->out)) {
+        if ((st = tasks_ready(L, s)) != CSP_OK) return st;
         const TaskList &CT = L->col_tasks;
         const int32_t *cp = L->col_ptr, *rc = L->rows_by_col;
         const void *vc = L->vals_c;
@@ -1835,10 +1849,12 @@ csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, co
         return act_in ? segment_lds_dispatch<F32, kEpiActGrad>(L, CT, cp, rc, vc, dY, L->out, L->in, B, dX, ep, s)
                       : segment_lds_dispatch<F32, kEpiNone>(L, CT, cp, rc, vc, dY, L->out, L->in, B, dX, ep, s);
     }
+    const bool tiled = L->dtype == CSP_F32 && segment_tiles_usable(L, pow2_ld(B));
+    if (!tiled && (st = tasks_ready(L, s)) != CSP_OK) return st;
     st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
     const void *dyt = B == 1 ? dY : L->act.a;
-    if (L->dtype == CSP_F32 && segment_tiles_usable(L, pow2_ld(B))) {
+    if (tiled) {
         const Tiles &T = L->tiles_c;
         const float *v = (const float *)L->vals_c, *g = (const float *)dyt;
         return act_in ? launch_segment_tiles<kEpiActGrad>(L, kTimeBoth, T, L->rows_by_col, v, g, B, (float *)dX, ep, s)
@@ -1855,6 +1871,7 @@ csp_status bwd_values_slice(csp_layer *L, const void *dY, const void *X, int64_t
 {
     csp_status st = CSP_OK;
     if (lds_table_fits(L, B, L->in)) {
+        if ((st = tasks_ready(L, s)) != CSP_OK) return st;
         const Epi ep;
         return L->dtype == CSP_BF16 ? gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, nullptr, dW, false, acc, ep, s)
                                     : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, nullptr, dW, false, acc, ep, s);
@@ -1874,6 +1891,7 @@ csp_status bwd_slice(csp_layer *L, const void *dY, const void *X, int64_t B, voi
     Epi ep;
     ep.act_in = act_in;
     if (lds_table_fits(L, B, L->in > L->out ? L->in : L->out)) {
+        if ((st = tasks_ready(L, s)) != CSP_OK) return st;
         if (L->dtype == CSP_BF16)
             return act_in ? gradients_lds_dispatch<BF16, kEpiActGrad>(L, X, dY, B, dX, dW, true, acc, ep, s)
                           : gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, dX, dW, true, acc, ep, s);

@@ -230,6 +230,47 @@ csp_status restructure(sparse_layer_t layer, int64_t n_prune, uint64_t seed, uin
 csp_status restructure_grad(sparse_layer_t layer, int64_t n_prune, const void *dY, const void *X, int64_t B,
                             float regrow_value, void *stream);
 
+/*
+ * restructure_async -- the step of restructure (same rule, same result bit
+ * for bit for the same seed and step) enqueued on "stream" with no host
+ * synchronization and no allocation, so that a dynamic-sparse-training step
+ * (products, optimizer update, restructure) can be captured in one HIP graph
+ * (Abstract: restructuring connections during dynamic sparse training).
+ *   step_dev  device pointer to a uint64 step counter: the call draws its
+ *             candidates with step *step_dev and then adds 1 to it on the
+ *             device, so every replay of a captured call draws a new stream.
+ * Differences from restructure:
+ *  - layers with position bitmaps only (out * in < 2^32, bitmaps within
+ *    1 GiB), and n_prune whose candidates fit one batch; else
+ *    CSP_ERR_INVALID_ARG before anything is enqueued;
+ *  - one batch of candidates, about 1.5 times the expected need plus 4096:
+ *    should it hold fewer than n_prune empty, first-seen positions (a
+ *    deviation of hundreds of standard deviations for layers of 10^5
+ *    entries and more), a device flag is set, and the next call that
+ *    synchronizes on the layer (sparse_layer_sync, or a call that needs the
+ *    task lists) returns CSP_ERR_INVALID_ARG and refuses the layer;
+ *  - the canonical arrays stay in the layer's own buffers (values are written
+ *    back, not moved): sparse_layer_values pointers and captured graphs
+ *    remain valid;
+ *  - the host-side task-list counts are read back later, by the first call
+ *    that needs them (a product outside the LDS-tile path, spmm_fwd_static,
+ *    restructure, restructure_grad) or by sparse_layer_sync.  Such a call on
+ *    a stream under capture returns CSP_ERR_INVALID_ARG instead: call
+ *    sparse_layer_sync before capturing it.  The LDS-tile products
+ *    (fp32 layers with tiles, batch chunks of 33..64 rows) need no counts.
+ * Calls on one layer must be ordered on one stream, as for every call.
+ */
+csp_status restructure_async(sparse_layer_t layer, int64_t n_prune, uint64_t seed, uint64_t *step_dev,
+                             float regrow_value, void *stream);
+
+/*
+ * sparse_layer_sync -- completes the bookkeeping of earlier restructure_async
+ * calls: synchronizes on "stream", reads back the task-list counts and the
+ * short-regrow flag (CSP_ERR_INVALID_ARG, and the layer refused, if set).
+ * Returns at once when nothing is pending.  Not for use under capture.
+ */
+csp_status sparse_layer_sync(sparse_layer_t layer, void *stream);
+
 /* Number of stored entries; -1 for NULL. */
 int64_t sparse_layer_nnz(sparse_layer_t layer);
 /* Shape and dtype; returns CSP_ERR_INVALID_ARG for NULL arguments. */
