@@ -449,9 +449,12 @@ __global__ __launch_bounds__(kThreads) void k_bm_cand_count(const uint32_t *__re
 }
 
 // One block of 1024: exclusive scan of the block counts; the batch takes
-// min(flags, still needed) and the running total advances.
+// min(flags, still needed) and the running total advances.  step_dev
+// (restructure_async, one batch): the step counter moves on, and a batch that
+// took fewer than n_prune positions sets a sticky flag (read back by the next
+// synchronizing call, which then refuses the layer).
 __global__ __launch_bounds__(1024) void k_bm_cand_scan(uint32_t *tile_cnt, int64_t nt, uint32_t n_prune,
-                                                       uint32_t *sel)
+                                                       uint32_t *sel, uint64_t *step_dev)
 {
     __shared__ uint32_t lds[17];
     const int64_t per = ceil_div(nt, 1024), b0 = (int64_t)threadIdx.x * per;
@@ -466,8 +469,13 @@ __global__ __launch_bounds__(1024) void k_bm_cand_scan(uint32_t *tile_cnt, int64
     }
     if (threadIdx.x == 0) {
         const uint32_t nacc = sel[kSelCounts + 4], need = n_prune - nacc;
+        const uint32_t now = nacc + (total < need ? total : need);
         sel[kSelCounts + 5] = nacc;
-        sel[kSelCounts + 4] = nacc + (total < need ? total : need);
+        sel[kSelCounts + 4] = now;
+        if (step_dev) {
+            *step_dev += 1;
+            if (now != n_prune) sel[kSelAsyncShort] = 1u;
+        }
     }
 }
 
@@ -829,31 +837,23 @@ int hash_bits_for(int64_t M)  // smallest b with 2^b >= 2M
     return b < 1 ? 1 : b;
 }
 
-// End of restructure_async: the step counter moves on, and a sticky flag
-// records a regrow that took fewer than n_prune positions in its one batch
-// (read back by the next synchronizing call, which then refuses the layer).
-__global__ void k_bm_async_end(uint64_t *step_dev, uint32_t *sel, uint32_t n_prune)
+// Plain copies of three arrays of 32-bit words (16-byte aligned), one launch:
+// thread i copies 16-byte piece i of the concatenation, word by word at an
+// array's end.
+struct CopySeg {
+    const uint32_t *src;
+    uint32_t *dst;
+    int64_t n;
+};
+__global__ __launch_bounds__(kThreads) void k_copy3(CopySeg a, CopySeg b, CopySeg c)
 {
-    if (threadIdx.x != 0) return;
-    *step_dev += 1;
-    if (sel[kSelCounts + 4] != n_prune) sel[kSelAsyncShort] = 1u;
-}
-
-// Plain copy of n 32-bit words (16-byte pieces, then the tail).
-__global__ __launch_bounds__(kThreads) void k_copy_words(const uint32_t *__restrict__ src, uint32_t *__restrict__ dst,
-                                                         int64_t n)
-{
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x, n4 = n >> 2;
-    if (i < n4) reinterpret_cast<uint4 *>(dst)[i] = reinterpret_cast<const uint4 *>(src)[i];
-    if (i < (n & 3)) dst[4 * n4 + i] = src[4 * n4 + i];
-}
-
-csp_status copy_words(const void *src, void *dst, int64_t n, hipStream_t s)
-{
-    if (n <= 0) return CSP_OK;
-    k_copy_words<<<blocks_for(ceil_div(n, 4), kThreads), kThreads, 0, s>>>((const uint32_t *)src, (uint32_t *)dst, n);
-    CSP_LAUNCHED("k_copy_words");
-    return CSP_OK;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t na = ceil_div(a.n, 4), nb = ceil_div(b.n, 4);
+    const CopySeg &g = i < na ? a : (i < na + nb ? b : c);
+    const int64_t j = i < na ? i : (i < na + nb ? i - na : i - na - nb), w = 4 * j;
+    if (w + 4 <= g.n) reinterpret_cast<uint4 *>(g.dst)[j] = reinterpret_cast<const uint4 *>(g.src)[j];
+    else
+        for (int64_t k = w; k < g.n; ++k) g.dst[k] = g.src[k];
 }
 
 template <typename V>
@@ -886,7 +886,7 @@ struct BitmapRun {
         CSP_LAUNCHED("k_bm_cand_insert");
         k_bm_cand_count<<<nt, kThreads, 0, s>>>(W.u_a, M, W.hash, hb, (uint64_t *)W.u_b, W.hist);
         CSP_LAUNCHED("k_bm_cand_count");
-        k_bm_cand_scan<<<1, 1024, 0, s>>>(W.hist, nt, (uint32_t)n_prune, W.sel);
+        k_bm_cand_scan<<<1, 1024, 0, s>>>(W.hist, nt, (uint32_t)n_prune, W.sel, const_cast<uint64_t *>(step_dev));
         CSP_LAUNCHED("k_bm_cand_scan");
         k_bm_cand_take<<<nt, kThreads, 0, s>>>(W.u_a, M, (const uint64_t *)W.u_b, W.hist, W.sel, (uint32_t)n_prune,
                                                L->in, W.occ_next, W.occ_row_words);
@@ -1025,12 +1025,12 @@ struct BitmapRun {
         csp_status st = prune(W.hash, int64_t(1) << hb);
         if (st == CSP_OK) st = batch(M, hb);
         if (st == CSP_OK) st = rebuild_device(L->rows, L->cols);
-        if (st == CSP_OK) st = copy_words(W.vals_k, L->vals, ceil_div(L->nnz * (int64_t)sizeof(V), 4), s);
-        if (st == CSP_OK) st = copy_words(W.occ_next, W.occ, W.occ_words, s);
-        if (st == CSP_OK) st = copy_words(W.occ_pref_next, W.occ_pref, W.occ_words + 1, s);
         if (st != CSP_OK) return st;
-        k_bm_async_end<<<1, 64, 0, s>>>(const_cast<uint64_t *>(step_dev), W.sel, (uint32_t)n_prune);
-        CSP_LAUNCHED("k_bm_async_end");
+        const CopySeg a{(const uint32_t *)W.vals_k, (uint32_t *)L->vals, ceil_div(L->nnz * (int64_t)sizeof(V), 4)};
+        const CopySeg b{W.occ_next, W.occ, W.occ_words}, c{W.occ_pref_next, W.occ_pref, W.occ_words + 1};
+        const int64_t pieces = ceil_div(a.n, 4) + ceil_div(b.n, 4) + ceil_div(c.n, 4);
+        k_copy3<<<blocks_for(pieces, kThreads), kThreads, 0, s>>>(a, b, c);
+        CSP_LAUNCHED("k_copy3");
         return CSP_OK;
     }
 
@@ -1146,16 +1146,17 @@ csp_status restructure_gradient(csp_layer *L, int64_t n_prune, const void *dY, c
 }
 
 // Candidates restructure_async draws in its one batch: the expected need
-// (n_prune over the empty fraction) times 1.5, plus 4096, so that falling
-// short (fewer empty, first-seen positions than n_prune) takes a deviation of
-// hundreds of standard deviations at the layer sizes of interest; 0 when the
-// batch would exceed the workspace.
+// (n_prune over the empty fraction) times 1.2, plus 4096.  Falling short
+// (fewer empty, first-seen positions than n_prune) then takes a deviation of
+// hundreds of standard deviations: at 8192 x 8192 and 95% sparsity the
+// batch's expected surplus is ~65,000 positions against a spread of ~150.
+// 0 when the batch would exceed the workspace.
 int64_t async_batch(const csp_layer *L, int64_t n_prune)
 {
     const Workspace &W = L->ws;
     const uint64_t npos = (uint64_t)L->out * (uint64_t)L->in;
     const double free_frac = (double)(npos - (uint64_t)(L->nnz - n_prune)) / (double)npos;
-    const double want = (double)n_prune / free_frac * 1.5 + 4096.0;
+    const double want = (double)n_prune / free_frac * 1.2 + 4096.0;
     if (want > (double)W.bm_batch_cap) return 0;
     int64_t M = (int64_t)want;
     return M + (4 - M % 4) % 4;  // whole Philox blocks
