@@ -22,7 +22,8 @@ EXPORTED = ["sparse_layer_create", "sparse_layer_destroy", "spmm_fwd", "spmm_fwd
             "spmm_fwd_act", "spmm_bwd_input_act", "spmm_bwd_act", "restructure_grad",
             "restructure", "sparse_layer_nnz", "sparse_layer_shape", "sparse_layer_export",
             "sparse_layer_export_index", "sparse_layer_values", "sparse_layer_set_values", "sparse_layer_time_next",
-            "sparse_layer_last_error", "restructure_async", "sparse_layer_sync"]
+            "sparse_layer_last_error", "restructure_async", "sparse_layer_sync", "spmm_batch_minor", "spmm_fwd_bm",
+            "spmm_bwd_bm"]
 
 
 class CspError(RuntimeError):
@@ -66,6 +67,14 @@ def load(path: str = LIB_PATH):
     L.spmm_bwd_act.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p, c_void_p]
     L.restructure.restype = c_int
     L.restructure.argtypes = [c_void_p, c_int64, c_uint64, c_uint64, c_float, c_void_p]
+    L.spmm_batch_minor.restype = c_int
+    L.spmm_batch_minor.argtypes = [c_void_p, c_int64, c_int64, c_int32, c_void_p, c_void_p]
+    L.spmm_fwd_bm.restype = c_int
+    L.spmm_fwd_bm.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_void_p, c_void_p, c_void_p,
+                              c_void_p]
+    L.spmm_bwd_bm.restype = c_int
+    L.spmm_bwd_bm.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int64, c_int, c_void_p, c_void_p,
+                              c_void_p, c_void_p, c_void_p]
     L.restructure_async.restype = c_int
     L.restructure_async.argtypes = [c_void_p, c_int64, c_uint64, c_void_p, c_float, c_void_p]
     L.sparse_layer_sync.restype = c_int
@@ -292,6 +301,73 @@ def spmm_bwd_act(layer: int, dY, X, H_in, act="gelu", dX=None, dW=None, stream=N
     dxp = _dev(dX, "dX", td, (B, in_))
     wp = _dev(dW, "dW", _torch().float32, (nnz,))
     _check(load().spmm_bwd_act(c_void_p(layer), gp, xp, B, _act_code(act), hp, dxp, wp, _stream(stream)))
+    return dX, dW
+
+
+def batch_minor_ld(B: int) -> int:
+    """Row length of a batch-minor copy at batch B (the power of two >= B)."""
+    ld = 1
+    while ld < B:
+        ld *= 2
+    return ld
+
+
+def spmm_batch_minor(src, dst=None, stream=None):
+    """dst[c, b] = src[b, c] for b < B, zero pad slots up to batch_minor_ld(B); src [B, n], 2 <= B <= 64."""
+    torch = _torch()
+    B, n = int(src.shape[0]), int(src.shape[1])
+    ld = batch_minor_ld(B)
+    sp = _dev(src, "src", None, (B, n))
+    if dst is None:
+        dst = torch.empty((n, ld), dtype=src.dtype, device=src.device)
+    dp = _dev(dst, "dst", src.dtype, (n, ld))
+    _check(load().spmm_batch_minor(sp, n, B, _dtype_code(src), dp, _stream(stream)))
+    return dst
+
+
+def spmm_fwd_bm(layer: int, X, XT=None, bias=None, act="none", Y=None, H=None, YT=None, stream=None):
+    """spmm_fwd_act with X's batch-minor copy XT (optional input) and Y's copy YT (optional output,
+    [out, ld], pad slots kept zero by the caller).  2 <= B <= 64."""
+    out, in_, dt = sparse_layer_shape(layer)
+    B = int(X.shape[0])
+    ld = batch_minor_ld(B)
+    td = _torch_dtype(dt)
+    xp = _dev(X, "X", td, (B, in_))
+    xtp = None if XT is None else _dev(XT, "XT", td, (in_, ld))
+    bp = None if bias is None else _dev(bias, "bias", td, (out,))
+    if Y is None:
+        Y = _torch().empty((B, out), dtype=X.dtype, device=X.device)
+    yp = _dev(Y, "Y", td, (B, out))
+    hp = None if H is None else _dev(H, "H", td, (B, out))
+    ytp = None if YT is None else _dev(YT, "YT", td, (out, ld))
+    _check(load().spmm_fwd_bm(c_void_p(layer), xp, xtp, B, bp, _act_code(act), yp, hp, ytp, _stream(stream)))
+    return Y
+
+
+def spmm_bwd_bm(layer: int, dY, X, dYT=None, XT=None, H_in=None, act="none", dX=None, dXT=None, dW=None,
+                stream=None):
+    """spmm_bwd_act with the batch-minor copies dYT and XT (optional inputs) and dX's copy dXT
+    (optional output, [in, ld]).  2 <= B <= 64."""
+    torch = _torch()
+    out, in_, dt = sparse_layer_shape(layer)
+    nnz = sparse_layer_nnz(layer)
+    B = int(X.shape[0])
+    ld = batch_minor_ld(B)
+    td = _torch_dtype(dt)
+    gp = _dev(dY, "dY", td, (B, out))
+    xp = _dev(X, "X", td, (B, in_))
+    gtp = None if dYT is None else _dev(dYT, "dYT", td, (out, ld))
+    xtp = None if XT is None else _dev(XT, "XT", td, (in_, ld))
+    hp = None if H_in is None else _dev(H_in, "H_in", td, (B, in_))
+    if dX is None:
+        dX = torch.empty((B, in_), dtype=X.dtype, device=X.device)
+    if dW is None:
+        dW = torch.empty((nnz,), dtype=torch.float32, device=X.device)
+    dxp = _dev(dX, "dX", td, (B, in_))
+    dxtp = None if dXT is None else _dev(dXT, "dXT", td, (in_, ld))
+    wp = _dev(dW, "dW", torch.float32, (nnz,))
+    _check(load().spmm_bwd_bm(c_void_p(layer), gp, gtp, xp, xtp, B, _act_code(act), hp, dxp, dxtp, wp,
+                              _stream(stream)))
     return dX, dW
 
 

@@ -257,16 +257,29 @@ struct FwdWork {
     void *operand = nullptr;
     float *partial = nullptr;
 };
+// Caller-held batch-minor copies [n][ld], ld = the power of two >= B (one
+// slice: 2 <= B <= 64), of the gathered operands (used in place of the call's
+// own copy) and of the output (written beside the row-major one; pad slots
+// b >= B untouched): spmm_fwd_bm and spmm_bwd_bm.
+struct BmIO {
+    const void *xt = nullptr;   // X (forward, value gradient)
+    const void *dyt = nullptr;  // dY (input gradient, value gradient)
+    void *outt = nullptr;       // Y (forward) or dX (input gradient)
+};
 // fe == nullptr: plain forward.  act_in != nullptr: the input gradient is
 // multiplied by GELU'(act_in[b, c]) (act_in [B, in], layer dtype).
 csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s,
-                      const FwdWork *work = nullptr);
+                      const FwdWork *work = nullptr, const BmIO &io = BmIO{});
 // Bytes of each FwdWork buffer a forward of B rows needs (its largest slice).
 csp_status fwd_work_bytes(csp_layer *L, int64_t B, size_t *operand_bytes, size_t *partial_bytes);
-csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s);
-csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s);
+csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s,
+                            const BmIO &io = BmIO{});
+csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s,
+                             const BmIO &io = BmIO{});
 csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
-                      hipStream_t s);
+                      hipStream_t s, const BmIO &io = BmIO{});
+// The batch-minor copy [n][ld] of a row-major operand [B, n] (esz bytes per element).
+csp_status batch_minor_copy(int esz, int64_t B, const void *src, int64_t n, void *dst, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // restructure.hip

@@ -416,6 +416,60 @@ csp_status spmm_bwd_act(sparse_layer_t L, const void *dY, const void *X, int64_t
     return launch_bwd(L, dY, X, B, dX, dW, act == CSP_ACT_GELU ? H_in : nullptr, (hipStream_t)stream);
 }
 
+csp_status spmm_fwd_bm(sparse_layer_t L, const void *X, const void *XT, int64_t B, const void *bias, csp_act act,
+                       void *Y, void *H, void *YT, void *stream)
+{
+    if (!L || !X || !Y) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_fwd_bm");
+    if (B < 2 || B > kSliceRows)
+        return set_error(CSP_ERR_INVALID_ARG, "spmm_fwd_bm takes batch-minor operands for 2 <= B <= %d, got %lld",
+                         (int)kSliceRows, (long long)B);
+    if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+    if ((H && H == Y) || (YT && (YT == Y || YT == H))) return set_error(CSP_ERR_INVALID_ARG, "outputs must not overlap");
+    DeviceGuard g(L->device);
+    CSP_USABLE(L);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    FwdEpilogue fe;
+    fe.bias = bias;
+    fe.pre = H;
+    fe.gelu = act == CSP_ACT_GELU;
+    const bool plain = !bias && !H && act == CSP_ACT_NONE;  // then exactly spmm_fwd's arithmetic
+    BmIO io;
+    io.xt = XT;
+    io.outt = YT;
+    return launch_fwd(L, X, B, Y, plain ? nullptr : &fe, (hipStream_t)stream, nullptr, io);
+}
+
+csp_status spmm_bwd_bm(sparse_layer_t L, const void *dY, const void *dYT, const void *X, const void *XT, int64_t B,
+                       csp_act act, const void *H_in, void *dX, void *dXT, float *dW, void *stream)
+{
+    if (!L || !dY || !X || !dX || (!dW && L->nnz > 0)) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_bwd_bm");
+    if (B < 2 || B > kSliceRows)
+        return set_error(CSP_ERR_INVALID_ARG, "spmm_bwd_bm takes batch-minor operands for 2 <= B <= %d, got %lld",
+                         (int)kSliceRows, (long long)B);
+    if (act != CSP_ACT_NONE && act != CSP_ACT_GELU) return set_error(CSP_ERR_INVALID_ARG, "unknown activation %d", (int)act);
+    if (act == CSP_ACT_GELU && !H_in) return set_error(CSP_ERR_INVALID_ARG, "CSP_ACT_GELU needs H_in");
+    if (dXT && dXT == dX) return set_error(CSP_ERR_INVALID_ARG, "outputs must not overlap");
+    DeviceGuard g(L->device);
+    CSP_USABLE(L);
+    if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
+    BmIO io;
+    io.xt = XT;
+    io.dyt = dYT;
+    io.outt = dXT;
+    return launch_bwd(L, dY, X, B, dX, dW, act == CSP_ACT_GELU ? H_in : nullptr, (hipStream_t)stream, io);
+}
+
+csp_status spmm_batch_minor(const void *src, int64_t n, int64_t B, int32_t dtype, void *dst, void *stream)
+{
+    if (!src || !dst) return set_error(CSP_ERR_INVALID_ARG, "NULL argument to spmm_batch_minor");
+    if (B < 2 || B > kSliceRows || n < 0 || n > kIndexLimit)
+        return set_error(CSP_ERR_INVALID_ARG, "spmm_batch_minor: B %lld outside [2, %d] or n %lld outside [0, 2^31)",
+                         (long long)B, (int)kSliceRows, (long long)n);
+    if (dtype != CSP_F32 && dtype != CSP_BF16) return set_error(CSP_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+    if (n == 0) return CSP_OK;
+    return batch_minor_copy(dtype == CSP_F32 ? 4 : 2, B, src, n, dst, (hipStream_t)stream);
+}
+
 csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_t step, float regrow_value,
                        void *stream)
 {

@@ -157,6 +157,11 @@ struct Epi {
     void *pre = nullptr;           // [B, n_seg], layer dtype
     const void *act_in = nullptr;  // [B, n_seg], layer dtype
     int gelu = 0;
+    // Optional second copy of the output in the batch-minor layout
+    // [n_seg][ldT] (slots b < B written), for the next call that gathers
+    // from it: spmm_fwd_bm / spmm_bwd_bm.
+    void *outT = nullptr;
+    int ldT = 0;
 };
 
 __device__ inline float gelu_f(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
@@ -178,6 +183,16 @@ __device__ inline typename D::T finish_out(float acc, int64_t b, int64_t seg, in
     } else {
         return D::from_f(acc * gelu_grad_f(D::load((const T *)ep.act_in, b * n_seg + seg)));
     }
+}
+
+// Every store of an output value: out[b, seg], and its batch-minor copy when asked.
+template <int E, class D>
+__device__ __forceinline__ void store_out(typename D::T *__restrict__ out, float acc, int64_t b, int64_t seg,
+                                          int64_t n_seg, const Epi &ep)
+{
+    const typename D::T y = finish_out<E, D>(acc, b, seg, n_seg, ep);
+    out[b * n_seg + seg] = y;
+    if (ep.outT) reinterpret_cast<typename D::T *>(ep.outT)[seg * ep.ldT + b] = y;
 }
 
 // Lane map.  Each lane owns VW consecutive batch values of an entry (one
@@ -369,7 +384,7 @@ __device__ __attribute__((always_inline)) inline void segment_task_body(const Ta
             const int64_t b = q * VW + w;
             if (b >= B) continue;
             if (kStore == 1 || (kStore == 0 && T.slot < 0))
-                out[b * n_seg + T.seg] = finish_out<E, D>(acc[w], b, T.seg, n_seg, ep);
+                store_out<E, D>(out, acc[w], b, T.seg, n_seg, ep);
             else
                 partial[(int64_t)T.slot * LD + q * VW + w] = acc[w];
         }
@@ -530,7 +545,7 @@ __device__ __attribute__((always_inline)) inline void packed_task_body(const Tas
 #pragma unroll
         for (int w = 0; w < VW; ++w) {
             const float y = has ? res[lane * VW + w] : 0.f;
-            if (w < B) out[(int64_t)w * n_seg + T.seg + lane] = finish_out<E, D>(y, w, T.seg + lane, n_seg, ep);
+            if (w < B) store_out<E, D>(out, y, w, T.seg + lane, n_seg, ep);
         }
     }
     __builtin_amdgcn_wave_barrier();  // sums read before the next task clears the marks
@@ -611,7 +626,7 @@ __global__ __launch_bounds__(kGroupWaves * kWave) void k_segment_grouped(
                 const int4 r = recs[r2];
                 float tot = 0.f;
                 for (int32_t j = 0; j < r.z; ++j) tot += part[s2 * wps + j][b];
-                out[b * n_seg + r.x] = finish_out<E, D>(tot, b, r.x, n_seg, ep);
+                store_out<E, D>(out, tot, b, r.x, n_seg, ep);
             }
         }
         return;
@@ -652,7 +667,7 @@ __global__ __launch_bounds__(256) void k_split_fixup(const int4 *__restrict__ sp
         for (int j = 0; j < 8; ++j) tot += v[j];
     }
     for (; p < r.z; ++p) tot += src[p * stride];
-    out[bg * n_seg + r.x] = finish_out<E, D>(tot, bg, r.x, n_seg, ep);
+    store_out<E, D>(out, tot, bg, r.x, n_seg, ep);
 }
 
 // ----------------------------------------------- value gradient, row order
@@ -1137,7 +1152,7 @@ __global__ __launch_bounds__(256) void k_tile_reduce(const float *__restrict__ P
 #pragma unroll
     for (int i = 0; i < 64 * kReduceSegs / 256; ++i) {
         const int64_t b = threadIdx.x / kReduceSegs + (256 / kReduceSegs) * i;
-        if (b < B && sl < nsg) out[b * n_seg + s0 + sl] = finish_out<E, F32>(t[sl][b], b, s0 + sl, n_seg, ep);
+        if (b < B && sl < nsg) store_out<E, F32>(out, t[sl][b], b, s0 + sl, n_seg, ep);
     }
 }
 
@@ -1285,7 +1300,7 @@ __global__ __launch_bounds__(kLdsThreads) void k_segment_lds(const int4 *__restr
             const int64_t b = threadIdx.x;
             float tot = 0.f;
             for (int32_t j = 0; j < cnt; ++j) tot += part[j][b];
-            out[b * n_seg + seg] = finish_out<E, D>(tot, b, seg, n_seg, ep);
+            store_out<E, D>(out, tot, b, seg, n_seg, ep);
         }
         __syncthreads();  // partial sums consumed before the next group writes them
     }
@@ -1352,6 +1367,11 @@ csp_status batch_minor(csp_layer *L, int64_t B, const void *X1, int64_t n1, void
                        void *O2, hipStream_t s)
 {
     if (B == 1) return CSP_OK;
+    if (!X1) {  // only the second operand
+        X1 = X2, n1 = n2, O1 = O2;
+        X2 = nullptr;
+    }
+    if (!X1) return CSP_OK;
     const int ld = pow2_ld(B);
     if (!X2) n2 = 0;
     const int64_t blocks = ceil_div(n1, kBmCols) + ceil_div(n2, kBmCols);
@@ -1787,10 +1807,12 @@ Epi make_epi(const FwdEpilogue *fe)
 }
 
 csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s,
-                     const FwdWork &wk)
+                     const FwdWork &wk, const BmIO &io)
 {
     csp_status st = CSP_OK;
-    const Epi ep = make_epi(fe);
+    Epi ep = make_epi(fe);
+    ep.outT = io.outt;
+    ep.ldT = pow2_ld(B);
     if (lds_segment_fits(L, B, L->in)) {
         if ((st = tasks_ready(L, s)) != CSP_OK) return st;
         const TaskList &RT = fwd_tasks(L, B);
@@ -1804,9 +1826,9 @@ csp_status fwd_slice(csp_layer *L, const void *X, int64_t B, void *Y, const FwdE
     }
     const bool tiled = L->dtype == CSP_F32 && wk.operand == L->act.a && segment_tiles_usable(L, pow2_ld(B));
     if (!tiled && (st = tasks_ready(L, s)) != CSP_OK) return st;
-    st = batch_minor(L, B, X, L->in, wk.operand, nullptr, 0, nullptr, s);
+    st = batch_minor(L, B, io.xt ? nullptr : X, L->in, wk.operand, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
-    const void *xt = B == 1 ? X : wk.operand;
+    const void *xt = io.xt ? io.xt : (B == 1 ? X : wk.operand);
     float *pt = wk.partial;
     // LDS tiles need the layer's own partial-sum buffer (not a caller's workspace)
     if (tiled) {
@@ -1833,11 +1855,14 @@ void fwd_slice_work(csp_layer *L, int64_t B, size_t *operand_bytes, size_t *part
     if (TL.nsplit > 0 && !grouped_splits(TL, B, L->in, L->in)) *partial_bytes = sizeof(float) * ld * (size_t)TL.count;
 }
 
-csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s)
+csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s,
+                           const BmIO &io)
 {
     csp_status st = CSP_OK;
     Epi ep;
     ep.act_in = act_in;
+    ep.outT = io.outt;
+    ep.ldT = pow2_ld(B);
     if (lds_segment_fits(L, B, L->out)) {
         if ((st = tasks_ready(L, s)) != CSP_OK) return st;
         const TaskList &CT = L->col_tasks;
@@ -1851,9 +1876,9 @@ csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, co
     }
     const bool tiled = L->dtype == CSP_F32 && segment_tiles_usable(L, pow2_ld(B));
     if (!tiled && (st = tasks_ready(L, s)) != CSP_OK) return st;
-    st = batch_minor(L, B, dY, L->out, L->act.a, nullptr, 0, nullptr, s);
+    st = batch_minor(L, B, io.dyt ? nullptr : dY, L->out, L->act.a, nullptr, 0, nullptr, s);
     if (st != CSP_OK) return st;
-    const void *dyt = B == 1 ? dY : L->act.a;
+    const void *dyt = io.dyt ? io.dyt : (B == 1 ? dY : L->act.a);
     if (tiled) {
         const Tiles &T = L->tiles_c;
         const float *v = (const float *)L->vals_c, *g = (const float *)dyt;
@@ -1867,7 +1892,8 @@ csp_status bwd_input_slice(csp_layer *L, const void *dY, int64_t B, void *dX, co
                   : bwd_input_dispatch<F32, kEpiNone>(L, dyt, B, dX, ep, s);
 }
 
-csp_status bwd_values_slice(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, bool acc, hipStream_t s)
+csp_status bwd_values_slice(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, bool acc, hipStream_t s,
+                            const BmIO &io)
 {
     csp_status st = CSP_OK;
     if (lds_table_fits(L, B, L->in)) {
@@ -1876,20 +1902,22 @@ csp_status bwd_values_slice(csp_layer *L, const void *dY, const void *X, int64_t
         return L->dtype == CSP_BF16 ? gradients_lds_dispatch<BF16, kEpiNone>(L, X, dY, B, nullptr, dW, false, acc, ep, s)
                                     : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, nullptr, dW, false, acc, ep, s);
     }
-    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
+    st = batch_minor(L, B, io.xt ? nullptr : X, L->in, L->act.a, io.dyt ? nullptr : dY, L->out, L->act.b, s);
     if (st != CSP_OK) return st;
-    const void *xt = B == 1 ? X : L->act.a;
-    const void *dyt = B == 1 ? dY : L->act.b;
+    const void *xt = io.xt ? io.xt : (B == 1 ? X : L->act.a);
+    const void *dyt = io.dyt ? io.dyt : (B == 1 ? dY : L->act.b);
     return L->dtype == CSP_BF16 ? bwd_values_dispatch<BF16>(L, xt, dyt, B, dW, acc, s)
                                 : bwd_values_dispatch<F32>(L, xt, dyt, B, dW, acc, s);
 }
 
 csp_status bwd_slice(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
-                     bool acc, hipStream_t s)
+                     bool acc, hipStream_t s, const BmIO &io)
 {
     csp_status st = CSP_OK;
     Epi ep;
     ep.act_in = act_in;
+    ep.outT = io.outt;
+    ep.ldT = pow2_ld(B);
     if (lds_table_fits(L, B, L->in > L->out ? L->in : L->out)) {
         if ((st = tasks_ready(L, s)) != CSP_OK) return st;
         if (L->dtype == CSP_BF16)
@@ -1898,10 +1926,10 @@ csp_status bwd_slice(csp_layer *L, const void *dY, const void *X, int64_t B, voi
         return act_in ? gradients_lds_dispatch<F32, kEpiActGrad>(L, X, dY, B, dX, dW, true, acc, ep, s)
                       : gradients_lds_dispatch<F32, kEpiNone>(L, X, dY, B, dX, dW, true, acc, ep, s);
     }
-    st = batch_minor(L, B, X, L->in, L->act.a, dY, L->out, L->act.b, s);
+    st = batch_minor(L, B, io.xt ? nullptr : X, L->in, L->act.a, io.dyt ? nullptr : dY, L->out, L->act.b, s);
     if (st != CSP_OK) return st;
-    const void *xt = B == 1 ? X : L->act.a;
-    const void *dyt = B == 1 ? dY : L->act.b;
+    const void *xt = io.xt ? io.xt : (B == 1 ? X : L->act.a);
+    const void *dyt = io.dyt ? io.dyt : (B == 1 ? dY : L->act.b);
     if (L->dtype == CSP_BF16)
         return act_in ? bwd_dispatch<BF16, kEpiActGrad>(L, xt, dyt, B, dX, dW, acc, ep, s)
                       : bwd_dispatch<BF16, kEpiNone>(L, xt, dyt, B, dX, dW, acc, ep, s);
@@ -1941,7 +1969,7 @@ csp_status fwd_work_bytes(csp_layer *L, int64_t B, size_t *operand_bytes, size_t
 }
 
 csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const FwdEpilogue *fe, hipStream_t s,
-                      const FwdWork *work)
+                      const FwdWork *work, const BmIO &io)
 {
     FwdWork wk;
     if (work) wk = *work;
@@ -1957,46 +1985,56 @@ csp_status launch_fwd(csp_layer *L, const void *X, int64_t B, void *Y, const Fwd
             f.pre = rows_at(f.pre, b0, L->out, L->esz);
         }
         const csp_status st = fwd_slice(L, rows_at(X, b0, L->in, L->esz), bs, rows_at(Y, b0, L->out, L->esz),
-                                        fe ? &f : nullptr, s, wk);
+                                        fe ? &f : nullptr, s, wk, io);
         if (st != CSP_OK) return st;
     }
     return CSP_OK;
 }
 
-csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s)
+csp_status launch_bwd_input(csp_layer *L, const void *dY, int64_t B, void *dX, const void *act_in, hipStream_t s,
+                            const BmIO &io)
 {
     for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
         const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
         const csp_status st = bwd_input_slice(L, rows_at(dY, b0, L->out, L->esz), bs, rows_at(dX, b0, L->in, L->esz),
-                                              rows_at(act_in, b0, L->in, L->esz), s);
+                                              rows_at(act_in, b0, L->in, L->esz), s, io);
         if (st != CSP_OK) return st;
     }
     return CSP_OK;
 }
 
-csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s)
+csp_status launch_bwd_values(csp_layer *L, const void *dY, const void *X, int64_t B, float *dW, hipStream_t s,
+                             const BmIO &io)
 {
     if (L->nnz == 0) return CSP_OK;
     for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
         const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
         const csp_status st = bwd_values_slice(L, rows_at(dY, b0, L->out, L->esz), rows_at(X, b0, L->in, L->esz), bs, dW,
-                                               b0 > 0, s);
+                                               b0 > 0, s, io);
         if (st != CSP_OK) return st;
     }
     return CSP_OK;
 }
 
 csp_status launch_bwd(csp_layer *L, const void *dY, const void *X, int64_t B, void *dX, float *dW, const void *act_in,
-                      hipStream_t s)
+                      hipStream_t s, const BmIO &io)
 {
     for (int64_t b0 = 0; b0 < B; b0 += kSliceB) {
         const int64_t bs = B - b0 < kSliceB ? B - b0 : kSliceB;
         const csp_status st = bwd_slice(L, rows_at(dY, b0, L->out, L->esz), rows_at(X, b0, L->in, L->esz), bs,
                                         rows_at(dX, b0, L->in, L->esz), dW, rows_at(act_in, b0, L->in, L->esz),
-                                        b0 > 0, s);
+                                        b0 > 0, s, io);
         if (st != CSP_OK) return st;
     }
     return CSP_OK;
+}
+
+// spmm_batch_minor: the copy itself, for a caller's operand.
+csp_status batch_minor_copy(int esz, int64_t B, const void *src, int64_t n, void *dst, hipStream_t s)
+{
+    csp_layer tmp;  // only its element size is read
+    tmp.esz = esz;
+    return batch_minor(&tmp, B, src, n, dst, nullptr, 0, nullptr, s);
 }
 
 }  // namespace csp

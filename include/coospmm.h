@@ -182,6 +182,41 @@ csp_status spmm_bwd_act(sparse_layer_t layer, const void *dY, const void *X, int
                         const void *H_in, void *dX, float *dW, void *stream);
 
 /*
+ * Batch-minor operands.  For 2 <= B <= 64 the products gather their dense
+ * operand through a batch-minor copy: T[c * ld + b] = A[b, c] for b < B,
+ * where ld is the smallest power of two >= B and the pad slots B <= b < ld
+ * hold zeros.  The calls below let a caller keep such copies and hand them
+ * from one call to the next instead of each call making its own (one launch
+ * per operand): a producing call writes its output's copy beside the
+ * row-major output, and a consuming call takes it.  This is how a layer
+ * chain (the page's GPT-2 training with truly sparse layers, Abstract) avoids
+ * re-laying out every activation.  Copies are device arrays [n][ld] of the
+ * layer dtype, caller-owned.  A call writes slots b < B of an output copy; the
+ * caller keeps its pad slots zero (e.g. a buffer zeroed once, reused at the
+ * same B).  Results are bitwise those of the plain calls.
+ */
+
+/* spmm_batch_minor -- T = the batch-minor copy of the row-major [B, n]
+ * array src (dtype CSP_F32 or CSP_BF16), pad slots written as zeros.
+ * 2 <= B <= 64, else CSP_ERR_INVALID_ARG.  Asynchronous on stream. */
+csp_status spmm_batch_minor(const void *src, int64_t n, int64_t B, int32_t dtype, void *dst, void *stream);
+
+/* spmm_fwd_bm -- spmm_fwd_act (bias and act optional: with neither, and no
+ * H, exactly spmm_fwd) for 2 <= B <= 64, with
+ *   XT  the batch-minor copy of X, or NULL (the call makes its own; X itself
+ *       is always passed: some paths read it row-major);
+ *   YT  NULL, or [out][ld]: also receives Y's batch-minor copy. */
+csp_status spmm_fwd_bm(sparse_layer_t layer, const void *X, const void *XT, int64_t B, const void *bias, csp_act act,
+                       void *Y, void *H, void *YT, void *stream);
+
+/* spmm_bwd_bm -- spmm_bwd_act (act CSP_ACT_NONE: exactly spmm_bwd) for
+ * 2 <= B <= 64, with dYT and XT the batch-minor copies of dY and X, or NULL,
+ * and dXT NULL or [in][ld]: also receives dX's batch-minor copy (the next
+ * layer down takes it as its dYT). */
+csp_status spmm_bwd_bm(sparse_layer_t layer, const void *dY, const void *dYT, const void *X, const void *XT, int64_t B,
+                       csp_act act, const void *H_in, void *dX, void *dXT, float *dW, void *stream);
+
+/*
  * restructure -- one prune-and-regrow step of dynamic sparse training
  * (Abstract: an API for restructuring connections).  The rule:
  *  1. prune the n_prune stored entries with the smallest |v|, ordered by the
