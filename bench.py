@@ -506,14 +506,21 @@ class Bench:
         layers = self.layers
         st = {"h": [csp.sparse_layer_create(L.out, L.in_, *u) for L, u in zip(layers, self.uploaded)],
               "X": self.t(self.acts[B]["X"]), "dY": self.t(self.acts[B]["dY"])}
+        ld = csp.batch_minor_ld(B)
         if kind == "stack":
             st.update(acts=[torch.empty((B, L.out), device=dev, dtype=torch.bfloat16) for L in layers])
+            if B >= 2:  # batch-minor copies handed from layer to layer (pad slots stay zero)
+                st.update(XT=torch.zeros((layers[0].in_, ld), device=dev, dtype=torch.bfloat16),
+                          actsT=[torch.zeros((L.out, ld), device=dev, dtype=torch.bfloat16) for L in layers[:-1]])
         elif kind == "mlp":
             L1, L2 = layers
             st.update(H=torch.empty((B, L1.out), device=dev), A=torch.empty((B, L1.out), device=dev),
                       Y=torch.empty((B, L2.out), device=dev), dA=torch.empty((B, L1.out), device=dev),
                       dH=torch.empty((B, L1.out), device=dev), dX=torch.empty((B, L1.in_), device=dev),
                       dW1=torch.empty((L1.nnz,), device=dev), dW2=torch.empty((L2.nnz,), device=dev))
+            if B >= 2:
+                st.update(XT=torch.zeros((L1.in_, ld), device=dev), AT=torch.zeros((L1.out, ld), device=dev),
+                          dHT=torch.zeros((L1.out, ld), device=dev))
         else:
             L = layers[0]
             st.update(Y=torch.empty((B, L.out), device=dev, dtype=st["X"].dtype))
@@ -576,21 +583,79 @@ class Bench:
             return f"k_gradients_lds<{self.ld}, {self.dt_name()}, {epi}, {ks}>"
         return f"k_gradients<{self.ld}, {self.dt_name()}, false, {epi}, {ks}>"
 
+    def hands_copies(self):
+        """Whether the step hands batch-minor copies from call to call: B >= 2 and the first layer's
+        operand table too large for the LDS-table path (which reads row-major operands and copies
+        nothing; a one-row operand is its own copy)."""
+        return self.kind in ("mlp", "stack") and self.B >= 2 and not self.lds_fits(self.layers[0].in_, segment=True)
+
     def calls(self, st, stream, split=False):
         """The library calls of one step as (label, layer handle, thunk, main kernel name, algorithmic
         bytes).  split: time the two gradients of a single layer as separate calls when spmm_bwd would
         run them as two kernels anyway (one main kernel per call)."""
         csp, kind, B = self.csp, self.kind, self.B
         out = []
+        ld = csp.batch_minor_ld(B)
+        copy_bytes = lambda n, s: s * n * (B + ld)  # a batch-minor copy: read [B, n], write [n, ld]
+        copies = self.hands_copies()
         if kind == "stack":
+            if not copies:
+                for li, (h, L) in enumerate(zip(st["h"], self.layers)):
+                    src = st["X"] if li == 0 else st["acts"][li - 1]
+
+                    def f(h=h, src=src, dst=st["acts"][li], last=li + 1 == len(self.layers)):
+                        # GELU fused into the producing layer's epilogue
+                        csp.spmm_fwd_act(h, src, act="none" if last else "gelu", Y=dst, stream=stream)
+
+                    out.append((f"forward {li + 1}", h, f, self.fwd_name(L, 1),
+                                bytes_fwd(L.nnz, L.out, L.in_, B, 2, 2)))
+                return out
+            # B >= 2: the input's copy once, then each layer writes its output's copy for the next
+            out.append(("copy of X", None, lambda: csp.spmm_batch_minor(st["X"], st["XT"], stream=stream),
+                        "k_batch_minor", copy_bytes(self.layers[0].in_, 2)))
+            n = len(self.layers)
             for li, (h, L) in enumerate(zip(st["h"], self.layers)):
-                src = st["X"] if li == 0 else st["acts"][li - 1]
+                src, srcT = (st["X"], st["XT"]) if li == 0 else (st["acts"][li - 1], st["actsT"][li - 1])
+                last = li + 1 == n
+                dstT = None if last else st["actsT"][li]
 
-                def f(h=h, src=src, dst=st["acts"][li], last=li + 1 == len(self.layers)):
-                    # GELU fused into the producing layer's epilogue
-                    csp.spmm_fwd_act(h, src, act="none" if last else "gelu", Y=dst, stream=stream)
+                def f(h=h, src=src, srcT=srcT, dst=st["acts"][li], dstT=dstT, last=last):
+                    csp.spmm_fwd_bm(h, src, XT=srcT, act="none" if last else "gelu", Y=dst, YT=dstT, stream=stream)
 
-                out.append((f"forward {li + 1}", h, f, self.fwd_name(L, 1), bytes_fwd(L.nnz, L.out, L.in_, B, 2, 2)))
+                out.append((f"forward {li + 1}", h, f, self.fwd_name(L, 0 if last else 1),
+                            bytes_fwd(L.nnz, L.out, L.in_, B, 2, 2) + (0 if last else 2 * ld * L.out)))
+            return out
+        if kind == "mlp" and copies:
+            (h1, h2), (L1, L2) = st["h"], self.layers
+
+            # the copies handed along: X's made once; A's written by the first forward (read by the
+            # second forward and the second backward); dH's written by the second backward (read by
+            # the first); the second backward still copies dY itself
+            def c0():
+                csp.spmm_batch_minor(st["X"], st["XT"], stream=stream)
+
+            def f1():
+                csp.spmm_fwd_bm(h1, st["X"], XT=st["XT"], act="gelu", Y=st["A"], H=st["H"], YT=st["AT"],
+                                stream=stream)
+
+            def f2():
+                csp.spmm_fwd_bm(h2, st["A"], XT=st["AT"], Y=st["Y"], stream=stream)
+
+            def b2():
+                csp.spmm_bwd_bm(h2, st["dY"], st["A"], XT=st["AT"], H_in=st["H"], act="gelu", dX=st["dH"],
+                                dXT=st["dHT"], dW=st["dW2"], stream=stream)
+
+            def b1():
+                csp.spmm_bwd_bm(h1, st["dH"], st["X"], dYT=st["dHT"], XT=st["XT"], dX=st["dX"], dW=st["dW1"],
+                                stream=stream)
+
+            out.append(("copy of X", None, c0, "k_batch_minor", copy_bytes(L1.in_, 4)))
+            out.append(("forward 1", h1, f1, self.fwd_name(L1, 1),
+                        bytes_fwd(L1.nnz, L1.out, L1.in_, B) + 4 * ld * L1.out))
+            out.append(("forward 2", h2, f2, self.fwd_name(L2), bytes_fwd(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("backward 2", h2, b2, self.grad_name(L2, 2),
+                        bytes_gradients(L2.nnz, L2.out, L2.in_, B) + copy_bytes(L2.out, 4) + 4 * ld * L2.in_))
+            out.append(("backward 1", h1, b1, self.grad_name(L1), bytes_gradients(L1.nnz, L1.out, L1.in_, B)))
             return out
         if kind == "mlp":
             (h1, h2), (L1, L2) = st["h"], self.layers
@@ -697,8 +762,13 @@ class Bench:
         for i in range(K):
             st = self.reps[self.cycle.next()]
             for (label, h, fn, _, _), (a, b) in zip(self.calls(st, stream, split=True), ev[i]):
-                csp.sparse_layer_time_next(h, a, b)
-                fn()
+                if h is None:  # a layer-free call (the batch-minor copy): events around it
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                else:
+                    csp.sparse_layer_time_next(h, a, b)
+                    fn()
         torch.cuda.synchronize()
         per = {}
         for ci, (label, _, _, kname, kbytes) in enumerate(self.calls(self.reps[0], stream, split=True)):
@@ -932,11 +1002,14 @@ def main():
     value = sbytes / (ms_per_step * 1e-3) / 1e9
     n_ops = 1 if (kind in ("inference", "stack") or args.only) else 3
     flops = sum(2 * L.nnz * B * n_ops for L in layers)
-    steps_desc = {"stack": f"{len(layers)} x spmm_fwd with GELU between (one token batch through the stack)",
+    copies = " (X's batch-minor copy once, each later operand's copy written by the call that produced it; " \
+             "copies charged in the byte model)" if main_b.hands_copies() else ""
+    steps_desc = {"stack": f"{len(layers)} x spmm_fwd with GELU between (one token batch through the stack)" + copies,
                   "linear": "spmm_fwd + spmm_bwd (dX and dW)",
                   "dst": "spmm_fwd + spmm_bwd (dX and dW); the full training step is under dst_step",
                   "inference": "spmm_fwd",
-                  "mlp": "fwd1 with GELU epilogue, fwd2, bwd2 (dA * GELU'(H) epilogue, dW2), bwd1 (dX, dW1)"}[kind]
+                  "mlp": "fwd1 with GELU epilogue, fwd2, bwd2 (dA * GELU'(H) epilogue, dW2), bwd1 (dX, dW1)"
+                         + copies}[kind]
     if args.only:
         steps_desc = {"fwd": "spmm_fwd", "dx": "spmm_bwd_input", "dw": "spmm_bwd_values"}[args.only] + " only"
     w = main_b.w
