@@ -520,7 +520,7 @@ class Bench:
                       dW1=torch.empty((L1.nnz,), device=dev), dW2=torch.empty((L2.nnz,), device=dev))
             if B >= 2:
                 st.update(XT=torch.zeros((L1.in_, ld), device=dev), AT=torch.zeros((L1.out, ld), device=dev),
-                          dHT=torch.zeros((L1.out, ld), device=dev))
+                          dHT=torch.zeros((L1.out, ld), device=dev), dYT=torch.zeros((L2.out, ld), device=dev))
         else:
             L = layers[0]
             st.update(Y=torch.empty((B, L.out), device=dev, dtype=st["X"].dtype))
@@ -628,11 +628,14 @@ class Bench:
         if kind == "mlp" and copies:
             (h1, h2), (L1, L2) = st["h"], self.layers
 
-            # the copies handed along: X's made once; A's written by the first forward (read by the
-            # second forward and the second backward); dH's written by the second backward (read by
-            # the first); the second backward still copies dY itself
+            # the copies handed along: X's and dY's made by explicit copy calls (each charged with its
+            # own bytes and time); A's written by the first forward (read by the second forward and the
+            # second backward); dH's written by the second backward (read by the first)
             def c0():
                 csp.spmm_batch_minor(st["X"], st["XT"], stream=stream)
+
+            def c1():
+                csp.spmm_batch_minor(st["dY"], st["dYT"], stream=stream)
 
             def f1():
                 csp.spmm_fwd_bm(h1, st["X"], XT=st["XT"], act="gelu", Y=st["A"], H=st["H"], YT=st["AT"],
@@ -642,8 +645,8 @@ class Bench:
                 csp.spmm_fwd_bm(h2, st["A"], XT=st["AT"], Y=st["Y"], stream=stream)
 
             def b2():
-                csp.spmm_bwd_bm(h2, st["dY"], st["A"], XT=st["AT"], H_in=st["H"], act="gelu", dX=st["dH"],
-                                dXT=st["dHT"], dW=st["dW2"], stream=stream)
+                csp.spmm_bwd_bm(h2, st["dY"], st["A"], dYT=st["dYT"], XT=st["AT"], H_in=st["H"], act="gelu",
+                                dX=st["dH"], dXT=st["dHT"], dW=st["dW2"], stream=stream)
 
             def b1():
                 csp.spmm_bwd_bm(h1, st["dH"], st["X"], dYT=st["dHT"], XT=st["XT"], dX=st["dX"], dW=st["dW1"],
@@ -653,8 +656,9 @@ class Bench:
             out.append(("forward 1", h1, f1, self.fwd_name(L1, 1),
                         bytes_fwd(L1.nnz, L1.out, L1.in_, B) + 4 * ld * L1.out))
             out.append(("forward 2", h2, f2, self.fwd_name(L2), bytes_fwd(L2.nnz, L2.out, L2.in_, B)))
+            out.append(("copy of dY", None, c1, "k_batch_minor", copy_bytes(L2.out, 4)))
             out.append(("backward 2", h2, b2, self.grad_name(L2, 2),
-                        bytes_gradients(L2.nnz, L2.out, L2.in_, B) + copy_bytes(L2.out, 4) + 4 * ld * L2.in_))
+                        bytes_gradients(L2.nnz, L2.out, L2.in_, B) + 4 * ld * L2.in_))
             out.append(("backward 1", h1, b1, self.grad_name(L1), bytes_gradients(L1.nnz, L1.out, L1.in_, B)))
             return out
         if kind == "mlp":
@@ -1002,8 +1006,9 @@ def main():
     value = sbytes / (ms_per_step * 1e-3) / 1e9
     n_ops = 1 if (kind in ("inference", "stack") or args.only) else 3
     flops = sum(2 * L.nnz * B * n_ops for L in layers)
-    copies = " (X's batch-minor copy once, each later operand's copy written by the call that produced it; " \
-             "copies charged in the byte model)" if main_b.hands_copies() else ""
+    copies = " (batch-minor copies handed from call to call: the inputs' copies made by explicit copy calls, each " \
+             "later operand's copy written by the call that produced it; all charged in the byte model)" \
+        if main_b.hands_copies() else ""
     steps_desc = {"stack": f"{len(layers)} x spmm_fwd with GELU between (one token batch through the stack)" + copies,
                   "linear": "spmm_fwd + spmm_bwd (dX and dW)",
                   "dst": "spmm_fwd + spmm_bwd (dX and dW); the full training step is under dst_step",
