@@ -417,9 +417,10 @@ __global__ __launch_bounds__(256) void k_tile_ptr(const int32_t *__restrict__ se
 // more share a bin; segments past the view count -1 and come last), by a
 // counting sort.  Segments of equal count land in any order: the order only
 // pairs segments for the waves of the tile kernels, whose sums do not depend
-// on it.
+// on it.  Each slot records its segment's entry range in the tile beside the
+// segment, so that a tile kernel's wave finds its work with one load.
 __global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restrict__ tile_ptr, int64_t nseg,
-                                                         int64_t ncb, int16_t *__restrict__ tile_rows)
+                                                         int64_t ncb, int2 *__restrict__ slots)
 {
     static_assert(kTileRows % kWave == 0 && kTileRows <= 1024, "one thread per row and per bin");
     __shared__ uint32_t bin_n[kTileRows], bin_at[kTileRows];
@@ -427,7 +428,8 @@ __global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restri
     const int64_t tile = blockIdx.x, rb = tile / ncb, cb = tile - rb * ncb;
     const int l = threadIdx.x;
     const int64_t r = rb * kTileRows + l;
-    const int32_t c = r < nseg ? tile_ptr[r * (ncb + 1) + cb + 1] - tile_ptr[r * (ncb + 1) + cb] : -1;
+    const int32_t beg = r < nseg ? tile_ptr[r * (ncb + 1) + cb] : 0;
+    const int32_t c = r < nseg ? tile_ptr[r * (ncb + 1) + cb + 1] - beg : -1;
     const int bin = (c < kTileRows - 2 ? c : kTileRows - 2) + 1;  // 0 .. kTileRows - 1
     bin_n[l] = 0;
     __syncthreads();
@@ -439,7 +441,8 @@ __global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restri
     bin_at[kTileRows - 1 - l] = before;
     __syncthreads();
     const uint32_t pos = atomicAdd(&bin_at[bin], 1u);
-    tile_rows[tile * kTileRows + pos] = (int16_t)l;
+    static_assert(kTileRows <= 32768 && kTileCols < 65536, "segment and count share one word");
+    slots[tile * kTileRows + pos] = make_int2(beg, (l << 16) | (c > 0 ? c : 0));
 }
 
 csp_status build_tiles(csp_layer *L, hipStream_t s)
@@ -454,7 +457,7 @@ csp_status build_tiles(csp_layer *L, hipStream_t s)
             CSP_LAUNCHED("k_tile_ptr");
         }
         k_tile_rows<<<(unsigned)(T[v]->nrb * T[v]->ncb), kTileRows, 0, s>>>(T[v]->ptr, T[v]->nseg, T[v]->ncb,
-                                                                             T[v]->rows);
+                                                                             T[v]->slots);
         CSP_LAUNCHED("k_tile_rows");
     }
     L->tile_ptr_ready = false;

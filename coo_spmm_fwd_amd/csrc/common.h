@@ -113,7 +113,10 @@ constexpr int kTileRows = 512;
 
 struct Tiles {
     int32_t *ptr = nullptr;   // [nseg][ncb + 1]
-    int16_t *rows = nullptr;  // [nrb * ncb][kTileRows], tile = row block * ncb + column block
+    // [nrb * ncb][kTileRows], tile = row block * ncb + column block: per slot, in
+    // the order the tile kernels take them, {first entry of the segment in the
+    // tile, local segment << 16 | its entry count in the tile}
+    int2 *slots = nullptr;
     int64_t nseg = 0, nop = 0, ncb = 0, nrb = 0;
 };
 

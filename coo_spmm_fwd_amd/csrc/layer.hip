@@ -75,7 +75,7 @@ void free_layer(csp_layer *L)
                     L->col_tasks.desc, L->col_tasks.split, L->col_tasks.seg_first,
                     L->row_packed.desc, L->row_packed.split,
                     L->row_tasks.split_cls, L->col_tasks.split_cls, L->row_packed.split_cls,
-                    L->tiles_r.ptr, L->tiles_r.rows, L->tiles_c.ptr, L->tiles_c.rows, L->tile_partial};
+                    L->tiles_r.ptr, L->tiles_r.slots, L->tiles_c.ptr, L->tiles_c.slots, L->tile_partial};
     for (void *p : ptrs)
         if (p) (void)hipFree(p);
     delete L;
@@ -161,7 +161,8 @@ csp_status alloc_layer(csp_layer *L)
             T[v]->nrb = ceil_div(nseg[v], kTileRows);
             csp_status st = dalloc((void **)&T[v]->ptr, 4 * (size_t)nseg[v] * (size_t)(T[v]->ncb + 1), "tile offsets");
             if (st == CSP_OK)
-                st = dalloc((void **)&T[v]->rows, 2 * (size_t)(T[v]->nrb * T[v]->ncb) * kTileRows, "tile row order");
+                st = dalloc((void **)&T[v]->slots, sizeof(int2) * (size_t)(T[v]->nrb * T[v]->ncb) * kTileRows,
+                            "tile segment slots");
             if (st != CSP_OK) return st;
             const size_t p = sizeof(float) * kSliceRows * (size_t)T[v]->ncb * (size_t)nseg[v];
             partial = p > partial ? p : partial;

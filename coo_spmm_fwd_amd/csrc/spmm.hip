@@ -865,8 +865,7 @@ __device__ __forceinline__ float tile_reduce16(const float (&p)[16], int q)
     return keep + dpp_mov<0x128>(send);  // row_ror 8: lane xor 8 within the 16
 }
 
-__global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int32_t *__restrict__ tile_ptr,
-                                                                     const int16_t *__restrict__ tile_rows,
+__global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int2 *__restrict__ slots,
                                                                      int64_t ncb, const int32_t *__restrict__ cols,
                                                                      const float *__restrict__ XT,
                                                                      const float *__restrict__ dYT, int64_t in,
@@ -883,12 +882,10 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int32
     // lane l < 4G: row (group l / 4, slot l % 4) of the wave, and its entries in the tile
     int mybeg = 0, myend = 0, myrow = 0;
     if (lane < 4 * G) {
-        myrow = tile_rows[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
-        const int64_t r = r0 + myrow;
-        if (r < out) {
-            mybeg = tile_ptr[r * (ncb + 1) + cb];
-            myend = tile_ptr[r * (ncb + 1) + cb + 1];
-        }
+        const int2 sl = slots[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
+        myrow = sl.y >> 16;
+        mybeg = sl.x;
+        myend = sl.x + (sl.y & 0xFFFF);
     }
     const int64_t ncols = in - c0 < kTileCols ? in - c0 : kTileCols;
     const float4 *x4 = reinterpret_cast<const float4 *>(XT);
@@ -1000,8 +997,7 @@ __device__ __forceinline__ void tile_steps(const char *tab, int coff, float v, i
     __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
 }
 
-__global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int32_t *__restrict__ tile_ptr,
-                                                                      const int16_t *__restrict__ tile_rows,
+__global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int2 *__restrict__ slots,
                                                                       int64_t ncb, const int32_t *__restrict__ idx,
                                                                       const float *__restrict__ vals,
                                                                       const float *__restrict__ opT, int64_t n_op,
@@ -1016,12 +1012,10 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int3
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
     int mybeg = 0, myend = 0, myrow = 0;
     if (lane < 4 * G) {
-        myrow = tile_rows[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
-        const int64_t r = r0 + myrow;
-        if (r < n_seg) {
-            mybeg = tile_ptr[r * (ncb + 1) + cb];
-            myend = tile_ptr[r * (ncb + 1) + cb + 1];
-        }
+        const int2 sl = slots[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
+        myrow = sl.y >> 16;
+        mybeg = sl.x;
+        myend = sl.x + (sl.y & 0xFFFF);
     }
     const int64_t ncols = n_op - c0 < kTileCols ? n_op - c0 : kTileCols;
     const float4 *o4 = reinterpret_cast<const float4 *>(opT);
@@ -1668,8 +1662,8 @@ csp_status launch_value_tiles(csp_layer *L, int mark, const float *XT, const flo
                               hipStream_t s)
 {
     const Tiles &T = L->tiles_r;
-    launch_main(L, mark, k_values_tiles, dim3((unsigned)(T.nrb * T.ncb)), dim3(kTileWaves * kWave), 0u, s, T.ptr,
-                T.rows, T.ncb, L->cols, XT, dYT, L->in, L->out, dW, (int)acc);
+    launch_main(L, mark, k_values_tiles, dim3((unsigned)(T.nrb * T.ncb)), dim3(kTileWaves * kWave), 0u, s, T.slots,
+                T.ncb, L->cols, XT, dYT, L->in, L->out, dW, (int)acc);
     CSP_LAUNCHED("k_values_tiles");
     return CSP_OK;
 }
@@ -1691,7 +1685,7 @@ csp_status launch_segment_tiles(csp_layer *L, int mark, const Tiles &T, const in
                                 const float *opT, int64_t B, float *out, const Epi &ep, hipStream_t s)
 {
     launch_main(L, mark & kTimeStart, k_segment_tiles, dim3((unsigned)(T.nrb * T.ncb)), dim3(kTileWaves * kWave), 0u,
-                s, T.ptr, T.rows, T.ncb, idx, vals, opT, T.nop, T.nseg, L->tile_partial);
+                s, T.slots, T.ncb, idx, vals, opT, T.nop, T.nseg, L->tile_partial);
     CSP_LAUNCHED("k_segment_tiles");
     launch_main(L, mark & kTimeStop, k_tile_reduce<E>, dim3((unsigned)ceil_div(T.nseg, kReduceSegs)), dim3(256), 0u, s,
                 (const float *)L->tile_partial, T.ncb, T.nseg, B, out, ep);
