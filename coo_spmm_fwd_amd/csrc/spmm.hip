@@ -283,11 +283,14 @@ __device__ inline void block_fence()
 // takes one contiguous range of tasks keeps neighbouring segments -- whose
 // outputs share cache lines -- on one XCD, so each output line is written
 // back whole by one L2 instead of in pieces by several.
-__device__ __forceinline__ int64_t xcd_block()
+// Workgroup b of nb (both counted from a multiple of 8) to its place in the
+// XCD-contiguous order.
+__device__ __forceinline__ int64_t xcd_index(int64_t b, int64_t nb)
 {
-    const int64_t nb = gridDim.x, b = blockIdx.x, x = b & 7, per = nb >> 3, extra = nb & 7;
+    const int64_t x = b & 7, per = nb >> 3, extra = nb & 7;
     return x * per + (x < extra ? x : extra) + (b >> 3);
 }
+__device__ __forceinline__ int64_t xcd_block() { return xcd_index(blockIdx.x, gridDim.x); }
 
 // Waves per workgroup of the product kernels that run one task per wave
 // (k_segment_spmm, k_values_rows, k_gradients).
@@ -794,9 +797,9 @@ constexpr int kTilePF = 3;
 // The price is each operand block filled once per XCD that needs it (8 MiB of
 // fills rather than 2 at 8192 x 8192).
 constexpr int kTilePanel = 4;
-__device__ __forceinline__ void tile_of(int64_t ncb, int64_t nrb, int64_t &rb, int64_t &cb)
+__device__ __forceinline__ void tile_of(int64_t L, int64_t ncb, int64_t nrb, int64_t &rb, int64_t &cb)
 {
-    const int64_t L = xcd_block(), panel = L / (kTilePanel * ncb), within = L - panel * kTilePanel * ncb;
+    const int64_t panel = L / (kTilePanel * ncb), within = L - panel * kTilePanel * ncb;
     const int64_t rows = nrb - panel * kTilePanel < kTilePanel ? nrb - panel * kTilePanel : kTilePanel;
     cb = within / rows;
     rb = panel * kTilePanel + within % rows;
@@ -865,18 +868,19 @@ __device__ __forceinline__ float tile_reduce16(const float (&p)[16], int q)
     return keep + dpp_mov<0x128>(send);  // row_ror 8: lane xor 8 within the 16
 }
 
-__global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int2 *__restrict__ slots,
-                                                                     int64_t ncb, const int32_t *__restrict__ cols,
-                                                                     const float *__restrict__ XT,
-                                                                     const float *__restrict__ dYT, int64_t in,
-                                                                     int64_t out, float *__restrict__ dW, int acc)
+// The LDS table of a tile kernel's workgroup: the block's operand rows, then a
+// row of zeros (read by the segment sums' steps past a segment's entries).
+constexpr int kTileTab = (kTileCols + 1) * 16;
+
+// One workgroup's tile (rb, cb) of the value gradient; tab: kTileTab float4 of LDS.
+__device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4 *tab, const int2 *__restrict__ slots,
+                                                  int64_t ncb, const int32_t *__restrict__ cols,
+                                                  const float *__restrict__ XT, const float *__restrict__ dYT,
+                                                  int64_t in, int64_t out, float *__restrict__ dW, int acc)
 {
     constexpr int G = kTileRows / (4 * kTileWaves);  // groups of four rows per wave
     static_assert(4 * G <= kWave, "one lane per row of the wave");
     constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);  // 16-byte pieces per thread
-    __shared__ float4 tab[kTileCols * 16];
-    int64_t rb, cb;
-    tile_of(ncb, gridDim.x / ncb, rb, cb);
     const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
     // lane l < 4G: row (group l / 4, slot l % 4) of the wave, and its entries in the tile
@@ -955,6 +959,18 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int2 
     }
 }
 
+__global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int2 *__restrict__ slots,
+                                                                     int64_t ncb, const int32_t *__restrict__ cols,
+                                                                     const float *__restrict__ XT,
+                                                                     const float *__restrict__ dYT, int64_t in,
+                                                                     int64_t out, float *__restrict__ dW, int acc)
+{
+    __shared__ float4 tab[kTileTab];
+    int64_t rb, cb;
+    tile_of(xcd_block(), ncb, gridDim.x / ncb, rb, cb);
+    values_tiles_body(rb, cb, tab, slots, ncb, cols, XT, dYT, in, out, dW, acc);
+}
+
 // ------------------------------------------- segment sums, LDS tiles
 // fp32, batch chunks of width 64: the same tiles for the forward (row view:
 // segments are rows, entries their columns, operand X) and the input gradient
@@ -997,17 +1013,14 @@ __device__ __forceinline__ void tile_steps(const char *tab, int coff, float v, i
     __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
 }
 
-__global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int2 *__restrict__ slots,
-                                                                      int64_t ncb, const int32_t *__restrict__ idx,
-                                                                      const float *__restrict__ vals,
-                                                                      const float *__restrict__ opT, int64_t n_op,
-                                                                      int64_t n_seg, float *__restrict__ P)
+// One workgroup's tile (rb, cb) of a segment-sum pass; tab: kTileTab float4 of LDS.
+__device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float4 *tab, const int2 *__restrict__ slots,
+                                                   int64_t ncb, const int32_t *__restrict__ idx,
+                                                   const float *__restrict__ vals, const float *__restrict__ opT,
+                                                   int64_t n_op, int64_t n_seg, float *__restrict__ P)
 {
     constexpr int G = kTileRows / (4 * kTileWaves);
     constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);
-    __shared__ float4 tab[(kTileCols + 1) * 16];  // the block's operand rows, then a row of zeros
-    int64_t rb, cb;
-    tile_of(ncb, gridDim.x / ncb, rb, cb);
     const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
     int mybeg = 0, myend = 0, myrow = 0;
@@ -1090,6 +1103,45 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int2
             ci[j] = ni[j];
             cv[j] = nv[j];
         }
+    }
+}
+
+__global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int2 *__restrict__ slots,
+                                                                      int64_t ncb, const int32_t *__restrict__ idx,
+                                                                      const float *__restrict__ vals,
+                                                                      const float *__restrict__ opT, int64_t n_op,
+                                                                      int64_t n_seg, float *__restrict__ P)
+{
+    __shared__ float4 tab[kTileTab];
+    int64_t rb, cb;
+    tile_of(xcd_block(), ncb, gridDim.x / ncb, rb, cb);
+    segment_tiles_body(rb, cb, tab, slots, ncb, idx, vals, opT, n_op, n_seg, P);
+}
+
+// Both gradients' tile passes in one launch: workgroups [0, ndx) take the
+// input gradient's tiles (column view over dY, partial sums into P; ndx is
+// their count rounded up to a multiple of 8, the surplus workgroups exit),
+// the rest the value gradient's (row view).  A CU holds one tile workgroup
+// (128 KiB of LDS), so the value-gradient tiles start on each CU as soon as
+// its input-gradient tile is done, instead of after the slowest one and a
+// second launch.  The arithmetic is the two separate kernels'.
+__global__ __launch_bounds__(kTileWaves * kWave) void k_gradient_tiles(
+    int64_t ndx, const int2 *__restrict__ cslots, int64_t cncb, int64_t cnrb, const int32_t *__restrict__ rows_by_col,
+    const float *__restrict__ vals_c, const int2 *__restrict__ rslots, int64_t rncb, int64_t rnrb,
+    const int32_t *__restrict__ cols, const float *__restrict__ XT, const float *__restrict__ dYT, int64_t in,
+    int64_t out, float *__restrict__ P, float *__restrict__ dW, int acc)
+{
+    __shared__ float4 tab[kTileTab];
+    const int64_t b = blockIdx.x;
+    int64_t rb, cb;
+    if (b < ndx) {
+        const int64_t t = xcd_index(b, ndx);
+        if (t >= cnrb * cncb) return;  // rounding surplus
+        tile_of(t, cncb, cnrb, rb, cb);
+        segment_tiles_body(rb, cb, tab, cslots, cncb, rows_by_col, vals_c, dYT, out, in, P);
+    } else {
+        tile_of(xcd_index(b - ndx, (int64_t)gridDim.x - ndx), rncb, rnrb, rb, cb);
+        values_tiles_body(rb, cb, tab, rslots, rncb, cols, XT, dYT, in, out, dW, acc);
     }
 }
 
@@ -1693,6 +1745,31 @@ csp_status launch_segment_tiles(csp_layer *L, int mark, const Tiles &T, const in
     return CSP_OK;
 }
 
+// Both gradients' tiles in one launch (k_gradient_tiles), then the input
+// gradient's reduce.  The variable COOSPMM_FUSED_TILES=0 launches the two
+// tile kernels separately instead (a test hook; the results are the same bits).
+inline bool gradient_tiles_fused()
+{
+    const char *e = std::getenv("COOSPMM_FUSED_TILES");
+    return !(e && e[0] == '0');
+}
+
+template <int E>
+csp_status launch_gradient_tiles(csp_layer *L, const float *XT, const float *dYT, int64_t B, float *dX, float *dW,
+                                 bool acc, const Epi &ep, hipStream_t s)
+{
+    const Tiles &C = L->tiles_c, &R = L->tiles_r;
+    const int64_t ndx = ceil_div(C.nrb * C.ncb, 8) * 8;
+    launch_main(L, kTimeStart, k_gradient_tiles, dim3((unsigned)(ndx + R.nrb * R.ncb)), dim3(kTileWaves * kWave), 0u,
+                s, ndx, C.slots, C.ncb, C.nrb, L->rows_by_col, (const float *)L->vals_c, R.slots, R.ncb, R.nrb, L->cols,
+                XT, dYT, L->in, L->out, L->tile_partial, dW, (int)acc);
+    CSP_LAUNCHED("k_gradient_tiles");
+    launch_main(L, kTimeStop, k_tile_reduce<E>, dim3((unsigned)ceil_div(C.nseg, kReduceSegs)), dim3(256), 0u, s,
+                (const float *)L->tile_partial, C.ncb, C.nseg, B, dX, ep);
+    CSP_LAUNCHED("k_tile_reduce");
+    return CSP_OK;
+}
+
 template <class D>
 csp_status bwd_values_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B, float *dW, bool acc,
                                hipStream_t s)
@@ -1741,8 +1818,14 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         const unsigned gx = (unsigned)ceil_div(CT.count, kPW), gw = (unsigned)ceil_div(nrow, kPW);
         const int m1 = gw > 0 ? kTimeStart : kTimeBoth;  // the value-gradient kernel carries the end
         const bool ks = CT.nsplit == 0;
-        bool dx_tiled = false;
-        if constexpr (sizeof(T) == 4) dx_tiled = segment_tiles_usable(L, ld);
+        bool dx_tiled = false, dw_tiled = false;
+        if constexpr (sizeof(T) == 4) {
+            dx_tiled = segment_tiles_usable(L, ld);
+            dw_tiled = gw > 0 && value_tiles_usable(L, ld);
+            if (dx_tiled && dw_tiled && gradient_tiles_fused())
+                return launch_gradient_tiles<E>(L, (const float *)XT, (const float *)dYT, B, (float *)dX, dW, acc, ep,
+                                                 s);
+        }
         if (dx_tiled) {
             const csp_status st = launch_segment_tiles<E>(L, m1, L->tiles_c, L->rows_by_col, (const float *)L->vals_c,
                                                           (const float *)dYT, B, (float *)dX, ep, s);
@@ -1759,9 +1842,7 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
 #undef CSP_DX2_ARGS
         CSP_LAUNCHED("k_segment_spmm (input gradient)");
         }
-        bool tiled = false;
-        if constexpr (sizeof(T) == 4) tiled = gw > 0 && value_tiles_usable(L, ld);
-        if (tiled) {
+        if (dw_tiled) {
             const csp_status st = launch_value_tiles(L, kTimeStop, (const float *)XT, (const float *)dYT, dW, acc, s);
             if (st != CSP_OK) return st;
         } else if (gw > 0) {

@@ -87,6 +87,34 @@ def test_value_tiles_match_task_kernel(monkeypatch, B):
         csp.sparse_layer_destroy(h)
 
 
+@pytest.mark.parametrize("B", [64, 100])
+def test_gradient_tiles_one_launch_match_two(orc, monkeypatch, B):
+    """spmm_bwd on a tiled layer runs both gradients' tiles in one launch (the input gradient's
+    tiles first, their count rounded up to a multiple of 8 with idle workgroups: 17 x 17 = 289 here,
+    so 7 of them).  Its outputs must be the bits of the two separate launches, also with the GELU'
+    epilogue and over two batch chunks (the second accumulates dW), and dX must match the oracle."""
+    rows, cols, vals = tiled_layer(65)
+    h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
+    try:
+        X = dev(W.random_dense((B, IN), 66 + B))
+        dY = W.random_dense((B, OUT), 67 + B)
+        Hin = dev(W.random_dense((B, IN), 68 + B))
+        out = {}
+        for flag in ("0", "1"):
+            monkeypatch.setenv("COOSPMM_FUSED_TILES", flag)
+            dX, dW = csp.spmm_bwd(h, dev(dY), X)
+            dXa, dWa = csp.spmm_bwd_act(h, dev(dY), X, Hin, act="gelu")
+            torch.cuda.synchronize()
+            out[flag] = [host(t) for t in (dX, dW, dXa, dWa)]
+        for k, name in enumerate(("dX", "dW", "dX with GELU'", "dW beside it")):
+            assert np.array_equal(bits(out["0"][k]), bits(out["1"][k])), f"{name}: one launch differs from two"
+        refx, Sx = orc.spmm_bwd_input(OUT, IN, rows, cols, vals, dY)
+        assert_within(out["1"][0], refx, Sx, FP32_REL, f"input gradient of the one-launch tiles B={B}")
+        check_sample(h, dev(out["1"][1]), X, dev(dY), 69 + B)
+    finally:
+        csp.sparse_layer_destroy(h)
+
+
 def test_value_tiles_after_restructure(monkeypatch):
     rows, cols, vals = tiled_layer(67)
     h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
