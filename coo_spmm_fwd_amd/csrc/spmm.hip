@@ -785,6 +785,7 @@ __global__ __launch_bounds__(kPW * kWave) void k_values_rows(const int4 *__restr
 // they are equal across a quad or half), so the results are bitwise the same.
 constexpr int kTileWaves = 16;
 constexpr int kTilePF = 3;
+static_assert(kTilePF == 3, "the window selections below spell out three prefetched windows");
 
 // Tile (row block rb, column block cb) of a tile kernel's workgroup.  The
 // logical tile order runs in panels of kTilePanel row blocks, column block by
@@ -803,6 +804,33 @@ __device__ __forceinline__ void tile_of(int64_t L, int64_t ncb, int64_t nrb, int
     const int64_t rows = nrb - panel * kTilePanel < kTilePanel ? nrb - panel * kTilePanel : kTilePanel;
     cb = within / rows;
     rb = panel * kTilePanel + within % rows;
+}
+
+// Work of a tile workgroup: its kTileRows segments in groups of four, one
+// group per wave at a time (a 16-lane DPP row per segment).  The slots are
+// sorted by entry count, most first, and the groups go to the waves on
+// demand: wave w starts with group w, then takes the next group from an LDS
+// counter as it starts each one, so the longest groups run first and the
+// waves end together.  (With eight fixed groups per wave, the waves of a
+// tile ended up to ~4 us apart, and the workgroup waits for its last.)  The
+// sums do not depend on which wave adds a segment.
+// tile_groups_init copies the tile's slot records to LDS (shared by all
+// waves, read after the workgroup's barrier) and sets the counter; it returns
+// the record of the lane's segment in the wave's first group, read from
+// global memory so that its entries can load before the barrier.
+__device__ __forceinline__ int2 tile_groups_init(const int2 *__restrict__ tslots, int2 *lds, int *next, int wave, int g)
+{
+    if (threadIdx.x < kTileRows) lds[threadIdx.x] = tslots[threadIdx.x];
+    if (threadIdx.x == 0) *next = kTileWaves;
+    return tslots[4 * wave + g];
+}
+
+// The wave's next group (kTileRows / 4 or more: none left).
+__device__ __forceinline__ int tile_groups_next(int *next, int lane)
+{
+    int gn = 0;
+    if (lane == 0) gn = atomicAdd(next, 1);
+    return __builtin_amdgcn_readfirstlane(gn);
 }
 
 template <int T>
@@ -878,19 +906,13 @@ __device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4
                                                   const float *__restrict__ XT, const float *__restrict__ dYT,
                                                   int64_t in, int64_t out, float *__restrict__ dW, int acc)
 {
-    constexpr int G = kTileRows / (4 * kTileWaves);  // groups of four rows per wave
-    static_assert(4 * G <= kWave, "one lane per row of the wave");
     constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);  // 16-byte pieces per thread
     const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
-    // lane l < 4G: row (group l / 4, slot l % 4) of the wave, and its entries in the tile
-    int mybeg = 0, myend = 0, myrow = 0;
-    if (lane < 4 * G) {
-        const int2 sl = slots[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
-        myrow = sl.y >> 16;
-        mybeg = sl.x;
-        myend = sl.x + (sl.y & 0xFFFF);
-    }
+    // Groups of four rows on demand (tile_groups): this lane's row of the wave's first group.
+    __shared__ int2 vslot[kTileRows];
+    __shared__ int vnext;
+    const int2 first = tile_groups_init(slots + tile * kTileRows, vslot, &vnext, wave, g);
     const int64_t ncols = in - c0 < kTileCols ? in - c0 : kTileCols;
     const float4 *x4 = reinterpret_cast<const float4 *>(XT);
     float4 fl[FILL];
@@ -902,10 +924,10 @@ __device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4
     int cbeg, cn, nbeg = 0, nn = 0;
     int ci[kTilePF], ni[kTilePF] = {};
     float4 cdy, ndy = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto fetch = [&](int i, int &beg, int &n, int (&ii)[kTilePF], float4 &dy) {
-        beg = __shfl(mybeg, 4 * i + g);
-        n = __shfl(myend, 4 * i + g) - beg;
-        const int64_t r = r0 + __shfl(myrow, 4 * i + g);
+    auto fetch = [&](int2 sl, int &beg, int &n, int (&ii)[kTilePF], float4 &dy) {
+        beg = sl.x;
+        n = sl.y & 0xFFFF;
+        const int64_t r = r0 + (sl.y >> 16);
         dy = reinterpret_cast<const float4 *>(dYT)[(r < out ? r : 0) * 16 + q];
 #pragma unroll
         for (int j = 0; j < kTilePF; ++j) {
@@ -913,7 +935,7 @@ __device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4
             ii[j] = cols[e < n ? beg + e : 0];
         }
     };
-    fetch(0, cbeg, cn, ci, cdy);
+    fetch(first, cbeg, cn, ci, cdy);
 #pragma unroll
     for (int j = 0; j < FILL; ++j) {
         const int i = threadIdx.x + kTileWaves * kWave * j;
@@ -921,8 +943,10 @@ __device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4
     }
     __syncthreads();
     const char *base = reinterpret_cast<const char *>(tab);
-    for (int i = 0; i < G; ++i) {
-        if (i + 1 < G) fetch(i + 1, nbeg, nn, ni, ndy);
+    for (;;) {
+        const int gn = tile_groups_next(&vnext, lane);
+        const bool more = gn < kTileRows / 4;
+        if (more) fetch(vslot[4 * gn + g], nbeg, nn, ni, ndy);
         const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
                              max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
         const float dy[4] = {cdy.x, cdy.y, cdy.z, cdy.w};
@@ -951,11 +975,13 @@ __device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4
                 else dW[cbeg + e] += r;
             }
         }
+        if (!more) break;
         cbeg = nbeg;
         cn = nn;
         cdy = ndy;
-#pragma unroll
-        for (int j = 0; j < kTilePF; ++j) ci[j] = ni[j];
+        ci[0] = ni[0];  // kTilePF == 3 (static_assert at its definition)
+        ci[1] = ni[1];
+        ci[2] = ni[2];
     }
 }
 
@@ -1019,17 +1045,13 @@ __device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float
                                                    const float *__restrict__ vals, const float *__restrict__ opT,
                                                    int64_t n_op, int64_t n_seg, float *__restrict__ P)
 {
-    constexpr int G = kTileRows / (4 * kTileWaves);
     constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);
     const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
-    int mybeg = 0, myend = 0, myrow = 0;
-    if (lane < 4 * G) {
-        const int2 sl = slots[tile * kTileRows + 4 * kTileWaves * (lane >> 2) + 4 * wave + (lane & 3)];
-        myrow = sl.y >> 16;
-        mybeg = sl.x;
-        myend = sl.x + (sl.y & 0xFFFF);
-    }
+    // Groups of four segments on demand (tile_groups): this lane's segment of the wave's first group.
+    __shared__ int2 sslot[kTileRows];
+    __shared__ int snext;
+    const int2 first = tile_groups_init(slots + tile * kTileRows, sslot, &snext, wave, g);
     const int64_t ncols = n_op - c0 < kTileCols ? n_op - c0 : kTileCols;
     const float4 *o4 = reinterpret_cast<const float4 *>(opT);
     float4 fl[FILL];
@@ -1038,12 +1060,13 @@ __device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float
         const int i = threadIdx.x + kTileWaves * kWave * j, c = i >> 4;
         fl[j] = o4[(c0 + (c < ncols ? c : 0)) * 16 + (i & 15)];
     }
-    int cbeg, cn, nbeg = 0, nn = 0;
+    int cbeg, cn, crow, nbeg = 0, nn = 0, nrow = 0;
     int ci[kTilePF], ni[kTilePF] = {};
     float cv[kTilePF], nv[kTilePF] = {};
-    auto fetch = [&](int i, int &beg, int &n, int (&ii)[kTilePF], float (&vv)[kTilePF]) {
-        beg = __shfl(mybeg, 4 * i + g);
-        n = __shfl(myend, 4 * i + g) - beg;
+    auto fetch = [&](int2 sl, int &beg, int &n, int &row, int (&ii)[kTilePF], float (&vv)[kTilePF]) {
+        beg = sl.x;
+        n = sl.y & 0xFFFF;
+        row = sl.y >> 16;
 #pragma unroll
         for (int j = 0; j < kTilePF; ++j) {
             const int e = 16 * j + q;
@@ -1052,7 +1075,7 @@ __device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float
             vv[j] = vals[p];
         }
     };
-    fetch(0, cbeg, cn, ci, cv);
+    fetch(first, cbeg, cn, crow, ci, cv);
 #pragma unroll
     for (int j = 0; j < FILL; ++j) {
         const int i = threadIdx.x + kTileWaves * kWave * j;
@@ -1061,8 +1084,10 @@ __device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float
     if (threadIdx.x < 16) tab[kTileCols * 16 + threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
     __syncthreads();
     const char *base = reinterpret_cast<const char *>(tab);
-    for (int i = 0; i < G; ++i) {
-        if (i + 1 < G) fetch(i + 1, nbeg, nn, ni, nv);
+    for (;;) {
+        const int gn = tile_groups_next(&snext, lane);
+        const bool more = gn < kTileRows / 4;
+        if (more) fetch(sslot[4 * gn + g], nbeg, nn, nrow, ni, nv);
         const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
                              max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1093,16 +1118,15 @@ __device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float
             if (k + 12 >= nmax) continue;
             tile_steps<12>(base, coff, vv, q16, acc);
         }
-        const int64_t r = r0 + __shfl(myrow, 4 * i + g);
+        const int64_t r = r0 + crow;
         if (r < n_seg)
             reinterpret_cast<float4 *>(P)[(cb * n_seg + r) * 16 + q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        if (!more) break;
         cbeg = nbeg;
         cn = nn;
-#pragma unroll
-        for (int j = 0; j < kTilePF; ++j) {
-            ci[j] = ni[j];
-            cv[j] = nv[j];
-        }
+        crow = nrow;
+        ci[0] = ni[0], ci[1] = ni[1], ci[2] = ni[2];
+        cv[0] = nv[0], cv[1] = nv[1], cv[2] = nv[2];
     }
 }
 
