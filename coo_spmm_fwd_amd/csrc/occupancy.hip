@@ -341,21 +341,34 @@ __global__ __launch_bounds__(kThreads) void k_bm_occ_prune(const uint32_t *__res
                                                            const uint64_t *__restrict__ pruned,
                                                            uint32_t *__restrict__ occ_next)
 {
-    const int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (w >= nw) return;
-    const uint32_t o = occ[w], k0 = pref[w];
-    uint32_t keep = o;
-    if (o) {
-        // the word's entries k0 .. k0 + popc - 1 span at most two mask words
-        const uint32_t k1 = k0 + (uint32_t)__popc(o) - 1u;
-        const uint64_t lo = pruned[k0 >> 6], hi = pruned[k1 >> 6];
-        uint32_t k = k0;
-        for (uint32_t m = o; m; m &= m - 1, ++k) {
-            const uint64_t pw = (k >> 6) == (k0 >> 6) ? lo : hi;
-            if ((pw >> (k & 63)) & 1ull) keep &= ~(m & (0u - m));
+    // Four consecutive words per thread (nw is a multiple of 8): 16-byte loads
+    // and store, and one round of dependent loads for the whole bitmap.
+    const int64_t w4 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (4 * w4 >= nw) return;
+    const uint4 o4 = reinterpret_cast<const uint4 *>(occ)[w4], k4 = reinterpret_cast<const uint4 *>(pref)[w4];
+    const uint32_t o[4] = {o4.x, o4.y, o4.z, o4.w}, k0[4] = {k4.x, k4.y, k4.z, k4.w};
+    const uint32_t n = (uint32_t)(__popc(o4.x) + __popc(o4.y) + __popc(o4.z) + __popc(o4.w));
+    // the words' entries k4.x .. k4.x + n - 1 (n <= 128) span at most three mask words
+    const uint32_t base = k4.x >> 6;
+    uint64_t m[3] = {0, 0, 0};
+    if (n) {
+        const uint32_t last = (k4.x + n - 1u) >> 6;
+        m[0] = pruned[base];
+        m[1] = pruned[base + 1 < last ? base + 1 : last];
+        m[2] = pruned[last];
+    }
+    uint32_t keep[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        keep[i] = o[i];
+        uint32_t k = k0[i];
+        for (uint32_t b = o[i]; b; b &= b - 1, ++k) {
+            const uint32_t d = (k >> 6) - base;  // 0, 1 or 2
+            const uint64_t pw = d == 0 ? m[0] : (d == 1 ? m[1] : m[2]);
+            if ((pw >> (k & 63)) & 1ull) keep[i] &= ~(b & (0u - b));
         }
     }
-    occ_next[w] = keep;
+    reinterpret_cast<uint4 *>(occ_next)[w4] = make_uint4(keep[0], keep[1], keep[2], keep[3]);
 }
 
 // --------------------------------------------------------------------- regrow
@@ -986,7 +999,7 @@ struct BitmapRun {
         csp_status st = select(MagKeys<V>{(const V *)L->vals}, L->nnz, n_prune, passes, top, (uint64_t *)W.acc_b,
                                clear, nclear);
         if (st != CSP_OK) return st;
-        k_bm_occ_prune<<<blocks_for(W.occ_words, kThreads), kThreads, 0, s>>>(W.occ, W.occ_pref, W.occ_words,
+        k_bm_occ_prune<<<blocks_for(W.occ_words / 4, kThreads), kThreads, 0, s>>>(W.occ, W.occ_pref, W.occ_words,
                                                                               (const uint64_t *)W.acc_b, W.occ_next);
         CSP_LAUNCHED("k_bm_occ_prune");
         return CSP_OK;
