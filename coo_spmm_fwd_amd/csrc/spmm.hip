@@ -900,31 +900,27 @@ __device__ __forceinline__ float tile_reduce16(const float (&p)[16], int q)
 // row of zeros (read by the segment sums' steps past a segment's entries).
 constexpr int kTileTab = (kTileCols + 1) * 16;
 
-// One workgroup's tile (rb, cb) of the value gradient; tab: kTileTab float4 of LDS.
-__device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4 *tab, const int2 *__restrict__ slots,
-                                                  int64_t ncb, const int32_t *__restrict__ cols,
-                                                  const float *__restrict__ XT, const float *__restrict__ dYT,
-                                                  int64_t in, int64_t out, float *__restrict__ dW, int acc)
-{
-    constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);  // 16-byte pieces per thread
-    const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
-    // Groups of four rows on demand (tile_groups): this lane's row of the wave's first group.
-    __shared__ int2 vslot[kTileRows];
-    __shared__ int vnext;
-    const int2 first = tile_groups_init(slots + tile * kTileRows, vslot, &vnext, wave, g);
-    const int64_t ncols = in - c0 < kTileCols ? in - c0 : kTileCols;
-    const float4 *x4 = reinterpret_cast<const float4 *>(XT);
+// One workgroup's tile (rb, cb) of the value gradient, in three phases:
+// start (slot records to LDS, the operand fill's loads and the wave's first
+// group's loads put in flight), fill (the operand rows to LDS; the caller then
+// syncs the workgroup) and run (the groups on demand).  A caller may run
+// other work between start and fill: the loads stay in flight.
+struct ValuesTile {
+    static constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);  // 16-byte pieces per thread
+    const int32_t *cols;
+    const float *dYT;
+    float *dW;
+    int64_t out, c0, r0, ncols;
+    int acc, lane, q, g, q16;
+    int2 *lslot;
+    int *next;
     float4 fl[FILL];
-#pragma unroll
-    for (int j = 0; j < FILL; ++j) {  // every fill load in flight before the first LDS store
-        const int i = threadIdx.x + kTileWaves * kWave * j, c = i >> 4;
-        fl[j] = x4[(c0 + (c < ncols ? c : 0)) * 16 + (i & 15)];
-    }
-    int cbeg, cn, nbeg = 0, nn = 0;
-    int ci[kTilePF], ni[kTilePF] = {};
-    float4 cdy, ndy = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto fetch = [&](int2 sl, int &beg, int &n, int (&ii)[kTilePF], float4 &dy) {
+    int cbeg, cn;
+    int ci[kTilePF];
+    float4 cdy;
+
+    __device__ __forceinline__ void fetch(int2 sl, int &beg, int &n, int (&ii)[kTilePF], float4 &dy) const
+    {
         beg = sl.x;
         n = sl.y & 0xFFFF;
         const int64_t r = r0 + (sl.y >> 16);
@@ -934,56 +930,87 @@ __device__ __forceinline__ void values_tiles_body(int64_t rb, int64_t cb, float4
             const int e = 16 * j + q;
             ii[j] = cols[e < n ? beg + e : 0];
         }
-    };
-    fetch(first, cbeg, cn, ci, cdy);
+    }
+
+    __device__ __forceinline__ void start(int64_t rb, int64_t cb, const int2 *__restrict__ slots, int64_t ncb,
+                                          const int32_t *__restrict__ cols_, const float *__restrict__ XT,
+                                          const float *__restrict__ dYT_, int64_t in, int64_t out_,
+                                          float *__restrict__ dW_, int acc_, int2 *lslot_, int *next_)
+    {
+        cols = cols_, dYT = dYT_, dW = dW_, out = out_, acc = acc_, lslot = lslot_, next = next_;
+        const int64_t tile = rb * ncb + cb;
+        c0 = cb * kTileCols, r0 = rb * kTileRows;
+        const int wave = threadIdx.x >> 6;
+        lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
+        // Groups of four rows on demand (tile_groups): this lane's row of the wave's first group.
+        const int2 first = tile_groups_init(slots + tile * kTileRows, lslot, next, wave, g);
+        ncols = in - c0 < kTileCols ? in - c0 : kTileCols;
+        const float4 *x4 = reinterpret_cast<const float4 *>(XT);
 #pragma unroll
-    for (int j = 0; j < FILL; ++j) {
-        const int i = threadIdx.x + kTileWaves * kWave * j;
-        tab[i] = (i >> 4) < ncols ? fl[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    __syncthreads();
-    const char *base = reinterpret_cast<const char *>(tab);
-    for (;;) {
-        const int gn = tile_groups_next(&vnext, lane);
-        const bool more = gn < kTileRows / 4;
-        if (more) fetch(vslot[4 * gn + g], nbeg, nn, ni, ndy);
-        const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
-                             max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
-        const float dy[4] = {cdy.x, cdy.y, cdy.z, cdy.w};
-        for (int k = 0; k < nmax; k += 16) {
-            const int e = k + q;
-            int c;
-            if (k < 16 * kTilePF) {
-                const int j = k >> 4;
-                c = j == 0 ? ci[0] : (j == 1 ? ci[1] : ci[2]);
-            } else {  // a row with more than 16 * kTilePF entries in the tile
-                c = cols[e < cn ? cbeg + e : 0];
-            }
-            const uint32_t rel = (uint32_t)((int64_t)c - c0);
-            const int coff = e < cn && rel < (uint32_t)kTileCols ? (int)rel * 256 : 0;
-            float p[16];
-            tile_dots<0>(base, coff, q16, dy, p);
-            if (k + 4 < nmax) tile_dots<4>(base, coff, q16, dy, p);
-            else p[4] = p[5] = p[6] = p[7] = 0.f;
-            if (k + 8 < nmax) tile_dots<8>(base, coff, q16, dy, p);
-            else p[8] = p[9] = p[10] = p[11] = 0.f;
-            if (k + 12 < nmax) tile_dots<12>(base, coff, q16, dy, p);
-            else p[12] = p[13] = p[14] = p[15] = 0.f;
-            const float r = tile_reduce16(p, q);
-            if (e < cn) {
-                if (!acc) dW[cbeg + e] = r;
-                else dW[cbeg + e] += r;
-            }
+        for (int j = 0; j < FILL; ++j) {  // every fill load in flight before the first LDS store
+            const int i = threadIdx.x + kTileWaves * kWave * j, c = i >> 4;
+            fl[j] = x4[(c0 + (c < ncols ? c : 0)) * 16 + (i & 15)];
         }
-        if (!more) break;
-        cbeg = nbeg;
-        cn = nn;
-        cdy = ndy;
-        ci[0] = ni[0];  // kTilePF == 3 (static_assert at its definition)
-        ci[1] = ni[1];
-        ci[2] = ni[2];
+        fetch(first, cbeg, cn, ci, cdy);
     }
-}
+
+    __device__ __forceinline__ void fill(float4 *tab) const
+    {
+#pragma unroll
+        for (int j = 0; j < FILL; ++j) {
+            const int i = threadIdx.x + kTileWaves * kWave * j;
+            tab[i] = (i >> 4) < ncols ? fl[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+
+    __device__ __forceinline__ void run(const float4 *tab)
+    {
+        const char *base = reinterpret_cast<const char *>(tab);
+        int nbeg = 0, nn = 0;
+        int ni[kTilePF] = {};
+        float4 ndy = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (;;) {
+            const int gn = tile_groups_next(next, lane);
+            const bool more = gn < kTileRows / 4;
+            if (more) fetch(lslot[4 * gn + g], nbeg, nn, ni, ndy);
+            const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
+                                 max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
+            const float dy[4] = {cdy.x, cdy.y, cdy.z, cdy.w};
+            for (int k = 0; k < nmax; k += 16) {
+                const int e = k + q;
+                int c;
+                if (k < 16 * kTilePF) {
+                    const int j = k >> 4;
+                    c = j == 0 ? ci[0] : (j == 1 ? ci[1] : ci[2]);
+                } else {  // a row with more than 16 * kTilePF entries in the tile
+                    c = cols[e < cn ? cbeg + e : 0];
+                }
+                const uint32_t rel = (uint32_t)((int64_t)c - c0);
+                const int coff = e < cn && rel < (uint32_t)kTileCols ? (int)rel * 256 : 0;
+                float p[16];
+                tile_dots<0>(base, coff, q16, dy, p);
+                if (k + 4 < nmax) tile_dots<4>(base, coff, q16, dy, p);
+                else p[4] = p[5] = p[6] = p[7] = 0.f;
+                if (k + 8 < nmax) tile_dots<8>(base, coff, q16, dy, p);
+                else p[8] = p[9] = p[10] = p[11] = 0.f;
+                if (k + 12 < nmax) tile_dots<12>(base, coff, q16, dy, p);
+                else p[12] = p[13] = p[14] = p[15] = 0.f;
+                const float r = tile_reduce16(p, q);
+                if (e < cn) {
+                    if (!acc) dW[cbeg + e] = r;
+                    else dW[cbeg + e] += r;
+                }
+            }
+            if (!more) break;
+            cbeg = nbeg;
+            cn = nn;
+            cdy = ndy;
+            ci[0] = ni[0];  // kTilePF == 3 (static_assert at its definition)
+            ci[1] = ni[1];
+            ci[2] = ni[2];
+        }
+    }
+};
 
 __global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int2 *__restrict__ slots,
                                                                      int64_t ncb, const int32_t *__restrict__ cols,
@@ -992,9 +1019,15 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_values_tiles(const int2 
                                                                      int64_t out, float *__restrict__ dW, int acc)
 {
     __shared__ float4 tab[kTileTab];
+    __shared__ int2 lslot[kTileRows];
+    __shared__ int next;
     int64_t rb, cb;
     tile_of(xcd_block(), ncb, gridDim.x / ncb, rb, cb);
-    values_tiles_body(rb, cb, tab, slots, ncb, cols, XT, dYT, in, out, dW, acc);
+    ValuesTile V;
+    V.start(rb, cb, slots, ncb, cols, XT, dYT, in, out, dW, acc, lslot, &next);
+    V.fill(tab);
+    __syncthreads();
+    V.run(tab);
 }
 
 // ------------------------------------------- segment sums, LDS tiles
@@ -1039,31 +1072,25 @@ __device__ __forceinline__ void tile_steps(const char *tab, int coff, float v, i
     __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
 }
 
-// One workgroup's tile (rb, cb) of a segment-sum pass; tab: kTileTab float4 of LDS.
-__device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float4 *tab, const int2 *__restrict__ slots,
-                                                   int64_t ncb, const int32_t *__restrict__ idx,
-                                                   const float *__restrict__ vals, const float *__restrict__ opT,
-                                                   int64_t n_op, int64_t n_seg, float *__restrict__ P)
-{
-    constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);
-    const int64_t tile = rb * ncb + cb, c0 = cb * kTileCols, r0 = rb * kTileRows;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
-    // Groups of four segments on demand (tile_groups): this lane's segment of the wave's first group.
-    __shared__ int2 sslot[kTileRows];
-    __shared__ int snext;
-    const int2 first = tile_groups_init(slots + tile * kTileRows, sslot, &snext, wave, g);
-    const int64_t ncols = n_op - c0 < kTileCols ? n_op - c0 : kTileCols;
-    const float4 *o4 = reinterpret_cast<const float4 *>(opT);
+// One workgroup's tile (rb, cb) of a segment-sum pass, in the phases of
+// ValuesTile (start, fill, run); fill also writes the zero row.
+struct SegmentTile {
+    static constexpr int FILL = kTileCols * 16 / (kTileWaves * kWave);
+    const int32_t *idx;
+    const float *vals;
+    float *P;
+    int64_t cb, n_seg, c0, r0, ncols;
+    int lane, q, g, q16;
+    int2 *lslot;
+    int *next;
     float4 fl[FILL];
-#pragma unroll
-    for (int j = 0; j < FILL; ++j) {
-        const int i = threadIdx.x + kTileWaves * kWave * j, c = i >> 4;
-        fl[j] = o4[(c0 + (c < ncols ? c : 0)) * 16 + (i & 15)];
-    }
-    int cbeg, cn, crow, nbeg = 0, nn = 0, nrow = 0;
-    int ci[kTilePF], ni[kTilePF] = {};
-    float cv[kTilePF], nv[kTilePF] = {};
-    auto fetch = [&](int2 sl, int &beg, int &n, int &row, int (&ii)[kTilePF], float (&vv)[kTilePF]) {
+    int cbeg, cn, crow;
+    int ci[kTilePF];
+    float cv[kTilePF];
+
+    __device__ __forceinline__ void fetch(int2 sl, int &beg, int &n, int &row, int (&ii)[kTilePF],
+                                          float (&vv)[kTilePF]) const
+    {
         beg = sl.x;
         n = sl.y & 0xFFFF;
         row = sl.y >> 16;
@@ -1074,61 +1101,92 @@ __device__ __forceinline__ void segment_tiles_body(int64_t rb, int64_t cb, float
             ii[j] = idx[p];
             vv[j] = vals[p];
         }
-    };
-    fetch(first, cbeg, cn, crow, ci, cv);
+    }
+
+    __device__ __forceinline__ void start(int64_t rb, int64_t cb_, const int2 *__restrict__ slots, int64_t ncb,
+                                          const int32_t *__restrict__ idx_, const float *__restrict__ vals_,
+                                          const float *__restrict__ opT, int64_t n_op, int64_t n_seg_,
+                                          float *__restrict__ P_, int2 *lslot_, int *next_)
+    {
+        idx = idx_, vals = vals_, P = P_, cb = cb_, n_seg = n_seg_, lslot = lslot_, next = next_;
+        const int64_t tile = rb * ncb + cb;
+        c0 = cb * kTileCols, r0 = rb * kTileRows;
+        const int wave = threadIdx.x >> 6;
+        lane = threadIdx.x & 63, q = lane & 15, g = lane >> 4, q16 = q * 16;
+        // Groups of four segments on demand (tile_groups): this lane's segment of the wave's first group.
+        const int2 first = tile_groups_init(slots + tile * kTileRows, lslot, next, wave, g);
+        ncols = n_op - c0 < kTileCols ? n_op - c0 : kTileCols;
+        const float4 *o4 = reinterpret_cast<const float4 *>(opT);
 #pragma unroll
-    for (int j = 0; j < FILL; ++j) {
-        const int i = threadIdx.x + kTileWaves * kWave * j;
-        tab[i] = (i >> 4) < ncols ? fl[j] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (threadIdx.x < 16) tab[kTileCols * 16 + threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
-    __syncthreads();
-    const char *base = reinterpret_cast<const char *>(tab);
-    for (;;) {
-        const int gn = tile_groups_next(&snext, lane);
-        const bool more = gn < kTileRows / 4;
-        if (more) fetch(sslot[4 * gn + g], nbeg, nn, nrow, ni, nv);
-        const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
-                             max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < nmax; k += 16) {
-            const int e = k + q;
-            int c;
-            float v;
-            if (k < 16 * kTilePF) {
-                const int j = k >> 4;
-                c = j == 0 ? ci[0] : (j == 1 ? ci[1] : ci[2]);
-                v = j == 0 ? cv[0] : (j == 1 ? cv[1] : cv[2]);
-            } else {  // a segment with more than 16 * kTilePF entries in the tile
-                const int p = e < cn ? cbeg + e : 0;
-                c = idx[p];
-                v = vals[p];
-            }
-            const uint32_t rel = (uint32_t)((int64_t)c - c0);
-            const bool ok = e < cn && rel < (uint32_t)kTileCols;
-            // steps past the segment's entries read the zero row (an inf or NaN in
-            // the block's first row must not reach the sum through a zero weight)
-            const int coff = ok ? (int)rel * 256 : kTileCols * 256;
-            const float vv = ok ? v : 0.f;
-            tile_steps<0>(base, coff, vv, q16, acc);
-            if (k + 4 >= nmax) continue;
-            tile_steps<4>(base, coff, vv, q16, acc);
-            if (k + 8 >= nmax) continue;
-            tile_steps<8>(base, coff, vv, q16, acc);
-            if (k + 12 >= nmax) continue;
-            tile_steps<12>(base, coff, vv, q16, acc);
+        for (int j = 0; j < FILL; ++j) {
+            const int i = threadIdx.x + kTileWaves * kWave * j, c = i >> 4;
+            fl[j] = o4[(c0 + (c < ncols ? c : 0)) * 16 + (i & 15)];
         }
-        const int64_t r = r0 + crow;
-        if (r < n_seg)
-            reinterpret_cast<float4 *>(P)[(cb * n_seg + r) * 16 + q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        if (!more) break;
-        cbeg = nbeg;
-        cn = nn;
-        crow = nrow;
-        ci[0] = ni[0], ci[1] = ni[1], ci[2] = ni[2];
-        cv[0] = nv[0], cv[1] = nv[1], cv[2] = nv[2];
+        fetch(first, cbeg, cn, crow, ci, cv);
     }
-}
+
+    __device__ __forceinline__ void fill(float4 *tab) const
+    {
+#pragma unroll
+        for (int j = 0; j < FILL; ++j) {
+            const int i = threadIdx.x + kTileWaves * kWave * j;
+            tab[i] = (i >> 4) < ncols ? fl[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if (threadIdx.x < 16) tab[kTileCols * 16 + threadIdx.x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    __device__ __forceinline__ void run(const float4 *tab)
+    {
+        const char *base = reinterpret_cast<const char *>(tab);
+        int nbeg = 0, nn = 0, nrow = 0;
+        int ni[kTilePF] = {};
+        float nv[kTilePF] = {};
+        for (;;) {
+            const int gn = tile_groups_next(next, lane);
+            const bool more = gn < kTileRows / 4;
+            if (more) fetch(lslot[4 * gn + g], nbeg, nn, nrow, ni, nv);
+            const int nmax = max(max(__builtin_amdgcn_readlane(cn, 0), __builtin_amdgcn_readlane(cn, 16)),
+                                 max(__builtin_amdgcn_readlane(cn, 32), __builtin_amdgcn_readlane(cn, 48)));
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < nmax; k += 16) {
+                const int e = k + q;
+                int c;
+                float v;
+                if (k < 16 * kTilePF) {
+                    const int j = k >> 4;
+                    c = j == 0 ? ci[0] : (j == 1 ? ci[1] : ci[2]);
+                    v = j == 0 ? cv[0] : (j == 1 ? cv[1] : cv[2]);
+                } else {  // a segment with more than 16 * kTilePF entries in the tile
+                    const int p = e < cn ? cbeg + e : 0;
+                    c = idx[p];
+                    v = vals[p];
+                }
+                const uint32_t rel = (uint32_t)((int64_t)c - c0);
+                const bool ok = e < cn && rel < (uint32_t)kTileCols;
+                // steps past the segment's entries read the zero row (an inf or NaN in
+                // the block's first row must not reach the sum through a zero weight)
+                const int coff = ok ? (int)rel * 256 : kTileCols * 256;
+                const float vv = ok ? v : 0.f;
+                tile_steps<0>(base, coff, vv, q16, acc);
+                if (k + 4 >= nmax) continue;
+                tile_steps<4>(base, coff, vv, q16, acc);
+                if (k + 8 >= nmax) continue;
+                tile_steps<8>(base, coff, vv, q16, acc);
+                if (k + 12 >= nmax) continue;
+                tile_steps<12>(base, coff, vv, q16, acc);
+            }
+            const int64_t r = r0 + crow;
+            if (r < n_seg)
+                reinterpret_cast<float4 *>(P)[(cb * n_seg + r) * 16 + q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            if (!more) break;
+            cbeg = nbeg;
+            cn = nn;
+            crow = nrow;
+            ci[0] = ni[0], ci[1] = ni[1], ci[2] = ni[2];
+            cv[0] = nv[0], cv[1] = nv[1], cv[2] = nv[2];
+        }
+    }
+};
 
 __global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int2 *__restrict__ slots,
                                                                       int64_t ncb, const int32_t *__restrict__ idx,
@@ -1137,36 +1195,49 @@ __global__ __launch_bounds__(kTileWaves * kWave) void k_segment_tiles(const int2
                                                                       int64_t n_seg, float *__restrict__ P)
 {
     __shared__ float4 tab[kTileTab];
+    __shared__ int2 lslot[kTileRows];
+    __shared__ int next;
     int64_t rb, cb;
     tile_of(xcd_block(), ncb, gridDim.x / ncb, rb, cb);
-    segment_tiles_body(rb, cb, tab, slots, ncb, idx, vals, opT, n_op, n_seg, P);
+    SegmentTile S;
+    S.start(rb, cb, slots, ncb, idx, vals, opT, n_op, n_seg, P, lslot, &next);
+    S.fill(tab);
+    __syncthreads();
+    S.run(tab);
 }
 
-// Both gradients' tile passes in one launch: workgroups [0, ndx) take the
-// input gradient's tiles (column view over dY, partial sums into P; ndx is
-// their count rounded up to a multiple of 8, the surplus workgroups exit),
-// the rest the value gradient's (row view).  A CU holds one tile workgroup
-// (128 KiB of LDS), so the value-gradient tiles start on each CU as soon as
-// its input-gradient tile is done, instead of after the slowest one and a
-// second launch.  The arithmetic is the two separate kernels'.
+// Both gradients' tile passes in one launch, one tile of each per workgroup
+// (the two views have the same number of tiles): the input gradient's tile
+// (column view over dY, partial sums into P), then the value gradient's (row
+// view).  The value-gradient tile's start -- its slot records, operand fill
+// and first groups' loads -- is issued before the input-gradient tile runs,
+// so its loads arrive meanwhile instead of after it; the workgroup then
+// fills the LDS table again and runs it.  The arithmetic is the two
+// separate kernels'.
 __global__ __launch_bounds__(kTileWaves * kWave) void k_gradient_tiles(
-    int64_t ndx, const int2 *__restrict__ cslots, int64_t cncb, int64_t cnrb, const int32_t *__restrict__ rows_by_col,
+    const int2 *__restrict__ cslots, int64_t cncb, int64_t cnrb, const int32_t *__restrict__ rows_by_col,
     const float *__restrict__ vals_c, const int2 *__restrict__ rslots, int64_t rncb, int64_t rnrb,
     const int32_t *__restrict__ cols, const float *__restrict__ XT, const float *__restrict__ dYT, int64_t in,
     int64_t out, float *__restrict__ P, float *__restrict__ dW, int acc)
 {
     __shared__ float4 tab[kTileTab];
-    const int64_t b = blockIdx.x;
+    __shared__ int2 sslot[kTileRows], vslot[kTileRows];
+    __shared__ int snext, vnext;
+    const int64_t t = xcd_block();
     int64_t rb, cb;
-    if (b < ndx) {
-        const int64_t t = xcd_index(b, ndx);
-        if (t >= cnrb * cncb) return;  // rounding surplus
-        tile_of(t, cncb, cnrb, rb, cb);
-        segment_tiles_body(rb, cb, tab, cslots, cncb, rows_by_col, vals_c, dYT, out, in, P);
-    } else {
-        tile_of(xcd_index(b - ndx, (int64_t)gridDim.x - ndx), rncb, rnrb, rb, cb);
-        values_tiles_body(rb, cb, tab, rslots, rncb, cols, XT, dYT, in, out, dW, acc);
-    }
+    SegmentTile S;
+    tile_of(t, cncb, cnrb, rb, cb);
+    S.start(rb, cb, cslots, cncb, rows_by_col, vals_c, dYT, out, in, P, sslot, &snext);
+    ValuesTile V;
+    tile_of(t, rncb, rnrb, rb, cb);
+    V.start(rb, cb, rslots, rncb, cols, XT, dYT, in, out, dW, acc, vslot, &vnext);
+    S.fill(tab);
+    __syncthreads();
+    S.run(tab);
+    __syncthreads();  // every wave is done with the input gradient's table
+    V.fill(tab);
+    __syncthreads();
+    V.run(tab);
 }
 
 // out[b, seg] = epilogue(sum over column blocks cb, in order, of P[cb][seg][b]).
@@ -1783,10 +1854,9 @@ csp_status launch_gradient_tiles(csp_layer *L, const float *XT, const float *dYT
                                  bool acc, const Epi &ep, hipStream_t s)
 {
     const Tiles &C = L->tiles_c, &R = L->tiles_r;
-    const int64_t ndx = ceil_div(C.nrb * C.ncb, 8) * 8;
-    launch_main(L, kTimeStart, k_gradient_tiles, dim3((unsigned)(ndx + R.nrb * R.ncb)), dim3(kTileWaves * kWave), 0u,
-                s, ndx, C.slots, C.ncb, C.nrb, L->rows_by_col, (const float *)L->vals_c, R.slots, R.ncb, R.nrb, L->cols,
-                XT, dYT, L->in, L->out, L->tile_partial, dW, (int)acc);
+    launch_main(L, kTimeStart, k_gradient_tiles, dim3((unsigned)(C.nrb * C.ncb)), dim3(kTileWaves * kWave), 0u, s,
+                C.slots, C.ncb, C.nrb, L->rows_by_col, (const float *)L->vals_c, R.slots, R.ncb, R.nrb, L->cols, XT,
+                dYT, L->in, L->out, L->tile_partial, dW, (int)acc);
     CSP_LAUNCHED("k_gradient_tiles");
     launch_main(L, kTimeStop, k_tile_reduce<E>, dim3((unsigned)ceil_div(C.nseg, kReduceSegs)), dim3(256), 0u, s,
                 (const float *)L->tile_partial, C.ncb, C.nseg, B, dX, ep);
@@ -1846,7 +1916,8 @@ csp_status bwd_dispatch(csp_layer *L, const void *XT, const void *dYT, int64_t B
         if constexpr (sizeof(T) == 4) {
             dx_tiled = segment_tiles_usable(L, ld);
             dw_tiled = gw > 0 && value_tiles_usable(L, ld);
-            if (dx_tiled && dw_tiled && gradient_tiles_fused())
+            if (dx_tiled && dw_tiled && gradient_tiles_fused() &&
+                L->tiles_c.nrb * L->tiles_c.ncb == L->tiles_r.nrb * L->tiles_r.ncb)
                 return launch_gradient_tiles<E>(L, (const float *)XT, (const float *)dYT, B, (float *)dX, dW, acc, ep,
                                                  s);
         }
