@@ -89,10 +89,10 @@ def test_value_tiles_match_task_kernel(monkeypatch, B):
 
 @pytest.mark.parametrize("B", [64, 100])
 def test_gradient_tiles_one_launch_match_two(orc, monkeypatch, B):
-    """spmm_bwd on a tiled layer runs both gradients' tiles in one launch (the input gradient's
-    tiles first, their count rounded up to a multiple of 8 with idle workgroups: 17 x 17 = 289 here,
-    so 7 of them).  Its outputs must be the bits of the two separate launches, also with the GELU'
-    epilogue and over two batch chunks (the second accumulates dW), and dX must match the oracle."""
+    """spmm_bwd on a tiled layer runs both gradients' tile passes in one launch, one tile of each
+    view per workgroup (17 x 17 = 289 of each here, partial ones at the edges).  Its outputs must be
+    the bits of the two separate launches, also with the GELU' epilogue and over two batch chunks
+    (the second accumulates dW), and dX must match the oracle."""
     rows, cols, vals = tiled_layer(65)
     h = csp.sparse_layer_create(OUT, IN, dev(rows), dev(cols), dev(vals))
     try:
