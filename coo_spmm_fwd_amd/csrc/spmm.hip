@@ -1175,15 +1175,22 @@ struct SegmentTile {
                 if (k + 12 >= nmax) continue;
                 tile_steps<12>(base, coff, vv, q16, acc);
             }
+            // The next group's prefetched loads are taken over before this
+            // group's store is issued: stores count in the same in-order
+            // memory counter as loads, so taking them over after the store
+            // would wait for the store's completion at every group.
             const int64_t r = r0 + crow;
-            if (r < n_seg)
-                reinterpret_cast<float4 *>(P)[(cb * n_seg + r) * 16 + q] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            const float4 res = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            if (more) {
+                cbeg = nbeg;
+                cn = nn;
+                crow = nrow;
+                ci[0] = ni[0], ci[1] = ni[1], ci[2] = ni[2];
+                cv[0] = nv[0], cv[1] = nv[1], cv[2] = nv[2];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (r < n_seg) reinterpret_cast<float4 *>(P)[(cb * n_seg + r) * 16 + q] = res;
             if (!more) break;
-            cbeg = nbeg;
-            cn = nn;
-            crow = nrow;
-            ci[0] = ni[0], ci[1] = ni[1], ci[2] = ni[2];
-            cv[0] = nv[0], cv[1] = nv[1], cv[2] = nv[2];
         }
     }
 };
