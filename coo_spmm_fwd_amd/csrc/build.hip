@@ -307,6 +307,7 @@ int32_t pack_limit(const csp_layer *L)
 csp_status build_task_lists(csp_layer *L, hipStream_t s, bool with_packed)
 {
     L->packed_pending = with_packed;
+    L->tasks_pending = false;
     if (!with_packed) L->packed_valid = false;  // the list no longer matches the layer
     TaskBuild tb;
     TaskList *T[kLists] = {&L->row_tasks, &L->col_tasks, &L->row_packed};
@@ -364,16 +365,13 @@ csp_status set_task_counts(csp_layer *L, const uint32_t *counts)
     return CSP_OK;
 }
 
-csp_status tasks_ready(csp_layer *L, hipStream_t s)
+// The counts and the short-regrow flag that restructure_async left on the
+// device, read back; the flag leaves the layer refused.
+static csp_status read_async_counts(csp_layer *L, hipStream_t s, uint32_t *counts)
 {
-    if (!L->counts_stale) return CSP_OK;
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-        return set_error(CSP_ERR_INVALID_ARG, "this call needs the task lists that restructure_async left pending: "
-                                              "call sparse_layer_sync before capturing it");
-    uint32_t counts[kSelCountWords + 1] = {};  // the counts, then the short-regrow flag
     static_assert(kSelAsyncShort == kSelCounts + kSelCountWords, "the flag follows the counts");
-    CSP_HIP(hipMemcpyAsync(counts, L->ws.sel + kSelCounts, sizeof counts, hipMemcpyDeviceToHost, s));
+    CSP_HIP(hipMemcpyAsync(counts, L->ws.sel + kSelCounts, (kSelCountWords + 1) * sizeof(uint32_t),
+                           hipMemcpyDeviceToHost, s));
     CSP_HIP(hipStreamSynchronize(s));
     L->counts_stale = false;
     if (counts[kSelCountWords]) {
@@ -381,7 +379,55 @@ csp_status tasks_ready(csp_layer *L, hipStream_t s)
         return set_error(CSP_ERR_INVALID_ARG, "a restructure_async found fewer empty positions than it pruned in "
                                               "its batch of candidates; the layer is incomplete");
     }
+    return CSP_OK;
+}
+
+bool stream_capturing(hipStream_t s)
+{
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
+// A captured restructure_async leaves the layer's task state unknown after
+// any replay: it is taken as pending at every call.
+static void assume_replayed(csp_layer *L)
+{
+    if (!L->async_in_graph) return;
+    L->counts_stale = true;
+    if (L->tile_partial) L->tasks_pending = true;
+}
+
+csp_status tasks_ready(csp_layer *L, hipStream_t s)
+{
+    if (stream_capturing(s)) {
+        if (L->async_in_graph)
+            return set_error(CSP_ERR_INVALID_ARG, "this call reads the layer's task lists, which a captured "
+                                                  "restructure_async changes at every replay: it cannot be captured");
+        if (L->counts_stale || L->tasks_pending)
+            return set_error(CSP_ERR_INVALID_ARG, "this call needs the task lists that restructure_async left "
+                                                  "pending: call sparse_layer_sync before capturing it");
+        L->tasks_in_graph = true;
+        return CSP_OK;
+    }
+    assume_replayed(L);
+    if (!L->counts_stale && !L->tasks_pending) return CSP_OK;
+    if (L->tasks_pending) {
+        const csp_status st = build_task_lists(L, s, L->narrow_seen);
+        if (st != CSP_OK) return st;
+    }
+    uint32_t counts[kSelCountWords + 1] = {};  // the counts, then the short-regrow flag
+    const csp_status st = read_async_counts(L, s, counts);
+    if (st != CSP_OK) return st;
     return set_task_counts(L, counts);
+}
+
+csp_status async_checked(csp_layer *L, hipStream_t s)
+{
+    assume_replayed(L);
+    if (!L->tasks_pending) return tasks_ready(L, s);
+    if (!L->counts_stale) return CSP_OK;
+    uint32_t counts[kSelCountWords + 1] = {};
+    return read_async_counts(L, s, counts);  // the counts wait for the task lists
 }
 
 // ------------------------------------------------------------- LDS tiles

@@ -164,6 +164,17 @@ struct csp_layer {
     // Set by restructure_async: the host's task counts are those of the layer
     // before it, until tasks_ready reads back the new ones.
     bool counts_stale = false;
+    // Set by restructure_async on a layer with LDS tiles, which leaves the task
+    // lists unbuilt (the tile kernels never read them): tasks_ready builds
+    // them before the first call that does.
+    bool tasks_pending = false;
+    // Host state cannot follow graph replays.  async_in_graph: a
+    // restructure_async was captured, so any replay may have changed the
+    // layer: every call that needs the task lists rebuilds (layers with tiles)
+    // and reads them back first, and none may be captured.  tasks_in_graph: a
+    // call that reads the task lists was captured, whose launch sizes a
+    // captured restructure_async would make stale: capturing one is refused.
+    bool async_in_graph = false, tasks_in_graph = false;
     csp::Workspace ws;
     csp::ActBuffer act;
     hipEvent_t time_before = nullptr, time_after = nullptr;  // one-shot main-kernel timing request
@@ -233,10 +244,17 @@ csp_status build_task_lists(csp_layer *L, hipStream_t s, bool with_packed);
 int32_t pack_limit(const csp_layer *L);
 // Takes the kSelCountWords counts read back from sel[kSelCounts]; checks the capacities.
 csp_status set_task_counts(csp_layer *L, const uint32_t *counts);
-// After restructure_async: reads back the task counts (a synchronization on
-// s; refused on a stream that is being captured) and the short-regrow flag
-// (which leaves the layer refused).  Nothing to do otherwise.
+// After restructure_async: builds the task lists if it left them pending,
+// then reads back the task counts (a synchronization on s; refused on a
+// stream that is being captured) and the short-regrow flag (which leaves the
+// layer refused).  Nothing to do otherwise.
 csp_status tasks_ready(csp_layer *L, hipStream_t s);
+// Before a restructure: the short-regrow flag of a pending restructure_async
+// is checked as in tasks_ready, but task lists it left pending stay so (the
+// restructure rebuilds them).
+csp_status async_checked(csp_layer *L, hipStream_t s);
+// True while s is being captured into a graph.
+bool stream_capturing(hipStream_t s);
 // vals_c[j] = vals[perm_c[j]] after the canonical values changed.
 csp_status refresh_column_values(csp_layer *L, hipStream_t s);
 // Tiles of both views from row_ptr / cols and col_ptr / rows_by_col (four

@@ -482,7 +482,7 @@ csp_status restructure(sparse_layer_t L, int64_t n_prune, uint64_t seed, uint64_
     CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
-    csp_status st = tasks_ready(L, s);  // a pending restructure_async must have completed in full
+    csp_status st = async_checked(L, s);  // a pending restructure_async must have completed in full
     if (st != CSP_OK) return st;
     st = run_restructure(L, n_prune, seed, step, regrow_word(L, regrow_value), s);
     if (st == CSP_OK && n_prune > 0) st = build_tiles(L, s);
@@ -506,7 +506,7 @@ csp_status restructure_grad(sparse_layer_t L, int64_t n_prune, const void *dY, c
     CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     hipStream_t s = (hipStream_t)stream;
-    csp_status st = tasks_ready(L, s);
+    csp_status st = async_checked(L, s);
     if (st != CSP_OK) return st;
     st = restructure_gradient(L, n_prune, dY, X, B, regrow_word(L, regrow_value), s);
     if (st == CSP_OK && n_prune > 0) st = build_tiles(L, s);
@@ -536,6 +536,13 @@ csp_status restructure_async(sparse_layer_t L, int64_t n_prune, uint64_t seed, u
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
     if (n_prune == 0) return CSP_OK;
     hipStream_t s = (hipStream_t)stream;
+    if (stream_capturing(s)) {
+        if (L->tasks_in_graph)
+            return set_error(CSP_ERR_INVALID_ARG, "restructure_async cannot be captured on a layer with captured "
+                                                  "calls that read its task lists (their launch sizes would go "
+                                                  "stale at its replays)");
+        L->async_in_graph = true;
+    }
     csp_status st = restructure_bitmap_async(L, n_prune, seed, step_dev, regrow_word(L, regrow_value), s);
     if (st == CSP_OK) st = build_tiles(L, s);
     if (st == CSP_OK) L->counts_stale = true;
@@ -549,7 +556,13 @@ csp_status sparse_layer_sync(sparse_layer_t L, void *stream)
     DeviceGuard g(L->device);
     CSP_USABLE(L);
     if (!g.ok) return set_error(CSP_ERR_HIP, "cannot select the layer's device");
-    return tasks_ready(L, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    if (stream_capturing(s)) {  // nothing is launched: only a layer with nothing pending passes
+        if (L->counts_stale || L->tasks_pending || L->async_in_graph)
+            return set_error(CSP_ERR_INVALID_ARG, "sparse_layer_sync cannot run under stream capture");
+        return CSP_OK;
+    }
+    return tasks_ready(L, s);
 }
 
 int64_t sparse_layer_nnz(sparse_layer_t L) { return L ? L->nnz : -1; }

@@ -933,6 +933,12 @@ struct BitmapRun {
                                                         (V *)L->vals_c, L->col_ptr, L->tiles_c.ptr, L->tiles_c.ncb);
         CSP_LAUNCHED("k_bm_tgather");
         L->tile_ptr_ready = L->tiles_r.ptr != nullptr;  // build_tiles then only orders the tiles' rows
+        if (step_dev && L->tile_partial) {
+            // restructure_async on a layer with tiles: the task lists wait for
+            // the first call that reads them (tasks_ready).
+            L->tasks_pending = true;
+            return CSP_OK;
+        }
         return build_task_lists(L, s, L->narrow_seen);
     }
 

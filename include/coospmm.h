@@ -292,7 +292,17 @@ csp_status restructure_grad(sparse_layer_t layer, int64_t n_prune, const void *d
  *    restructure, restructure_grad) or by sparse_layer_sync.  Such a call on
  *    a stream under capture returns CSP_ERR_INVALID_ARG instead: call
  *    sparse_layer_sync before capturing it.  The LDS-tile products
- *    (fp32 layers with tiles, batch chunks of 33..64 rows) need no counts.
+ *    (fp32 layers with tiles, batch chunks of 33..64 rows) need no counts;
+ *  - on a layer with LDS tiles the task lists themselves are not rebuilt
+ *    either: the first product outside the LDS-tile path, spmm_fwd_static or
+ *    sparse_layer_sync builds them on "stream" before reading the counts (a
+ *    restructure or restructure_grad rebuilds them itself);
+ *  - once captured, it may change the layer at any replay, which the host
+ *    cannot follow: from then on every call that needs the task lists
+ *    rebuilds them (layers with tiles) and reads them back first, and such a
+ *    call cannot itself be captured (CSP_ERR_INVALID_ARG).  Capturing it on
+ *    a layer with such a call already captured is refused the same way,
+ *    since that call's launch sizes would go stale.
  * Calls on one layer must be ordered on one stream, as for every call.
  */
 csp_status restructure_async(sparse_layer_t layer, int64_t n_prune, uint64_t seed, uint64_t *step_dev,
@@ -300,8 +310,9 @@ csp_status restructure_async(sparse_layer_t layer, int64_t n_prune, uint64_t see
 
 /*
  * sparse_layer_sync -- completes the bookkeeping of earlier restructure_async
- * calls: synchronizes on "stream", reads back the task-list counts and the
- * short-regrow flag (CSP_ERR_INVALID_ARG, and the layer refused, if set).
+ * calls: builds the task lists they left pending, synchronizes on "stream",
+ * reads back the task-list counts and the short-regrow flag
+ * (CSP_ERR_INVALID_ARG, and the layer refused, if set).
  * Returns at once when nothing is pending.  Not for use under capture.
  */
 csp_status sparse_layer_sync(sparse_layer_t layer, void *stream);

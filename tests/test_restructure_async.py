@@ -182,3 +182,119 @@ def test_async_refusals(monkeypatch):
         assert int(step.item()) == 0
     finally:
         csp.sparse_layer_destroy(h)
+
+
+def products_equal(h1, h2, X, dY, what):
+    for name, fn in (("forward", lambda h: csp.spmm_fwd(h, X)),
+                     ("input gradient", lambda h: csp.spmm_bwd_input(h, dY)),
+                     ("both gradients", lambda h: torch.cat([t.flatten() for t in csp.spmm_bwd(h, dY, X)]))):
+        assert np.array_equal(bits(host(fn(h1))), bits(host(fn(h2)))), f"{what}: {name}"
+
+
+def test_task_lists_left_to_first_reader():
+    """On a layer with LDS tiles restructure_async leaves the task lists to the first call that reads
+    them: an eager restructure straight after it rebuilds them itself, a call that needs them is
+    refused under capture, and sparse_layer_sync builds them.  Products at a batch off the tile
+    path (B = 8) then equal an eager twin's bit for bit."""
+    out, in_, nnz = TILED
+    L, h1, h2 = twins(TILED, 61)
+    try:
+        n_prune, seed, B = nnz // 10, 62, 8
+        X = dev(W.random_dense((B, in_), 63))
+        dY = dev(W.random_dense((B, out), 64))
+        Y = torch.empty((B, out), device="cuda")
+        step = torch.tensor([5], dtype=torch.int64, device="cuda")
+        csp.restructure(h1, n_prune, seed, 5)
+        csp.restructure_async(h2, n_prune, seed, step)
+        csp.restructure(h1, n_prune, seed, 6)
+        csp.restructure(h2, n_prune, seed, 6)   # straight after the async step
+        same_layer(h1, h2, "eager step after an async one")
+        products_equal(h1, h2, X, dY, "after the eager step")
+        step.fill_(7)
+        csp.restructure(h1, n_prune, seed, 7)
+        csp.restructure_async(h2, n_prune, seed, step)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with pytest.raises(csp.CspError, match="sparse_layer_sync"):
+            with torch.cuda.graph(g):
+                csp.spmm_fwd(h2, X, Y, stream=torch.cuda.current_stream())
+        del g
+        torch.cuda.synchronize()
+        csp.sparse_layer_sync(h2)
+        same_layer(h1, h2, "async step, then sync")
+        products_equal(h1, h2, X, dY, "after sync")
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h1)
+        csp.sparse_layer_destroy(h2)
+
+
+@pytest.mark.parametrize("shape", [SMALL, TILED], ids=["small", "tiled"])
+def test_replayed_async_then_task_readers(shape):
+    """A captured restructure_async changes the layer at every replay, which host state cannot
+    follow: each later call that needs the task lists rebuilds (tiled layer) and reads them back
+    first, so products at B = 8 equal an eager twin's after every replay; such a call cannot itself
+    be captured."""
+    out, in_, nnz = shape
+    L, h1, h2 = twins(shape, 71)
+    try:
+        n_prune, seed, s0, B = nnz // 10, 72, 300, 8
+        X = dev(W.random_dense((B, in_), 73))
+        dY = dev(W.random_dense((B, out), 74))
+        Y = torch.empty((B, out), device="cuda")
+        step = torch.tensor([s0], dtype=torch.int64, device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            csp.restructure_async(h2, n_prune, seed, step, stream=torch.cuda.current_stream())
+        for k in range(2):
+            g.replay()
+            csp.restructure(h1, n_prune, seed, s0 + k)
+            torch.cuda.synchronize()
+            same_layer(h1, h2, f"replay {k}")
+            products_equal(h1, h2, X, dY, f"replay {k}")
+        g2 = torch.cuda.CUDAGraph()
+        with pytest.raises(csp.CspError, match="captured restructure_async"):
+            with torch.cuda.graph(g2):
+                csp.spmm_fwd(h2, X, Y, stream=torch.cuda.current_stream())
+        del g2
+        torch.cuda.synchronize()
+        csp.sparse_layer_sync(h2)
+        del g
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h1)
+        csp.sparse_layer_destroy(h2)
+
+
+def test_async_capture_refused_after_task_reader_captured():
+    """A captured product that reads the task lists has its launch sizes fixed at capture; a
+    captured restructure_async on the same layer would make them stale, so its capture is refused
+    (and the layer stays usable: the same call runs eagerly)."""
+    out, in_, nnz = SMALL
+    L = W.random_layer(out, in_, nnz, seed=81)
+    h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        X = dev(W.random_dense((8, in_), 82))
+        Y = torch.empty((8, out), device="cuda")
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            csp.spmm_fwd(h, X, Y, stream=torch.cuda.current_stream())
+        g.replay()
+        torch.cuda.synchronize()
+        step = torch.tensor([0], dtype=torch.int64, device="cuda")
+        g2 = torch.cuda.CUDAGraph()
+        with pytest.raises(csp.CspError, match="captured calls that read"):
+            with torch.cuda.graph(g2):
+                csp.restructure_async(h, nnz // 10, 83, step, stream=torch.cuda.current_stream())
+        del g2
+        torch.cuda.synchronize()
+        assert int(step.item()) == 0
+        csp.restructure_async(h, nnz // 10, 83, step)
+        csp.sparse_layer_sync(h)
+        assert int(step.item()) == 1
+        del g
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h)
