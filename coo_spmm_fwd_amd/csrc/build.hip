@@ -464,14 +464,26 @@ __global__ __launch_bounds__(256) void k_tile_ptr(const int32_t *__restrict__ se
 // counting sort.  Segments of equal count land in any order: the order only
 // pairs segments for the waves of the tile kernels, whose sums do not depend
 // on it.  Each slot records its segment's entry range in the tile beside the
-// segment, so that a tile kernel's wave finds its work with one load.
-__global__ __launch_bounds__(kTileRows) void k_tile_rows(const int32_t *__restrict__ tile_ptr, int64_t nseg,
-                                                         int64_t ncb, int2 *__restrict__ slots)
+// segment, so that a tile kernel's wave finds its work with one load.  One
+// launch takes both views: the row view's tiles first, then the column
+// view's.
+struct TileRowsView {
+    const int32_t *tile_ptr;
+    int64_t nseg, ncb, ntiles;
+    int2 *slots;
+};
+
+__global__ __launch_bounds__(kTileRows) void k_tile_rows(TileRowsView v0, TileRowsView v1)
 {
     static_assert(kTileRows % kWave == 0 && kTileRows <= 1024, "one thread per row and per bin");
     __shared__ uint32_t bin_n[kTileRows], bin_at[kTileRows];
     __shared__ uint32_t lds[17];
-    const int64_t tile = blockIdx.x, rb = tile / ncb, cb = tile - rb * ncb;
+    const bool first = blockIdx.x < v0.ntiles;
+    const int32_t *__restrict__ tile_ptr = first ? v0.tile_ptr : v1.tile_ptr;
+    int2 *__restrict__ slots = first ? v0.slots : v1.slots;
+    const int64_t nseg = first ? v0.nseg : v1.nseg, ncb = first ? v0.ncb : v1.ncb;
+    const int64_t tile = first ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - v0.ntiles, rb = tile / ncb,
+                  cb = tile - rb * ncb;
     const int l = threadIdx.x;
     const int64_t r = rb * kTileRows + l;
     const int32_t beg = r < nseg ? tile_ptr[r * (ncb + 1) + cb] : 0;
@@ -496,16 +508,17 @@ csp_status build_tiles(csp_layer *L, hipStream_t s)
     if (!L->tile_partial) return CSP_OK;
     const Tiles *T[2] = {&L->tiles_r, &L->tiles_c};
     const int32_t *seg_ptr[2] = {L->row_ptr, L->col_ptr}, *idx[2] = {L->cols, L->rows_by_col};
+    TileRowsView tv[2];
     for (int v = 0; v < 2; ++v) {
         if (!L->tile_ptr_ready) {
             k_tile_ptr<<<(unsigned)ceil_div(T[v]->nseg, 4), 256, 0, s>>>(seg_ptr[v], idx[v], T[v]->nseg, T[v]->ncb,
                                                                          T[v]->ptr);
             CSP_LAUNCHED("k_tile_ptr");
         }
-        k_tile_rows<<<(unsigned)(T[v]->nrb * T[v]->ncb), kTileRows, 0, s>>>(T[v]->ptr, T[v]->nseg, T[v]->ncb,
-                                                                             T[v]->slots);
-        CSP_LAUNCHED("k_tile_rows");
+        tv[v] = TileRowsView{T[v]->ptr, T[v]->nseg, T[v]->ncb, T[v]->nrb * T[v]->ncb, T[v]->slots};
     }
+    k_tile_rows<<<(unsigned)(tv[0].ntiles + tv[1].ntiles), kTileRows, 0, s>>>(tv[0], tv[1]);
+    CSP_LAUNCHED("k_tile_rows");
     L->tile_ptr_ready = false;
     return CSP_OK;
 }

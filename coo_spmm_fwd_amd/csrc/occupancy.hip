@@ -602,18 +602,32 @@ __global__ __launch_bounds__(kThreads) void k_bm_or(uint32_t *__restrict__ occ, 
 // index; any other (regrown, also a just-pruned one) gets the regrow value.
 // The thread of a row's first word also writes row_ptr.
 template <typename V>
-__global__ __launch_bounds__(kThreads) void k_bm_canon(const uint32_t *__restrict__ occ,
-                                                       const uint32_t *__restrict__ pref,
-                                                       const uint32_t *__restrict__ occ_old,
-                                                       const uint32_t *__restrict__ pref_old,
-                                                       const uint64_t *__restrict__ pruned,
-                                                       const V *__restrict__ vals_old, V regrow, uint32_t nw,
-                                                       uint32_t inw, int64_t out, int32_t *__restrict__ rows,
-                                                       int32_t *__restrict__ cols, V *__restrict__ vals,
-                                                       int32_t *__restrict__ row_ptr, int32_t *__restrict__ tptr,
-                                                       int64_t ncb)
+struct CanonArgs {
+    const uint32_t *occ, *pref, *occ_old, *pref_old;
+    const uint64_t *pruned;
+    const V *vals_old;
+    V regrow;
+    uint32_t nw, inw;
+    int64_t out;
+    int32_t *rows, *cols;
+    V *vals;
+    int32_t *row_ptr, *tptr;
+    int64_t ncb;
+};
+
+template <typename V>
+__device__ __forceinline__ void bm_canon(uint32_t w, const CanonArgs<V> &A)
 {
-    const uint32_t w = blockIdx.x * kThreads + threadIdx.x;
+    const uint32_t *__restrict__ occ = A.occ, *__restrict__ pref = A.pref, *__restrict__ occ_old = A.occ_old,
+                                 *__restrict__ pref_old = A.pref_old;
+    const uint64_t *__restrict__ pruned = A.pruned;
+    const V *__restrict__ vals_old = A.vals_old;
+    const V regrow = A.regrow;
+    const uint32_t nw = A.nw, inw = A.inw;
+    const int64_t out = A.out, ncb = A.ncb;
+    int32_t *__restrict__ rows = A.rows, *__restrict__ cols = A.cols, *__restrict__ row_ptr = A.row_ptr,
+            *__restrict__ tptr = A.tptr;
+    V *__restrict__ vals = A.vals;
     if (w > nw) return;
     const uint32_t r = w / inw, cw = w - r * inw;
     uint32_t pos = pref[w];
@@ -681,13 +695,13 @@ __device__ __forceinline__ uint2 tile_row_words(const uint32_t *__restrict__ occ
 }
 
 // Entries per column within each 1024-row chunk: tcnt[c * nrc + chunk].
-// One block per tile, wave w takes slices w, w + 4, ...
-__global__ __launch_bounds__(kThreads) void k_bm_tcount(const uint32_t *__restrict__ occ, int64_t inw,
-                                                        int64_t rows_alloc, int64_t nrc, uint32_t *__restrict__ tcnt)
+// One block per tile (block index bid), wave w takes slices w, w + 4, ...
+__device__ __forceinline__ void bm_tcount(int64_t bid, const uint32_t *__restrict__ occ, int64_t inw,
+                                          int64_t rows_alloc, int64_t nrc, uint32_t *__restrict__ tcnt)
 {
     __shared__ uint32_t part[4][kTC];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int64_t rc = blockIdx.x % nrc, cg = blockIdx.x / nrc;
+    const int64_t rc = bid % nrc, cg = bid / nrc;
     uint2 wd[kTSlices / 4];
 #pragma unroll
     for (int i = 0; i < kTSlices / 4; ++i)
@@ -712,13 +726,50 @@ __global__ __launch_bounds__(kThreads) void k_bm_tcount(const uint32_t *__restri
     }
 }
 
+// The canonical arrays and the per-chunk column counts read only the next
+// bitmap and its ranks, so one launch does both: the ntc count blocks
+// first, then one thread per bitmap word.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void k_bm_canon_tcount(CanonArgs<V> A, int64_t rows_alloc, int64_t nrc,
+                                                              uint32_t *__restrict__ tcnt, uint32_t ntc)
+{
+    if (blockIdx.x < ntc) {
+        bm_tcount(blockIdx.x, A.occ, A.inw, rows_alloc, nrc, tcnt);
+        return;
+    }
+    bm_canon<V>((blockIdx.x - ntc) * kThreads + threadIdx.x, A);
+}
+
+// Plain copies of three arrays of 32-bit words (16-byte aligned): piece i of
+// their concatenation is 16 bytes, copied word by word at an array's end.
+struct CopySeg {
+    const uint32_t *src;
+    uint32_t *dst;
+    int64_t n;
+};
+__device__ __forceinline__ void copy3_piece(int64_t i, const CopySeg &a, const CopySeg &b, const CopySeg &c)
+{
+    const int64_t na = ceil_div(a.n, 4), nb = ceil_div(b.n, 4);
+    const CopySeg &g = i < na ? a : (i < na + nb ? b : c);
+    const int64_t j = i < na ? i : (i < na + nb ? i - na : i - na - nb), w = 4 * j;
+    if (w + 4 <= g.n) reinterpret_cast<uint4 *>(g.dst)[j] = reinterpret_cast<const uint4 *>(g.src)[j];
+    else
+        for (int64_t k = w; k < g.n; ++k) g.dst[k] = g.src[k];
+}
+__host__ __device__ inline int64_t copy3_pieces(const CopySeg &a, const CopySeg &b, const CopySeg &c)
+{
+    return ceil_div(a.n, 4) + ceil_div(b.n, 4) + ceil_div(c.n, 4);
+}
+
 // Transposed view, one block per tile: the tile's output is, per column, a
 // run of consecutive transposed ranks from tscan[c * nrc + rc] (exclusive
 // scan of tcnt).  Lanes walk the tile's entries in that order, so stores are
 // coalesced: output o -> column (search in the column starts) -> row (search
 // in the column's cumulative word counts, then the bit) -> canonical index
 // (the row's first entry in the tile plus its entries to the left).  rc = 0
-// also writes col_ptr.
+// also writes col_ptr.  Blocks from ntiles on copy the pieces of (ca, cb, cc)
+// instead (restructure_async's write-back, which reads nothing the tiles
+// write and writes nothing they read).
 template <typename V>
 __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restrict__ occ,
                                                    const uint32_t *__restrict__ pref, int64_t inw, int64_t rows_alloc,
@@ -726,8 +777,13 @@ __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restr
                                                    const V *__restrict__ vals, int32_t *__restrict__ perm_c,
                                                    int32_t *__restrict__ rows_by_col, V *__restrict__ vals_c,
                                                    int32_t *__restrict__ col_ptr, int32_t *__restrict__ tptr,
-                                                   int64_t nrb)
+                                                   int64_t nrb, int64_t ntiles, CopySeg ca, CopySeg cb, CopySeg cc)
 {
+    if ((int64_t)blockIdx.x >= ntiles) {
+        const int64_t i = ((int64_t)blockIdx.x - ntiles) * kThreads + threadIdx.x;
+        if (i < copy3_pieces(ca, cb, cc)) copy3_piece(i, ca, cb, cc);
+        return;
+    }
     __shared__ uint2 rw[kTR];                     // row words
     __shared__ uint32_t seg[kTR];                 // canonical index of the row's first entry in the tile
     __shared__ uint32_t cw[kTC][kTR / 32 + 1];    // column words (padded against bank conflicts)
@@ -850,25 +906,6 @@ int hash_bits_for(int64_t M)  // smallest b with 2^b >= 2M
     return b < 1 ? 1 : b;
 }
 
-// Plain copies of three arrays of 32-bit words (16-byte aligned), one launch:
-// thread i copies 16-byte piece i of the concatenation, word by word at an
-// array's end.
-struct CopySeg {
-    const uint32_t *src;
-    uint32_t *dst;
-    int64_t n;
-};
-__global__ __launch_bounds__(kThreads) void k_copy3(CopySeg a, CopySeg b, CopySeg c)
-{
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t na = ceil_div(a.n, 4), nb = ceil_div(b.n, 4);
-    const CopySeg &g = i < na ? a : (i < na + nb ? b : c);
-    const int64_t j = i < na ? i : (i < na + nb ? i - na : i - na - nb), w = 4 * j;
-    if (w + 4 <= g.n) reinterpret_cast<uint4 *>(g.dst)[j] = reinterpret_cast<const uint4 *>(g.src)[j];
-    else
-        for (int64_t k = w; k < g.n; ++k) g.dst[k] = g.src[k];
-}
-
 template <typename V>
 struct BitmapRun {
     csp_layer *L;
@@ -912,25 +949,27 @@ struct BitmapRun {
     // lists.  rows_out and cols_out take the canonical rows and columns (the
     // staged arrays, or the layer's own: nothing of the old ones is read);
     // the values always go to the staged array (the old ones are read).
-    csp_status rebuild_device(int32_t *rows_out, int32_t *cols_out)
+    csp_status rebuild_device(int32_t *rows_out, int32_t *cols_out, const CopySeg *copy = nullptr)
     {
         Workspace &W = L->ws;
         const int64_t nw = W.occ_words, inw = W.occ_row_words, rows_alloc = W.occ_rows;
         const int64_t nrc = ceil_div(rows_alloc, kTR), ncg = inw / 2, ntiles = nrc * ncg;
         csp_status st = exclusive_scan_popc(W.occ_next, W.occ_pref_next, nw, W.hist, s);
         if (st != CSP_OK) return st;
-        k_bm_canon<V><<<blocks_for(nw + 1, kThreads), kThreads, 0, s>>>(
-            W.occ_next, W.occ_pref_next, W.occ, W.occ_pref, (const uint64_t *)W.acc_b, (const V *)L->vals, regrow,
-            (uint32_t)nw, (uint32_t)inw, L->out, rows_out, cols_out, (V *)W.vals_k, L->row_ptr, L->tiles_r.ptr,
-            L->tiles_r.ncb);
-        CSP_LAUNCHED("k_bm_canon");
-        k_bm_tcount<<<(unsigned)ntiles, kThreads, 0, s>>>(W.occ_next, inw, rows_alloc, nrc, W.tcnt);
-        CSP_LAUNCHED("k_bm_tcount");
+        const CanonArgs<V> ca{W.occ_next, W.occ_pref_next, W.occ, W.occ_pref, (const uint64_t *)W.acc_b,
+                              (const V *)L->vals, regrow, (uint32_t)nw, (uint32_t)inw, L->out, rows_out, cols_out,
+                              (V *)W.vals_k, L->row_ptr, L->tiles_r.ptr, L->tiles_r.ncb};
+        k_bm_canon_tcount<V><<<(unsigned)ntiles + blocks_for(nw + 1, kThreads), kThreads, 0, s>>>(
+            ca, rows_alloc, nrc, W.tcnt, (uint32_t)ntiles);
+        CSP_LAUNCHED("k_bm_canon_tcount");
         st = exclusive_scan_u32(W.tcnt, W.tcnt, ncg * kTC * nrc, W.hist, (uint32_t *)(L->col_ptr + L->in), s);
         if (st != CSP_OK) return st;
-        k_bm_tgather<V><<<(unsigned)ntiles, kThreads, 0, s>>>(W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in,
-                                                        W.tcnt, (const V *)W.vals_k, L->perm_c, L->rows_by_col,
-                                                        (V *)L->vals_c, L->col_ptr, L->tiles_c.ptr, L->tiles_c.ncb);
+        const CopySeg none{nullptr, nullptr, 0};
+        const CopySeg c0 = copy ? copy[0] : none, c1 = copy ? copy[1] : none, c2 = copy ? copy[2] : none;
+        const unsigned cblocks = blocks_for(copy3_pieces(c0, c1, c2), kThreads);
+        k_bm_tgather<V><<<(unsigned)ntiles + cblocks, kThreads, 0, s>>>(
+            W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in, W.tcnt, (const V *)W.vals_k, L->perm_c,
+            L->rows_by_col, (V *)L->vals_c, L->col_ptr, L->tiles_c.ptr, L->tiles_c.ncb, ntiles, c0, c1, c2);
         CSP_LAUNCHED("k_bm_tgather");
         L->tile_ptr_ready = L->tiles_r.ptr != nullptr;  // build_tiles then only orders the tiles' rows
         if (step_dev && L->tile_partial) {
@@ -1043,14 +1082,13 @@ struct BitmapRun {
         const int hb = hash_bits_for(M);
         csp_status st = prune(W.hash, int64_t(1) << hb);
         if (st == CSP_OK) st = batch(M, hb);
-        if (st == CSP_OK) st = rebuild_device(L->rows, L->cols);
         if (st != CSP_OK) return st;
-        const CopySeg a{(const uint32_t *)W.vals_k, (uint32_t *)L->vals, ceil_div(L->nnz * (int64_t)sizeof(V), 4)};
-        const CopySeg b{W.occ_next, W.occ, W.occ_words}, c{W.occ_pref_next, W.occ_pref, W.occ_words + 1};
-        const int64_t pieces = ceil_div(a.n, 4) + ceil_div(b.n, 4) + ceil_div(c.n, 4);
-        k_copy3<<<blocks_for(pieces, kThreads), kThreads, 0, s>>>(a, b, c);
-        CSP_LAUNCHED("k_copy3");
-        return CSP_OK;
+        // the staged values and bitmaps written back by the transposing launch
+        const CopySeg copy[3] = {
+            {(const uint32_t *)W.vals_k, (uint32_t *)L->vals, ceil_div(L->nnz * (int64_t)sizeof(V), 4)},
+            {W.occ_next, W.occ, W.occ_words},
+            {W.occ_pref_next, W.occ_pref, W.occ_words + 1}};
+        return rebuild_device(L->rows, L->cols, copy);
     }
 
     csp_status run()
