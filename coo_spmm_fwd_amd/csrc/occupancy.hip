@@ -1216,6 +1216,10 @@ int64_t async_batch(const csp_layer *L, int64_t n_prune)
     const double want = (double)n_prune / free_frac * 1.2 + 4096.0;
     if (want > (double)W.bm_batch_cap) return 0;
     int64_t M = (int64_t)want;
+    if (const char *e = std::getenv("COOSPMM_REGROW_BATCH")) {  // test hook: a smaller batch (may come up short)
+        const long long v = std::atoll(e);
+        if (v >= 4 && v < M) M = v;
+    }
     return M + (4 - M % 4) % 4;  // whole Philox blocks
 }
 

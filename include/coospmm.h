@@ -278,7 +278,7 @@ csp_status restructure_grad(sparse_layer_t layer, int64_t n_prune, const void *d
  *  - layers with position bitmaps only (out * in < 2^32, bitmaps within
  *    1 GiB), and n_prune whose candidates fit one batch; else
  *    CSP_ERR_INVALID_ARG before anything is enqueued;
- *  - one batch of candidates, about 1.5 times the expected need plus 4096:
+ *  - one batch of candidates, about 1.2 times the expected need plus 4096:
  *    should it hold fewer than n_prune empty, first-seen positions (a
  *    deviation of hundreds of standard deviations for layers of 10^5
  *    entries and more), a device flag is set, and the next call that

@@ -298,3 +298,26 @@ def test_async_capture_refused_after_task_reader_captured():
     finally:
         torch.cuda.synchronize()
         csp.sparse_layer_destroy(h)
+
+
+def test_short_async_batch_refuses_layer(monkeypatch):
+    """A batch with fewer empty, first-seen positions than were pruned (forced here with a batch of
+    64 candidates) sets the device flag: the step counter still advances, the next synchronizing call
+    reports the short regrow, and the layer is refused from then on."""
+    out, in_, nnz = SMALL
+    L = W.random_layer(out, in_, nnz, seed=91)
+    h = csp.sparse_layer_create(out, in_, dev(L.rows), dev(L.cols), dev(L.vals))
+    try:
+        monkeypatch.setenv("COOSPMM_REGROW_BATCH", "64")
+        step = torch.tensor([3], dtype=torch.int64, device="cuda")
+        csp.restructure_async(h, nnz // 10, 92, step)
+        torch.cuda.synchronize()
+        assert int(step.item()) == 4
+        with pytest.raises(csp.CspError, match="fewer empty positions"):
+            csp.sparse_layer_sync(h)
+        X = dev(W.random_dense((8, in_), 93))
+        with pytest.raises(csp.CspError):
+            csp.spmm_fwd(h, X)
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h)
