@@ -387,7 +387,8 @@ def restructure_async(layer: int, n_prune: int, seed: int, step_dev, regrow_valu
 
 
 def sparse_layer_sync(layer: int, stream=None):
-    """Finish the bookkeeping of earlier restructure_async calls (synchronizes)."""
+    """Finish the bookkeeping of earlier restructure_async calls: build the task lists they left
+    pending, then read back their counts and the short-regrow flag (synchronizes)."""
     _check(load().sparse_layer_sync(c_void_p(layer), _stream(stream)))
 
 
