@@ -247,3 +247,47 @@ def test_restructured_tiles_match_a_fresh_layer():
                 csp.sparse_layer_destroy(h2)
     finally:
         csp.sparse_layer_destroy(h)
+
+
+NS_OUT, NS_IN = 6000 + 11, 12000 + 5   # row view 12 x 24 tiles, column view 24 x 12
+
+
+def test_nonsquare_tiles_against_oracle(orc):
+    """A layer whose two views cut into different tile grids (12 x 24 and 24 x 12 blocks of 512),
+    so every per-view tile count and block stride is exercised: forward, input gradient and sampled
+    value gradient at B = 64 against the oracle, at create and after a restructure, and the
+    asynchronous restructure's layer equal to the eager one bit for bit."""
+    B, nnz = 64, int(0.04 * NS_OUT * NS_IN)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert -(-NS_OUT // 512) * -(-NS_IN // 512) >= cus, "the layer must have a tile per compute unit"
+    L = W.random_layer(NS_OUT, NS_IN, nnz, seed=301)
+    mk = lambda: csp.sparse_layer_create(NS_OUT, NS_IN, dev(L.rows), dev(L.cols), dev(L.vals))
+    h, h2 = mk(), mk()
+    try:
+        X = dev(W.random_dense((B, NS_IN), 302))
+        dY = dev(W.random_dense((B, NS_OUT), 303))
+
+        def check(hh, what):
+            r, c, v = (host(t) for t in csp.sparse_layer_export(hh))
+            ref, S = orc.spmm_fwd(NS_OUT, NS_IN, r, c, v, host(X))
+            assert_within(host(csp.spmm_fwd(hh, X)), ref, S, FP32_REL, f"{what}: forward")
+            dX, dW = csp.spmm_bwd(hh, dY, X)
+            refx, Sx = orc.spmm_bwd_input(NS_OUT, NS_IN, r, c, v, host(dY))
+            assert_within(host(dX), refx, Sx, FP32_REL, f"{what}: input gradient")
+            check_sample(hh, dW, X, dY, 304)
+
+        check(h, "created")
+        step = torch.tensor([9], dtype=torch.int64, device="cuda")
+        csp.restructure(h, nnz // 10, 305, 9)
+        csp.restructure_async(h2, nnz // 10, 305, step)
+        torch.cuda.synchronize()
+        a = [host(t) for t in csp.sparse_layer_export(h) + csp.sparse_layer_export_index(h)]
+        b = [host(t) for t in csp.sparse_layer_export(h2) + csp.sparse_layer_export_index(h2)]
+        for x, y in zip(a, b):
+            assert np.array_equal(bits(x) if x.dtype == np.float32 else x, bits(y) if y.dtype == np.float32 else y)
+        check(h, "restructured")
+        check(h2, "restructured asynchronously")
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h)
+        csp.sparse_layer_destroy(h2)
