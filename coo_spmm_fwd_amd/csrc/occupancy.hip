@@ -527,15 +527,24 @@ __global__ __launch_bounds__(kThreads) void k_bm_cand_take(const uint32_t *__res
 // tiles of kScoreB batch rows at a time in LDS.
 constexpr int kScoreTile = 128;
 constexpr int kScoreB = 32;
+// The block also adds its keys to the first histogram pass of the select
+// that follows (hist0: pass 0's kCopies x 256 bins, digit (~key >> shift0) &
+// 255, in the select's order of InvKeys), so that pass needs no launch of
+// its own: per-block counts in LDS (4 copies by lane), then one atomic per
+// nonzero bin into copy blockIdx % kCopies.
 template <class D>
 __global__ __launch_bounds__(kThreads) void k_bm_scores(const typename D::T *__restrict__ dY,
                                                         const typename D::T *__restrict__ X, int64_t B, int64_t out,
                                                         int64_t in, const uint32_t *__restrict__ occ, int64_t inw,
-                                                        int64_t rows_alloc, uint32_t *__restrict__ keys)
+                                                        int64_t rows_alloc, uint32_t *__restrict__ keys,
+                                                        uint32_t *__restrict__ hist0, int shift0)
 {
     __shared__ __align__(16) float ty[kScoreB][kScoreTile + 4];  // [b][row]
     __shared__ __align__(16) float tx[kScoreB][kScoreTile + 4];  // [b][col]
+    constexpr int kHistCopies = 4;  // keeps four blocks' LDS within a CU
+    __shared__ uint32_t hh[kHistCopies][256];
     const int t = threadIdx.x, tr = t >> 4, tc = t & 15;         // 16 x 16 threads, 8 x 8 each
+    for (int i = t; i < kHistCopies * 256; i += kThreads) (&hh[0][0])[i] = 0u;  // ordered by the first barrier below
     const int64_t ncb = inw * 32 / kScoreTile;                    // column blocks
     const int64_t r0 = (int64_t)(blockIdx.x / ncb) * kScoreTile, c0 = (int64_t)(blockIdx.x % ncb) * kScoreTile;
     float acc[8][8];
@@ -582,8 +591,16 @@ __global__ __launch_bounds__(kThreads) void k_bm_scores(const typename D::T *__r
         uint4 *dst = reinterpret_cast<uint4 *>(keys + r * inw * 32 + c);
         dst[0] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
         dst[1] = make_uint4(kv[4], kv[5], kv[6], kv[7]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) atomicAdd(&hh[t & (kHistCopies - 1)][(~kv[j] >> shift0) & 255u], 1u);
     }
+    __syncthreads();
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kHistCopies; ++k) cnt += hh[k][t];
+    if (cnt) atomicAdd(&hist0[(blockIdx.x & (kCopies - 1)) * 256 + t], cnt);
 }
+static_assert(kThreads == 256, "one thread per bin of the scores' histogram");
 
 // Adds the chosen positions (bit mask in bitmap word order) to the next
 // bitmap; records that all n_prune are taken.
@@ -1009,12 +1026,14 @@ struct BitmapRun {
     // bit per index of the chosen ones (ties go to the smaller index) in mask;
     // `clear` (optional) is filled with empty hash slots by the first pass.
     template <class K>
+    // first = 1: pass 0's histogram is already in place (the producer of the
+    // keys counted them), and there is nothing to clear.
     csp_status select(K keyof, int64_t n, int64_t count, int passes, int top, uint64_t *mask, uint64_t *clear,
-                      int64_t nclear)
+                      int64_t nclear, int first = 0)
     {
         Workspace &W = L->ws;
         const int64_t hgrid = ceil_div(n, kHistThreads * 8) < 256 ? ceil_div(n, kHistThreads * 8) : 256;
-        for (int p = 0; p < passes; ++p) {
+        for (int p = first; p < passes; ++p) {
             k_bm_hist<K><<<(unsigned)hgrid, kHistThreads, 0, s>>>(keyof, n, p, top, (uint32_t)count, W.sel,
                                                                    p == 0 ? clear : nullptr, p == 0 ? nclear : 0);
             CSP_LAUNCHED("k_bm_hist");
@@ -1061,10 +1080,10 @@ struct BitmapRun {
         k_bm_scores<D><<<(unsigned)(rblk * cblk), kThreads, 0, s>>>((const typename D::T *)dY,
                                                                      (const typename D::T *)X, B, L->out, L->in,
                                                                      W.occ_next, W.occ_row_words, W.occ_rows,
-                                                                     W.score);
+                                                                     W.score, W.sel, 24);
         CSP_LAUNCHED("k_bm_scores");
         uint64_t *chosen = (uint64_t *)W.occ_pref_next;  // scratch until the rebuild
-        csp_status st = select(InvKeys{W.score}, npad, n_prune, 4, 24, chosen, nullptr, 0);
+        csp_status st = select(InvKeys{W.score}, npad, n_prune, 4, 24, chosen, nullptr, 0, 1);
         if (st != CSP_OK) return st;
         k_bm_or<<<blocks_for(W.occ_words, kThreads), kThreads, 0, s>>>(W.occ_next, (const uint32_t *)chosen,
                                                                        W.occ_words, W.sel, (uint32_t)n_prune);
