@@ -227,43 +227,71 @@ __global__ __launch_bounds__(kThreads) void k_bm_prune_count(K keyof, int64_t n,
 }
 
 // One block of 1024: exclusive scans (in place) of the interleaved per-tile
-// counts; clears the regrow counters and the select histograms.  A thread
-// takes a run of tiles and reads it in groups of kScanGroup pairs, all loads
-// of a group in flight together (a run read one load after another left the
-// block waiting on dozens of serial loads over the 67 M positions of the
-// gradient-informed regrow).
-constexpr int kScanGroup = 16;
+// counts; clears the regrow counters and the select histograms.  The pairs
+// are read and written coalesced: in each round wave w takes kScanRows rows
+// of 64 consecutive pairs (lane l holds pair 64 g + l of its run), scans them
+// row by row across the lanes with a running carry, and the waves' totals are
+// added in order through LDS.  (A thread reading its own run of consecutive
+// pairs touched a cache line per lane per load: 27 us for the 16 K tiles of
+// the gradient-informed select.)
+constexpr int kScanRows = 8;
 __global__ __launch_bounds__(1024) void k_bm_prune_scan(uint32_t *tiles, int64_t nt, uint32_t *sel)
 {
-    __shared__ uint32_t lds[17];
-    const int64_t per = ceil_div(nt, 1024), b0 = (int64_t)threadIdx.x * per;
-    const int64_t e0 = b0 < nt ? b0 : nt, e1 = b0 + per < nt ? b0 + per : nt;
+    constexpr int kWaves = 1024 / 64;
+    constexpr int64_t kRound = (int64_t)kWaves * 64 * kScanRows;  // pairs per round
+    __shared__ uint32_t wt[2][kWaves];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     uint2 *pairs = reinterpret_cast<uint2 *>(tiles);  // (below, equal) of tile i
-    uint32_t s0 = 0, s1 = 0;
-    for (int64_t i = e0; i < e1; i += kScanGroup) {
-        uint2 v[kScanGroup];
+    uint32_t carry0 = 0, carry1 = 0;                  // totals of the earlier rounds
+    for (int64_t r0 = 0; r0 < nt; r0 += kRound) {
+        const int64_t base = r0 + (int64_t)w * 64 * kScanRows + lane;
+        uint2 v[kScanRows];
 #pragma unroll
-        for (int g = 0; g < kScanGroup; ++g) v[g] = i + g < e1 ? pairs[i + g] : make_uint2(0u, 0u);
-#pragma unroll
-        for (int g = 0; g < kScanGroup; ++g) {
-            s0 += v[g].x;
-            s1 += v[g].y;
+        for (int g = 0; g < kScanRows; ++g) {
+            const int64_t i = base + 64 * g;
+            const uint2 x = pairs[i < nt ? i : 0];
+            v[g] = i < nt ? x : make_uint2(0u, 0u);
         }
-    }
-    uint32_t t0, t1;
-    uint32_t r0 = block_exclusive_scan(s0, lds, &t0);
-    uint32_t r1 = block_exclusive_scan(s1, lds, &t1);
-    for (int64_t i = e0; i < e1; i += kScanGroup) {
-        uint2 v[kScanGroup];
+        uint32_t run0 = 0, run1 = 0;  // the wave's pairs before row g
 #pragma unroll
-        for (int g = 0; g < kScanGroup; ++g) v[g] = i + g < e1 ? pairs[i + g] : make_uint2(0u, 0u);
+        for (int g = 0; g < kScanRows; ++g) {
+            uint32_t a0 = v[g].x, a1 = v[g].y;
 #pragma unroll
-        for (int g = 0; g < kScanGroup; ++g)
-            if (i + g < e1) {
-                pairs[i + g] = make_uint2(r0, r1);
-                r0 += v[g].x;
-                r1 += v[g].y;
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t y0 = __shfl_up(a0, off, 64), y1 = __shfl_up(a1, off, 64);
+                if (lane >= off) {
+                    a0 += y0;
+                    a1 += y1;
+                }
             }
+            const uint32_t own0 = v[g].x, own1 = v[g].y;
+            v[g] = make_uint2(run0 + a0 - own0, run1 + a1 - own1);  // exclusive, within the wave's run
+            run0 += __shfl(a0, 63, 64);
+            run1 += __shfl(a1, 63, 64);
+        }
+        if (lane == 0) {
+            wt[0][w] = run0;
+            wt[1][w] = run1;
+        }
+        __syncthreads();
+        uint32_t off0 = carry0, off1 = carry1, tot0 = 0, tot1 = 0;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) {
+            if (k < w) {
+                off0 += wt[0][k];
+                off1 += wt[1][k];
+            }
+            tot0 += wt[0][k];
+            tot1 += wt[1][k];
+        }
+#pragma unroll
+        for (int g = 0; g < kScanRows; ++g) {
+            const int64_t i = base + 64 * g;
+            if (i < nt) pairs[i] = make_uint2(off0 + v[g].x, off1 + v[g].y);
+        }
+        carry0 += tot0;
+        carry1 += tot1;
+        __syncthreads();  // wt is written again in the next round
     }
     if (threadIdx.x == 0) {
         sel[kSelCounts + 4] = 0;
