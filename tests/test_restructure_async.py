@@ -14,7 +14,7 @@ import torch
 import oracle
 from coo_spmm_fwd_amd import binding as csp
 from coo_spmm_fwd_amd import workloads as W
-from tests.gpu_util import bits, dev, host
+from tests.gpu_util import FP32_REL, assert_within, bits, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -321,3 +321,33 @@ def test_short_async_batch_refuses_layer(monkeypatch):
     finally:
         torch.cuda.synchronize()
         csp.sparse_layer_destroy(h)
+
+
+def test_pending_task_lists_with_packed_rows(orc):
+    """The packed row list (forward at B <= 4) through the pending task lists: after the first narrow
+    forward a restructure rebuilds it, so the lists restructure_async left pending on the tiled layer
+    are built with it by the next narrow forward.  Twice, each time against an eager twin bit for
+    bit (the first time both on the plain list, then both on the packed one), and once against the
+    oracle."""
+    out, in_, nnz = TILED
+    L, h1, h2 = twins(TILED, 111)
+    try:
+        n_prune, seed = nnz // 10, 112
+        step = torch.tensor([50], dtype=torch.int64, device="cuda")
+        for k in range(2):
+            csp.restructure(h1, n_prune, seed, 50 + k)
+            csp.restructure_async(h2, n_prune, seed, step)
+            torch.cuda.synchronize()
+            same_layer(h1, h2, f"step {k}")
+            for B in (2, 4):
+                X = dev(W.random_dense((B, in_), 113 + B))
+                assert np.array_equal(bits(host(csp.spmm_fwd(h1, X))), bits(host(csp.spmm_fwd(h2, X)))), \
+                    f"step {k}, B = {B}"
+        X = dev(W.random_dense((2, in_), 117))
+        r, c, v = (host(t) for t in csp.sparse_layer_export(h2))
+        ref, S = orc.spmm_fwd(out, in_, r, c, v, host(X))
+        assert_within(host(csp.spmm_fwd(h2, X)), ref, S, FP32_REL, "forward at B = 2 after the async steps")
+    finally:
+        torch.cuda.synchronize()
+        csp.sparse_layer_destroy(h1)
+        csp.sparse_layer_destroy(h2)
