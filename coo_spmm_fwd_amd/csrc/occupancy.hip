@@ -739,10 +739,12 @@ __device__ __forceinline__ uint2 tile_row_words(const uint32_t *__restrict__ occ
     return ok ? w : make_uint2(0u, 0u);
 }
 
-// Entries per column within each 1024-row chunk: tcnt[c * nrc + chunk].
+// Entries per column within each 1024-row chunk: tcnt[c * nrc + chunk], and
+// their sum over the tile's 64 columns: gsum[column group * nrc + chunk].
 // One block per tile (block index bid), wave w takes slices w, w + 4, ...
 __device__ __forceinline__ void bm_tcount(int64_t bid, const uint32_t *__restrict__ occ, int64_t inw,
-                                          int64_t rows_alloc, int64_t nrc, uint32_t *__restrict__ tcnt)
+                                          int64_t rows_alloc, int64_t nrc, uint32_t *__restrict__ tcnt,
+                                          uint32_t *__restrict__ gsum)
 {
     __shared__ uint32_t part[4][kTC];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -765,9 +767,13 @@ __device__ __forceinline__ void bm_tcount(int64_t bid, const uint32_t *__restric
         part[w][32 + lane] = c1;
     }
     __syncthreads();
+    static_assert(kTC == kWave, "the tile's columns are the lanes of wave 0");
     if (threadIdx.x < kTC) {
         const int c = threadIdx.x;
-        tcnt[(cg * kTC + c) * nrc + rc] = part[0][c] + part[1][c] + part[2][c] + part[3][c];
+        const uint32_t n = part[0][c] + part[1][c] + part[2][c] + part[3][c];
+        tcnt[(cg * kTC + c) * nrc + rc] = n;
+        const uint32_t g = wave_sum(n);
+        if (c == 0) gsum[cg * nrc + rc] = g;
     }
 }
 
@@ -776,10 +782,11 @@ __device__ __forceinline__ void bm_tcount(int64_t bid, const uint32_t *__restric
 // first, then one thread per bitmap word.
 template <typename V>
 __global__ __launch_bounds__(kThreads) void k_bm_canon_tcount(CanonArgs<V> A, int64_t rows_alloc, int64_t nrc,
-                                                              uint32_t *__restrict__ tcnt, uint32_t ntc)
+                                                              uint32_t *__restrict__ tcnt, uint32_t *__restrict__ gsum,
+                                                              uint32_t ntc)
 {
     if (blockIdx.x < ntc) {
-        bm_tcount(blockIdx.x, A.occ, A.inw, rows_alloc, nrc, tcnt);
+        bm_tcount(blockIdx.x, A.occ, A.inw, rows_alloc, nrc, tcnt, gsum);
         return;
     }
     bm_canon<V>((blockIdx.x - ntc) * kThreads + threadIdx.x, A);
@@ -807,8 +814,11 @@ __host__ __device__ inline int64_t copy3_pieces(const CopySeg &a, const CopySeg 
 }
 
 // Transposed view, one block per tile: the tile's output is, per column, a
-// run of consecutive transposed ranks from tscan[c * nrc + rc] (exclusive
-// scan of tcnt).  Lanes walk the tile's entries in that order, so stores are
+// run of consecutive transposed ranks, starting after the entries of all
+// earlier column groups (gsum), of the group's earlier columns and of the
+// column's earlier row chunks (tcnt); wave 0 adds these up while the tile's
+// bitmap words load, so no scan pass runs in between.  Lanes walk the tile's
+// entries in that order, so stores are
 // coalesced: output o -> column (search in the column starts) -> row (search
 // in the column's cumulative word counts, then the bit) -> canonical index
 // (the row's first entry in the tile plus its entries to the left).  rc = 0
@@ -818,7 +828,8 @@ __host__ __device__ inline int64_t copy3_pieces(const CopySeg &a, const CopySeg 
 template <typename V>
 __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restrict__ occ,
                                                    const uint32_t *__restrict__ pref, int64_t inw, int64_t rows_alloc,
-                                                   int64_t nrc, int64_t in, const uint32_t *__restrict__ tscan,
+                                                   int64_t nrc, int64_t in, const uint32_t *__restrict__ tcnt,
+                                                   const uint32_t *__restrict__ gsum,
                                                    const V *__restrict__ vals, int32_t *__restrict__ perm_c,
                                                    int32_t *__restrict__ rows_by_col, V *__restrict__ vals_c,
                                                    int32_t *__restrict__ col_ptr, int32_t *__restrict__ tptr,
@@ -837,6 +848,48 @@ __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restr
     __shared__ uint32_t gout[kTC];                // transposed rank of each run's first entry
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int64_t rc = blockIdx.x % nrc, cg = blockIdx.x / nrc, r0 = rc * kTR;
+    const int64_t c_glob = cg * kTC + lane;
+    uint32_t col_start = 0, group_end = 0;  // wave 0: lane's column, and the group's end
+    if (wv == 0) {
+        constexpr int U = 8;
+        const int64_t ng = cg * nrc;  // chunk sums of the earlier column groups
+        uint32_t groups = 0;
+        for (int64_t k0 = lane; k0 < ng; k0 += U * kWave) {
+            uint32_t x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t k = k0 + u * kWave;
+                const uint32_t v = gsum[k < ng ? k : 0];
+                x[u] = k < ng ? v : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) groups += x[u];
+        }
+        groups = wave_sum(groups);
+        uint32_t col = 0, above = 0;  // the column's entries, and those in chunks before rc
+        for (int64_t k0 = 0; k0 < nrc; k0 += U) {
+            uint32_t x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t k = k0 + u;
+                const uint32_t v = tcnt[c_glob * nrc + (k < nrc ? k : 0)];
+                x[u] = k < nrc ? v : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                col += x[u];
+                above += k0 + u < rc ? x[u] : 0u;
+            }
+        }
+        uint32_t incl = col;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += y;
+        }
+        col_start = groups + (incl - col) + above;
+        group_end = groups + __shfl(incl, 63, 64);
+    }
 #pragma unroll
     for (int i = 0; i < kTSlices / 4; ++i) {
         const int sl = 4 * i + wv;
@@ -866,9 +919,9 @@ __global__ __launch_bounds__(kThreads) void k_bm_tgather(const uint32_t *__restr
             cstart[kTC] = incl;
             total_s = incl;
         }
-        const int64_t c_glob = cg * kTC + lane;
-        gout[lane] = tscan[c_glob * nrc + rc];
+        gout[lane] = col_start;
         if (rc == 0 && c_glob < in) col_ptr[c_glob] = (int32_t)gout[lane];
+        if (rc == 0 && cg == inw / 2 - 1 && lane == 63) col_ptr[in] = (int32_t)group_end;  // every entry
         // Tile offsets of the column view (when the layer has tiles), in
         // 512-row blocks: this chunk's two blocks start at the column's first
         // entry in the chunk and after its entries in the chunk's first 512
@@ -1004,16 +1057,15 @@ struct BitmapRun {
         const CanonArgs<V> ca{W.occ_next, W.occ_pref_next, W.occ, W.occ_pref, (const uint64_t *)W.acc_b,
                               (const V *)L->vals, regrow, (uint32_t)nw, (uint32_t)inw, L->out, rows_out, cols_out,
                               (V *)W.vals_k, L->row_ptr, L->tiles_r.ptr, L->tiles_r.ncb};
+        uint32_t *gsum = W.tcnt + ncg * kTC * nrc;  // after the per-column counts
         k_bm_canon_tcount<V><<<(unsigned)ntiles + blocks_for(nw + 1, kThreads), kThreads, 0, s>>>(
-            ca, rows_alloc, nrc, W.tcnt, (uint32_t)ntiles);
+            ca, rows_alloc, nrc, W.tcnt, gsum, (uint32_t)ntiles);
         CSP_LAUNCHED("k_bm_canon_tcount");
-        st = exclusive_scan_u32(W.tcnt, W.tcnt, ncg * kTC * nrc, W.hist, (uint32_t *)(L->col_ptr + L->in), s);
-        if (st != CSP_OK) return st;
         const CopySeg none{nullptr, nullptr, 0};
         const CopySeg c0 = copy ? copy[0] : none, c1 = copy ? copy[1] : none, c2 = copy ? copy[2] : none;
         const unsigned cblocks = blocks_for(copy3_pieces(c0, c1, c2), kThreads);
         k_bm_tgather<V><<<(unsigned)ntiles + cblocks, kThreads, 0, s>>>(
-            W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in, W.tcnt, (const V *)W.vals_k, L->perm_c,
+            W.occ_next, W.occ_pref_next, inw, rows_alloc, nrc, L->in, W.tcnt, gsum, (const V *)W.vals_k, L->perm_c,
             L->rows_by_col, (V *)L->vals_c, L->col_ptr, L->tiles_c.ptr, L->tiles_c.ncb, ntiles, c0, c1, c2);
         CSP_LAUNCHED("k_bm_tgather");
         L->tile_ptr_ready = L->tiles_r.ptr != nullptr;  // build_tiles then only orders the tiles' rows
@@ -1182,8 +1234,8 @@ bool plan_bitmap(csp_layer *L)
     if (const char *e = std::getenv("COOSPMM_RESTRUCTURE"))  // test hook: force the sorted path
         if (std::strcmp(e, "sorted") == 0) return false;
     const int64_t inw = ceil_div(L->in, 256) * 8, rows_alloc = ceil_div(L->out, 64) * 64;
-    const int64_t nw = rows_alloc * inw, tcnt = inw * 32 * ceil_div(rows_alloc, kTR) + 1;
-    // two bitmaps and their ranks, the transposition counts
+    const int64_t nw = rows_alloc * inw, tcnt = (inw * 32 + inw / 2) * ceil_div(rows_alloc, kTR);
+    // two bitmaps and their ranks, the transposition counts and their sums per tile
     const size_t bytes = (size_t)nw * 16 + 8 + (size_t)tcnt * 4;
     if (bytes > kBitmapBytesLimit) return false;
     W.bitmap = true;
